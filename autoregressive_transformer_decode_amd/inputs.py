@@ -1,0 +1,300 @@
+"""Model shapes, workloads and seeded synthetic inputs.
+
+This module describes *what* is decoded (layer counts, widths, step counts)
+and draws the synthetic weights and inputs.  It holds none of the decode
+arithmetic: both the GPU path and the CPU oracle receive the arrays made
+here and nothing else.
+
+Random draws follow one fixed recipe so that any consumer can regenerate the
+same values: every tensor has an integer id; its elements are drawn in blocks
+of ``BLOCK`` values, block ``b`` from ``numpy.random.default_rng([seed,
+model_id, tensor_id, b])`` as float32 standard normals times the scale.  For
+bf16 models the float32 draw is rounded to bf16 (round to nearest even).
+Norm gains are 1.  Block seeding makes the values independent of how many
+threads draw them.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BLOCK = 1 << 20
+WEIGHT_SCALE = 0.02
+
+F32 = "f32"
+BF16 = "bf16"
+
+# tensor ids inside a layer (layer l uses ids 1000*(l+1) + k)
+_T_WQ, _T_WK, _T_WV, _T_BQ, _T_BK, _T_BV, _T_WO, _T_WG, _T_WU, _T_WD = range(1, 11)
+_T_HEAD = 90_000
+_T_TABLE = 80_000
+_T_PREFILL = 70_000
+_T_TEXT = 70_001
+_T_TOKENS = 70_002
+_T_KV = 60_000
+
+
+@dataclasses.dataclass(frozen=True)
+class ModelShape:
+    """Shape of one decoder stack (Qwen2/Qwen3 style)."""
+
+    name: str
+    n_layers: int
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int            # vocab of every LM head of this stack
+    n_lm_heads: int       # 1, or 15 for the code predictor
+    qk_norm: bool
+    qkv_bias: bool
+    rope_theta: float
+    rms_eps: float
+    dtype: str            # weight, embedding and KV-cache storage: F32 or BF16
+    table_vocabs: Tuple[int, ...]   # vocab of each embedding table
+    model_id: int = 0     # separates the random streams of two stacks
+
+    @property
+    def q_dim(self) -> int:
+        return self.n_q_heads * self.head_dim
+
+    @property
+    def kv_dim(self) -> int:
+        return self.n_kv_heads * self.head_dim
+
+    def weight_elems(self, with_head: bool = True) -> int:
+        h, q, kv, f = self.hidden, self.q_dim, self.kv_dim, self.ffn
+        per_layer = h * q + 2 * h * kv + q * h + 3 * h * f
+        n = per_layer * self.n_layers
+        if with_head:
+            n += self.vocab * h
+        return n
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    model: ModelShape
+    batch: int
+    prefill: int
+    steps: int
+    s_init: int                      # initial KV capacity (bucket)
+    s_max: int                       # largest KV capacity used
+    cp: Optional[ModelShape] = None  # code predictor (Talker frames)
+    frames: int = 0
+    penalty: float = 1.0
+    prefill_kind: str = "embeddings"  # or "tokens"
+    len_range: Tuple[int, int] = (0, 0)  # batched: per-stream KV length range
+
+
+def _shape(name, L, h, hq, hkv, d, f, v, dtype, qk_norm, qkv_bias, tables,
+           n_heads=1, model_id=0):
+    return ModelShape(name=name, n_layers=L, hidden=h, n_q_heads=hq,
+                      n_kv_heads=hkv, head_dim=d, ffn=f, vocab=v,
+                      n_lm_heads=n_heads, qk_norm=qk_norm, qkv_bias=qkv_bias,
+                      rope_theta=1.0e6, rms_eps=1.0e-6, dtype=dtype,
+                      table_vocabs=tuple(tables), model_id=model_id)
+
+
+TINY = _shape("tiny", 2, 512, 8, 4, 64, 1536, 2048, F32, True, False, [2048])
+ASR = _shape("asr", 8, 512, 8, 8, 64, 2048, 151936, BF16, False, True, [151936])
+TALKER06 = _shape("talker0.6b", 28, 1024, 16, 8, 128, 3072, 3072, BF16, True,
+                  False, [3072] + [2048] * 15)
+CP06 = _shape("code_predictor", 5, 1024, 16, 8, 128, 3072, 2048, BF16, True,
+              False, [3072] + [2048] * 15, n_heads=15, model_id=1)
+TALKER17 = _shape("talker1.7b", 28, 2048, 16, 8, 128, 6144, 3072, BF16, True,
+                  False, [3072])
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", TINY, batch=1, prefill=16, steps=16, s_init=128,
+                     s_max=128, prefill_kind="tokens"),
+    "asr": Workload("asr", ASR, batch=1, prefill=110, steps=400, s_init=128,
+                    s_max=512),
+    "talker0.6b": Workload("talker0.6b", TALKER06, batch=1, prefill=64,
+                           steps=74, s_init=256, s_max=256, cp=CP06,
+                           frames=75, penalty=1.05),
+    "talker1.7b": Workload("talker1.7b", TALKER17, batch=1, prefill=512,
+                           steps=1536, s_init=2048, s_max=2048),
+    "batched64": Workload("batched64", TALKER17, batch=64, prefill=0,
+                          steps=32, s_init=4096 + 64, s_max=4096 + 64,
+                          len_range=(256, 4096)),
+}
+
+# code-predictor cache: 2 prefill rows + 14 steps
+CP_CAPACITY = 16
+
+
+# --------------------------------------------------------------------------
+# drawing
+# --------------------------------------------------------------------------
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def normal(seed: int, model_id: int, tensor_id: int, shape: Sequence[int],
+           scale: float = WEIGHT_SCALE) -> np.ndarray:
+    """float32 N(0,1)*scale, block-seeded (see module docstring)."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, np.float32)
+    nb = (n + BLOCK - 1) // BLOCK
+
+    def fill(b):
+        lo, hi = b * BLOCK, min(n, (b + 1) * BLOCK)
+        rng = np.random.default_rng([seed, model_id, tensor_id, b])
+        rng.standard_normal(hi - lo, dtype=np.float32, out=out[lo:hi])
+        out[lo:hi] *= np.float32(scale)
+
+    if nb > 2:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nb)))
+    else:
+        for b in range(nb):
+            fill(b)
+    return out.reshape(shape)
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even.
+
+    Storage conversion of generated inputs (NaN never occurs here)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Tensor:
+    """A generated tensor: float32 values, plus bf16 bits when stored as bf16."""
+
+    values: np.ndarray
+    bits: Optional[np.ndarray] = None
+
+    @property
+    def storage(self) -> np.ndarray:
+        return self.bits if self.bits is not None else self.values
+
+
+def _stored(values: np.ndarray, dtype: str) -> Tensor:
+    if dtype == BF16:
+        bits = to_bf16_bits(values)
+        return Tensor(bf16_bits_to_f32(bits).reshape(values.shape),
+                      bits.reshape(values.shape))
+    return Tensor(np.ascontiguousarray(values, np.float32))
+
+
+@dataclasses.dataclass
+class LayerWeights:
+    attn_norm: np.ndarray           # [h] f32
+    wq: Tensor                      # [Hq*D, h]
+    wk: Tensor                      # [Hkv*D, h]
+    wv: Tensor                      # [Hkv*D, h]
+    bq: Optional[np.ndarray]        # [Hq*D] f32 or None
+    bk: Optional[np.ndarray]
+    bv: Optional[np.ndarray]
+    q_norm: Optional[np.ndarray]    # [D] f32 or None
+    k_norm: Optional[np.ndarray]
+    wo: Tensor                      # [h, Hq*D]
+    mlp_norm: np.ndarray            # [h]
+    w_gate: Tensor                  # [F, h]
+    w_up: Tensor                    # [F, h]
+    w_down: Tensor                  # [h, F]
+
+
+@dataclasses.dataclass
+class ModelWeights:
+    shape: ModelShape
+    layers: List[LayerWeights]
+    final_norm: np.ndarray          # [h]
+    heads: List[Tensor]             # n_lm_heads x [V, h]
+    tables: List[Tensor]            # embedding tables [V_g, h]
+
+
+def make_tables(shape: ModelShape, seed: int = 0) -> List[Tensor]:
+    """Embedding tables.  Drawn with model_id 0 so stacks can share them."""
+    return [_stored(normal(seed, 0, _T_TABLE + g, (v, shape.hidden)), shape.dtype)
+            for g, v in enumerate(shape.table_vocabs)]
+
+
+def make_weights(shape: ModelShape, seed: int = 0,
+                 tables: Optional[List[Tensor]] = None) -> ModelWeights:
+    h, q, kv, f, d = shape.hidden, shape.q_dim, shape.kv_dim, shape.ffn, shape.head_dim
+    mid = shape.model_id
+    ones_h = np.ones(h, np.float32)
+    layers = []
+    for l in range(shape.n_layers):
+        base = 1000 * (l + 1)
+
+        def w(k, shp):
+            return _stored(normal(seed, mid, base + k, shp), shape.dtype)
+
+        def b(k, n):
+            return normal(seed, mid, base + k, (n,)) if shape.qkv_bias else None
+
+        layers.append(LayerWeights(
+            attn_norm=ones_h.copy(),
+            wq=w(_T_WQ, (q, h)), wk=w(_T_WK, (kv, h)), wv=w(_T_WV, (kv, h)),
+            bq=b(_T_BQ, q), bk=b(_T_BK, kv), bv=b(_T_BV, kv),
+            q_norm=np.ones(d, np.float32) if shape.qk_norm else None,
+            k_norm=np.ones(d, np.float32) if shape.qk_norm else None,
+            wo=w(_T_WO, (h, q)), mlp_norm=ones_h.copy(),
+            w_gate=w(_T_WG, (f, h)), w_up=w(_T_WU, (f, h)), w_down=w(_T_WD, (h, f)),
+        ))
+    heads = [_stored(normal(seed, mid, _T_HEAD + j, (shape.vocab, h)), shape.dtype)
+             for j in range(shape.n_lm_heads)]
+    if tables is None:
+        tables = make_tables(shape, seed)
+    return ModelWeights(shape, layers, ones_h.copy(), heads, tables)
+
+
+def prefill_embeddings(wl: Workload, seed: int = 0) -> np.ndarray:
+    """[T, h] float32 N(0, 0.02) prefill inputs ("random embeddings")."""
+    return normal(seed, 2, _T_PREFILL, (wl.prefill, wl.model.hidden))
+
+
+def prefill_tokens(wl: Workload, seed: int = 0) -> np.ndarray:
+    """[T] int32 token ids uniform in [0, V) (token prefill workloads)."""
+    rng = np.random.default_rng([seed, 2, _T_TOKENS])
+    return rng.integers(0, wl.model.table_vocabs[0], wl.prefill).astype(np.int32)
+
+
+def text_embeddings(wl: Workload, seed: int = 0) -> np.ndarray:
+    """[frames+1, h] float32 per-frame text embeddings N(0, 0.02)."""
+    return normal(seed, 2, _T_TEXT, (wl.frames + 1, wl.model.hidden))
+
+
+def batched_lengths(wl: Workload, seed: int = 0) -> np.ndarray:
+    """Per-stream KV lengths, uniform in [lo, hi] inclusive."""
+    lo, hi = wl.len_range
+    return np.random.default_rng(seed).integers(lo, hi + 1, wl.batch).astype(np.int32)
+
+
+def batched_first_inputs(wl: Workload, seed: int = 0) -> np.ndarray:
+    """[B, h] float32 first-step inputs for the batched workload."""
+    return normal(seed, 2, _T_PREFILL + 1, (wl.batch, wl.model.hidden))
+
+
+def batched_kv(shape: ModelShape, stream: int, length: int, layer: int,
+               seed: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Synthetic cache contents of one stream and layer: K, V [Hkv, length, D]
+    as bf16 bit patterns, N(0, 1)."""
+    kvshape = (shape.n_kv_heads, length, shape.head_dim)
+    tid = _T_KV + 1000 * stream + 2 * layer
+    k = to_bf16_bits(normal(seed, 3, tid, kvshape, scale=1.0))
+    v = to_bf16_bits(normal(seed, 3, tid + 1, kvshape, scale=1.0))
+    return k.reshape(kvshape), v.reshape(kvshape)

@@ -1,0 +1,130 @@
+"""Loop-only float64 recompute of the whole sequence, for tiny shapes.
+
+A second form of the same definition as ``decoder``, kept deliberately
+different in structure: no KV cache (every prefix is recomputed from its
+first row), scalar Python loops instead of array products, the rotation
+written per channel pair, bf16 rounding done with frexp/round-half-even
+instead of bit manipulation.  Agreement of the cached oracle with this form at
+every step pins the cache logic (append position, visible length, bucket
+copies, reset) -- the "stepwise decode equals full recompute" check of the
+RKNN sidecar page and the ncnn port's KV-cache section.
+
+Only for tiny models: cost grows as T^2 * L * h * (Hq*D) in pure Python.
+"""
+
+from __future__ import annotations
+
+import math
+import struct
+from typing import List, Sequence
+
+
+def _bf16(x: float) -> float:
+    """Nearest bf16 value (8 significant bits), ties to even."""
+    if x == 0.0 or math.isinf(x) or math.isnan(x):
+        return x
+    m, e = math.frexp(x)              # x = m * 2^e, 0.5 <= |m| < 1
+    return math.ldexp(round(m * 256.0), e - 8)   # round(): half to even
+
+
+def _dot(a: Sequence[float], b: Sequence[float]) -> float:
+    s = 0.0
+    for i in range(len(a)):
+        s += float(a[i]) * float(b[i])
+    return s
+
+
+def _matvec(W, x) -> List[float]:
+    return [_dot(W[n], x) for n in range(len(W))]
+
+
+def _rms(x: Sequence[float], g, eps: float) -> List[float]:
+    ms = 0.0
+    for v in x:
+        ms += v * v
+    inv = 1.0 / math.sqrt(ms / len(x) + eps)
+    return [x[i] * inv * float(g[i]) for i in range(len(x))]
+
+
+def _f32(x: float) -> float:
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def _rotate(v: List[float], pos: int, theta: float) -> List[float]:
+    """Rotate channel pairs (i, i + D/2) by pos * theta^(-2i/D); the cosine
+    and sine are taken at float32 precision, as the definition fixes."""
+    D = len(v)
+    half = D // 2
+    out = list(v)
+    for i in range(half):
+        ang = pos * theta ** (-2.0 * i / D)
+        c, s = _f32(math.cos(ang)), _f32(math.sin(ang))
+        a, b = v[i], v[i + half]
+        out[i] = a * c - b * s
+        out[i + half] = b * c + a * s
+    return out
+
+
+def forward_rows(model, rows: Sequence[Sequence[float]]) -> List[List[float]]:
+    """Residual stream after the last layer for every row, rows at positions
+    0..T-1, row t attending to rows 0..t (recomputed, no cache)."""
+    hq, hkv, D = model.n_q_heads, model.n_kv_heads, model.head_dim
+    grp = hq // hkv
+    eps = model.rms_eps
+    xs = [[float(v) for v in r] for r in rows]
+    T = len(xs)
+    for L in model.layers:
+        Q, K, Vv = [], [], []
+        for t in range(T):
+            u = _rms(xs[t], L["attn_norm"], eps)
+            q = _matvec(L["wq"], u)
+            k = _matvec(L["wk"], u)
+            v = _matvec(L["wv"], u)
+            if L["bq"] is not None:
+                q = [q[i] + float(L["bq"][i]) for i in range(len(q))]
+                k = [k[i] + float(L["bk"][i]) for i in range(len(k))]
+                v = [v[i] + float(L["bv"][i]) for i in range(len(v))]
+            qh = [q[h * D:(h + 1) * D] for h in range(hq)]
+            kh = [k[h * D:(h + 1) * D] for h in range(hkv)]
+            vh = [v[h * D:(h + 1) * D] for h in range(hkv)]
+            if model.qk_norm:
+                qh = [_rms(a, L["q_norm"], eps) for a in qh]
+                kh = [_rms(a, L["k_norm"], eps) for a in kh]
+            qh = [_rotate(a, t, model.rope_theta) for a in qh]
+            kh = [_rotate(a, t, model.rope_theta) for a in kh]
+            if model.kv_bf16:
+                kh = [[_bf16(c) for c in a] for a in kh]
+                vh = [[_bf16(c) for c in a] for a in vh]
+            Q.append(qh)
+            K.append(kh)
+            Vv.append(vh)
+        new = []
+        for t in range(T):
+            o = []
+            for h in range(hq):
+                g = h // grp
+                sc = [_dot(Q[t][h], K[j][g]) / math.sqrt(D) for j in range(t + 1)]
+                mx = max(sc)
+                w = [math.exp(s - mx) for s in sc]
+                tot = sum(w)
+                for d in range(D):
+                    acc = 0.0
+                    for j in range(t + 1):
+                        acc += w[j] / tot * Vv[j][g][d]
+                    o.append(acc)
+            x = [xs[t][i] + v for i, v in enumerate(_matvec(L["wo"], o))]
+            wv = _rms(x, L["mlp_norm"], eps)
+            gt = _matvec(L["w_gate"], wv)
+            up = _matvec(L["w_up"], wv)
+            a = [gt[i] / (1.0 + math.exp(-gt[i])) * up[i] for i in range(len(gt))]
+            x = [x[i] + v for i, v in enumerate(_matvec(L["w_down"], a))]
+            new.append(x)
+        xs = new
+    return xs
+
+
+def last_outputs(model, rows, head: int = 0):
+    """(y, z) of the last row: final RMSNorm and LM head."""
+    x = forward_rows(model, rows)[-1]
+    y = _rms(x, model.final_norm, model.rms_eps)
+    return y, _matvec(model.heads[head], y)

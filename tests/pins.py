@@ -1,0 +1,363 @@
+"""Pins of the CPU oracle: checks against closed forms, invariants, library
+routines and brute force, each raising AssertionError on failure.
+
+They are functions (not tests) so that tests/test_oracle_pins.py can run each
+one on the real oracle and, with a planted mistake, show that it fails."""
+
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+from oracle import brute
+from oracle import decoder as od
+from tests._models import tiny_model
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _close(a, b, tol):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    err = np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+    assert err <= tol, f"normwise error {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def check_rms_closed_form():
+    """[3, 4] has mean square 12.5; unit gains give [3, 4] / sqrt(12.5 + eps)."""
+    x = np.array([3.0, 4.0])
+    got = od.rms_norm(x, np.ones(2), 1e-6)
+    exp = np.array([3.0, 4.0]) / math.sqrt(12.5 + 1e-6)
+    _close(got, exp, 1e-15)
+    # gains multiply the normalised value (x_hat * g)
+    got2 = od.rms_norm(x, np.array([2.0, 0.5]), 1e-6)
+    _close(got2, exp * np.array([2.0, 0.5]), 1e-15)
+
+
+def check_rms_invariant():
+    """With g = 1 the output's root-mean-square is 1/sqrt(1 + eps/mean(x^2))."""
+    rng = np.random.default_rng(3)
+    for scale in (1e-3, 1.0, 50.0):
+        x = rng.standard_normal(64) * scale
+        eps = 1e-6
+        y = od.rms_norm(x, np.ones(64), eps)
+        ms = np.mean(x * x)
+        assert abs(math.sqrt(np.mean(y * y)) - 1 / math.sqrt(1 + eps / ms)) < 1e-12
+
+
+# ---------------------------------------------------------------- bf16
+
+def check_bf16_vs_torch():
+    """Round-to-nearest-even to bf16 agrees with torch's float32 -> bfloat16."""
+    import torch
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * 3,
+        np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -1.0 - 2**-8, 0.0, 2**-130,
+                  65504.0, 1.00390625, 1.01171875], np.float32)])
+    t = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = od.bf16_round(x)
+    assert np.array_equal(got, t), "oracle bf16 rounding differs from torch"
+    got_b = np.array([brute._bf16(float(v)) for v in x], np.float32)
+    normal = np.abs(x) >= 2**-126
+    assert np.array_equal(got_b[normal], t[normal]), "brute bf16 differs from torch"
+
+
+# ---------------------------------------------------------------- RoPE
+
+def check_rope_hand_values():
+    """D = 4, theta = 100, position 1: channel pairs (0,2) and (1,3) turn by
+    1 rad and 0.1 rad (omega_i = theta^(-2i/D)), counter-clockwise."""
+    cos, sin = od.rope_cos_sin(1, 4, 100.0)
+    e0 = od.rope(np.array([1.0, 0, 0, 0]), cos, sin)
+    e1 = od.rope(np.array([0, 1.0, 0, 0]), cos, sin)
+    e2 = od.rope(np.array([0, 0, 1.0, 0]), cos, sin)
+    _close(e0, [math.cos(1), 0, math.sin(1), 0], 1e-7)
+    _close(e1, [0, math.cos(0.1), 0, math.sin(0.1)], 1e-7)
+    _close(e2, [-math.sin(1), 0, math.cos(1), 0], 1e-7)
+
+
+def check_rope_complex_form():
+    """Rotate-half RoPE equals multiplying z = a + ib (a = v[:D/2], b =
+    v[D/2:]) by exp(i*phi); position 0 is the identity; norms of every pair
+    are preserved."""
+    rng = np.random.default_rng(7)
+    D = 16
+    v = rng.standard_normal(D)
+    for p in (0, 1, 5, 1000):
+        cos, sin = od.rope_cos_sin(p, D, 1.0e6)
+        got = od.rope(v, cos, sin)
+        phi = p * 1.0e6 ** (-2.0 * np.arange(D // 2) / D)
+        z = (v[:D // 2] + 1j * v[D // 2:]) * np.exp(1j * phi)
+        _close(got, np.concatenate([z.real, z.imag]), 1e-6)
+        pairs = got[:D // 2] ** 2 + got[D // 2:] ** 2
+        _close(pairs, v[:D // 2] ** 2 + v[D // 2:] ** 2, 1e-6)
+        if p == 0:
+            assert np.array_equal(got, v)
+
+
+def check_rope_relative():
+    """RoPE_m(q) . RoPE_n(k) depends only on m - n."""
+    rng = np.random.default_rng(8)
+    D = 32
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+
+    def dot(m, n):
+        cm, sm = od.rope_cos_sin(m, D, 1.0e4)
+        cn, sn = od.rope_cos_sin(n, D, 1.0e4)
+        return od.rope(q, cm, sm) @ od.rope(k, cn, sn)
+
+    for m, n, s in ((3, 1, 10), (7, 7, 100), (2, 9, 33)):
+        assert abs(dot(m, n) - dot(m + s, n + s)) < 1e-5
+
+
+def check_mrope_degenerates():
+    """Interleaved mRoPE sections [24, 20, 20] (ncnn port: base = c % (D/2),
+    modality = base % 3 when base < 60, else 0) with equal t/h/w positions is
+    plain RoPE."""
+    D = 128
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal(D)
+    p = 37
+    pos3 = (p, p, p)
+    half = D // 2
+    i = np.arange(half)
+    modality = np.where(i < 60, i % 3, 0)
+    ang = np.array([pos3[m] for m in modality], np.float64) * 1.0e6 ** (-2.0 * i / D)
+    c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    mr = np.concatenate([v[:half] * c - v[half:] * s, v[half:] * c + v[:half] * s])
+    cos, sin = od.rope_cos_sin(p, D, 1.0e6)
+    _close(od.rope(v, cos, sin), mr, 1e-12)
+
+
+# ---------------------------------------------------------------- attention
+
+def check_attention_closed_form():
+    """q = 1 (D = 4), keys [1,1,1,1] and 0: scores 4/sqrt(4) = 2 and 0, so the
+    weights are e^2/(e^2+1) and 1/(e^2+1) on values e0 and e1."""
+    q = np.ones(4)
+    K = np.array([[1.0, 1, 1, 1], [0, 0, 0, 0], [9, 9, 9, 9]])
+    V = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0], [5, 5, 5, 5]])
+    o = od.attention(q, K, V, 2)      # the third row is beyond the valid length
+    a0 = math.e ** 2 / (math.e ** 2 + 1)
+    _close(o, [a0, 1 - a0, 0, 0], 1e-14)
+
+
+def check_attention_invariants():
+    """One cached row returns its V; q = 0 gives the mean of V; the weights
+    equal scipy's softmax of the scaled scores and sum to 1."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(11)
+    D, n = 8, 13
+    K, V = rng.standard_normal((n + 3, D)), rng.standard_normal((n + 3, D))
+    q = rng.standard_normal(D)
+    _close(od.attention(q, K, V, 1), V[0], 1e-14)
+    _close(od.attention(np.zeros(D), K, V, n), V[:n].mean(0), 1e-13)
+    eye = np.eye(n + 3, n + 3)
+    w = od.attention(q, K, eye, n)
+    ref = softmax(K[:n] @ q / math.sqrt(D))
+    _close(w[:n], ref, 1e-13)
+    assert abs(w.sum() - 1.0) < 1e-13
+
+
+def check_gqa_equals_mha():
+    """GQA over Hkv heads equals MHA over K, V repeated r times per head
+    (numpy repeat = repeat_interleave: query head h reads KV head h // r)."""
+    rng = np.random.default_rng(12)
+    hq, hkv, S, D, n = 8, 2, 10, 4, 7
+    q = rng.standard_normal((hq, D))
+    K, V = rng.standard_normal((hkv, S, D)), rng.standard_normal((hkv, S, D))
+    r = hq // hkv
+    mha = od.gqa_attention(q, np.repeat(K, r, axis=0), np.repeat(V, r, axis=0), n)
+    _close(od.gqa_attention(q, K, V, n), mha, 1e-14)
+
+
+# ---------------------------------------------------------------- MLP
+
+def check_mlp_closed_form():
+    """Gate W_g = 2I, up W_u = I, down W_d = I, unit gains: the residual adds
+    silu(2w) * w with w = RMSNorm(x); silu(z) = z * expit(z)."""
+    from scipy.special import expit
+    m = tiny_model(L=1, h=4, hq=2, hkv=1, D=2, F=4, bias=False, gains_random=False)
+    L = m.layers[0]
+    L["w_gate"], L["w_up"], L["w_down"] = 2 * np.eye(4), np.eye(4), np.eye(4)
+    x = np.array([0.5, -1.0, 2.0, 0.25])
+    w = x / math.sqrt(np.mean(x * x) + 1e-6)
+    exp = x + (2 * w) * expit(2 * w) * w
+    _close(od._mlp(m, L, x), exp, 1e-14)
+
+
+def check_projection_orientation():
+    """Weights are [out, in]: a permutation matrix permutes the input."""
+    m = tiny_model(L=1, h=4, hq=2, hkv=1, D=2, F=4, bias=False, qk_norm=False,
+                   gains_random=False)
+    L = m.layers[0]
+    P = np.eye(4)[[2, 0, 3, 1]]
+    L["wq"] = P
+    u = np.array([1.0, 2.0, 3.0, 4.0])
+    q, _, _ = od._qkv(m, L, u)
+    _close(q.reshape(-1), [3.0, 1.0, 4.0, 2.0], 0)
+
+
+# ---------------------------------------------------------------- cache / stack
+
+def _brute_model(kv_bf16, qk_norm=True, bias=True, hq=4, hkv=2):
+    return tiny_model(L=2, h=12, hq=hq, hkv=hkv, D=4, F=16, V=24, qk_norm=qk_norm,
+                      bias=bias, kv_bf16=kv_bf16, seed=21, scale=0.5)
+
+
+def check_cached_equals_recompute(kv_bf16=False, qk_norm=True, bias=True, hq=4, hkv=2):
+    """Cached decode (prefill 3 rows, then steps with bucket growth from
+    capacity 4) equals a from-scratch recompute of the whole sequence at every
+    step (float64 brute force, no cache)."""
+    m = _brute_model(kv_bf16, qk_norm, bias, hq, hkv)
+    rng = np.random.default_rng(22)
+    rows = [rng.standard_normal(12) for _ in range(9)]
+    cache = od.Cache(m, 4)
+    y, z = od.prefill(m, cache, np.stack(rows[:3]), 0)
+    yb, zb = brute.last_outputs(m, rows[:3])
+    _close(y, yb, 1e-9)
+    _close(z, zb, 1e-9)
+    for t in range(3, 9):
+        cap = od.bucket_for(cache.pos, cache.capacity)
+        if cap != cache.capacity:
+            cache.grow(cap)
+        y, z = od.step(m, cache, rows[t], 0)
+        yb, zb = brute.last_outputs(m, rows[:t + 1])
+        _close(y, yb, 1e-9)
+        _close(z, zb, 1e-9)
+    assert cache.pos == 9 and cache.capacity == 16
+
+
+def check_prefill_equals_steps():
+    """The block (matrix) prefill equals feeding its rows one at a time."""
+    m = tiny_model(kv_bf16=True, seed=31)
+    rng = np.random.default_rng(32)
+    X = rng.standard_normal((6, 16))
+    c1, c2 = od.Cache(m, 8), od.Cache(m, 8)
+    y1, z1 = od.prefill(m, c1, X, 0)
+    for t in range(6):
+        y2, z2 = od.step(m, c2, X[t], 0)
+    _close(y1, y2, 1e-12)
+    _close(z1, z2, 1e-12)
+    for l in range(m.n_layers):
+        _close(c1.K[l][:, :6], c2.K[l][:, :6], 1e-12)
+
+
+def check_bucket_copy_invariance():
+    """Growing the cache 4 -> 8 -> 16 leaves every output bit-identical to a
+    run that starts at capacity 16."""
+    m = tiny_model(kv_bf16=True, seed=41)
+    rng = np.random.default_rng(42)
+    X = rng.standard_normal((12, 16))
+    a, b = od.Cache(m, 4), od.Cache(m, 16)
+    od.prefill(m, a, X[:2], 0)
+    od.prefill(m, b, X[:2], 0)
+    for t in range(2, 12):
+        cap = od.bucket_for(a.pos, a.capacity)
+        if cap != a.capacity:
+            a.grow(cap)
+        ya, za = od.step(m, a, X[t], 0)
+        yb, zb = od.step(m, b, X[t], 0)
+        assert np.array_equal(ya, yb) and np.array_equal(za, zb)
+    assert a.capacity == 16
+
+
+def check_code_predictor_recompute():
+    """A Code Predictor pass with its per-frame cache (2-row prefill, then a
+    step per group, head j for group j) equals recomputing every prefix from
+    scratch (the ncnn port recomputes the Code Predictor each frame)."""
+    m = tiny_model(L=2, h=12, hq=4, hkv=2, D=4, F=16, V=10, n_heads=4,
+                   tables=(12, 10, 10, 10), bias=False, seed=51, scale=0.5)
+    rng = np.random.default_rng(52)
+    y_talker = rng.standard_normal(12)
+    codes, trace = od.code_predictor_frame(m, y_talker, c0=5, cp_capacity=8)
+    rows = [y_talker, m.tables[0][5]]
+    for j in range(4):
+        yb, zb = brute.last_outputs(m, rows, head=j)
+        _close(trace[j][0], yb, 1e-9)
+        _close(trace[j][1], zb, 1e-9)
+        assert codes[j] == int(np.argmax(zb))
+        if j + 1 < 4:
+            rows.append(m.tables[j + 1][codes[j]])
+
+
+def check_frame_input():
+    """Talker frame input = E_tk[c0] + sum_j E_cp[j][c_j] + text: with
+    one-hot tables the sum lands on known coordinates."""
+    m = tiny_model(L=1, h=20, tables=(4, 3, 3), seed=61)
+    m.tables = [np.eye(4, 20), np.eye(3, 20, k=4), np.eye(3, 20, k=7)]
+    text = np.zeros(20)
+    text[19] = 0.5
+    x = od.embed(m, [2, 1, 0], [0, 1, 2], text)
+    exp = np.zeros(20)
+    exp[[2, 5, 7]] = 1.0
+    exp[19] = 0.5
+    _close(x, exp, 0)
+
+
+# ---------------------------------------------------------------- penalty / argmax
+
+def check_penalty_and_argmax():
+    z = np.array([2.0, -1.0, 2.05, 0.5], np.float32)
+    # rho = 1: plain argmax, margin to the runner-up
+    t, mg = od.penalized_argmax(z, None, 1.0)
+    assert t == 2 and abs(mg - 0.05) < 1e-6
+    # positive logit divided: 2.05 / 1.05 = 1.952 < 2.0
+    seen = np.array([False, False, True, False])
+    t, mg = od.penalized_argmax(z, seen, 1.05)
+    assert t == 0 and abs(mg - (2.0 - np.float32(2.05) / np.float32(1.05))) < 1e-6
+    assert seen[0] and seen[2]
+    # negative logit multiplied: -1.0 * 1.05 = -1.05 < -1.02
+    z2 = np.array([-1.0, -1.02], np.float32)
+    t, _ = od.penalized_argmax(z2, np.array([True, False]), 1.05)
+    assert t == 1
+    # ties: lowest index, margin 0
+    t, mg = od.penalized_argmax(np.array([1.0, 3.0, 3.0], np.float32), None, 1.0)
+    assert t == 1 and mg == 0.0
+
+
+# ---------------------------------------------------------------- golden
+
+def read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def check_bucket_schedule_golden():
+    """Growing before a write at position == capacity (start 128, doubling)
+    reproduces the buckets and migration counts of the Audio8-ASR runs.  A
+    run of N tokens (first token and EOS included) is a prefill and N - 1
+    decode steps; step k writes KV position prefill + k - 1."""
+    for label, pre, toks, final, migr in read_golden("asr_bucket_runs.txt"):
+        pre, toks, final, migr = int(pre), int(toks), int(final), int(migr)
+        cap, moves = od.bucket_for(pre - 1, 128), 0
+        assert cap == 128
+        for k in range(1, toks):
+            p = pre + k - 1
+            new = od.bucket_for(p, cap)
+            if new != cap:
+                moves += 1
+                cap = new
+        assert (cap, moves) == (final, migr), (label, cap, moves)
+
+
+def check_talker_bytes_golden():
+    """The 0.6B Talker shape (28 layers x 7 matmuls + a 3072-row head, h 1024,
+    q 2048, kv 1024, FFN 3072) at Q8_0 moves 471.3 MB per token."""
+    from autoregressive_transformer_decode_amd import inputs
+    g = {k: float(v) for k, v in read_golden("talker_q8_bytes.txt")}
+    s = inputs.TALKER06
+    assert s.n_layers * 7 == g["matmuls"]
+    n = s.weight_elems(with_head=True)
+    mb = n * g["q8_0_bytes_per_block"] / g["q8_0_weights_per_block"] / 1e6
+    assert round(mb, 1) == g["mb_per_token"], mb

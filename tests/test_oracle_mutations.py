@@ -1,0 +1,165 @@
+"""Planted mistakes in the oracle (CPU only): each plausible slip -- a dropped
+term, a wrong sign or index, a transposed operand -- must make at least one
+pin fail.  The mistakes are planted by monkeypatching oracle.decoder."""
+
+import numpy as np
+import pytest
+
+from oracle import decoder as od
+from tests import pins
+from tests.test_oracle_pins import PINS
+
+_orig = {k: getattr(od, k) for k in dir(od) if not k.startswith("__")}
+
+
+def _all_pins():
+    yield from PINS
+    yield lambda: pins.check_cached_equals_recompute(False, True, True, 4, 2)
+    yield lambda: pins.check_cached_equals_recompute(True, False, True, 4, 4)
+
+
+def _rms_one_plus(x, g, eps):
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * (1 + g)
+
+
+def _rms_no_eps(x, g, eps):
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) * g
+
+
+def _rope_adjacent(v, cos, sin):
+    a, b = v[..., 0::2], v[..., 1::2]
+    out = np.empty_like(v)
+    out[..., 0::2] = a * cos - b * sin
+    out[..., 1::2] = b * cos + a * sin
+    return out
+
+
+def _rope_sign(v, cos, sin):
+    h = v.shape[-1] // 2
+    a, b = v[..., :h], v[..., h:]
+    return np.concatenate([a * cos + b * sin, b * cos - a * sin], axis=-1)
+
+
+def _freq_wrong(pos, D, theta):
+    i = np.arange(D // 2, dtype=np.float64)
+    phi = pos * theta ** (-i / D)
+    return np.cos(phi).astype(np.float32), np.sin(phi).astype(np.float32)
+
+
+def _attn_scale_d(q, K, V, n):
+    s = K[:n] @ q / q.shape[-1]
+    e = np.exp(s - s.max())
+    return (e / e.sum()) @ V[:n]
+
+
+def _attn_short(q, K, V, n):
+    return _orig["attention"](q, K, V, max(n - 1, 1))
+
+
+def _gqa_modulo(q, K, V, n):
+    hkv = K.shape[0]
+    return np.stack([od.attention(q[h], K[h % hkv], V[h % hkv], n)
+                     for h in range(q.shape[0])])
+
+
+def _mlp_swapped(model, L, x):
+    w = od.rms_norm(x, L["mlp_norm"], model.rms_eps)
+    a = (w @ L["w_gate"].T) * od.silu(w @ L["w_up"].T)
+    return x + a @ L["w_down"].T
+
+
+def _qkv_transposed(model, L, u):
+    L2 = dict(L)
+    for k in ("wq", "wk", "wv"):
+        W = L[k]
+        L2[k] = W.T.reshape(W.shape) if W.shape[0] != W.shape[1] else W.T
+    return _orig["_qkv"](model, L2, u)
+
+
+def _penalty_mul_pos(z, seen, rho):
+    z = np.array(z, np.float32, copy=True)
+    if seen is None or rho == 1.0:
+        return z
+    idx = np.nonzero(seen)[0]
+    z[idx] = z[idx] * np.float32(rho)
+    return z
+
+
+def _argmax_last(z, seen, rho):
+    zp = od.penalized_logits(z, seen, rho)
+    tok = int(len(zp) - 1 - np.argmax(zp[::-1]))
+    rest = np.delete(zp, tok)
+    if seen is not None:
+        seen[tok] = True
+    return tok, float(zp[tok] - rest.max())
+
+
+def _bf16_trunc(a):
+    f = np.asarray(a, np.float32)
+    u = f.view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(np.asarray(a).dtype)
+
+
+def _embed_no_extra(model, toks, table_ids, extra=None):
+    return _orig["embed"](model, toks, table_ids, None)
+
+
+class _ShortGrowCache(od.Cache):
+    def grow(self, capacity):
+        keep = self.pos
+        self.pos = max(keep - 1, 0)
+        super().grow(capacity)
+        self.pos = keep
+
+
+def _prefill_no_mask(model, cache, X, head=0):
+    real = np.tril
+    np.tril = lambda m: np.ones_like(m)
+    try:
+        return _orig["prefill"](model, cache, X, head)
+    finally:
+        np.tril = real
+
+
+def _cp_head0(cp, y_talker, c0, cp_capacity=16, forced=None):
+    real_step = od.step
+    try:
+        od.step = lambda m, c, x, head=0: real_step(m, c, x, 0)
+        return _orig["code_predictor_frame"](cp, y_talker, c0, cp_capacity, forced)
+    finally:
+        od.step = real_step
+
+
+MUTATIONS = {
+    "rms_gain_one_plus_g": ("rms_norm", _rms_one_plus),
+    "rms_no_eps": ("rms_norm", _rms_no_eps),
+    "rope_adjacent_pairs": ("rope", _rope_adjacent),
+    "rope_sign": ("rope", _rope_sign),
+    "rope_frequency": ("rope_cos_sin", _freq_wrong),
+    "attention_scale_1_over_D": ("attention", _attn_scale_d),
+    "attention_one_row_short": ("attention", _attn_short),
+    "gqa_modulo_mapping": ("gqa_attention", _gqa_modulo),
+    "swiglu_gate_up_swapped": ("_mlp", _mlp_swapped),
+    "qkv_transposed": ("_qkv", _qkv_transposed),
+    "penalty_multiplies_positive": ("penalized_logits", _penalty_mul_pos),
+    "argmax_last_tie": ("penalized_argmax", _argmax_last),
+    "bf16_truncates": ("bf16_round", _bf16_trunc),
+    "embed_drops_extra": ("embed", _embed_no_extra),
+    "grow_copies_short": ("Cache", _ShortGrowCache),
+    "prefill_no_causal_mask": ("prefill", _prefill_no_mask),
+    "code_predictor_one_head": ("code_predictor_frame", _cp_head0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, repl = MUTATIONS[name]
+    monkeypatch.setattr(od, attr, repl)
+    caught = []
+    for pin in _all_pins():
+        try:
+            pin()
+        except Exception as e:  # noqa: BLE001 -- an error also flags the slip
+            caught.append(type(e).__name__)
+            break
+    assert caught, f"no pin catches the planted mistake {name}"

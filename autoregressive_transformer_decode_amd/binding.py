@@ -1,0 +1,158 @@
+"""ctypes binding of libatd.so: one Python function per C entry point, same
+names and argument order (pointers as integers, the stream as an integer
+hipStream_t).  Marshalling and error translation only: every computation
+runs in the library's HIP kernels.  Importing this module fails loudly if the
+library has not been built."""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libatd.so")
+
+ATD_OK = 0
+ATD_ERR_INVALID_ARG = -1
+ATD_ERR_SHAPE = -2
+ATD_ERR_DTYPE = -3
+ATD_ERR_KV_FULL = -4
+ATD_ERR_CAPACITY = -5
+ATD_ERR_DEVICE = -6
+ATD_ERR_UNSUPPORTED = -7
+ATD_F32 = 0
+ATD_BF16 = 1
+ATD_FLAG_DRY_RUN = 1
+
+STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FULL",
+                -5: "CAPACITY", -6: "DEVICE", -7: "UNSUPPORTED"}
+
+EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
+           "decoder_set_position", "decoder_get_position", "decoder_prefill",
+           "decoder_step", "decoder_embed", "greedy_argmax")
+
+
+class AtdError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+class atd_config(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("hidden", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
+                ("vocab", C.c_int32), ("n_lm_heads", C.c_int32), ("n_tables", C.c_int32),
+                ("qk_norm", C.c_int32), ("qkv_bias", C.c_int32), ("dtype", C.c_int32),
+                ("rope_theta", C.c_double), ("rms_eps", C.c_float),
+                ("max_slots", C.c_int32), ("max_rows", C.c_int32), ("max_ctx", C.c_int32),
+                ("flags", C.c_int32)]
+
+
+class atd_layer_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "attn_norm", "wq", "wk", "wv", "bq", "bk", "bv", "q_norm", "k_norm", "wo",
+        "mlp_norm", "w_gate", "w_up", "w_down")]
+
+
+class atd_weights(C.Structure):
+    _fields_ = [("layers", C.POINTER(atd_layer_weights)), ("final_norm", C.c_void_p),
+                ("lm_heads", C.POINTER(C.c_void_p)), ("tables", C.POINTER(C.c_void_p)),
+                ("table_vocab", C.POINTER(C.c_int32))]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m autoregressive_transformer_decode_amd.build` (there is no fallback)")
+    lib = C.CDLL(LIB_PATH)
+    vp, i32, f32 = C.c_void_p, C.c_int32, C.c_float
+    sig = {
+        "decoder_create": ([C.POINTER(atd_config), C.POINTER(atd_weights), C.POINTER(vp)], C.c_int),
+        "decoder_destroy": ([vp], C.c_int),
+        "decoder_last_error": ([vp], C.c_char_p),
+        "kv_bucket_grow": ([vp, i32, C.POINTER(vp), C.POINTER(vp), i32, vp], C.c_int),
+        "decoder_set_position": ([vp, i32, i32, vp], C.c_int),
+        "decoder_get_position": ([vp, i32, C.POINTER(i32), C.POINTER(i32)], C.c_int),
+        "decoder_prefill": ([vp, i32, vp, i32, i32, vp, vp, vp], C.c_int),
+        "decoder_step": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, vp, vp], C.c_int),
+        "decoder_embed": ([vp, i32, vp, i32, C.POINTER(i32), vp, vp, vp], C.c_int),
+        "greedy_argmax": ([vp, i32, i32, vp, f32, vp, vp, vp], C.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int, handle=None):
+    if rc != ATD_OK:
+        msg = lib.decoder_last_error(handle).decode(errors="replace")
+        raise AtdError(rc, msg)
+    return rc
+
+
+def _i32_array(vals):
+    arr = (C.c_int32 * max(1, len(vals)))(*vals)
+    return arr
+
+
+def _ptr_array(vals):
+    return (C.c_void_p * max(1, len(vals)))(*vals)
+
+
+# ----------------------------------------------------------------- entry points
+
+def decoder_create(cfg: atd_config, weights: atd_weights) -> int:
+    out = C.c_void_p()
+    _check(lib.decoder_create(C.byref(cfg), C.byref(weights), C.byref(out)))
+    return out.value
+
+
+def decoder_destroy(handle: int) -> None:
+    _check(lib.decoder_destroy(handle))
+
+
+def decoder_last_error(handle) -> str:
+    return lib.decoder_last_error(handle).decode(errors="replace")
+
+
+def kv_bucket_grow(handle: int, slot: int, k_new, v_new, s_new: int, stream: int) -> None:
+    _check(lib.kv_bucket_grow(handle, slot, _ptr_array(k_new), _ptr_array(v_new), s_new,
+                              stream), handle)
+
+
+def decoder_set_position(handle: int, slot: int, pos: int, stream: int) -> None:
+    _check(lib.decoder_set_position(handle, slot, pos, stream), handle)
+
+
+def decoder_get_position(handle: int, slot: int):
+    p, c = C.c_int32(), C.c_int32()
+    _check(lib.decoder_get_position(handle, slot, C.byref(p), C.byref(c)), handle)
+    return p.value, c.value
+
+
+def decoder_prefill(handle: int, slot: int, x: int, T: int, head: int, y_out, logits_out: int,
+                    stream: int) -> None:
+    _check(lib.decoder_prefill(handle, slot, x, T, head, y_out, logits_out, stream), handle)
+
+
+def decoder_step(handle: int, slot0: int, B: int, tok, G: int, table_ids, extra, head: int,
+                 y_out, logits_out: int, stream: int) -> None:
+    _check(lib.decoder_step(handle, slot0, B, tok, G, _i32_array(list(table_ids)), extra, head,
+                            y_out, logits_out, stream), handle)
+
+
+def decoder_embed(handle: int, B: int, tok, G: int, table_ids, extra, x_out: int,
+                  stream: int) -> None:
+    _check(lib.decoder_embed(handle, B, tok, G, _i32_array(list(table_ids)), extra, x_out,
+                             stream), handle)
+
+
+def greedy_argmax(logits: int, B: int, V: int, seen, penalty: float, tok_out: int, margin_out,
+                  stream: int) -> None:
+    _check(lib.greedy_argmax(logits, B, V, seen, penalty, tok_out, margin_out, stream))

@@ -1,0 +1,680 @@
+// C-ABI entry points: host-side validation, decoder state and the launch
+// sequence of a step.  Every check runs before any HIP call, so a refused
+// call leaves the decoder unchanged and touches no device.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/atd.h"
+#include "internal.h"
+
+using namespace atd;
+
+struct atd_decoder {
+  atd_config cfg{};
+  std::vector<atd_layer_weights> layers;
+  const float* final_norm = nullptr;
+  std::vector<const void*> heads, tables;
+  std::vector<int32_t> table_vocab;
+  // host mirror of every slot
+  std::vector<int32_t> pos, cap;
+  std::vector<char> attached;
+  std::vector<std::vector<void*>> kp, vp;
+  int device = 0;
+  // device scratch, one allocation
+  void* mem = nullptr;
+  float *cos_t = nullptr, *sin_t = nullptr;
+  float *x = nullptr, *qkv = nullptr, *q = nullptr, *o = nullptr, *act = nullptr;
+  float *pml = nullptr, *pacc = nullptr;
+  void** kv_tab = nullptr;
+  int *slot_pos = nullptr, *slot_cap = nullptr;
+  int nsplit_max = 0;
+  bool dry = false;  // ATD_FLAG_DRY_RUN: host state only, no HIP calls
+  std::string err;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(atd_decoder* d, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (d)
+    d->err = buf;
+  else
+    g_err = buf;
+  return code;
+}
+
+int hip_fail(atd_decoder* d, hipError_t e, const char* what) {
+  return fail(d, ATD_ERR_DEVICE, "%s failed: %s (%s)", what, hipGetErrorName(e),
+              hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(const atd_config& c) { return c.dtype == ATD_BF16 ? 2 : 4; }
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int check_config(const atd_config* c) {
+  if (!c) return fail(nullptr, ATD_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->dtype != ATD_F32 && c->dtype != ATD_BF16)
+    return fail(nullptr, ATD_ERR_DTYPE, "dtype %d is not ATD_F32 (0) or ATD_BF16 (1)", c->dtype);
+  if (c->n_layers < 1 || c->n_layers > kMaxLayers)
+    return fail(nullptr, ATD_ERR_UNSUPPORTED, "n_layers %d outside [1, %d]", c->n_layers,
+                kMaxLayers);
+  if (c->hidden < 8 || c->hidden % 8 || c->hidden > 8192)
+    return fail(nullptr, ATD_ERR_UNSUPPORTED, "hidden %d: must be a multiple of 8 in [8, 8192]",
+                c->hidden);
+  if (c->ffn < 8 || c->ffn % 8 || c->ffn > 8192)
+    return fail(nullptr, ATD_ERR_UNSUPPORTED, "ffn %d: must be a multiple of 8 in [8, 8192]",
+                c->ffn);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(nullptr, ATD_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are implemented",
+                c->head_dim);
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads)
+    return fail(nullptr, ATD_ERR_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                c->n_q_heads, c->n_kv_heads);
+  {
+    const int r = c->n_q_heads / c->n_kv_heads;
+    if (r != 1 && r != 2 && r != 4 && r != 8)
+      return fail(nullptr, ATD_ERR_UNSUPPORTED, "n_q_heads / n_kv_heads = %d not in {1,2,4,8}",
+                  r);
+  }
+  if ((long)c->n_q_heads * c->head_dim > 8192)
+    return fail(nullptr, ATD_ERR_UNSUPPORTED, "n_q_heads * head_dim %d > 8192",
+                c->n_q_heads * c->head_dim);
+  if (c->vocab < 2)
+    return fail(nullptr, ATD_ERR_SHAPE, "vocab %d < 2", c->vocab);
+  if (c->n_lm_heads < 1)
+    return fail(nullptr, ATD_ERR_SHAPE, "n_lm_heads %d < 1", c->n_lm_heads);
+  if (c->n_tables < 1 || c->n_tables > kMaxTables)
+    return fail(nullptr, ATD_ERR_UNSUPPORTED, "n_tables %d outside [1, %d]", c->n_tables,
+                kMaxTables);
+  if (c->qk_norm != 0 && c->qk_norm != 1)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "qk_norm %d is not 0 or 1", c->qk_norm);
+  if (c->qkv_bias != 0 && c->qkv_bias != 1)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "qkv_bias %d is not 0 or 1", c->qkv_bias);
+  if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta))
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "rope_theta %g is not positive", c->rope_theta);
+  if (!(c->rms_eps >= 0.0f) || !std::isfinite(c->rms_eps))
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "rms_eps %g is negative", (double)c->rms_eps);
+  if (c->max_slots < 1 || c->max_slots > 65536)
+    return fail(nullptr, ATD_ERR_CAPACITY, "max_slots %d outside [1, 65536]", c->max_slots);
+  if (c->max_rows < 1 || c->max_rows > 65536)
+    return fail(nullptr, ATD_ERR_CAPACITY, "max_rows %d outside [1, 65536]", c->max_rows);
+  if (c->max_ctx < 1 || c->max_ctx > (1 << 20))
+    return fail(nullptr, ATD_ERR_CAPACITY, "max_ctx %d outside [1, 2^20]", c->max_ctx);
+  if (c->flags & ~ATD_FLAG_DRY_RUN)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)c->flags);
+  return ATD_OK;
+}
+
+#define NEED(ptr, name)                                                                    \
+  do {                                                                                     \
+    if (!(ptr)) return fail(nullptr, ATD_ERR_INVALID_ARG, "%s is NULL", name);              \
+    if (!aligned16(ptr)) return fail(nullptr, ATD_ERR_INVALID_ARG, "%s %p not 16-byte aligned", \
+                                     name, (const void*)(ptr));                             \
+  } while (0)
+
+int check_weights(const atd_config* c, const atd_weights* w) {
+  if (!w) return fail(nullptr, ATD_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->layers || !w->lm_heads || !w->tables || !w->table_vocab)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "weights has a NULL host array");
+  char name[64];
+  for (int l = 0; l < c->n_layers; ++l) {
+    const atd_layer_weights& L = w->layers[l];
+#define LW(field)                                                 \
+  snprintf(name, sizeof name, "layers[%d]." #field, l);           \
+  NEED(L.field, name);
+    LW(attn_norm) LW(wq) LW(wk) LW(wv) LW(wo) LW(mlp_norm) LW(w_gate) LW(w_up) LW(w_down)
+    if (c->qkv_bias) {
+      LW(bq) LW(bk) LW(bv)
+    } else if (L.bq || L.bk || L.bv) {
+      return fail(nullptr, ATD_ERR_INVALID_ARG,
+                  "layers[%d] has q/k/v bias pointers but qkv_bias = 0", l);
+    }
+    if (c->qk_norm) {
+      LW(q_norm) LW(k_norm)
+    } else if (L.q_norm || L.k_norm) {
+      return fail(nullptr, ATD_ERR_INVALID_ARG,
+                  "layers[%d] has QK-norm gains but qk_norm = 0", l);
+    }
+#undef LW
+  }
+  NEED(w->final_norm, "final_norm");
+  for (int j = 0; j < c->n_lm_heads; ++j) {
+    snprintf(name, sizeof name, "lm_heads[%d]", j);
+    NEED(w->lm_heads[j], name);
+  }
+  for (int g = 0; g < c->n_tables; ++g) {
+    snprintf(name, sizeof name, "tables[%d]", g);
+    NEED(w->tables[g], name);
+    if (w->table_vocab[g] < 1)
+      return fail(nullptr, ATD_ERR_SHAPE, "table_vocab[%d] = %d < 1", g, w->table_vocab[g]);
+  }
+  return ATD_OK;
+}
+
+SlotTables slots_of(const atd_decoder* d) {
+  SlotTables st;
+  st.kv = d->kv_tab;
+  st.pos = d->slot_pos;
+  st.cap = d->slot_cap;
+  st.L = d->cfg.n_layers;
+  return st;
+}
+
+int chunk_for(int M) { return M <= 2 ? kAttnChunkSmall : kAttnChunkLarge; }
+
+// The per-layer launch sequence for M rows (decode step or prefill block).
+hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hipStream_t s) {
+  const atd_config& c = d->cfg;
+  const int h = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv;
+  const int bf16 = c.dtype == ATD_BF16;
+  const SlotTables st = slots_of(d);
+  const int chunk = chunk_for(M);
+  const int nsplit = std::min(d->nsplit_max, (max_len_bound + chunk - 1) / chunk);
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
+    const atd_layer_weights& W = d->layers[l];
+    GemvArgs g{};
+    g.W[0] = W.wq;
+    g.W[1] = W.wk;
+    g.W[2] = W.wv;
+    g.bias[0] = (const float*)W.bq;
+    g.bias[1] = (const float*)W.bk;
+    g.bias[2] = (const float*)W.bv;
+    g.seg_end[0] = nq;
+    g.seg_end[1] = nq + nkv;
+    g.seg_end[2] = nqkv;
+    g.x = d->x;
+    g.ldx = h;
+    g.gain = (const float*)W.attn_norm;
+    g.eps = c.rms_eps;
+    g.out = d->qkv;
+    g.ldo = nqkv;
+    g.K = h;
+    g.N = nqkv;
+    g.M = M;
+    if ((e = launch_gemv(g, kEpiStore, true, bf16, s)) != hipSuccess) break;
+
+    RopeArgs r{};
+    r.qkv = d->qkv;
+    r.q_out = d->q;
+    r.q_norm = (const float*)W.q_norm;
+    r.k_norm = (const float*)W.k_norm;
+    r.eps = c.rms_eps;
+    r.cos_t = d->cos_t;
+    r.sin_t = d->sin_t;
+    r.st = st;
+    r.rows = rows;
+    r.layer = l;
+    r.M = M;
+    r.Hq = Hq;
+    r.Hkv = Hkv;
+    r.D = D;
+    r.qk_norm = c.qk_norm;
+    if ((e = launch_rope_append(r, bf16, s)) != hipSuccess) break;
+
+    AttnArgs a{};
+    a.q = d->q;
+    a.st = st;
+    a.rows = rows;
+    a.layer = l;
+    a.M = M;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.chunk = chunk;
+    a.nsplit_max = nsplit;
+    a.scale = 1.0f / std::sqrt((float)D);
+    a.pml = d->pml;
+    a.pacc = d->pacc;
+    a.o = d->o;
+    if ((e = launch_attention(a, bf16, D, Hq / Hkv, s)) != hipSuccess) break;
+
+    GemvArgs op{};
+    op.W[0] = W.wo;
+    op.seg_end[0] = op.seg_end[1] = op.seg_end[2] = h;
+    op.x = d->o;
+    op.ldx = nq;
+    op.out = d->x;
+    op.ldo = h;
+    op.K = nq;
+    op.N = h;
+    op.M = M;
+    if ((e = launch_gemv(op, kEpiResidual, false, bf16, s)) != hipSuccess) break;
+
+    GemvArgs gu{};
+    gu.W[0] = W.w_gate;
+    gu.W2 = W.w_up;
+    gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = c.ffn;
+    gu.x = d->x;
+    gu.ldx = h;
+    gu.gain = (const float*)W.mlp_norm;
+    gu.eps = c.rms_eps;
+    gu.out = d->act;
+    gu.ldo = c.ffn;
+    gu.K = h;
+    gu.N = c.ffn;
+    gu.M = M;
+    if ((e = launch_gemv(gu, kEpiSwiglu, true, bf16, s)) != hipSuccess) break;
+
+    GemvArgs dn{};
+    dn.W[0] = W.w_down;
+    dn.seg_end[0] = dn.seg_end[1] = dn.seg_end[2] = h;
+    dn.x = d->act;
+    dn.ldx = c.ffn;
+    dn.out = d->x;
+    dn.ldo = h;
+    dn.K = c.ffn;
+    dn.N = h;
+    dn.M = M;
+    e = launch_gemv(dn, kEpiResidual, false, bf16, s);
+  }
+  return e;
+}
+
+hipError_t run_head(atd_decoder* d, const float* xrows, int M, int head, float* y_out,
+                    float* logits, hipStream_t s) {
+  const atd_config& c = d->cfg;
+  GemvArgs g{};
+  g.W[0] = d->heads[head];
+  g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = c.vocab;
+  g.x = xrows;
+  g.ldx = c.hidden;
+  g.gain = d->final_norm;
+  g.eps = c.rms_eps;
+  g.out = logits;
+  g.ldo = c.vocab;
+  g.y_out = y_out;
+  g.K = c.hidden;
+  g.N = c.vocab;
+  g.M = M;
+  return launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16, s);
+}
+
+int check_tables(atd_decoder* d, int G, const int32_t* table_ids, const int32_t* tok,
+                 const float* extra) {
+  if (G < 0 || G > kMaxTables)
+    return fail(d, ATD_ERR_INVALID_ARG, "G = %d outside [0, %d]", G, kMaxTables);
+  if (G == 0 && !extra)
+    return fail(d, ATD_ERR_INVALID_ARG, "G = 0 needs extra input rows");
+  if (G > 0 && (!tok || !table_ids))
+    return fail(d, ATD_ERR_INVALID_ARG, "tok or table_ids is NULL with G = %d", G);
+  for (int g = 0; g < G; ++g)
+    if (table_ids[g] < 0 || table_ids[g] >= d->cfg.n_tables)
+      return fail(d, ATD_ERR_INVALID_ARG, "table_ids[%d] = %d outside [0, %d)", g, table_ids[g],
+                  d->cfg.n_tables);
+  return ATD_OK;
+}
+
+EmbedArgs embed_args(atd_decoder* d, int B, const int32_t* tok, int G,
+                     const int32_t* table_ids, const float* extra, float* out) {
+  EmbedArgs e{};
+  for (int g = 0; g < G; ++g) {
+    e.tab[g] = d->tables[table_ids[g]];
+    e.vocab[g] = d->table_vocab[table_ids[g]];
+  }
+  e.G = G;
+  e.tok = tok;
+  e.extra = extra;
+  e.out = out;
+  e.h = d->cfg.hidden;
+  e.M = B;
+  return e;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_decoder** out) {
+  if (!out) return fail(nullptr, ATD_ERR_INVALID_ARG, "out is NULL");
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if ((rc = check_weights(cfg, w))) return rc;
+
+  atd_decoder* d = new atd_decoder();
+  d->cfg = *cfg;
+  d->layers.assign(w->layers, w->layers + cfg->n_layers);
+  d->final_norm = (const float*)w->final_norm;
+  d->heads.assign(w->lm_heads, w->lm_heads + cfg->n_lm_heads);
+  d->tables.assign(w->tables, w->tables + cfg->n_tables);
+  d->table_vocab.assign(w->table_vocab, w->table_vocab + cfg->n_tables);
+  const int S = cfg->max_slots;
+  d->pos.assign(S, 0);
+  d->cap.assign(S, 0);
+  d->attached.assign(S, 0);
+  d->kp.assign(S, std::vector<void*>(cfg->n_layers, nullptr));
+  d->vp.assign(S, std::vector<void*>(cfg->n_layers, nullptr));
+
+  d->dry = (cfg->flags & ATD_FLAG_DRY_RUN) != 0;
+  d->nsplit_max = (cfg->max_ctx + kAttnChunkSmall - 1) / kAttnChunkSmall;
+  if (d->dry) {
+    *out = d;
+    return ATD_OK;
+  }
+  const int R = cfg->max_rows, h = cfg->hidden, D = cfg->head_dim;
+  const int nq = cfg->n_q_heads * D, nqkv = nq + 2 * cfg->n_kv_heads * D;
+  const size_t half = D / 2;
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t o_cos = carve((size_t)cfg->max_ctx * half * 4);
+  const size_t o_sin = carve((size_t)cfg->max_ctx * half * 4);
+  const size_t o_x = carve((size_t)R * h * 4);
+  const size_t o_qkv = carve((size_t)R * nqkv * 4);
+  const size_t o_q = carve((size_t)R * nq * 4);
+  const size_t o_o = carve((size_t)R * nq * 4);
+  const size_t o_act = carve((size_t)R * cfg->ffn * 4);
+  const size_t o_pml = carve((size_t)R * cfg->n_q_heads * d->nsplit_max * 2 * 4);
+  const size_t o_pacc = carve((size_t)R * cfg->n_q_heads * d->nsplit_max * D * 4);
+  const size_t o_kv = carve((size_t)S * cfg->n_layers * 2 * sizeof(void*));
+  const size_t o_pos = carve((size_t)S * 4);
+  const size_t o_cap = carve((size_t)S * 4);
+
+  hipError_t e = hipGetDevice(&d->device);
+  if (e == hipSuccess) e = hipMalloc(&d->mem, off);
+  if (e != hipSuccess) {
+    rc = hip_fail(nullptr, e, "hipMalloc of decoder scratch");
+    delete d;
+    return rc;
+  }
+  char* base = static_cast<char*>(d->mem);
+  d->cos_t = (float*)(base + o_cos);
+  d->sin_t = (float*)(base + o_sin);
+  d->x = (float*)(base + o_x);
+  d->qkv = (float*)(base + o_qkv);
+  d->q = (float*)(base + o_q);
+  d->o = (float*)(base + o_o);
+  d->act = (float*)(base + o_act);
+  d->pml = (float*)(base + o_pml);
+  d->pacc = (float*)(base + o_pacc);
+  d->kv_tab = (void**)(base + o_kv);
+  d->slot_pos = (int*)(base + o_pos);
+  d->slot_cap = (int*)(base + o_cap);
+
+  // RoPE table: phi = p * theta^(-2i/D) in double, cos/sin rounded to float.
+  std::vector<float> ct((size_t)cfg->max_ctx * half), sn((size_t)cfg->max_ctx * half);
+  for (int p = 0; p < cfg->max_ctx; ++p)
+    for (size_t i = 0; i < half; ++i) {
+      const double omega = std::pow(cfg->rope_theta, -2.0 * (double)i / (double)D);
+      const double phi = (double)p * omega;
+      ct[(size_t)p * half + i] = (float)std::cos(phi);
+      sn[(size_t)p * half + i] = (float)std::sin(phi);
+    }
+  e = hipMemcpy(d->cos_t, ct.data(), ct.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(d->sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(base + o_kv, 0, off - o_kv);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    rc = hip_fail(nullptr, e, "decoder scratch initialisation");
+    (void)hipFree(d->mem);
+    delete d;
+    return rc;
+  }
+  *out = d;
+  return ATD_OK;
+}
+
+extern "C" int decoder_destroy(atd_decoder* d) {
+  if (!d) return ATD_OK;
+  hipError_t e = hipSuccess;
+  if (d->mem && !d->dry) {
+    e = hipDeviceSynchronize();
+    hipError_t e2 = hipFree(d->mem);
+    if (e == hipSuccess) e = e2;
+  }
+  delete d;
+  return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "decoder_destroy");
+}
+
+extern "C" const char* decoder_last_error(const atd_decoder* d) {
+  return d ? d->err.c_str() : g_err.c_str();
+}
+
+extern "C" int kv_bucket_grow(atd_decoder* d, int32_t slot, void* const* k_new,
+                              void* const* v_new, int32_t s_new, void* stream) {
+  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
+  const atd_config& c = d->cfg;
+  if (slot < 0 || slot >= c.max_slots)
+    return fail(d, ATD_ERR_INVALID_ARG, "slot %d outside [0, %d)", slot, c.max_slots);
+  if (!k_new || !v_new) return fail(d, ATD_ERR_INVALID_ARG, "k_new or v_new is NULL");
+  if (s_new < 1 || s_new > c.max_ctx)
+    return fail(d, ATD_ERR_CAPACITY, "s_new %d outside [1, max_ctx %d]", s_new, c.max_ctx);
+  const bool first = !d->attached[slot];
+  if (!first && s_new <= d->pos[slot])
+    return fail(d, ATD_ERR_CAPACITY, "s_new %d does not exceed the %d valid rows of slot %d",
+                s_new, d->pos[slot], slot);
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (!k_new[l] || !v_new[l] || !aligned16(k_new[l]) || !aligned16(v_new[l]))
+      return fail(d, ATD_ERR_INVALID_ARG, "layer %d K/V buffer NULL or not 16-byte aligned", l);
+    for (int j = 0; j < c.n_layers && !first; ++j)
+      if (k_new[l] == d->kp[slot][j] || v_new[l] == d->vp[slot][j] ||
+          k_new[l] == d->vp[slot][j] || v_new[l] == d->kp[slot][j])
+        return fail(d, ATD_ERR_INVALID_ARG, "layer %d new buffer aliases a buffer in use", l);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (!d->dry && !first && d->pos[slot] > 0) {
+    KvCopyArgs a{};
+    for (int l = 0; l < c.n_layers; ++l) {
+      a.src[2 * l] = d->kp[slot][l];
+      a.src[2 * l + 1] = d->vp[slot][l];
+      a.dst[2 * l] = k_new[l];
+      a.dst[2 * l + 1] = v_new[l];
+    }
+    a.n = 2 * c.n_layers;
+    a.Hkv = c.n_kv_heads;
+    a.D = c.head_dim;
+    a.rows = d->pos[slot];
+    a.s_old = d->cap[slot];
+    a.s_new = s_new;
+    a.elem_bytes = elem_bytes(c);
+    e = launch_kv_copy(a, s);
+  }
+  if (e == hipSuccess && !d->dry)
+    e = launch_set_slot(slots_of(d), slot, k_new, v_new, s_new, first ? 0 : -1, 1, s);
+  if (e != hipSuccess) return hip_fail(d, e, "kv_bucket_grow");
+  for (int l = 0; l < c.n_layers; ++l) {
+    d->kp[slot][l] = k_new[l];
+    d->vp[slot][l] = v_new[l];
+  }
+  d->cap[slot] = s_new;
+  if (first) d->pos[slot] = 0;
+  d->attached[slot] = 1;
+  return ATD_OK;
+}
+
+extern "C" int decoder_set_position(atd_decoder* d, int32_t slot, int32_t pos, void* stream) {
+  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
+  if (slot < 0 || slot >= d->cfg.max_slots)
+    return fail(d, ATD_ERR_INVALID_ARG, "slot %d outside [0, %d)", slot, d->cfg.max_slots);
+  if (!d->attached[slot])
+    return fail(d, ATD_ERR_INVALID_ARG, "slot %d has no KV buffers attached", slot);
+  if (pos < 0 || pos > d->cap[slot])
+    return fail(d, ATD_ERR_CAPACITY, "pos %d outside [0, capacity %d]", pos, d->cap[slot]);
+  hipError_t e = d->dry ? hipSuccess
+                        : launch_set_slot(slots_of(d), slot, nullptr, nullptr, -1, pos, 0,
+                                          (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(d, e, "decoder_set_position");
+  d->pos[slot] = pos;
+  return ATD_OK;
+}
+
+extern "C" int decoder_get_position(const atd_decoder* d, int32_t slot, int32_t* pos,
+                                    int32_t* capacity) {
+  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
+  if (slot < 0 || slot >= d->cfg.max_slots)
+    return fail(const_cast<atd_decoder*>(d), ATD_ERR_INVALID_ARG, "slot %d outside [0, %d)",
+                slot, d->cfg.max_slots);
+  if (pos) *pos = d->pos[slot];
+  if (capacity) *capacity = d->cap[slot];
+  return ATD_OK;
+}
+
+extern "C" int decoder_embed(atd_decoder* d, int32_t B, const int32_t* tok, int32_t G,
+                             const int32_t* table_ids, const float* extra, float* x_out,
+                             void* stream) {
+  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
+  if (B < 1 || B > d->cfg.max_rows)
+    return fail(d, ATD_ERR_CAPACITY, "B = %d outside [1, max_rows %d]", B, d->cfg.max_rows);
+  if (!x_out) return fail(d, ATD_ERR_INVALID_ARG, "x_out is NULL");
+  int rc = check_tables(d, G, table_ids, tok, extra);
+  if (rc) return rc;
+  if (d->dry) return ATD_OK;
+  EmbedArgs a = embed_args(d, B, tok, G, table_ids, extra, x_out);
+  hipError_t e = launch_embed(a, d->cfg.dtype == ATD_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? ATD_OK : hip_fail(d, e, "decoder_embed");
+}
+
+extern "C" int decoder_prefill(atd_decoder* d, int32_t slot, const float* x, int32_t T,
+                               int32_t head, float* y_out, float* logits_out, void* stream) {
+  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
+  const atd_config& c = d->cfg;
+  if (slot < 0 || slot >= c.max_slots)
+    return fail(d, ATD_ERR_INVALID_ARG, "slot %d outside [0, %d)", slot, c.max_slots);
+  if (!d->attached[slot])
+    return fail(d, ATD_ERR_INVALID_ARG, "slot %d has no KV buffers attached", slot);
+  if (!x || !logits_out) return fail(d, ATD_ERR_INVALID_ARG, "x or logits_out is NULL");
+  if (y_out && !aligned16(y_out))
+    return fail(d, ATD_ERR_INVALID_ARG, "y_out %p not 16-byte aligned", (void*)y_out);
+  if (head < 0 || head >= c.n_lm_heads)
+    return fail(d, ATD_ERR_INVALID_ARG, "head %d outside [0, %d)", head, c.n_lm_heads);
+  if (T < 1) return fail(d, ATD_ERR_INVALID_ARG, "T = %d < 1", T);
+  if (T > c.max_rows || T > c.max_ctx)
+    return fail(d, ATD_ERR_CAPACITY, "T = %d beyond max_rows %d / max_ctx %d", T, c.max_rows,
+                c.max_ctx);
+  if (T > d->cap[slot])
+    return fail(d, ATD_ERR_KV_FULL, "T = %d rows exceed slot %d capacity %d", T, slot,
+                d->cap[slot]);
+  if (d->dry) {
+    d->pos[slot] = T;
+    return ATD_OK;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  RowMap rows{kRowsPrefill, slot};
+  EmbedArgs ea = embed_args(d, T, nullptr, 0, nullptr, x, d->x);
+  hipError_t e = launch_embed(ea, c.dtype == ATD_BF16, s);
+  if (e == hipSuccess) e = run_layers(d, rows, T, T, s);
+  if (e == hipSuccess)
+    e = run_head(d, d->x + (size_t)(T - 1) * c.hidden, 1, head, y_out, logits_out, s);
+  if (e == hipSuccess) e = launch_advance(slots_of(d), rows, T, s);
+  if (e != hipSuccess) return hip_fail(d, e, "decoder_prefill");
+  d->pos[slot] = T;
+  return ATD_OK;
+}
+
+extern "C" int decoder_step(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok,
+                            int32_t G, const int32_t* table_ids, const float* extra,
+                            int32_t head, float* y_out, float* logits_out, void* stream) {
+  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
+  const atd_config& c = d->cfg;
+  if (B < 1 || B > c.max_rows)
+    return fail(d, ATD_ERR_CAPACITY, "B = %d outside [1, max_rows %d]", B, c.max_rows);
+  if (slot0 < 0 || slot0 + B > c.max_slots)
+    return fail(d, ATD_ERR_INVALID_ARG, "slots [%d, %d) outside [0, %d)", slot0, slot0 + B,
+                c.max_slots);
+  if (!logits_out) return fail(d, ATD_ERR_INVALID_ARG, "logits_out is NULL");
+  if (y_out && !aligned16(y_out))
+    return fail(d, ATD_ERR_INVALID_ARG, "y_out %p not 16-byte aligned", (void*)y_out);
+  if (head < 0 || head >= c.n_lm_heads)
+    return fail(d, ATD_ERR_INVALID_ARG, "head %d outside [0, %d)", head, c.n_lm_heads);
+  int rc = check_tables(d, G, table_ids, tok, extra);
+  if (rc) return rc;
+  int max_cap = 0;
+  for (int b = 0; b < B; ++b) {
+    const int sl = slot0 + b;
+    if (!d->attached[sl])
+      return fail(d, ATD_ERR_INVALID_ARG, "slot %d has no KV buffers attached", sl);
+    if (d->pos[sl] >= d->cap[sl])
+      return fail(d, ATD_ERR_KV_FULL, "slot %d is full: position %d, capacity %d", sl,
+                  d->pos[sl], d->cap[sl]);
+    if (d->pos[sl] + 1 > c.max_ctx)
+      return fail(d, ATD_ERR_CAPACITY, "slot %d position %d reaches max_ctx %d", sl, d->pos[sl],
+                  c.max_ctx);
+    max_cap = std::max(max_cap, std::min(d->cap[sl], c.max_ctx));
+  }
+  if (d->dry) {
+    for (int b = 0; b < B; ++b) d->pos[slot0 + b] += 1;
+    return ATD_OK;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  RowMap rows{kRowsStep, slot0};
+  EmbedArgs ea = embed_args(d, B, tok, G, table_ids, extra, d->x);
+  hipError_t e = launch_embed(ea, c.dtype == ATD_BF16, s);
+  if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, s);
+  if (e == hipSuccess) e = run_head(d, d->x, B, head, y_out, logits_out, s);
+  if (e == hipSuccess) e = launch_advance(slots_of(d), rows, B, s);
+  if (e != hipSuccess) return hip_fail(d, e, "decoder_step");
+  for (int b = 0; b < B; ++b) d->pos[slot0 + b] += 1;
+  return ATD_OK;
+}
+
+// ---------------------------------------------------------------- argmax
+
+namespace {
+struct ArgmaxScratch {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_argmax_mu;
+std::map<int, ArgmaxScratch> g_argmax_scratch;
+}  // namespace
+
+extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
+                             float penalty, int32_t* tok_out, float* margin_out, void* stream) {
+  if (!logits || !tok_out) return fail(nullptr, ATD_ERR_INVALID_ARG, "logits or tok_out is NULL");
+  if (B < 1) return fail(nullptr, ATD_ERR_INVALID_ARG, "B = %d < 1", B);
+  if (V < 2) return fail(nullptr, ATD_ERR_INVALID_ARG, "V = %d < 2", V);
+  if (!(penalty > 0.0f) || !std::isfinite(penalty))
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "penalty %g is not a positive number",
+                (double)penalty);
+  ArgmaxArgs a{};
+  a.z = logits;
+  a.B = B;
+  a.V = V;
+  a.seen = seen;
+  a.nwords = (V + 31) / 32;
+  a.penalty = penalty;
+  a.tok = tok_out;
+  a.margin = margin_out;
+  a.nblk = (V + kArgmaxChunk - 1) / kArgmaxChunk;
+  const size_t need = (size_t)B * a.nblk * 3 * sizeof(float);
+  {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_argmax_mu);
+    ArgmaxScratch& sc = g_argmax_scratch[dev];
+    if (sc.bytes < need) {
+      if (sc.p) (void)hipFree(sc.p);
+      sc.p = nullptr;
+      sc.bytes = 0;
+      e = hipMalloc(&sc.p, std::max(need, size_t(1) << 16));
+      if (e != hipSuccess) return hip_fail(nullptr, e, "hipMalloc of argmax scratch");
+      sc.bytes = std::max(need, size_t(1) << 16);
+    }
+    a.part = (float*)sc.p;
+  }
+  hipError_t e = launch_argmax(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "greedy_argmax");
+}

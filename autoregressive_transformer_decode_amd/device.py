@@ -1,0 +1,189 @@
+"""Device-memory plumbing around the C ABI (torch allocates, the library
+computes).
+
+``DeviceModel`` uploads generated weights to HBM and builds the
+``atd_weights`` pointer structs; ``Decoder`` owns a decoder handle plus the
+KV buckets it attaches, and forwards each call to the binding with tensor
+data pointers and the current torch stream."""
+
+from __future__ import annotations
+
+import ctypes as C
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .inputs import BF16, ModelShape, ModelWeights
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _to_dev(arr: np.ndarray, device) -> torch.Tensor:
+    if arr.dtype == np.uint16:
+        t = torch.from_numpy(arr.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, np.float32))
+    return t.to(device, non_blocking=False).contiguous()
+
+
+class DeviceModel:
+    """Weights of one stack in HBM.  ``tables`` may be shared with another
+    stack (the Talker and the Code Predictor use the same code embeddings)."""
+
+    def __init__(self, mw: ModelWeights, device="cuda",
+                 tables: Optional[List[torch.Tensor]] = None):
+        s = mw.shape
+        self.shape = s
+        self.keep: List[torch.Tensor] = []
+
+        def up(a):
+            if a is None:
+                return None
+            t = _to_dev(a, device)
+            self.keep.append(t)
+            return t
+
+        self.layers = []
+        for Lw in mw.layers:
+            self.layers.append(dict(
+                attn_norm=up(Lw.attn_norm), wq=up(Lw.wq.storage), wk=up(Lw.wk.storage),
+                wv=up(Lw.wv.storage), bq=up(Lw.bq), bk=up(Lw.bk), bv=up(Lw.bv),
+                q_norm=up(Lw.q_norm), k_norm=up(Lw.k_norm), wo=up(Lw.wo.storage),
+                mlp_norm=up(Lw.mlp_norm), w_gate=up(Lw.w_gate.storage),
+                w_up=up(Lw.w_up.storage), w_down=up(Lw.w_down.storage)))
+        self.final_norm = up(mw.final_norm)
+        self.heads = [up(h.storage) for h in mw.heads]
+        if tables is None:
+            tables = [up(t.storage) for t in mw.tables]
+        else:
+            self.keep.extend(tables)
+        self.tables = tables
+        self.table_vocab = [int(t.shape[0]) for t in tables]
+        self._build_structs()
+
+    def _build_structs(self):
+        n = len(self.layers)
+        self._layers = (B.atd_layer_weights * n)()
+        for i, L in enumerate(self.layers):
+            for k, v in L.items():
+                setattr(self._layers[i], k, v.data_ptr() if v is not None else None)
+        self._heads = (C.c_void_p * len(self.heads))(*[h.data_ptr() for h in self.heads])
+        self._tables = (C.c_void_p * len(self.tables))(*[t.data_ptr() for t in self.tables])
+        self._vocab = (C.c_int32 * len(self.tables))(*self.table_vocab)
+        self.weights = B.atd_weights(
+            layers=C.cast(self._layers, C.POINTER(B.atd_layer_weights)),
+            final_norm=self.final_norm.data_ptr(),
+            lm_heads=C.cast(self._heads, C.POINTER(C.c_void_p)),
+            tables=C.cast(self._tables, C.POINTER(C.c_void_p)),
+            table_vocab=C.cast(self._vocab, C.POINTER(C.c_int32)))
+
+
+def make_config(s: ModelShape, max_slots: int, max_rows: int, max_ctx: int,
+                n_tables: Optional[int] = None) -> B.atd_config:
+    return B.atd_config(
+        n_layers=s.n_layers, hidden=s.hidden, n_q_heads=s.n_q_heads, n_kv_heads=s.n_kv_heads,
+        head_dim=s.head_dim, ffn=s.ffn, vocab=s.vocab, n_lm_heads=s.n_lm_heads,
+        n_tables=n_tables if n_tables is not None else len(s.table_vocabs),
+        qk_norm=int(s.qk_norm), qkv_bias=int(s.qkv_bias),
+        dtype=B.ATD_BF16 if s.dtype == BF16 else B.ATD_F32,
+        rope_theta=s.rope_theta, rms_eps=s.rms_eps,
+        max_slots=max_slots, max_rows=max_rows, max_ctx=max_ctx)
+
+
+class Decoder:
+    """A decoder handle plus the KV buckets it holds for each slot."""
+
+    def __init__(self, model: DeviceModel, max_slots: int = 1, max_rows: int = 1,
+                 max_ctx: int = 4096):
+        self.model = model
+        s = model.shape
+        self.shape = s
+        self.cfg = make_config(s, max_slots, max_rows, max_ctx)
+        self.handle = B.decoder_create(self.cfg, model.weights)
+        self.kv = {}   # slot -> (list of K tensors, list of V tensors)
+        self.kv_dtype = torch.bfloat16 if s.dtype == BF16 else torch.float32
+
+    def close(self):
+        if self.handle:
+            B.decoder_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- KV buckets
+    def alloc_kv(self, capacity: int, device="cuda"):
+        s = self.shape
+        shp = (s.n_kv_heads, capacity, s.head_dim)
+        ks = [torch.zeros(shp, dtype=self.kv_dtype, device=device) for _ in range(s.n_layers)]
+        vs = [torch.zeros(shp, dtype=self.kv_dtype, device=device) for _ in range(s.n_layers)]
+        return ks, vs
+
+    def grow(self, slot: int, capacity: int, kv=None):
+        """Attach a new bucket (allocated here unless given); the old one is
+        dropped after the stream passes the copy."""
+        ks, vs = kv if kv is not None else self.alloc_kv(capacity)
+        B.kv_bucket_grow(self.handle, slot, [k.data_ptr() for k in ks],
+                         [v.data_ptr() for v in vs], capacity, _stream())
+        old = self.kv.get(slot)
+        self.kv[slot] = (ks, vs)
+        if old is not None:
+            torch.cuda.current_stream().synchronize()
+        return ks, vs
+
+    def position(self, slot: int = 0):
+        return B.decoder_get_position(self.handle, slot)
+
+    def set_position(self, slot: int, pos: int):
+        B.decoder_set_position(self.handle, slot, pos, _stream())
+
+    # -- compute
+    def prefill(self, x: torch.Tensor, slot: int = 0, head: int = 0,
+                y_out: Optional[torch.Tensor] = None, logits_out: Optional[torch.Tensor] = None):
+        T = int(x.shape[0])
+        if logits_out is None:
+            logits_out = torch.empty(self.shape.vocab, device=x.device, dtype=torch.float32)
+        B.decoder_prefill(self.handle, slot, x.data_ptr(), T, head,
+                          y_out.data_ptr() if y_out is not None else None,
+                          logits_out.data_ptr(), _stream())
+        return y_out, logits_out
+
+    def step(self, tok: Optional[torch.Tensor], table_ids: Sequence[int], slot0: int = 0,
+             nrows: int = 1, extra: Optional[torch.Tensor] = None, head: int = 0,
+             y_out: Optional[torch.Tensor] = None, logits_out: Optional[torch.Tensor] = None):
+        G = len(table_ids)
+        if logits_out is None:
+            logits_out = torch.empty(nrows, self.shape.vocab, device="cuda", dtype=torch.float32)
+        B.decoder_step(self.handle, slot0, nrows, tok.data_ptr() if tok is not None else None, G,
+                       table_ids, extra.data_ptr() if extra is not None else None, head,
+                       y_out.data_ptr() if y_out is not None else None, logits_out.data_ptr(),
+                       _stream())
+        return y_out, logits_out
+
+    def embed(self, tok: Optional[torch.Tensor], table_ids: Sequence[int], x_out: torch.Tensor,
+              nrows: int = 1, extra: Optional[torch.Tensor] = None):
+        B.decoder_embed(self.handle, nrows, tok.data_ptr() if tok is not None else None,
+                        len(table_ids), table_ids,
+                        extra.data_ptr() if extra is not None else None, x_out.data_ptr(),
+                        _stream())
+        return x_out
+
+
+def greedy_argmax(logits: torch.Tensor, seen: Optional[torch.Tensor], penalty: float,
+                  tok_out: torch.Tensor, margin_out: Optional[torch.Tensor] = None):
+    Bn, V = (1, logits.shape[0]) if logits.dim() == 1 else logits.shape
+    B.greedy_argmax(logits.data_ptr(), Bn, V, seen.data_ptr() if seen is not None else None,
+                    float(penalty), tok_out.data_ptr(),
+                    margin_out.data_ptr() if margin_out is not None else None, _stream())
+    return tok_out
+
+
+def seen_words(vocab: int) -> int:
+    return (vocab + 31) // 32

@@ -1,0 +1,221 @@
+/*
+ * atd.h -- C ABI of the MI355X (gfx950) decode-step library.
+ *
+ * The library runs the autoregressive decode step of a Qwen-style decoder
+ * stack on one GPU: input embedding sum, per layer RMSNorm + q/k/v
+ * projection, per-head QK RMSNorm + RoPE + KV-cache append, causal GQA
+ * attention over the cache, output projection + residual, RMSNorm + SwiGLU
+ * MLP + residual, then the final RMSNorm and an LM head; plus penalized
+ * greedy argmax and KV bucket growth.
+ *
+ * Sources (page title, section):
+ *  - "Qwen3-TTS ncnn port" (ncnn discussion 6799), "Talker: non-standard
+ *    structure and two-level generation": QK RMSNorm over head_dim after
+ *    the q/k projections, 8 KV heads shared by 16 query heads, interleaved
+ *    mRoPE equal to plain RoPE for TTS, the frame loop, repetition penalty.
+ *  - "Audio8-ASR dynamic KV-cache bucket" (RK3576 acceptance report),
+ *    "dynamic window mechanism": external [heads, Smax, head_dim] cache
+ *    owned and written by the host side, growth by copying the valid region
+ *    to a larger buffer and continuing at the same token and RoPE position,
+ *    no sliding window.
+ *  - "qwen3-tts-hip OPTIMIZATION_LOG", DecodeStepStack profile entry (the
+ *    per-layer sequence of operations) and the repetition-penalty entry.
+ *  - "NEON library" maintainers page, "Contracts": input storage stays valid
+ *    during a call, outputs belong to the caller, validation happens before
+ *    any work starts and leaves the object reusable, one object is used
+ *    serially.
+ *
+ * Conventions for every entry point:
+ *  - Pointers documented as "device" are HIP device memory of the current
+ *    device, owned by the caller; "host" pointers are read during the call
+ *    only.  Weights and KV buffers must stay allocated while a decoder that
+ *    references them is in use.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously on it; outputs are valid once the stream reaches that
+ *    point.  Results never depend on the stream.
+ *  - Every argument is checked on the host before anything is enqueued.  On
+ *    any error other than ATD_ERR_DEVICE nothing was enqueued and the decoder
+ *    is unchanged and reusable.  decoder_last_error() names the refused
+ *    argument and its value.  There is no fallback path: an unsupported
+ *    configuration is an error.
+ *  - All floating-point activations, hidden states, logits and biases are
+ *    float32.  Weights, embedding tables and the KV cache are stored in the
+ *    configured dtype (float32 or bf16); arithmetic accumulates in float32.
+ *  - A decoder is used from one host thread at a time.
+ */
+#ifndef ATD_H
+#define ATD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  ATD_OK = 0,
+  ATD_ERR_INVALID_ARG = -1, /* null/misaligned pointer, value out of range   */
+  ATD_ERR_SHAPE = -2,       /* sizes inconsistent with the config           */
+  ATD_ERR_DTYPE = -3,       /* unknown storage dtype                        */
+  ATD_ERR_KV_FULL = -4,     /* the write position reached the KV capacity   */
+  ATD_ERR_CAPACITY = -5,    /* beyond max_rows / max_slots / max_ctx, or a
+                               bucket too small for the valid rows           */
+  ATD_ERR_DEVICE = -6,      /* a HIP call failed (message names the error)  */
+  ATD_ERR_UNSUPPORTED = -7  /* config outside what the kernels implement    */
+};
+
+/* Storage dtypes of weights, embedding tables and the KV cache. */
+enum { ATD_F32 = 0, ATD_BF16 = 1 };
+
+/* Shape of one decoder stack (hyper-parameters; host struct). */
+typedef struct atd_config {
+  int32_t n_layers;    /* L >= 1                                             */
+  int32_t hidden;      /* h, multiple of 8, <= 8192                          */
+  int32_t n_q_heads;   /* Hq                                                 */
+  int32_t n_kv_heads;  /* Hkv; Hq / Hkv in {1, 2, 4, 8}                      */
+  int32_t head_dim;    /* D in {64, 128}                                     */
+  int32_t ffn;         /* F, multiple of 8, <= 8192                          */
+  int32_t vocab;       /* V of every LM head, >= 2                           */
+  int32_t n_lm_heads;  /* number of LM heads (15 for the code predictor)     */
+  int32_t n_tables;    /* number of embedding tables, 1..16                  */
+  int32_t qk_norm;     /* 1: per-head RMSNorm of q and k before RoPE         */
+  int32_t qkv_bias;    /* 1: q/k/v projections carry a bias                  */
+  int32_t dtype;       /* ATD_F32 or ATD_BF16                                */
+  double rope_theta;   /* RoPE base (1e6 for the Qwen3 Talker)               */
+  float rms_eps;       /* epsilon of every RMSNorm                           */
+  int32_t max_slots;   /* independent streams (KV caches) the decoder keeps  */
+  int32_t max_rows;    /* largest B of a step / T of a prefill               */
+  int32_t max_ctx;     /* largest number of cached rows any slot reaches     */
+  int32_t flags;       /* ATD_FLAG_* bits                                    */
+} atd_config;
+
+/* atd_config.flags: ATD_FLAG_DRY_RUN makes a host-only decoder: every
+ * argument check runs and the host state (slot positions, capacities,
+ * attached buffers) advances as usual, but no HIP call is made and no
+ * device memory is touched.  For validating a decode schedule without a
+ * GPU. */
+#define ATD_FLAG_DRY_RUN 1
+
+/* Device pointers of one layer.  Matrices are row-major [out, in] in the
+ * config dtype; gains and biases are float32. */
+typedef struct atd_layer_weights {
+  const void* attn_norm; /* [h]            input RMSNorm gain               */
+  const void* wq;        /* [Hq*D, h]                                       */
+  const void* wk;        /* [Hkv*D, h]                                      */
+  const void* wv;        /* [Hkv*D, h]                                      */
+  const void* bq;        /* [Hq*D]  or NULL when qkv_bias == 0               */
+  const void* bk;        /* [Hkv*D] or NULL                                  */
+  const void* bv;        /* [Hkv*D] or NULL                                  */
+  const void* q_norm;    /* [D] QK-norm gain of q, or NULL when qk_norm == 0 */
+  const void* k_norm;    /* [D] QK-norm gain of k, or NULL                   */
+  const void* wo;        /* [h, Hq*D]                                       */
+  const void* mlp_norm;  /* [h]            post-attention RMSNorm gain      */
+  const void* w_gate;    /* [F, h]                                          */
+  const void* w_up;      /* [F, h]                                          */
+  const void* w_down;    /* [h, F]                                          */
+} atd_layer_weights;
+
+/* All weights of a stack.  The arrays are host arrays of device pointers;
+ * they are copied during decoder_create. */
+typedef struct atd_weights {
+  const atd_layer_weights* layers; /* host [n_layers]                        */
+  const void* final_norm;          /* device [h] float32                     */
+  const void* const* lm_heads;     /* host [n_lm_heads] -> device [V, h]     */
+  const void* const* tables;       /* host [n_tables] -> device [V_g, h]     */
+  const int32_t* table_vocab;      /* host [n_tables]: V_g of each table     */
+} atd_weights;
+
+typedef struct atd_decoder atd_decoder;
+
+/* Create a decoder.  Validates cfg and w (all device pointers non-NULL where
+ * required, 16-byte aligned), then allocates its device scratch (residual
+ * stream, projections, attention partials, RoPE table, slot tables) sized by
+ * max_rows, max_slots and max_ctx.  Slots start with no KV buffers attached
+ * (attach them with kv_bucket_grow).  *out is set only on ATD_OK.
+ * Errors: INVALID_ARG, SHAPE, DTYPE, UNSUPPORTED, DEVICE. */
+int decoder_create(const atd_config* cfg, const atd_weights* w, atd_decoder** out);
+
+/* Release the decoder and its scratch (the caller's weights and KV buffers
+ * are untouched).  Waits for work still queued that uses the scratch.
+ * NULL is accepted. */
+int decoder_destroy(atd_decoder* dec);
+
+/* Message of the last error on this decoder, or of the last failed
+ * decoder_create / greedy_argmax call in this thread when dec is NULL.
+ * Valid until the next failing call. */
+const char* decoder_last_error(const atd_decoder* dec);
+
+/* Attach KV buffers of capacity s_new rows to `slot` (Audio8-ASR report,
+ * dynamic window mechanism).  k_new / v_new: host arrays [n_layers] of
+ * device pointers, each [Hkv, s_new, D] in the config dtype, 16-byte
+ * aligned.  When the slot already holds buffers, the valid rows
+ * [:, :pos, :] of every layer are copied into the new ones on `stream`; the
+ * position is kept, so decoding continues at the same token and RoPE
+ * position.  The old buffers are the caller's to free once the stream has
+ * passed this call.  With no buffers attached yet this is the first attach
+ * (position 0).  Errors: INVALID_ARG, CAPACITY (s_new <= pos or
+ * s_new > max_ctx), DEVICE. */
+int kv_bucket_grow(atd_decoder* dec, int32_t slot, void* const* k_new,
+                   void* const* v_new, int32_t s_new, void* stream);
+
+/* Set the number of valid cached rows of `slot` (0 <= pos <= capacity), for
+ * caches filled by the caller or resumed from saved buffers.  Enqueued on
+ * `stream`.  Errors: INVALID_ARG, CAPACITY, DEVICE. */
+int decoder_set_position(atd_decoder* dec, int32_t slot, int32_t pos, void* stream);
+
+/* Host copy of the position and capacity of `slot` (no device access). */
+int decoder_get_position(const atd_decoder* dec, int32_t slot, int32_t* pos,
+                         int32_t* capacity);
+
+/* Prefill: reset `slot` to position 0 and run the T rows of x (device
+ * [T, h] float32) at positions 0..T-1 through the stack, each row attending
+ * to the rows before it and itself.  Writes KV rows 0..T-1 and leaves the
+ * position at T.  Outputs of the last row: y_out (device [h] float32, the
+ * final-norm hidden state; may be NULL) and logits_out (device [V]
+ * float32) of LM head `head`.  Errors: INVALID_ARG, KV_FULL (T > capacity),
+ * CAPACITY (T > max_rows or T > max_ctx), DEVICE. */
+int decoder_prefill(atd_decoder* dec, int32_t slot, const float* x, int32_t T,
+                    int32_t head, float* y_out, float* logits_out, void* stream);
+
+/* One decode step of B streams, slots slot0 .. slot0+B-1, each at its own
+ * position p.  Input row b = sum over g < G of
+ * tables[table_ids[g]][tok[b*G + g]] + extra[b] (extra: device [B, h]
+ * float32 or NULL; G may be 0 when extra is given).  tok: device int32
+ * [B, G]; ids outside [0, V_g) are clamped into range.  table_ids: host
+ * [G].  Writes each slot's KV row p, advances its position by one, and
+ * writes y_out (device [B, h] or NULL) and logits_out (device [B, V]) of
+ * LM head `head`.  Positions are mirrored on the host, so a full cache is
+ * refused before any work: ATD_ERR_KV_FULL, and the caller grows the bucket
+ * and retries.  Errors: INVALID_ARG, KV_FULL, CAPACITY, DEVICE. */
+int decoder_step(atd_decoder* dec, int32_t slot0, int32_t B, const int32_t* tok,
+                 int32_t G, const int32_t* table_ids, const float* extra,
+                 int32_t head, float* y_out, float* logits_out, void* stream);
+
+/* The input-embedding part of decoder_step alone: x_out (device [B, h]
+ * float32) = sum_g tables[table_ids[g]][tok[b*G+g]] + extra[b].  Used to
+ * build prefill rows from device-resident tokens.  Errors: INVALID_ARG,
+ * CAPACITY, DEVICE. */
+int decoder_embed(atd_decoder* dec, int32_t B, const int32_t* tok, int32_t G,
+                  const int32_t* table_ids, const float* extra, float* x_out,
+                  void* stream);
+
+/* Greedy token with repetition penalty (qwen3-tts-hip log, penalty entry;
+ * ncnn port, Talker section).  For each row b of logits (device [B, V]
+ * float32): logits of tokens whose bit is set in seen (device uint32
+ * [B, ceil(V/32)], bit t of row b = word t/32, bit t%32; may be NULL) are
+ * divided by `penalty` when positive and multiplied by it otherwise; the
+ * token is the lowest index of the maximum; margin = best - second best
+ * (0 on a tie).  Writes tok_out (device int32 [B]) and margin_out (device
+ * float32 [B] or NULL) and sets the chosen token's bit in seen.  The logits
+ * are not modified.  Uses a device scratch buffer that the library keeps
+ * per device (allocated on first use).  Errors: INVALID_ARG, DEVICE. */
+int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
+                  float penalty, int32_t* tok_out, float* margin_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATD_H */

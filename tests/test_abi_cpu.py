@@ -1,0 +1,214 @@
+"""C-ABI tests that need no GPU: the library loads, exports every entry point
+declared in include/atd.h, and the host validation layer refuses bad
+arguments with the documented status codes (dry-run decoders never touch
+HIP)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from autoregressive_transformer_decode_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "atd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", src, flags=re.M)
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(B.lib, n), n
+
+
+def _cfg(**kw):
+    base = dict(n_layers=2, hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=128,
+                vocab=100, n_lm_heads=2, n_tables=2, qk_norm=1, qkv_bias=0, dtype=B.ATD_BF16,
+                rope_theta=1e6, rms_eps=1e-6, max_slots=4, max_rows=8, max_ctx=64,
+                flags=B.ATD_FLAG_DRY_RUN)
+    base.update(kw)
+    return B.atd_config(**base)
+
+
+class FakeWeights:
+    """Aligned, never-dereferenced pointer values for dry-run decoders."""
+
+    def __init__(self, cfg, bias=False, qk=True, misalign=None):
+        self.next = 0x10000
+        self.layers = (B.atd_layer_weights * cfg.n_layers)()
+        for l in range(cfg.n_layers):
+            for f in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up",
+                      "w_down"):
+                setattr(self.layers[l], f, self._p())
+            if bias:
+                for f in ("bq", "bk", "bv"):
+                    setattr(self.layers[l], f, self._p())
+            if qk:
+                for f in ("q_norm", "k_norm"):
+                    setattr(self.layers[l], f, self._p())
+        if misalign:
+            setattr(self.layers[0], misalign, getattr(self.layers[0], misalign) + 4)
+        self.heads = (C.c_void_p * cfg.n_lm_heads)(*[self._p() for _ in range(cfg.n_lm_heads)])
+        self.tables = (C.c_void_p * cfg.n_tables)(*[self._p() for _ in range(cfg.n_tables)])
+        self.vocab = (C.c_int32 * cfg.n_tables)(*([100] * cfg.n_tables))
+        self.w = B.atd_weights(layers=C.cast(self.layers, C.POINTER(B.atd_layer_weights)),
+                               final_norm=self._p(),
+                               lm_heads=C.cast(self.heads, C.POINTER(C.c_void_p)),
+                               tables=C.cast(self.tables, C.POINTER(C.c_void_p)),
+                               table_vocab=C.cast(self.vocab, C.POINTER(C.c_int32)))
+
+    def _p(self):
+        self.next += 0x1000
+        return self.next
+
+
+def _create(cfg, fw=None):
+    fw = fw or FakeWeights(cfg, bias=bool(cfg.qkv_bias), qk=bool(cfg.qk_norm))
+    return B.decoder_create(cfg, fw.w), fw
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(head_dim=96), B.ATD_ERR_UNSUPPORTED, "head_dim 96"),
+    (dict(dtype=7), B.ATD_ERR_DTYPE, "dtype 7"),
+    (dict(n_q_heads=6, n_kv_heads=4), B.ATD_ERR_SHAPE, "n_q_heads 6"),
+    (dict(n_q_heads=6, n_kv_heads=2), B.ATD_ERR_UNSUPPORTED, "= 3"),
+    (dict(hidden=60), B.ATD_ERR_UNSUPPORTED, "hidden 60"),
+    (dict(ffn=16384), B.ATD_ERR_UNSUPPORTED, "ffn 16384"),
+    (dict(vocab=1), B.ATD_ERR_SHAPE, "vocab 1"),
+    (dict(n_tables=17), B.ATD_ERR_UNSUPPORTED, "n_tables 17"),
+    (dict(max_rows=0), B.ATD_ERR_CAPACITY, "max_rows 0"),
+    (dict(rope_theta=-1.0), B.ATD_ERR_INVALID_ARG, "rope_theta"),
+    (dict(flags=8), B.ATD_ERR_INVALID_ARG, "flags"),
+])
+def test_create_rejects_config(kw, code, needle):
+    cfg = _cfg(**kw)
+    fw = FakeWeights(_cfg())
+    with pytest.raises(B.AtdError) as ei:
+        B.decoder_create(cfg, fw.w)
+    assert ei.value.code == code
+    assert needle in str(ei.value)
+
+
+def test_create_rejects_weights():
+    cfg = _cfg()
+    with pytest.raises(B.AtdError) as ei:
+        B.decoder_create(cfg, FakeWeights(cfg, misalign="wk").w)
+    assert ei.value.code == B.ATD_ERR_INVALID_ARG and "layers[0].wk" in str(ei.value)
+    fw = FakeWeights(cfg)
+    fw.layers[1].w_up = None
+    with pytest.raises(B.AtdError) as ei:
+        B.decoder_create(cfg, fw.w)
+    assert "layers[1].w_up is NULL" in str(ei.value)
+    with pytest.raises(B.AtdError) as ei:     # bias given without qkv_bias
+        B.decoder_create(cfg, FakeWeights(cfg, bias=True).w)
+    assert "qkv_bias = 0" in str(ei.value)
+    with pytest.raises(B.AtdError) as ei:     # qk-norm gains required
+        B.decoder_create(cfg, FakeWeights(cfg, qk=False).w)
+    assert "q_norm is NULL" in str(ei.value)
+
+
+def test_dry_run_schedule_and_kv_full():
+    cfg = _cfg()
+    h, fw = _create(cfg)
+    try:
+        kv = [0x900000 + 0x1000 * i for i in range(cfg.n_layers)]
+        vv = [0xA00000 + 0x1000 * i for i in range(cfg.n_layers)]
+        # nothing attached yet
+        with pytest.raises(B.AtdError) as ei:
+            B.decoder_prefill(h, 0, 0x5000, 4, 0, None, 0x6000, 0)
+        assert "no KV buffers" in str(ei.value)
+        B.kv_bucket_grow(h, 0, kv, vv, 4, 0)
+        assert B.decoder_get_position(h, 0) == (0, 4)
+        with pytest.raises(B.AtdError) as ei:
+            B.decoder_prefill(h, 0, 0x5000, 5, 0, None, 0x6000, 0)
+        assert ei.value.code == B.ATD_ERR_KV_FULL
+        B.decoder_prefill(h, 0, 0x5000, 3, 1, None, 0x6000, 0)
+        assert B.decoder_get_position(h, 0) == (3, 4)
+        B.decoder_step(h, 0, 1, 0x7000, 1, [0], None, 0, None, 0x6000, 0)
+        assert B.decoder_get_position(h, 0) == (4, 4)
+        with pytest.raises(B.AtdError) as ei:       # position == capacity
+            B.decoder_step(h, 0, 1, 0x7000, 1, [0], None, 0, None, 0x6000, 0)
+        assert ei.value.code == B.ATD_ERR_KV_FULL and "position 4, capacity 4" in str(ei.value)
+        assert B.decoder_get_position(h, 0) == (4, 4)   # refused call changed nothing
+        with pytest.raises(B.AtdError) as ei:       # bucket must exceed the valid rows
+            B.kv_bucket_grow(h, 0, [p + 0x400000 for p in kv], [p + 0x400000 for p in vv], 4, 0)
+        assert ei.value.code == B.ATD_ERR_CAPACITY
+        with pytest.raises(B.AtdError) as ei:       # aliasing the buffers in use
+            B.kv_bucket_grow(h, 0, kv, [p + 0x400000 for p in vv], 8, 0)
+        assert "aliases" in str(ei.value)
+        B.kv_bucket_grow(h, 0, [p + 0x400000 for p in kv], [p + 0x400000 for p in vv], 8, 0)
+        assert B.decoder_get_position(h, 0) == (4, 8)   # same position after growth
+        B.decoder_step(h, 0, 1, 0x7000, 1, [0], None, 0, None, 0x6000, 0)
+        assert B.decoder_get_position(h, 0) == (5, 8)
+        with pytest.raises(B.AtdError) as ei:
+            B.kv_bucket_grow(h, 0, kv, vv, 65, 0)   # beyond max_ctx
+        assert ei.value.code == B.ATD_ERR_CAPACITY
+    finally:
+        B.decoder_destroy(h)
+
+
+def test_dry_run_step_argument_checks():
+    cfg = _cfg()
+    h, fw = _create(cfg)
+    try:
+        for s in range(2):
+            B.kv_bucket_grow(h, s, [0x900000 + 0x1000 * (i + 8 * s) for i in range(2)],
+                             [0xA00000 + 0x1000 * (i + 8 * s) for i in range(2)], 16, 0)
+        cases = [
+            (dict(B=9), B.ATD_ERR_CAPACITY, "max_rows 8"),
+            (dict(slot0=3, B=2), B.ATD_ERR_INVALID_ARG, "slots [3, 5)"),
+            (dict(B=3), B.ATD_ERR_INVALID_ARG, "slot 2 has no KV"),
+            (dict(head=2), B.ATD_ERR_INVALID_ARG, "head 2"),
+            (dict(table_ids=[2]), B.ATD_ERR_INVALID_ARG, "table_ids[0] = 2"),
+            (dict(G=0, table_ids=[]), B.ATD_ERR_INVALID_ARG, "G = 0 needs extra"),
+            (dict(logits=None), B.ATD_ERR_INVALID_ARG, "logits_out is NULL"),
+            (dict(y=0x6004), B.ATD_ERR_INVALID_ARG, "not 16-byte aligned"),
+        ]
+        for kw, code, needle in cases:
+            a = dict(slot0=0, B=1, tok=0x7000, G=1, table_ids=[0], extra=None, head=0, y=None,
+                     logits=0x6000)
+            a.update(kw)
+            with pytest.raises(B.AtdError) as ei:
+                B.decoder_step(h, a["slot0"], a["B"], a["tok"], a["G"], a["table_ids"],
+                               a["extra"], a["head"], a["y"], a["logits"], 0)
+            assert ei.value.code == code, (kw, ei.value)
+            assert needle in str(ei.value), (kw, str(ei.value))
+        assert B.decoder_get_position(h, 0) == (0, 16)
+        B.decoder_step(h, 0, 2, 0x7000, 2, [0, 1], 0x8000, 1, 0x6000, 0x6000, 0)
+        assert B.decoder_get_position(h, 1) == (1, 16)
+        B.decoder_set_position(h, 1, 16, 0)
+        with pytest.raises(B.AtdError) as ei:
+            B.decoder_step(h, 0, 2, 0x7000, 1, [0], None, 0, None, 0x6000, 0)
+        assert ei.value.code == B.ATD_ERR_KV_FULL and "slot 1" in str(ei.value)
+        with pytest.raises(B.AtdError):
+            B.decoder_set_position(h, 1, 17, 0)
+    finally:
+        B.decoder_destroy(h)
+
+
+def test_greedy_argmax_argument_checks():
+    for args, needle in [((0, 1, 10, None, 1.0, 0x100, None, 0), "NULL"),
+                         ((0x100, 0, 10, None, 1.0, 0x100, None, 0), "B = 0"),
+                         ((0x100, 1, 1, None, 1.0, 0x100, None, 0), "V = 1"),
+                         ((0x100, 1, 10, None, 0.0, 0x100, None, 0), "penalty"),
+                         ((0x100, 1, 10, None, float("nan"), 0x100, None, 0), "penalty")]:
+        with pytest.raises(B.AtdError) as ei:
+            B.greedy_argmax(*args)
+        assert ei.value.code == B.ATD_ERR_INVALID_ARG and needle in str(ei.value)
+
+
+def test_create_without_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    cfg = _cfg(flags=0)
+    fw = FakeWeights(cfg)
+    with pytest.raises(B.AtdError) as ei:
+        B.decoder_create(cfg, fw.w)
+    assert ei.value.code == B.ATD_ERR_DEVICE

@@ -1,0 +1,130 @@
+"""Talker workloads on the GPU against the oracle (full model sizes, sampled
+frames / steps; oracle in float32 for time)."""
+
+import numpy as np
+import pytest
+import torch
+
+from autoregressive_transformer_decode_amd import device as dv
+from autoregressive_transformer_decode_amd import inputs
+from oracle import decoder as od
+from tests._models import normwise_rel, oracle_from_weights
+from tests.gpu_util import MARGIN, TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _set_bits(seen_t, toks):
+    seen_t.zero_()
+    for t in toks:
+        seen_t[0, t // 32] |= (1 << (t % 32)) if t % 32 < 31 else -(1 << 31)
+
+
+def test_talker06_frames_teacher_forced():
+    """0.6B Talker + 5-layer Code Predictor: 64-row prefill, then frames of
+    one Code Predictor pass (2-row prefill + 14 steps, head j for group j)
+    and one Talker step (16 code embeddings + text embedding, penalty 1.05).
+    Every pass is fed the oracle's codes and compared."""
+    wl = inputs.WORKLOADS["talker0.6b"]
+    n_frames = 6
+    tmw = inputs.make_weights(wl.model, seed=0)
+    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables)
+    X0 = inputs.prefill_embeddings(wl, seed=0)
+    text = inputs.text_embeddings(wl, seed=0)
+    ot = oracle_from_weights(tmw, np.float32)
+    oc = oracle_from_weights(cmw, np.float32)
+    frames, _ = od.run_talker(ot, oc, X0, text, n_frames, wl.s_init, rho=wl.penalty,
+                              cp_capacity=inputs.CP_CAPACITY)
+
+    tdm = dv.DeviceModel(tmw)
+    cdm = dv.DeviceModel(cmw, tables=tdm.tables)
+    tdec = dv.Decoder(tdm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_init)
+    cdec = dv.Decoder(cdm, max_slots=1, max_rows=2, max_ctx=inputs.CP_CAPACITY)
+    tdec.grow(0, wl.s_init)
+    cdec.grow(0, inputs.CP_CAPACITY)
+    h = wl.model.hidden
+    cp_x = torch.empty(2, h, device="cuda")
+    zt = torch.empty(1, wl.model.vocab, device="cuda")
+    zc = torch.empty(1, wl.cp.vocab, device="cuda")
+    yc = torch.empty(1, h, device="cuda")
+    codes = torch.zeros(1, 16, dtype=torch.int32, device="cuda")
+    gt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    seen = torch.zeros(1, dv.seen_words(wl.model.vocab), dtype=torch.int32, device="cuda")
+    text_d = torch.from_numpy(text).cuda()
+    worst = 0.0
+    tdec.prefill(torch.from_numpy(X0).cuda(), y_out=cp_x[0], logits_out=zt[0])
+    for f in range(n_frames):
+        fr = frames[f]
+        # Talker output of this frame (prefill for f = 0, step otherwise)
+        dv.greedy_argmax(zt[0], seen, wl.penalty, gt)
+        torch.cuda.synchronize()
+        e = max(normwise_rel(cp_x[0].cpu().numpy(), fr["y"]), normwise_rel(zt[0].cpu().numpy(), fr["z"]))
+        worst = max(worst, e)
+        assert e <= TOL, (f, "talker", e)
+        if fr["margin"] > MARGIN:
+            assert int(gt.item()) == fr["c0"], (f, int(gt.item()), fr["c0"])
+        codes[0, 0] = fr["c0"]
+        # Code Predictor pass
+        cdec.embed(codes[:, 0:1], [0], cp_x[1:2])
+        cdec.prefill(cp_x, head=0, y_out=yc[0], logits_out=zc[0])
+        for j in range(15):
+            if j > 0:
+                codes[0, j] = fr["codes"][j - 1]
+                cdec.step(codes[:, j:j + 1], [j], head=j, y_out=yc, logits_out=zc)
+            dv.greedy_argmax(zc[0], None, 1.0, gt)
+            torch.cuda.synchronize()
+            yr, zr, mr = fr["cp"][j]
+            e = max(normwise_rel(yc[0].cpu().numpy(), yr), normwise_rel(zc[0].cpu().numpy(), zr))
+            worst = max(worst, e)
+            assert e <= TOL, (f, "cp", j, e)
+            if mr > MARGIN:
+                assert int(gt.item()) == fr["codes"][j], (f, j)
+        codes[0, 15] = fr["codes"][14]
+        if f == n_frames - 1:
+            break
+        _set_bits(seen, [frames[g]["c0"] for g in range(f + 1)])
+        tdec.step(codes, list(range(16)), extra=text_d[f + 1:f + 2], y_out=cp_x[0:1],
+                  logits_out=zt)
+    print(f"talker0.6b: {n_frames} frames, worst {worst:.2e}", flush=True)
+    tdec.close()
+    cdec.close()
+
+
+def test_talker17_prefill_and_steps():
+    """1.7B Talker shape: 512-row prefill then teacher-forced steps; at the
+    end the context is pushed to 2048 rows (the full workload length) and the
+    last step is checked for determinism and normalisation."""
+    wl = inputs.WORKLOADS["talker1.7b"]
+    mw = inputs.make_weights(wl.model, seed=0)
+    X0 = inputs.prefill_embeddings(wl, seed=0)
+    om = oracle_from_weights(mw, np.float32)
+    n_check = 4
+    ref, _ = od.run_lm(om, X0, n_check, wl.s_init)
+    dm = dv.DeviceModel(mw)
+    dec = dv.Decoder(dm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max)
+    dec.grow(0, wl.s_init)
+    y = torch.empty(1, wl.model.hidden, device="cuda")
+    z = torch.empty(1, wl.model.vocab, device="cuda")
+    dec.prefill(torch.from_numpy(X0).cuda(), y_out=y[0], logits_out=z[0])
+    tok = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    worst = 0.0
+    for k in range(n_check + 1):
+        if k:
+            tok.fill_(ref[k - 1][2])
+            dec.step(tok, [0], y_out=y, logits_out=z)
+        torch.cuda.synchronize()
+        e = max(normwise_rel(y[0].cpu().numpy(), ref[k][0]), normwise_rel(z[0].cpu().numpy(), ref[k][1]))
+        worst = max(worst, e)
+        assert e <= TOL, (k, e)
+    print(f"talker1.7b: {n_check} steps after prefill 512, worst {worst:.2e}", flush=True)
+    # run on to context 2048 feeding the GPU's own argmax
+    gt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    while dec.position(0)[0] < wl.s_max - 1:
+        dv.greedy_argmax(z[0], None, 1.0, gt)
+        dec.step(gt.view(1, 1), [0], y_out=y, logits_out=z)
+    torch.cuda.synchronize()
+    assert dec.position(0) == (wl.s_max - 1, wl.s_max)
+    yv = y[0].cpu().numpy()
+    assert np.isfinite(z.cpu().numpy()).all()
+    assert abs(np.sqrt(np.mean(yv.astype(np.float64) ** 2)) - 1.0) < 1e-3   # unit gains
+    dec.close()

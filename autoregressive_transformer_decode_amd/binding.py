@@ -29,7 +29,11 @@ STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FU
 
 EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
-           "decoder_step", "decoder_embed", "greedy_argmax")
+           "decoder_step", "decoder_embed", "greedy_argmax", "decoder_generate",
+           "decoder_profile_stage", "decoder_profile_result")
+
+ATD_STAGE_QKV, ATD_STAGE_ROPE, ATD_STAGE_ATTN, ATD_STAGE_OPROJ, ATD_STAGE_GATEUP, \
+    ATD_STAGE_DOWN, ATD_STAGE_HEAD = range(7)
 
 
 class AtdError(RuntimeError):
@@ -43,6 +47,7 @@ class atd_config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
                 ("vocab", C.c_int32), ("n_lm_heads", C.c_int32), ("n_tables", C.c_int32),
                 ("qk_norm", C.c_int32), ("qkv_bias", C.c_int32), ("dtype", C.c_int32),
+                ("kv_dtype", C.c_int32),
                 ("rope_theta", C.c_double), ("rms_eps", C.c_float),
                 ("max_slots", C.c_int32), ("max_rows", C.c_int32), ("max_ctx", C.c_int32),
                 ("flags", C.c_int32)]
@@ -78,6 +83,10 @@ def _load():
         "decoder_step": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, vp, vp], C.c_int),
         "decoder_embed": ([vp, i32, vp, i32, C.POINTER(i32), vp, vp, vp], C.c_int),
         "greedy_argmax": ([vp, i32, i32, vp, f32, vp, vp, vp], C.c_int),
+        "decoder_generate": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, f32, vp, vp,
+                              vp, vp], C.c_int),
+        "decoder_profile_stage": ([vp, i32, i32], C.c_int),
+        "decoder_profile_result": ([vp, C.POINTER(C.c_double), C.POINTER(C.c_int64)], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -156,3 +165,21 @@ def decoder_embed(handle: int, B: int, tok, G: int, table_ids, extra, x_out: int
 def greedy_argmax(logits: int, B: int, V: int, seen, penalty: float, tok_out: int, margin_out,
                   stream: int) -> None:
     _check(lib.greedy_argmax(logits, B, V, seen, penalty, tok_out, margin_out, stream))
+
+
+def decoder_generate(handle: int, slot: int, n_steps: int, tok_io: int, G: int, table_ids,
+                     extra, head: int, seen, penalty: float, tokens_out, y_out, logits_out: int,
+                     stream: int) -> None:
+    _check(lib.decoder_generate(handle, slot, n_steps, tok_io, G, _i32_array(list(table_ids)),
+                                extra, head, seen, penalty, tokens_out, y_out, logits_out,
+                                stream), handle)
+
+
+def decoder_profile_stage(handle: int, stage: int, enable: int) -> None:
+    _check(lib.decoder_profile_stage(handle, stage, enable), handle)
+
+
+def decoder_profile_result(handle: int):
+    ms, n = C.c_double(), C.c_int64()
+    _check(lib.decoder_profile_result(handle, C.byref(ms), C.byref(n)), handle)
+    return ms.value, n.value

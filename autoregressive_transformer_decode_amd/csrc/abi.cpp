@@ -36,8 +36,22 @@ struct atd_decoder {
   float *pml = nullptr, *pacc = nullptr;
   void** kv_tab = nullptr;
   int *slot_pos = nullptr, *slot_cap = nullptr;
+  float* part = nullptr;       // argmax partials [max_rows, nblk, 3]
+  int32_t* counter = nullptr;  // token counter of decoder_generate
   int nsplit_max = 0;
   bool dry = false;  // ATD_FLAG_DRY_RUN: host state only, no HIP calls
+  // stage timing (decoder_profile_stage)
+  int probe_stage = -1;
+  bool capturing = false;
+  std::vector<hipEvent_t> probe_ev;  // start/stop pairs
+  size_t probe_used = 0;
+  // graph cache of decoder_generate
+  hipStream_t cap_stream = nullptr;
+  struct GraphEntry {
+    std::vector<int64_t> key;
+    hipGraphExec_t exec;
+  };
+  std::vector<GraphEntry> graphs;
   std::string err;
 };
 
@@ -65,7 +79,7 @@ int hip_fail(atd_decoder* d, hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int elem_bytes(const atd_config& c) { return c.dtype == ATD_BF16 ? 2 : 4; }
+int kv_elem_bytes(const atd_config& c) { return c.kv_dtype == ATD_BF16 ? 2 : 4; }
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
@@ -73,6 +87,9 @@ int check_config(const atd_config* c) {
   if (!c) return fail(nullptr, ATD_ERR_INVALID_ARG, "cfg is NULL");
   if (c->dtype != ATD_F32 && c->dtype != ATD_BF16)
     return fail(nullptr, ATD_ERR_DTYPE, "dtype %d is not ATD_F32 (0) or ATD_BF16 (1)", c->dtype);
+  if (c->kv_dtype != ATD_F32 && c->kv_dtype != ATD_BF16)
+    return fail(nullptr, ATD_ERR_DTYPE, "kv_dtype %d is not ATD_F32 (0) or ATD_BF16 (1)",
+                c->kv_dtype);
   if (c->n_layers < 1 || c->n_layers > kMaxLayers)
     return fail(nullptr, ATD_ERR_UNSUPPORTED, "n_layers %d outside [1, %d]", c->n_layers,
                 kMaxLayers);
@@ -180,17 +197,37 @@ SlotTables slots_of(const atd_decoder* d) {
 
 int chunk_for(int M) { return M <= 2 ? kAttnChunkSmall : kAttnChunkLarge; }
 
+// Event pair around one launch of the profiled stage (eager calls only).
+hipError_t probe_mark(atd_decoder* d, int stage, hipStream_t s) {
+  if (d->probe_stage != stage || d->capturing) return hipSuccess;
+  if (d->probe_used == d->probe_ev.size()) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return r;
+    d->probe_ev.push_back(e);
+  }
+  return hipEventRecord(d->probe_ev[d->probe_used++], s);
+}
+
+#define PROBED(stage, call)                                        \
+  do {                                                             \
+    if ((e = probe_mark(d, stage, s)) != hipSuccess) return e;     \
+    if ((e = (call)) != hipSuccess) return e;                      \
+    if ((e = probe_mark(d, stage, s)) != hipSuccess) return e;     \
+  } while (0)
+
 // The per-layer launch sequence for M rows (decode step or prefill block).
 hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hipStream_t s) {
   const atd_config& c = d->cfg;
   const int h = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv;
   const int bf16 = c.dtype == ATD_BF16;
+  const int kv_bf16 = c.kv_dtype == ATD_BF16;
   const SlotTables st = slots_of(d);
   const int chunk = chunk_for(M);
   const int nsplit = std::min(d->nsplit_max, (max_len_bound + chunk - 1) / chunk);
   hipError_t e = hipSuccess;
-  for (int l = 0; l < c.n_layers && e == hipSuccess; ++l) {
+  for (int l = 0; l < c.n_layers; ++l) {
     const atd_layer_weights& W = d->layers[l];
     GemvArgs g{};
     g.W[0] = W.wq;
@@ -211,7 +248,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     g.K = h;
     g.N = nqkv;
     g.M = M;
-    if ((e = launch_gemv(g, kEpiStore, true, bf16, s)) != hipSuccess) break;
+    PROBED(ATD_STAGE_QKV, launch_gemv(g, kEpiStore, true, bf16, s));
 
     RopeArgs r{};
     r.qkv = d->qkv;
@@ -229,7 +266,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     r.Hkv = Hkv;
     r.D = D;
     r.qk_norm = c.qk_norm;
-    if ((e = launch_rope_append(r, bf16, s)) != hipSuccess) break;
+    PROBED(ATD_STAGE_ROPE, launch_rope_append(r, kv_bf16, s));
 
     AttnArgs a{};
     a.q = d->q;
@@ -245,7 +282,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     a.pml = d->pml;
     a.pacc = d->pacc;
     a.o = d->o;
-    if ((e = launch_attention(a, bf16, D, Hq / Hkv, s)) != hipSuccess) break;
+    PROBED(ATD_STAGE_ATTN, launch_attention(a, kv_bf16, D, Hq / Hkv, s));
 
     GemvArgs op{};
     op.W[0] = W.wo;
@@ -257,7 +294,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     op.K = nq;
     op.N = h;
     op.M = M;
-    if ((e = launch_gemv(op, kEpiResidual, false, bf16, s)) != hipSuccess) break;
+    PROBED(ATD_STAGE_OPROJ, launch_gemv(op, kEpiResidual, false, bf16, s));
 
     GemvArgs gu{};
     gu.W[0] = W.w_gate;
@@ -272,7 +309,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     gu.K = h;
     gu.N = c.ffn;
     gu.M = M;
-    if ((e = launch_gemv(gu, kEpiSwiglu, true, bf16, s)) != hipSuccess) break;
+    PROBED(ATD_STAGE_GATEUP, launch_gemv(gu, kEpiSwiglu, true, bf16, s));
 
     GemvArgs dn{};
     dn.W[0] = W.w_down;
@@ -284,7 +321,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     dn.K = c.ffn;
     dn.N = h;
     dn.M = M;
-    e = launch_gemv(dn, kEpiResidual, false, bf16, s);
+    PROBED(ATD_STAGE_DOWN, launch_gemv(dn, kEpiResidual, false, bf16, s));
   }
   return e;
 }
@@ -305,7 +342,9 @@ hipError_t run_head(atd_decoder* d, const float* xrows, int M, int head, float* 
   g.K = c.hidden;
   g.N = c.vocab;
   g.M = M;
-  return launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16, s);
+  hipError_t e = hipSuccess;
+  PROBED(ATD_STAGE_HEAD, launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16, s));
+  return e;
 }
 
 int check_tables(atd_decoder* d, int G, const int32_t* table_ids, const int32_t* tok,
@@ -336,6 +375,19 @@ EmbedArgs embed_args(atd_decoder* d, int B, const int32_t* tok, int G,
   e.out = out;
   e.h = d->cfg.hidden;
   e.M = B;
+  return e;
+}
+
+// Launch sequence of one decode step of B rows (slots slot0..slot0+B-1).
+hipError_t enqueue_step(atd_decoder* d, int slot0, int B, const int32_t* tok, int G,
+                        const int32_t* table_ids, const float* extra, int head, float* y_out,
+                        float* logits_out, int max_cap, hipStream_t s) {
+  RowMap rows{kRowsStep, slot0};
+  EmbedArgs ea = embed_args(d, B, tok, G, table_ids, extra, d->x);
+  hipError_t e = launch_embed(ea, d->cfg.dtype == ATD_BF16, s);
+  if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, s);
+  if (e == hipSuccess) e = run_head(d, d->x, B, head, y_out, logits_out, s);
+  if (e == hipSuccess) e = launch_advance(slots_of(d), rows, B, s);
   return e;
 }
 
@@ -390,6 +442,9 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   const size_t o_kv = carve((size_t)S * cfg->n_layers * 2 * sizeof(void*));
   const size_t o_pos = carve((size_t)S * 4);
   const size_t o_cap = carve((size_t)S * 4);
+  const int nblk_v = (cfg->vocab + kArgmaxChunk - 1) / kArgmaxChunk;
+  const size_t o_part = carve((size_t)R * nblk_v * 3 * 4);
+  const size_t o_cnt = carve(4);
 
   hipError_t e = hipGetDevice(&d->device);
   if (e == hipSuccess) e = hipMalloc(&d->mem, off);
@@ -411,6 +466,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->kv_tab = (void**)(base + o_kv);
   d->slot_pos = (int*)(base + o_pos);
   d->slot_cap = (int*)(base + o_cap);
+  d->part = (float*)(base + o_part);
+  d->counter = (int32_t*)(base + o_cnt);
 
   // RoPE table: phi = p * theta^(-2i/D) in double, cos/sin rounded to float.
   std::vector<float> ct((size_t)cfg->max_ctx * half), sn((size_t)cfg->max_ctx * half);
@@ -440,6 +497,9 @@ extern "C" int decoder_destroy(atd_decoder* d) {
   hipError_t e = hipSuccess;
   if (d->mem && !d->dry) {
     e = hipDeviceSynchronize();
+    for (auto& g : d->graphs) (void)hipGraphExecDestroy(g.exec);
+    for (auto ev : d->probe_ev) (void)hipEventDestroy(ev);
+    if (d->cap_stream) (void)hipStreamDestroy(d->cap_stream);
     hipError_t e2 = hipFree(d->mem);
     if (e == hipSuccess) e = e2;
   }
@@ -488,7 +548,7 @@ extern "C" int kv_bucket_grow(atd_decoder* d, int32_t slot, void* const* k_new,
     a.rows = d->pos[slot];
     a.s_old = d->cap[slot];
     a.s_new = s_new;
-    a.elem_bytes = elem_bytes(c);
+    a.elem_bytes = kv_elem_bytes(c);
     e = launch_kv_copy(a, s);
   }
   if (e == hipSuccess && !d->dry)
@@ -617,13 +677,8 @@ extern "C" int decoder_step(atd_decoder* d, int32_t slot0, int32_t B, const int3
     for (int b = 0; b < B; ++b) d->pos[slot0 + b] += 1;
     return ATD_OK;
   }
-  hipStream_t s = (hipStream_t)stream;
-  RowMap rows{kRowsStep, slot0};
-  EmbedArgs ea = embed_args(d, B, tok, G, table_ids, extra, d->x);
-  hipError_t e = launch_embed(ea, c.dtype == ATD_BF16, s);
-  if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, s);
-  if (e == hipSuccess) e = run_head(d, d->x, B, head, y_out, logits_out, s);
-  if (e == hipSuccess) e = launch_advance(slots_of(d), rows, B, s);
+  hipError_t e = enqueue_step(d, slot0, B, tok, G, table_ids, extra, head, y_out, logits_out,
+                              max_cap, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(d, e, "decoder_step");
   for (int b = 0; b < B; ++b) d->pos[slot0 + b] += 1;
   return ATD_OK;
@@ -677,4 +732,132 @@ extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t
   }
   hipError_t e = launch_argmax(a, (hipStream_t)stream);
   return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "greedy_argmax");
+}
+
+// ---------------------------------------------------------------- generation
+
+extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, int32_t* tok_io,
+                                int32_t G, const int32_t* table_ids, const float* extra,
+                                int32_t head, uint32_t* seen, float penalty,
+                                int32_t* tokens_out, float* y_out, float* logits_out,
+                                void* stream) {
+  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
+  const atd_config& c = d->cfg;
+  if (slot < 0 || slot >= c.max_slots)
+    return fail(d, ATD_ERR_INVALID_ARG, "slot %d outside [0, %d)", slot, c.max_slots);
+  if (!d->attached[slot])
+    return fail(d, ATD_ERR_INVALID_ARG, "slot %d has no KV buffers attached", slot);
+  if (n_steps < 0) return fail(d, ATD_ERR_INVALID_ARG, "n_steps %d < 0", n_steps);
+  if (!tok_io || !logits_out) return fail(d, ATD_ERR_INVALID_ARG, "tok_io or logits_out is NULL");
+  if (G < 1) return fail(d, ATD_ERR_INVALID_ARG, "G = %d < 1", G);
+  int rc = check_tables(d, G, table_ids, tok_io, extra);
+  if (rc) return rc;
+  if (y_out && !aligned16(y_out))
+    return fail(d, ATD_ERR_INVALID_ARG, "y_out %p not 16-byte aligned", (void*)y_out);
+  if (head < 0 || head >= c.n_lm_heads)
+    return fail(d, ATD_ERR_INVALID_ARG, "head %d outside [0, %d)", head, c.n_lm_heads);
+  if (!(penalty > 0.0f) || !std::isfinite(penalty))
+    return fail(d, ATD_ERR_INVALID_ARG, "penalty %g is not a positive number", (double)penalty);
+  if ((int64_t)d->pos[slot] + n_steps > d->cap[slot])
+    return fail(d, ATD_ERR_KV_FULL, "slot %d: %d steps from position %d exceed capacity %d",
+                slot, n_steps, d->pos[slot], d->cap[slot]);
+  if ((int64_t)d->pos[slot] + n_steps > c.max_ctx)
+    return fail(d, ATD_ERR_CAPACITY, "slot %d: %d steps from position %d exceed max_ctx %d", slot,
+                n_steps, d->pos[slot], c.max_ctx);
+  if (n_steps == 0) return ATD_OK;
+  if (d->dry) {
+    d->pos[slot] += n_steps;
+    return ATD_OK;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int max_cap = std::min(d->cap[slot], c.max_ctx);
+
+  std::vector<int64_t> key = {slot, G, (int64_t)(uintptr_t)extra, head,
+                              (int64_t)(uintptr_t)tok_io, (int64_t)(uintptr_t)seen,
+                              (int64_t)(uintptr_t)tokens_out, (int64_t)(uintptr_t)y_out,
+                              (int64_t)(uintptr_t)logits_out, max_cap};
+  {
+    uint32_t pb;
+    std::memcpy(&pb, &penalty, 4);
+    key.push_back(pb);
+    for (int g = 0; g < G; ++g) key.push_back(table_ids[g]);
+  }
+  hipGraphExec_t exec = nullptr;
+  for (auto& ge : d->graphs)
+    if (ge.key == key) exec = ge.exec;
+  hipError_t e = hipSuccess;
+  if (!exec) {
+    if (!d->cap_stream) {
+      e = hipStreamCreateWithFlags(&d->cap_stream, hipStreamNonBlocking);
+      if (e != hipSuccess) return hip_fail(d, e, "hipStreamCreate (capture stream)");
+    }
+    hipStream_t cs = d->cap_stream;
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return hip_fail(d, e, "hipStreamBeginCapture");
+    d->capturing = true;
+    hipError_t le = enqueue_step(d, slot, 1, tok_io, G, table_ids, extra, head, y_out, logits_out,
+                                 max_cap, cs);
+    if (le == hipSuccess) {
+      ArgmaxArgs a{};
+      a.z = logits_out;
+      a.B = 1;
+      a.V = c.vocab;
+      a.seen = seen;
+      a.nwords = (c.vocab + 31) / 32;
+      a.penalty = penalty;
+      a.tok = tok_io;
+      a.margin = nullptr;
+      a.part = d->part;
+      a.nblk = (c.vocab + kArgmaxChunk - 1) / kArgmaxChunk;
+      le = launch_argmax(a, cs);
+    }
+    if (le == hipSuccess && tokens_out) le = launch_record_token(tok_io, tokens_out, d->counter, cs);
+    d->capturing = false;
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    if (le != hipSuccess || e != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return hip_fail(d, le != hipSuccess ? le : e, "capture of a decode step");
+    }
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return hip_fail(d, e, "hipGraphInstantiate");
+    if (d->graphs.size() >= 8) {
+      (void)hipGraphExecDestroy(d->graphs.front().exec);
+      d->graphs.erase(d->graphs.begin());
+    }
+    d->graphs.push_back({key, exec});
+  }
+  if (tokens_out) e = launch_fill_i32(d->counter, 1, 0, s);
+  for (int k = 0; k < n_steps && e == hipSuccess; ++k) e = hipGraphLaunch(exec, s);
+  if (e != hipSuccess) return hip_fail(d, e, "decoder_generate replay");
+  d->pos[slot] += n_steps;
+  return ATD_OK;
+}
+
+// ---------------------------------------------------------------- stage timing
+
+extern "C" int decoder_profile_stage(atd_decoder* d, int32_t stage, int32_t enable) {
+  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
+  if (stage < 0 || stage >= ATD_STAGE_COUNT)
+    return fail(d, ATD_ERR_INVALID_ARG, "stage %d outside [0, %d)", stage, ATD_STAGE_COUNT);
+  d->probe_stage = enable ? stage : -1;
+  d->probe_used = 0;
+  return ATD_OK;
+}
+
+extern "C" int decoder_profile_result(atd_decoder* d, double* total_ms, int64_t* launches) {
+  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
+  double tot = 0.0;
+  const size_t pairs = d->probe_used / 2;
+  for (size_t i = 0; i < pairs; ++i) {
+    hipError_t e = hipEventSynchronize(d->probe_ev[2 * i + 1]);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, d->probe_ev[2 * i], d->probe_ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(d, e, "decoder_profile_result");
+    tot += ms;
+  }
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = (int64_t)pairs;
+  return ATD_OK;
 }

@@ -116,5 +116,7 @@ hipError_t launch_set_slot(const SlotTables& st, int slot, void* const* k, void*
                            int cap, int pos, int set_ptrs, hipStream_t s);
 hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s);
+hipError_t launch_record_token(const int32_t* tok, int32_t* out, int32_t* counter, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 
 }  // namespace atd

@@ -561,6 +561,20 @@ __global__ __launch_bounds__(64) void k_argmax_final(ArgmaxArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ generation bookkeeping
+__global__ void k_record_token(const int32_t* tok, int32_t* out, int32_t* counter) {
+  if (threadIdx.x == 0) {
+    const int k = *counter;
+    out[k] = *tok;
+    *counter = k + 1;
+  }
+}
+
+__global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_embed(const EmbedArgs& a, int bf16, hipStream_t s) {
@@ -694,6 +708,17 @@ hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s) {
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_argmax_part, dim3(a.nblk, a.B), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_argmax_final, dim3(a.B), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_record_token(const int32_t* tok, int32_t* out, int32_t* counter,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_record_token, dim3(1), dim3(64), 0, s, tok, out, counter);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 

@@ -90,6 +90,7 @@ def make_config(s: ModelShape, max_slots: int, max_rows: int, max_ctx: int,
         n_tables=n_tables if n_tables is not None else len(s.table_vocabs),
         qk_norm=int(s.qk_norm), qkv_bias=int(s.qkv_bias),
         dtype=B.ATD_BF16 if s.dtype == BF16 else B.ATD_F32,
+        kv_dtype=B.ATD_BF16 if s.kv_dtype == BF16 else B.ATD_F32,
         rope_theta=s.rope_theta, rms_eps=s.rms_eps,
         max_slots=max_slots, max_rows=max_rows, max_ctx=max_ctx)
 
@@ -105,7 +106,7 @@ class Decoder:
         self.cfg = make_config(s, max_slots, max_rows, max_ctx)
         self.handle = B.decoder_create(self.cfg, model.weights)
         self.kv = {}   # slot -> (list of K tensors, list of V tensors)
-        self.kv_dtype = torch.bfloat16 if s.dtype == BF16 else torch.float32
+        self.kv_dtype = torch.bfloat16 if s.kv_dtype == BF16 else torch.float32
 
     def close(self):
         if self.handle:
@@ -166,6 +167,26 @@ class Decoder:
                        y_out.data_ptr() if y_out is not None else None, logits_out.data_ptr(),
                        _stream())
         return y_out, logits_out
+
+    def generate(self, n_steps: int, tok_io: torch.Tensor, table_ids: Sequence[int] = (0,),
+                 slot: int = 0, extra: Optional[torch.Tensor] = None, head: int = 0,
+                 seen: Optional[torch.Tensor] = None, penalty: float = 1.0,
+                 tokens_out: Optional[torch.Tensor] = None, y_out: Optional[torch.Tensor] = None,
+                 logits_out: Optional[torch.Tensor] = None):
+        """n_steps greedy steps on the device (graph-replayed step + argmax)."""
+        if logits_out is None:
+            logits_out = torch.empty(self.shape.vocab, device="cuda", dtype=torch.float32)
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        B.decoder_generate(self.handle, slot, n_steps, tok_io.data_ptr(), len(table_ids),
+                           table_ids, ptr(extra), head, ptr(seen), float(penalty),
+                           ptr(tokens_out), ptr(y_out), logits_out.data_ptr(), _stream())
+        return logits_out
+
+    def profile_stage(self, stage: int, enable: bool = True):
+        B.decoder_profile_stage(self.handle, stage, int(enable))
+
+    def profile_result(self):
+        return B.decoder_profile_result(self.handle)
 
     def embed(self, tok: Optional[torch.Tensor], table_ids: Sequence[int], x_out: torch.Tensor,
               nrows: int = 1, extra: Optional[torch.Tensor] = None):

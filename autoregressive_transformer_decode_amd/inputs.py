@@ -57,9 +57,10 @@ class ModelShape:
     qkv_bias: bool
     rope_theta: float
     rms_eps: float
-    dtype: str            # weight, embedding and KV-cache storage: F32 or BF16
+    dtype: str            # weight and embedding storage: F32 or BF16
     table_vocabs: Tuple[int, ...]   # vocab of each embedding table
     model_id: int = 0     # separates the random streams of two stacks
+    kv_dtype: str = F32   # KV-cache storage: F32 or BF16
 
     @property
     def q_dim(self) -> int:
@@ -95,12 +96,13 @@ class Workload:
 
 
 def _shape(name, L, h, hq, hkv, d, f, v, dtype, qk_norm, qkv_bias, tables,
-           n_heads=1, model_id=0):
+           n_heads=1, model_id=0, kv_dtype=F32):
     return ModelShape(name=name, n_layers=L, hidden=h, n_q_heads=hq,
                       n_kv_heads=hkv, head_dim=d, ffn=f, vocab=v,
                       n_lm_heads=n_heads, qk_norm=qk_norm, qkv_bias=qkv_bias,
                       rope_theta=1.0e6, rms_eps=1.0e-6, dtype=dtype,
-                      table_vocabs=tuple(tables), model_id=model_id)
+                      table_vocabs=tuple(tables), model_id=model_id,
+                      kv_dtype=kv_dtype)
 
 
 TINY = _shape("tiny", 2, 512, 8, 4, 64, 1536, 2048, F32, True, False, [2048])
@@ -111,6 +113,8 @@ CP06 = _shape("code_predictor", 5, 1024, 16, 8, 128, 3072, 2048, BF16, True,
               False, [3072] + [2048] * 15, n_heads=15, model_id=1)
 TALKER17 = _shape("talker1.7b", 28, 2048, 16, 8, 128, 6144, 3072, BF16, True,
                   False, [3072])
+# the batched workload states bf16 for the KV cache as well as the weights
+TALKER17_KVBF16 = dataclasses.replace(TALKER17, name="talker1.7b-kvbf16", kv_dtype=BF16)
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", TINY, batch=1, prefill=16, steps=16, s_init=128,
@@ -122,7 +126,7 @@ WORKLOADS: Dict[str, Workload] = {
                            frames=75, penalty=1.05),
     "talker1.7b": Workload("talker1.7b", TALKER17, batch=1, prefill=512,
                            steps=1536, s_init=2048, s_max=2048),
-    "batched64": Workload("batched64", TALKER17, batch=64, prefill=0,
+    "batched64": Workload("batched64", TALKER17_KVBF16, batch=64, prefill=0,
                           steps=32, s_init=4096 + 64, s_max=4096 + 64,
                           len_range=(256, 4096)),
 }
@@ -292,7 +296,7 @@ def batched_first_inputs(wl: Workload, seed: int = 0) -> np.ndarray:
 def batched_kv(shape: ModelShape, stream: int, length: int, layer: int,
                seed: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Synthetic cache contents of one stream and layer: K, V [Hkv, length, D]
-    as bf16 bit patterns, N(0, 1)."""
+    as bf16 bit patterns, N(0, 1) (the batched workload's bf16 cache)."""
     kvshape = (shape.n_kv_heads, length, shape.head_dim)
     tid = _T_KV + 1000 * stream + 2 * layer
     k = to_bf16_bits(normal(seed, 3, tid, kvshape, scale=1.0))

@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload talker1.7b]
+
+A step is one decode step of the whole stack (embedding, every layer, final
+norm, LM head, penalized greedy argmax feeding the next step) on synthetic
+seeded weights and inputs already resident in HBM.  The default workload is
+the 1.7B Talker shape at batch 1: a 512-row prefill (untimed), then K greedy
+steps replayed from a HIP graph on the device (K = 1536 runs the context to
+2048).  Prints one JSON line.
+
+Also measured in the same run:
+  roofline      the dominant kernel (RMSNorm + gate/up + SwiGLU GEMV): its
+                algorithmic bytes per launch over its average duration, timed
+                with HIP event pairs on the launching stream during a pass of
+                the same steps; HBM traffic per launch from the committed
+                rocprofv3 counter summary when it matches the kernel source.
+  cpu_baseline  the CPU oracle on this host's cores, on a bounded sample of
+                the same workload (decode steps after the same prefill).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/sec at batch 1 and 64; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "autoregressive_transformer_decode_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemv_talker1.7b_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def weight_bytes(shape) -> int:
+    return shape.weight_elems(with_head=True) * (2 if shape.dtype == "bf16" else 4)
+
+
+def kv_row_bytes(shape) -> int:
+    return 2 * shape.n_layers * shape.kv_dim * (2 if shape.kv_dtype == "bf16" else 4)
+
+
+def gateup_bytes(shape) -> int:
+    """Algorithmic bytes of one gate/up launch: both [F, h] matrices once,
+    the input row in and the [F] activation out (float32)."""
+    wb = 2 if shape.dtype == "bf16" else 4
+    return 2 * shape.ffn * shape.hidden * wb + 4 * shape.hidden + 4 * shape.ffn
+
+
+def oracle_model(mw, dtype):
+    from oracle import decoder as od
+    s = mw.shape
+    hp = dict(n_layers=s.n_layers, hidden=s.hidden, n_q_heads=s.n_q_heads,
+              n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, ffn=s.ffn,
+              rope_theta=s.rope_theta, rms_eps=s.rms_eps, qk_norm=s.qk_norm,
+              kv_bf16=(s.kv_dtype == "bf16"))
+    layers = [dict(attn_norm=L.attn_norm, wq=L.wq.values, wk=L.wk.values, wv=L.wv.values,
+                   bq=L.bq, bk=L.bk, bv=L.bv, q_norm=L.q_norm, k_norm=L.k_norm,
+                   wo=L.wo.values, mlp_norm=L.mlp_norm, w_gate=L.w_gate.values,
+                   w_up=L.w_up.values, w_down=L.w_down.values) for L in mw.layers]
+    return od.make_model(hp, layers, mw.final_norm, [h.values for h in mw.heads],
+                         [t.values for t in mw.tables], dtype=dtype)
+
+
+def cpu_baseline(mw, X0, s_init, budget_s, max_steps):
+    """The oracle (float32, as it stands) on the host: prefill, then greedy
+    steps until the time budget is spent; tokens/s over the timed steps."""
+    import numpy as np
+    from oracle import decoder as od
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    om = oracle_model(mw, np.float32)
+    cache = od.Cache(om, s_init)
+    _, z = od.prefill(om, cache, X0, 0)
+    tok = int(np.argmax(z))
+    n, t0 = 0, time.perf_counter()
+    while n < max_steps:
+        _, z = od.step(om, cache, om.tables[0][tok], 0)
+        tok = int(np.argmax(z))
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{n} greedy decode steps after the {X0.shape[0]}-row prefill "
+                       f"(context {X0.shape[0] + 1}..{X0.shape[0] + n}), float32 numpy, "
+                       f"prefill untimed")
+
+
+def traffic_per_launch():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def bench_lm(args, wl):
+    import numpy as np
+    import torch
+    from autoregressive_transformer_decode_amd import binding as B
+    from autoregressive_transformer_decode_amd import device as dv
+    from autoregressive_transformer_decode_amd import inputs
+
+    s = wl.model
+    t = time.perf_counter()
+    mw = inputs.make_weights(s, seed=0)
+    X0 = inputs.prefill_embeddings(wl, seed=0)
+    log(f"weights generated in {time.perf_counter() - t:.1f}s")
+    dm = dv.DeviceModel(mw)
+    dec = dv.Decoder(dm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max)
+    dec.grow(0, wl.s_init)
+    P0 = wl.prefill
+    K = args.steps if args.steps is not None else wl.steps
+    W = args.warmup
+    if P0 + max(K, W) > wl.s_init:
+        raise SystemExit(f"--steps/--warmup beyond the {wl.s_init}-row cache of {wl.name}")
+    z = torch.empty(s.vocab, device="cuda")
+    y = torch.empty(s.hidden, device="cuda")
+    dec.prefill(torch.from_numpy(X0).cuda(), logits_out=z)
+    tok0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dv.greedy_argmax(z, None, 1.0, tok0)
+    tok = tok0.clone()
+    torch.cuda.synchronize()
+    log(f"prefill {P0} rows done")
+
+    # warmup (also captures the step graph), then rewind to the prefill state
+    if W:
+        dec.generate(W, tok, y_out=y, logits_out=z)
+    torch.cuda.synchronize()
+    dec.set_position(0, P0)
+    tok.copy_(tok0)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    dec.generate(K, tok, y_out=y, logits_out=z)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    log(f"timed {K} steps: {dt * 1e3:.1f} ms")
+
+    # roofline pass: same steps, eager, HIP events around every gate/up launch
+    dec.set_position(0, P0)
+    tok.copy_(tok0)
+    n_prof = min(K, 128)
+    dec.profile_stage(B.ATD_STAGE_GATEUP, True)
+    zz = torch.empty(1, s.vocab, device="cuda")
+    for _ in range(n_prof):
+        dec.step(tok.view(1, 1), [0], logits_out=zz)
+        dv.greedy_argmax(zz[0], None, 1.0, tok)
+    torch.cuda.synchronize()
+    prof_ms, launches = dec.profile_result()
+    dec.profile_stage(B.ATD_STAGE_GATEUP, False)
+    avg_s = prof_ms / 1e3 / max(launches, 1)
+    per_launch = gateup_bytes(s)
+    achieved = per_launch / avg_s / 1e9
+    traffic = traffic_per_launch()
+
+    mean_ctx = P0 + (K + 1) / 2.0
+    step_bytes = weight_bytes(s) + kv_row_bytes(s) * mean_ctx
+    ms_step = dt * 1e3 / K
+    out = dict(
+        metric=METRIC, value=K / dt, unit="tokens/s", n_gpus=1, steps=K, warmup=W,
+        ms_per_step=ms_step, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16" if s.dtype == "bf16" else "f32", data="synthetic",
+        config=dict(workload=wl.name, batch=1, prefill=P0, context=[P0 + 1, P0 + K],
+                    layers=s.n_layers, hidden=s.hidden, heads=[s.n_q_heads, s.n_kv_heads],
+                    head_dim=s.head_dim, ffn=s.ffn, vocab=s.vocab, kv_capacity=wl.s_init,
+                    step="graph-replayed decode step + greedy argmax on device"),
+        roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=traffic,
+                      kernel="k_gemv (RMSNorm + gate/up + SwiGLU), bf16 weights",
+                      bytes_per_launch=per_launch, avg_launch_us=avg_s * 1e6,
+                      launches_timed=launches),
+        step_hbm=dict(algorithmic_bytes=step_bytes, achieved_gbs=step_bytes / (ms_step / 1e3) / 1e9,
+                      frac=step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS),
+    )
+    dec.close()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(mw, X0, wl.s_init, args.cpu_seconds, 64)
+    else:
+        out["cpu_baseline"] = None
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", default="talker1.7b",
+                    choices=["talker1.7b", "asr", "tiny"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    from autoregressive_transformer_decode_amd import inputs
+    wl = inputs.WORKLOADS[args.workload]
+    out = bench_lm(args, wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

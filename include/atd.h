@@ -39,8 +39,9 @@
  *    argument and its value.  There is no fallback path: an unsupported
  *    configuration is an error.
  *  - All floating-point activations, hidden states, logits and biases are
- *    float32.  Weights, embedding tables and the KV cache are stored in the
- *    configured dtype (float32 or bf16); arithmetic accumulates in float32.
+ *    float32.  Weights and embedding tables are stored in atd_config.dtype,
+ *    the KV cache in atd_config.kv_dtype (float32 or bf16 each); arithmetic
+ *    accumulates in float32.
  *  - A decoder is used from one host thread at a time.
  */
 #ifndef ATD_H
@@ -66,7 +67,8 @@ enum {
   ATD_ERR_UNSUPPORTED = -7  /* config outside what the kernels implement    */
 };
 
-/* Storage dtypes of weights, embedding tables and the KV cache. */
+/* Storage dtypes of weights and embedding tables (atd_config.dtype) and of
+ * the KV cache (atd_config.kv_dtype). */
 enum { ATD_F32 = 0, ATD_BF16 = 1 };
 
 /* Shape of one decoder stack (hyper-parameters; host struct). */
@@ -82,7 +84,9 @@ typedef struct atd_config {
   int32_t n_tables;    /* number of embedding tables, 1..16                  */
   int32_t qk_norm;     /* 1: per-head RMSNorm of q and k before RoPE         */
   int32_t qkv_bias;    /* 1: q/k/v projections carry a bias                  */
-  int32_t dtype;       /* ATD_F32 or ATD_BF16                                */
+  int32_t dtype;       /* weights and embedding tables: ATD_F32 or ATD_BF16  */
+  int32_t kv_dtype;    /* KV cache rows: ATD_F32 or ATD_BF16 (rounded to
+                          nearest even when stored)                         */
   double rope_theta;   /* RoPE base (1e6 for the Qwen3 Talker)               */
   float rms_eps;       /* epsilon of every RMSNorm                           */
   int32_t max_slots;   /* independent streams (KV caches) the decoder keeps  */
@@ -149,7 +153,7 @@ const char* decoder_last_error(const atd_decoder* dec);
 
 /* Attach KV buffers of capacity s_new rows to `slot` (Audio8-ASR report,
  * dynamic window mechanism).  k_new / v_new: host arrays [n_layers] of
- * device pointers, each [Hkv, s_new, D] in the config dtype, 16-byte
+ * device pointers, each [Hkv, s_new, D] in the config kv_dtype, 16-byte
  * aligned.  When the slot already holds buffers, the valid rows
  * [:, :pos, :] of every layer are copied into the new ones on `stream`; the
  * position is kept, so decoding continues at the same token and RoPE
@@ -213,6 +217,48 @@ int decoder_embed(atd_decoder* dec, int32_t B, const int32_t* tok, int32_t G,
  * per device (allocated on first use).  Errors: INVALID_ARG, DEVICE. */
 int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
                   float penalty, int32_t* tok_out, float* margin_out, void* stream);
+
+
+/* Greedy generation on the device: n_steps decode steps of `slot` with the
+ * token fed back without a host round trip (the qwen3-tts-hip log measures
+ * the host-side sampling and token copies as the remaining host cost).  Step
+ * k embeds tok_io[0..G-1] from tables table_ids (host [G]) plus extra
+ * (device [h] or NULL, the same every step), runs the stack and LM head
+ * `head`, then the penalized argmax of greedy_argmax (seen: device
+ * [ceil(V/32)] or NULL) writes the chosen token to tok_io[0] (the other
+ * G-1 ids are held) and, when tokens_out is not NULL, to tokens_out[k]
+ * (device int32 [n_steps]).  y_out (device [h] or NULL) and logits_out
+ * (device [V]) hold the last step's outputs.  The launches of one step are
+ * captured once into a HIP graph and replayed; the graph is cached for this
+ * argument set and bucket and rebuilt when either changes.  Refused with
+ * ATD_ERR_KV_FULL when pos + n_steps exceeds the slot's capacity (grow the
+ * bucket first; nothing runs).  Errors: INVALID_ARG, KV_FULL, CAPACITY,
+ * DEVICE. */
+int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* tok_io,
+                     int32_t G, const int32_t* table_ids, const float* extra, int32_t head,
+                     uint32_t* seen, float penalty, int32_t* tokens_out, float* y_out,
+                     float* logits_out, void* stream);
+
+/* Stages of a decode step, for decoder_profile_stage. */
+enum {
+  ATD_STAGE_QKV = 0,     /* RMSNorm + q/k/v projection                       */
+  ATD_STAGE_ROPE = 1,    /* QK norm + RoPE + cache append                     */
+  ATD_STAGE_ATTN = 2,    /* split-K attention + combine                       */
+  ATD_STAGE_OPROJ = 3,   /* output projection + residual                      */
+  ATD_STAGE_GATEUP = 4,  /* RMSNorm + gate/up projection + SwiGLU             */
+  ATD_STAGE_DOWN = 5,    /* down projection + residual                        */
+  ATD_STAGE_HEAD = 6,    /* final RMSNorm + LM head                           */
+  ATD_STAGE_COUNT = 7
+};
+
+/* Measurement hook: while enabled, every eager launch of `stage` made by
+ * decoder_step / decoder_prefill is bracketed by a HIP event pair recorded
+ * on the call's stream (graph replays of decoder_generate are not).
+ * Enabling clears previous records.  decoder_profile_result waits for the
+ * recorded events and returns their summed elapsed milliseconds and the
+ * number of launches.  Errors: INVALID_ARG, DEVICE. */
+int decoder_profile_stage(atd_decoder* dec, int32_t stage, int32_t enable);
+int decoder_profile_result(atd_decoder* dec, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

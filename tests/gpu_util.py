@@ -18,11 +18,12 @@ MARGIN = 1e-2       # tokens must agree where the oracle's top-2 margin exceeds 
 
 
 def small_shape(name, L, h, hq, hkv, D, F, V, dtype, qk_norm, bias, tables=None, n_heads=1,
-                theta=1e6):
+                theta=1e6, kv_dtype=None):
     return inputs.ModelShape(name=name, n_layers=L, hidden=h, n_q_heads=hq, n_kv_heads=hkv,
                              head_dim=D, ffn=F, vocab=V, n_lm_heads=n_heads, qk_norm=qk_norm,
                              qkv_bias=bias, rope_theta=theta, rms_eps=1e-6, dtype=dtype,
-                             table_vocabs=tuple(tables or [V]))
+                             table_vocabs=tuple(tables or [V]),
+                             kv_dtype=kv_dtype if kv_dtype is not None else dtype)
 
 
 @dataclasses.dataclass

@@ -30,6 +30,7 @@ def test_exports_every_declared_symbol():
 def _cfg(**kw):
     base = dict(n_layers=2, hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=128,
                 vocab=100, n_lm_heads=2, n_tables=2, qk_norm=1, qkv_bias=0, dtype=B.ATD_BF16,
+                kv_dtype=B.ATD_BF16,
                 rope_theta=1e6, rms_eps=1e-6, max_slots=4, max_rows=8, max_ctx=64,
                 flags=B.ATD_FLAG_DRY_RUN)
     base.update(kw)
@@ -76,6 +77,7 @@ def _create(cfg, fw=None):
 @pytest.mark.parametrize("kw,code,needle", [
     (dict(head_dim=96), B.ATD_ERR_UNSUPPORTED, "head_dim 96"),
     (dict(dtype=7), B.ATD_ERR_DTYPE, "dtype 7"),
+    (dict(kv_dtype=2), B.ATD_ERR_DTYPE, "kv_dtype 2"),
     (dict(n_q_heads=6, n_kv_heads=4), B.ATD_ERR_SHAPE, "n_q_heads 6"),
     (dict(n_q_heads=6, n_kv_heads=2), B.ATD_ERR_UNSUPPORTED, "= 3"),
     (dict(hidden=60), B.ATD_ERR_UNSUPPORTED, "hidden 60"),

@@ -207,3 +207,41 @@ def test_asr_workload():
     chk, ref, _ = lm_parity(mw, X0, wl.steps, wl.s_init, oracle_dtype=np.float32)
     _log(f"asr: {chk.n} steps, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
     assert chk.tokens_checked > 300
+
+
+def test_generate_graph_equals_eager_steps():
+    """decoder_generate (one captured step + argmax, replayed) produces the
+    same tokens and bit-identical final logits as eager decoder_step +
+    greedy_argmax, with the penalty on; a second call reuses the graph."""
+    shape = small_shape("gen", 2, 256, 8, 2, 128, 512, 700, "bf16", True, False)
+    mw = inputs.make_weights(shape, seed=7)
+    X0 = inputs.normal(7, 2, 1, (9, 256), scale=1.0)
+    dm = dv.DeviceModel(mw)
+    res = []
+    for mode in ("eager", "graph"):
+        dec = dv.Decoder(dm, max_slots=1, max_rows=9, max_ctx=128)
+        dec.grow(0, 128)
+        z = torch.empty(1, shape.vocab, device="cuda")
+        dec.prefill(torch.from_numpy(X0).cuda(), logits_out=z[0])
+        seen = torch.zeros(dv.seen_words(shape.vocab), dtype=torch.int32, device="cuda")
+        tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+        dv.greedy_argmax(z[0], seen, 1.3, tok)
+        toks = []
+        if mode == "eager":
+            for _ in range(40):
+                dec.step(tok.view(1, 1), [0], logits_out=z)
+                dv.greedy_argmax(z[0], seen, 1.3, tok)
+                toks.append(int(tok.item()))
+        else:
+            out = torch.zeros(40, dtype=torch.int32, device="cuda")
+            dec.generate(25, tok, seen=seen, penalty=1.3, tokens_out=out[:25], logits_out=z[0])
+            dec.generate(15, tok, seen=seen, penalty=1.3, tokens_out=out[25:], logits_out=z[0])
+            torch.cuda.synchronize()
+            toks = out.cpu().tolist()
+        torch.cuda.synchronize()
+        assert dec.position(0)[0] == 9 + 40
+        res.append((toks, z[0].cpu().numpy().copy(), seen.cpu().numpy().copy()))
+        dec.close()
+    assert res[0][0] == res[1][0]
+    assert np.array_equal(res[0][1], res[1][1])
+    assert np.array_equal(res[0][2], res[1][2])

@@ -38,7 +38,7 @@ struct atd_decoder {
   int *slot_pos = nullptr, *slot_cap = nullptr;
   float* part = nullptr;       // argmax partials [max_rows, nblk, 3]
   int32_t* counter = nullptr;  // token counter of decoder_generate
-  int nsplit_max = 0;
+  size_t part_floats = 0;      // capacity of pacc in floats / D
   bool dry = false;  // ATD_FLAG_DRY_RUN: host state only, no HIP calls
   // stage timing (decoder_profile_stage)
   int probe_stage = -1;
@@ -114,6 +114,10 @@ int check_config(const atd_config* c) {
   if ((long)c->n_q_heads * c->head_dim > 8192)
     return fail(nullptr, ATD_ERR_UNSUPPORTED, "n_q_heads * head_dim %d > 8192",
                 c->n_q_heads * c->head_dim);
+  if (c->dtype == ATD_F32 &&
+      (c->hidden > 4096 || c->ffn > 4096 || c->n_q_heads * c->head_dim > 4096))
+    return fail(nullptr, ATD_ERR_UNSUPPORTED,
+                "float32 weights need hidden, ffn and n_q_heads*head_dim <= 4096");
   if (c->vocab < 2)
     return fail(nullptr, ATD_ERR_SHAPE, "vocab %d < 2", c->vocab);
   if (c->n_lm_heads < 1)
@@ -195,7 +199,10 @@ SlotTables slots_of(const atd_decoder* d) {
   return st;
 }
 
-int chunk_for(int M) { return M <= 2 ? kAttnChunkSmall : kAttnChunkLarge; }
+
+// Split-count target of the attention for M rows: enough waves to spread the
+// KV stream over the chip, few enough that each split carries real work.
+int attn_waves(int M) { return M <= 4 ? 512 : kAttnWavesMax; }
 
 // Event pair around one launch of the profiled stage (eager calls only).
 hipError_t probe_mark(atd_decoder* d, int stage, hipStream_t s) {
@@ -224,8 +231,8 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
   const int bf16 = c.dtype == ATD_BF16;
   const int kv_bf16 = c.kv_dtype == ATD_BF16;
   const SlotTables st = slots_of(d);
-  const int chunk = chunk_for(M);
-  const int nsplit = std::min(d->nsplit_max, (max_len_bound + chunk - 1) / chunk);
+  const int waves = attn_waves(M);
+  const int nsplit = attn_max_splits(max_len_bound, M, Hkv, waves);
   hipError_t e = hipSuccess;
   for (int l = 0; l < c.n_layers; ++l) {
     const atd_layer_weights& W = d->layers[l];
@@ -250,25 +257,37 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     g.M = M;
     PROBED(ATD_STAGE_QKV, launch_gemv(g, kEpiStore, true, bf16, s));
 
-    RopeArgs r{};
-    r.qkv = d->qkv;
-    r.q_out = d->q;
-    r.q_norm = (const float*)W.q_norm;
-    r.k_norm = (const float*)W.k_norm;
-    r.eps = c.rms_eps;
-    r.cos_t = d->cos_t;
-    r.sin_t = d->sin_t;
-    r.st = st;
-    r.rows = rows;
-    r.layer = l;
-    r.M = M;
-    r.Hq = Hq;
-    r.Hkv = Hkv;
-    r.D = D;
-    r.qk_norm = c.qk_norm;
-    PROBED(ATD_STAGE_ROPE, launch_rope_append(r, kv_bf16, s));
+    const bool fused = rows.mode == kRowsStep;
+    if (!fused) {
+      // prefill rows of one slot read each other's keys: append them all first
+      RopeArgs r{};
+      r.qkv = d->qkv;
+      r.q_out = d->q;
+      r.q_norm = (const float*)W.q_norm;
+      r.k_norm = (const float*)W.k_norm;
+      r.eps = c.rms_eps;
+      r.cos_t = d->cos_t;
+      r.sin_t = d->sin_t;
+      r.st = st;
+      r.rows = rows;
+      r.layer = l;
+      r.M = M;
+      r.Hq = Hq;
+      r.Hkv = Hkv;
+      r.D = D;
+      r.qk_norm = c.qk_norm;
+      PROBED(ATD_STAGE_ROPE, launch_rope_append(r, kv_bf16, s));
+    }
 
     AttnArgs a{};
+    a.fused = fused;
+    a.qkv = d->qkv;
+    a.q_norm = (const float*)W.q_norm;
+    a.k_norm = (const float*)W.k_norm;
+    a.qk_norm = c.qk_norm;
+    a.eps = c.rms_eps;
+    a.cos_t = d->cos_t;
+    a.sin_t = d->sin_t;
     a.q = d->q;
     a.st = st;
     a.rows = rows;
@@ -276,8 +295,13 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     a.M = M;
     a.Hq = Hq;
     a.Hkv = Hkv;
-    a.chunk = chunk;
     a.nsplit_max = nsplit;
+    a.waves = waves;
+    if (rows.mode == kRowsPrefill || M == 1) {   // one slot: pass its rows directly
+      a.k_direct = d->kp[rows.slot0][l];
+      a.v_direct = d->vp[rows.slot0][l];
+      a.cap_direct = d->cap[rows.slot0];
+    }
     a.scale = 1.0f / std::sqrt((float)D);
     a.pml = d->pml;
     a.pacc = d->pacc;
@@ -416,7 +440,6 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->vp.assign(S, std::vector<void*>(cfg->n_layers, nullptr));
 
   d->dry = (cfg->flags & ATD_FLAG_DRY_RUN) != 0;
-  d->nsplit_max = (cfg->max_ctx + kAttnChunkSmall - 1) / kAttnChunkSmall;
   if (d->dry) {
     *out = d;
     return ATD_OK;
@@ -437,8 +460,12 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   const size_t o_q = carve((size_t)R * nq * 4);
   const size_t o_o = carve((size_t)R * nq * 4);
   const size_t o_act = carve((size_t)R * cfg->ffn * 4);
-  const size_t o_pml = carve((size_t)R * cfg->n_q_heads * d->nsplit_max * 2 * 4);
-  const size_t o_pacc = carve((size_t)R * cfg->n_q_heads * d->nsplit_max * D * 4);
+  // attention partials: M * Hq * attn_max_splits(L, M, Hkv) <= this many per head dim
+  d->part_floats = (size_t)cfg->n_q_heads *
+                   std::min((size_t)R * ((cfg->max_ctx + kAttnMinChunk - 1) / kAttnMinChunk),
+                            (size_t)(kAttnWavesMax / cfg->n_kv_heads + R));
+  const size_t o_pml = carve(d->part_floats * 2 * 4);
+  const size_t o_pacc = carve(d->part_floats * D * 4);
   const size_t o_kv = carve((size_t)S * cfg->n_layers * 2 * sizeof(void*));
   const size_t o_pos = carve((size_t)S * 4);
   const size_t o_cap = carve((size_t)S * 4);
@@ -554,6 +581,9 @@ extern "C" int kv_bucket_grow(atd_decoder* d, int32_t slot, void* const* k_new,
   if (e == hipSuccess && !d->dry)
     e = launch_set_slot(slots_of(d), slot, k_new, v_new, s_new, first ? 0 : -1, 1, s);
   if (e != hipSuccess) return hip_fail(d, e, "kv_bucket_grow");
+  // captured steps hold the slot's cache rows as kernel arguments: drop them
+  for (auto& ge : d->graphs) (void)hipGraphExecDestroy(ge.exec);
+  d->graphs.clear();
   for (int l = 0; l < c.n_layers; ++l) {
     d->kp[slot][l] = k_new[l];
     d->vp[slot][l] = v_new[l];

@@ -12,9 +12,37 @@ namespace atd {
 constexpr int kMaxTables = 16;
 constexpr int kMaxLayers = 64;
 constexpr int kGemvMaxRows = 2;      // rows a GEMV launch handles at once
-constexpr int kAttnChunkSmall = 128; // keys per attention split, <= 2 rows
-constexpr int kAttnChunkLarge = 256; // keys per attention split, > 2 rows
 constexpr int kArgmaxChunk = 4096;   // logits per argmax block
+constexpr int kAttnWavesMax = 2048;  // largest split-count target of a launch
+constexpr int kAttnMinChunk = 16;    // fewest keys per split
+
+#if defined(__HIP__)
+#define ATD_HD __host__ __device__
+#else
+#define ATD_HD
+#endif
+
+// Keys per attention split for a row whose valid length is len, in a launch
+// of M rows over Hkv KV heads aiming at `waves` splits in total: at least
+// kAttnMinChunk keys, a multiple of 16.  Depends on (len, M, Hkv, waves)
+// only, never on the cache capacity.
+inline ATD_HD int attn_splits_per_head(int M, int Hkv, int waves) {
+  const int per = waves / (M * Hkv);
+  return per < 1 ? 1 : per;
+}
+inline ATD_HD int attn_chunk(int len, int M, int Hkv, int waves) {
+  const int per = attn_splits_per_head(M, Hkv, waves);
+  int c = (len + per - 1) / per;
+  c = (c + 15) & ~15;
+  return c < kAttnMinChunk ? kAttnMinChunk : c;
+}
+
+// Upper bound of the split count of any row of length <= max_len.
+inline int attn_max_splits(int max_len, int M, int Hkv, int waves) {
+  const int a = (max_len + kAttnMinChunk - 1) / kAttnMinChunk;
+  const int b = attn_splits_per_head(M, Hkv, waves);
+  return a < b ? a : b;
+}
 
 // How the rows of a launch map to (slot, position):
 //  kRowsStep:    row m -> slot slot0 + m at that slot's current position
@@ -24,24 +52,6 @@ enum RowMode { kRowsStep = 0, kRowsPrefill = 1 };
 struct RowMap {
   int mode;
   int slot0;
-};
-
-// ---------------------------------------------------------------- GEMV
-enum GemvEpilogue { kEpiStore = 0, kEpiResidual = 1, kEpiSwiglu = 2 };
-
-struct GemvArgs {
-  const void* W[3];       // row segments [rows_s, K]; segment s ends at seg_end[s]
-  const float* bias[3];   // per-segment bias or null (kEpiStore only)
-  int seg_end[3];
-  const void* W2;         // up-projection [N, K] (kEpiSwiglu)
-  const float* x;         // input rows [M, ldx]
-  int ldx;
-  const float* gain;      // RMSNorm gain [K] when the input is normalised
-  float eps;
-  float* out;             // output rows [M, ldo]
-  int ldo;
-  float* y_out;           // normalised input rows [M, K] (block 0 writes), or null
-  int K, N, M;
 };
 
 // ---------------------------------------------------------------- rows/KV
@@ -65,11 +75,51 @@ struct RopeArgs {
   int layer, M, Hq, Hkv, D, qk_norm;
 };
 
+// ---------------------------------------------------------------- GEMV
+enum GemvEpilogue { kEpiStore = 0, kEpiResidual = 1, kEpiSwiglu = 2 };
+
+struct GemvArgs {
+  const void* W[3];       // row segments [rows_s, K]; segment s ends at seg_end[s]
+  const float* bias[3];   // per-segment bias or null (kEpiStore only)
+  int seg_end[3];
+  const void* W2;         // up-projection [N, K] (kEpiSwiglu)
+  const float* x;         // input rows [M, ldx]
+  int ldx;
+  const float* gain;      // RMSNorm gain [K] when the input is normalised
+  float eps;
+  float* out;             // output rows [M, ldo]
+  int ldo;
+  float* y_out;           // normalised input rows [M, K] (block 0 writes), or null
+  int K, N, M;
+};
+
+
+
+
+
 struct AttnArgs {
-  const float* q;     // [M, Hq, D]
+  // fused (decode steps): q and the new k/v row come raw from qkv and get the
+  // QK norm + RoPE here; the last split's wave appends the new row to the
+  // cache.  Otherwise (prefill) q is the rotated q_out and every row is
+  // already in the cache.
+  int fused;
+  const float* qkv;   // [M, (Hq + 2 Hkv) D] raw projections (fused)
+  const float* q_norm;
+  const float* k_norm;
+  int qk_norm;
+  float eps;
+  const float* cos_t; // [max_ctx, D/2]
+  const float* sin_t;
+  const float* q;     // [M, Hq, D] rotated queries (not fused)
   SlotTables st;
   RowMap rows;
-  int layer, M, Hq, Hkv, chunk, nsplit_max;
+  int layer, M, Hq, Hkv, nsplit_max;   // nsplit_max: split stride of the partials
+  int waves;                           // split-count target (attn_chunk)
+  // single-slot launches: the slot's cache rows of this layer and capacity,
+  // passed directly so no pointer table is read (null: use st)
+  void* k_direct;
+  void* v_direct;
+  int cap_direct;
   float scale;
   float* pml;         // [M, Hq, nsplit_max, 2] running max and sum
   float* pacc;        // [M, Hq, nsplit_max, D]

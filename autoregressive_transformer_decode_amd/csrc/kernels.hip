@@ -29,10 +29,39 @@ namespace atd {
 
 // ------------------------------------------------------------------ helpers
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+// Cross-lane moves through DPP (no LDS traffic).  Controls: quad_perm
+// [1,0,3,2] = xor 1, quad_perm [2,3,0,1] = xor 2, row_half_mirror pairs lane
+// i with 7-i of its 8-lane half row, row_mirror pairs i with 15-i of its
+// 16-lane row, row_ror:8 rotates a row by 8 lanes (= xor 8).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+              kDppRor8 = 0x128;
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8, 16, 32, 64), result in
+// every lane of the group.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp<kDppMirror>(v);
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (N >= 64) v += __shfl_xor(v, 32, 64);
   return v;
+}
+
+// Wave-wide sum, identical in every lane: rows of 16 by DPP, then the four
+// row sums read out and added in a fixed order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
@@ -73,6 +102,20 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// 16-byte load through the global address space (pointers taken from memory
+// are generic; a flat load would also count against the scalar-memory
+// counter and couple to unrelated scalar waits).
+typedef unsigned int V4U32 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(1))) const V4U32 GV4U32;
+  const V4U32 v = *(GV4U32*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+
 __device__ __forceinline__ void row_of(const RowMap& r, const SlotTables& st, int m,
                                        int& slot, int& pos) {
   if (r.mode == kRowsPrefill) {
@@ -105,178 +148,48 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   a.out[(size_t)m * a.h + i] = s;
 }
 
-// ------------------------------------------------------------------ GEMV
-// out[m, n] = epi( sum_k W[n, k] * xin[m, k] ),  xin = x or RMSNorm(x) * gain
-// One wave owns RPW consecutive rows and sweeps k with 16-byte loads per
-// lane; the (normalised) input rows sit in LDS.  MR input rows share every
-// weight load.
-template <typename WT, int MR, int RPW, int EPI, bool NORM>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
-  extern __shared__ float xs[];
-  __shared__ float red[4][MR];
-  constexpr int VEC = Vec16<WT>::N;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.K;
-
-  float ss[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    ss[m] = 0.f;
-    const float* xr = a.x + (size_t)m * a.ldx;
-    for (int i = tid * 4; i < K; i += 1024) {
-      float4 v = *reinterpret_cast<const float4*>(xr + i);
-      *reinterpret_cast<float4*>(xs + m * K + i) = v;
-      ss[m] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-  }
-  if constexpr (NORM) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      float v = wave_sum(ss[m]);
-      if (lane == 0) red[wave][m] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const float tot = red[0][m] + red[1][m] + red[2][m] + red[3][m];
-      const float inv = 1.0f / sqrtf(tot / (float)K + a.eps);
-      for (int i = tid * 4; i < K; i += 1024) {
-        float4 v = *reinterpret_cast<float4*>(xs + m * K + i);
-        const float4 g = *reinterpret_cast<const float4*>(a.gain + i);
-        v.x = v.x * inv * g.x;
-        v.y = v.y * inv * g.y;
-        v.z = v.z * inv * g.z;
-        v.w = v.w * inv * g.w;
-        *reinterpret_cast<float4*>(xs + m * K + i) = v;
-        if (a.y_out && blockIdx.x == 0)
-          *reinterpret_cast<float4*>(a.y_out + (size_t)m * K + i) = v;
-      }
-    }
-  }
-  __syncthreads();
-
-  const int row0 = (blockIdx.x * 4 + wave) * RPW;
-  if (row0 >= a.N) return;
-  const int s = row0 < a.seg_end[0] ? 0 : (row0 < a.seg_end[1] ? 1 : 2);
-  const int sbeg = s == 0 ? 0 : a.seg_end[s - 1];
-  const int nr = min(RPW, a.seg_end[s] - row0);
-  const WT* Wp = reinterpret_cast<const WT*>(a.W[s]) + (size_t)(row0 - sbeg) * K;
-  const WT* W2p = nullptr;
-  if constexpr (EPI == kEpiSwiglu) W2p = reinterpret_cast<const WT*>(a.W2) + (size_t)row0 * K;
-
-  float acc[RPW][MR], acc2[RPW][MR];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int m = 0; m < MR; ++m) acc[r][m] = acc2[r][m] = 0.f;
-
-#pragma unroll 2
-  for (int k = lane * VEC; k < K; k += 64 * VEC) {
-    uint4 w[RPW], w2[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      w[r] = r < nr ? ld16(Wp + (size_t)r * K + k) : make_uint4(0, 0, 0, 0);
-      if constexpr (EPI == kEpiSwiglu)
-        w2[r] = r < nr ? ld16(W2p + (size_t)r * K + k) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      float xv[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; e += 4) {
-        const float4 t = *reinterpret_cast<const float4*>(xs + m * K + k + e);
-        xv[e] = t.x;
-        xv[e + 1] = t.y;
-        xv[e + 2] = t.z;
-        xv[e + 3] = t.w;
-      }
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        float wf[VEC];
-        Vec16<WT>::unpack(w[r], wf);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[r][m] = fmaf(wf[e], xv[e], acc[r][m]);
-        if constexpr (EPI == kEpiSwiglu) {
-          Vec16<WT>::unpack(w2[r], wf);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc2[r][m] = fmaf(wf[e], xv[e], acc2[r][m]);
-        }
-      }
-    }
-  }
-
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      acc[r][m] = wave_sum(acc[r][m]);
-      if constexpr (EPI == kEpiSwiglu) acc2[r][m] = wave_sum(acc2[r][m]);
-    }
-
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      if (r >= nr) break;
-      const int row = row0 + r;
-#pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        float* o = a.out + (size_t)m * a.ldo + row;
-        const float v = acc[r][m];
-        if constexpr (EPI == kEpiStore) {
-          *o = a.bias[s] ? v + a.bias[s][row - sbeg] : v;
-        } else if constexpr (EPI == kEpiResidual) {
-          *o = *o + v;
-        } else {
-          *o = v / (1.0f + expf(-v)) * acc2[r][m];
-        }
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------ QK norm + RoPE + append
-// One block (D threads) per (row, head) of q, k and v.  q and k heads get
-// the optional per-head RMSNorm over D and rotate-half RoPE at the row's
-// position; q goes to q_out, k and v are stored into the cache row.
+// One (row m, head slot hh) of the raw projection: hh < Hq is a query head,
+// then Hkv key heads, then Hkv value heads.  q and k heads get the optional
+// per-head RMSNorm over D and rotate-half RoPE at the row's position; q goes
+// to q_out, k and v are stored (rounded for a bf16 cache) into the cache row.
+// Called by every thread of a block of >= D threads (uniform barriers);
+// threads t < D own one channel each.
 template <typename KT>
-__global__ __launch_bounds__(128) void k_rope_append(RopeArgs a) {
-  __shared__ float buf[128];
-  __shared__ float red[2];
-  const int hh = blockIdx.x, m = blockIdx.y, t = threadIdx.x;
-  const int D = a.D, half = D >> 1;
+__device__ __forceinline__ void rope_head(const RopeArgs& a, int m, int hh, float* buf,
+                                          float* red) {
+  const int t = threadIdx.x, D = a.D, half = D >> 1;
   int slot, pos;
   row_of(a.rows, a.st, m, slot, pos);
   const int ld = (a.Hq + 2 * a.Hkv) * D;
-  int kind, hd;
-  if (hh < a.Hq) {
-    kind = 0;
-    hd = hh;
-  } else if (hh < a.Hq + a.Hkv) {
-    kind = 1;
-    hd = hh - a.Hq;
-  } else {
-    kind = 2;
-    hd = hh - a.Hq - a.Hkv;
-  }
+  const int kind = hh < a.Hq ? 0 : (hh < a.Hq + a.Hkv ? 1 : 2);
+  const int hd = kind == 0 ? hh : (kind == 1 ? hh - a.Hq : hh - a.Hq - a.Hkv);
   const int col = (kind == 0 ? 0 : (kind == 1 ? a.Hq * D : (a.Hq + a.Hkv) * D)) + hd * D;
-  float v = a.qkv[(size_t)m * ld + col + t];
+  const bool own = t < D;
+  float v = own ? a.qkv[(size_t)m * ld + col + t] : 0.f;
   if (kind < 2 && a.qk_norm) {
-    float s2 = wave_sum(v * v);
+    const float s2 = wave_sum(v * v);
     if ((t & 63) == 0) red[t >> 6] = s2;
     __syncthreads();
-    const float tot = red[0] + (D > 64 ? red[1] : 0.f);
+    float tot = 0.f;
+    for (int w = 0; w < D / 64; ++w) tot += red[w];
     const float inv = 1.0f / sqrtf(tot / (float)D + a.eps);
-    v = v * inv * (kind == 0 ? a.q_norm[t] : a.k_norm[t]);
+    if (own) v = v * inv * (kind == 0 ? a.q_norm[t] : a.k_norm[t]);
+    __syncthreads();
   }
   if (kind < 2) {
-    buf[t] = v;
+    if (own) buf[t] = v;
     __syncthreads();
-    const int i = t < half ? t : t - half;
-    const float c = a.cos_t[(size_t)pos * half + i];
-    const float sn = a.sin_t[(size_t)pos * half + i];
-    const float x0 = buf[i], x1 = buf[i + half];
-    v = t < half ? x0 * c - x1 * sn : x1 * c + x0 * sn;
+    if (own) {
+      const int i = t < half ? t : t - half;
+      const float c = a.cos_t[(size_t)pos * half + i];
+      const float sn = a.sin_t[(size_t)pos * half + i];
+      const float x0 = buf[i], x1 = buf[i + half];
+      v = t < half ? x0 * c - x1 * sn : x1 * c + x0 * sn;
+    }
+    __syncthreads();
   }
+  if (!own) return;
   if (kind == 0) {
     a.q_out[((size_t)m * a.Hq + hd) * D + t] = v;
   } else {
@@ -290,100 +203,459 @@ __global__ __launch_bounds__(128) void k_rope_append(RopeArgs a) {
   }
 }
 
+// Standalone form: one block of D threads per (row, head slot).
+template <typename KT>
+__global__ __launch_bounds__(128) void k_rope_append(RopeArgs a) {
+  __shared__ float buf[128];
+  __shared__ float red[2];
+  rope_head<KT>(a, blockIdx.y, blockIdx.x, buf, red);
+}
+
+// ------------------------------------------------------------------ GEMV
+// out[m, n] = epi( sum_k W[n, k] * xin[m, k] ),  xin = x or RMSNorm(x) * gain
+//
+// A block of 4 waves owns 4 consecutive output rows.  The K dimension of the
+// block's rows is cut into KS slices: wave q takes slice q % KS of the
+// KS rows of its group (4 / KS groups per block).  Every lane streams KI
+// 16-byte chunks per row, so all 64 lanes of a wave read consecutive
+// addresses of a row and a whole slice is in flight at once.  The loads are
+// issued first (the weights do not depend on the activations); the lane's
+// slice of the input rows is then read straight into registers, normalised
+// with the sum of squares gathered in LDS, and multiplied; partial dots of
+// the KS slices meet in LDS and are added in a fixed order.  MR input rows
+// share every weight load.
+template <typename WT, int MR, int KS, int KI, int EPI, bool NORM>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+  constexpr int VEC = Vec16<WT>::N;
+  constexpr int NW = EPI == kEpiSwiglu ? 2 : 1;
+  constexpr int RW = KS;           // rows per wave group
+  constexpr int NG = 4 / KS;       // row groups per block
+  __shared__ float red_ss[4][MR];
+  __shared__ float red_acc[4][RW][MR][NW];
+  const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
+  const int ks = q % KS, grp = q / KS;
+  const int K = a.K, nk = K / VEC, ql = (nk + KS - 1) / KS;  // last slice may be short
+  const int row0 = blockIdx.x * 4 + grp * RW;
+  const bool active = row0 < a.N;
+  int s = 0, sbeg = 0, nr = 0;
+  const WT* Wp = nullptr;
+  const WT* W2p = nullptr;
+  if (active) {
+    s = row0 < a.seg_end[0] ? 0 : (row0 < a.seg_end[1] ? 1 : 2);
+    sbeg = s == 0 ? 0 : a.seg_end[s - 1];
+    nr = min(RW, a.seg_end[s] - row0);
+    Wp = reinterpret_cast<const WT*>(a.W[s]) + (size_t)(row0 - sbeg) * K;
+    if constexpr (EPI == kEpiSwiglu) W2p = reinterpret_cast<const WT*>(a.W2) + (size_t)row0 * K;
+  }
+  uint4 w[KI][RW][NW];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int cq = lane + 64 * i;
+    const int c = ks * ql + cq;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const bool ok = r < nr && cq < ql && c < nk;
+      w[i][r][0] = ok ? ld16(Wp + (size_t)r * K + (size_t)c * VEC) : make_uint4(0, 0, 0, 0);
+      if constexpr (NW == 2)
+        w[i][r][1] = ok ? ld16(W2p + (size_t)r * K + (size_t)c * VEC) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  float xv[MR][KI][VEC];
+  float ss[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    ss[m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int cq = lane + 64 * i;
+      const int c = ks * ql + cq;
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const float4 t = (cq < ql && c < nk) ? *reinterpret_cast<const float4*>(a.x + (size_t)m * a.ldx +
+                                                                    (size_t)c * VEC + e)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        xv[m][i][e] = t.x;
+        xv[m][i][e + 1] = t.y;
+        xv[m][i][e + 2] = t.z;
+        xv[m][i][e + 3] = t.w;
+        ss[m] += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+      }
+    }
+  }
+  if constexpr (NORM) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float v = wave_sum(ss[m]);
+      if (lane == 0) red_ss[q][m] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float tot = 0.f;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) tot += red_ss[grp * KS + j][m];
+      const float inv = 1.0f / sqrtf(tot / (float)K + a.eps);
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const int cq = lane + 64 * i;
+        const int c = ks * ql + cq;
+        if (cq < ql && c < nk) {
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4) {
+            const float4 g = *reinterpret_cast<const float4*>(a.gain + (size_t)c * VEC + e);
+            xv[m][i][e] = xv[m][i][e] * inv * g.x;
+            xv[m][i][e + 1] = xv[m][i][e + 1] * inv * g.y;
+            xv[m][i][e + 2] = xv[m][i][e + 2] * inv * g.z;
+            xv[m][i][e + 3] = xv[m][i][e + 3] * inv * g.w;
+            if (a.y_out && blockIdx.x == 0 && grp == 0)
+              *reinterpret_cast<float4*>(a.y_out + (size_t)m * K + (size_t)c * VEC + e) =
+                  make_float4(xv[m][i][e], xv[m][i][e + 1], xv[m][i][e + 2], xv[m][i][e + 3]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int t = 0; t < NW; ++t) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          float wf[VEC];
+          Vec16<WT>::unpack(w[i][r][t], wf);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc = fmaf(wf[e], xv[m][i][e], acc);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) red_acc[q][r][m][t] = acc;
+      }
+  __syncthreads();
+  // thread (g, r, m) of the first 4*MR threads finishes one output
+  if (tid < 4 * MR) {
+    const int m = tid / 4, rr = tid % 4, g = rr / RW, r = rr % RW;
+    const int row = blockIdx.x * 4 + rr;
+    const int gs = row < a.seg_end[0] ? 0 : (row < a.seg_end[1] ? 1 : 2);
+    const int gbeg = gs == 0 ? 0 : a.seg_end[gs - 1];
+    if (row < a.N) {
+      float v[NW];
+#pragma unroll
+      for (int t = 0; t < NW; ++t) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) acc += red_acc[g * KS + j][r][m][t];
+        v[t] = acc;
+      }
+      float* o = a.out + (size_t)m * a.ldo + row;
+      if constexpr (EPI == kEpiStore) {
+        *o = a.bias[gs] ? v[0] + a.bias[gs][row - gbeg] : v[0];
+      } else if constexpr (EPI == kEpiResidual) {
+        *o = *o + v[0];
+      } else {
+        *o = v[0] / (1.0f + expf(-v[0])) * v[NW - 1];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ attention
-// Split-K decode attention.  Block (split, kv head g, row m) covers keys
-// [split*chunk, min(len, (split+1)*chunk)) for the R query heads that share
-// KV head g.  A key row of D elements is read by LPK lanes with 16-byte
-// loads; a wave covers KPW keys per load.  Each lane group keeps an online
-// softmax state (max, sum, weighted V) that is merged across groups, waves
-// and (in k_attn_combine) splits, always in the same order.
+// Split-K decode attention, one split per wave.  Block (split group, kv head
+// g, row m); wave w takes split 4*blockIdx.x + w of the row's key range
+// (attn_chunk keys each, from its valid length) for the R query heads that
+// share KV head g.  A key row of D elements is read by LPK lanes with
+// 16-byte loads, so a wave covers KPW keys per load; U key groups are in
+// flight per iteration.  Each lane group keeps an online softmax state
+// (max, sum, weighted V); groups are merged with shuffles in a fixed order and
+// the split's state is written for k_attn_combine.
+//
+// Fused mode (decode steps): the wave applies the QK norm and RoPE to its raw
+// queries itself, and the wave of the row's last split builds the new k/v
+// row (norm, RoPE, rounding to the cache dtype), stores it at the row's
+// position and uses those register values for that key.  Only that wave
+// touches the new row, so no other synchronisation is needed.
+// Per-head RMSNorm (optional) + rotate-half RoPE of a head vector spread over
+// the LPK lanes of a group, VEC channels [dl, dl+VEC) per lane.
+template <int D, int VEC, int LPK>
+__device__ __forceinline__ void norm_rope_lanes(float (&v)[VEC], int dl, bool do_norm,
+                                                const float* gain, float eps, int pos,
+                                                const float* cos_t, const float* sin_t) {
+  constexpr int half = D / 2;
+  static_assert(VEC % 4 == 0, "channels per lane come in float4 groups");
+  if (do_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ss += v[e] * v[e];
+    ss = group_sum<LPK>(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4) {
+      const float4 g = *reinterpret_cast<const float4*>(gain + dl + e);
+      v[e] = v[e] * inv * g.x;
+      v[e + 1] = v[e + 1] * inv * g.y;
+      v[e + 2] = v[e + 2] * inv * g.z;
+      v[e + 3] = v[e + 3] * inv * g.w;
+    }
+  }
+  const bool lo = dl < half;
+  const float* cp = cos_t + (size_t)pos * half + (dl % half);   // channels dl.. pair with dl%half..
+  const float* sp = sin_t + (size_t)pos * half + (dl % half);
+#pragma unroll
+  for (int e = 0; e < VEC; e += 4) {
+    const float4 c4 = *reinterpret_cast<const float4*>(cp + e);
+    const float4 s4 = *reinterpret_cast<const float4*>(sp + e);
+    const float c[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float other = __shfl_xor(v[e + t], LPK / 2, 64);  // channel dl+e+t -/+ D/2
+      v[e + t] = lo ? v[e + t] * c[t] - other * sn[t] : v[e + t] * c[t] + other * sn[t];
+    }
+  }
+}
+
+template <typename KT, int VEC>
+__device__ __forceinline__ uint4 pack_kv(const float (&v)[VEC]) {
+  uint4 r;
+  if constexpr (sizeof(KT) == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    r = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    r = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                   __float_as_uint(v[3]));
+  }
+  return r;
+}
+
 template <typename KT, int D, int R>
 __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
-  constexpr int VEC = Vec16<KT>::N;
-  constexpr int LPK = D / VEC;
-  constexpr int KPW = 64 / LPK;
-  constexpr int U = 2;
-  __shared__ float sm[4][R], sl[4][R];
-  __shared__ float sacc[4][R][D];
+  constexpr int VEC = Vec16<KT>::N;   // channels per 16-byte load
+  constexpr int LPK = 8;              // lanes per key row
+  constexpr int DPL = D / LPK;        // channels per lane
+  constexpr int NV = DPL / VEC;       // 16-byte loads per lane per row
+  constexpr int KPW = 64 / LPK;       // key rows per wave-wide load
+  constexpr int U = 2;                // key rows per lane group per tile
+  constexpr int TILE = KPW * U;       // keys per wave per tile
 
-  const int split = blockIdx.x, g = blockIdx.y, m = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x * 4 + wave, g = blockIdx.y, m = blockIdx.z;
+  const int sub = lane / LPK, dl = (lane % LPK) * DPL;
+  const int ldq = (a.Hq + 2 * a.Hkv) * D;
+  // the raw query rows do not depend on the position: load them with it
+  float qv[R][DPL];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int h = g * R + j;
+    const float* qp = a.fused ? a.qkv + (size_t)m * ldq + (size_t)h * D + dl
+                              : a.q + ((size_t)m * a.Hq + h) * D + dl;
+#pragma unroll
+    for (int e = 0; e < DPL; e += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(qp + e);
+      qv[j][e] = t.x;
+      qv[j][e + 1] = t.y;
+      qv[j][e + 2] = t.z;
+      qv[j][e + 3] = t.w;
+    }
+  }
   int slot, pos;
   row_of(a.rows, a.st, m, slot, pos);
   const int len = pos + 1;
-  const int k0 = split * a.chunk;
+  const int chunk = attn_chunk(len, a.M, a.Hkv, a.waves);
+  const int k0 = split * chunk;
   if (k0 >= len) return;
-  const int k1 = min(len, k0 + a.chunk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane / LPK, dl = (lane % LPK) * VEC;
-  const int cap = a.st.cap[slot];
-  void* const* kvp = a.st.kv + ((size_t)slot * a.st.L + a.layer) * 2;
-  const KT* Kb = reinterpret_cast<const KT*>(kvp[0]) + (size_t)g * cap * D + dl;
-  const KT* Vb = reinterpret_cast<const KT*>(kvp[1]) + (size_t)g * cap * D + dl;
+  const int k1 = min(len, k0 + chunk);
+  const bool owns_new = a.fused && k1 == len;
 
-  float qv[R][VEC];
+  // position-dependent small loads first (RoPE table, gains, the new row),
+  // then the cache rows: the in-order memory counter lets the query math
+  // start before the rows arrive
+  const int half = D / 2;
+  const float* cp = a.cos_t + (size_t)pos * half + (dl % half);
+  const float* sp = a.sin_t + (size_t)pos * half + (dl % half);
+  float4 cs[DPL / 4], sn[DPL / 4];
+  if (a.fused) {
+#pragma unroll
+    for (int e = 0; e < DPL / 4; ++e) {
+      cs[e] = *reinterpret_cast<const float4*>(cp + 4 * e);
+      sn[e] = *reinterpret_cast<const float4*>(sp + 4 * e);
+    }
+  }
+  float kf[DPL], vf[DPL];
+  if (owns_new) {
+    const float* kp = a.qkv + (size_t)m * ldq + (size_t)(a.Hq + g) * D + dl;
+    const float* vp = a.qkv + (size_t)m * ldq + (size_t)(a.Hq + a.Hkv + g) * D + dl;
+#pragma unroll
+    for (int e = 0; e < DPL; e += 4) {
+      const float4 tk = *reinterpret_cast<const float4*>(kp + e);
+      const float4 tv = *reinterpret_cast<const float4*>(vp + e);
+      kf[e] = tk.x; kf[e + 1] = tk.y; kf[e + 2] = tk.z; kf[e + 3] = tk.w;
+      vf[e] = tv.x; vf[e + 1] = tv.y; vf[e + 2] = tv.z; vf[e + 3] = tv.w;
+    }
+  }
+
+  int cap;
+  const KT *Kh, *Vh;
+  if (a.k_direct) {
+    cap = a.cap_direct;
+    Kh = reinterpret_cast<const KT*>(a.k_direct);
+    Vh = reinterpret_cast<const KT*>(a.v_direct);
+  } else {
+    cap = a.st.cap[slot];
+    void* const* kvp = a.st.kv + ((size_t)slot * a.st.L + a.layer) * 2;
+    Kh = reinterpret_cast<const KT*>(kvp[0]);
+    Vh = reinterpret_cast<const KT*>(kvp[1]);
+  }
+  Kh += (size_t)g * cap * D + dl;
+  Vh += (size_t)g * cap * D + dl;
+
+  // keys past the split end are clamped to its last key (always in bounds)
+  // and masked out in the softmax
+  uint4 kr[U][NV], vr[U][NV];
+  auto load = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int key = min(kb + u * KPW + sub, k1 - 1);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        kr[u][v] = ldg16(Kh + (size_t)key * D + v * VEC);
+        vr[u][v] = ldg16(Vh + (size_t)key * D + v * VEC);
+      }
+    }
+  };
+  load(k0);
+
+  auto rope = [&](float (&x)[DPL], const float* gain) {
+    if (a.qk_norm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ss += x[e] * x[e];
+      ss = group_sum<LPK>(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+      for (int e = 0; e < DPL; e += 4) {
+        const float4 gg = *reinterpret_cast<const float4*>(gain + dl + e);
+        x[e] = x[e] * inv * gg.x;
+        x[e + 1] = x[e + 1] * inv * gg.y;
+        x[e + 2] = x[e + 2] * inv * gg.z;
+        x[e + 3] = x[e + 3] * inv * gg.w;
+      }
+    }
+    const bool lo = dl < half;
+#pragma unroll
+    for (int e = 0; e < DPL / 4; ++e) {
+      const float c[4] = {cs[e].x, cs[e].y, cs[e].z, cs[e].w};
+      const float si[4] = {sn[e].x, sn[e].y, sn[e].z, sn[e].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float other = __shfl_xor(x[4 * e + t], LPK / 2, 64);   // channel -/+ D/2
+        x[4 * e + t] = lo ? x[4 * e + t] * c[t] - other * si[t] : x[4 * e + t] * c[t] + other * si[t];
+      }
+    }
+  };
+
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    const float* qp = a.q + ((size_t)m * a.Hq + g * R + j) * D + dl;
+    if (a.fused) rope(qv[j], a.q_norm);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) qv[j][e] = qp[e] * a.scale;
+    for (int e = 0; e < DPL; ++e) qv[j][e] *= a.scale;
   }
-  float mx[R], ls[R], acc[R][VEC];
+
+  // the new row of a fused step, built in registers by the last split's wave
+  uint4 knew[NV], vnew[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) knew[v] = vnew[v] = make_uint4(0, 0, 0, 0);
+  if (owns_new) {
+    rope(kf, a.k_norm);
+    KT* Kw = const_cast<KT*>(Kh) + (size_t)pos * D;
+    KT* Vw = const_cast<KT*>(Vh) + (size_t)pos * D;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      float t[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) t[e] = kf[v * VEC + e];
+      knew[v] = pack_kv<KT, VEC>(t);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) t[e] = vf[v * VEC + e];
+      vnew[v] = pack_kv<KT, VEC>(t);
+      if (sub == 0) {
+        *reinterpret_cast<uint4*>(Kw + v * VEC) = knew[v];
+        *reinterpret_cast<uint4*>(Vw + v * VEC) = vnew[v];
+      }
+    }
+  }
+
+  float mx[R], ls[R], acc[R][DPL];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     mx[j] = -1e30f;
     ls[j] = 0.f;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[j][e] = 0.f;
+    for (int e = 0; e < DPL; ++e) acc[j][e] = 0.f;
   }
 
-  for (int kb = k0 + wave * KPW * U; kb < k1; kb += 4 * KPW * U) {
-    uint4 kr[U], vr[U];
+  for (int kb = k0; kb < k1; kb += TILE) {
+    float kt[U][DPL], vt[U][DPL];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int key = kb + u * KPW + sub;
       ok[u] = key < k1;
-      kr[u] = ok[u] ? ld16(Kb + (size_t)key * D) : make_uint4(0, 0, 0, 0);
-      vr[u] = ok[u] ? ld16(Vb + (size_t)key * D) : make_uint4(0, 0, 0, 0);
-    }
+      const bool fresh = owns_new && key == pos;   // the cache row may not be written yet
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float kf[VEC], vf[VEC];
-      Vec16<KT>::unpack(kr[u], kf);
-      Vec16<KT>::unpack(vr[u], vf);
-#pragma unroll
-      for (int j = 0; j < R; ++j) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) s = fmaf(qv[j][e], kf[e], s);
-#pragma unroll
-        for (int off = LPK >> 1; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-        if (ok[u]) {
-          const float nm = fmaxf(mx[j], s);
-          const float c = expf(mx[j] - nm);
-          const float p = expf(s - nm);
-          ls[j] = ls[j] * c + p;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[j][e] = fmaf(acc[j][e], c, p * vf[e]);
-          mx[j] = nm;
-        }
+      for (int v = 0; v < NV; ++v) {
+        Vec16<KT>::unpack(fresh ? knew[v] : kr[u][v], &kt[u][v * VEC]);
+        Vec16<KT>::unpack(fresh ? vnew[v] : vr[u][v], &vt[u][v * VEC]);
       }
+    }
+    if (kb + TILE < k1) load(kb + TILE);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      float sc[U];
+      float tmax = mx[j];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) d = fmaf(qv[j][e], kt[u][e], d);
+        sc[u] = group_sum<LPK>(d);
+        if (ok[u]) tmax = fmaxf(tmax, sc[u]);
+      }
+      // one rescale per tile
+      const float c = expf(mx[j] - tmax);
+      ls[j] *= c;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[j][e] *= c;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = ok[u] ? expf(sc[u] - tmax) : 0.f;
+        ls[j] += p;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[j][e] = fmaf(p, vt[u][e], acc[j][e]);
+      }
+      mx[j] = tmax;
     }
   }
 
-  // merge the KPW key groups of the wave (lanes with equal dl)
+  // merge the KPW key groups of the wave (lanes with equal dl): xor 8 by DPP,
+  // xor 16 and 32 across rows
 #pragma unroll
-  for (int off = LPK; off < 64; off <<= 1) {
+  for (int step = 0; step < 3; ++step) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      const float om = __shfl_xor(mx[j], off, 64);
-      const float ol = __shfl_xor(ls[j], off, 64);
+      auto xch = [&](float v) {
+        return step == 0 ? dpp<kDppRor8>(v) : __shfl_xor(v, step == 1 ? 16 : 32, 64);
+      };
+      const float om = xch(mx[j]);
+      const float ol = xch(ls[j]);
       const float nm = fmaxf(mx[j], om);
       const float ca = expf(mx[j] - nm), cb = expf(om - nm);
       ls[j] = ls[j] * ca + ol * cb;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float oa = __shfl_xor(acc[j][e], off, 64);
+      for (int e = 0; e < DPL; ++e) {
+        const float oa = xch(acc[j][e]);
         acc[j][e] = acc[j][e] * ca + oa * cb;
       }
       mx[j] = nm;
@@ -392,54 +664,106 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   if (lane < LPK) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
+      const size_t base = ((size_t)m * a.Hq + g * R + j) * a.nsplit_max + split;
+#pragma unroll
+      for (int e = 0; e < DPL; e += 4)
+        *reinterpret_cast<float4*>(a.pacc + base * D + dl + e) =
+            make_float4(acc[j][e], acc[j][e + 1], acc[j][e + 2], acc[j][e + 3]);
       if (lane == 0) {
-        sm[wave][j] = mx[j];
-        sl[wave][j] = ls[j];
+        a.pml[base * 2] = mx[j];
+        a.pml[base * 2 + 1] = ls[j];
       }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sacc[wave][j][dl + e] = acc[j][e];
-    }
-  }
-  __syncthreads();
-  // merge the 4 waves in order and write this split's partial state
-  for (int idx = tid; idx < R * D; idx += 256) {
-    const int j = idx / D, d = idx % D;
-    float M = sm[0][j];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w][j]);
-    float l = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float c = expf(sm[w][j] - M);
-      l += sl[w][j] * c;
-      o += sacc[w][j][d] * c;
-    }
-    const size_t base = ((size_t)m * a.Hq + g * R + j) * a.nsplit_max + split;
-    a.pacc[base * D + d] = o;
-    if (d == 0) {
-      a.pml[base * 2] = M;
-      a.pml[base * 2 + 1] = l;
     }
   }
 }
 
-// o[m, h*D + d] = sum_s acc_s[d] e^(m_s - M) / sum_s l_s e^(m_s - M)
+// o[m, h*D + d] = sum_s acc_s[d] e^(m_s - M) / sum_s l_s e^(m_s - M).
+// One block per (head, row).  The split weights are formed once in LDS;
+// thread t accumulates the float4 channel group t % (D/4) over splits
+// t / (D/4), t / (D/4) + NSP, ... (independent loads), and the NSP partial
+// sums are added in a fixed order.
 template <int D>
-__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
-  const int h = blockIdx.x, m = blockIdx.y, t = threadIdx.x;
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
+  constexpr int NC = D / 4;        // float4 channel groups
+  constexpr int NSP = 256 / NC;    // split phases
+  constexpr int PRE = 4;           // partials per thread loaded ahead of the position
+  __shared__ float wgt[kAttnWavesMax + 1];
+  __shared__ float red[2][4];
+  __shared__ float4 part[NSP][NC];
+  const int h = blockIdx.x, m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t base = ((size_t)m * a.Hq + h) * a.nsplit_max;
+  const int c = tid % NC, sp = tid / NC;
+  const float4* pa = reinterpret_cast<const float4*>(a.pacc) + base * NC + c;
+  // the first partials and statistics are read together with the position
+  float4 pre[PRE];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    const int s = sp + i * NSP;
+    pre[i] = s < a.nsplit_max ? pa[(size_t)s * NC] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float m0 = tid < a.nsplit_max ? a.pml[(base + tid) * 2] : -1e30f;
+  const float l0 = tid < a.nsplit_max ? a.pml[(base + tid) * 2 + 1] : 0.f;
   int slot, pos;
   row_of(a.rows, a.st, m, slot, pos);
-  const int ns = (pos + 1 + a.chunk - 1) / a.chunk;
-  const size_t base = ((size_t)m * a.Hq + h) * a.nsplit_max;
-  float M = -1e30f;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.pml[(base + s) * 2]);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float c = expf(a.pml[(base + s) * 2] - M);
-    l += a.pml[(base + s) * 2 + 1] * c;
-    o += a.pacc[(base + s) * D + t] * c;
+  const int len = pos + 1;
+  const int chunk = attn_chunk(len, a.M, a.Hkv, a.waves);
+  const int ns = (len + chunk - 1) / chunk;
+  float mloc = tid < ns ? m0 : -1e30f;
+  for (int s = tid + 256; s < ns; s += 256) mloc = fmaxf(mloc, a.pml[(base + s) * 2]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
+  if (lane == 0) red[0][wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  float lloc = 0.f;
+  if (tid < ns) {
+    const float w = expf(m0 - M);
+    wgt[tid] = w;
+    lloc = l0 * w;
   }
-  a.o[((size_t)m * a.Hq + h) * D + t] = o / l;
+  for (int s = tid + 256; s < ns; s += 256) {
+    const float w = expf(a.pml[(base + s) * 2] - M);
+    wgt[s] = w;
+    lloc += a.pml[(base + s) * 2 + 1] * w;
+  }
+  lloc = wave_sum(lloc);
+  if (lane == 0) red[1][wave] = lloc;
+  __syncthreads();
+  const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    const int s = sp + i * NSP;
+    if (s < ns) {
+      const float w = wgt[s];
+      o.x = fmaf(pre[i].x, w, o.x);
+      o.y = fmaf(pre[i].y, w, o.y);
+      o.z = fmaf(pre[i].z, w, o.z);
+      o.w = fmaf(pre[i].w, w, o.w);
+    }
+  }
+#pragma unroll 4
+  for (int s = sp + PRE * NSP; s < ns; s += NSP) {
+    const float4 v = pa[(size_t)s * NC];
+    const float w = wgt[s];
+    o.x = fmaf(v.x, w, o.x);
+    o.y = fmaf(v.y, w, o.y);
+    o.z = fmaf(v.z, w, o.z);
+    o.w = fmaf(v.w, w, o.w);
+  }
+  part[sp][c] = o;
+  __syncthreads();
+  if (tid < NC) {
+    float4 r = part[0][c];
+    for (int p = 1; p < NSP; ++p) {
+      r.x += part[p][c].x;
+      r.y += part[p][c].y;
+      r.z += part[p][c].z;
+      r.w += part[p][c].w;
+    }
+    float4* out = reinterpret_cast<float4*>(a.o + ((size_t)m * a.Hq + h) * D) + c;
+    *out = make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
+  }
 }
 
 // ------------------------------------------------------------------ slot bookkeeping
@@ -586,18 +910,34 @@ hipError_t launch_embed(const EmbedArgs& a, int bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
+// K slices per block and 16-byte chunks per lane per slice, from K.
+// (nk <= 1024 is guaranteed by the config limits, so ki <= 4.)
+static void gemv_shape(int K, int vec, int& ks, int& ki) {
+  const int nk = K / vec;
+  ks = nk >= 256 ? 4 : (nk >= 128 ? 2 : 1);
+  ki = ((nk + ks - 1) / ks + 63) / 64;
+}
+
 template <typename WT, int MR, int EPI, bool NORM>
-static void gemv_dispatch_rpw(const GemvArgs& a, hipStream_t s) {
-  // rows per wave: as many as keep >= 512 workgroups in flight
-  const int n = a.N;
-  const size_t lds = (size_t)MR * a.K * sizeof(float);
-  if ((n + 15) / 16 >= 512) {
-    hipLaunchKernelGGL((k_gemv<WT, MR, 4, EPI, NORM>), dim3((n + 15) / 16), dim3(256), lds, s, a);
-  } else if ((n + 7) / 8 >= 512) {
-    hipLaunchKernelGGL((k_gemv<WT, MR, 2, EPI, NORM>), dim3((n + 7) / 8), dim3(256), lds, s, a);
+static void gemv_dispatch_shape(const GemvArgs& a, hipStream_t s) {
+  int ks, ki;
+  gemv_shape(a.K, Vec16<WT>::N, ks, ki);
+  const dim3 grid((a.N + 3) / 4), block(256);
+#define ATD_GEMV(KS_, KI_) \
+  hipLaunchKernelGGL((k_gemv<WT, MR, KS_, KI_, EPI, NORM>), grid, block, 0, s, a)
+  if (ks == 4) {
+    switch (ki) {
+      case 1: ATD_GEMV(4, 1); break;
+      case 2: ATD_GEMV(4, 2); break;
+      case 3: ATD_GEMV(4, 3); break;
+      default: ATD_GEMV(4, 4); break;
+    }
+  } else if (ks == 2) {
+    if (ki == 1) ATD_GEMV(2, 1); else ATD_GEMV(2, 2);
   } else {
-    hipLaunchKernelGGL((k_gemv<WT, MR, 1, EPI, NORM>), dim3((n + 3) / 4), dim3(256), lds, s, a);
+    if (ki == 1) ATD_GEMV(1, 1); else ATD_GEMV(1, 2);
   }
+#undef ATD_GEMV
 }
 
 template <typename WT, int EPI, bool NORM>
@@ -609,9 +949,9 @@ static void gemv_dispatch_mr(const GemvArgs& a, hipStream_t s) {
     b.out = a.out + (size_t)c * a.ldo;
     b.y_out = a.y_out ? a.y_out + (size_t)c * a.K : nullptr;
     if (b.M == 2)
-      gemv_dispatch_rpw<WT, 2, EPI, NORM>(b, s);
+      gemv_dispatch_shape<WT, 2, EPI, NORM>(b, s);
     else
-      gemv_dispatch_rpw<WT, 1, EPI, NORM>(b, s);
+      gemv_dispatch_shape<WT, 1, EPI, NORM>(b, s);
   }
 }
 
@@ -655,7 +995,7 @@ static void attn_dispatch_r(const AttnArgs& a, int r, dim3 grid, hipStream_t s) 
 }
 
 hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream_t s) {
-  dim3 grid(a.nsplit_max, a.Hkv, a.M);
+  dim3 grid((a.nsplit_max + 3) / 4, a.Hkv, a.M);
   if (bf16) {
     if (D == 64)
       attn_dispatch_r<uint16_t, 64>(a, r, grid, s);
@@ -669,9 +1009,9 @@ hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream
   }
   dim3 cgrid(a.Hq, a.M);
   if (D == 64)
-    hipLaunchKernelGGL(k_attn_combine<64>, cgrid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_attn_combine<64>, cgrid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

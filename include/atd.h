@@ -74,11 +74,11 @@ enum { ATD_F32 = 0, ATD_BF16 = 1 };
 /* Shape of one decoder stack (hyper-parameters; host struct). */
 typedef struct atd_config {
   int32_t n_layers;    /* L >= 1                                             */
-  int32_t hidden;      /* h, multiple of 8, <= 8192                          */
+  int32_t hidden;      /* h, multiple of 8, <= 8192 (<= 4096 for F32)       */
   int32_t n_q_heads;   /* Hq                                                 */
   int32_t n_kv_heads;  /* Hkv; Hq / Hkv in {1, 2, 4, 8}                      */
   int32_t head_dim;    /* D in {64, 128}                                     */
-  int32_t ffn;         /* F, multiple of 8, <= 8192                          */
+  int32_t ffn;         /* F, multiple of 8, <= 8192 (<= 4096 for F32)       */
   int32_t vocab;       /* V of every LM head, >= 2                           */
   int32_t n_lm_heads;  /* number of LM heads (15 for the code predictor)     */
   int32_t n_tables;    /* number of embedding tables, 1..16                  */
@@ -242,8 +242,10 @@ int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* t
 /* Stages of a decode step, for decoder_profile_stage. */
 enum {
   ATD_STAGE_QKV = 0,     /* RMSNorm + q/k/v projection                       */
-  ATD_STAGE_ROPE = 1,    /* QK norm + RoPE + cache append                     */
-  ATD_STAGE_ATTN = 2,    /* split-K attention + combine                       */
+  ATD_STAGE_ROPE = 1,    /* QK norm + RoPE + cache append of a prefill block  */
+  ATD_STAGE_ATTN = 2,    /* split-K attention + combine (for decode steps it
+                            also applies the QK norm + RoPE and appends the
+                            new cache row)                                   */
   ATD_STAGE_OPROJ = 3,   /* output projection + residual                      */
   ATD_STAGE_GATEUP = 4,  /* RMSNorm + gate/up projection + SwiGLU             */
   ATD_STAGE_DOWN = 5,    /* down projection + residual                        */

@@ -9,6 +9,12 @@ from __future__ import annotations
 import ctypes as C
 import os
 
+# One HIP runtime per process: torch ships its own libamdhip64 with the same
+# soname as the system one.  Loading torch first makes the library bind to the
+# runtime that torch's allocator and streams live in; loading the library
+# first would bring in a second runtime.
+import torch  # noqa: F401  (imported for its HIP runtime)
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libatd.so")
 
@@ -30,7 +36,7 @@ STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FU
 EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
            "decoder_step", "decoder_embed", "greedy_argmax", "decoder_generate",
-           "decoder_profile_stage", "decoder_profile_result")
+           "decoder_time_stage")
 
 ATD_STAGE_QKV, ATD_STAGE_ROPE, ATD_STAGE_ATTN, ATD_STAGE_OPROJ, ATD_STAGE_GATEUP, \
     ATD_STAGE_DOWN, ATD_STAGE_HEAD = range(7)
@@ -85,8 +91,7 @@ def _load():
         "greedy_argmax": ([vp, i32, i32, vp, f32, vp, vp, vp], C.c_int),
         "decoder_generate": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, f32, vp, vp,
                               vp, vp], C.c_int),
-        "decoder_profile_stage": ([vp, i32, i32], C.c_int),
-        "decoder_profile_result": ([vp, C.POINTER(C.c_double), C.POINTER(C.c_int64)], C.c_int),
+        "decoder_time_stage": ([vp, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -175,11 +180,7 @@ def decoder_generate(handle: int, slot: int, n_steps: int, tok_io: int, G: int, 
                                 stream), handle)
 
 
-def decoder_profile_stage(handle: int, stage: int, enable: int) -> None:
-    _check(lib.decoder_profile_stage(handle, stage, enable), handle)
-
-
-def decoder_profile_result(handle: int):
-    ms, n = C.c_double(), C.c_int64()
-    _check(lib.decoder_profile_result(handle, C.byref(ms), C.byref(n)), handle)
-    return ms.value, n.value
+def decoder_time_stage(handle: int, stage: int, slot: int, reps: int, stream: int) -> float:
+    us = C.c_double()
+    _check(lib.decoder_time_stage(handle, stage, slot, reps, stream, C.byref(us)), handle)
+    return us.value

@@ -40,11 +40,8 @@ struct atd_decoder {
   int32_t* counter = nullptr;  // token counter of decoder_generate
   size_t part_floats = 0;      // capacity of pacc in floats / D
   bool dry = false;  // ATD_FLAG_DRY_RUN: host state only, no HIP calls
-  // stage timing (decoder_profile_stage)
-  int probe_stage = -1;
-  bool capturing = false;
-  std::vector<hipEvent_t> probe_ev;  // start/stop pairs
-  size_t probe_used = 0;
+  // stage timing (decoder_time_stage): layers to enqueue, -1 = all
+  int only_stage = -1;
   // graph cache of decoder_generate
   hipStream_t cap_stream = nullptr;
   struct GraphEntry {
@@ -204,23 +201,11 @@ SlotTables slots_of(const atd_decoder* d) {
 // KV stream over the chip, few enough that each split carries real work.
 int attn_waves(int M) { return M <= 4 ? 512 : kAttnWavesMax; }
 
-// Event pair around one launch of the profiled stage (eager calls only).
-hipError_t probe_mark(atd_decoder* d, int stage, hipStream_t s) {
-  if (d->probe_stage != stage || d->capturing) return hipSuccess;
-  if (d->probe_used == d->probe_ev.size()) {
-    hipEvent_t e;
-    hipError_t r = hipEventCreate(&e);
-    if (r != hipSuccess) return r;
-    d->probe_ev.push_back(e);
-  }
-  return hipEventRecord(d->probe_ev[d->probe_used++], s);
-}
-
-#define PROBED(stage, call)                                        \
-  do {                                                             \
-    if ((e = probe_mark(d, stage, s)) != hipSuccess) return e;     \
-    if ((e = (call)) != hipSuccess) return e;                      \
-    if ((e = probe_mark(d, stage, s)) != hipSuccess) return e;     \
+// Launch a stage unless decoder_time_stage restricts the sequence to another.
+#define STAGE(stage, call)                                              \
+  do {                                                                  \
+    if (d->only_stage < 0 || d->only_stage == (stage))                  \
+      if ((e = (call)) != hipSuccess) return e;                         \
   } while (0)
 
 // The per-layer launch sequence for M rows (decode step or prefill block).
@@ -255,7 +240,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     g.K = h;
     g.N = nqkv;
     g.M = M;
-    PROBED(ATD_STAGE_QKV, launch_gemv(g, kEpiStore, true, bf16, s));
+    STAGE(ATD_STAGE_QKV, launch_gemv(g, kEpiStore, true, bf16, s));
 
     const bool fused = rows.mode == kRowsStep;
     if (!fused) {
@@ -276,7 +261,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
       r.Hkv = Hkv;
       r.D = D;
       r.qk_norm = c.qk_norm;
-      PROBED(ATD_STAGE_ROPE, launch_rope_append(r, kv_bf16, s));
+      STAGE(ATD_STAGE_ROPE, launch_rope_append(r, kv_bf16, s));
     }
 
     AttnArgs a{};
@@ -306,7 +291,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     a.pml = d->pml;
     a.pacc = d->pacc;
     a.o = d->o;
-    PROBED(ATD_STAGE_ATTN, launch_attention(a, kv_bf16, D, Hq / Hkv, s));
+    STAGE(ATD_STAGE_ATTN, launch_attention(a, kv_bf16, D, Hq / Hkv, s));
 
     GemvArgs op{};
     op.W[0] = W.wo;
@@ -318,7 +303,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     op.K = nq;
     op.N = h;
     op.M = M;
-    PROBED(ATD_STAGE_OPROJ, launch_gemv(op, kEpiResidual, false, bf16, s));
+    STAGE(ATD_STAGE_OPROJ, launch_gemv(op, kEpiResidual, false, bf16, s));
 
     GemvArgs gu{};
     gu.W[0] = W.w_gate;
@@ -333,7 +318,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     gu.K = h;
     gu.N = c.ffn;
     gu.M = M;
-    PROBED(ATD_STAGE_GATEUP, launch_gemv(gu, kEpiSwiglu, true, bf16, s));
+    STAGE(ATD_STAGE_GATEUP, launch_gemv(gu, kEpiSwiglu, true, bf16, s));
 
     GemvArgs dn{};
     dn.W[0] = W.w_down;
@@ -345,7 +330,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     dn.K = c.ffn;
     dn.N = h;
     dn.M = M;
-    PROBED(ATD_STAGE_DOWN, launch_gemv(dn, kEpiResidual, false, bf16, s));
+    STAGE(ATD_STAGE_DOWN, launch_gemv(dn, kEpiResidual, false, bf16, s));
   }
   return e;
 }
@@ -367,7 +352,7 @@ hipError_t run_head(atd_decoder* d, const float* xrows, int M, int head, float* 
   g.N = c.vocab;
   g.M = M;
   hipError_t e = hipSuccess;
-  PROBED(ATD_STAGE_HEAD, launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16, s));
+  STAGE(ATD_STAGE_HEAD, launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16, s));
   return e;
 }
 
@@ -525,7 +510,6 @@ extern "C" int decoder_destroy(atd_decoder* d) {
   if (d->mem && !d->dry) {
     e = hipDeviceSynchronize();
     for (auto& g : d->graphs) (void)hipGraphExecDestroy(g.exec);
-    for (auto ev : d->probe_ev) (void)hipEventDestroy(ev);
     if (d->cap_stream) (void)hipStreamDestroy(d->cap_stream);
     hipError_t e2 = hipFree(d->mem);
     if (e == hipSuccess) e = e2;
@@ -824,7 +808,6 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
     hipStream_t cs = d->cap_stream;
     e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return hip_fail(d, e, "hipStreamBeginCapture");
-    d->capturing = true;
     hipError_t le = enqueue_step(d, slot, 1, tok_io, G, table_ids, extra, head, y_out, logits_out,
                                  max_cap, cs);
     if (le == hipSuccess) {
@@ -842,7 +825,6 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
       le = launch_argmax(a, cs);
     }
     if (le == hipSuccess && tokens_out) le = launch_record_token(tok_io, tokens_out, d->counter, cs);
-    d->capturing = false;
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     if (le != hipSuccess || e != hipSuccess) {
@@ -867,27 +849,34 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
 
 // ---------------------------------------------------------------- stage timing
 
-extern "C" int decoder_profile_stage(atd_decoder* d, int32_t stage, int32_t enable) {
+extern "C" int decoder_time_stage(atd_decoder* d, int32_t stage, int32_t slot, int32_t reps,
+                                  void* stream, double* us_per_launch) {
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
-  if (stage < 0 || stage >= ATD_STAGE_COUNT)
-    return fail(d, ATD_ERR_INVALID_ARG, "stage %d outside [0, %d)", stage, ATD_STAGE_COUNT);
-  d->probe_stage = enable ? stage : -1;
-  d->probe_used = 0;
-  return ATD_OK;
-}
-
-extern "C" int decoder_profile_result(atd_decoder* d, double* total_ms, int64_t* launches) {
-  if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
-  double tot = 0.0;
-  const size_t pairs = d->probe_used / 2;
-  for (size_t i = 0; i < pairs; ++i) {
-    hipError_t e = hipEventSynchronize(d->probe_ev[2 * i + 1]);
-    float ms = 0.f;
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, d->probe_ev[2 * i], d->probe_ev[2 * i + 1]);
-    if (e != hipSuccess) return hip_fail(d, e, "decoder_profile_result");
-    tot += ms;
-  }
-  if (total_ms) *total_ms = tot;
-  if (launches) *launches = (int64_t)pairs;
+  if (stage != ATD_STAGE_QKV && stage != ATD_STAGE_OPROJ && stage != ATD_STAGE_GATEUP &&
+      stage != ATD_STAGE_DOWN)
+    return fail(d, ATD_ERR_INVALID_ARG, "stage %d is not a per-layer projection stage", stage);
+  if (slot < 0 || slot >= d->cfg.max_slots || !d->attached[slot])
+    return fail(d, ATD_ERR_INVALID_ARG, "slot %d is not attached", slot);
+  if (reps < 1) return fail(d, ATD_ERR_INVALID_ARG, "reps %d < 1", reps);
+  if (!us_per_launch) return fail(d, ATD_ERR_INVALID_ARG, "us_per_launch is NULL");
+  if (d->dry) return fail(d, ATD_ERR_DEVICE, "dry-run decoder has no device");
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  const RowMap rows{kRowsStep, slot};
+  const int bound = std::min(std::max(d->pos[slot] + 1, 1), d->cfg.max_ctx);
+  d->only_stage = stage;
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = run_layers(d, rows, 1, bound, s);
+  d->only_stage = -1;
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return hip_fail(d, e, "decoder_time_stage");
+  *us_per_launch = (double)ms * 1e3 / ((double)reps * d->cfg.n_layers);
   return ATD_OK;
 }

@@ -182,11 +182,9 @@ class Decoder:
                            ptr(tokens_out), ptr(y_out), logits_out.data_ptr(), _stream())
         return logits_out
 
-    def profile_stage(self, stage: int, enable: bool = True):
-        B.decoder_profile_stage(self.handle, stage, int(enable))
-
-    def profile_result(self):
-        return B.decoder_profile_result(self.handle)
+    def time_stage(self, stage: int, slot: int = 0, reps: int = 8) -> float:
+        """Mean microseconds per launch of one projection stage (all layers)."""
+        return B.decoder_time_stage(self.handle, stage, slot, reps, _stream())
 
     def embed(self, tok: Optional[torch.Tensor], table_ids: Sequence[int], x_out: torch.Tensor,
               nrows: int = 1, extra: Optional[torch.Tensor] = None):

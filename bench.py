@@ -12,9 +12,10 @@ steps replayed from a HIP graph on the device (K = 1536 runs the context to
 
 Also measured in the same run:
   roofline      the dominant kernel (RMSNorm + gate/up + SwiGLU GEMV): its
-                algorithmic bytes per launch over its average duration, timed
-                with HIP event pairs on the launching stream during a pass of
-                the same steps; HBM traffic per launch from the committed
+                algorithmic bytes per launch over its average duration; the
+                library enqueues that kernel for every layer in turn (each
+                layer's weights once, as in a step) between two HIP events on
+                this stream; HBM traffic per launch from the committed
                 rocprofv3 counter summary when it matches the kernel source.
   cpu_baseline  the CPU oracle on this host's cores, on a bounded sample of
                 the same workload (decode steps after the same prefill).
@@ -159,19 +160,11 @@ def bench_lm(args, wl):
     dt = time.perf_counter() - t0
     log(f"timed {K} steps: {dt * 1e3:.1f} ms")
 
-    # roofline pass: same steps, eager, HIP events around every gate/up launch
-    dec.set_position(0, P0)
-    tok.copy_(tok0)
-    n_prof = min(K, 128)
-    dec.profile_stage(B.ATD_STAGE_GATEUP, True)
-    zz = torch.empty(1, s.vocab, device="cuda")
-    for _ in range(n_prof):
-        dec.step(tok.view(1, 1), [0], logits_out=zz)
-        dv.greedy_argmax(zz[0], None, 1.0, tok)
-    torch.cuda.synchronize()
-    prof_ms, launches = dec.profile_result()
-    dec.profile_stage(B.ATD_STAGE_GATEUP, False)
-    avg_s = prof_ms / 1e3 / max(launches, 1)
+    # roofline: the dominant kernel's launches, every layer's weights in turn
+    # as in a step, timed with HIP events on this stream
+    reps = 16
+    avg_s = dec.time_stage(B.ATD_STAGE_GATEUP, 0, reps) / 1e6
+    launches = reps * s.n_layers
     per_launch = gateup_bytes(s)
     achieved = per_launch / avg_s / 1e9
     traffic = traffic_per_launch()
@@ -213,6 +206,8 @@ def main():
                     choices=["talker1.7b", "asr", "tiny"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 8 plain device copies of 256 MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -222,6 +217,15 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        # a copy kernel of known size: each launch reads and writes 256 MiB
+        src = torch.ones(64 << 20, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4, "launches": 8}))
+        return
     from autoregressive_transformer_decode_amd import inputs
     wl = inputs.WORKLOADS[args.workload]
     out = bench_lm(args, wl)

@@ -253,14 +253,16 @@ enum {
   ATD_STAGE_COUNT = 7
 };
 
-/* Measurement hook: while enabled, every eager launch of `stage` made by
- * decoder_step / decoder_prefill is bracketed by a HIP event pair recorded
- * on the call's stream (graph replays of decoder_generate are not).
- * Enabling clears previous records.  decoder_profile_result waits for the
- * recorded events and returns their summed elapsed milliseconds and the
- * number of launches.  Errors: INVALID_ARG, DEVICE. */
-int decoder_profile_stage(atd_decoder* dec, int32_t stage, int32_t enable);
-int decoder_profile_result(atd_decoder* dec, double* total_ms, int64_t* launches);
+/* Measurement: enqueue the kernels of one per-layer projection stage
+ * (ATD_STAGE_QKV, _OPROJ, _GATEUP or _DOWN) of a one-row decode step of `slot` for
+ * every layer in turn (each layer's weights once, as in a step), `reps`
+ * times, between two HIP events recorded on `stream`, and return the mean
+ * time per launch in microseconds.  The kernels read and write only the
+ * decoder's own scratch (the residual stream they update there is rebuilt
+ * by the next step or prefill); caller memory and slot positions are not
+ * touched.  Waits for the stream.  Errors: INVALID_ARG, DEVICE. */
+int decoder_time_stage(atd_decoder* dec, int32_t stage, int32_t slot, int32_t reps,
+                       void* stream, double* us_per_launch);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,7 @@ ATD_ERR_UNSUPPORTED = -7
 ATD_F32 = 0
 ATD_BF16 = 1
 ATD_FLAG_DRY_RUN = 1
+ATD_FLAG_NO_MFMA = 2
 
 STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FULL",
                 -5: "CAPACITY", -6: "DEVICE", -7: "UNSUPPORTED"}

@@ -37,6 +37,9 @@ struct atd_decoder {
   void** kv_tab = nullptr;
   int *slot_pos = nullptr, *slot_cap = nullptr;
   float* part = nullptr;       // argmax partials [max_rows, nblk, 3]
+  bool mma = false;            // MFMA path for chunks of >= 3 rows
+  uint16_t *mhi = nullptr, *mlo = nullptr;  // [kMmaRows, Kmax] bf16 GEMM inputs
+  float* mpart = nullptr;      // split-K partials
   int32_t* counter = nullptr;  // token counter of decoder_generate
   size_t part_floats = 0;      // capacity of pacc in floats / D
   bool dry = false;  // ATD_FLAG_DRY_RUN: host state only, no HIP calls
@@ -136,7 +139,7 @@ int check_config(const atd_config* c) {
     return fail(nullptr, ATD_ERR_CAPACITY, "max_rows %d outside [1, 65536]", c->max_rows);
   if (c->max_ctx < 1 || c->max_ctx > (1 << 20))
     return fail(nullptr, ATD_ERR_CAPACITY, "max_ctx %d outside [1, 2^20]", c->max_ctx);
-  if (c->flags & ~ATD_FLAG_DRY_RUN)
+  if (c->flags & ~(ATD_FLAG_DRY_RUN | ATD_FLAG_NO_MFMA))
     return fail(nullptr, ATD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)c->flags);
   return ATD_OK;
 }
@@ -209,15 +212,73 @@ int attn_waves(int M) { return M <= 4 ? 512 : kAttnWavesMax; }
   } while (0)
 
 // The per-layer launch sequence for M rows (decode step or prefill block).
-hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hipStream_t s) {
+AttnArgs attn_args(const atd_decoder* d, RowMap rows, int l, int M, int max_len_bound,
+                   bool fused) {
+  const atd_config& c = d->cfg;
+  const atd_layer_weights& W = d->layers[l];
+  const int waves = attn_waves(M);
+  AttnArgs a{};
+  a.fused = fused;
+  a.qkv = d->qkv;
+  a.q_norm = (const float*)W.q_norm;
+  a.k_norm = (const float*)W.k_norm;
+  a.qk_norm = c.qk_norm;
+  a.eps = c.rms_eps;
+  a.cos_t = d->cos_t;
+  a.sin_t = d->sin_t;
+  a.q = d->q;
+  a.st = slots_of(d);
+  a.rows = rows;
+  a.layer = l;
+  a.M = M;
+  a.Hq = c.n_q_heads;
+  a.Hkv = c.n_kv_heads;
+  a.nsplit_max = attn_max_splits(max_len_bound, M, c.n_kv_heads, waves);
+  a.waves = waves;
+  if (rows.mode == kRowsPrefill || M == 1) {  // one slot: pass its rows directly
+    const int slot = rows.mode == kRowsPrefill ? rows.slot0 : rows.slot0 + rows.row0;
+    a.k_direct = d->kp[slot][l];
+    a.v_direct = d->vp[slot][l];
+    a.cap_direct = d->cap[slot];
+  }
+  a.scale = 1.0f / std::sqrt((float)c.head_dim);
+  a.pml = d->pml;
+  a.pacc = d->pacc;
+  a.o = d->o;
+  return a;
+}
+
+RopeArgs rope_args(const atd_decoder* d, RowMap rows, int l, int M) {
+  const atd_config& c = d->cfg;
+  const atd_layer_weights& W = d->layers[l];
+  RopeArgs r{};
+  r.qkv = d->qkv;
+  r.q_out = d->q;
+  r.q_norm = (const float*)W.q_norm;
+  r.k_norm = (const float*)W.k_norm;
+  r.eps = c.rms_eps;
+  r.cos_t = d->cos_t;
+  r.sin_t = d->sin_t;
+  r.st = slots_of(d);
+  r.rows = rows;
+  r.layer = l;
+  r.M = M;
+  r.Hq = c.n_q_heads;
+  r.Hkv = c.n_kv_heads;
+  r.D = c.head_dim;
+  r.qk_norm = c.qk_norm;
+  return r;
+}
+
+// GEMV path: the per-layer launch sequence for M <= 2 rows (or float32 weights).
+hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
+                           hipStream_t s) {
   const atd_config& c = d->cfg;
   const int h = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv;
   const int bf16 = c.dtype == ATD_BF16;
   const int kv_bf16 = c.kv_dtype == ATD_BF16;
-  const SlotTables st = slots_of(d);
-  const int waves = attn_waves(M);
-  const int nsplit = attn_max_splits(max_len_bound, M, Hkv, waves);
+  const bool fused = rows.mode == kRowsStep;
   hipError_t e = hipSuccess;
   for (int l = 0; l < c.n_layers; ++l) {
     const atd_layer_weights& W = d->layers[l];
@@ -231,7 +292,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     g.seg_end[0] = nq;
     g.seg_end[1] = nq + nkv;
     g.seg_end[2] = nqkv;
-    g.x = d->x;
+    g.x = x;
     g.ldx = h;
     g.gain = (const float*)W.attn_norm;
     g.eps = c.rms_eps;
@@ -241,64 +302,17 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     g.N = nqkv;
     g.M = M;
     STAGE(ATD_STAGE_QKV, launch_gemv(g, kEpiStore, true, bf16, s));
-
-    const bool fused = rows.mode == kRowsStep;
-    if (!fused) {
-      // prefill rows of one slot read each other's keys: append them all first
-      RopeArgs r{};
-      r.qkv = d->qkv;
-      r.q_out = d->q;
-      r.q_norm = (const float*)W.q_norm;
-      r.k_norm = (const float*)W.k_norm;
-      r.eps = c.rms_eps;
-      r.cos_t = d->cos_t;
-      r.sin_t = d->sin_t;
-      r.st = st;
-      r.rows = rows;
-      r.layer = l;
-      r.M = M;
-      r.Hq = Hq;
-      r.Hkv = Hkv;
-      r.D = D;
-      r.qk_norm = c.qk_norm;
-      STAGE(ATD_STAGE_ROPE, launch_rope_append(r, kv_bf16, s));
-    }
-
-    AttnArgs a{};
-    a.fused = fused;
-    a.qkv = d->qkv;
-    a.q_norm = (const float*)W.q_norm;
-    a.k_norm = (const float*)W.k_norm;
-    a.qk_norm = c.qk_norm;
-    a.eps = c.rms_eps;
-    a.cos_t = d->cos_t;
-    a.sin_t = d->sin_t;
-    a.q = d->q;
-    a.st = st;
-    a.rows = rows;
-    a.layer = l;
-    a.M = M;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.nsplit_max = nsplit;
-    a.waves = waves;
-    if (rows.mode == kRowsPrefill || M == 1) {   // one slot: pass its rows directly
-      a.k_direct = d->kp[rows.slot0][l];
-      a.v_direct = d->vp[rows.slot0][l];
-      a.cap_direct = d->cap[rows.slot0];
-    }
-    a.scale = 1.0f / std::sqrt((float)D);
-    a.pml = d->pml;
-    a.pacc = d->pacc;
-    a.o = d->o;
-    STAGE(ATD_STAGE_ATTN, launch_attention(a, kv_bf16, D, Hq / Hkv, s));
+    // prefill rows of one slot read each other's keys: append them all first
+    if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
+    STAGE(ATD_STAGE_ATTN, launch_attention(attn_args(d, rows, l, M, max_len_bound, fused),
+                                           kv_bf16, D, Hq / Hkv, s));
 
     GemvArgs op{};
     op.W[0] = W.wo;
     op.seg_end[0] = op.seg_end[1] = op.seg_end[2] = h;
     op.x = d->o;
     op.ldx = nq;
-    op.out = d->x;
+    op.out = x;
     op.ldo = h;
     op.K = nq;
     op.N = h;
@@ -309,7 +323,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     gu.W[0] = W.w_gate;
     gu.W2 = W.w_up;
     gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = c.ffn;
-    gu.x = d->x;
+    gu.x = x;
     gu.ldx = h;
     gu.gain = (const float*)W.mlp_norm;
     gu.eps = c.rms_eps;
@@ -325,7 +339,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
     dn.seg_end[0] = dn.seg_end[1] = dn.seg_end[2] = h;
     dn.x = d->act;
     dn.ldx = c.ffn;
-    dn.out = d->x;
+    dn.out = x;
     dn.ldo = h;
     dn.K = c.ffn;
     dn.N = h;
@@ -335,9 +349,130 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, hip
   return e;
 }
 
+// MFMA path pieces -----------------------------------------------------------
+int mma_splits(int K) { return (K + kMmaKb - 1) / kMmaKb; }
+
+hipError_t mma_prep(atd_decoder* d, const float* x, int ldx, int K, int M, const float* gain,
+                    float* y_out, hipStream_t s) {
+  PrepArgs p{};
+  p.x = x;
+  p.ldx = ldx;
+  p.gain = gain;
+  p.eps = d->cfg.rms_eps;
+  p.y_out = y_out;
+  p.hi = d->mhi;
+  p.lo = d->mlo;
+  p.K = K;
+  p.M = M;
+  return launch_prep(p, s);
+}
+
+hipError_t mma_gemm(atd_decoder* d, const void* w0, const void* w1, const void* w2, int e0,
+                    int e1, int N, int K, hipStream_t s) {
+  GemmArgs g{};
+  g.hi = d->mhi;
+  g.lo = d->mlo;
+  g.W[0] = w0;
+  g.W[1] = w1;
+  g.W[2] = w2;
+  g.seg_end[0] = e0;
+  g.seg_end[1] = e1;
+  g.seg_end[2] = N;
+  g.K = K;
+  g.N = N;
+  g.ks = mma_splits(K);
+  g.part = d->mpart;
+  return launch_gemm(g, s);
+}
+
+hipError_t mma_reduce(atd_decoder* d, int N, int K, int M, int epi, float* out, int ldo,
+                      const float* const* bias, int e0, int e1, hipStream_t s) {
+  ReduceArgs r{};
+  r.part = d->mpart;
+  r.ks = mma_splits(K);
+  r.N = N;
+  r.M = M;
+  if (bias)
+    for (int i = 0; i < 3; ++i) r.bias[i] = bias[i];
+  r.seg_end[0] = e0;
+  r.seg_end[1] = e1;
+  r.seg_end[2] = N;
+  r.out = out;
+  r.ldo = ldo;
+  r.hi = d->mhi;
+  r.lo = d->mlo;
+  return launch_reduce(r, epi, s);
+}
+
+// MFMA path: the per-layer launch sequence for a chunk of 3..kMmaRows rows.
+hipError_t run_layers_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
+                          hipStream_t s) {
+  const atd_config& c = d->cfg;
+  const int h = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv, F = c.ffn;
+  const int kv_bf16 = c.kv_dtype == ATD_BF16;
+  const bool fused = rows.mode == kRowsStep;
+  hipError_t e = hipSuccess;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const atd_layer_weights& W = d->layers[l];
+    const float* bias[3] = {(const float*)W.bq, (const float*)W.bk, (const float*)W.bv};
+    STAGE(ATD_STAGE_QKV, mma_prep(d, x, h, h, M, (const float*)W.attn_norm, nullptr, s));
+    STAGE(ATD_STAGE_QKV, mma_gemm(d, W.wq, W.wk, W.wv, nq, nq + nkv, nqkv, h, s));
+    STAGE(ATD_STAGE_QKV, mma_reduce(d, nqkv, h, M, kRedStore, d->qkv, nqkv, bias, nq,
+                                    nq + nkv, s));
+    if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
+    STAGE(ATD_STAGE_ATTN, launch_attention(attn_args(d, rows, l, M, max_len_bound, fused),
+                                           kv_bf16, D, Hq / Hkv, s));
+    STAGE(ATD_STAGE_OPROJ, mma_prep(d, d->o, nq, nq, M, nullptr, nullptr, s));
+    STAGE(ATD_STAGE_OPROJ, mma_gemm(d, W.wo, W.wo, W.wo, h, h, h, nq, s));
+    STAGE(ATD_STAGE_OPROJ, mma_reduce(d, h, nq, M, kRedResidual, x, h, nullptr, h, h, s));
+    STAGE(ATD_STAGE_GATEUP, mma_prep(d, x, h, h, M, (const float*)W.mlp_norm, nullptr, s));
+    STAGE(ATD_STAGE_GATEUP, mma_gemm(d, W.w_gate, W.w_up, W.w_up, F, 2 * F, 2 * F, h, s));
+    STAGE(ATD_STAGE_GATEUP, mma_reduce(d, 2 * F, h, M, kRedSwigluHiLo, nullptr, 0, nullptr, F,
+                                       2 * F, s));
+    STAGE(ATD_STAGE_DOWN, mma_gemm(d, W.w_down, W.w_down, W.w_down, h, h, h, F, s));
+    STAGE(ATD_STAGE_DOWN, mma_reduce(d, h, F, M, kRedResidual, x, h, nullptr, h, h, s));
+  }
+  return e;
+}
+
+// Rows of a call run through the stack: chunks of kMmaRows on the MFMA path
+// (one chunk after the other keeps prefill causal: a chunk's rows only read
+// keys of earlier rows, already appended), otherwise the GEMV path.
+hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
+                      hipStream_t s) {
+  if (!d->mma || M < 3) return run_layers_gemv(d, rows, M, max_len_bound, x, s);
+  hipError_t e = hipSuccess;
+  for (int c0 = 0; c0 < M && e == hipSuccess; c0 += kMmaRows) {
+    RowMap r = rows;
+    r.row0 = rows.row0 + c0;
+    const int cm = std::min(kMmaRows, M - c0);
+    const int bound = rows.mode == kRowsPrefill ? std::min(max_len_bound, r.row0 + cm)
+                                                : max_len_bound;
+    e = cm >= 3 ? run_layers_mma(d, r, cm, bound, x + (size_t)c0 * d->cfg.hidden, s)
+                : run_layers_gemv(d, r, cm, bound, x + (size_t)c0 * d->cfg.hidden, s);
+  }
+  return e;
+}
+
 hipError_t run_head(atd_decoder* d, const float* xrows, int M, int head, float* y_out,
                     float* logits, hipStream_t s) {
   const atd_config& c = d->cfg;
+  hipError_t e = hipSuccess;
+  if (d->mma && M >= 3) {
+    for (int c0 = 0; c0 < M && e == hipSuccess; c0 += kMmaRows) {
+      const int cm = std::min(kMmaRows, M - c0);
+      e = mma_prep(d, xrows + (size_t)c0 * c.hidden, c.hidden, c.hidden, cm, d->final_norm,
+                   y_out ? y_out + (size_t)c0 * c.hidden : nullptr, s);
+      if (e == hipSuccess)
+        e = mma_gemm(d, d->heads[head], d->heads[head], d->heads[head], c.vocab, c.vocab,
+                     c.vocab, c.hidden, s);
+      if (e == hipSuccess)
+        e = mma_reduce(d, c.vocab, c.hidden, cm, kRedStore, logits + (size_t)c0 * c.vocab,
+                       c.vocab, nullptr, c.vocab, c.vocab, s);
+    }
+    return e;
+  }
   GemvArgs g{};
   g.W[0] = d->heads[head];
   g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = c.vocab;
@@ -351,7 +486,6 @@ hipError_t run_head(atd_decoder* d, const float* xrows, int M, int head, float* 
   g.K = c.hidden;
   g.N = c.vocab;
   g.M = M;
-  hipError_t e = hipSuccess;
   STAGE(ATD_STAGE_HEAD, launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16, s));
   return e;
 }
@@ -391,10 +525,10 @@ EmbedArgs embed_args(atd_decoder* d, int B, const int32_t* tok, int G,
 hipError_t enqueue_step(atd_decoder* d, int slot0, int B, const int32_t* tok, int G,
                         const int32_t* table_ids, const float* extra, int head, float* y_out,
                         float* logits_out, int max_cap, hipStream_t s) {
-  RowMap rows{kRowsStep, slot0};
+  RowMap rows{kRowsStep, slot0, 0};
   EmbedArgs ea = embed_args(d, B, tok, G, table_ids, extra, d->x);
   hipError_t e = launch_embed(ea, d->cfg.dtype == ATD_BF16, s);
-  if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, s);
+  if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, d->x, s);
   if (e == hipSuccess) e = run_head(d, d->x, B, head, y_out, logits_out, s);
   if (e == hipSuccess) e = launch_advance(slots_of(d), rows, B, s);
   return e;
@@ -457,6 +591,20 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   const int nblk_v = (cfg->vocab + kArgmaxChunk - 1) / kArgmaxChunk;
   const size_t o_part = carve((size_t)R * nblk_v * 3 * 4);
   const size_t o_cnt = carve(4);
+  // MFMA path: hi/lo activations of one 64-row chunk and split-K partials of
+  // the largest GEMM (q/k/v, o, gate/up, down, LM head)
+  d->mma = cfg->dtype == ATD_BF16 && !(cfg->flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 &&
+           nq % 32 == 0 && cfg->ffn % 32 == 0 && std::max(R, S) >= 3;
+  size_t o_mhi = 0, o_mlo = 0, o_mpart = 0;
+  if (d->mma) {
+    const size_t kmax = std::max({(size_t)h, (size_t)nq, (size_t)cfg->ffn});
+    auto parts = [](int n, int k) { return (size_t)((k + kMmaKb - 1) / kMmaKb) * kMmaRows * n; };
+    const size_t pmax = std::max({parts(nqkv, h), parts(h, nq), parts(2 * cfg->ffn, h),
+                                  parts(h, cfg->ffn), parts(cfg->vocab, h)});
+    o_mhi = carve((size_t)kMmaRows * kmax * 2);
+    o_mlo = carve((size_t)kMmaRows * kmax * 2);
+    o_mpart = carve(pmax * 4);
+  }
 
   hipError_t e = hipGetDevice(&d->device);
   if (e == hipSuccess) e = hipMalloc(&d->mem, off);
@@ -480,6 +628,11 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->slot_cap = (int*)(base + o_cap);
   d->part = (float*)(base + o_part);
   d->counter = (int32_t*)(base + o_cnt);
+  if (d->mma) {
+    d->mhi = (uint16_t*)(base + o_mhi);
+    d->mlo = (uint16_t*)(base + o_mlo);
+    d->mpart = (float*)(base + o_mpart);
+  }
 
   // RoPE table: phi = p * theta^(-2i/D) in double, cos/sin rounded to float.
   std::vector<float> ct((size_t)cfg->max_ctx * half), sn((size_t)cfg->max_ctx * half);
@@ -645,10 +798,10 @@ extern "C" int decoder_prefill(atd_decoder* d, int32_t slot, const float* x, int
     return ATD_OK;
   }
   hipStream_t s = (hipStream_t)stream;
-  RowMap rows{kRowsPrefill, slot};
+  RowMap rows{kRowsPrefill, slot, 0};
   EmbedArgs ea = embed_args(d, T, nullptr, 0, nullptr, x, d->x);
   hipError_t e = launch_embed(ea, c.dtype == ATD_BF16, s);
-  if (e == hipSuccess) e = run_layers(d, rows, T, T, s);
+  if (e == hipSuccess) e = run_layers(d, rows, T, T, d->x, s);
   if (e == hipSuccess)
     e = run_head(d, d->x + (size_t)(T - 1) * c.hidden, 1, head, y_out, logits_out, s);
   if (e == hipSuccess) e = launch_advance(slots_of(d), rows, T, s);
@@ -864,11 +1017,11 @@ extern "C" int decoder_time_stage(atd_decoder* d, int32_t stage, int32_t slot, i
   hipEvent_t e0 = nullptr, e1 = nullptr;
   hipError_t e = hipEventCreate(&e0);
   if (e == hipSuccess) e = hipEventCreate(&e1);
-  const RowMap rows{kRowsStep, slot};
+  const RowMap rows{kRowsStep, slot, 0};
   const int bound = std::min(std::max(d->pos[slot] + 1, 1), d->cfg.max_ctx);
   d->only_stage = stage;
   if (e == hipSuccess) e = hipEventRecord(e0, s);
-  for (int r = 0; r < reps && e == hipSuccess; ++r) e = run_layers(d, rows, 1, bound, s);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = run_layers(d, rows, 1, bound, d->x, s);
   d->only_stage = -1;
   if (e == hipSuccess) e = hipEventRecord(e1, s);
   if (e == hipSuccess) e = hipEventSynchronize(e1);

@@ -52,6 +52,7 @@ enum RowMode { kRowsStep = 0, kRowsPrefill = 1 };
 struct RowMap {
   int mode;
   int slot0;
+  int row0;   // rows of this launch are rows row0 .. of the call
 };
 
 // ---------------------------------------------------------------- rows/KV
@@ -155,6 +156,47 @@ struct KvCopyArgs {
   int Hkv, D, rows, s_old, s_new, elem_bytes;
 };
 
+// ---------------------------------------------------------------- MFMA path (M >= 3 rows)
+// Activations enter a GEMM as a bf16 pair hi + lo (hi = bf16(v), lo =
+// bf16(v - hi)), so the products keep ~16 bits of the float32 input while the
+// bf16 weights are used exactly; rows are padded to kMmaRows with zeros.
+constexpr int kMmaRows = 64;     // rows per GEMM chunk
+constexpr int kMmaBlockN = 128;  // weight rows per workgroup
+constexpr int kMmaKb = 256;      // K per split
+
+struct PrepArgs {
+  const float* x;      // [M, ldx]
+  int ldx;
+  const float* gain;   // RMSNorm gain [K] or null (no norm)
+  float eps;
+  float* y_out;        // normalised rows [M, K] (float32) or null
+  uint16_t* hi;        // [kMmaRows, K] bf16
+  uint16_t* lo;
+  int K, M;
+};
+
+struct GemmArgs {
+  const uint16_t* hi;  // [kMmaRows, K]
+  const uint16_t* lo;
+  const void* W[3];    // bf16 row segments [rows_s, K]; segment boundaries multiples of 16
+  int seg_end[3];
+  int K, N, ks;        // ks = number of K splits of kMmaKb
+  float* part;         // [ks, kMmaRows, N]
+};
+
+enum ReduceEpilogue { kRedStore = 0, kRedResidual = 1, kRedSwigluHiLo = 2 };
+
+struct ReduceArgs {
+  const float* part;   // [ks, kMmaRows, N]
+  int ks, N, M;
+  const float* bias[3];  // kRedStore: per-segment bias or null
+  int seg_end[3];
+  float* out;          // kRedStore / kRedResidual: [M, ldo]
+  int ldo;
+  uint16_t* hi;        // kRedSwigluHiLo: [kMmaRows, N/2] (gate = cols < N/2, up = the rest)
+  uint16_t* lo;
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns the first HIP error of its launches (hipSuccess otherwise).
 hipError_t launch_embed(const EmbedArgs& a, int bf16, hipStream_t s);
@@ -168,5 +210,8 @@ hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s);
 hipError_t launch_record_token(const int32_t* tok, int32_t* out, int32_t* counter, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, int epi, hipStream_t s);
 
 }  // namespace atd

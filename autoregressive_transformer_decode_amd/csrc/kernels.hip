@@ -120,9 +120,9 @@ __device__ __forceinline__ void row_of(const RowMap& r, const SlotTables& st, in
                                        int& slot, int& pos) {
   if (r.mode == kRowsPrefill) {
     slot = r.slot0;
-    pos = m;
+    pos = r.row0 + m;
   } else {
-    slot = r.slot0 + m;
+    slot = r.slot0 + r.row0 + m;
     pos = st.pos[slot];
   }
 }
@@ -229,7 +229,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int VEC = Vec16<WT>::N;
   constexpr int NW = EPI == kEpiSwiglu ? 2 : 1;
   constexpr int RW = KS;           // rows per wave group
-  constexpr int NG = 4 / KS;       // row groups per block
   __shared__ float red_ss[4][MR];
   __shared__ float red_acc[4][RW][MR][NW];
   const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
@@ -885,6 +884,168 @@ __global__ __launch_bounds__(64) void k_argmax_final(ArgmaxArgs a) {
   }
 }
 
+
+// ------------------------------------------------------------------ MFMA path
+typedef __bf16 Bf16x8 __attribute__((ext_vector_type(8)));
+typedef float Floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Bf16x8 as_bf16x8(uint4 v) {
+  union {
+    uint4 u;
+    Bf16x8 b;
+  } c;
+  c.u = v;
+  return c.b;
+}
+
+// Rows of x (optionally RMSNorm'd) -> bf16 hi/lo pairs, rows >= M zeroed.
+__global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
+  __shared__ float red[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  uint16_t* hi = a.hi + (size_t)m * a.K;
+  uint16_t* lo = a.lo + (size_t)m * a.K;
+  if (m >= a.M) {
+    for (int i = tid; i < a.K; i += 256) hi[i] = lo[i] = 0;
+    return;
+  }
+  const float* xr = a.x + (size_t)m * a.ldx;
+  float inv = 1.f;
+  if (a.gain) {
+    float ss = 0.f;
+    for (int i = tid; i < a.K; i += 256) ss += xr[i] * xr[i];
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    inv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)a.K + a.eps);
+  }
+  for (int i = tid; i < a.K; i += 256) {
+    float v = xr[i];
+    if (a.gain) {
+      v = v * inv * a.gain[i];
+      if (a.y_out) a.y_out[(size_t)m * a.K + i] = v;
+    }
+    const uint16_t h = f32_to_bf16(v);
+    hi[i] = h;
+    lo[i] = f32_to_bf16(v - __uint_as_float((uint32_t)h << 16));
+  }
+}
+
+// Split-K GEMM of 64 padded rows: part[split, m, n] = sum over the split's
+// K range of (hi + lo)[m, k] * W[n, k].  Block (128 weight rows, split): 4
+// waves x 32 rows (two 16-row tiles); the block's weight tile is issued to
+// registers first, the activation slice is staged in LDS, then each wave runs
+// 16 MFMAs (4 row tiles x 2 column tiles x hi/lo) per 32-wide K step.
+template <int KSTEPS>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
+  // LDS [2][kMmaRows][kMmaKb] bf16 (64 KiB); the 16-byte chunk c of row r
+  // sits at chunk c ^ (r & 15), so the 16 rows an MFMA operand load touches
+  // fall on different banks
+  constexpr int LDK = kMmaKb;
+  extern __shared__ uint16_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.y;
+  const int k0 = split * kMmaKb;
+  const int K = a.K;
+  const int li = lane & 15, lk = (lane >> 4) * 8;
+
+  // weights: two 16-row tiles per wave, KSTEPS 32-wide K steps
+  uint4 wt[2][KSTEPS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = blockIdx.x * kMmaBlockN + wave * 32 + t * 16 + li;
+    const bool rok = row < a.N;
+    const int sg = row < a.seg_end[0] ? 0 : (row < a.seg_end[1] ? 1 : 2);
+    const int sb = sg == 0 ? 0 : a.seg_end[sg - 1];
+    const uint16_t* wr = reinterpret_cast<const uint16_t*>(a.W[sg]) + (size_t)(rok ? row - sb : 0) * K;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int k = k0 + ks * 32 + lk;
+      wt[t][ks] = (rok && k < K) ? ldg16(wr + k) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // activation slice -> LDS (hi then lo), zero beyond K
+  for (int i = tid; i < 2 * kMmaRows * (kMmaKb / 8); i += 256) {
+    const int part = i / (kMmaRows * (kMmaKb / 8));
+    const int r = (i / (kMmaKb / 8)) % kMmaRows;
+    const int c = (i % (kMmaKb / 8)) * 8;
+    const uint16_t* src = (part ? a.lo : a.hi) + (size_t)r * K + k0 + c;
+    const uint4 v = (k0 + c < K) ? ldg16(src) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(lds + ((size_t)part * kMmaRows + r) * LDK + (((c >> 3) ^ (r & 15)) << 3)) = v;
+  }
+  __syncthreads();
+
+  Floatx4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[i][t] = Floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const Bf16x8 b0 = as_bf16x8(wt[0][ks]), b1 = as_bf16x8(wt[1][ks]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* ph = lds + (size_t)(i * 16 + li) * LDK + ((((ks * 32 + lk) >> 3) ^ li) << 3);
+      const Bf16x8 ah = as_bf16x8(*reinterpret_cast<const uint4*>(ph));
+      const Bf16x8 al = as_bf16x8(*reinterpret_cast<const uint4*>(ph + (size_t)kMmaRows * LDK));
+      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b0, acc[i][0], 0, 0, 0);
+      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b0, acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b1, acc[i][1], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b1, acc[i][1], 0, 0, 0);
+    }
+  }
+  // C lane layout: column li, rows 4*(lane/16) + r of each 16x16 tile
+  float* P = a.part + (size_t)split * kMmaRows * a.N;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int col = blockIdx.x * kMmaBlockN + wave * 32 + t * 16 + li;
+    if (col < a.N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) P[(size_t)(i * 16 + (lane >> 4) * 4 + r) * a.N + col] = acc[i][t][r];
+    }
+  }
+}
+
+// out = epi(sum over splits, in order)
+template <int EPI>
+__global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
+  const int m = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int NO = EPI == kRedSwigluHiLo ? a.N / 2 : a.N;
+  if (n >= NO) return;
+  if constexpr (EPI == kRedSwigluHiLo) {
+    uint16_t* hi = a.hi + (size_t)m * NO;
+    uint16_t* lo = a.lo + (size_t)m * NO;
+    if (m >= a.M) {
+      hi[n] = lo[n] = 0;
+      return;
+    }
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < a.ks; ++s) {
+      const float* P = a.part + ((size_t)s * kMmaRows + m) * a.N;
+      g += P[n];
+      u += P[NO + n];
+    }
+    const float v = g / (1.0f + expf(-g)) * u;
+    const uint16_t h = f32_to_bf16(v);
+    hi[n] = h;
+    lo[n] = f32_to_bf16(v - __uint_as_float((uint32_t)h << 16));
+  } else {
+    if (m >= a.M) return;
+    float v = 0.f;
+    for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * kMmaRows + m) * a.N + n];
+    float* o = a.out + (size_t)m * a.ldo + n;
+    if constexpr (EPI == kRedStore) {
+      const int sg = n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
+      const int sb = sg == 0 ? 0 : a.seg_end[sg - 1];
+      *o = a.bias[sg] ? v + a.bias[sg][n - sb] : v;
+    } else {
+      *o = *o + v;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ generation bookkeeping
 __global__ void k_record_token(const int32_t* tok, int32_t* out, int32_t* counter) {
   if (threadIdx.x == 0) {
@@ -1059,6 +1220,30 @@ hipError_t launch_record_token(const int32_t* tok, int32_t* out, int32_t* counte
 
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_prep, dim3(kMmaRows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid((a.N + kMmaBlockN - 1) / kMmaBlockN, a.ks);
+  const size_t lds = 2ull * kMmaRows * kMmaKb * sizeof(uint16_t);
+  hipLaunchKernelGGL(k_gemm<kMmaKb / 32>, grid, dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, int epi, hipStream_t s) {
+  const int no = epi == kRedSwigluHiLo ? a.N / 2 : a.N;
+  const dim3 grid((no + 255) / 256, kMmaRows);
+  if (epi == kRedStore)
+    hipLaunchKernelGGL(k_reduce<kRedStore>, grid, dim3(256), 0, s, a);
+  else if (epi == kRedResidual)
+    hipLaunchKernelGGL(k_reduce<kRedResidual>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_reduce<kRedSwigluHiLo>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

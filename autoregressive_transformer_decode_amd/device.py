@@ -83,7 +83,7 @@ class DeviceModel:
 
 
 def make_config(s: ModelShape, max_slots: int, max_rows: int, max_ctx: int,
-                n_tables: Optional[int] = None) -> B.atd_config:
+                n_tables: Optional[int] = None, flags: int = 0) -> B.atd_config:
     return B.atd_config(
         n_layers=s.n_layers, hidden=s.hidden, n_q_heads=s.n_q_heads, n_kv_heads=s.n_kv_heads,
         head_dim=s.head_dim, ffn=s.ffn, vocab=s.vocab, n_lm_heads=s.n_lm_heads,
@@ -92,18 +92,19 @@ def make_config(s: ModelShape, max_slots: int, max_rows: int, max_ctx: int,
         dtype=B.ATD_BF16 if s.dtype == BF16 else B.ATD_F32,
         kv_dtype=B.ATD_BF16 if s.kv_dtype == BF16 else B.ATD_F32,
         rope_theta=s.rope_theta, rms_eps=s.rms_eps,
-        max_slots=max_slots, max_rows=max_rows, max_ctx=max_ctx)
+        max_slots=max_slots, max_rows=max_rows, max_ctx=max_ctx, flags=flags)
 
 
 class Decoder:
     """A decoder handle plus the KV buckets it holds for each slot."""
 
     def __init__(self, model: DeviceModel, max_slots: int = 1, max_rows: int = 1,
-                 max_ctx: int = 4096):
+                 max_ctx: int = 4096, mfma: bool = True):
         self.model = model
         s = model.shape
         self.shape = s
-        self.cfg = make_config(s, max_slots, max_rows, max_ctx)
+        self.cfg = make_config(s, max_slots, max_rows, max_ctx,
+                               flags=0 if mfma else B.ATD_FLAG_NO_MFMA)
         self.handle = B.decoder_create(self.cfg, model.weights)
         self.kv = {}   # slot -> (list of K tensors, list of V tensors)
         self.kv_dtype = torch.bfloat16 if s.kv_dtype == BF16 else torch.float32

@@ -293,12 +293,29 @@ def batched_first_inputs(wl: Workload, seed: int = 0) -> np.ndarray:
     return normal(seed, 2, _T_PREFILL + 1, (wl.batch, wl.model.hidden))
 
 
-def batched_kv(shape: ModelShape, stream: int, length: int, layer: int,
-               seed: int = 0) -> Tuple[np.ndarray, np.ndarray]:
-    """Synthetic cache contents of one stream and layer: K, V [Hkv, length, D]
-    as bf16 bit patterns, N(0, 1) (the batched workload's bf16 cache)."""
-    kvshape = (shape.n_kv_heads, length, shape.head_dim)
-    tid = _T_KV + 1000 * stream + 2 * layer
+KV_POOL_ROWS = 8192
+
+
+def batched_kv_pool(shape: ModelShape, layer: int, seed: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Synthetic cache rows of one layer for the batched workload: K, V
+    [Hkv, KV_POOL_ROWS, D] as bf16 bit patterns of N(0, 1) values."""
+    kvshape = (shape.n_kv_heads, KV_POOL_ROWS, shape.head_dim)
+    tid = _T_KV + 2 * layer
     k = to_bf16_bits(normal(seed, 3, tid, kvshape, scale=1.0))
     v = to_bf16_bits(normal(seed, 3, tid + 1, kvshape, scale=1.0))
     return k.reshape(kvshape), v.reshape(kvshape)
+
+
+def batched_kv_offset(stream: int, length: int) -> int:
+    """First pool row of a stream's cache window (windows of different
+    streams start at different rows)."""
+    return (stream * 1237) % (KV_POOL_ROWS - length + 1)
+
+
+def batched_kv(shape: ModelShape, stream: int, length: int, layer: int,
+               seed: int = 0, pool=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Cache contents of one stream and layer: K, V [Hkv, length, D] bf16 bit
+    patterns, a window of the layer's pool."""
+    k, v = pool if pool is not None else batched_kv_pool(shape, layer, seed)
+    o = batched_kv_offset(stream, length)
+    return k[:, o:o + length], v[:, o:o + length]

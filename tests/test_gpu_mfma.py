@@ -1,0 +1,172 @@
+"""Matrix-core (MFMA) path against the CPU oracle: prefill blocks and batched
+steps of 3 or more rows run as 64-row GEMM chunks (bf16 hi/lo activations,
+float32 accumulation).  Same bar as the vector path: normwise max relative
+error <= 2e-3 on y and logits, tokens equal where the oracle's top-2 margin
+exceeds 1e-2."""
+
+import numpy as np
+import pytest
+import torch
+
+from autoregressive_transformer_decode_amd import device as dv
+from autoregressive_transformer_decode_amd import inputs
+from oracle import decoder as od
+from tests._models import normwise_rel, oracle_from_weights
+from tests.gpu_util import MARGIN, TOL, lm_parity, small_shape
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# h, Hq*D and F multiples of 32 (MFMA-eligible); N ragged against the
+# 128-row block (o and down 288, gate/up 1344, vocab 1000) and K ragged
+# against the 256-wide split (h = 288: the last split 32 wide; F = 672: 3
+# splits, the last 160 wide)
+MFMA_SHAPE = ("mfma", 2, 288, 8, 2, 128, 672, 1000, "bf16", True, True)
+
+
+@pytest.mark.parametrize("T", [3, 64, 66, 133])
+def test_prefill_chunks(T):
+    """Prefill of T rows: full 64-row chunks, a ragged MFMA chunk, and a
+    1-2 row tail on the vector path; then teacher-forced steps read the KV
+    rows every chunk appended."""
+    shape = small_shape(*MFMA_SHAPE)
+    mw = inputs.make_weights(shape, seed=7)
+    X0 = inputs.normal(7, 2, 11, (T, shape.hidden), scale=1.0)
+    chk, ref, _ = lm_parity(mw, X0, 6, 256)
+    _log(f"prefill T={T}: {chk.n} checks, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
+
+
+def test_prefill_mfma_equals_vector_path():
+    """The same prefill through both paths agrees to the tolerance (and
+    both agree with the oracle)."""
+    shape = small_shape(*MFMA_SHAPE)
+    mw = inputs.make_weights(shape, seed=8)
+    X0 = torch.from_numpy(inputs.normal(8, 2, 12, (100, shape.hidden), scale=1.0)).cuda()
+    dm = dv.DeviceModel(mw)
+    out = []
+    for mfma in (True, False):
+        dec = dv.Decoder(dm, max_slots=1, max_rows=100, max_ctx=128, mfma=mfma)
+        dec.grow(0, 128)
+        y = torch.empty(shape.hidden, device="cuda")
+        z = torch.empty(shape.vocab, device="cuda")
+        dec.prefill(X0, y_out=y, logits_out=z)
+        torch.cuda.synchronize()
+        out.append((y.cpu().numpy(), z.cpu().numpy()))
+        dec.close()
+    e = max(normwise_rel(out[0][0], out[1][0]), normwise_rel(out[0][1], out[1][1]))
+    _log(f"mfma vs vector prefill: {e:.2e}")
+    assert e <= TOL
+
+
+def test_batched_steps_across_chunks():
+    """B = 69 streams (a 64-row chunk plus a 5-row chunk), each at its own
+    position; every stream equals its own oracle run for several steps."""
+    shape = small_shape(*MFMA_SHAPE)
+    mw = inputs.make_weights(shape, seed=9)
+    om = oracle_from_weights(mw)
+    dm = dv.DeviceModel(mw)
+    Bn, steps = 69, 3
+    lens = [1 + (7 * b) % 40 for b in range(Bn)]
+    dec = dv.Decoder(dm, max_slots=Bn, max_rows=Bn, max_ctx=64)
+    caches, toks = [], []
+    for b in range(Bn):
+        dec.grow(b, 64)
+        X = inputs.normal(9, 2, 200 + b, (lens[b], shape.hidden), scale=1.0)
+        c = od.Cache(om, 64)
+        _, z = od.prefill(om, c, X, 0)
+        caches.append(c)
+        toks.append(int(np.argmax(z)))
+        dec.prefill(torch.from_numpy(X).cuda(), slot=b)
+    y = torch.empty(Bn, shape.hidden, device="cuda")
+    z = torch.empty(Bn, shape.vocab, device="cuda")
+    worst = 0.0
+    for k in range(steps):
+        tok = torch.tensor(toks, dtype=torch.int32, device="cuda").view(Bn, 1)
+        dec.step(tok, [0], slot0=0, nrows=Bn, y_out=y, logits_out=z)
+        torch.cuda.synchronize()
+        yg, zg = y.cpu().numpy(), z.cpu().numpy()
+        for b in range(Bn):
+            yr, zr = od.step(om, caches[b], od.embed(om, [toks[b]], [0]), 0)
+            e = max(normwise_rel(yg[b], yr), normwise_rel(zg[b], zr))
+            worst = max(worst, e)
+            assert e <= TOL, (k, b, e)
+            toks[b] = int(np.argmax(zr))
+    for b in range(Bn):
+        assert dec.position(b)[0] == lens[b] + steps
+    dec.close()
+    _log(f"batched 69 streams: worst {worst:.2e}")
+
+
+def test_batched64_full_size_sampled_streams():
+    """The batched workload at its full size: the 1.7B shape, 64 streams with
+    seeded KV lengths in [256, 4096], bf16 weights and KV, one step per
+    stream per iteration.  The streams with the shortest and the longest
+    context and one in between are checked against the oracle over two
+    iterations (the first from given inputs, the second from tokens)."""
+    wl = inputs.WORKLOADS["batched64"]
+    s = wl.model
+    lens = inputs.batched_lengths(wl, seed=0)
+    X1 = inputs.batched_first_inputs(wl, seed=0)
+    mw = inputs.make_weights(s, seed=0)
+    dm = dv.DeviceModel(mw)
+    Bn = wl.batch
+    dec = dv.Decoder(dm, max_slots=Bn, max_rows=Bn, max_ctx=wl.s_max)
+    caps = [int(l) + 8 for l in lens]
+    for b in range(Bn):
+        dec.grow(b, caps[b])
+    sample = [int(np.argmin(lens)), int(np.argmax(lens)), 17]
+    om = oracle_from_weights(mw, np.float32)
+    caches = {b: od.Cache(om, caps[b]) for b in sample}
+    for l in range(s.n_layers):
+        pool = inputs.batched_kv_pool(s, l, seed=0)
+        pk = torch.from_numpy(pool[0].view(np.int16)).cuda().view(torch.bfloat16)
+        pv = torch.from_numpy(pool[1].view(np.int16)).cuda().view(torch.bfloat16)
+        for b in range(Bn):
+            o, n = inputs.batched_kv_offset(b, int(lens[b])), int(lens[b])
+            dec.kv[b][0][l][:, :n].copy_(pk[:, o:o + n])
+            dec.kv[b][1][l][:, :n].copy_(pv[:, o:o + n])
+        for b in sample:
+            k, v = inputs.batched_kv(s, b, int(lens[b]), l, pool=pool)
+            caches[b].K[l][:, :lens[b]] = inputs.bf16_bits_to_f32(k)
+            caches[b].V[l][:, :lens[b]] = inputs.bf16_bits_to_f32(v)
+    for b in range(Bn):
+        dec.set_position(b, int(lens[b]))
+    for b in sample:
+        caches[b].pos = int(lens[b])
+    torch.cuda.synchronize()
+    _log(f"batched64: caches filled, sample streams {sample} lengths {[int(lens[b]) for b in sample]}")
+
+    y = torch.empty(Bn, s.hidden, device="cuda")
+    z = torch.empty(Bn, s.vocab, device="cuda")
+    tok = torch.zeros(Bn, dtype=torch.int32, device="cuda")
+    margin = torch.zeros(Bn, device="cuda")
+    dec.step(None, [], nrows=Bn, extra=torch.from_numpy(X1).cuda(), y_out=y, logits_out=z)
+    dv.greedy_argmax(z, None, 1.0, tok, margin)
+    torch.cuda.synchronize()
+    worst, feed = 0.0, {}
+    for b in sample:
+        yr, zr = od.step(om, caches[b], X1[b].astype(np.float32), 0)
+        e = max(normwise_rel(y[b].cpu().numpy(), yr), normwise_rel(z[b].cpu().numpy(), zr))
+        worst = max(worst, e)
+        assert e <= TOL, (0, b, e)
+        top = np.sort(zr)[-2:]
+        if top[1] - top[0] > MARGIN:
+            assert int(tok[b].item()) == int(np.argmax(zr)), b
+        feed[b] = int(np.argmax(zr))
+    for b, t in feed.items():      # teacher-force the oracle's tokens
+        tok[b] = t
+    dec.step(tok.view(Bn, 1), [0], nrows=Bn, y_out=y, logits_out=z)
+    torch.cuda.synchronize()
+    for b in sample:
+        yr, zr = od.step(om, caches[b], od.embed(om, [feed[b]], [0]), 0)
+        e = max(normwise_rel(y[b].cpu().numpy(), yr), normwise_rel(z[b].cpu().numpy(), zr))
+        worst = max(worst, e)
+        assert e <= TOL, (1, b, e)
+    for b in range(Bn):
+        assert dec.position(b)[0] == int(lens[b]) + 2
+    dec.close()
+    _log(f"batched64 full size: worst {worst:.2e}")

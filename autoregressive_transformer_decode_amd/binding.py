@@ -92,7 +92,7 @@ def _load():
         "greedy_argmax": ([vp, i32, i32, vp, f32, vp, vp, vp], C.c_int),
         "decoder_generate": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, f32, vp, vp,
                               vp, vp], C.c_int),
-        "decoder_time_stage": ([vp, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
+        "decoder_time_stage": ([vp, i32, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -181,7 +181,8 @@ def decoder_generate(handle: int, slot: int, n_steps: int, tok_io: int, G: int, 
                                 stream), handle)
 
 
-def decoder_time_stage(handle: int, stage: int, slot: int, reps: int, stream: int) -> float:
-    us = C.c_double()
-    _check(lib.decoder_time_stage(handle, stage, slot, reps, stream, C.byref(us)), handle)
+def decoder_time_stage(handle: int, stage: int, slot0: int, B: int, reps: int,
+                       stream: int) -> float:
+    us = C.c_double(0.0)
+    _check(lib.decoder_time_stage(handle, stage, slot0, B, reps, stream, C.byref(us)), handle)
     return us.value

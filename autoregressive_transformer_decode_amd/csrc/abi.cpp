@@ -38,8 +38,9 @@ struct atd_decoder {
   int *slot_pos = nullptr, *slot_cap = nullptr;
   float* part = nullptr;       // argmax partials [max_rows, nblk, 3]
   bool mma = false;            // MFMA path for chunks of >= 3 rows
-  uint16_t *mhi = nullptr, *mlo = nullptr;  // [kMmaRows, Kmax] bf16 GEMM inputs
-  float* mpart = nullptr;      // split-K partials
+  float* mpart = nullptr;      // split-K partials of the MFMA GEMMs
+  float* mss = nullptr;        // row sums of squares [kMmaRows, ceil(h / kSsCols)]
+  float* mxg = nullptr;        // normalised-GEMM input x * gain [kMmaRows, h]
   int32_t* counter = nullptr;  // token counter of decoder_generate
   size_t part_floats = 0;      // capacity of pacc in floats / D
   bool dry = false;  // ATD_FLAG_DRY_RUN: host state only, no HIP calls
@@ -349,130 +350,11 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
   return e;
 }
 
-// MFMA path pieces -----------------------------------------------------------
-int mma_splits(int K) { return (K + kMmaKb - 1) / kMmaKb; }
-
-hipError_t mma_prep(atd_decoder* d, const float* x, int ldx, int K, int M, const float* gain,
-                    float* y_out, hipStream_t s) {
-  PrepArgs p{};
-  p.x = x;
-  p.ldx = ldx;
-  p.gain = gain;
-  p.eps = d->cfg.rms_eps;
-  p.y_out = y_out;
-  p.hi = d->mhi;
-  p.lo = d->mlo;
-  p.K = K;
-  p.M = M;
-  return launch_prep(p, s);
-}
-
-hipError_t mma_gemm(atd_decoder* d, const void* w0, const void* w1, const void* w2, int e0,
-                    int e1, int N, int K, hipStream_t s) {
-  GemmArgs g{};
-  g.hi = d->mhi;
-  g.lo = d->mlo;
-  g.W[0] = w0;
-  g.W[1] = w1;
-  g.W[2] = w2;
-  g.seg_end[0] = e0;
-  g.seg_end[1] = e1;
-  g.seg_end[2] = N;
-  g.K = K;
-  g.N = N;
-  g.ks = mma_splits(K);
-  g.part = d->mpart;
-  return launch_gemm(g, s);
-}
-
-hipError_t mma_reduce(atd_decoder* d, int N, int K, int M, int epi, float* out, int ldo,
-                      const float* const* bias, int e0, int e1, hipStream_t s) {
-  ReduceArgs r{};
-  r.part = d->mpart;
-  r.ks = mma_splits(K);
-  r.N = N;
-  r.M = M;
-  if (bias)
-    for (int i = 0; i < 3; ++i) r.bias[i] = bias[i];
-  r.seg_end[0] = e0;
-  r.seg_end[1] = e1;
-  r.seg_end[2] = N;
-  r.out = out;
-  r.ldo = ldo;
-  r.hi = d->mhi;
-  r.lo = d->mlo;
-  return launch_reduce(r, epi, s);
-}
-
-// MFMA path: the per-layer launch sequence for a chunk of 3..kMmaRows rows.
-hipError_t run_layers_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
-                          hipStream_t s) {
-  const atd_config& c = d->cfg;
-  const int h = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
-  const int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv, F = c.ffn;
-  const int kv_bf16 = c.kv_dtype == ATD_BF16;
-  const bool fused = rows.mode == kRowsStep;
-  hipError_t e = hipSuccess;
-  for (int l = 0; l < c.n_layers; ++l) {
-    const atd_layer_weights& W = d->layers[l];
-    const float* bias[3] = {(const float*)W.bq, (const float*)W.bk, (const float*)W.bv};
-    STAGE(ATD_STAGE_QKV, mma_prep(d, x, h, h, M, (const float*)W.attn_norm, nullptr, s));
-    STAGE(ATD_STAGE_QKV, mma_gemm(d, W.wq, W.wk, W.wv, nq, nq + nkv, nqkv, h, s));
-    STAGE(ATD_STAGE_QKV, mma_reduce(d, nqkv, h, M, kRedStore, d->qkv, nqkv, bias, nq,
-                                    nq + nkv, s));
-    if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
-    STAGE(ATD_STAGE_ATTN, launch_attention(attn_args(d, rows, l, M, max_len_bound, fused),
-                                           kv_bf16, D, Hq / Hkv, s));
-    STAGE(ATD_STAGE_OPROJ, mma_prep(d, d->o, nq, nq, M, nullptr, nullptr, s));
-    STAGE(ATD_STAGE_OPROJ, mma_gemm(d, W.wo, W.wo, W.wo, h, h, h, nq, s));
-    STAGE(ATD_STAGE_OPROJ, mma_reduce(d, h, nq, M, kRedResidual, x, h, nullptr, h, h, s));
-    STAGE(ATD_STAGE_GATEUP, mma_prep(d, x, h, h, M, (const float*)W.mlp_norm, nullptr, s));
-    STAGE(ATD_STAGE_GATEUP, mma_gemm(d, W.w_gate, W.w_up, W.w_up, F, 2 * F, 2 * F, h, s));
-    STAGE(ATD_STAGE_GATEUP, mma_reduce(d, 2 * F, h, M, kRedSwigluHiLo, nullptr, 0, nullptr, F,
-                                       2 * F, s));
-    STAGE(ATD_STAGE_DOWN, mma_gemm(d, W.w_down, W.w_down, W.w_down, h, h, h, F, s));
-    STAGE(ATD_STAGE_DOWN, mma_reduce(d, h, F, M, kRedResidual, x, h, nullptr, h, h, s));
-  }
-  return e;
-}
-
-// Rows of a call run through the stack: chunks of kMmaRows on the MFMA path
-// (one chunk after the other keeps prefill causal: a chunk's rows only read
-// keys of earlier rows, already appended), otherwise the GEMV path.
-hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
-                      hipStream_t s) {
-  if (!d->mma || M < 3) return run_layers_gemv(d, rows, M, max_len_bound, x, s);
-  hipError_t e = hipSuccess;
-  for (int c0 = 0; c0 < M && e == hipSuccess; c0 += kMmaRows) {
-    RowMap r = rows;
-    r.row0 = rows.row0 + c0;
-    const int cm = std::min(kMmaRows, M - c0);
-    const int bound = rows.mode == kRowsPrefill ? std::min(max_len_bound, r.row0 + cm)
-                                                : max_len_bound;
-    e = cm >= 3 ? run_layers_mma(d, r, cm, bound, x + (size_t)c0 * d->cfg.hidden, s)
-                : run_layers_gemv(d, r, cm, bound, x + (size_t)c0 * d->cfg.hidden, s);
-  }
-  return e;
-}
-
-hipError_t run_head(atd_decoder* d, const float* xrows, int M, int head, float* y_out,
-                    float* logits, hipStream_t s) {
+// GEMV path: final RMSNorm + LM head for M rows.
+hipError_t run_head_gemv(atd_decoder* d, const float* xrows, int M, int head, float* y_out,
+                         float* logits, hipStream_t s) {
   const atd_config& c = d->cfg;
   hipError_t e = hipSuccess;
-  if (d->mma && M >= 3) {
-    for (int c0 = 0; c0 < M && e == hipSuccess; c0 += kMmaRows) {
-      const int cm = std::min(kMmaRows, M - c0);
-      e = mma_prep(d, xrows + (size_t)c0 * c.hidden, c.hidden, c.hidden, cm, d->final_norm,
-                   y_out ? y_out + (size_t)c0 * c.hidden : nullptr, s);
-      if (e == hipSuccess)
-        e = mma_gemm(d, d->heads[head], d->heads[head], d->heads[head], c.vocab, c.vocab,
-                     c.vocab, c.hidden, s);
-      if (e == hipSuccess)
-        e = mma_reduce(d, c.vocab, c.hidden, cm, kRedStore, logits + (size_t)c0 * c.vocab,
-                       c.vocab, nullptr, c.vocab, c.vocab, s);
-    }
-    return e;
-  }
   GemvArgs g{};
   g.W[0] = d->heads[head];
   g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = c.vocab;
@@ -487,6 +369,147 @@ hipError_t run_head(atd_decoder* d, const float* xrows, int M, int head, float* 
   g.N = c.vocab;
   g.M = M;
   STAGE(ATD_STAGE_HEAD, launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16, s));
+  return e;
+}
+
+// MFMA path pieces -----------------------------------------------------------
+// GEMM of the M rows of x ([M, K]) with an [N, K] weight given as up to three
+// row segments; split partials into d->mpart.
+hipError_t mma_gemm(atd_decoder* d, const float* x, int M, const void* w0, const void* w1,
+                    const void* w2, int e0, int e1, int N, int K, hipStream_t s) {
+  GemmArgs g{};
+  g.x = x;
+  g.M = M;
+  g.W[0] = w0;
+  g.W[1] = w1;
+  g.W[2] = w2;
+  g.seg_end[0] = e0;
+  g.seg_end[1] = e1;
+  g.seg_end[2] = N;
+  g.K = K;
+  g.N = N;
+  g.kc = mma_kc(N, K);
+  g.ks = mma_ks(N, K);
+  g.part = d->mpart;
+  return launch_gemm(g, s);
+}
+
+// Reductions of the splits of the last GEMM (N columns, ks splits) over M rows.
+ReduceArgs mma_red(atd_decoder* d, int N, int ks, int M, float* out, int ldo) {
+  ReduceArgs r{};
+  r.part = d->mpart;
+  r.ks = ks;
+  r.N = N;
+  r.M = M;
+  r.seg_end[0] = r.seg_end[1] = r.seg_end[2] = N;
+  r.out = out;
+  r.ldo = ldo;
+  r.nss = (d->cfg.hidden + kSsCols - 1) / kSsCols;
+  r.hn = d->cfg.hidden;
+  r.eps = d->cfg.rms_eps;
+  return r;
+}
+
+// x += splits (ks = 0: none), then xg = x * gain and the row sums of squares
+// for the next normalised GEMM
+hipError_t mma_residual(atd_decoder* d, int ks, int M, float* x, const float* gain,
+                        hipStream_t s) {
+  const int h = d->cfg.hidden;
+  ReduceArgs r = mma_red(d, h, ks, M, x, h);
+  r.ss = d->mss;
+  r.gain = gain;
+  r.xg = d->mxg;
+  return launch_reduce(r, kRedResidual, s);
+}
+
+// LM-head outputs of a call's rows (row 0 of the span the pointers address).
+struct HeadOut {
+  int head;
+  float* y_out;    // [rows, h] or null
+  float* logits;   // [rows, V]
+};
+
+// MFMA path for one chunk of 3..kMmaRows rows: every layer, then (if asked)
+// the final norm and LM head.  Kernel chain per layer: GEMM q/k/v of x*g ->
+// norm factor + bias -> attention (split + combine) -> GEMM o -> residual
+// (+ x*g, sums of squares) -> GEMM gate/up -> norm factor + SwiGLU -> GEMM
+// down -> residual (+ x*g for the next norm, sums of squares).
+hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
+                         const HeadOut* ho, hipStream_t s) {
+  const atd_config& c = d->cfg;
+  const int h = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+  const int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv, F = c.ffn;
+  const int kv_bf16 = c.kv_dtype == ATD_BF16;
+  const bool fused = rows.mode == kRowsStep;
+  float* xg = d->mxg;
+  hipError_t e = hipSuccess;
+  STAGE(ATD_STAGE_QKV, mma_residual(d, 0, M, x, (const float*)d->layers[0].attn_norm, s));
+  for (int l = 0; l < c.n_layers; ++l) {
+    const atd_layer_weights& W = d->layers[l];
+    const float* next_gain =
+        l + 1 < c.n_layers ? (const float*)d->layers[l + 1].attn_norm : d->final_norm;
+    STAGE(ATD_STAGE_QKV, mma_gemm(d, xg, M, W.wq, W.wk, W.wv, nq, nq + nkv, nqkv, h, s));
+    ReduceArgs rq = mma_red(d, nqkv, mma_ks(nqkv, h), M, d->qkv, nqkv);
+    rq.bias[0] = (const float*)W.bq;
+    rq.bias[1] = (const float*)W.bk;
+    rq.bias[2] = (const float*)W.bv;
+    rq.seg_end[0] = nq;
+    rq.seg_end[1] = nq + nkv;
+    rq.ss = d->mss;
+    STAGE(ATD_STAGE_QKV, launch_reduce(rq, kRedStore, s));
+    if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
+    STAGE(ATD_STAGE_ATTN, launch_attention(attn_args(d, rows, l, M, max_len_bound, fused),
+                                           kv_bf16, D, Hq / Hkv, s));
+    STAGE(ATD_STAGE_OPROJ, mma_gemm(d, d->o, M, W.wo, W.wo, W.wo, h, h, h, nq, s));
+    STAGE(ATD_STAGE_OPROJ, mma_residual(d, mma_ks(h, nq), M, x, (const float*)W.mlp_norm, s));
+    STAGE(ATD_STAGE_GATEUP, mma_gemm(d, xg, M, W.w_gate, W.w_up, W.w_up, F, 2 * F, 2 * F, h, s));
+    ReduceArgs rg = mma_red(d, 2 * F, mma_ks(2 * F, h), M, d->act, F);
+    rg.ss = d->mss;
+    STAGE(ATD_STAGE_GATEUP, launch_reduce(rg, kRedSwiglu, s));
+    STAGE(ATD_STAGE_DOWN, mma_gemm(d, d->act, M, W.w_down, W.w_down, W.w_down, h, h, h, F, s));
+    STAGE(ATD_STAGE_DOWN, mma_residual(d, mma_ks(h, F), M, x, next_gain, s));
+  }
+  if (ho) {
+    const void* Wh = d->heads[ho->head];
+    STAGE(ATD_STAGE_HEAD, mma_gemm(d, xg, M, Wh, Wh, Wh, c.vocab, c.vocab, c.vocab, h, s));
+    ReduceArgs rh = mma_red(d, c.vocab, mma_ks(c.vocab, h), M, ho->logits, c.vocab);
+    rh.ss = d->mss;
+    rh.xg = xg;
+    rh.y_out = ho->y_out;
+    STAGE(ATD_STAGE_HEAD, launch_reduce(rh, kRedStore, s));
+  }
+  return e;
+}
+
+// Rows of a call run through the stack (and the LM head when `ho` is set):
+// chunks of kMmaRows on the MFMA path, one after the other (which keeps a
+// prefill causal: a chunk's rows only read keys of earlier rows, already
+// appended), otherwise the GEMV path.
+hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
+                      const HeadOut* ho, hipStream_t s) {
+  const int h = d->cfg.hidden, V = d->cfg.vocab;
+  hipError_t e = hipSuccess;
+  const int step = d->mma && M >= 3 ? kMmaRows : M;
+  for (int c0 = 0; c0 < M && e == hipSuccess; c0 += step) {
+    RowMap r = rows;
+    r.row0 = rows.row0 + c0;
+    const int cm = std::min(step, M - c0);
+    const int bound = rows.mode == kRowsPrefill ? std::min(max_len_bound, r.row0 + cm)
+                                                : max_len_bound;
+    float* xc = x + (size_t)c0 * h;
+    HeadOut hc{};
+    if (ho) {
+      hc.head = ho->head;
+      hc.y_out = ho->y_out ? ho->y_out + (size_t)c0 * h : nullptr;
+      hc.logits = ho->logits + (size_t)c0 * V;
+    }
+    if (d->mma && cm >= 3) {
+      e = run_chunk_mma(d, r, cm, bound, xc, ho ? &hc : nullptr, s);
+    } else {
+      e = run_layers_gemv(d, r, cm, bound, xc, s);
+      if (e == hipSuccess && ho) e = run_head_gemv(d, xc, cm, hc.head, hc.y_out, hc.logits, s);
+    }
+  }
   return e;
 }
 
@@ -528,8 +551,8 @@ hipError_t enqueue_step(atd_decoder* d, int slot0, int B, const int32_t* tok, in
   RowMap rows{kRowsStep, slot0, 0};
   EmbedArgs ea = embed_args(d, B, tok, G, table_ids, extra, d->x);
   hipError_t e = launch_embed(ea, d->cfg.dtype == ATD_BF16, s);
-  if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, d->x, s);
-  if (e == hipSuccess) e = run_head(d, d->x, B, head, y_out, logits_out, s);
+  const HeadOut ho{head, y_out, logits_out};
+  if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, d->x, &ho, s);
   if (e == hipSuccess) e = launch_advance(slots_of(d), rows, B, s);
   return e;
 }
@@ -595,14 +618,13 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   // the largest GEMM (q/k/v, o, gate/up, down, LM head)
   d->mma = cfg->dtype == ATD_BF16 && !(cfg->flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 &&
            nq % 32 == 0 && cfg->ffn % 32 == 0 && std::max(R, S) >= 3;
-  size_t o_mhi = 0, o_mlo = 0, o_mpart = 0;
+  size_t o_mss = 0, o_mxg = 0, o_mpart = 0;
   if (d->mma) {
-    const size_t kmax = std::max({(size_t)h, (size_t)nq, (size_t)cfg->ffn});
-    auto parts = [](int n, int k) { return (size_t)((k + kMmaKb - 1) / kMmaKb) * kMmaRows * n; };
+    auto parts = [](int n, int k) { return (size_t)mma_ks(n, k) * kMmaRows * n; };
     const size_t pmax = std::max({parts(nqkv, h), parts(h, nq), parts(2 * cfg->ffn, h),
                                   parts(h, cfg->ffn), parts(cfg->vocab, h)});
-    o_mhi = carve((size_t)kMmaRows * kmax * 2);
-    o_mlo = carve((size_t)kMmaRows * kmax * 2);
+    o_mss = carve((size_t)kMmaRows * ((h + kSsCols - 1) / kSsCols) * 4);
+    o_mxg = carve((size_t)kMmaRows * h * 4);
     o_mpart = carve(pmax * 4);
   }
 
@@ -629,8 +651,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->part = (float*)(base + o_part);
   d->counter = (int32_t*)(base + o_cnt);
   if (d->mma) {
-    d->mhi = (uint16_t*)(base + o_mhi);
-    d->mlo = (uint16_t*)(base + o_mlo);
+    d->mss = (float*)(base + o_mss);
+    d->mxg = (float*)(base + o_mxg);
     d->mpart = (float*)(base + o_mpart);
   }
 
@@ -801,9 +823,9 @@ extern "C" int decoder_prefill(atd_decoder* d, int32_t slot, const float* x, int
   RowMap rows{kRowsPrefill, slot, 0};
   EmbedArgs ea = embed_args(d, T, nullptr, 0, nullptr, x, d->x);
   hipError_t e = launch_embed(ea, c.dtype == ATD_BF16, s);
-  if (e == hipSuccess) e = run_layers(d, rows, T, T, d->x, s);
+  if (e == hipSuccess) e = run_layers(d, rows, T, T, d->x, nullptr, s);
   if (e == hipSuccess)
-    e = run_head(d, d->x + (size_t)(T - 1) * c.hidden, 1, head, y_out, logits_out, s);
+    e = run_head_gemv(d, d->x + (size_t)(T - 1) * c.hidden, 1, head, y_out, logits_out, s);
   if (e == hipSuccess) e = launch_advance(slots_of(d), rows, T, s);
   if (e != hipSuccess) return hip_fail(d, e, "decoder_prefill");
   d->pos[slot] = T;
@@ -1002,26 +1024,37 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
 
 // ---------------------------------------------------------------- stage timing
 
-extern "C" int decoder_time_stage(atd_decoder* d, int32_t stage, int32_t slot, int32_t reps,
-                                  void* stream, double* us_per_launch) {
+extern "C" int decoder_time_stage(atd_decoder* d, int32_t stage, int32_t slot0, int32_t B,
+                                  int32_t reps, void* stream, double* us_per_layer) {
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
-  if (stage != ATD_STAGE_QKV && stage != ATD_STAGE_OPROJ && stage != ATD_STAGE_GATEUP &&
-      stage != ATD_STAGE_DOWN)
-    return fail(d, ATD_ERR_INVALID_ARG, "stage %d is not a per-layer projection stage", stage);
-  if (slot < 0 || slot >= d->cfg.max_slots || !d->attached[slot])
-    return fail(d, ATD_ERR_INVALID_ARG, "slot %d is not attached", slot);
+  if (stage != ATD_STAGE_QKV && stage != ATD_STAGE_ATTN && stage != ATD_STAGE_OPROJ &&
+      stage != ATD_STAGE_GATEUP && stage != ATD_STAGE_DOWN)
+    return fail(d, ATD_ERR_INVALID_ARG, "stage %d is not a per-layer decode stage", stage);
+  if (B < 1 || B > d->cfg.max_rows)
+    return fail(d, ATD_ERR_CAPACITY, "B = %d outside [1, max_rows = %d]", B, d->cfg.max_rows);
+  if (slot0 < 0 || slot0 + B > d->cfg.max_slots)
+    return fail(d, ATD_ERR_INVALID_ARG, "slots %d..%d outside [0, %d)", slot0, slot0 + B - 1,
+                d->cfg.max_slots);
+  int bound = 1;
+  for (int b = slot0; b < slot0 + B; ++b) {
+    if (!d->attached[b]) return fail(d, ATD_ERR_INVALID_ARG, "slot %d is not attached", b);
+    if (d->pos[b] >= d->cap[b])
+      return fail(d, ATD_ERR_KV_FULL, "slot %d: position %d at capacity %d", b, d->pos[b],
+                  d->cap[b]);
+    bound = std::max(bound, d->pos[b] + 1);
+  }
   if (reps < 1) return fail(d, ATD_ERR_INVALID_ARG, "reps %d < 1", reps);
-  if (!us_per_launch) return fail(d, ATD_ERR_INVALID_ARG, "us_per_launch is NULL");
+  if (!us_per_layer) return fail(d, ATD_ERR_INVALID_ARG, "us_per_layer is NULL");
   if (d->dry) return fail(d, ATD_ERR_DEVICE, "dry-run decoder has no device");
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   hipError_t e = hipEventCreate(&e0);
   if (e == hipSuccess) e = hipEventCreate(&e1);
-  const RowMap rows{kRowsStep, slot, 0};
-  const int bound = std::min(std::max(d->pos[slot] + 1, 1), d->cfg.max_ctx);
+  const RowMap rows{kRowsStep, slot0, 0};
   d->only_stage = stage;
   if (e == hipSuccess) e = hipEventRecord(e0, s);
-  for (int r = 0; r < reps && e == hipSuccess; ++r) e = run_layers(d, rows, 1, bound, d->x, s);
+  for (int r = 0; r < reps && e == hipSuccess; ++r)
+    e = run_layers(d, rows, B, bound, d->x, nullptr, s);
   d->only_stage = -1;
   if (e == hipSuccess) e = hipEventRecord(e1, s);
   if (e == hipSuccess) e = hipEventSynchronize(e1);
@@ -1030,6 +1063,6 @@ extern "C" int decoder_time_stage(atd_decoder* d, int32_t stage, int32_t slot, i
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
   if (e != hipSuccess) return hip_fail(d, e, "decoder_time_stage");
-  *us_per_launch = (double)ms * 1e3 / ((double)reps * d->cfg.n_layers);
+  *us_per_layer = (double)ms * 1e3 / ((double)reps * d->cfg.n_layers);
   return ATD_OK;
 }

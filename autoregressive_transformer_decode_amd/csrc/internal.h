@@ -159,42 +159,58 @@ struct KvCopyArgs {
 // ---------------------------------------------------------------- MFMA path (M >= 3 rows)
 // Activations enter a GEMM as a bf16 pair hi + lo (hi = bf16(v), lo =
 // bf16(v - hi)), so the products keep ~16 bits of the float32 input while the
-// bf16 weights are used exactly; rows are padded to kMmaRows with zeros.
+// bf16 weights are used exactly; each float32 activation is split into bf16
+// hi + lo parts as it is staged, so the products carry ~16 mantissa bits.
 constexpr int kMmaRows = 64;     // rows per GEMM chunk
-constexpr int kMmaBlockN = 128;  // weight rows per workgroup
-constexpr int kMmaKb = 256;      // K per split
+constexpr int kMmaBlockN = 64;   // weight rows per workgroup (16 per wave)
+constexpr int kMmaCh = 64;       // K per pipeline stage
+constexpr int kMmaTargetBlocks = 512;
+constexpr int kSsCols = 256;     // columns per partial sum of squares
 
-struct PrepArgs {
-  const float* x;      // [M, ldx]
-  int ldx;
-  const float* gain;   // RMSNorm gain [K] or null (no norm)
-  float eps;
-  float* y_out;        // normalised rows [M, K] (float32) or null
-  uint16_t* hi;        // [kMmaRows, K] bf16
-  uint16_t* lo;
-  int K, M;
-};
+// K per split of the GEMM of an [N, K] weight: about kMmaTargetBlocks
+// workgroups in all, whole pipeline stages per split
+inline int mma_kc(int N, int K) {
+  const long nb = (N + kMmaBlockN - 1) / kMmaBlockN;
+  long kc = ((long)K * nb + kMmaTargetBlocks - 1) / kMmaTargetBlocks;
+  kc = (kc + kMmaCh - 1) / kMmaCh * kMmaCh;
+  return (int)(kc < K ? kc : (K + kMmaCh - 1) / kMmaCh * kMmaCh);
+}
+inline int mma_ks(int N, int K) {
+  const int kc = mma_kc(N, K);
+  return (K + kc - 1) / kc;
+}
 
 struct GemmArgs {
-  const uint16_t* hi;  // [kMmaRows, K]
-  const uint16_t* lo;
-  const void* W[3];    // bf16 row segments [rows_s, K]; segment boundaries multiples of 16
+  const float* x;      // activations [M, K] (row stride K), M <= kMmaRows
+  int M;
+  const void* W[3];    // bf16 row segments [rows_s, K]
   int seg_end[3];
-  int K, N, ks;        // ks = number of K splits of kMmaKb
+  int K, N;            // K multiple of 32
+  int kc, ks;          // K per split (multiple of kMmaCh) and number of splits
   float* part;         // [ks, kMmaRows, N]
 };
 
-enum ReduceEpilogue { kRedStore = 0, kRedResidual = 1, kRedSwigluHiLo = 2 };
+enum ReduceEpilogue { kRedStore = 0, kRedResidual = 1, kRedSwiglu = 2 };
 
+// RMSNorm(x) W^T = inv_m * ((x * g) W^T) with inv_m = 1 / sqrt(mean(x_m^2) + eps):
+// the residual reduction leaves x * g (the next GEMM's input) and partial sums
+// of squares of x; the reduction after that GEMM applies inv_m.
 struct ReduceArgs {
   const float* part;   // [ks, kMmaRows, N]
-  int ks, N, M;
+  int ks, N, M;        // ks = 0: no partials (kRedResidual then only refreshes xg / ss)
   const float* bias[3];  // kRedStore: per-segment bias or null
   int seg_end[3];
-  float* out;          // kRedStore / kRedResidual: [M, ldo]
+  float* out;          // [M, ldo]: kRedStore / kRedSwiglu write, kRedResidual adds
   int ldo;
-  uint16_t* hi;        // kRedSwigluHiLo: [kMmaRows, N/2] (gate = cols < N/2, up = the rest)
-  uint16_t* lo;
+  // kRedResidual: writes ss [M, gridDim.x] (kSsCols-column partial sums of squares
+  // of the updated rows) and xg = out * gain.  kRedStore / kRedSwiglu: when ss is
+  // set, the sums are scaled by inv_m from ss [M, nss] over hn columns.
+  float* ss;
+  int nss, hn;
+  float eps;
+  const float* gain;
+  float* xg;           // [M, N] (kRedResidual) / read for y_out (kRedStore)
+  float* y_out;        // kRedStore: normalised rows xg * inv_m [M, hn] or null
 };
 
 // ---------------------------------------------------------------- launchers
@@ -210,7 +226,6 @@ hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s);
 hipError_t launch_record_token(const int32_t* tok, int32_t* out, int32_t* counter, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
-hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, int epi, hipStream_t s);
 

@@ -898,151 +898,172 @@ __device__ __forceinline__ Bf16x8 as_bf16x8(uint4 v) {
   return c.b;
 }
 
-// Rows of x (optionally RMSNorm'd) -> bf16 hi/lo pairs, rows >= M zeroed.
-__global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
-  __shared__ float red[4];
-  const int m = blockIdx.x, tid = threadIdx.x;
-  uint16_t* hi = a.hi + (size_t)m * a.K;
-  uint16_t* lo = a.lo + (size_t)m * a.K;
-  if (m >= a.M) {
-    for (int i = tid; i < a.K; i += 256) hi[i] = lo[i] = 0;
-    return;
-  }
-  const float* xr = a.x + (size_t)m * a.ldx;
-  float inv = 1.f;
-  if (a.gain) {
-    float ss = 0.f;
-    for (int i = tid; i < a.K; i += 256) ss += xr[i] * xr[i];
-    ss = wave_sum(ss);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
-    __syncthreads();
-    inv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)a.K + a.eps);
-  }
-  for (int i = tid; i < a.K; i += 256) {
-    float v = xr[i];
-    if (a.gain) {
-      v = v * inv * a.gain[i];
-      if (a.y_out) a.y_out[(size_t)m * a.K + i] = v;
-    }
-    const uint16_t h = f32_to_bf16(v);
-    hi[i] = h;
-    lo[i] = f32_to_bf16(v - __uint_as_float((uint32_t)h << 16));
-  }
-}
-
-// Split-K GEMM of 64 padded rows: part[split, m, n] = sum over the split's
-// K range of (hi + lo)[m, k] * W[n, k].  Block (128 weight rows, split): 4
-// waves x 32 rows (two 16-row tiles); the block's weight tile is issued to
-// registers first, the activation slice is staged in LDS, then each wave runs
-// 16 MFMAs (4 row tiles x 2 column tiles x hi/lo) per 32-wide K step.
-template <int KSTEPS>
+// Split-K GEMM of a chunk of up to 64 rows: part[split, m, n] = sum over the
+// split's K range of x[m, k] * W[n, k], with x entering as bf16 hi + lo
+// parts: bf16 MFMA 16x16x32, float32 accumulation.  Workgroup (64 weight
+// rows, split): wave w owns 16 rows.  The split is walked in 64-wide stages;
+// each stage's activation tile (64 rows) is read with row-contiguous loads,
+// split into hi/lo in registers and stored to a double-buffered LDS tile, from
+// which every wave reads its MFMA fragments, while the weight fragments go
+// straight to registers.  Both come through a P-deep register ring, so the
+// loads of P stages are in flight while a stage is multiplied, and the
+// in-order memory counter only ever waits for the oldest stage.
+template <int P>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
-  // LDS [2][kMmaRows][kMmaKb] bf16 (64 KiB); the 16-byte chunk c of row r
-  // sits at chunk c ^ (r & 15), so the 16 rows an MFMA operand load touches
-  // fall on different banks
-  constexpr int LDK = kMmaKb;
-  extern __shared__ uint16_t lds[];
+  // LDS tile [buf][hi/lo][row][8 x 16 bytes]; the 16-byte chunk c of row r
+  // sits at c ^ (r & 7) so that a fragment read spreads over the banks
+  __shared__ uint4 sa[2][2][kMmaRows][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.y;
-  const int k0 = split * kMmaKb;
+  const int li = lane & 15, lg = lane >> 4;
+  const int n0 = blockIdx.x * kMmaBlockN + wave * 16, split = blockIdx.y;
   const int K = a.K;
-  const int li = lane & 15, lk = (lane >> 4) * 8;
+  const int kb = split * a.kc, ke = min(K, kb + a.kc);
+  const int nch = (ke - kb + kMmaCh - 1) / kMmaCh;
 
-  // weights: two 16-row tiles per wave, KSTEPS 32-wide K steps
-  uint4 wt[2][KSTEPS];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = blockIdx.x * kMmaBlockN + wave * 32 + t * 16 + li;
-    const bool rok = row < a.N;
-    const int sg = row < a.seg_end[0] ? 0 : (row < a.seg_end[1] ? 1 : 2);
-    const int sb = sg == 0 ? 0 : a.seg_end[sg - 1];
-    const uint16_t* wr = reinterpret_cast<const uint16_t*>(a.W[sg]) + (size_t)(rok ? row - sb : 0) * K;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int k = k0 + ks * 32 + lk;
-      wt[t][ks] = (rok && k < K) ? ldg16(wr + k) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  // activation slice -> LDS (hi then lo), zero beyond K
-  for (int i = tid; i < 2 * kMmaRows * (kMmaKb / 8); i += 256) {
-    const int part = i / (kMmaRows * (kMmaKb / 8));
-    const int r = (i / (kMmaKb / 8)) % kMmaRows;
-    const int c = (i % (kMmaKb / 8)) * 8;
-    const uint16_t* src = (part ? a.lo : a.hi) + (size_t)r * K + k0 + c;
-    const uint4 v = (k0 + c < K) ? ldg16(src) : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(lds + ((size_t)part * kMmaRows + r) * LDK + (((c >> 3) ^ (r & 15)) << 3)) = v;
-  }
-  __syncthreads();
+  const int row = n0 + li;
+  const int sg = row < a.seg_end[0] ? 0 : (row < a.seg_end[1] ? 1 : 2);
+  const int sb = sg == 0 ? 0 : a.seg_end[sg - 1];
+  // rows past N read row 0 of the segment (in bounds); their sums are not stored
+  const uint16_t* wp = reinterpret_cast<const uint16_t*>(a.W[sg]) +
+                       (size_t)(row < a.N ? row - sb : 0) * K + lg * 8;
+  // staging: thread -> rows srow and srow + 32, k group sc (8 values)
+  const int srow = tid >> 3, sc = tid & 7;
+  const bool r0ok = srow < a.M, r1ok = srow + 32 < a.M;
+  const float* x0 = a.x + (size_t)(r0ok ? srow : 0) * K + sc * 8;
+  const float* x1 = a.x + (size_t)(r1ok ? srow + 32 : 0) * K + sc * 8;
 
-  Floatx4 acc[4][2];
+  uint4 ar[P][4], wr[P][2];
+  auto issue_a = [&](int p, int c) {
+    const int k = kb + c * kMmaCh + sc * 8;
+    const bool ok = k < ke;   // whole groups of 8: K and the split ends are multiples of 32
+    const int kk = ok ? k - sc * 8 : 0;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    ar[p][0] = ok && r0ok ? ldg16(x0 + kk) : z;
+    ar[p][1] = ok && r0ok ? ldg16(x0 + kk + 4) : z;
+    ar[p][2] = ok && r1ok ? ldg16(x1 + kk) : z;
+    ar[p][3] = ok && r1ok ? ldg16(x1 + kk + 4) : z;
+  };
+  auto issue_w = [&](int p, int c) {
+    // stages past the split end read in-bounds weights that meet zero activations
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int s = 0; s < 2; ++s) wr[p][s] = ldg16(wp + min(kb + c * kMmaCh + s * 32, K - 32));
+  };
 #pragma unroll
-    for (int t = 0; t < 2; ++t) acc[i][t] = Floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < P; ++p) {
+    issue_a(p, p);
+    issue_w(p, p);
+  }
+  Floatx4 acc[4];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    const Bf16x8 b0 = as_bf16x8(wt[0][ks]), b1 = as_bf16x8(wt[1][ks]);
+  for (int i = 0; i < 4; ++i) acc[i] = Floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nch; c0 += P) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t* ph = lds + (size_t)(i * 16 + li) * LDK + ((((ks * 32 + lk) >> 3) ^ li) << 3);
-      const Bf16x8 ah = as_bf16x8(*reinterpret_cast<const uint4*>(ph));
-      const Bf16x8 al = as_bf16x8(*reinterpret_cast<const uint4*>(ph + (size_t)kMmaRows * LDK));
-      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b0, acc[i][0], 0, 0, 0);
-      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b0, acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b1, acc[i][1], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b1, acc[i][1], 0, 0, 0);
+    for (int p = 0; p < P; ++p) {
+      const int c = c0 + p;
+      if (c < nch) {
+        const int buf = c & 1;
+        const int sw = sc ^ (srow & 7);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint4 u0 = ar[p][2 * q], u1 = ar[p][2 * q + 1];
+          const uint32_t u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v0 = __uint_as_float(u[2 * e]), v1 = __uint_as_float(u[2 * e + 1]);
+            const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
+            const uint16_t l0 = f32_to_bf16(v0 - __uint_as_float((uint32_t)h0 << 16));
+            const uint16_t l1 = f32_to_bf16(v1 - __uint_as_float((uint32_t)h1 << 16));
+            hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          }
+          sa[buf][0][srow + 32 * q][sw] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          sa[buf][1][srow + 32 * q][sw] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+        __syncthreads();
+        issue_a(p, c + P);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int pos = (s * 4 + lg) ^ (li & 7);
+          const Bf16x8 b = as_bf16x8(wr[p][s]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sa[buf][0][i * 16 + li][pos]), b,
+                                                             acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sa[buf][1][i * 16 + li][pos]), b,
+                                                             acc[i], 0, 0, 0);
+          }
+        }
+        issue_w(p, c + P);
+      }
     }
   }
-  // C lane layout: column li, rows 4*(lane/16) + r of each 16x16 tile
-  float* P = a.part + (size_t)split * kMmaRows * a.N;
+  // C layout: column li, rows 4 * lg + r of each 16x16 tile; rows >= M hold
+  // zero products and are stored too (the reduction ignores them)
+  if (row < a.N) {
+    float* Pp = a.part + (size_t)split * kMmaRows * a.N + row;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int col = blockIdx.x * kMmaBlockN + wave * 32 + t * 16 + li;
-    if (col < a.N) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) P[(size_t)(i * 16 + (lane >> 4) * 4 + r) * a.N + col] = acc[i][t][r];
-    }
+      for (int r = 0; r < 4; ++r) Pp[(size_t)(i * 16 + lg * 4 + r) * a.N] = acc[i][r];
   }
 }
 
-// out = epi(sum over splits, in order)
+// out = epi(sum over splits, in order); one thread per (row, column).
 template <int EPI>
 __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
-  const int m = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  const int NO = EPI == kRedSwigluHiLo ? a.N / 2 : a.N;
-  if (n >= NO) return;
-  if constexpr (EPI == kRedSwigluHiLo) {
-    uint16_t* hi = a.hi + (size_t)m * NO;
-    uint16_t* lo = a.lo + (size_t)m * NO;
-    if (m >= a.M) {
-      hi[n] = lo[n] = 0;
-      return;
+  const int m = blockIdx.y, tid = threadIdx.x;
+  const int n = blockIdx.x * 256 + tid;
+  const int NO = EPI == kRedSwiglu ? a.N / 2 : a.N;
+  if constexpr (EPI == kRedResidual) {
+    __shared__ float red[4];
+    float t = 0.f;
+    if (n < NO) {
+      float v = 0.f;
+      for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * kMmaRows + m) * a.N + n];
+      float* o = a.out + (size_t)m * a.ldo + n;
+      t = *o + v;
+      *o = t;
+      if (a.xg) a.xg[(size_t)m * a.N + n] = t * a.gain[n];
     }
+    if (a.ss) {
+      const float sq = wave_sum(t * t);
+      if ((tid & 63) == 0) red[tid >> 6] = sq;
+      __syncthreads();
+      if (tid == 0)
+        a.ss[(size_t)m * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+    }
+    return;
+  }
+  float inv = 1.f;
+  if (a.ss) {
+    float ss = 0.f;
+    for (int b = 0; b < a.nss; ++b) ss += a.ss[(size_t)m * a.nss + b];
+    inv = 1.0f / sqrtf(ss / (float)a.hn + a.eps);
+  }
+  if constexpr (EPI == kRedStore) {
+    if (a.y_out)
+      for (int j = n; j < a.hn; j += gridDim.x * 256)
+        a.y_out[(size_t)m * a.hn + j] = a.xg[(size_t)m * a.hn + j] * inv;
+  }
+  if (n >= NO) return;
+  if constexpr (EPI == kRedSwiglu) {
     float g = 0.f, u = 0.f;
     for (int s = 0; s < a.ks; ++s) {
       const float* P = a.part + ((size_t)s * kMmaRows + m) * a.N;
       g += P[n];
       u += P[NO + n];
     }
-    const float v = g / (1.0f + expf(-g)) * u;
-    const uint16_t h = f32_to_bf16(v);
-    hi[n] = h;
-    lo[n] = f32_to_bf16(v - __uint_as_float((uint32_t)h << 16));
+    g *= inv;
+    u *= inv;
+    a.out[(size_t)m * a.ldo + n] = g / (1.0f + expf(-g)) * u;
   } else {
-    if (m >= a.M) return;
     float v = 0.f;
     for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * kMmaRows + m) * a.N + n];
-    float* o = a.out + (size_t)m * a.ldo + n;
-    if constexpr (EPI == kRedStore) {
-      const int sg = n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
-      const int sb = sg == 0 ? 0 : a.seg_end[sg - 1];
-      *o = a.bias[sg] ? v + a.bias[sg][n - sb] : v;
-    } else {
-      *o = *o + v;
-    }
+    v *= inv;
+    const int sg = n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
+    const int sb = sg == 0 ? 0 : a.seg_end[sg - 1];
+    a.out[(size_t)m * a.ldo + n] = a.bias[sg] ? v + a.bias[sg][n - sb] : v;
   }
 }
 
@@ -1223,27 +1244,21 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_prep, dim3(kMmaRows), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   const dim3 grid((a.N + kMmaBlockN - 1) / kMmaBlockN, a.ks);
-  const size_t lds = 2ull * kMmaRows * kMmaKb * sizeof(uint16_t);
-  hipLaunchKernelGGL(k_gemm<kMmaKb / 32>, grid, dim3(256), lds, s, a);
+  hipLaunchKernelGGL(k_gemm<3>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, int epi, hipStream_t s) {
-  const int no = epi == kRedSwigluHiLo ? a.N / 2 : a.N;
-  const dim3 grid((no + 255) / 256, kMmaRows);
+  const int no = epi == kRedSwiglu ? a.N / 2 : a.N;
+  const dim3 grid((no + 255) / 256, a.M);
   if (epi == kRedStore)
     hipLaunchKernelGGL(k_reduce<kRedStore>, grid, dim3(256), 0, s, a);
   else if (epi == kRedResidual)
     hipLaunchKernelGGL(k_reduce<kRedResidual>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_reduce<kRedSwigluHiLo>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_reduce<kRedSwiglu>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

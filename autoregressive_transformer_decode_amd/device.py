@@ -9,12 +9,14 @@ data pointers and the current torch stream."""
 from __future__ import annotations
 
 import ctypes as C
+import dataclasses
 from typing import List, Optional, Sequence
 
 import numpy as np
 import torch
 
 from . import binding as B
+from . import inputs
 from .inputs import BF16, ModelShape, ModelWeights
 
 
@@ -99,9 +101,11 @@ class Decoder:
     """A decoder handle plus the KV buckets it holds for each slot."""
 
     def __init__(self, model: DeviceModel, max_slots: int = 1, max_rows: int = 1,
-                 max_ctx: int = 4096, mfma: bool = True):
+                 max_ctx: int = 4096, mfma: bool = True, kv_dtype: Optional[str] = None):
         self.model = model
         s = model.shape
+        if kv_dtype is not None and kv_dtype != s.kv_dtype:
+            s = dataclasses.replace(s, kv_dtype=kv_dtype)
         self.shape = s
         self.cfg = make_config(s, max_slots, max_rows, max_ctx,
                                flags=0 if mfma else B.ATD_FLAG_NO_MFMA)
@@ -183,9 +187,9 @@ class Decoder:
                            ptr(tokens_out), ptr(y_out), logits_out.data_ptr(), _stream())
         return logits_out
 
-    def time_stage(self, stage: int, slot: int = 0, reps: int = 8) -> float:
-        """Mean microseconds per launch of one projection stage (all layers)."""
-        return B.decoder_time_stage(self.handle, stage, slot, reps, _stream())
+    def time_stage(self, stage: int, slot0: int = 0, nrows: int = 1, reps: int = 8) -> float:
+        """Mean microseconds per layer of one decode stage over nrows slots."""
+        return B.decoder_time_stage(self.handle, stage, slot0, nrows, reps, _stream())
 
     def embed(self, tok: Optional[torch.Tensor], table_ids: Sequence[int], x_out: torch.Tensor,
               nrows: int = 1, extra: Optional[torch.Tensor] = None):
@@ -207,3 +211,21 @@ def greedy_argmax(logits: torch.Tensor, seen: Optional[torch.Tensor], penalty: f
 
 def seen_words(vocab: int) -> int:
     return (vocab + 31) // 32
+
+
+def fill_batched_caches(dec: "Decoder", lens: Sequence[int], seed: int = 0) -> None:
+    """Load the batched workload's synthetic caches: slot b gets its seeded
+    window of each layer's pool (inputs.batched_kv) in rows [0, lens[b]) and
+    its write position set to lens[b].  Buckets must be attached already."""
+    s = dec.shape
+    for l in range(s.n_layers):
+        pool = inputs.batched_kv_pool(s, l, seed=seed)
+        pk = torch.from_numpy(pool[0].view(np.int16)).cuda().view(torch.bfloat16)
+        pv = torch.from_numpy(pool[1].view(np.int16)).cuda().view(torch.bfloat16)
+        for b, n in enumerate(lens):
+            o, n = inputs.batched_kv_offset(b, int(n)), int(n)
+            dec.kv[b][0][l][:, :n].copy_(pk[:, o:o + n])
+            dec.kv[b][1][l][:, :n].copy_(pv[:, o:o + n])
+    for b, n in enumerate(lens):
+        dec.set_position(b, int(n))
+

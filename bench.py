@@ -163,7 +163,7 @@ def bench_lm(args, wl):
     # roofline: the dominant kernel's launches, every layer's weights in turn
     # as in a step, timed with HIP events on this stream
     reps = 16
-    avg_s = dec.time_stage(B.ATD_STAGE_GATEUP, 0, reps) / 1e6
+    avg_s = dec.time_stage(B.ATD_STAGE_GATEUP, 0, 1, reps) / 1e6
     launches = reps * s.n_layers
     per_launch = gateup_bytes(s)
     achieved = per_launch / avg_s / 1e9
@@ -197,13 +197,109 @@ def bench_lm(args, wl):
     return out
 
 
+def attn_stage_bytes(shape, lens) -> int:
+    """Algorithmic bytes of one layer's attention stage over a batch of decode
+    rows at cache lengths `lens`: every valid K and V row once, the new row
+    written, the step's q/k/v row in and the attention output out (float32)."""
+    kvb = 2 if shape.kv_dtype == "bf16" else 4
+    per_row = 2 * shape.kv_dim * kvb
+    B = len(lens)
+    qkv = shape.q_dim + 2 * shape.kv_dim
+    return int(sum(int(l) for l in lens)) * per_row + B * per_row + B * (qkv + shape.q_dim) * 4
+
+
+def bench_batched(args, wl, dm=None, steps=None, warmup=None):
+    """The batched workload: 64 streams, one decode step each per iteration,
+    seeded cache lengths, tokens fed back by the on-device greedy argmax."""
+    import numpy as np
+    import torch
+    from autoregressive_transformer_decode_amd import binding as B
+    from autoregressive_transformer_decode_amd import device as dv
+    from autoregressive_transformer_decode_amd import inputs
+
+    s = wl.model
+    Bn = wl.batch
+    K = steps if steps is not None else wl.steps
+    W = warmup if warmup is not None else 4
+    if dm is None:
+        dm = dv.DeviceModel(inputs.make_weights(s, seed=0))
+    lens = inputs.batched_lengths(wl, seed=0)
+    X1 = torch.from_numpy(inputs.batched_first_inputs(wl, seed=0)).cuda()
+    dec = dv.Decoder(dm, max_slots=Bn, max_rows=Bn, max_ctx=wl.s_max, kv_dtype=s.kv_dtype)
+    for b in range(Bn):
+        dec.grow(b, int(lens[b]) + max(K, W) + 1)
+    t = time.perf_counter()
+    dv.fill_batched_caches(dec, lens, seed=0)
+    torch.cuda.synchronize()
+    log(f"batched: {Bn} caches filled in {time.perf_counter() - t:.1f}s "
+        f"(lengths {int(lens.min())}..{int(lens.max())}, mean {float(lens.mean()):.0f})")
+    y = torch.empty(Bn, s.hidden, device="cuda")
+    z = torch.empty(Bn, s.vocab, device="cuda")
+    tok = torch.zeros(Bn, 1, dtype=torch.int32, device="cuda")
+
+    def iterations(n):
+        for it in range(n):
+            if it == 0:
+                dec.step(None, [], nrows=Bn, extra=X1, y_out=y, logits_out=z)
+            else:
+                dec.step(tok, [0], nrows=Bn, y_out=y, logits_out=z)
+            dv.greedy_argmax(z, None, 1.0, tok.view(Bn))
+
+    def rewind():
+        for b in range(Bn):
+            dec.set_position(b, int(lens[b]))
+
+    iterations(W)
+    rewind()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    iterations(K)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    log(f"batched: timed {K} iterations x {Bn} streams: {dt * 1e3:.1f} ms")
+    rewind()
+    torch.cuda.synchronize()
+    reps = 4
+    st = {name: dec.time_stage(code, 0, Bn, reps)
+          for name, code in (("qkv", B.ATD_STAGE_QKV), ("attention", B.ATD_STAGE_ATTN),
+                             ("o_proj", B.ATD_STAGE_OPROJ), ("gate_up", B.ATD_STAGE_GATEUP),
+                             ("down", B.ATD_STAGE_DOWN))}
+    dec.close()
+    a_bytes = attn_stage_bytes(s, lens)
+    a_gbs = a_bytes / (st["attention"] / 1e6) / 1e9
+    gu_flops = 2.0 * Bn * 2 * s.ffn * s.hidden
+    gu_w = 2 * s.ffn * s.hidden * (2 if s.dtype == "bf16" else 4)
+    mean_ctx = float(lens.mean()) + (K + 1) / 2.0
+    step_bytes = weight_bytes(s) + kv_row_bytes(s) * mean_ctx * Bn
+    ms_it = dt * 1e3 / K
+    return dict(
+        value=Bn * K / dt, unit="tokens/s", streams=Bn, iterations=K, warmup=W,
+        ms_per_iteration=ms_it,
+        config=dict(workload=wl.name, batch=Bn, kv_lengths=[int(lens.min()), int(lens.max())],
+                    kv_length_mean=float(lens.mean()), kv_dtype=s.kv_dtype,
+                    layers=s.n_layers, hidden=s.hidden, ffn=s.ffn, vocab=s.vocab),
+        roofline=dict(bound="hbm", achieved=a_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=a_gbs / HBM_PEAK_GBS, traffic=None,
+                      kernel="attention stage (k_attn_split + k_attn_combine), 64 rows",
+                      bytes_per_launch=a_bytes, avg_launch_us=st["attention"],
+                      launches_timed=reps * s.n_layers),
+        gemm_gate_up=dict(us=st["gate_up"], tflops=gu_flops / (st["gate_up"] / 1e6) / 1e12,
+                          mfma_peak_tflops=2500.0,
+                          weight_gbs=gu_w / (st["gate_up"] / 1e6) / 1e9),
+        stage_us_per_layer=st,
+        step_hbm=dict(algorithmic_bytes=step_bytes,
+                      achieved_gbs=step_bytes / (ms_it / 1e3) / 1e9,
+                      frac=step_bytes / (ms_it / 1e3) / 1e9 / HBM_PEAK_GBS),
+    )
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="talker1.7b",
-                    choices=["talker1.7b", "asr", "tiny"])
+                    choices=["talker1.7b", "asr", "tiny", "batched64"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -228,7 +324,16 @@ def main():
         return
     from autoregressive_transformer_decode_amd import inputs
     wl = inputs.WORKLOADS[args.workload]
-    out = bench_lm(args, wl)
+    if wl.batch > 1:
+        r = bench_batched(args, wl, steps=args.steps, warmup=args.warmup)
+        out = dict(metric=METRIC, value=r["value"], unit="tokens/s", n_gpus=1, steps=r["iterations"],
+                   warmup=r["warmup"], ms_per_step=r["ms_per_iteration"], higher_is_better=True,
+                   scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+                   config=r["config"], roofline=r["roofline"], gemm_gate_up=r["gemm_gate_up"],
+                   stage_us_per_layer=r["stage_us_per_layer"], step_hbm=r["step_hbm"],
+                   cpu_baseline=None)
+    else:
+        out = bench_lm(args, wl)
     print(json.dumps(out), flush=True)
 
 

@@ -259,16 +259,20 @@ enum {
   ATD_STAGE_COUNT = 7
 };
 
-/* Measurement: enqueue the kernels of one per-layer projection stage
- * (ATD_STAGE_QKV, _OPROJ, _GATEUP or _DOWN) of a one-row decode step of `slot` for
- * every layer in turn (each layer's weights once, as in a step), `reps`
+/* Measurement: enqueue the kernels of one per-layer stage (ATD_STAGE_QKV,
+ * _ATTN, _OPROJ, _GATEUP or _DOWN) of a decode step of the B rows on slots
+ * slot0 .. slot0+B-1 (the launch shapes of decoder_step with those rows:
+ * the vector kernels for B <= 2, the 64-row matrix-core chunks otherwise)
+ * for every layer in turn (each layer's weights once, as in a step), `reps`
  * times, between two HIP events recorded on `stream`, and return the mean
- * time per launch in microseconds.  The kernels read and write only the
- * decoder's own scratch (the residual stream they update there is rebuilt
- * by the next step or prefill); caller memory and slot positions are not
- * touched.  Waits for the stream.  Errors: INVALID_ARG, DEVICE. */
-int decoder_time_stage(atd_decoder* dec, int32_t stage, int32_t slot, int32_t reps,
-                       void* stream, double* us_per_launch);
+ * time of the stage per layer in microseconds.  The kernels read and write
+ * the decoder's own scratch (the residual stream they update there is
+ * rebuilt by the next step or prefill); ATD_STAGE_ATTN also writes the
+ * not-yet-valid cache row at each slot's write position, which the next
+ * step overwrites.  Slot positions do not move.  Waits for the stream.
+ * Errors: INVALID_ARG, CAPACITY, DEVICE. */
+int decoder_time_stage(atd_decoder* dec, int32_t stage, int32_t slot0, int32_t B,
+                       int32_t reps, void* stream, double* us_per_layer);
 
 #ifdef __cplusplus
 }

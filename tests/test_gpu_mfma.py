@@ -121,20 +121,13 @@ def test_batched64_full_size_sampled_streams():
     sample = [int(np.argmin(lens)), int(np.argmax(lens)), 17]
     om = oracle_from_weights(mw, np.float32)
     caches = {b: od.Cache(om, caps[b]) for b in sample}
+    dv.fill_batched_caches(dec, lens, seed=0)
     for l in range(s.n_layers):
         pool = inputs.batched_kv_pool(s, l, seed=0)
-        pk = torch.from_numpy(pool[0].view(np.int16)).cuda().view(torch.bfloat16)
-        pv = torch.from_numpy(pool[1].view(np.int16)).cuda().view(torch.bfloat16)
-        for b in range(Bn):
-            o, n = inputs.batched_kv_offset(b, int(lens[b])), int(lens[b])
-            dec.kv[b][0][l][:, :n].copy_(pk[:, o:o + n])
-            dec.kv[b][1][l][:, :n].copy_(pv[:, o:o + n])
         for b in sample:
             k, v = inputs.batched_kv(s, b, int(lens[b]), l, pool=pool)
             caches[b].K[l][:, :lens[b]] = inputs.bf16_bits_to_f32(k)
             caches[b].V[l][:, :lens[b]] = inputs.bf16_bits_to_f32(v)
-    for b in range(Bn):
-        dec.set_position(b, int(lens[b]))
     for b in sample:
         caches[b].pos = int(lens[b])
     torch.cuda.synchronize()

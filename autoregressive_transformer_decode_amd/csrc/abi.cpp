@@ -40,7 +40,7 @@ struct atd_decoder {
   bool mma = false;            // MFMA path for chunks of >= 3 rows
   float* mpart = nullptr;      // split-K partials of the MFMA GEMMs
   float* mss = nullptr;        // row sums of squares [kMmaRows, ceil(h / kSsCols)]
-  float* mxg = nullptr;        // normalised-GEMM input x * gain [kMmaRows, h]
+  uint16_t *mhi = nullptr, *mlo = nullptr;  // GEMM input as bf16 hi/lo [kMmaRows, Kmax]
   int32_t* counter = nullptr;  // token counter of decoder_generate
   size_t part_floats = 0;      // capacity of pacc in floats / D
   bool dry = false;  // ATD_FLAG_DRY_RUN: host state only, no HIP calls
@@ -373,13 +373,13 @@ hipError_t run_head_gemv(atd_decoder* d, const float* xrows, int M, int head, fl
 }
 
 // MFMA path pieces -----------------------------------------------------------
-// GEMM of the M rows of x ([M, K]) with an [N, K] weight given as up to three
-// row segments; split partials into d->mpart.
-hipError_t mma_gemm(atd_decoder* d, const float* x, int M, const void* w0, const void* w1,
-                    const void* w2, int e0, int e1, int N, int K, hipStream_t s) {
+// GEMM of the chunk's activations (d->mhi / d->mlo, [kMmaRows, K]) with an
+// [N, K] weight given as up to three row segments; split partials into d->mpart.
+hipError_t mma_gemm(atd_decoder* d, const void* w0, const void* w1, const void* w2, int e0,
+                    int e1, int N, int K, hipStream_t s) {
   GemmArgs g{};
-  g.x = x;
-  g.M = M;
+  g.hi = d->mhi;
+  g.lo = d->mlo;
   g.W[0] = w0;
   g.W[1] = w1;
   g.W[2] = w2;
@@ -410,15 +410,16 @@ ReduceArgs mma_red(atd_decoder* d, int N, int ks, int M, float* out, int ldo) {
   return r;
 }
 
-// x += splits (ks = 0: none), then xg = x * gain and the row sums of squares
-// for the next normalised GEMM
+// x += splits (ks = 0: none), then x * gain as the next GEMM's hi/lo input
+// and the row sums of squares for its norm factor
 hipError_t mma_residual(atd_decoder* d, int ks, int M, float* x, const float* gain,
                         hipStream_t s) {
   const int h = d->cfg.hidden;
   ReduceArgs r = mma_red(d, h, ks, M, x, h);
   r.ss = d->mss;
   r.gain = gain;
-  r.xg = d->mxg;
+  r.hi = d->mhi;
+  r.lo = d->mlo;
   return launch_reduce(r, kRedResidual, s);
 }
 
@@ -431,9 +432,9 @@ struct HeadOut {
 
 // MFMA path for one chunk of 3..kMmaRows rows: every layer, then (if asked)
 // the final norm and LM head.  Kernel chain per layer: GEMM q/k/v of x*g ->
-// norm factor + bias -> attention (split + combine) -> GEMM o -> residual
-// (+ x*g, sums of squares) -> GEMM gate/up -> norm factor + SwiGLU -> GEMM
-// down -> residual (+ x*g for the next norm, sums of squares).
+// norm factor + bias -> attention (split + combine, o as hi/lo) -> GEMM o ->
+// residual (+ x*g as hi/lo, sums of squares) -> GEMM gate/up -> norm factor
+// + SwiGLU (as hi/lo) -> GEMM down -> residual (+ x*g for the next norm).
 hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
                          const HeadOut* ho, hipStream_t s) {
   const atd_config& c = d->cfg;
@@ -441,14 +442,13 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
   const int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv, F = c.ffn;
   const int kv_bf16 = c.kv_dtype == ATD_BF16;
   const bool fused = rows.mode == kRowsStep;
-  float* xg = d->mxg;
   hipError_t e = hipSuccess;
   STAGE(ATD_STAGE_QKV, mma_residual(d, 0, M, x, (const float*)d->layers[0].attn_norm, s));
   for (int l = 0; l < c.n_layers; ++l) {
     const atd_layer_weights& W = d->layers[l];
     const float* next_gain =
         l + 1 < c.n_layers ? (const float*)d->layers[l + 1].attn_norm : d->final_norm;
-    STAGE(ATD_STAGE_QKV, mma_gemm(d, xg, M, W.wq, W.wk, W.wv, nq, nq + nkv, nqkv, h, s));
+    STAGE(ATD_STAGE_QKV, mma_gemm(d, W.wq, W.wk, W.wv, nq, nq + nkv, nqkv, h, s));
     ReduceArgs rq = mma_red(d, nqkv, mma_ks(nqkv, h), M, d->qkv, nqkv);
     rq.bias[0] = (const float*)W.bq;
     rq.bias[1] = (const float*)W.bk;
@@ -458,23 +458,28 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
     rq.ss = d->mss;
     STAGE(ATD_STAGE_QKV, launch_reduce(rq, kRedStore, s));
     if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
-    STAGE(ATD_STAGE_ATTN, launch_attention(attn_args(d, rows, l, M, max_len_bound, fused),
-                                           kv_bf16, D, Hq / Hkv, s));
-    STAGE(ATD_STAGE_OPROJ, mma_gemm(d, d->o, M, W.wo, W.wo, W.wo, h, h, h, nq, s));
+    AttnArgs aa = attn_args(d, rows, l, M, max_len_bound, fused);
+    aa.o_hi = d->mhi;
+    aa.o_lo = d->mlo;
+    STAGE(ATD_STAGE_ATTN, launch_attention(aa, kv_bf16, D, Hq / Hkv, s));
+    STAGE(ATD_STAGE_OPROJ, mma_gemm(d, W.wo, W.wo, W.wo, h, h, h, nq, s));
     STAGE(ATD_STAGE_OPROJ, mma_residual(d, mma_ks(h, nq), M, x, (const float*)W.mlp_norm, s));
-    STAGE(ATD_STAGE_GATEUP, mma_gemm(d, xg, M, W.w_gate, W.w_up, W.w_up, F, 2 * F, 2 * F, h, s));
-    ReduceArgs rg = mma_red(d, 2 * F, mma_ks(2 * F, h), M, d->act, F);
+    STAGE(ATD_STAGE_GATEUP, mma_gemm(d, W.w_gate, W.w_up, W.w_up, F, 2 * F, 2 * F, h, s));
+    ReduceArgs rg = mma_red(d, 2 * F, mma_ks(2 * F, h), M, nullptr, 0);
     rg.ss = d->mss;
+    rg.hi = d->mhi;
+    rg.lo = d->mlo;
     STAGE(ATD_STAGE_GATEUP, launch_reduce(rg, kRedSwiglu, s));
-    STAGE(ATD_STAGE_DOWN, mma_gemm(d, d->act, M, W.w_down, W.w_down, W.w_down, h, h, h, F, s));
+    STAGE(ATD_STAGE_DOWN, mma_gemm(d, W.w_down, W.w_down, W.w_down, h, h, h, F, s));
     STAGE(ATD_STAGE_DOWN, mma_residual(d, mma_ks(h, F), M, x, next_gain, s));
   }
   if (ho) {
     const void* Wh = d->heads[ho->head];
-    STAGE(ATD_STAGE_HEAD, mma_gemm(d, xg, M, Wh, Wh, Wh, c.vocab, c.vocab, c.vocab, h, s));
+    STAGE(ATD_STAGE_HEAD, mma_gemm(d, Wh, Wh, Wh, c.vocab, c.vocab, c.vocab, h, s));
     ReduceArgs rh = mma_red(d, c.vocab, mma_ks(c.vocab, h), M, ho->logits, c.vocab);
     rh.ss = d->mss;
-    rh.xg = xg;
+    rh.x = x;
+    rh.gain = d->final_norm;
     rh.y_out = ho->y_out;
     STAGE(ATD_STAGE_HEAD, launch_reduce(rh, kRedStore, s));
   }
@@ -618,13 +623,15 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   // the largest GEMM (q/k/v, o, gate/up, down, LM head)
   d->mma = cfg->dtype == ATD_BF16 && !(cfg->flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 &&
            nq % 32 == 0 && cfg->ffn % 32 == 0 && std::max(R, S) >= 3;
-  size_t o_mss = 0, o_mxg = 0, o_mpart = 0;
+  size_t o_mss = 0, o_mhi = 0, o_mlo = 0, o_mpart = 0;
   if (d->mma) {
     auto parts = [](int n, int k) { return (size_t)mma_ks(n, k) * kMmaRows * n; };
     const size_t pmax = std::max({parts(nqkv, h), parts(h, nq), parts(2 * cfg->ffn, h),
                                   parts(h, cfg->ffn), parts(cfg->vocab, h)});
     o_mss = carve((size_t)kMmaRows * ((h + kSsCols - 1) / kSsCols) * 4);
-    o_mxg = carve((size_t)kMmaRows * h * 4);
+    const size_t kmax = std::max({(size_t)h, (size_t)nq, (size_t)cfg->ffn});
+    o_mhi = carve((size_t)kMmaRows * kmax * 2);
+    o_mlo = carve((size_t)kMmaRows * kmax * 2);
     o_mpart = carve(pmax * 4);
   }
 
@@ -652,7 +659,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->counter = (int32_t*)(base + o_cnt);
   if (d->mma) {
     d->mss = (float*)(base + o_mss);
-    d->mxg = (float*)(base + o_mxg);
+    d->mhi = (uint16_t*)(base + o_mhi);
+    d->mlo = (uint16_t*)(base + o_mlo);
     d->mpart = (float*)(base + o_mpart);
   }
 

@@ -125,6 +125,8 @@ struct AttnArgs {
   float* pml;         // [M, Hq, nsplit_max, 2] running max and sum
   float* pacc;        // [M, Hq, nsplit_max, D]
   float* o;           // [M, Hq * D] (combine output)
+  uint16_t* o_hi;     // or, when set, bf16 hi/lo parts of o: [kMmaRows, Hq * D]
+  uint16_t* o_lo;
 };
 
 struct EmbedArgs {
@@ -181,8 +183,8 @@ inline int mma_ks(int N, int K) {
 }
 
 struct GemmArgs {
-  const float* x;      // activations [M, K] (row stride K), M <= kMmaRows
-  int M;
+  const uint16_t* hi;  // activations as bf16 hi + lo parts [kMmaRows, K]; rows >= M may
+  const uint16_t* lo;  // hold anything (each output row depends on its own row only)
   const void* W[3];    // bf16 row segments [rows_s, K]
   int seg_end[3];
   int K, N;            // K multiple of 32
@@ -193,24 +195,26 @@ struct GemmArgs {
 enum ReduceEpilogue { kRedStore = 0, kRedResidual = 1, kRedSwiglu = 2 };
 
 // RMSNorm(x) W^T = inv_m * ((x * g) W^T) with inv_m = 1 / sqrt(mean(x_m^2) + eps):
-// the residual reduction leaves x * g (the next GEMM's input) and partial sums
-// of squares of x; the reduction after that GEMM applies inv_m.
+// the residual reduction leaves x * g (the next GEMM's input, as hi/lo) and
+// partial sums of squares of x; the reduction after that GEMM applies inv_m.
 struct ReduceArgs {
   const float* part;   // [ks, kMmaRows, N]
-  int ks, N, M;        // ks = 0: no partials (kRedResidual then only refreshes xg / ss)
+  int ks, N, M;        // ks = 0: no partials (kRedResidual then only refreshes hi/lo, ss)
   const float* bias[3];  // kRedStore: per-segment bias or null
   int seg_end[3];
-  float* out;          // [M, ldo]: kRedStore / kRedSwiglu write, kRedResidual adds
+  float* out;          // kRedStore: [M, ldo] written; kRedResidual: [M, ldo] updated
   int ldo;
-  // kRedResidual: writes ss [M, gridDim.x] (kSsCols-column partial sums of squares
-  // of the updated rows) and xg = out * gain.  kRedStore / kRedSwiglu: when ss is
-  // set, the sums are scaled by inv_m from ss [M, nss] over hn columns.
+  uint16_t* hi;        // kRedResidual: x * gain; kRedSwiglu: the activation ([kMmaRows, N or N/2])
+  uint16_t* lo;
+  const float* gain;   // kRedResidual: gain of the next norm; kRedStore: gain for y_out
+  // kRedResidual writes ss [M, gridDim.x] (kSsCols-column partial sums of squares
+  // of the updated rows); kRedStore / kRedSwiglu with ss set scale the sums by
+  // inv_m from ss [M, nss] over hn columns.
   float* ss;
   int nss, hn;
   float eps;
-  const float* gain;
-  float* xg;           // [M, N] (kRedResidual) / read for y_out (kRedStore)
-  float* y_out;        // kRedStore: normalised rows xg * inv_m [M, hn] or null
+  const float* x;      // kRedStore: rows whose norm goes to y_out ([M, hn])
+  float* y_out;        // kRedStore: x * inv_m * gain [M, hn] or null
 };
 
 // ---------------------------------------------------------------- launchers

@@ -413,6 +413,13 @@ __device__ __forceinline__ void norm_rope_lanes(float (&v)[VEC], int dl, bool do
   }
 }
 
+// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi): ~16 significant bits
+// in two bf16 matrix-core operands
+__device__ __forceinline__ void split_hi_lo(float v, uint16_t& h, uint16_t& l) {
+  h = f32_to_bf16(v);
+  l = f32_to_bf16(v - __uint_as_float((uint32_t)h << 16));
+}
+
 template <typename KT, int VEC>
 __device__ __forceinline__ uint4 pack_kv(const float (&v)[VEC]) {
   uint4 r;
@@ -760,8 +767,20 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
       r.z += part[p][c].z;
       r.w += part[p][c].w;
     }
-    float4* out = reinterpret_cast<float4*>(a.o + ((size_t)m * a.Hq + h) * D) + c;
-    *out = make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
+    const float v[4] = {r.x / L, r.y / L, r.z / L, r.w / L};
+    if (a.o_hi) {
+      const size_t off = ((size_t)m * a.Hq + h) * D + 4 * c;
+      uint16_t hv[4], lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split_hi_lo(v[i], hv[i], lv[i]);
+      *reinterpret_cast<uint2*>(a.o_hi + off) =
+          make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+      *reinterpret_cast<uint2*>(a.o_lo + off) =
+          make_uint2(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
+    } else {
+      float4* out = reinterpret_cast<float4*>(a.o + ((size_t)m * a.Hq + h) * D) + c;
+      *out = make_float4(v[0], v[1], v[2], v[3]);
+    }
   }
 }
 
@@ -899,15 +918,14 @@ __device__ __forceinline__ Bf16x8 as_bf16x8(uint4 v) {
 }
 
 // Split-K GEMM of a chunk of up to 64 rows: part[split, m, n] = sum over the
-// split's K range of x[m, k] * W[n, k], with x entering as bf16 hi + lo
-// parts: bf16 MFMA 16x16x32, float32 accumulation.  Workgroup (64 weight
-// rows, split): wave w owns 16 rows.  The split is walked in 64-wide stages;
-// each stage's activation tile (64 rows) is read with row-contiguous loads,
-// split into hi/lo in registers and stored to a double-buffered LDS tile, from
-// which every wave reads its MFMA fragments, while the weight fragments go
-// straight to registers.  Both come through a P-deep register ring, so the
-// loads of P stages are in flight while a stage is multiplied, and the
-// in-order memory counter only ever waits for the oldest stage.
+// split's K range of (hi + lo)[m, k] * W[n, k]: bf16 MFMA 16x16x32, float32
+// accumulation.  Workgroup (64 weight rows, split): wave w owns 16 rows.  The
+// split is walked in 64-wide stages; each stage's activation tile (64 rows,
+// hi and lo) is read with row-contiguous loads into a double-buffered LDS
+// tile, from which every wave reads its MFMA fragments, while the weight
+// fragments go straight to registers.  Both come through a P-deep register
+// ring, so the loads of P stages are in flight while a stage is multiplied,
+// and the in-order memory counter only ever waits for the oldest stage.
 template <int P>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   // LDS tile [buf][hi/lo][row][8 x 16 bytes]; the 16-byte chunk c of row r
@@ -926,22 +944,21 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   // rows past N read row 0 of the segment (in bounds); their sums are not stored
   const uint16_t* wp = reinterpret_cast<const uint16_t*>(a.W[sg]) +
                        (size_t)(row < a.N ? row - sb : 0) * K + lg * 8;
-  // staging: thread -> rows srow and srow + 32, k group sc (8 values)
+  // staging: thread -> rows srow and srow + 32, 16-byte group sc
   const int srow = tid >> 3, sc = tid & 7;
-  const bool r0ok = srow < a.M, r1ok = srow + 32 < a.M;
-  const float* x0 = a.x + (size_t)(r0ok ? srow : 0) * K + sc * 8;
-  const float* x1 = a.x + (size_t)(r1ok ? srow + 32 : 0) * K + sc * 8;
+  const uint16_t* sh = a.hi + (size_t)srow * K + sc * 8;
+  const uint16_t* sl = a.lo + (size_t)srow * K + sc * 8;
 
   uint4 ar[P][4], wr[P][2];
   auto issue_a = [&](int p, int c) {
     const int k = kb + c * kMmaCh + sc * 8;
-    const bool ok = k < ke;   // whole groups of 8: K and the split ends are multiples of 32
+    const bool ok = k < ke;   // whole groups: K and the split ends are multiples of 32
     const int kk = ok ? k - sc * 8 : 0;
     const uint4 z = make_uint4(0, 0, 0, 0);
-    ar[p][0] = ok && r0ok ? ldg16(x0 + kk) : z;
-    ar[p][1] = ok && r0ok ? ldg16(x0 + kk + 4) : z;
-    ar[p][2] = ok && r1ok ? ldg16(x1 + kk) : z;
-    ar[p][3] = ok && r1ok ? ldg16(x1 + kk + 4) : z;
+    ar[p][0] = ok ? ldg16(sh + kk) : z;
+    ar[p][1] = ok ? ldg16(sh + (size_t)32 * K + kk) : z;
+    ar[p][2] = ok ? ldg16(sl + kk) : z;
+    ar[p][3] = ok ? ldg16(sl + (size_t)32 * K + kk) : z;
   };
   auto issue_w = [&](int p, int c) {
     // stages past the split end read in-bounds weights that meet zero activations
@@ -963,23 +980,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       if (c < nch) {
         const int buf = c & 1;
         const int sw = sc ^ (srow & 7);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const uint4 u0 = ar[p][2 * q], u1 = ar[p][2 * q + 1];
-          const uint32_t u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-          uint32_t hw[4], lw[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v0 = __uint_as_float(u[2 * e]), v1 = __uint_as_float(u[2 * e + 1]);
-            const uint16_t h0 = f32_to_bf16(v0), h1 = f32_to_bf16(v1);
-            const uint16_t l0 = f32_to_bf16(v0 - __uint_as_float((uint32_t)h0 << 16));
-            const uint16_t l1 = f32_to_bf16(v1 - __uint_as_float((uint32_t)h1 << 16));
-            hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-          }
-          sa[buf][0][srow + 32 * q][sw] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-          sa[buf][1][srow + 32 * q][sw] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        }
+        sa[buf][0][srow][sw] = ar[p][0];
+        sa[buf][0][srow + 32][sw] = ar[p][1];
+        sa[buf][1][srow][sw] = ar[p][2];
+        sa[buf][1][srow + 32][sw] = ar[p][3];
         __syncthreads();
         issue_a(p, c + P);
 #pragma unroll
@@ -998,8 +1002,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       }
     }
   }
-  // C layout: column li, rows 4 * lg + r of each 16x16 tile; rows >= M hold
-  // zero products and are stored too (the reduction ignores them)
+  // C layout: column li, rows 4 * lg + r of each 16x16 tile
   if (row < a.N) {
     float* Pp = a.part + (size_t)split * kMmaRows * a.N + row;
 #pragma unroll
@@ -1024,15 +1027,12 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
       float* o = a.out + (size_t)m * a.ldo + n;
       t = *o + v;
       *o = t;
-      if (a.xg) a.xg[(size_t)m * a.N + n] = t * a.gain[n];
+      split_hi_lo(t * a.gain[n], a.hi[(size_t)m * a.N + n], a.lo[(size_t)m * a.N + n]);
     }
-    if (a.ss) {
-      const float sq = wave_sum(t * t);
-      if ((tid & 63) == 0) red[tid >> 6] = sq;
-      __syncthreads();
-      if (tid == 0)
-        a.ss[(size_t)m * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
-    }
+    const float sq = wave_sum(t * t);
+    if ((tid & 63) == 0) red[tid >> 6] = sq;
+    __syncthreads();
+    if (tid == 0) a.ss[(size_t)m * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
     return;
   }
   float inv = 1.f;
@@ -1044,7 +1044,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
   if constexpr (EPI == kRedStore) {
     if (a.y_out)
       for (int j = n; j < a.hn; j += gridDim.x * 256)
-        a.y_out[(size_t)m * a.hn + j] = a.xg[(size_t)m * a.hn + j] * inv;
+        a.y_out[(size_t)m * a.hn + j] = a.x[(size_t)m * a.hn + j] * inv * a.gain[j];
   }
   if (n >= NO) return;
   if constexpr (EPI == kRedSwiglu) {
@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     }
     g *= inv;
     u *= inv;
-    a.out[(size_t)m * a.ldo + n] = g / (1.0f + expf(-g)) * u;
+    split_hi_lo(g / (1.0f + expf(-g)) * u, a.hi[(size_t)m * NO + n], a.lo[(size_t)m * NO + n]);
   } else {
     float v = 0.f;
     for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * kMmaRows + m) * a.N + n];

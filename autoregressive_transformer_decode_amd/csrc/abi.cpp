@@ -249,6 +249,13 @@ AttnArgs attn_args(const atd_decoder* d, RowMap rows, int l, int M, int max_len_
   return a;
 }
 
+// Attention launch; its partials must fit the buffer sized at creation (a
+// broken sizing invariant is reported, never written past).
+hipError_t attention(const atd_decoder* d, const AttnArgs& a, hipStream_t s) {
+  if ((size_t)a.M * a.Hq * a.nsplit_max > d->part_floats) return hipErrorInvalidValue;
+  return launch_attention(a, d->cfg.kv_dtype == ATD_BF16, d->cfg.head_dim, a.Hq / a.Hkv, s);
+}
+
 RopeArgs rope_args(const atd_decoder* d, RowMap rows, int l, int M) {
   const atd_config& c = d->cfg;
   const atd_layer_weights& W = d->layers[l];
@@ -305,8 +312,7 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
     STAGE(ATD_STAGE_QKV, launch_gemv(g, kEpiStore, true, bf16, s));
     // prefill rows of one slot read each other's keys: append them all first
     if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
-    STAGE(ATD_STAGE_ATTN, launch_attention(attn_args(d, rows, l, M, max_len_bound, fused),
-                                           kv_bf16, D, Hq / Hkv, s));
+    STAGE(ATD_STAGE_ATTN, attention(d, attn_args(d, rows, l, M, max_len_bound, fused), s));
 
     GemvArgs op{};
     op.W[0] = W.wo;
@@ -461,7 +467,7 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
     AttnArgs aa = attn_args(d, rows, l, M, max_len_bound, fused);
     aa.o_hi = d->mhi;
     aa.o_lo = d->mlo;
-    STAGE(ATD_STAGE_ATTN, launch_attention(aa, kv_bf16, D, Hq / Hkv, s));
+    STAGE(ATD_STAGE_ATTN, attention(d, aa, s));
     STAGE(ATD_STAGE_OPROJ, mma_gemm(d, W.wo, W.wo, W.wo, h, h, h, nq, s));
     STAGE(ATD_STAGE_OPROJ, mma_residual(d, mma_ks(h, nq), M, x, (const float*)W.mlp_norm, s));
     STAGE(ATD_STAGE_GATEUP, mma_gemm(d, W.w_gate, W.w_up, W.w_up, F, 2 * F, 2 * F, h, s));
@@ -1046,10 +1052,10 @@ extern "C" int decoder_time_stage(atd_decoder* d, int32_t stage, int32_t slot0, 
   int bound = 1;
   for (int b = slot0; b < slot0 + B; ++b) {
     if (!d->attached[b]) return fail(d, ATD_ERR_INVALID_ARG, "slot %d is not attached", b);
-    if (d->pos[b] >= d->cap[b])
+    if (stage == ATD_STAGE_ATTN && d->pos[b] >= d->cap[b])   // it writes the row at pos
       return fail(d, ATD_ERR_KV_FULL, "slot %d: position %d at capacity %d", b, d->pos[b],
                   d->cap[b]);
-    bound = std::max(bound, d->pos[b] + 1);
+    bound = std::max(bound, std::min(d->pos[b] + 1, d->cap[b]));
   }
   if (reps < 1) return fail(d, ATD_ERR_INVALID_ARG, "reps %d < 1", reps);
   if (!us_per_layer) return fail(d, ATD_ERR_INVALID_ARG, "us_per_layer is NULL");

@@ -13,8 +13,9 @@ constexpr int kMaxTables = 16;
 constexpr int kMaxLayers = 64;
 constexpr int kGemvMaxRows = 2;      // rows a GEMV launch handles at once
 constexpr int kArgmaxChunk = 4096;   // logits per argmax block
-constexpr int kAttnWavesMax = 2048;  // largest split-count target of a launch
-constexpr int kAttnMinChunk = 16;    // fewest keys per split
+constexpr int kAttnWavesMax = 8192;   // largest split-count target of a launch
+constexpr int kAttnSplitsMax = 256;   // most splits of one (row, KV head)
+constexpr int kAttnMinChunk = 16;     // fewest keys per split
 
 #if defined(__HIP__)
 #define ATD_HD __host__ __device__
@@ -23,12 +24,14 @@ constexpr int kAttnMinChunk = 16;    // fewest keys per split
 #endif
 
 // Keys per attention split for a row whose valid length is len, in a launch
-// of M rows over Hkv KV heads aiming at `waves` splits in total: at least
+// of M rows over Hkv KV heads aiming at `waves` splits in total: every row
+// gets the same number of splits (all waves busy), each at least
 // kAttnMinChunk keys, a multiple of 16.  Depends on (len, M, Hkv, waves)
-// only, never on the cache capacity.
+// only, never on the cache capacity (results do not change when a bucket
+// grows).
 inline ATD_HD int attn_splits_per_head(int M, int Hkv, int waves) {
   const int per = waves / (M * Hkv);
-  return per < 1 ? 1 : per;
+  return per < 1 ? 1 : (per > kAttnSplitsMax ? kAttnSplitsMax : per);
 }
 inline ATD_HD int attn_chunk(int len, int M, int Hkv, int waves) {
   const int per = attn_splits_per_head(M, Hkv, waves);

@@ -436,15 +436,14 @@ __device__ __forceinline__ uint4 pack_kv(const float (&v)[VEC]) {
   return r;
 }
 
-template <typename KT, int D, int R>
+template <typename KT, int D, int R, int LPK, int U>
 __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   constexpr int VEC = Vec16<KT>::N;   // channels per 16-byte load
-  constexpr int LPK = 8;              // lanes per key row
-  constexpr int DPL = D / LPK;        // channels per lane
+  constexpr int DPL = D / LPK;        // channels per lane (LPK lanes per key row)
   constexpr int NV = DPL / VEC;       // 16-byte loads per lane per row
   constexpr int KPW = 64 / LPK;       // key rows per wave-wide load
-  constexpr int U = 2;                // key rows per lane group per tile
-  constexpr int TILE = KPW * U;       // keys per wave per tile
+  constexpr int TILE = KPW * U;       // keys per wave per tile (U rows per lane group)
+  static_assert(NV >= 1 && DPL % 4 == 0, "a lane holds whole 16-byte groups");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x * 4 + wave, g = blockIdx.y, m = blockIdx.z;
@@ -603,7 +602,8 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   }
 
   for (int kb = k0; kb < k1; kb += TILE) {
-    float kt[U][DPL], vt[U][DPL];
+    // the tile's raw rows (unpacked to float where used, to keep registers low)
+    uint4 kc[U][NV], vc[U][NV];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -612,8 +612,8 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       const bool fresh = owns_new && key == pos;   // the cache row may not be written yet
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        Vec16<KT>::unpack(fresh ? knew[v] : kr[u][v], &kt[u][v * VEC]);
-        Vec16<KT>::unpack(fresh ? vnew[v] : vr[u][v], &vt[u][v * VEC]);
+        kc[u][v] = fresh ? knew[v] : kr[u][v];
+        vc[u][v] = fresh ? vnew[v] : vr[u][v];
       }
     }
     if (kb + TILE < k1) load(kb + TILE);
@@ -625,7 +625,12 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       for (int u = 0; u < U; ++u) {
         float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) d = fmaf(qv[j][e], kt[u][e], d);
+        for (int v = 0; v < NV; ++v) {
+          float kv[VEC];
+          Vec16<KT>::unpack(kc[u][v], kv);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) d = fmaf(qv[j][v * VEC + e], kv[e], d);
+        }
         sc[u] = group_sum<LPK>(d);
         if (ok[u]) tmax = fmaxf(tmax, sc[u]);
       }
@@ -639,21 +644,24 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
         const float p = ok[u] ? expf(sc[u] - tmax) : 0.f;
         ls[j] += p;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[j][e] = fmaf(p, vt[u][e], acc[j][e]);
+        for (int v = 0; v < NV; ++v) {
+          float vv[VEC];
+          Vec16<KT>::unpack(vc[u][v], vv);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[j][v * VEC + e] = fmaf(p, vv[e], acc[j][v * VEC + e]);
+        }
       }
       mx[j] = tmax;
     }
   }
 
-  // merge the KPW key groups of the wave (lanes with equal dl): xor 8 by DPP,
-  // xor 16 and 32 across rows
+  // merge the KPW key groups of the wave (lanes with equal dl): xor LPK,
+  // 2 LPK, ... 32 (xor 8 within a row of 16 lanes by DPP)
 #pragma unroll
-  for (int step = 0; step < 3; ++step) {
+  for (int off = LPK; off < 64; off <<= 1) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      auto xch = [&](float v) {
-        return step == 0 ? dpp<kDppRor8>(v) : __shfl_xor(v, step == 1 ? 16 : 32, 64);
-      };
+      auto xch = [&](float v) { return off == 8 ? dpp<kDppRor8>(v) : __shfl_xor(v, off, 64); };
       const float om = xch(mx[j]);
       const float ol = xch(ls[j]);
       const float nm = fmaxf(mx[j], om);
@@ -693,7 +701,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   constexpr int NC = D / 4;        // float4 channel groups
   constexpr int NSP = 256 / NC;    // split phases
   constexpr int PRE = 4;           // partials per thread loaded ahead of the position
-  __shared__ float wgt[kAttnWavesMax + 1];
+  __shared__ float wgt[kAttnSplitsMax + 1];
   __shared__ float red[2][4];
   __shared__ float4 part[NSP][NC];
   const int h = blockIdx.x, m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1168,11 +1176,15 @@ hipError_t launch_rope_append(const RopeArgs& a, int bf16, hipStream_t s) {
 
 template <typename KT, int D>
 static void attn_dispatch_r(const AttnArgs& a, int r, dim3 grid, hipStream_t s) {
+  // lanes per key row and rows per lane group per tile
+  constexpr int LPK0 = sizeof(KT) == 2 ? 8 : 8;
+  constexpr int LPK = LPK0 < D / Vec16<KT>::N ? LPK0 : D / Vec16<KT>::N;
+  constexpr int U = sizeof(KT) == 2 ? 2 : 2;
   switch (r) {
-    case 1: hipLaunchKernelGGL((k_attn_split<KT, D, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_split<KT, D, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_split<KT, D, 4>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_attn_split<KT, D, 8>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_attn_split<KT, D, 1, LPK, U>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_split<KT, D, 2, LPK, U>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_split<KT, D, 4, LPK, U>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_attn_split<KT, D, 8, LPK, U>), grid, dim3(256), 0, s, a); break;
   }
 }
 

@@ -8,7 +8,9 @@ norm, LM head, penalized greedy argmax feeding the next step) on synthetic
 seeded weights and inputs already resident in HBM.  The default workload is
 the 1.7B Talker shape at batch 1: a 512-row prefill (untimed), then K greedy
 steps replayed from a HIP graph on the device (K = 1536 runs the context to
-2048).  Prints one JSON line.
+2048).  The same run then times the batched workload on the same weights (64
+streams, seeded cache lengths in [256, 4096], bf16 cache, 32 iterations of
+one step per stream) and reports it under "batch64".  Prints one JSON line.
 
 Also measured in the same run:
   roofline      the dominant kernel (RMSNorm + gate/up + SwiGLU GEMV): its
@@ -44,8 +46,19 @@ def log(msg):
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the source of the roofline kernel (the GEMV template and its
+    launch shape), so that stored counters stay valid while other kernels in
+    the file change."""
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    parts = []
+    for start in ("template <typename WT, int MR, int KS, int KI, int EPI, bool NORM>",
+                  "static void gemv_shape(", "hipError_t launch_gemv("):
+        i = src.find(start)
+        if i < 0:
+            return "missing"
+        parts.append(src[i:src.find("\n}\n", i) + 3])
+    return hashlib.sha256("".join(parts).encode()).hexdigest()[:16]
 
 
 def weight_bytes(shape) -> int:
@@ -189,6 +202,15 @@ def bench_lm(args, wl):
                       frac=step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS),
     )
     dec.close()
+    # the batched workload is the same stack (same weights) with a bf16 cache
+    bwl = inputs.WORKLOADS["batched64"]
+    import dataclasses
+    same_stack = dataclasses.replace(bwl.model, name=s.name, kv_dtype=s.kv_dtype) == s
+    if not args.no_batched and same_stack:
+        log("batched64 ...")
+        out["batch64"] = bench_batched(args, bwl, dm=dm, steps=bwl.steps, warmup=4)
+    del dm
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(mw, X0, wl.s_init, args.cpu_seconds, 64)
@@ -302,6 +324,8 @@ def main():
                     choices=["talker1.7b", "asr", "tiny", "batched64"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the 64-stream leg of the default (1.7B) run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 plain device copies of 256 MiB (counter calibration)")
     args = ap.parse_args()

@@ -269,8 +269,9 @@ enum {
  * the decoder's own scratch (the residual stream they update there is
  * rebuilt by the next step or prefill); ATD_STAGE_ATTN also writes the
  * not-yet-valid cache row at each slot's write position, which the next
- * step overwrites.  Slot positions do not move.  Waits for the stream.
- * Errors: INVALID_ARG, CAPACITY, DEVICE. */
+ * step overwrites (so it needs each slot's position below its capacity).
+ * Slot positions do not move.  Waits for the stream.
+ * Errors: INVALID_ARG, CAPACITY, KV_FULL, DEVICE. */
 int decoder_time_stage(atd_decoder* dec, int32_t stage, int32_t slot0, int32_t B,
                        int32_t reps, void* stream, double* us_per_layer);
 

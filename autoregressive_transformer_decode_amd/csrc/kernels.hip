@@ -218,12 +218,20 @@ __global__ __launch_bounds__(128) void k_rope_append(RopeArgs a) {
 // block's rows is cut into KS slices: wave q takes slice q % KS of the
 // KS rows of its group (4 / KS groups per block).  Every lane streams KI
 // 16-byte chunks per row, so all 64 lanes of a wave read consecutive
-// addresses of a row and a whole slice is in flight at once.  The loads are
-// issued first (the weights do not depend on the activations); the lane's
-// slice of the input rows is then read straight into registers, normalised
-// with the sum of squares gathered in LDS, and multiplied; partial dots of
-// the KS slices meet in LDS and are added in a fixed order.  MR input rows
-// share every weight load.
+// addresses of a row and a whole slice is in flight at once.  Load order
+// follows the in-order memory counter: first the small operands the math
+// needs early (the lane's slice of the input rows and the gain, and the
+// epilogue's bias or residual), then the weights, so the norm's sum of
+// squares and its cross-wave reduction run while the weights stream in.
+// Partial dots of the KS slices meet in LDS and are added in a fixed order.
+// MR input rows share every weight load.  Argument arrays are only indexed
+// with constants (a run-time index would turn into a memory load of the
+// argument block ahead of everything else).
+template <typename T>
+__device__ __forceinline__ T pick3(const T (&v)[3], int i) {
+  return i == 0 ? v[0] : (i == 1 ? v[1] : v[2]);
+}
+
 template <typename WT, int MR, int KS, int KI, int EPI, bool NORM>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int VEC = Vec16<WT>::N;
@@ -236,55 +244,93 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int K = a.K, nk = K / VEC, ql = (nk + KS - 1) / KS;  // last slice may be short
   const int row0 = blockIdx.x * 4 + grp * RW;
   const bool active = row0 < a.N;
-  int s = 0, sbeg = 0, nr = 0;
-  const WT* Wp = nullptr;
-  const WT* W2p = nullptr;
-  if (active) {
-    s = row0 < a.seg_end[0] ? 0 : (row0 < a.seg_end[1] ? 1 : 2);
-    sbeg = s == 0 ? 0 : a.seg_end[s - 1];
-    nr = min(RW, a.seg_end[s] - row0);
-    Wp = reinterpret_cast<const WT*>(a.W[s]) + (size_t)(row0 - sbeg) * K;
-    if constexpr (EPI == kEpiSwiglu) W2p = reinterpret_cast<const WT*>(a.W2) + (size_t)row0 * K;
-  }
-  uint4 w[KI][RW][NW];
-#pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    const int cq = lane + 64 * i;
-    const int c = ks * ql + cq;
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      const bool ok = r < nr && cq < ql && c < nk;
-      w[i][r][0] = ok ? ld16(Wp + (size_t)r * K + (size_t)c * VEC) : make_uint4(0, 0, 0, 0);
-      if constexpr (NW == 2)
-        w[i][r][1] = ok ? ld16(W2p + (size_t)r * K + (size_t)c * VEC) : make_uint4(0, 0, 0, 0);
-    }
-  }
+
+  // 1) small operands: input slice, gain slice, epilogue operand
   float xv[MR][KI][VEC];
-  float ss[MR];
 #pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    ss[m] = 0.f;
+  for (int m = 0; m < MR; ++m)
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int cq = lane + 64 * i;
       const int c = ks * ql + cq;
+      const bool in = cq < ql && c < nk;
 #pragma unroll
       for (int e = 0; e < VEC; e += 4) {
-        const float4 t = (cq < ql && c < nk) ? *reinterpret_cast<const float4*>(a.x + (size_t)m * a.ldx +
-                                                                    (size_t)c * VEC + e)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-        xv[m][i][e] = t.x;
-        xv[m][i][e + 1] = t.y;
-        xv[m][i][e + 2] = t.z;
-        xv[m][i][e + 3] = t.w;
-        ss[m] += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+        const uint4 t = in ? ldg16(a.x + (size_t)m * a.ldx + (size_t)c * VEC + e) : make_uint4(0, 0, 0, 0);
+        xv[m][i][e] = __uint_as_float(t.x);
+        xv[m][i][e + 1] = __uint_as_float(t.y);
+        xv[m][i][e + 2] = __uint_as_float(t.z);
+        xv[m][i][e + 3] = __uint_as_float(t.w);
+      }
+    }
+  float gv[KI][VEC];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int cq = lane + 64 * i;
+      const int c = ks * ql + cq;
+      const bool in = cq < ql && c < nk;
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const uint4 t = in ? ldg16(a.gain + (size_t)c * VEC + e) : make_uint4(0, 0, 0, 0);
+        gv[i][e] = __uint_as_float(t.x);
+        gv[i][e + 1] = __uint_as_float(t.y);
+        gv[i][e + 2] = __uint_as_float(t.z);
+        gv[i][e + 3] = __uint_as_float(t.w);
       }
     }
   }
+  // thread (m, rr) of the first 4*MR threads finishes output row rr of input m
+  const int em = tid / 4, err = tid % 4, erow = blockIdx.x * 4 + err;
+  const bool fin = tid < 4 * MR && erow < a.N;
+  float eo = 0.f;
+  if (fin) {
+    if constexpr (EPI == kEpiStore) {
+      const int gs = erow < a.seg_end[0] ? 0 : (erow < a.seg_end[1] ? 1 : 2);
+      const float* b = pick3(a.bias, gs);
+      const int gbeg = gs == 0 ? 0 : (gs == 1 ? a.seg_end[0] : a.seg_end[1]);
+      if (b) eo = b[erow - gbeg];
+    } else if constexpr (EPI == kEpiResidual) {
+      eo = a.out[(size_t)em * a.ldo + erow];
+    }
+  }
+
+  // 2) weights: every lane issues all its loads (addresses clamped into the
+  // matrix; positions past the slice meet zero inputs and rows past N are
+  // never stored), so the number of loads behind the small operands is fixed
+  // and waiting for those does not wait for the weights
+  const int rowc = active ? row0 : a.N - 1;
+  const int sg = rowc < a.seg_end[0] ? 0 : (rowc < a.seg_end[1] ? 1 : 2);
+  const int sbeg = sg == 0 ? 0 : (sg == 1 ? a.seg_end[0] : a.seg_end[1]);
+  const int nr = min(RW, pick3(a.seg_end, sg) - rowc);   // >= 1
+  const WT* Wp = reinterpret_cast<const WT*>(pick3(a.W, sg)) + (size_t)(rowc - sbeg) * K;
+  const WT* W2p = EPI == kEpiSwiglu ? reinterpret_cast<const WT*>(a.W2) + (size_t)rowc * K : nullptr;
+  uint4 w[KI][RW][NW];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int cq = lane + 64 * i;
+    const int c = min(ks * ql + cq, nk - 1);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const size_t off = (size_t)min(r, nr - 1) * K + (size_t)c * VEC;
+      w[i][r][0] = ldg16(Wp + off);
+      if constexpr (NW == 2) w[i][r][1] = ldg16(W2p + off);
+    }
+  }
+  // keep the scheduler from hoisting the norm (which waits for the small
+  // operands) between the weight loads
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3) the norm, while the weights arrive
   if constexpr (NORM) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-      const float v = wave_sum(ss[m]);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < KI; ++i)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ss += xv[m][i][e] * xv[m][i][e];
+      const float v = wave_sum(ss);
       if (lane == 0) red_ss[q][m] = v;
     }
     __syncthreads();
@@ -295,18 +341,17 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       for (int j = 0; j < KS; ++j) tot += red_ss[grp * KS + j][m];
       const float inv = 1.0f / sqrtf(tot / (float)K + a.eps);
 #pragma unroll
-      for (int i = 0; i < KI; ++i) {
-        const int cq = lane + 64 * i;
-        const int c = ks * ql + cq;
-        if (cq < ql && c < nk) {
+      for (int i = 0; i < KI; ++i)
 #pragma unroll
-          for (int e = 0; e < VEC; e += 4) {
-            const float4 g = *reinterpret_cast<const float4*>(a.gain + (size_t)c * VEC + e);
-            xv[m][i][e] = xv[m][i][e] * inv * g.x;
-            xv[m][i][e + 1] = xv[m][i][e + 1] * inv * g.y;
-            xv[m][i][e + 2] = xv[m][i][e + 2] * inv * g.z;
-            xv[m][i][e + 3] = xv[m][i][e + 3] * inv * g.w;
-            if (a.y_out && blockIdx.x == 0 && grp == 0)
+        for (int e = 0; e < VEC; ++e) xv[m][i][e] = xv[m][i][e] * inv * gv[i][e];
+      if (a.y_out && blockIdx.x == 0 && grp == 0) {
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          const int cq = lane + 64 * i;
+          const int c = ks * ql + cq;
+          if (cq < ql && c < nk) {
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
               *reinterpret_cast<float4*>(a.y_out + (size_t)m * K + (size_t)c * VEC + e) =
                   make_float4(xv[m][i][e], xv[m][i][e + 1], xv[m][i][e + 2], xv[m][i][e + 3]);
           }
@@ -314,6 +359,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       }
     }
   }
+
+  // 4) dot products
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -332,30 +379,21 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         if (lane == 0) red_acc[q][r][m][t] = acc;
       }
   __syncthreads();
-  // thread (g, r, m) of the first 4*MR threads finishes one output
-  if (tid < 4 * MR) {
-    const int m = tid / 4, rr = tid % 4, g = rr / RW, r = rr % RW;
-    const int row = blockIdx.x * 4 + rr;
-    const int gs = row < a.seg_end[0] ? 0 : (row < a.seg_end[1] ? 1 : 2);
-    const int gbeg = gs == 0 ? 0 : a.seg_end[gs - 1];
-    if (row < a.N) {
-      float v[NW];
+  if (fin) {
+    const int g = err / RW, r = err % RW;
+    float v[NW];
 #pragma unroll
-      for (int t = 0; t < NW; ++t) {
-        float acc = 0.f;
+    for (int t = 0; t < NW; ++t) {
+      float acc = 0.f;
 #pragma unroll
-        for (int j = 0; j < KS; ++j) acc += red_acc[g * KS + j][r][m][t];
-        v[t] = acc;
-      }
-      float* o = a.out + (size_t)m * a.ldo + row;
-      if constexpr (EPI == kEpiStore) {
-        *o = a.bias[gs] ? v[0] + a.bias[gs][row - gbeg] : v[0];
-      } else if constexpr (EPI == kEpiResidual) {
-        *o = *o + v[0];
-      } else {
-        *o = v[0] / (1.0f + expf(-v[0])) * v[NW - 1];
-      }
+      for (int j = 0; j < KS; ++j) acc += red_acc[g * KS + j][r][em][t];
+      v[t] = acc;
     }
+    float* o = a.out + (size_t)em * a.ldo + erow;
+    if constexpr (EPI == kEpiSwiglu)
+      *o = v[0] / (1.0f + expf(-v[0])) * v[NW - 1];
+    else
+      *o = eo + v[0];
   }
 }
 
@@ -948,9 +986,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 
   const int row = n0 + li;
   const int sg = row < a.seg_end[0] ? 0 : (row < a.seg_end[1] ? 1 : 2);
-  const int sb = sg == 0 ? 0 : a.seg_end[sg - 1];
+  const int sb = sg == 0 ? 0 : (sg == 1 ? a.seg_end[0] : a.seg_end[1]);
   // rows past N read row 0 of the segment (in bounds); their sums are not stored
-  const uint16_t* wp = reinterpret_cast<const uint16_t*>(a.W[sg]) +
+  const uint16_t* wp = reinterpret_cast<const uint16_t*>(pick3(a.W, sg)) +
                        (size_t)(row < a.N ? row - sb : 0) * K + lg * 8;
   // staging: thread -> rows srow and srow + 32, 16-byte group sc
   const int srow = tid >> 3, sc = tid & 7;
@@ -1070,8 +1108,9 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * kMmaRows + m) * a.N + n];
     v *= inv;
     const int sg = n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
-    const int sb = sg == 0 ? 0 : a.seg_end[sg - 1];
-    a.out[(size_t)m * a.ldo + n] = a.bias[sg] ? v + a.bias[sg][n - sb] : v;
+    const int sb = sg == 0 ? 0 : (sg == 1 ? a.seg_end[0] : a.seg_end[1]);
+    const float* b = pick3(a.bias, sg);
+    a.out[(size_t)m * a.ldo + n] = b ? v + b[n - sb] : v;
   }
 }
 

@@ -554,6 +554,17 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   Kh += (size_t)g * cap * D + dl;
   Vh += (size_t)g * cap * D + dl;
 
+  // the QK-norm gains of the lane's channels, also ahead of the cache rows
+  float4 gq[DPL / 4], gk[DPL / 4];
+  if (a.fused && a.qk_norm) {
+#pragma unroll
+    for (int e = 0; e < DPL / 4; ++e) gq[e] = *reinterpret_cast<const float4*>(a.q_norm + dl + 4 * e);
+    if (owns_new) {
+#pragma unroll
+      for (int e = 0; e < DPL / 4; ++e) gk[e] = *reinterpret_cast<const float4*>(a.k_norm + dl + 4 * e);
+    }
+  }
+
   // keys past the split end are clamped to its last key (always in bounds)
   // and masked out in the softmax
   uint4 kr[U][NV], vr[U][NV];
@@ -569,8 +580,10 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
     }
   };
   load(k0);
+  // the norm and RoPE below wait only for the small loads above
+  __builtin_amdgcn_sched_barrier(0);
 
-  auto rope = [&](float (&x)[DPL], const float* gain) {
+  auto rope = [&](float (&x)[DPL], const float4 (&g4)[DPL / 4]) {
     if (a.qk_norm) {
       float ss = 0.f;
 #pragma unroll
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
       for (int e = 0; e < DPL; e += 4) {
-        const float4 gg = *reinterpret_cast<const float4*>(gain + dl + e);
+        const float4 gg = g4[e / 4];
         x[e] = x[e] * inv * gg.x;
         x[e + 1] = x[e + 1] * inv * gg.y;
         x[e + 2] = x[e + 2] * inv * gg.z;
@@ -601,7 +614,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
 
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    if (a.fused) rope(qv[j], a.q_norm);
+    if (a.fused) rope(qv[j], gq);
 #pragma unroll
     for (int e = 0; e < DPL; ++e) qv[j][e] *= a.scale;
   }
@@ -611,7 +624,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
 #pragma unroll
   for (int v = 0; v < NV; ++v) knew[v] = vnew[v] = make_uint4(0, 0, 0, 0);
   if (owns_new) {
-    rope(kf, a.k_norm);
+    rope(kf, gk);
     KT* Kw = const_cast<KT*>(Kh) + (size_t)pos * D;
     KT* Vw = const_cast<KT*>(Vh) + (size_t)pos * D;
 #pragma unroll

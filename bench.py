@@ -39,6 +39,7 @@ METRIC = "decode tokens/sec at batch 1 and 64; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "autoregressive_transformer_decode_amd", "csrc", "kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemv_talker1.7b_traffic.json")
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_split_batched64_traffic.json")
 
 
 def log(msg):
@@ -49,16 +50,8 @@ def kernel_hash() -> str:
     """Hash of the source of the roofline kernel (the GEMV template and its
     launch shape), so that stored counters stay valid while other kernels in
     the file change."""
-    with open(KERNEL_SRC) as f:
-        src = f.read()
-    parts = []
-    for start in ("template <typename WT, int MR, int KS, int KI, int EPI, bool NORM>",
-                  "static void gemv_shape(", "hipError_t launch_gemv("):
-        i = src.find(start)
-        if i < 0:
-            return "missing"
-        parts.append(src[i:src.find("\n}\n", i) + 3])
-    return hashlib.sha256("".join(parts).encode()).hexdigest()[:16]
+    return _source_hash(("template <typename WT, int MR, int KS, int KI, int EPI, bool NORM>",
+                         "static void gemv_shape(", "hipError_t launch_gemv("))
 
 
 def weight_bytes(shape) -> int:
@@ -119,13 +112,33 @@ def cpu_baseline(mw, X0, s_init, budget_s, max_steps):
                        f"prefill untimed")
 
 
-def traffic_per_launch():
+def _source_hash(starts) -> str:
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    parts = []
+    for start in starts:
+        i = src.find(start)
+        if i < 0:
+            return "missing"
+        parts.append(src[i:src.find("\n}\n", i) + 3])
+    return hashlib.sha256("".join(parts).encode()).hexdigest()[:16]
+
+
+def attn_kernel_hash() -> str:
+    """Hash of the split-K attention kernel's source and its launch shape."""
+    return _source_hash(("template <typename KT, int D, int R, int LPK, int U>",
+                         "static void attn_dispatch_r(", "hipError_t launch_attention("))
+
+
+def traffic_per_launch(path=None, hashfn=None):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    kernel's source changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path or TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_hash") != kernel_hash():
+    if t.get("kernel_hash") != (hashfn or kernel_hash)():
         return None
     return t.get("bytes_per_launch")
 
@@ -301,7 +314,9 @@ def bench_batched(args, wl, dm=None, steps=None, warmup=None):
                     kv_length_mean=float(lens.mean()), kv_dtype=s.kv_dtype,
                     layers=s.n_layers, hidden=s.hidden, ffn=s.ffn, vocab=s.vocab),
         roofline=dict(bound="hbm", achieved=a_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=a_gbs / HBM_PEAK_GBS, traffic=None,
+                      frac=a_gbs / HBM_PEAK_GBS,
+                      traffic=traffic_per_launch(ATTN_TRAFFIC_FILE, attn_kernel_hash),
+                      traffic_kernel="k_attn_split (counters of the split kernel alone)",
                       kernel="attention stage (k_attn_split + k_attn_combine), 64 rows",
                       bytes_per_launch=a_bytes, avg_launch_us=st["attention"],
                       launches_timed=reps * s.n_layers),

@@ -22,9 +22,8 @@ def _log(msg):
 
 
 # h, Hq*D and F multiples of 32 (MFMA-eligible); N ragged against the
-# 128-row block (o and down 288, gate/up 1344, vocab 1000) and K ragged
-# against the 256-wide split (h = 288: the last split 32 wide; F = 672: 3
-# splits, the last 160 wide)
+# 64-row workgroup tile (o and down 288, vocab 1000) and K ragged against the
+# 64-wide pipeline stage (h = 288 and F = 672 end in a half stage)
 MFMA_SHAPE = ("mfma", 2, 288, 8, 2, 128, 672, 1000, "bf16", True, True)
 
 

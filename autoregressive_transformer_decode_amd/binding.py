@@ -37,7 +37,7 @@ STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FU
 EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
            "decoder_step", "decoder_embed", "greedy_argmax", "decoder_generate",
-           "decoder_time_stage")
+           "talker_generate_frames", "decoder_time_stage")
 
 ATD_STAGE_QKV, ATD_STAGE_ROPE, ATD_STAGE_ATTN, ATD_STAGE_OPROJ, ATD_STAGE_GATEUP, \
     ATD_STAGE_DOWN, ATD_STAGE_HEAD = range(7)
@@ -92,6 +92,8 @@ def _load():
         "greedy_argmax": ([vp, i32, i32, vp, f32, vp, vp, vp], C.c_int),
         "decoder_generate": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, f32, vp, vp,
                               vp, vp], C.c_int),
+        "talker_generate_frames": ([vp, i32, vp, i32, i32, vp, vp, vp, vp, f32, vp, vp, vp, vp],
+                                   C.c_int),
         "decoder_time_stage": ([vp, i32, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
     }
     for name, (args, res) in sig.items():
@@ -179,6 +181,13 @@ def decoder_generate(handle: int, slot: int, n_steps: int, tok_io: int, G: int, 
     _check(lib.decoder_generate(handle, slot, n_steps, tok_io, G, _i32_array(list(table_ids)),
                                 extra, head, seen, penalty, tokens_out, y_out, logits_out,
                                 stream), handle)
+
+
+def talker_generate_frames(tk: int, tk_slot: int, cp: int, cp_slot: int, n_frames: int,
+                           codes_io: int, y_io: int, text, seen: int, penalty: float, codes_out,
+                           tk_logits: int, cp_logits: int, stream: int) -> None:
+    _check(lib.talker_generate_frames(tk, tk_slot, cp, cp_slot, n_frames, codes_io, y_io, text,
+                                      seen, penalty, codes_out, tk_logits, cp_logits, stream), tk)
 
 
 def decoder_time_stage(handle: int, stage: int, slot0: int, B: int, reps: int,

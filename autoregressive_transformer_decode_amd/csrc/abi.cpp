@@ -1036,6 +1036,188 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
   return ATD_OK;
 }
 
+// ---------------------------------------------------------------- Talker frame loop
+
+namespace {
+
+constexpr int kCodeGroups = 16;   // codes per Talker frame (c0 and 15 Code Predictor groups)
+
+// The Code Predictor pass of one frame, then the record of its 16 codes:
+// rows [y, table_0[c0]] -> 2-row prefill, head 0 -> c1; steps j = 1..14 fed
+// table_j[c_j], head j -> c_{j+1}.
+hipError_t enqueue_cp_pass(atd_decoder* cp, int cp_slot, int32_t* codes, const float* y,
+                           float* cp_logits, int32_t* codes_out, int32_t* counter, hipStream_t s) {
+  const atd_config& c = cp->cfg;
+  const int cp_cap = std::min(cp->cap[cp_slot], c.max_ctx);
+  ArgmaxArgs am{};
+  am.B = 1;
+  am.V = c.vocab;
+  am.nwords = (c.vocab + 31) / 32;
+  am.penalty = 1.0f;
+  am.part = cp->part;
+  am.nblk = (c.vocab + kArgmaxChunk - 1) / kArgmaxChunk;
+  am.z = cp_logits;
+  // prefill rows: the Talker's output and the embedding of c0 (table 0)
+  const int32_t t0 = 0;
+  EmbedArgs r0 = embed_args(cp, 1, nullptr, 0, nullptr, y, cp->x);
+  EmbedArgs r1 = embed_args(cp, 1, codes, 1, &t0, nullptr, cp->x + c.hidden);
+  hipError_t e = launch_embed(r0, c.dtype == ATD_BF16, s);
+  if (e == hipSuccess) e = launch_embed(r1, c.dtype == ATD_BF16, s);
+  const RowMap pre{kRowsPrefill, cp_slot, 0};
+  if (e == hipSuccess) e = run_layers(cp, pre, 2, 2, cp->x, nullptr, s);
+  if (e == hipSuccess) e = run_head_gemv(cp, cp->x + c.hidden, 1, 0, nullptr, cp_logits, s);
+  if (e == hipSuccess) e = launch_advance(slots_of(cp), pre, 2, s);
+  am.tok = codes + 1;
+  if (e == hipSuccess) e = launch_argmax(am, s);
+  for (int j = 1; j < kCodeGroups - 1 && e == hipSuccess; ++j) {
+    const int32_t tj = j;
+    e = enqueue_step(cp, cp_slot, 1, codes + j, 1, &tj, nullptr, j, nullptr, cp_logits, cp_cap, s);
+    am.tok = codes + j + 1;
+    if (e == hipSuccess) e = launch_argmax(am, s);
+  }
+  if (e == hipSuccess) e = launch_record_tokens(codes, kCodeGroups, codes_out, counter, s);
+  return e;
+}
+
+// One Talker step of the frame loop: input sum_g table_g[c_g] + text[*counter],
+// head 0 -> y and logits, penalised argmax -> c0.
+hipError_t enqueue_talker_step(atd_decoder* tk, int tk_slot, int32_t* codes, const float* text,
+                               int32_t* counter, uint32_t* seen, float penalty, float* y,
+                               float* tk_logits, hipStream_t s) {
+  const atd_config& c = tk->cfg;
+  int32_t tabs[kCodeGroups];
+  for (int g = 0; g < kCodeGroups; ++g) tabs[g] = g;
+  RowMap rows{kRowsStep, tk_slot, 0};
+  EmbedArgs ea = embed_args(tk, 1, codes, kCodeGroups, tabs, text, tk->x);
+  ea.extra_row = counter;
+  hipError_t e = launch_embed(ea, c.dtype == ATD_BF16, s);
+  const HeadOut ho{0, y, tk_logits};
+  const int max_cap = std::min(tk->cap[tk_slot], c.max_ctx);
+  if (e == hipSuccess) e = run_layers(tk, rows, 1, max_cap, tk->x, &ho, s);
+  if (e == hipSuccess) e = launch_advance(slots_of(tk), rows, 1, s);
+  if (e == hipSuccess) {
+    ArgmaxArgs am{};
+    am.z = tk_logits;
+    am.B = 1;
+    am.V = c.vocab;
+    am.seen = seen;
+    am.nwords = (c.vocab + 31) / 32;
+    am.penalty = penalty;
+    am.tok = codes;
+    am.part = tk->part;
+    am.nblk = (c.vocab + kArgmaxChunk - 1) / kArgmaxChunk;
+    e = launch_argmax(am, s);
+  }
+  return e;
+}
+
+}  // namespace
+
+extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_decoder* cp,
+                                      int32_t cp_slot, int32_t n_frames, int32_t* codes_io,
+                                      float* y_io, const float* text, uint32_t* seen,
+                                      float penalty, int32_t* codes_out, float* tk_logits,
+                                      float* cp_logits, void* stream) {
+  if (!tk) return fail(nullptr, ATD_ERR_INVALID_ARG, "Talker decoder is NULL");
+  if (!cp || cp == tk) return fail(tk, ATD_ERR_INVALID_ARG, "Code Predictor decoder is NULL or the Talker's");
+  const atd_config &tc = tk->cfg, &cc = cp->cfg;
+  if (tk->dry != cp->dry) return fail(tk, ATD_ERR_INVALID_ARG, "one decoder is a dry run, the other not");
+  if (n_frames < 1) return fail(tk, ATD_ERR_INVALID_ARG, "n_frames %d < 1", n_frames);
+  if (tc.hidden != cc.hidden)
+    return fail(tk, ATD_ERR_SHAPE, "hidden sizes differ: Talker %d, Code Predictor %d", tc.hidden,
+                cc.hidden);
+  if (tc.n_tables < kCodeGroups)
+    return fail(tk, ATD_ERR_SHAPE, "the Talker has %d tables, a frame input needs %d", tc.n_tables,
+                kCodeGroups);
+  if (cc.n_tables < kCodeGroups - 1 || cc.n_lm_heads < kCodeGroups - 1)
+    return fail(tk, ATD_ERR_SHAPE, "the Code Predictor has %d tables / %d heads, needs %d each",
+                cc.n_tables, cc.n_lm_heads, kCodeGroups - 1);
+  if (tk_slot < 0 || tk_slot >= tc.max_slots || !tk->attached[tk_slot])
+    return fail(tk, ATD_ERR_INVALID_ARG, "Talker slot %d is not an attached slot", tk_slot);
+  if (cp_slot < 0 || cp_slot >= cc.max_slots || !cp->attached[cp_slot])
+    return fail(tk, ATD_ERR_INVALID_ARG, "Code Predictor slot %d is not an attached slot", cp_slot);
+  if (cc.max_rows < 2)
+    return fail(tk, ATD_ERR_CAPACITY, "the Code Predictor's max_rows %d < 2", cc.max_rows);
+  if (std::min(cp->cap[cp_slot], cc.max_ctx) < kCodeGroups)
+    return fail(tk, ATD_ERR_KV_FULL, "Code Predictor slot %d holds %d rows, a pass needs %d",
+                cp_slot, std::min(cp->cap[cp_slot], cc.max_ctx), kCodeGroups);
+  const int steps = n_frames - 1;
+  if ((int64_t)tk->pos[tk_slot] + steps > std::min(tk->cap[tk_slot], tc.max_ctx))
+    return fail(tk, ATD_ERR_KV_FULL, "Talker slot %d: %d steps from position %d exceed %d rows",
+                tk_slot, steps, tk->pos[tk_slot], std::min(tk->cap[tk_slot], tc.max_ctx));
+  if (!codes_io || !y_io || !tk_logits || !cp_logits || !seen)
+    return fail(tk, ATD_ERR_INVALID_ARG, "codes_io, y_io, seen or a logits buffer is NULL");
+  if (steps > 0 && !text) return fail(tk, ATD_ERR_INVALID_ARG, "text is NULL");
+  if (!aligned16(y_io)) return fail(tk, ATD_ERR_INVALID_ARG, "y_io %p not 16-byte aligned", (void*)y_io);
+  if (!(penalty > 0.0f) || !std::isfinite(penalty))
+    return fail(tk, ATD_ERR_INVALID_ARG, "penalty %g is not a positive number", (double)penalty);
+  if (tk->dry) {
+    tk->pos[tk_slot] += steps;
+    cp->pos[cp_slot] = kCodeGroups;
+    return ATD_OK;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t pb;
+  std::memcpy(&pb, &penalty, 4);
+  const int64_t tag = 0x46524d;   // frame graphs in the Talker decoder's cache
+  auto graph_for = [&](int full, hipGraphExec_t* out) -> hipError_t {
+    std::vector<int64_t> key = {tag, full, tk_slot, (int64_t)(uintptr_t)cp, cp_slot,
+                                (int64_t)(uintptr_t)codes_io, (int64_t)(uintptr_t)y_io,
+                                (int64_t)(uintptr_t)text, (int64_t)(uintptr_t)seen, pb,
+                                (int64_t)(uintptr_t)codes_out, (int64_t)(uintptr_t)tk_logits,
+                                (int64_t)(uintptr_t)cp_logits,
+                                std::min(tk->cap[tk_slot], tc.max_ctx),
+                                std::min(cp->cap[cp_slot], cc.max_ctx)};
+    for (auto& ge : tk->graphs)
+      if (ge.key == key) {
+        *out = ge.exec;
+        return hipSuccess;
+      }
+    hipError_t e = hipSuccess;
+    if (!tk->cap_stream) {
+      e = hipStreamCreateWithFlags(&tk->cap_stream, hipStreamNonBlocking);
+      if (e != hipSuccess) return e;
+    }
+    hipStream_t cs = tk->cap_stream;
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) return e;
+    hipError_t le = hipSuccess;
+    if (full)
+      le = enqueue_talker_step(tk, tk_slot, codes_io, text, tk->counter, seen, penalty, y_io,
+                               tk_logits, cs);
+    if (le == hipSuccess)
+      le = enqueue_cp_pass(cp, cp_slot, codes_io, y_io, cp_logits, codes_out, tk->counter, cs);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    if (le != hipSuccess || e != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return le != hipSuccess ? le : e;
+    }
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return e;
+    if (tk->graphs.size() >= 8) {
+      (void)hipGraphExecDestroy(tk->graphs.front().exec);
+      tk->graphs.erase(tk->graphs.begin());
+    }
+    tk->graphs.push_back({key, exec});
+    *out = exec;
+    return hipSuccess;
+  };
+  hipGraphExec_t first = nullptr, rest = nullptr;
+  hipError_t e = graph_for(0, &first);
+  if (e == hipSuccess && steps > 0) e = graph_for(1, &rest);
+  if (e != hipSuccess) return hip_fail(tk, e, "capture of the frame loop");
+  e = launch_fill_i32(tk->counter, 1, 0, s);
+  if (e == hipSuccess) e = hipGraphLaunch(first, s);
+  for (int f = 1; f < n_frames && e == hipSuccess; ++f) e = hipGraphLaunch(rest, s);
+  if (e != hipSuccess) return hip_fail(tk, e, "talker_generate_frames replay");
+  tk->pos[tk_slot] += steps;
+  cp->pos[cp_slot] = kCodeGroups;
+  return ATD_OK;
+}
+
 // ---------------------------------------------------------------- stage timing
 
 extern "C" int decoder_time_stage(atd_decoder* d, int32_t stage, int32_t slot0, int32_t B,

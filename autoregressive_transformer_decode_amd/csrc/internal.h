@@ -138,6 +138,7 @@ struct EmbedArgs {
   int G;
   const int32_t* tok;   // [M, G]
   const float* extra;   // [M, h] or null
+  const int32_t* extra_row;  // device row index: extra starts (*extra_row) rows further, or null
   float* out;           // [M, h]
   int h, M;
 };
@@ -232,6 +233,11 @@ hipError_t launch_set_slot(const SlotTables& st, int slot, void* const* k, void*
 hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s);
 hipError_t launch_record_token(const int32_t* tok, int32_t* out, int32_t* counter, hipStream_t s);
+// out[*counter * n + i] = src[i] for i < n (out may be null), then ++*counter; n <= 64
+hipError_t launch_record_tokens(const int32_t* src, int n, int32_t* out, int32_t* counter,
+                                hipStream_t s);
+// dst[i] = src[i], i < n
+hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, int epi, hipStream_t s);

@@ -144,7 +144,10 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
     else
       s += row[i];
   }
-  if (a.extra) s += a.extra[(size_t)m * a.h + i];
+  if (a.extra) {
+    const float* ex = a.extra + (a.extra_row ? (size_t)(*a.extra_row) * a.h : 0);
+    s += ex[(size_t)m * a.h + i];
+  }
   a.out[(size_t)m * a.h + i] = s;
 }
 
@@ -1136,6 +1139,19 @@ __global__ void k_record_token(const int32_t* tok, int32_t* out, int32_t* counte
   }
 }
 
+// one wave: every lane reads the counter before lane 0 moves it on
+__global__ void k_record_tokens(const int32_t* src, int n, int32_t* out, int32_t* counter) {
+  const int i = threadIdx.x;
+  const int k = *counter;
+  if (out && i < n) out[(size_t)k * n + i] = src[i];
+  if (i == 0) *counter = k + 1;
+}
+
+__global__ void k_copy_f32(const float* src, float* dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
 __global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -1302,6 +1318,17 @@ hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s) {
 hipError_t launch_record_token(const int32_t* tok, int32_t* out, int32_t* counter,
                                hipStream_t s) {
   hipLaunchKernelGGL(k_record_token, dim3(1), dim3(64), 0, s, tok, out, counter);
+  return hipGetLastError();
+}
+
+hipError_t launch_record_tokens(const int32_t* src, int n, int32_t* out, int32_t* counter,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(k_record_tokens, dim3(1), dim3(64), 0, s, src, n, out, counter);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy_f32, dim3((n + 255) / 256), dim3(256), 0, s, src, dst, n);
   return hipGetLastError();
 }
 

@@ -200,6 +200,24 @@ class Decoder:
         return x_out
 
 
+def talker_frames(tk: "Decoder", cp: "Decoder", n_frames: int, codes_io: torch.Tensor,
+                  y_io: torch.Tensor, text: Optional[torch.Tensor], seen: torch.Tensor,
+                  penalty: float, codes_out: Optional[torch.Tensor] = None,
+                  tk_logits: Optional[torch.Tensor] = None, cp_logits: Optional[torch.Tensor] = None,
+                  tk_slot: int = 0, cp_slot: int = 0):
+    """n_frames frames of the Talker / Code Predictor loop on the device
+    (talker_generate_frames); returns (tk_logits, cp_logits)."""
+    if tk_logits is None:
+        tk_logits = torch.empty(tk.shape.vocab, device="cuda", dtype=torch.float32)
+    if cp_logits is None:
+        cp_logits = torch.empty(cp.shape.vocab, device="cuda", dtype=torch.float32)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    B.talker_generate_frames(tk.handle, tk_slot, cp.handle, cp_slot, n_frames, codes_io.data_ptr(),
+                             y_io.data_ptr(), ptr(text), seen.data_ptr(), float(penalty),
+                             ptr(codes_out), tk_logits.data_ptr(), cp_logits.data_ptr(), _stream())
+    return tk_logits, cp_logits
+
+
 def greedy_argmax(logits: torch.Tensor, seen: Optional[torch.Tensor], penalty: float,
                   tok_out: torch.Tensor, margin_out: Optional[torch.Tensor] = None):
     Bn, V = (1, logits.shape[0]) if logits.dim() == 1 else logits.shape

@@ -330,13 +330,81 @@ def bench_batched(args, wl, dm=None, steps=None, warmup=None):
     )
 
 
+def bench_frames(args, wl):
+    """The Talker frame loop (0.6B shape): 64-row prefill, then frames of one
+    Talker step and one Code Predictor pass (2-row prefill + 14 steps),
+    replayed from graphs on the device (talker_generate_frames)."""
+    import numpy as np
+    import torch
+    from autoregressive_transformer_decode_amd import device as dv
+    from autoregressive_transformer_decode_amd import inputs
+
+    s, c = wl.model, wl.cp
+    n = args.steps if args.steps is not None else wl.frames
+    tmw = inputs.make_weights(s, seed=0)
+    cmw = inputs.make_weights(c, seed=0, tables=tmw.tables)
+    tdm = dv.DeviceModel(tmw)
+    cdm = dv.DeviceModel(cmw, tables=tdm.tables)
+    tdec = dv.Decoder(tdm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_init)
+    cdec = dv.Decoder(cdm, max_slots=1, max_rows=2, max_ctx=inputs.CP_CAPACITY)
+    tdec.grow(0, wl.s_init)
+    cdec.grow(0, inputs.CP_CAPACITY)
+    if wl.prefill + n - 1 > wl.s_init:
+        raise SystemExit(f"--steps beyond the {wl.s_init}-row Talker cache")
+    X0 = torch.from_numpy(inputs.prefill_embeddings(wl, seed=0)).cuda()
+    text = torch.from_numpy(inputs.text_embeddings(wl, seed=0)).cuda()
+    if text.shape[0] < n:
+        text = torch.cat([text, text[1:2].expand(n - text.shape[0], -1)])
+    y = torch.empty(s.hidden, device="cuda")
+    zt = torch.empty(s.vocab, device="cuda")
+    codes = torch.zeros(16, dtype=torch.int32, device="cuda")
+    seen = torch.zeros(dv.seen_words(s.vocab), dtype=torch.int32, device="cuda")
+    out = torch.zeros(n, 16, dtype=torch.int32, device="cuda")
+
+    def start():
+        seen.zero_()
+        tdec.prefill(X0, y_out=y, logits_out=zt)
+        dv.greedy_argmax(zt, seen, wl.penalty, codes[0:1])
+
+    start()   # warm-up run of the loop (captures the frame graphs)
+    dv.talker_frames(tdec, cdec, min(n, 4), codes, y, text, seen, wl.penalty, codes_out=out)
+    start()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dv.talker_frames(tdec, cdec, n, codes, y, text, seen, wl.penalty, codes_out=out)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    tdec.close()
+    cdec.close()
+    fps = n / dt
+    kv_row = lambda sh: 2 * sh.n_layers * sh.kv_dim * (2 if sh.kv_dtype == "bf16" else 4)  # noqa: E731
+    mean_ctx = wl.prefill + (n - 1) / 2.0
+    talker_b = weight_bytes(s) + kv_row(s) * mean_ctx
+    # a pass: 15 forward passes (2-row prefill, 14 steps), each over every layer
+    # and one LM head (weight_bytes counts one head); cache rows 2..16
+    cp_b = 15 * weight_bytes(c) + kv_row(c) * sum(range(2, 17))
+    frame_b = ((n - 1) * talker_b + n * cp_b) / n
+    log(f"frames: {n} in {dt * 1e3:.1f} ms")
+    return dict(
+        metric="Talker frames/s (1 Talker step + 15 Code Predictor passes per frame)",
+        value=fps, unit="frames/s", n_gpus=1, steps=n, warmup=1, ms_per_step=dt * 1e3 / n,
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload=wl.name, frames=n, prefill=wl.prefill, penalty=wl.penalty,
+                    talker_layers=s.n_layers, cp_layers=c.n_layers, hidden=s.hidden,
+                    step="graph-replayed frames (talker_generate_frames)"),
+        codes_per_s=16 * fps, rtf_equivalent=(1.0 / fps) / 0.08,
+        frame_hbm=dict(algorithmic_bytes=frame_b, achieved_gbs=frame_b * fps / 1e9,
+                       frac=frame_b * fps / 1e9 / HBM_PEAK_GBS),
+        roofline=None, cpu_baseline=None)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="talker1.7b",
-                    choices=["talker1.7b", "asr", "tiny", "batched64"])
+                    choices=["talker1.7b", "asr", "tiny", "batched64", "talker0.6b"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true",
@@ -363,7 +431,9 @@ def main():
         return
     from autoregressive_transformer_decode_amd import inputs
     wl = inputs.WORKLOADS[args.workload]
-    if wl.batch > 1:
+    if wl.cp is not None:
+        out = bench_frames(args, wl)
+    elif wl.batch > 1:
         r = bench_batched(args, wl, steps=args.steps, warmup=args.warmup)
         out = dict(metric=METRIC, value=r["value"], unit="tokens/s", n_gpus=1, steps=r["iterations"],
                    warmup=r["warmup"], ms_per_step=r["ms_per_iteration"], higher_is_better=True,

@@ -245,7 +245,44 @@ int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* t
                      uint32_t* seen, float penalty, int32_t* tokens_out, float* y_out,
                      float* logits_out, void* stream);
 
-/* Stages of a decode step, for decoder_profile_stage. */
+/* The Talker's two-level frame loop on the device ("Qwen3-TTS ncnn port",
+ * section "Talker: non-standard structure and two-level generation"; the
+ * qwen3-tts-hip OPTIMIZATION_LOG's Code Predictor stages).  Runs n_frames
+ * frames, captured as HIP graphs on first use and replayed.  Frame f:
+ *   - unless f = 0, one Talker step (decoder tk, slot tk_slot) fed
+ *     sum_{g<16} table_g[c_g] + text[f] (the previous frame's codes), head 0:
+ *     writes y_io and tk_logits; the penalised greedy argmax over `seen`
+ *     (greedy_argmax rules) gives the frame's c0;
+ *   - the Code Predictor pass (decoder cp, slot cp_slot, restarted at
+ *     position 0): a 2-row prefill of [y_io, table_0[c0]] with head 0 gives
+ *     c1, then steps j = 1..14 fed table_j[c_j] with head j give c_{j+1}
+ *     (greedy, no penalty);
+ *   - the frame's 16 codes are appended to codes_out.
+ * codes_io   [16] int32 device.  On entry codes_io[0] is frame 0's c0 (the code
+ *            the caller chose from its prefill, already marked in `seen`).
+ *            On return it holds the last frame's codes.
+ * y_io       [h] float32 device, 16-byte aligned.  On entry the Talker
+ *            final-norm output that goes with frame 0's c0.  On return the last
+ *            Talker step's output.
+ * text       [n_frames, h] float32 device; row f is added to frame f's Talker
+ *            input (row 0 unused; may be NULL when n_frames = 1).
+ * seen       [ceil(V_tk / 32)] uint32 device, updated; penalty > 0.
+ * codes_out  [n_frames, 16] int32 device, or NULL.
+ * tk_logits  [V_tk] and cp_logits [V_cp] float32 device: the last logits of
+ *            each decoder.
+ * Requirements: equal hidden sizes; tk has >= 16 tables (table g: codes of
+ * group g); cp has >= 15 tables and >= 15 LM heads (table 0 must be the
+ * Talker's code table); cp_slot holds >= 16 rows and cp max_rows >= 2;
+ * tk_slot has room for n_frames - 1 more rows (no bucket growth inside).
+ * Afterwards tk_slot has advanced n_frames - 1 rows and cp_slot is at 16.
+ * Each of the two decoders' scratch is used, so neither may run other work
+ * concurrently.  Errors: INVALID_ARG, SHAPE, CAPACITY, KV_FULL, DEVICE. */
+int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_decoder* cp, int32_t cp_slot,
+                           int32_t n_frames, int32_t* codes_io, float* y_io, const float* text,
+                           uint32_t* seen, float penalty, int32_t* codes_out, float* tk_logits,
+                           float* cp_logits, void* stream);
+
+/* Stages of a decode step, for decoder_time_stage. */
 enum {
   ATD_STAGE_QKV = 0,     /* RMSNorm + q/k/v projection                       */
   ATD_STAGE_ROPE = 1,    /* QK norm + RoPE + cache append of a prefill block  */

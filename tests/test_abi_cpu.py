@@ -214,3 +214,44 @@ def test_create_without_gpu_reports_device_error():
     with pytest.raises(B.AtdError) as ei:
         B.decoder_create(cfg, fw.w)
     assert ei.value.code == B.ATD_ERR_DEVICE
+
+
+def test_dry_run_talker_frames():
+    """talker_generate_frames: shape/slot/capacity checks, and the positions
+    it leaves (Talker + n_frames - 1 rows, Code Predictor at 16)."""
+    tk, tfw = _create(_cfg(n_tables=16, n_lm_heads=1))
+    cp, cfw = _create(_cfg(n_tables=16, n_lm_heads=15))
+    small, sfw = _create(_cfg(n_tables=16, n_lm_heads=4))
+    L = 2
+    try:
+        kv = lambda base: ([base + 0x1000 * i for i in range(L)], [base + 0x80000 + 0x1000 * i for i in range(L)])  # noqa: E731
+        B.kv_bucket_grow(tk, 0, *kv(0x900000), 40, 0)
+        B.decoder_prefill(tk, 0, 0x5000, 8, 0, None, 0x6000, 0)
+        args = lambda n, cpd=cp: (tk, 0, cpd, 0, n, 0x7000, 0x8000, 0x9000, 0xA000, 1.05, None,  # noqa: E731
+                                  0xB000, 0xC000, 0)
+        with pytest.raises(B.AtdError) as ei:          # Code Predictor slot not attached
+            B.talker_generate_frames(*args(4))
+        assert "Code Predictor slot 0" in str(ei.value)
+        B.kv_bucket_grow(cp, 0, *kv(0xD00000), 12, 0)
+        with pytest.raises(B.AtdError) as ei:          # a pass needs 16 rows
+            B.talker_generate_frames(*args(4))
+        assert ei.value.code == B.ATD_ERR_KV_FULL
+        B.kv_bucket_grow(cp, 0, *kv(0xE00000), 16, 0)
+        B.kv_bucket_grow(small, 0, *kv(0xF00000), 16, 0)
+        with pytest.raises(B.AtdError) as ei:          # too few LM heads
+            B.talker_generate_frames(*args(4, small))
+        assert ei.value.code == B.ATD_ERR_SHAPE
+        with pytest.raises(B.AtdError) as ei:          # 33 more rows do not fit 40 from 8
+            B.talker_generate_frames(*args(34))
+        assert ei.value.code == B.ATD_ERR_KV_FULL
+        assert B.decoder_get_position(tk, 0) == (8, 40)
+        B.talker_generate_frames(*args(5))
+        assert B.decoder_get_position(tk, 0) == (12, 40)
+        assert B.decoder_get_position(cp, 0) == (16, 16)
+        B.talker_generate_frames(*args(1))             # one frame: no Talker step
+        assert B.decoder_get_position(tk, 0) == (12, 40)
+        with pytest.raises(B.AtdError):
+            B.talker_generate_frames(*args(0))
+    finally:
+        for h in (tk, cp, small):
+            B.decoder_destroy(h)

@@ -128,3 +128,99 @@ def test_talker17_prefill_and_steps():
     assert np.isfinite(z.cpu().numpy()).all()
     assert abs(np.sqrt(np.mean(yv.astype(np.float64) ** 2)) - 1.0) < 1e-3   # unit gains
     dec.close()
+
+
+def test_talker06_native_frame_loop():
+    """talker_generate_frames (graph-replayed frames) against (a) the same
+    frames composed from eager C-ABI calls, bit for bit, and (b) the oracle's
+    free-running frame loop, code for code up to the first code whose top-2
+    margin is <= 1e-2 (after that a different code is an equally valid
+    continuation)."""
+    wl = inputs.WORKLOADS["talker0.6b"]
+    n_frames = 8
+    tmw = inputs.make_weights(wl.model, seed=0)
+    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables)
+    X0 = inputs.prefill_embeddings(wl, seed=0)
+    text = inputs.text_embeddings(wl, seed=0)
+    ot = oracle_from_weights(tmw, np.float32)
+    oc = oracle_from_weights(cmw, np.float32)
+    frames, _ = od.run_talker(ot, oc, X0, text, n_frames, wl.s_init, rho=wl.penalty,
+                              cp_capacity=inputs.CP_CAPACITY)
+
+    tdm = dv.DeviceModel(tmw)
+    cdm = dv.DeviceModel(cmw, tables=tdm.tables)
+    tdec = dv.Decoder(tdm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_init)
+    cdec = dv.Decoder(cdm, max_slots=1, max_rows=2, max_ctx=inputs.CP_CAPACITY)
+    tdec.grow(0, wl.s_init)
+    cdec.grow(0, inputs.CP_CAPACITY)
+    h, Vt, Vc = wl.model.hidden, wl.model.vocab, wl.cp.vocab
+    text_d = torch.from_numpy(text).cuda()
+    X0_d = torch.from_numpy(X0).cuda()
+
+    def start():
+        y = torch.empty(h, device="cuda")
+        zt = torch.empty(Vt, device="cuda")
+        codes = torch.zeros(16, dtype=torch.int32, device="cuda")
+        seen = torch.zeros(dv.seen_words(Vt), dtype=torch.int32, device="cuda")
+        tdec.prefill(X0_d, y_out=y, logits_out=zt)
+        dv.greedy_argmax(zt, seen, wl.penalty, codes[0:1])
+        return y, zt, codes, seen
+
+    # (1) native loop
+    y, zt, codes, seen = start()
+    codes_out = torch.full((n_frames, 16), -1, dtype=torch.int32, device="cuda")
+    zt_n, zc_n = dv.talker_frames(tdec, cdec, n_frames, codes, y, text_d, seen, wl.penalty,
+                                  codes_out=codes_out)
+    torch.cuda.synchronize()
+    native = codes_out.cpu().numpy()
+    native_z = (zt_n.cpu().numpy(), zc_n.cpu().numpy(), y.cpu().numpy())
+    assert tdec.position(0)[0] == wl.prefill + n_frames - 1
+    assert cdec.position(0)[0] == inputs.CP_CAPACITY
+    # a second call replays the cached graphs and reproduces the run
+    y2, zt2, codes2, seen2 = start()
+    out2 = torch.full((n_frames, 16), -1, dtype=torch.int32, device="cuda")
+    dv.talker_frames(tdec, cdec, n_frames, codes2, y2, text_d, seen2, wl.penalty, codes_out=out2)
+    torch.cuda.synchronize()
+    assert (out2.cpu().numpy() == native).all()
+
+    # (2) the same frames from eager calls
+    y, zt, codes, seen = start()
+    cp_x = torch.empty(2, h, device="cuda")
+    zc = torch.empty(Vc, device="cuda")
+    eager = []
+    for f in range(n_frames):
+        if f > 0:
+            tdec.step(codes.view(1, 16), list(range(16)), extra=text_d[f:f + 1], y_out=y.view(1, h),
+                      logits_out=zt.view(1, Vt))
+            dv.greedy_argmax(zt, seen, wl.penalty, codes[0:1])
+        cp_x[0].copy_(y)
+        cdec.embed(codes[0:1].view(1, 1), [0], cp_x[1:2])
+        cdec.prefill(cp_x, head=0, logits_out=zc)
+        dv.greedy_argmax(zc, None, 1.0, codes[1:2])
+        for j in range(1, 15):
+            cdec.step(codes[j:j + 1].view(1, 1), [j], head=j, logits_out=zc.view(1, Vc))
+            dv.greedy_argmax(zc, None, 1.0, codes[j + 1:j + 2])
+        eager.append(codes.cpu().numpy().copy())
+    torch.cuda.synchronize()
+    assert (np.stack(eager) == native).all()
+    for a, b in zip(native_z, (zt.cpu().numpy(), zc.cpu().numpy(), y.cpu().numpy())):
+        assert np.array_equal(a, b)
+
+    # (3) the oracle's free-running loop, up to the first close call
+    checked = 0
+    for f in range(n_frames):
+        fr = frames[f]
+        seq = [(fr["c0"], fr["margin"])] + [(fr["codes"][j], fr["cp"][j][2]) for j in range(15)]
+        for g, (code, margin) in enumerate(seq):
+            if margin <= MARGIN:
+                break
+            assert int(native[f, g]) == code, (f, g, int(native[f, g]), code)
+            checked += 1
+        else:
+            continue
+        break
+    print(f"native frames: {n_frames} frames equal to eager calls; {checked} codes equal to the "
+          f"oracle before its first margin <= {MARGIN}", flush=True)
+    assert checked >= 16
+    tdec.close()
+    cdec.close()

@@ -754,9 +754,8 @@ extern "C" int kv_bucket_grow(atd_decoder* d, int32_t slot, void* const* k_new,
   if (e == hipSuccess && !d->dry)
     e = launch_set_slot(slots_of(d), slot, k_new, v_new, s_new, first ? 0 : -1, 1, s);
   if (e != hipSuccess) return hip_fail(d, e, "kv_bucket_grow");
-  // captured steps hold the slot's cache rows as kernel arguments: drop them
-  for (auto& ge : d->graphs) (void)hipGraphExecDestroy(ge.exec);
-  d->graphs.clear();
+  // captured steps hold the slot's cache rows as kernel arguments; their keys
+  // name the buckets (bucket_key), so graphs of the old buckets stop matching
   for (int l = 0; l < c.n_layers; ++l) {
     d->kp[slot][l] = k_new[l];
     d->vp[slot][l] = v_new[l];
@@ -939,6 +938,33 @@ extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t
 
 // ---------------------------------------------------------------- generation
 
+namespace {
+
+// Identifies the cache rows a captured graph was recorded with.
+int64_t bucket_key(const atd_decoder* d, int slot) {
+  uint64_t h = 1469598103934665603ull;
+  for (size_t l = 0; l < d->kp[slot].size(); ++l) {
+    h = (h ^ (uint64_t)(uintptr_t)d->kp[slot][l]) * 1099511628211ull;
+    h = (h ^ (uint64_t)(uintptr_t)d->vp[slot][l]) * 1099511628211ull;
+  }
+  return (int64_t)h;
+}
+
+// Adds a graph to the cache; evicting the oldest first waits for the device
+// (an evicted graph may still be in flight on the caller's stream).
+hipError_t cache_graph(atd_decoder* d, std::vector<int64_t> key, hipGraphExec_t exec) {
+  if (d->graphs.size() >= 8) {
+    const hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    (void)hipGraphExecDestroy(d->graphs.front().exec);
+    d->graphs.erase(d->graphs.begin());
+  }
+  d->graphs.push_back({std::move(key), exec});
+  return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, int32_t* tok_io,
                                 int32_t G, const int32_t* table_ids, const float* extra,
                                 int32_t head, uint32_t* seen, float penalty,
@@ -978,7 +1004,7 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
   std::vector<int64_t> key = {slot, G, (int64_t)(uintptr_t)extra, head,
                               (int64_t)(uintptr_t)tok_io, (int64_t)(uintptr_t)seen,
                               (int64_t)(uintptr_t)tokens_out, (int64_t)(uintptr_t)y_out,
-                              (int64_t)(uintptr_t)logits_out, max_cap};
+                              (int64_t)(uintptr_t)logits_out, max_cap, bucket_key(d, slot)};
   {
     uint32_t pb;
     std::memcpy(&pb, &penalty, 4);
@@ -1023,11 +1049,8 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return hip_fail(d, e, "hipGraphInstantiate");
-    if (d->graphs.size() >= 8) {
-      (void)hipGraphExecDestroy(d->graphs.front().exec);
-      d->graphs.erase(d->graphs.begin());
-    }
-    d->graphs.push_back({key, exec});
+    e = cache_graph(d, key, exec);
+    if (e != hipSuccess) return hip_fail(d, e, "graph cache");
   }
   if (tokens_out) e = launch_fill_i32(d->counter, 1, 0, s);
   for (int k = 0; k < n_steps && e == hipSuccess; ++k) e = hipGraphLaunch(exec, s);
@@ -1167,7 +1190,8 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
                                 (int64_t)(uintptr_t)codes_out, (int64_t)(uintptr_t)tk_logits,
                                 (int64_t)(uintptr_t)cp_logits,
                                 std::min(tk->cap[tk_slot], tc.max_ctx),
-                                std::min(cp->cap[cp_slot], cc.max_ctx)};
+                                std::min(cp->cap[cp_slot], cc.max_ctx), bucket_key(tk, tk_slot),
+                                bucket_key(cp, cp_slot)};
     for (auto& ge : tk->graphs)
       if (ge.key == key) {
         *out = ge.exec;
@@ -1197,11 +1221,8 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return e;
-    if (tk->graphs.size() >= 8) {
-      (void)hipGraphExecDestroy(tk->graphs.front().exec);
-      tk->graphs.erase(tk->graphs.begin());
-    }
-    tk->graphs.push_back({key, exec});
+    e = cache_graph(tk, key, exec);
+    if (e != hipSuccess) return e;
     *out = exec;
     return hipSuccess;
   };

@@ -95,7 +95,7 @@ def cpu_baseline(mw, X0, s_init, budget_s, max_steps):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     om = oracle_model(mw, np.float32)
-    cache = od.Cache(om, s_init)
+    cache = od.Cache(om, max(s_init, X0.shape[0] + max_steps + 1))
     _, z = od.prefill(om, cache, X0, 0)
     tok = int(np.argmax(z))
     n, t0 = 0, time.perf_counter()
@@ -157,34 +157,53 @@ def bench_lm(args, wl):
     log(f"weights generated in {time.perf_counter() - t:.1f}s")
     dm = dv.DeviceModel(mw)
     dec = dv.Decoder(dm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max)
-    dec.grow(0, wl.s_init)
     P0 = wl.prefill
     K = args.steps if args.steps is not None else wl.steps
     W = args.warmup
-    if P0 + max(K, W) > wl.s_init:
-        raise SystemExit(f"--steps/--warmup beyond the {wl.s_init}-row cache of {wl.name}")
+    if P0 + max(K, W) > wl.s_max:
+        raise SystemExit(f"--steps/--warmup beyond the {wl.s_max}-row context of {wl.name}")
+    # bucket ladder: the cache doubles before a write at its capacity (ASR report's
+    # dynamic window); the buckets are allocated up front, outside the timing
+    caps = [wl.s_init]
+    while caps[-1] < P0 + max(K, W):
+        caps.append(min(2 * caps[-1], wl.s_max))
+    buckets = [dec.alloc_kv(c) for c in caps]
+    dec.grow(0, caps[0], kv=buckets[0])
+    X0_d = torch.from_numpy(X0).cuda()
     z = torch.empty(s.vocab, device="cuda")
     y = torch.empty(s.hidden, device="cuda")
-    dec.prefill(torch.from_numpy(X0).cuda(), logits_out=z)
-    tok0 = torch.zeros(1, dtype=torch.int32, device="cuda")
-    dv.greedy_argmax(z, None, 1.0, tok0)
-    tok = tok0.clone()
-    torch.cuda.synchronize()
-    log(f"prefill {P0} rows done")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-    # warmup (also captures the step graph), then rewind to the prefill state
+    def schedule(n):
+        """Rewind to the first bucket, prefill (untimed), then n greedy steps
+        from the step graph, growing the bucket where the context reaches it;
+        returns the seconds of the decode loop."""
+        dec.set_position(0, 0)
+        if dec.position(0)[1] != caps[0]:
+            dec.grow(0, caps[0], kv=buckets[0])
+        dec.prefill(X0_d, logits_out=z)
+        dv.greedy_argmax(z, None, 1.0, tok)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        done, b = 0, 0
+        while done < n:
+            pos, cap = dec.position(0)
+            if pos >= cap:
+                b += 1
+                dec.grow(0, caps[b], kv=buckets[b])
+                continue
+            k = min(n - done, cap - pos)
+            dec.generate(k, tok, y_out=y, logits_out=z)
+            done += k
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    # warmup (captures the step graph of every bucket the timed run visits)
+    W = K if len(caps) > 1 else W
     if W:
-        dec.generate(W, tok, y_out=y, logits_out=z)
-    torch.cuda.synchronize()
-    dec.set_position(0, P0)
-    tok.copy_(tok0)
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    dec.generate(K, tok, y_out=y, logits_out=z)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    log(f"timed {K} steps: {dt * 1e3:.1f} ms")
+        schedule(W)
+    dt = schedule(K)
+    log(f"timed {K} steps: {dt * 1e3:.1f} ms (buckets {caps})")
 
     # roofline: the dominant kernel's launches, every layer's weights in turn
     # as in a step, timed with HIP events on this stream
@@ -204,8 +223,9 @@ def bench_lm(args, wl):
         dtype="bf16" if s.dtype == "bf16" else "f32", data="synthetic",
         config=dict(workload=wl.name, batch=1, prefill=P0, context=[P0 + 1, P0 + K],
                     layers=s.n_layers, hidden=s.hidden, heads=[s.n_q_heads, s.n_kv_heads],
-                    head_dim=s.head_dim, ffn=s.ffn, vocab=s.vocab, kv_capacity=wl.s_init,
-                    step="graph-replayed decode step + greedy argmax on device"),
+                    head_dim=s.head_dim, ffn=s.ffn, vocab=s.vocab,
+                    step="graph-replayed decode step + greedy argmax on device",
+                    kv_buckets=caps),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic,
                       kernel="k_gemv (RMSNorm + gate/up + SwiGLU), bf16 weights",

@@ -729,6 +729,33 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       mx[j] = nm;
     }
   }
+  if (a.nsplit_max == 1) {
+    // a single split per row and head: its state is the result (the combine
+    // kernel is skipped; acc / l is what it would compute for one split)
+    if (lane < LPK) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const size_t off = ((size_t)m * a.Hq + g * R + j) * D + dl;
+#pragma unroll
+        for (int e = 0; e < DPL; e += 4) {
+          const float v[4] = {acc[j][e] / ls[j], acc[j][e + 1] / ls[j], acc[j][e + 2] / ls[j],
+                              acc[j][e + 3] / ls[j]};
+          if (a.o_hi) {
+            uint16_t hv[4], lv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) split_hi_lo(v[i], hv[i], lv[i]);
+            *reinterpret_cast<uint2*>(a.o_hi + off + e) =
+                make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+            *reinterpret_cast<uint2*>(a.o_lo + off + e) =
+                make_uint2(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
+          } else {
+            *reinterpret_cast<float4*>(a.o + off + e) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+    }
+    return;
+  }
   if (lane < LPK) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -943,6 +970,12 @@ __global__ __launch_bounds__(256) void k_argmax_part(ArgmaxArgs a) {
   if (tid == 0) {
     Top2 r = st[0];
     for (int w = 1; w < 4; ++w) r = top2_merge(r, st[w]);
+    if (a.nblk == 1) {   // one block: this is the final result (k_argmax_final is skipped)
+      a.tok[b] = r.i1;
+      if (a.margin) a.margin[b] = r.v1 - r.v2;
+      if (a.seen) a.seen[(size_t)b * a.nwords + (r.i1 >> 5)] |= 1u << (r.i1 & 31);
+      return;
+    }
     float* p = a.part + ((size_t)b * a.nblk + blk) * 3;
     p[0] = r.v1;
     p[1] = __int_as_float(r.i1);
@@ -1271,6 +1304,7 @@ hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream
     else
       attn_dispatch_r<float, 128>(a, r, grid, s);
   }
+  if (a.nsplit_max == 1) return hipGetLastError();   // the split kernel wrote o
   dim3 cgrid(a.Hq, a.M);
   if (D == 64)
     hipLaunchKernelGGL(k_attn_combine<64>, cgrid, dim3(256), 0, s, a);
@@ -1311,7 +1345,7 @@ hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s) {
 
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_argmax_part, dim3(a.nblk, a.B), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_argmax_final, dim3(a.B), dim3(64), 0, s, a);
+  if (a.nblk > 1) hipLaunchKernelGGL(k_argmax_final, dim3(a.B), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -217,9 +217,11 @@ __global__ __launch_bounds__(128) void k_rope_append(RopeArgs a) {
 // ------------------------------------------------------------------ GEMV
 // out[m, n] = epi( sum_k W[n, k] * xin[m, k] ),  xin = x or RMSNorm(x) * gain
 //
-// A block of 4 waves owns 4 consecutive output rows.  The K dimension of the
-// block's rows is cut into KS slices: wave q takes slice q % KS of the
-// KS rows of its group (4 / KS groups per block).  Every lane streams KI
+// A block of 4 waves owns (4 / KS) * RW consecutive output rows: 4 / KS
+// groups of KS waves, each group RW rows whose K dimension is cut into KS
+// slices (wave q takes slice q % KS of its group's rows).  RW = KS, or 4 for
+// tall matrices with a short K (the ASR LM head), so that a wave's weight
+// stream outweighs its input loads.  Every lane streams KI
 // 16-byte chunks per row, so all 64 lanes of a wave read consecutive
 // addresses of a row and a whole slice is in flight at once.  Load order
 // follows the in-order memory counter: first the small operands the math
@@ -235,17 +237,17 @@ __device__ __forceinline__ T pick3(const T (&v)[3], int i) {
   return i == 0 ? v[0] : (i == 1 ? v[1] : v[2]);
 }
 
-template <typename WT, int MR, int KS, int KI, int EPI, bool NORM>
+template <typename WT, int MR, int KS, int KI, int EPI, bool NORM, int RW>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int VEC = Vec16<WT>::N;
   constexpr int NW = EPI == kEpiSwiglu ? 2 : 1;
-  constexpr int RW = KS;           // rows per wave group
+  constexpr int BR = (4 / KS) * RW;   // rows per block
   __shared__ float red_ss[4][MR];
   __shared__ float red_acc[4][RW][MR][NW];
   const int tid = threadIdx.x, lane = tid & 63, q = tid >> 6;
   const int ks = q % KS, grp = q / KS;
   const int K = a.K, nk = K / VEC, ql = (nk + KS - 1) / KS;  // last slice may be short
-  const int row0 = blockIdx.x * 4 + grp * RW;
+  const int row0 = blockIdx.x * BR + grp * RW;
   const bool active = row0 < a.N;
 
   // 1) small operands: input slice, gain slice, epilogue operand
@@ -283,9 +285,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       }
     }
   }
-  // thread (m, rr) of the first 4*MR threads finishes output row rr of input m
-  const int em = tid / 4, err = tid % 4, erow = blockIdx.x * 4 + err;
-  const bool fin = tid < 4 * MR && erow < a.N;
+  // thread (m, rr) of the first BR*MR threads finishes output row rr of input m
+  const int em = tid / BR, err = tid % BR, erow = blockIdx.x * BR + err;
+  const bool fin = tid < BR * MR && erow < a.N;
   float eo = 0.f;
   if (fin) {
     if constexpr (EPI == kEpiStore) {
@@ -1213,20 +1215,31 @@ template <typename WT, int MR, int EPI, bool NORM>
 static void gemv_dispatch_shape(const GemvArgs& a, hipStream_t s) {
   int ks, ki;
   gemv_shape(a.K, Vec16<WT>::N, ks, ki);
-  const dim3 grid((a.N + 3) / 4), block(256);
-#define ATD_GEMV(KS_, KI_) \
-  hipLaunchKernelGGL((k_gemv<WT, MR, KS_, KI_, EPI, NORM>), grid, block, 0, s, a)
+  // 4 rows per wave group when that still leaves >= 512 blocks
+  const int rw = ks == 4 || a.N >= 512 * (4 / ks) * 4 ? 4 : ks;
+  const int br = (4 / ks) * rw;   // rows per block
+  const dim3 grid((a.N + br - 1) / br), block(256);
+#define ATD_GEMV(KS_, KI_, RW_) \
+  hipLaunchKernelGGL((k_gemv<WT, MR, KS_, KI_, EPI, NORM, RW_>), grid, block, 0, s, a)
   if (ks == 4) {
     switch (ki) {
-      case 1: ATD_GEMV(4, 1); break;
-      case 2: ATD_GEMV(4, 2); break;
-      case 3: ATD_GEMV(4, 3); break;
-      default: ATD_GEMV(4, 4); break;
+      case 1: ATD_GEMV(4, 1, 4); break;
+      case 2: ATD_GEMV(4, 2, 4); break;
+      case 3: ATD_GEMV(4, 3, 4); break;
+      default: ATD_GEMV(4, 4, 4); break;
     }
   } else if (ks == 2) {
-    if (ki == 1) ATD_GEMV(2, 1); else ATD_GEMV(2, 2);
+    if (rw == 4) {
+      if (ki == 1) ATD_GEMV(2, 1, 4); else ATD_GEMV(2, 2, 4);
+    } else {
+      if (ki == 1) ATD_GEMV(2, 1, 2); else ATD_GEMV(2, 2, 2);
+    }
   } else {
-    if (ki == 1) ATD_GEMV(1, 1); else ATD_GEMV(1, 2);
+    if (rw == 4) {
+      if (ki == 1) ATD_GEMV(1, 1, 4); else ATD_GEMV(1, 2, 4);
+    } else {
+      if (ki == 1) ATD_GEMV(1, 1, 1); else ATD_GEMV(1, 2, 1);
+    }
   }
 #undef ATD_GEMV
 }

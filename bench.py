@@ -50,8 +50,8 @@ def kernel_hash() -> str:
     """Hash of the source of the roofline kernel (the GEMV template and its
     launch shape), so that stored counters stay valid while other kernels in
     the file change."""
-    return _source_hash(("template <typename WT, int MR, int KS, int KI, int EPI, bool NORM>",
-                         "static void gemv_shape(", "hipError_t launch_gemv("))
+    return _source_hash(("template <typename WT, int MR, int KS, int KI, int EPI, bool NORM, int RW>",
+                         "static void gemv_shape(", "static void gemv_dispatch_shape(", "hipError_t launch_gemv("))
 
 
 def weight_bytes(shape) -> int:

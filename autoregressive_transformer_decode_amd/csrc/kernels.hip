@@ -1386,7 +1386,7 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   const dim3 grid((a.N + kMmaBlockN - 1) / kMmaBlockN, a.ks);
-  hipLaunchKernelGGL(k_gemm<3>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_gemm<2>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -319,3 +319,14 @@ def batched_kv(shape: ModelShape, stream: int, length: int, layer: int,
     k, v = pool if pool is not None else batched_kv_pool(shape, layer, seed)
     o = batched_kv_offset(stream, length)
     return k[:, o:o + length], v[:, o:o + length]
+
+
+_T_UNIFORM = 70_003
+
+
+def uniforms(seed: int, stream: int, n) -> np.ndarray:
+    """Uniform draws in [0, 1) (float32) for sampled token choices, one per
+    choice: ``numpy.random.default_rng([seed, 2, _T_UNIFORM, stream])``.
+    ``n`` may be a shape."""
+    rng = np.random.default_rng([seed, 2, _T_UNIFORM, stream])
+    return rng.random(n, dtype=np.float32)

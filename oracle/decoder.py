@@ -23,13 +23,20 @@ RMSNorm eps 1e-6 and gain form x_hat*g; rotate-half RoPE pairing c with
 c + D/2, angles in float64 rounded to fp32; attention scale 1/sqrt(D), causal,
 no window; query head h reads KV head h // (Hq/Hkv); the KV cache stores bf16
 (round to nearest even) for bf16 models; argmax ties go to the lowest index;
-the penalty divides positive logits and multiplies the others.
+the penalty divides positive logits and multiplies the others.  Sampling
+(the log's GenerateOptions defaults and device-sampler entries): the top-k set
+is unique under (value descending, index ascending); the temperature divides
+the logits inside the softmax; top-p keeps the shortest descending prefix
+whose probability reaches top_p; the draw inverts the cumulative distribution
+over the candidates in descending order with a uniform that the caller passes
+in.
 """
 
 from __future__ import annotations
 
 import dataclasses
-from typing import List, Optional, Sequence, Tuple
+import math
+from typing import List, NamedTuple, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -323,6 +330,83 @@ def penalized_argmax(z: np.ndarray, seen: Optional[np.ndarray], rho: float):
 
 
 # --------------------------------------------------------------------------
+# sampled choice: repetition penalty, temperature, top-k, top-p, one uniform
+# --------------------------------------------------------------------------
+
+class SampleDraw(NamedTuple):
+    """One sampled token and how far the draw sat from a different outcome.
+
+    gap:     distance of u from the nearest interior boundary of the
+             cumulative distribution (inf with one candidate);
+    cut_gap: distance of top_p from the nearest cumulative probability of the
+             top-k candidates (inf when top_p >= 1);
+    kmargin: k-th largest penalized logit minus the (k+1)-th (inf when k = V).
+    """
+    tok: int
+    gap: float
+    cut_gap: float
+    kmargin: float
+
+
+def topk_candidates(zp: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest penalized logits, in descending order of
+    value, equal values by ascending index (the total order that makes the
+    top-k set unique)."""
+    order = np.lexsort((np.arange(zp.size), -zp.astype(np.float64)))
+    return order[:k]
+
+
+def sampling_distribution(z: np.ndarray, seen: Optional[np.ndarray], rho: float, k: int,
+                          temperature: float, top_p: float = 1.0):
+    """The distribution a sampled step draws from (qwen3-tts-hip
+    OPTIMIZATION_LOG, GenerateOptions defaults and device-sampler entries:
+    repetition penalty, temperature, top-k up to 256, top-p).
+
+    Order of the steps: the penalty on the seen tokens (float32, as in
+    penalized_logits); the top-k set of the penalized logits; softmax of
+    (logit / temperature) over that set; top-p keeps the shortest prefix, in
+    descending order, whose probability reaches top_p.  The temperature is a
+    positive scale, so taking the top-k set before or after it gives the same
+    set.  Returns (tokens in descending order of logit, probabilities that sum
+    to one, cumulative probabilities of the full top-k set, penalized
+    logits)."""
+    zp = penalized_logits(z, seen, rho)
+    cand = topk_candidates(zp, k)
+    v = zp[cand].astype(np.float64)
+    w = np.exp((v - v[0]) / float(temperature))
+    cum_k = np.cumsum(w) / np.sum(w)
+    m = len(cand)
+    if top_p < 1.0:
+        m = int(np.searchsorted(cum_k, top_p, side="left")) + 1   # first cum >= top_p
+        m = min(m, len(cand))
+    p = w[:m] / np.sum(w[:m])
+    return cand[:m], p, cum_k, zp
+
+
+def sample_topk(z: np.ndarray, seen: Optional[np.ndarray], rho: float, k: int,
+                temperature: float, top_p: float, u: float) -> SampleDraw:
+    """Sampled token by inversion of the cumulative distribution: the
+    candidates in descending order of logit, the first whose cumulative
+    probability exceeds the uniform u in [0, 1).  With k = 1 this is
+    penalized_argmax.  Marks the token in ``seen`` when given.  Float64
+    arithmetic after the float32 penalty."""
+    toks, p, cum_k, zp = sampling_distribution(z, seen, rho, k, temperature, top_p)
+    cdf = np.cumsum(p)
+    i = min(int(np.searchsorted(cdf, u, side="right")), len(toks) - 1)
+    tok = int(toks[i])
+    gap = float(np.min(np.abs(cdf[:-1] - u))) if len(toks) > 1 else math.inf
+    cut_gap = float(np.min(np.abs(cum_k - top_p))) if top_p < 1.0 else math.inf
+    if k < zp.size:
+        order = topk_candidates(zp, k + 1)
+        kmargin = float(zp[order[k - 1]]) - float(zp[order[k]])
+    else:
+        kmargin = math.inf
+    if seen is not None:
+        seen[tok] = True
+    return SampleDraw(tok, gap, cut_gap, kmargin)
+
+
+# --------------------------------------------------------------------------
 # loops
 # --------------------------------------------------------------------------
 
@@ -337,16 +421,18 @@ def bucket_for(pos: int, capacity: int) -> int:
 
 def run_lm(model: Model, X0: np.ndarray, n_steps: int, s_init: int,
            forced: Optional[Sequence[int]] = None, head: int = 0,
-           rho: float = 1.0, on_step=None):
-    """Plain greedy LM loop: prefill X0 (token 1 comes from its last row), then
+           rho: float = 1.0, on_step=None, sampling=None):
+    """Plain LM loop: prefill X0 (token 1 comes from its last row), then
     n_steps steps, step k consuming token k.  Buckets grow before a write at
     position == capacity.  With ``forced`` the fed tokens are taken from it
-    (teacher forcing) instead of the argmax.  Returns per-step lists of
-    (y, z, tok, margin), index 0 being the prefill."""
+    (teacher forcing) instead of the chosen ones.  Choices are greedy, or
+    with ``sampling`` = (k, temperature, top_p, u[n_steps + 1]) the choice
+    after the prefill (index 0) and after step k draws with u[k].  Returns
+    per-step lists of (y, z, tok, margin), index 0 being the prefill."""
     cache = Cache(model, s_init)
     seen = np.zeros(model.heads[head].shape[0], bool) if rho != 1.0 else None
     y, z = prefill(model, cache, X0, head)
-    tok, margin = penalized_argmax(z, seen, rho)
+    tok, margin = choose(z, seen, rho, sampling, 0)
     out = [(y, z, tok, margin)]
     if on_step:
         on_step(0, cache)
@@ -357,33 +443,50 @@ def run_lm(model: Model, X0: np.ndarray, n_steps: int, s_init: int,
             cache.grow(cap)
         x = embed(model, [fed], [0])
         y, z = step(model, cache, x, head)
-        tok, margin = penalized_argmax(z, seen, rho)
+        tok, margin = choose(z, seen, rho, sampling, k)
         out.append((y, z, tok, margin))
         if on_step:
             on_step(k, cache)
     return out, cache
 
 
+def choose(z: np.ndarray, seen: Optional[np.ndarray], rho: float, sampling=None,
+           i: int = 0) -> Tuple[int, float]:
+    """Greedy (sampling None) or sampled choice of one token.  ``sampling`` =
+    (k, temperature, top_p, uniforms) and the draw uses uniforms[i].  Returns
+    (token, robustness): the greedy top-2 margin, or for a draw the smallest
+    of its gap, cut_gap and kmargin (a decision that a small change of the
+    logits cannot flip has all three well above zero)."""
+    if sampling is None:
+        return penalized_argmax(z, seen, rho)
+    k, t, top_p, u = sampling
+    d = sample_topk(z, seen, rho, k, t, top_p, float(u[i]))
+    return d.tok, min(d.gap, d.cut_gap, d.kmargin)
+
+
 def code_predictor_frame(cp: Model, y_talker: np.ndarray, c0: int,
-                         cp_capacity: int = 16, forced: Optional[Sequence[int]] = None):
+                         cp_capacity: int = 16, forced: Optional[Sequence[int]] = None,
+                         sampling=None):
     """Code Predictor pass of one frame (ncnn port, two-level generation;
     qwen3-tts-hip CodePredictor sub-stages: prefill, first logits/token, then
     the remaining groups as decode steps).  The cache starts empty each frame.
     Prefill rows: the Talker hidden state y and the Talker embedding of c0, at
     positions 0 and 1; head 0 gives c1.  Step j (1..14) feeds E_cp[j][c_j]
-    at position j+1 and head j gives c_{j+1}.  Greedy, no penalty.
+    at position j+1 and head j gives c_{j+1}.  No penalty; greedy, or with
+    ``sampling`` = (k, temperature, top_p, u[15]) the choice of c_{j+1} draws
+    with u[j] (the log's subtalker sampling options).
     Returns codes [c1..c15] and per-pass (y, z, margin)."""
     cache = Cache(cp, cp_capacity)
     X = np.stack([np.asarray(y_talker, cp.dtype), cp.tables[0][c0]])
     yy, z = prefill(cp, cache, X, head=0)
-    c, m = penalized_argmax(z, None, 1.0)
+    c, m = choose(z, None, 1.0, sampling, 0)
     codes, trace = [c], [(yy, z, m)]
     n_groups = len(cp.heads)
     for j in range(1, n_groups):
         fed = forced[j - 1] if forced is not None else codes[-1]
         x = embed(cp, [fed], [j])
         yy, z = step(cp, cache, x, head=j)
-        c, m = penalized_argmax(z, None, 1.0)
+        c, m = choose(z, None, 1.0, sampling, j)
         codes.append(c)
         trace.append((yy, z, m))
     return codes, trace
@@ -391,7 +494,8 @@ def code_predictor_frame(cp: Model, y_talker: np.ndarray, c0: int,
 
 def run_talker(talker: Model, cp: Model, X0: np.ndarray, text: np.ndarray,
                n_frames: int, s_init: int, rho: float = 1.05,
-               cp_capacity: int = 16, forced: Optional[Sequence[Sequence[int]]] = None):
+               cp_capacity: int = 16, forced: Optional[Sequence[Sequence[int]]] = None,
+               tk_sampling=None, cp_sampling=None):
     """Two-level Talker frame loop (ncnn port, Talker section).
 
     Prefill X0 gives (y_0, z_0) and the main code c0_0 (penalty rho over the
@@ -399,11 +503,14 @@ def run_talker(talker: Model, cp: Model, X0: np.ndarray, text: np.ndarray,
     c0_f) into c1..c15; the next Talker input is E_tk[c0_f] + sum_j
     E_cp[j][c_j] + text[f+1]; a Talker step gives (y_{f+1}, z_{f+1}) and
     c0_{f+1}.  ``forced[f]`` (16 codes) replaces frame f's generated codes
-    when teacher forcing.  Returns per-frame dicts."""
+    when teacher forcing.  Sampled choices: tk_sampling = (k, temperature,
+    top_p, u[n_frames]) draws c0_f with u[f]; cp_sampling = (k, temperature,
+    top_p, u[n_frames, 15]) draws frame f's c_{j+1} with u[f, j].  Returns
+    per-frame dicts."""
     cache = Cache(talker, s_init)
     seen = np.zeros(talker.heads[0].shape[0], bool)
     y, z = prefill(talker, cache, X0, 0)
-    c0, m0 = penalized_argmax(z, seen, rho)
+    c0, m0 = choose(z, seen, rho, tk_sampling, 0)
     frames = []
     for f in range(n_frames):
         if forced is not None:
@@ -411,7 +518,10 @@ def run_talker(talker: Model, cp: Model, X0: np.ndarray, text: np.ndarray,
             cp_forced = forced[f][1:]
         else:
             c0_used, cp_forced = c0, None
-        codes, cp_trace = code_predictor_frame(cp, y, c0_used, cp_capacity, cp_forced)
+        cps = None
+        if cp_sampling is not None:
+            cps = cp_sampling[:3] + (np.asarray(cp_sampling[3])[f],)
+        codes, cp_trace = code_predictor_frame(cp, y, c0_used, cp_capacity, cp_forced, cps)
         used = [c0_used] + (list(cp_forced) if cp_forced is not None else codes)
         frames.append(dict(y=y, z=z, c0=c0, margin=m0, codes=codes, cp=cp_trace))
         if f == n_frames - 1:
@@ -422,5 +532,5 @@ def run_talker(talker: Model, cp: Model, X0: np.ndarray, text: np.ndarray,
             for g in range(f + 1):
                 seen[forced[g][0]] = True
         y, z = step(talker, cache, x, 0)
-        c0, m0 = penalized_argmax(z, seen, rho)
+        c0, m0 = choose(z, seen, rho, tk_sampling, f + 1)
     return frames, cache

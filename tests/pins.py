@@ -11,6 +11,7 @@ import os
 
 import numpy as np
 
+from autoregressive_transformer_decode_amd import inputs
 from oracle import brute
 from oracle import decoder as od
 from tests._models import tiny_model
@@ -319,6 +320,146 @@ def check_penalty_and_argmax():
     # ties: lowest index, margin 0
     t, mg = od.penalized_argmax(np.array([1.0, 3.0, 3.0], np.float32), None, 1.0)
     assert t == 1 and mg == 0.0
+
+
+# ---------------------------------------------------------------- sampling
+
+# logits log(1), log(2), log(3), log(4): at temperature 1 the softmax is
+# 0.1, 0.2, 0.3, 0.4
+_LOG4 = np.log(np.array([1.0, 2.0, 3.0, 4.0])).astype(np.float32)
+
+
+def _draw(z, k, t, top_p, u, seen=None, rho=1.0):
+    return od.sample_topk(z, seen, rho, k, t, top_p, u).tok
+
+
+def check_sampling_inverse_cdf():
+    """Temperature 1, k = 4: the tokens in descending order of logit carry
+    0.4, 0.3, 0.2, 0.1; the draw takes the first whose cumulative
+    probability exceeds u (boundaries 0.4, 0.7, 0.9)."""
+    toks, p, _, _ = od.sampling_distribution(_LOG4, None, 1.0, 4, 1.0)
+    assert list(toks) == [3, 2, 1, 0]
+    _close(p, [0.4, 0.3, 0.2, 0.1], 1e-6)
+    for u, exp in [(0.0, 3), (0.35, 3), (0.45, 2), (0.75, 1), (0.95, 0), (0.99999, 0)]:
+        assert _draw(_LOG4, 4, 1.0, 1.0, u) == exp, u
+
+
+def check_sampling_temperature():
+    """The temperature divides the logits: at 0.5 the weights are the squares
+    1, 4, 9, 16 (/30), at 2 the square roots."""
+    _, p, _, _ = od.sampling_distribution(_LOG4, None, 1.0, 4, 0.5)
+    _close(p, np.array([16.0, 9.0, 4.0, 1.0]) / 30.0, 1e-6)
+    r = np.sqrt(np.array([4.0, 3.0, 2.0, 1.0]))
+    _, p2, _, _ = od.sampling_distribution(_LOG4, None, 1.0, 4, 2.0)
+    _close(p2, r / r.sum(), 1e-6)
+    # u = 0.35 lies below the first boundary at 0.5 (16/30 = 0.533) and 1.0
+    # (0.4), above it at 2.0 (0.325)
+    assert _draw(_LOG4, 4, 0.5, 1.0, 0.35) == 3
+    assert _draw(_LOG4, 4, 1.0, 1.0, 0.35) == 3
+    assert _draw(_LOG4, 4, 2.0, 1.0, 0.35) == 2
+    assert _draw(_LOG4, 4, 0.5, 1.0, 0.9) == 1
+
+
+def check_sampling_topk():
+    """Top-k keeps the k largest and renormalises: k = 2 gives 4/7, 3/7;
+    k = 3 gives 4/9, 3/9, 2/9."""
+    toks, p, _, _ = od.sampling_distribution(_LOG4, None, 1.0, 2, 1.0)
+    assert list(toks) == [3, 2]
+    _close(p, [4 / 7, 3 / 7], 1e-6)
+    toks, p, _, _ = od.sampling_distribution(_LOG4, None, 1.0, 3, 1.0)
+    assert list(toks) == [3, 2, 1]
+    _close(p, [4 / 9, 3 / 9, 2 / 9], 1e-6)
+    assert _draw(_LOG4, 2, 1.0, 1.0, 0.5) == 3      # 0.5 < 4/7
+    assert _draw(_LOG4, 2, 1.0, 1.0, 0.6) == 2
+    assert _draw(_LOG4, 2, 1.0, 1.0, 0.99) == 2     # never a token outside the set
+
+
+def check_sampling_top_p():
+    """Top-p keeps the shortest descending prefix whose probability reaches
+    top_p, over the top-k set."""
+    cases = [(4, 0.6, [3, 2]), (4, 0.35, [3]), (4, 0.75, [3, 2, 1]), (4, 1.0, [3, 2, 1, 0]),
+             (3, 0.8, [3, 2, 1]), (3, 0.7, [3, 2])]   # k = 3: cumulative 4/9, 7/9, 1
+    for k, tp, exp in cases:
+        toks, p, _, _ = od.sampling_distribution(_LOG4, None, 1.0, k, 1.0, tp)
+        assert list(toks) == exp, (k, tp, list(toks))
+        _close(p, np.array([4.0, 3.0, 2.0, 1.0])[:len(exp)] / (10 - sum(range(1, 5 - len(exp)))), 1e-6)
+    assert _draw(_LOG4, 4, 1.0, 0.35, 0.99) == 3
+
+
+def check_sampling_ties_and_penalty():
+    """Equal logits: the set takes the lowest indices and shares the mass
+    equally.  The penalty acts before the set is taken."""
+    z = np.zeros(10, np.float32)
+    toks, p, _, _ = od.sampling_distribution(z, None, 1.0, 3, 0.9)
+    assert list(toks) == [0, 1, 2]
+    _close(p, [1 / 3] * 3, 1e-12)
+    assert _draw(z, 3, 0.9, 1.0, 0.5) == 1
+    z2 = np.array([1.0, 2.0, 2.0, 2.0, 0.0], np.float32)
+    toks, _, _, _ = od.sampling_distribution(z2, None, 1.0, 2, 1.0)
+    assert list(toks) == [1, 2]
+    z3 = np.array([3.0, 2.9, 1.0], np.float32)
+    seen = np.array([True, False, False])
+    assert _draw(z3, 1, 1.0, 1.0, 0.3, seen.copy(), 1.2) == 1    # 3.0 / 1.2 = 2.5 < 2.9
+    toks, _, _, _ = od.sampling_distribution(z3, seen, 1.2, 2, 1.0)
+    assert list(toks) == [1, 0]
+    s2 = seen.copy()
+    od.sample_topk(z3, s2, 1.2, 1, 1.0, 1.0, 0.3)
+    assert s2[1] and s2[0] and not s2[2]
+
+
+def check_sampling_greedy_limit():
+    """k = 1 is the penalized argmax for every u (ties included)."""
+    z = inputs.normal(5, 9, 1, (300,), scale=1.0)
+    z[17] = z[200] = z.max() + 1.0          # the penalty breaks this tie
+    seen = np.zeros(300, bool)
+    seen[[3, 17, 50]] = True
+    z2 = z.copy()
+    z2[260] = z2[250] = z.max() + 2.0       # an exact tie: the lower index
+    for zz, exp in ((z, 200), (z2, 250)):
+        for u in (0.0, 0.3, 0.999):
+            t = od.sample_topk(zz, seen.copy(), 1.05, 1, 0.9, 1.0, u).tok
+            g, _ = od.penalized_argmax(zz, seen.copy(), 1.05)
+            assert t == g == exp, (t, g, exp)
+
+
+def _brute_distribution(z, seen, rho, k, t, top_p):
+    """Scalar float64 definition: penalise, sort (value desc, index asc), keep
+    k, exp(z / t) normalised, shortest prefix reaching top_p."""
+    zp = []
+    for i, v in enumerate(z.tolist()):
+        if seen is not None and seen[i]:
+            v = v / rho if v > 0 else v * rho
+        zp.append(v)
+    order = sorted(range(len(zp)), key=lambda i: (-zp[i], i))[:k]
+    w = [math.exp(zp[i] / t) for i in order]
+    tot = sum(w)
+    keep, acc = [], 0.0
+    for i, wi in zip(order, w):
+        keep.append((i, wi))
+        acc += wi / tot
+        if acc >= top_p:
+            break
+    s = sum(wi for _, wi in keep)
+    return {i: wi / s for i, wi in keep}
+
+
+def check_sampling_frequencies():
+    """Brute force: over a uniform grid of u the draw hits each token with
+    its probability (within one grid step) and never a token outside the
+    kept set."""
+    z = inputs.normal(6, 9, 2, (60,), scale=1.5)
+    seen = np.zeros(60, bool)
+    seen[::7] = True
+    n = 4000
+    for k, t, tp in [(10, 0.7, 1.0), (25, 1.3, 0.8), (60, 0.9, 1.0)]:
+        exp = _brute_distribution(z, seen, 1.05, k, t, tp)
+        hits = {}
+        for i in range(n):
+            tok = _draw(z, k, t, tp, (i + 0.5) / n, seen.copy(), 1.05)
+            hits[tok] = hits.get(tok, 0) + 1
+        assert set(hits) <= set(exp), (k, set(hits) - set(exp))
+        for tok, p in exp.items():
+            assert abs(hits.get(tok, 0) / n - p) <= 1.0 / n + 1e-6, (k, tok, hits.get(tok, 0) / n, p)
 
 
 # ---------------------------------------------------------------- golden

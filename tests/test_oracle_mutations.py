@@ -130,7 +130,52 @@ def _cp_head0(cp, y_talker, c0, cp_capacity=16, forced=None):
         od.step = real_step
 
 
+def _dist_ascending(z, seen, rho, k, t, top_p=1.0):
+    toks, p, cum, zp = _orig["sampling_distribution"](z, seen, rho, k, t, top_p)
+    return toks[::-1], p[::-1], cum, zp
+
+
+def _dist_temp_multiplies(z, seen, rho, k, t, top_p=1.0):
+    return _orig["sampling_distribution"](z, seen, rho, k, 1.0 / t, top_p)
+
+
+def _dist_top_p_ignored(z, seen, rho, k, t, top_p=1.0):
+    return _orig["sampling_distribution"](z, seen, rho, k, t, 1.0)
+
+
+def _dist_not_renormalised(z, seen, rho, k, t, top_p=1.0):
+    toks, p, cum, zp = _orig["sampling_distribution"](z, seen, rho, k, t, top_p)
+    v = zp.astype(np.float64)
+    w = np.exp((v - v.max()) / t)
+    return toks, w[toks] / w.sum(), cum, zp
+
+
+def _dist_penalty_after_set(z, seen, rho, k, t, top_p=1.0):
+    cand = od.topk_candidates(np.asarray(z, np.float32), k)
+    zp = od.penalized_logits(z, seen, rho)
+    order = cand[np.lexsort((cand, -zp[cand].astype(np.float64)))]
+    v = zp[order].astype(np.float64)
+    w = np.exp((v - v[0]) / t)
+    return order, w / w.sum(), np.cumsum(w) / w.sum(), zp
+
+
+def _topk_high_index_ties(zp, k):
+    order = np.lexsort((-np.arange(zp.size), -zp.astype(np.float64)))
+    return order[:k]
+
+
+def _topk_one_more(zp, k):
+    return _orig["topk_candidates"](zp, k + 1)
+
+
 MUTATIONS = {
+    "sample_walks_ascending": ("sampling_distribution", _dist_ascending),
+    "sample_temperature_multiplies": ("sampling_distribution", _dist_temp_multiplies),
+    "sample_top_p_ignored": ("sampling_distribution", _dist_top_p_ignored),
+    "sample_not_renormalised": ("sampling_distribution", _dist_not_renormalised),
+    "sample_penalty_after_set": ("sampling_distribution", _dist_penalty_after_set),
+    "topk_ties_high_index": ("topk_candidates", _topk_high_index_ties),
+    "topk_one_more": ("topk_candidates", _topk_one_more),
     "rms_gain_one_plus_g": ("rms_norm", _rms_one_plus),
     "rms_no_eps": ("rms_norm", _rms_no_eps),
     "rope_adjacent_pairs": ("rope", _rope_adjacent),

@@ -23,6 +23,13 @@ PINS = [
     pins.check_code_predictor_recompute,
     pins.check_frame_input,
     pins.check_penalty_and_argmax,
+    pins.check_sampling_inverse_cdf,
+    pins.check_sampling_temperature,
+    pins.check_sampling_topk,
+    pins.check_sampling_top_p,
+    pins.check_sampling_ties_and_penalty,
+    pins.check_sampling_greedy_limit,
+    pins.check_sampling_frequencies,
     pins.check_bucket_schedule_golden,
     pins.check_talker_bytes_golden,
 ]

@@ -36,7 +36,7 @@ STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FU
 
 EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
-           "decoder_step", "decoder_embed", "greedy_argmax", "decoder_generate",
+           "decoder_step", "decoder_embed", "greedy_argmax", "sample_topk", "decoder_generate",
            "talker_generate_frames", "decoder_time_stage")
 
 ATD_STAGE_QKV, ATD_STAGE_ROPE, ATD_STAGE_ATTN, ATD_STAGE_OPROJ, ATD_STAGE_GATEUP, \
@@ -58,6 +58,14 @@ class atd_config(C.Structure):
                 ("rope_theta", C.c_double), ("rms_eps", C.c_float),
                 ("max_slots", C.c_int32), ("max_rows", C.c_int32), ("max_ctx", C.c_int32),
                 ("flags", C.c_int32)]
+
+
+ATD_TOPK_MAX = 256
+
+
+class atd_sampling(C.Structure):
+    _fields_ = [("top_k", C.c_int32), ("temperature", C.c_float), ("top_p", C.c_float),
+                ("uniforms", C.c_void_p)]
 
 
 class atd_layer_weights(C.Structure):
@@ -90,10 +98,12 @@ def _load():
         "decoder_step": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, vp, vp], C.c_int),
         "decoder_embed": ([vp, i32, vp, i32, C.POINTER(i32), vp, vp, vp], C.c_int),
         "greedy_argmax": ([vp, i32, i32, vp, f32, vp, vp, vp], C.c_int),
-        "decoder_generate": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, f32, vp, vp,
-                              vp, vp], C.c_int),
-        "talker_generate_frames": ([vp, i32, vp, i32, i32, vp, vp, vp, vp, f32, vp, vp, vp, vp],
-                                   C.c_int),
+        "sample_topk": ([vp, i32, i32, vp, f32, C.POINTER(atd_sampling), vp, vp], C.c_int),
+        "decoder_generate": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, f32,
+                              C.POINTER(atd_sampling), vp, vp, vp, vp], C.c_int),
+        "talker_generate_frames": ([vp, i32, vp, i32, i32, vp, vp, vp, vp, f32,
+                                    C.POINTER(atd_sampling), C.POINTER(atd_sampling), vp, vp, vp,
+                                    vp], C.c_int),
         "decoder_time_stage": ([vp, i32, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
     }
     for name, (args, res) in sig.items():
@@ -175,19 +185,32 @@ def greedy_argmax(logits: int, B: int, V: int, seen, penalty: float, tok_out: in
     _check(lib.greedy_argmax(logits, B, V, seen, penalty, tok_out, margin_out, stream))
 
 
+def _sampling(sp):
+    """None, or an atd_sampling passed by reference."""
+    return None if sp is None else C.byref(sp)
+
+
+def sample_topk(logits: int, B: int, V: int, seen, penalty: float, sampling: atd_sampling,
+                tok_out: int, stream: int) -> None:
+    _check(lib.sample_topk(logits, B, V, seen, penalty, C.byref(sampling), tok_out, stream))
+
+
 def decoder_generate(handle: int, slot: int, n_steps: int, tok_io: int, G: int, table_ids,
-                     extra, head: int, seen, penalty: float, tokens_out, y_out, logits_out: int,
-                     stream: int) -> None:
+                     extra, head: int, seen, penalty: float, sampling, tokens_out, y_out,
+                     logits_out: int, stream: int) -> None:
     _check(lib.decoder_generate(handle, slot, n_steps, tok_io, G, _i32_array(list(table_ids)),
-                                extra, head, seen, penalty, tokens_out, y_out, logits_out,
-                                stream), handle)
+                                extra, head, seen, penalty, _sampling(sampling), tokens_out,
+                                y_out, logits_out, stream), handle)
 
 
 def talker_generate_frames(tk: int, tk_slot: int, cp: int, cp_slot: int, n_frames: int,
-                           codes_io: int, y_io: int, text, seen: int, penalty: float, codes_out,
-                           tk_logits: int, cp_logits: int, stream: int) -> None:
+                           codes_io: int, y_io: int, text, seen: int, penalty: float,
+                           tk_sampling, cp_sampling, codes_out, tk_logits: int, cp_logits: int,
+                           stream: int) -> None:
     _check(lib.talker_generate_frames(tk, tk_slot, cp, cp_slot, n_frames, codes_io, y_io, text,
-                                      seen, penalty, codes_out, tk_logits, cp_logits, stream), tk)
+                                      seen, penalty, _sampling(tk_sampling),
+                                      _sampling(cp_sampling), codes_out, tk_logits, cp_logits,
+                                      stream), tk)
 
 
 def decoder_time_stage(handle: int, stage: int, slot0: int, B: int, reps: int,

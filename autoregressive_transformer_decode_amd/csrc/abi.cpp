@@ -37,6 +37,7 @@ struct atd_decoder {
   void** kv_tab = nullptr;
   int *slot_pos = nullptr, *slot_cap = nullptr;
   float* part = nullptr;       // argmax partials [max_rows, nblk, 3]
+  uint2* samp = nullptr;       // sampler chunk candidates [sample_blocks(V), kTopKMax]
   bool mma = false;            // MFMA path for chunks of >= 3 rows
   float* mpart = nullptr;      // split-K partials of the MFMA GEMMs
   float* mss = nullptr;        // row sums of squares [kMmaRows, ceil(h / kSsCols)]
@@ -625,6 +626,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   const int nblk_v = (cfg->vocab + kArgmaxChunk - 1) / kArgmaxChunk;
   const size_t o_part = carve((size_t)R * nblk_v * 3 * 4);
   const size_t o_cnt = carve(4);
+  const int nblk_s = sample_blocks(cfg->vocab);
+  const size_t o_samp = carve(nblk_s > 1 ? (size_t)nblk_s * kTopKMax * sizeof(uint2) : 0);
   // MFMA path: hi/lo activations of one 64-row chunk and split-K partials of
   // the largest GEMM (q/k/v, o, gate/up, down, LM head)
   d->mma = cfg->dtype == ATD_BF16 && !(cfg->flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 &&
@@ -663,6 +666,7 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->slot_cap = (int*)(base + o_cap);
   d->part = (float*)(base + o_part);
   d->counter = (int32_t*)(base + o_cnt);
+  d->samp = (uint2*)(base + o_samp);
   if (d->mma) {
     d->mss = (float*)(base + o_mss);
     d->mhi = (uint16_t*)(base + o_mhi);
@@ -889,12 +893,74 @@ extern "C" int decoder_step(atd_decoder* d, int32_t slot0, int32_t B, const int3
 // ---------------------------------------------------------------- argmax
 
 namespace {
-struct ArgmaxScratch {
+struct ChoiceScratch {
   void* p = nullptr;
   size_t bytes = 0;
 };
-std::mutex g_argmax_mu;
-std::map<int, ArgmaxScratch> g_argmax_scratch;
+std::mutex g_choice_mu;
+std::map<int, ChoiceScratch> g_choice_scratch;
+
+// Device scratch of greedy_argmax / sample_topk, one per device, grown on
+// demand (calls that overlap on one device share it).
+int choice_scratch(size_t need, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_choice_mu);
+  ChoiceScratch& sc = g_choice_scratch[dev];
+  if (sc.bytes < need) {
+    if (sc.p) (void)hipFree(sc.p);
+    sc.p = nullptr;
+    sc.bytes = 0;
+    const size_t bytes = std::max(need, size_t(1) << 16);
+    e = hipMalloc(&sc.p, bytes);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "hipMalloc of token-choice scratch");
+    sc.bytes = bytes;
+  }
+  *out = sc.p;
+  return ATD_OK;
+}
+
+// Validates sampling settings for a vocabulary of V (d may be NULL).
+int check_sampling(atd_decoder* d, const atd_sampling* sp, int V) {
+  if (!sp->uniforms) return fail(d, ATD_ERR_INVALID_ARG, "sampling uniforms is NULL");
+  if (sp->top_k < 1 || sp->top_k > kTopKMax || sp->top_k > V)
+    return fail(d, ATD_ERR_INVALID_ARG, "top_k %d outside [1, min(%d, V = %d)]", sp->top_k,
+                kTopKMax, V);
+  if (!(sp->temperature > 0.0f) || !std::isfinite(sp->temperature))
+    return fail(d, ATD_ERR_INVALID_ARG, "temperature %g is not a positive number",
+                (double)sp->temperature);
+  if (!(sp->top_p > 0.0f && sp->top_p <= 1.0f))
+    return fail(d, ATD_ERR_INVALID_ARG, "top_p %g outside (0, 1]", (double)sp->top_p);
+  const int nblk = sample_blocks(V);
+  if (nblk > 1 && (int64_t)nblk * sp->top_k > kSampleChunk)
+    return fail(d, ATD_ERR_UNSUPPORTED,
+                "V = %d in %d chunks of %d keeps %d candidates, above the %d one workgroup "
+                "selects from",
+                V, nblk, kSampleChunk, nblk * sp->top_k, kSampleChunk);
+  return ATD_OK;
+}
+
+SampleArgs sample_args(const float* z, int B, int V, uint32_t* seen, float penalty,
+                       const atd_sampling& sp, int32_t* tok, uint2* part) {
+  SampleArgs a{};
+  a.z = z;
+  a.B = B;
+  a.V = V;
+  a.seen = seen;
+  a.nwords = (V + 31) / 32;
+  a.penalty = penalty;
+  a.k = sp.top_k;
+  a.temperature = sp.temperature;
+  a.top_p = sp.top_p;
+  a.u = sp.uniforms;
+  a.u_row = nullptr;
+  a.u_stride = 0;
+  a.tok = tok;
+  a.part = part;
+  a.nblk = sample_blocks(V);
+  return a;
+}
 }  // namespace
 
 extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
@@ -915,25 +981,35 @@ extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t
   a.tok = tok_out;
   a.margin = margin_out;
   a.nblk = (V + kArgmaxChunk - 1) / kArgmaxChunk;
-  const size_t need = (size_t)B * a.nblk * 3 * sizeof(float);
-  {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDevice");
-    std::lock_guard<std::mutex> lk(g_argmax_mu);
-    ArgmaxScratch& sc = g_argmax_scratch[dev];
-    if (sc.bytes < need) {
-      if (sc.p) (void)hipFree(sc.p);
-      sc.p = nullptr;
-      sc.bytes = 0;
-      e = hipMalloc(&sc.p, std::max(need, size_t(1) << 16));
-      if (e != hipSuccess) return hip_fail(nullptr, e, "hipMalloc of argmax scratch");
-      sc.bytes = std::max(need, size_t(1) << 16);
-    }
-    a.part = (float*)sc.p;
-  }
+  void* p = nullptr;
+  const int rc = choice_scratch((size_t)B * a.nblk * 3 * sizeof(float), &p);
+  if (rc) return rc;
+  a.part = (float*)p;
   hipError_t e = launch_argmax(a, (hipStream_t)stream);
   return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "greedy_argmax");
+}
+
+extern "C" int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* seen,
+                           float penalty, const atd_sampling* sampling, int32_t* tok_out,
+                           void* stream) {
+  if (!logits || !tok_out || !sampling)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "logits, sampling or tok_out is NULL");
+  if (B < 1) return fail(nullptr, ATD_ERR_INVALID_ARG, "B = %d < 1", B);
+  if (V < 1) return fail(nullptr, ATD_ERR_INVALID_ARG, "V = %d < 1", V);
+  if (!(penalty > 0.0f) || !std::isfinite(penalty))
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "penalty %g is not a positive number",
+                (double)penalty);
+  int rc = check_sampling(nullptr, sampling, V);
+  if (rc) return rc;
+  SampleArgs a = sample_args(logits, B, V, seen, penalty, *sampling, tok_out, nullptr);
+  if (a.nblk > 1) {
+    void* p = nullptr;
+    rc = choice_scratch((size_t)B * a.nblk * a.k * sizeof(uint2), &p);
+    if (rc) return rc;
+    a.part = (uint2*)p;
+  }
+  hipError_t e = launch_sample(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "sample_topk");
 }
 
 // ---------------------------------------------------------------- generation
@@ -963,13 +1039,57 @@ hipError_t cache_graph(atd_decoder* d, std::vector<int64_t> key, hipGraphExec_t 
   return hipSuccess;
 }
 
+uint32_t float_bits(float f) {
+  uint32_t b;
+  std::memcpy(&b, &f, 4);
+  return b;
+}
+
+// Sampling settings as graph-key entries (a single 0 for greedy).
+void key_sampling(std::vector<int64_t>& key, const atd_sampling* sp) {
+  if (!sp) {
+    key.push_back(0);
+    return;
+  }
+  key.insert(key.end(), {1, sp->top_k, float_bits(sp->temperature), float_bits(sp->top_p),
+                         (int64_t)(uintptr_t)sp->uniforms});
+}
+
+// Token choice of one row of d's logits inside a captured step: the
+// penalised argmax (sp NULL) or the draw with
+// u = sp->uniforms[u_off + (*u_row) * u_stride].
+hipError_t enqueue_choice(atd_decoder* d, const float* z, uint32_t* seen, float penalty,
+                          const atd_sampling* sp, const int32_t* u_row, int u_stride, int u_off,
+                          int32_t* tok, hipStream_t s) {
+  const int V = d->cfg.vocab;
+  if (!sp) {
+    ArgmaxArgs a{};
+    a.z = z;
+    a.B = 1;
+    a.V = V;
+    a.seen = seen;
+    a.nwords = (V + 31) / 32;
+    a.penalty = penalty;
+    a.tok = tok;
+    a.margin = nullptr;
+    a.part = d->part;
+    a.nblk = (V + kArgmaxChunk - 1) / kArgmaxChunk;
+    return launch_argmax(a, s);
+  }
+  SampleArgs a = sample_args(z, 1, V, seen, penalty, *sp, tok, d->samp);
+  a.u = sp->uniforms + u_off;
+  a.u_row = u_row;
+  a.u_stride = u_stride;
+  return launch_sample(a, s);
+}
+
 }  // namespace
 
 extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, int32_t* tok_io,
                                 int32_t G, const int32_t* table_ids, const float* extra,
                                 int32_t head, uint32_t* seen, float penalty,
-                                int32_t* tokens_out, float* y_out, float* logits_out,
-                                void* stream) {
+                                const atd_sampling* sampling, int32_t* tokens_out, float* y_out,
+                                float* logits_out, void* stream) {
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
   const atd_config& c = d->cfg;
   if (slot < 0 || slot >= c.max_slots)
@@ -987,6 +1107,7 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
     return fail(d, ATD_ERR_INVALID_ARG, "head %d outside [0, %d)", head, c.n_lm_heads);
   if (!(penalty > 0.0f) || !std::isfinite(penalty))
     return fail(d, ATD_ERR_INVALID_ARG, "penalty %g is not a positive number", (double)penalty);
+  if (sampling && (rc = check_sampling(d, sampling, c.vocab)) != ATD_OK) return rc;
   if ((int64_t)d->pos[slot] + n_steps > d->cap[slot])
     return fail(d, ATD_ERR_KV_FULL, "slot %d: %d steps from position %d exceed capacity %d",
                 slot, n_steps, d->pos[slot], d->cap[slot]);
@@ -1005,12 +1126,10 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
                               (int64_t)(uintptr_t)tok_io, (int64_t)(uintptr_t)seen,
                               (int64_t)(uintptr_t)tokens_out, (int64_t)(uintptr_t)y_out,
                               (int64_t)(uintptr_t)logits_out, max_cap, bucket_key(d, slot)};
-  {
-    uint32_t pb;
-    std::memcpy(&pb, &penalty, 4);
-    key.push_back(pb);
-    for (int g = 0; g < G; ++g) key.push_back(table_ids[g]);
-  }
+  key.push_back(float_bits(penalty));
+  for (int g = 0; g < G; ++g) key.push_back(table_ids[g]);
+  key_sampling(key, sampling);
+  const bool count = tokens_out || sampling;   // the step index lives in d->counter
   hipGraphExec_t exec = nullptr;
   for (auto& ge : d->graphs)
     if (ge.key == key) exec = ge.exec;
@@ -1025,21 +1144,9 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
     if (e != hipSuccess) return hip_fail(d, e, "hipStreamBeginCapture");
     hipError_t le = enqueue_step(d, slot, 1, tok_io, G, table_ids, extra, head, y_out, logits_out,
                                  max_cap, cs);
-    if (le == hipSuccess) {
-      ArgmaxArgs a{};
-      a.z = logits_out;
-      a.B = 1;
-      a.V = c.vocab;
-      a.seen = seen;
-      a.nwords = (c.vocab + 31) / 32;
-      a.penalty = penalty;
-      a.tok = tok_io;
-      a.margin = nullptr;
-      a.part = d->part;
-      a.nblk = (c.vocab + kArgmaxChunk - 1) / kArgmaxChunk;
-      le = launch_argmax(a, cs);
-    }
-    if (le == hipSuccess && tokens_out) le = launch_record_token(tok_io, tokens_out, d->counter, cs);
+    if (le == hipSuccess)
+      le = enqueue_choice(d, logits_out, seen, penalty, sampling, d->counter, 1, 0, tok_io, cs);
+    if (le == hipSuccess && count) le = launch_record_token(tok_io, tokens_out, d->counter, cs);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     if (le != hipSuccess || e != hipSuccess) {
@@ -1052,7 +1159,7 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
     e = cache_graph(d, key, exec);
     if (e != hipSuccess) return hip_fail(d, e, "graph cache");
   }
-  if (tokens_out) e = launch_fill_i32(d->counter, 1, 0, s);
+  if (count) e = launch_fill_i32(d->counter, 1, 0, s);
   for (int k = 0; k < n_steps && e == hipSuccess; ++k) e = hipGraphLaunch(exec, s);
   if (e != hipSuccess) return hip_fail(d, e, "decoder_generate replay");
   d->pos[slot] += n_steps;
@@ -1067,19 +1174,14 @@ constexpr int kCodeGroups = 16;   // codes per Talker frame (c0 and 15 Code Pred
 
 // The Code Predictor pass of one frame, then the record of its 16 codes:
 // rows [y, table_0[c0]] -> 2-row prefill, head 0 -> c1; steps j = 1..14 fed
-// table_j[c_j], head j -> c_{j+1}.
+// table_j[c_j], head j -> c_{j+1}.  Choices greedy (sp NULL) or drawn with
+// u = sp->uniforms[(*counter) * 15 + j] for c_{j+1}.
 hipError_t enqueue_cp_pass(atd_decoder* cp, int cp_slot, int32_t* codes, const float* y,
-                           float* cp_logits, int32_t* codes_out, int32_t* counter, hipStream_t s) {
+                           float* cp_logits, int32_t* codes_out, int32_t* counter,
+                           const atd_sampling* sp, hipStream_t s) {
   const atd_config& c = cp->cfg;
   const int cp_cap = std::min(cp->cap[cp_slot], c.max_ctx);
-  ArgmaxArgs am{};
-  am.B = 1;
-  am.V = c.vocab;
-  am.nwords = (c.vocab + 31) / 32;
-  am.penalty = 1.0f;
-  am.part = cp->part;
-  am.nblk = (c.vocab + kArgmaxChunk - 1) / kArgmaxChunk;
-  am.z = cp_logits;
+  const int G = kCodeGroups - 1;
   // prefill rows: the Talker's output and the embedding of c0 (table 0)
   const int32_t t0 = 0;
   EmbedArgs r0 = embed_args(cp, 1, nullptr, 0, nullptr, y, cp->x);
@@ -1090,23 +1192,24 @@ hipError_t enqueue_cp_pass(atd_decoder* cp, int cp_slot, int32_t* codes, const f
   if (e == hipSuccess) e = run_layers(cp, pre, 2, 2, cp->x, nullptr, s);
   if (e == hipSuccess) e = run_head_gemv(cp, cp->x + c.hidden, 1, 0, nullptr, cp_logits, s);
   if (e == hipSuccess) e = launch_advance(slots_of(cp), pre, 2, s);
-  am.tok = codes + 1;
-  if (e == hipSuccess) e = launch_argmax(am, s);
-  for (int j = 1; j < kCodeGroups - 1 && e == hipSuccess; ++j) {
+  if (e == hipSuccess)
+    e = enqueue_choice(cp, cp_logits, nullptr, 1.0f, sp, counter, G, 0, codes + 1, s);
+  for (int j = 1; j < G && e == hipSuccess; ++j) {
     const int32_t tj = j;
     e = enqueue_step(cp, cp_slot, 1, codes + j, 1, &tj, nullptr, j, nullptr, cp_logits, cp_cap, s);
-    am.tok = codes + j + 1;
-    if (e == hipSuccess) e = launch_argmax(am, s);
+    if (e == hipSuccess)
+      e = enqueue_choice(cp, cp_logits, nullptr, 1.0f, sp, counter, G, j, codes + j + 1, s);
   }
   if (e == hipSuccess) e = launch_record_tokens(codes, kCodeGroups, codes_out, counter, s);
   return e;
 }
 
 // One Talker step of the frame loop: input sum_g table_g[c_g] + text[*counter],
-// head 0 -> y and logits, penalised argmax -> c0.
+// head 0 -> y and logits, penalised choice -> c0 (greedy, or drawn with
+// u = sp->uniforms[*counter]).
 hipError_t enqueue_talker_step(atd_decoder* tk, int tk_slot, int32_t* codes, const float* text,
-                               int32_t* counter, uint32_t* seen, float penalty, float* y,
-                               float* tk_logits, hipStream_t s) {
+                               int32_t* counter, uint32_t* seen, float penalty,
+                               const atd_sampling* sp, float* y, float* tk_logits, hipStream_t s) {
   const atd_config& c = tk->cfg;
   int32_t tabs[kCodeGroups];
   for (int g = 0; g < kCodeGroups; ++g) tabs[g] = g;
@@ -1118,19 +1221,7 @@ hipError_t enqueue_talker_step(atd_decoder* tk, int tk_slot, int32_t* codes, con
   const int max_cap = std::min(tk->cap[tk_slot], c.max_ctx);
   if (e == hipSuccess) e = run_layers(tk, rows, 1, max_cap, tk->x, &ho, s);
   if (e == hipSuccess) e = launch_advance(slots_of(tk), rows, 1, s);
-  if (e == hipSuccess) {
-    ArgmaxArgs am{};
-    am.z = tk_logits;
-    am.B = 1;
-    am.V = c.vocab;
-    am.seen = seen;
-    am.nwords = (c.vocab + 31) / 32;
-    am.penalty = penalty;
-    am.tok = codes;
-    am.part = tk->part;
-    am.nblk = (c.vocab + kArgmaxChunk - 1) / kArgmaxChunk;
-    e = launch_argmax(am, s);
-  }
+  if (e == hipSuccess) e = enqueue_choice(tk, tk_logits, seen, penalty, sp, counter, 1, 0, codes, s);
   return e;
 }
 
@@ -1139,8 +1230,9 @@ hipError_t enqueue_talker_step(atd_decoder* tk, int tk_slot, int32_t* codes, con
 extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_decoder* cp,
                                       int32_t cp_slot, int32_t n_frames, int32_t* codes_io,
                                       float* y_io, const float* text, uint32_t* seen,
-                                      float penalty, int32_t* codes_out, float* tk_logits,
-                                      float* cp_logits, void* stream) {
+                                      float penalty, const atd_sampling* tk_sampling,
+                                      const atd_sampling* cp_sampling, int32_t* codes_out,
+                                      float* tk_logits, float* cp_logits, void* stream) {
   if (!tk) return fail(nullptr, ATD_ERR_INVALID_ARG, "Talker decoder is NULL");
   if (!cp || cp == tk) return fail(tk, ATD_ERR_INVALID_ARG, "Code Predictor decoder is NULL or the Talker's");
   const atd_config &tc = tk->cfg, &cc = cp->cfg;
@@ -1174,14 +1266,16 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
   if (!aligned16(y_io)) return fail(tk, ATD_ERR_INVALID_ARG, "y_io %p not 16-byte aligned", (void*)y_io);
   if (!(penalty > 0.0f) || !std::isfinite(penalty))
     return fail(tk, ATD_ERR_INVALID_ARG, "penalty %g is not a positive number", (double)penalty);
+  int rc = ATD_OK;
+  if (tk_sampling && (rc = check_sampling(tk, tk_sampling, tc.vocab)) != ATD_OK) return rc;
+  if (cp_sampling && (rc = check_sampling(tk, cp_sampling, cc.vocab)) != ATD_OK) return rc;
   if (tk->dry) {
     tk->pos[tk_slot] += steps;
     cp->pos[cp_slot] = kCodeGroups;
     return ATD_OK;
   }
   hipStream_t s = (hipStream_t)stream;
-  uint32_t pb;
-  std::memcpy(&pb, &penalty, 4);
+  const uint32_t pb = float_bits(penalty);
   const int64_t tag = 0x46524d;   // frame graphs in the Talker decoder's cache
   auto graph_for = [&](int full, hipGraphExec_t* out) -> hipError_t {
     std::vector<int64_t> key = {tag, full, tk_slot, (int64_t)(uintptr_t)cp, cp_slot,
@@ -1192,6 +1286,8 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
                                 std::min(tk->cap[tk_slot], tc.max_ctx),
                                 std::min(cp->cap[cp_slot], cc.max_ctx), bucket_key(tk, tk_slot),
                                 bucket_key(cp, cp_slot)};
+    key_sampling(key, tk_sampling);
+    key_sampling(key, cp_sampling);
     for (auto& ge : tk->graphs)
       if (ge.key == key) {
         *out = ge.exec;
@@ -1207,10 +1303,11 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
     if (e != hipSuccess) return e;
     hipError_t le = hipSuccess;
     if (full)
-      le = enqueue_talker_step(tk, tk_slot, codes_io, text, tk->counter, seen, penalty, y_io,
-                               tk_logits, cs);
+      le = enqueue_talker_step(tk, tk_slot, codes_io, text, tk->counter, seen, penalty,
+                               tk_sampling, y_io, tk_logits, cs);
     if (le == hipSuccess)
-      le = enqueue_cp_pass(cp, cp_slot, codes_io, y_io, cp_logits, codes_out, tk->counter, cs);
+      le = enqueue_cp_pass(cp, cp_slot, codes_io, y_io, cp_logits, codes_out, tk->counter,
+                           cp_sampling, cs);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     if (le != hipSuccess || e != hipSuccess) {

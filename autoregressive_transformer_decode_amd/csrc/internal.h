@@ -155,6 +155,33 @@ struct ArgmaxArgs {
   int nblk;
 };
 
+// top-k sampling: one 1024-thread workgroup selects from up to kSampleChunk
+// values (8 per thread); longer rows are cut into chunks whose top-k
+// candidates a second workgroup selects from
+constexpr int kTopKMax = 256;
+constexpr int kSampleThreads = 1024;
+constexpr int kSamplePerThread = 8;
+constexpr int kSampleChunk = kSampleThreads * kSamplePerThread;
+
+inline int sample_blocks(int V) { return (V + kSampleChunk - 1) / kSampleChunk; }
+
+struct SampleArgs {
+  const float* z;        // [B, V]
+  int B, V;
+  uint32_t* seen;        // [B, nwords] or null
+  int nwords;
+  float penalty;
+  int k;                 // 1..kTopKMax, <= V
+  float temperature;     // > 0
+  float top_p;           // (0, 1]
+  const float* u;        // row b draws u[(u_row ? *u_row : 0) * u_stride + b]
+  const int32_t* u_row;  // device index or null
+  int u_stride;
+  int32_t* tok;          // [B]
+  uint2* part;           // [B, nblk, k] candidates (order key, index) when nblk > 1
+  int nblk;              // sample_blocks(V)
+};
+
 struct KvCopyArgs {
   const void* src[2 * kMaxLayers];
   void* dst[2 * kMaxLayers];
@@ -241,6 +268,7 @@ hipError_t launch_set_slot(const SlotTables& st, int slot, void* const* k, void*
                            int cap, int pos, int set_ptrs, hipStream_t s);
 hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s);
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
 hipError_t launch_record_token(const int32_t* tok, int32_t* out, int32_t* counter, hipStream_t s);
 // out[*counter * n + i] = src[i] for i < n (out may be null), then ++*counter; n <= 64
 hipError_t launch_record_tokens(const int32_t* src, int n, int32_t* out, int32_t* counter,

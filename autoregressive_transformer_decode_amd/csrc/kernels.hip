@@ -1001,6 +1001,265 @@ __global__ __launch_bounds__(64) void k_argmax_final(ArgmaxArgs a) {
 }
 
 
+// ------------------------------------------------------------------ top-k sampling
+// Unsigned order of the keys is the order of the values; -0 and +0 share a
+// key.  Key 0 (a NaN pattern) marks an empty element.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  if (v == 0.f) v = 0.f;
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The selected set: keys >= t (tie false), or keys > t plus the r keys equal
+// to t that come first in index order (tie true).
+struct TopkSel {
+  uint32_t t;
+  int r;
+  bool tie;
+};
+
+// Radix select of the kk-th largest key of the block (1 <= kk <= number of
+// non-empty keys), four bits per pass from the top.  The count of each digit
+// in a wave comes from ballots; lane b < 16 of every wave then sums bin b over
+// the waves from LDS (hist: two buffers of [16 waves][16 bins], alternating,
+// so one barrier per pass suffices) and every wave finds the digit itself.
+// Stops early once the chosen group holds exactly the keys still wanted.
+__device__ TopkSel block_select(const uint32_t (&key)[kSamplePerThread], int kk,
+                                uint32_t* hist) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t P = 0;
+  int r = kk;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int s = 28 - 4 * pass;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kSamplePerThread; ++j) {
+      const bool act = key[j] != 0u && (pass == 0 || (key[j] >> (s + 4)) == P);
+      if (__ballot(act) == 0) continue;
+      const uint32_t d = (key[j] >> s) & 15u;
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        const uint32_t c = (uint32_t)__popcll(__ballot(act && d == (uint32_t)b));
+        if (lane == b) mine += c;
+      }
+    }
+    uint32_t* h = hist + (pass & 1) * 256;
+    if (lane < 16) h[w * 16 + lane] = mine;
+    __syncthreads();
+    uint32_t tot = 0;
+    if (lane < 16)
+      for (int v = 0; v < nw; ++v) tot += h[v * 16 + lane];
+    uint32_t incl = tot;   // lane b < 16: keys of the group in bins >= b
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const uint32_t o = __shfl_down(incl, off, 64);
+      if (lane + off < 16) incl += o;
+    }
+    const uint32_t above = incl - tot;
+    const uint64_t hit = __ballot(lane < 16 && above < (uint32_t)r && (uint32_t)r <= incl);
+    const int d = hit ? __builtin_ctzll(hit) : 0;
+    const uint32_t td = __shfl(tot, d, 64);
+    r -= (int)__shfl(above, d, 64);
+    P = (P << 4) | (uint32_t)d;
+    if (td == (uint32_t)r) return TopkSel{P << s, r, false};
+  }
+  return TopkSel{P, r, true};
+}
+
+// Exclusive prefix sum of v over the block in thread order (sbuf: one word
+// per wave).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sbuf) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) sbuf[w] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int v2 = 0; v2 < w; ++v2) base += sbuf[v2];
+  return base + incl - v;
+}
+
+// Writes the selected (key, index) pairs to dst[0..kk) in index order
+// (thread t holds elements t*e .. t*e+e-1).
+__device__ void compact_selected(const uint32_t (&key)[kSamplePerThread],
+                                 const uint32_t (&idx)[kSamplePerThread], TopkSel sel, int kk,
+                                 uint2* dst, uint32_t* sbuf) {
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kSamplePerThread; ++j) {
+    if (key[j] == 0u) continue;
+    if (sel.tie ? key[j] > sel.t : key[j] >= sel.t) ++gt;
+    else if (sel.tie && key[j] == sel.t) ++eq;
+  }
+  const uint32_t base = block_excl_scan(gt | (eq << 16), sbuf);
+  uint32_t gb = base & 0xffffu, eb = base >> 16;
+  const uint32_t r = (uint32_t)sel.r;
+#pragma unroll
+  for (int j = 0; j < kSamplePerThread; ++j) {
+    if (key[j] == 0u) continue;
+    if (sel.tie ? key[j] > sel.t : key[j] >= sel.t) {
+      const uint32_t slot = gb + min(eb, r);
+      ++gb;
+      if (slot < (uint32_t)kk) dst[slot] = make_uint2(key[j], idx[j]);
+    } else if (sel.tie && key[j] == sel.t) {
+      if (eb < r && gb + eb < (uint32_t)kk) dst[gb + eb] = make_uint2(key[j], idx[j]);
+      ++eb;
+    }
+  }
+}
+
+// Keys of this thread's elements of row b, chunk [lo, lo + n): penalised
+// logits, indices implicit.
+__device__ __forceinline__ void load_logit_keys(const SampleArgs& a, int b, int lo, int n,
+                                                uint32_t (&key)[kSamplePerThread],
+                                                uint32_t (&idx)[kSamplePerThread]) {
+  const int e = (n + blockDim.x - 1) / blockDim.x;
+  const int i0 = threadIdx.x * e;
+  const float* z = a.z + (size_t)b * a.V + lo;
+  const uint32_t* seen = a.seen ? a.seen + (size_t)b * a.nwords : nullptr;
+#pragma unroll
+  for (int j = 0; j < kSamplePerThread; ++j) {
+    key[j] = 0u;
+    idx[j] = 0u;
+    const int i = i0 + j;
+    if (j < e && i < n) {
+      float v = z[i];
+      const int g = lo + i;
+      if (seen && ((seen[g >> 5] >> (g & 31)) & 1u)) v = v > 0.f ? v / a.penalty : v * a.penalty;
+      key[j] = order_key(v);
+      idx[j] = (uint32_t)g;
+    }
+  }
+}
+
+// Chunk blk of row b -> its top-k candidates in part (index order; slots past
+// the chunk's length hold empty keys).
+__global__ __launch_bounds__(kSampleThreads) void k_sample_part(SampleArgs a) {
+  __shared__ uint32_t hist[512];
+  __shared__ uint32_t sbuf[kSampleThreads / 64];
+  const int blk = blockIdx.x, b = blockIdx.y;
+  const int lo = blk * kSampleChunk, n = min(a.V - lo, kSampleChunk);
+  uint32_t key[kSamplePerThread], idx[kSamplePerThread];
+  load_logit_keys(a, b, lo, n, key, idx);
+  const int kk = min(a.k, n);
+  const TopkSel sel = block_select(key, kk, hist);
+  uint2* dst = a.part + ((size_t)b * a.nblk + blk) * a.k;
+  compact_selected(key, idx, sel, kk, dst, sbuf);
+  const int t = threadIdx.x;
+  if (t >= kk && t < a.k) dst[t] = make_uint2(0u, 0u);
+}
+
+// Row b: the top-k set (from the logits, or from the chunks' candidates),
+// sorted by key descending and index ascending, then the draw: weights
+// exp((v - v_max) / temperature) summed in that order, the shortest prefix
+// whose weight reaches top_p of the total, and the first candidate whose
+// running sum exceeds u times the prefix's weight.
+__global__ __launch_bounds__(kSampleThreads) void k_sample_final(SampleArgs a) {
+  __shared__ uint32_t hist[512];
+  __shared__ uint32_t sbuf[kSampleThreads / 64];
+  __shared__ uint2 cand[kTopKMax];
+  __shared__ uint2 sorted[kTopKMax];
+  const int b = blockIdx.x, t = threadIdx.x;
+  uint32_t key[kSamplePerThread], idx[kSamplePerThread];
+  if (a.nblk == 1) {
+    load_logit_keys(a, b, 0, a.V, key, idx);
+  } else {
+    const int n = a.nblk * a.k;
+    const int e = (n + blockDim.x - 1) / blockDim.x;
+    const uint2* src = a.part + (size_t)b * n;
+#pragma unroll
+    for (int j = 0; j < kSamplePerThread; ++j) {
+      const int i = t * e + j;
+      uint2 c = make_uint2(0u, 0u);
+      if (j < e && i < n) c = src[i];
+      key[j] = c.x;
+      idx[j] = c.y;
+    }
+  }
+  const int kk = a.k;
+  if (t < kTopKMax) cand[t] = make_uint2(0u, 0u);
+  const TopkSel sel = block_select(key, kk, hist);   // its barriers order the clear above
+  compact_selected(key, idx, sel, kk, cand, sbuf);
+  __syncthreads();
+  if (t < kk) {
+    const uint2 c = cand[t];
+    int rank = 0;
+    for (int j = 0; j < kk; ++j) {
+      const uint32_t kj = cand[j].x;
+      rank += (kj > c.x || (kj == c.x && j < t)) ? 1 : 0;
+    }
+    sorted[rank] = c;
+  }
+  __syncthreads();
+  if (t >= 64) return;
+  const int lane = t;
+  const float vmax = key_value(sorted[0].x);
+  float c[4];
+  float run = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = lane * 4 + q;
+    float p = 0.f;
+    if (i < kk && sorted[i].x != 0u) p = expf((key_value(sorted[i].x) - vmax) / a.temperature);
+    run += p;
+    c[q] = run;
+  }
+  float incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  const float excl = incl - run;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) c[q] += excl;
+  const float total = __shfl(incl, 63, 64);
+  int m = kk;
+  float mass = total;
+  if (a.top_p < 1.f) {
+    const float thr = a.top_p * total;
+    int qf = 4;
+    float cf = 0.f;
+#pragma unroll
+    for (int q = 3; q >= 0; --q)
+      if (lane * 4 + q < kk && c[q] >= thr) {
+        qf = q;
+        cf = c[q];
+      }
+    const uint64_t hb = __ballot(qf < 4);
+    if (hb) {
+      const int L = __builtin_ctzll(hb);
+      m = L * 4 + __shfl(qf, L, 64) + 1;
+      mass = __shfl(cf, L, 64);
+    }
+  }
+  const float u = a.u[(size_t)(a.u_row ? *a.u_row : 0) * a.u_stride + b];
+  const float target = u * mass;
+  int qd = 4;
+#pragma unroll
+  for (int q = 3; q >= 0; --q)
+    if (lane * 4 + q < m && c[q] > target) qd = q;
+  const uint64_t hd = __ballot(qd < 4);
+  int pos = m - 1;
+  if (hd) {
+    const int L = __builtin_ctzll(hd);
+    pos = L * 4 + __shfl(qd, L, 64);
+  }
+  if (lane == 0) {
+    const int tok = (int)sorted[pos].y;
+    a.tok[b] = tok;
+    if (a.seen) a.seen[(size_t)b * a.nwords + (tok >> 5)] |= 1u << (tok & 31);
+  }
+}
+
 // ------------------------------------------------------------------ MFMA path
 typedef __bf16 Bf16x8 __attribute__((ext_vector_type(8)));
 typedef float Floatx4 __attribute__((ext_vector_type(4)));
@@ -1169,7 +1428,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
 __global__ void k_record_token(const int32_t* tok, int32_t* out, int32_t* counter) {
   if (threadIdx.x == 0) {
     const int k = *counter;
-    out[k] = *tok;
+    if (out) out[k] = *tok;
     *counter = k + 1;
   }
 }
@@ -1359,6 +1618,13 @@ hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s) {
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_argmax_part, dim3(a.nblk, a.B), dim3(256), 0, s, a);
   if (a.nblk > 1) hipLaunchKernelGGL(k_argmax_final, dim3(a.B), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {
+  if (a.nblk > 1)
+    hipLaunchKernelGGL(k_sample_part, dim3(a.nblk, a.B), dim3(kSampleThreads), 0, s, a);
+  hipLaunchKernelGGL(k_sample_final, dim3(a.B), dim3(kSampleThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -177,14 +177,17 @@ class Decoder:
                  slot: int = 0, extra: Optional[torch.Tensor] = None, head: int = 0,
                  seen: Optional[torch.Tensor] = None, penalty: float = 1.0,
                  tokens_out: Optional[torch.Tensor] = None, y_out: Optional[torch.Tensor] = None,
-                 logits_out: Optional[torch.Tensor] = None):
-        """n_steps greedy steps on the device (graph-replayed step + argmax)."""
+                 logits_out: Optional[torch.Tensor] = None,
+                 sampling: Optional["Sampling"] = None):
+        """n_steps steps on the device (graph-replayed step + token choice):
+        greedy, or sampled with ``sampling`` (its uniforms: one per step)."""
         if logits_out is None:
             logits_out = torch.empty(self.shape.vocab, device="cuda", dtype=torch.float32)
         ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         B.decoder_generate(self.handle, slot, n_steps, tok_io.data_ptr(), len(table_ids),
                            table_ids, ptr(extra), head, ptr(seen), float(penalty),
-                           ptr(tokens_out), ptr(y_out), logits_out.data_ptr(), _stream())
+                           _c_sampling(sampling), ptr(tokens_out), ptr(y_out),
+                           logits_out.data_ptr(), _stream())
         return logits_out
 
     def time_stage(self, stage: int, slot0: int = 0, nrows: int = 1, reps: int = 8) -> float:
@@ -204,9 +207,12 @@ def talker_frames(tk: "Decoder", cp: "Decoder", n_frames: int, codes_io: torch.T
                   y_io: torch.Tensor, text: Optional[torch.Tensor], seen: torch.Tensor,
                   penalty: float, codes_out: Optional[torch.Tensor] = None,
                   tk_logits: Optional[torch.Tensor] = None, cp_logits: Optional[torch.Tensor] = None,
-                  tk_slot: int = 0, cp_slot: int = 0):
+                  tk_slot: int = 0, cp_slot: int = 0, tk_sampling: Optional["Sampling"] = None,
+                  cp_sampling: Optional["Sampling"] = None):
     """n_frames frames of the Talker / Code Predictor loop on the device
-    (talker_generate_frames); returns (tk_logits, cp_logits)."""
+    (talker_generate_frames); greedy, or sampled with tk_sampling (uniforms
+    [n_frames]) / cp_sampling (uniforms [n_frames, 15]); returns (tk_logits,
+    cp_logits)."""
     if tk_logits is None:
         tk_logits = torch.empty(tk.shape.vocab, device="cuda", dtype=torch.float32)
     if cp_logits is None:
@@ -214,8 +220,36 @@ def talker_frames(tk: "Decoder", cp: "Decoder", n_frames: int, codes_io: torch.T
     ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     B.talker_generate_frames(tk.handle, tk_slot, cp.handle, cp_slot, n_frames, codes_io.data_ptr(),
                              y_io.data_ptr(), ptr(text), seen.data_ptr(), float(penalty),
-                             ptr(codes_out), tk_logits.data_ptr(), cp_logits.data_ptr(), _stream())
+                             _c_sampling(tk_sampling), _c_sampling(cp_sampling), ptr(codes_out),
+                             tk_logits.data_ptr(), cp_logits.data_ptr(), _stream())
     return tk_logits, cp_logits
+
+
+@dataclasses.dataclass
+class Sampling:
+    """Sampled-choice settings (atd_sampling) with their device uniforms."""
+    top_k: int
+    temperature: float
+    top_p: float
+    uniforms: torch.Tensor    # float32 on the device, values in [0, 1)
+
+
+def _c_sampling(sp: Optional[Sampling]):
+    if sp is None:
+        return None
+    assert sp.uniforms.dtype == torch.float32 and sp.uniforms.is_cuda and sp.uniforms.is_contiguous()
+    return B.atd_sampling(int(sp.top_k), float(sp.temperature), float(sp.top_p),
+                          sp.uniforms.data_ptr())
+
+
+def sample_topk(logits: torch.Tensor, seen: Optional[torch.Tensor], penalty: float,
+                sampling: Sampling, tok_out: torch.Tensor):
+    """Sampled token per row of logits ([V] or [B, V]); row b draws
+    sampling.uniforms[b]."""
+    Bn, V = (1, logits.shape[0]) if logits.dim() == 1 else logits.shape
+    B.sample_topk(logits.data_ptr(), Bn, V, seen.data_ptr() if seen is not None else None,
+                  float(penalty), _c_sampling(sampling), tok_out.data_ptr(), _stream())
+    return tok_out
 
 
 def greedy_argmax(logits: torch.Tensor, seen: Optional[torch.Tensor], penalty: float,

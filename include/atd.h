@@ -137,6 +137,30 @@ typedef struct atd_weights {
   const int32_t* table_vocab;      /* host [n_tables]: V_g of each table     */
 } atd_weights;
 
+/* Settings of a sampled token choice (qwen3-tts-hip OPTIMIZATION_LOG: the
+ * GenerateOptions defaults top_k 50, top_p 1.0, temperature 0.9, and the
+ * device-sampler entry, top_k 1..256).  A draw over one row of logits:
+ *   1. the repetition penalty of greedy_argmax on the seen tokens;
+ *   2. the top_k largest penalised logits (equal values: lower index first);
+ *   3. weights exp((z - z_max) / temperature) over them, in descending order
+ *      of logit (equal values: lower index first), summed in that order;
+ *   4. the shortest prefix of that order whose weight reaches top_p times the
+ *      total (top_p = 1 keeps all top_k);
+ *   5. the first candidate whose running weight exceeds u times the prefix's
+ *      weight, u in [0, 1) read from `uniforms` (each call states which
+ *      entry a draw reads); u so close to 1 that no running weight exceeds
+ *      it in float32 takes the prefix's last candidate.
+ * top_k = 1 gives greedy_argmax's token.  The random numbers come in from
+ * the caller so that a replayed graph and any checker draw the same ones. */
+typedef struct atd_sampling {
+  int32_t top_k;          /* 1 .. ATD_TOPK_MAX, and <= V */
+  float temperature;      /* > 0, finite */
+  float top_p;            /* (0, 1] */
+  const float* uniforms;  /* device float32 values in [0, 1) */
+} atd_sampling;
+
+#define ATD_TOPK_MAX 256
+
 typedef struct atd_decoder atd_decoder;
 
 /* Create a decoder.  Validates cfg and w (all device pointers non-NULL where
@@ -153,7 +177,8 @@ int decoder_create(const atd_config* cfg, const atd_weights* w, atd_decoder** ou
 int decoder_destroy(atd_decoder* dec);
 
 /* Message of the last error on this decoder, or of the last failed
- * decoder_create / greedy_argmax call in this thread when dec is NULL.
+ * decoder_create / greedy_argmax / sample_topk call in this thread when dec
+ * is NULL.
  * Valid until the next failing call. */
 const char* decoder_last_error(const atd_decoder* dec);
 
@@ -224,26 +249,41 @@ int decoder_embed(atd_decoder* dec, int32_t B, const int32_t* tok, int32_t G,
 int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
                   float penalty, int32_t* tok_out, float* margin_out, void* stream);
 
+/* Sampled token per row (the draw of atd_sampling; qwen3-tts-hip log,
+ * device-sampler entry).  logits device [B, V] float32; seen and penalty as
+ * in greedy_argmax (the chosen token's bit is set); row b draws
+ * sampling->uniforms[b] (device [B]).  Writes tok_out (device int32 [B]).
+ * Rows of up to 8192 logits run in one workgroup each; longer rows first
+ * reduce each 8192-logit chunk to its top_k candidates, which needs
+ * ceil(V / 8192) * top_k <= 8192.  Uses the per-device scratch buffer of
+ * greedy_argmax.  Errors: INVALID_ARG, UNSUPPORTED (V too long for top_k),
+ * DEVICE. */
+int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* seen, float penalty,
+                const atd_sampling* sampling, int32_t* tok_out, void* stream);
 
-/* Greedy generation on the device: n_steps decode steps of `slot` with the
- * token fed back without a host round trip (the qwen3-tts-hip log measures
- * the host-side sampling and token copies as the remaining host cost).  Step
- * k embeds tok_io[0..G-1] from tables table_ids (host [G]) plus extra
+
+/* Generation on the device: n_steps decode steps of `slot` with the token
+ * fed back without a host round trip (the qwen3-tts-hip log measures the
+ * host-side sampling and token copies as the remaining host cost).  Step k
+ * embeds tok_io[0..G-1] from tables table_ids (host [G]) plus extra
  * (device [h] or NULL, the same every step), runs the stack and LM head
- * `head`, then the penalized argmax of greedy_argmax (seen: device
- * [ceil(V/32)] or NULL) writes the chosen token to tok_io[0] (the other
- * G-1 ids are held) and, when tokens_out is not NULL, to tokens_out[k]
- * (device int32 [n_steps]).  y_out (device [h] or NULL) and logits_out
+ * `head`, then chooses the token over `seen` (device [ceil(V/32)] or NULL)
+ * and `penalty`: the penalized argmax of greedy_argmax when sampling is
+ * NULL, else the draw of atd_sampling with u = sampling->uniforms[k]
+ * (device [n_steps]).  The token goes to tok_io[0] (the other G-1 ids are
+ * held) and, when tokens_out is not NULL, to tokens_out[k] (device int32
+ * [n_steps]).  y_out (device [h] or NULL) and logits_out
  * (device [V]) hold the last step's outputs.  The launches of one step are
  * captured once into a HIP graph and replayed; the graph is cached for this
- * argument set and bucket and rebuilt when either changes.  Refused with
- * ATD_ERR_KV_FULL when pos + n_steps exceeds the slot's capacity (grow the
- * bucket first; nothing runs).  Errors: INVALID_ARG, KV_FULL, CAPACITY,
- * DEVICE. */
+ * argument set (sampling settings and uniforms pointer included) and
+ * bucket and rebuilt when either changes.  Refused with ATD_ERR_KV_FULL when
+ * pos + n_steps exceeds the slot's capacity (grow the bucket first; nothing
+ * runs).  Errors: INVALID_ARG, KV_FULL, CAPACITY, UNSUPPORTED (a sampled
+ * vocabulary too long for top_k, see sample_topk), DEVICE. */
 int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* tok_io,
                      int32_t G, const int32_t* table_ids, const float* extra, int32_t head,
-                     uint32_t* seen, float penalty, int32_t* tokens_out, float* y_out,
-                     float* logits_out, void* stream);
+                     uint32_t* seen, float penalty, const atd_sampling* sampling,
+                     int32_t* tokens_out, float* y_out, float* logits_out, void* stream);
 
 /* The Talker's two-level frame loop on the device ("Qwen3-TTS ncnn port",
  * section "Talker: non-standard structure and two-level generation"; the
@@ -251,12 +291,16 @@ int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* t
  * frames, captured as HIP graphs on first use and replayed.  Frame f:
  *   - unless f = 0, one Talker step (decoder tk, slot tk_slot) fed
  *     sum_{g<16} table_g[c_g] + text[f] (the previous frame's codes), head 0:
- *     writes y_io and tk_logits; the penalised greedy argmax over `seen`
- *     (greedy_argmax rules) gives the frame's c0;
+ *     writes y_io and tk_logits; the choice over `seen` with `penalty`
+ *     gives the frame's c0: greedy (greedy_argmax rules) when tk_sampling
+ *     is NULL, else the draw of atd_sampling with
+ *     u = tk_sampling->uniforms[f];
  *   - the Code Predictor pass (decoder cp, slot cp_slot, restarted at
  *     position 0): a 2-row prefill of [y_io, table_0[c0]] with head 0 gives
- *     c1, then steps j = 1..14 fed table_j[c_j] with head j give c_{j+1}
- *     (greedy, no penalty);
+ *     c1, then steps j = 1..14 fed table_j[c_j] with head j give c_{j+1};
+ *     no penalty; greedy when cp_sampling is NULL, else the draw with
+ *     u = cp_sampling->uniforms[f * 15 + j] for c_{j+1} (the log's
+ *     "subtalker" settings);
  *   - the frame's 16 codes are appended to codes_out.
  * codes_io   [16] int32 device.  On entry codes_io[0] is frame 0's c0 (the code
  *            the caller chose from its prefill, already marked in `seen`).
@@ -267,6 +311,9 @@ int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* t
  * text       [n_frames, h] float32 device; row f is added to frame f's Talker
  *            input (row 0 unused; may be NULL when n_frames = 1).
  * seen       [ceil(V_tk / 32)] uint32 device, updated; penalty > 0.
+ * tk_sampling uniforms: device [n_frames] (entry 0 unused); cp_sampling
+ *            uniforms: device [n_frames, 15].  Both settings belong to the
+ *            captured graphs' key.
  * codes_out  [n_frames, 16] int32 device, or NULL.
  * tk_logits  [V_tk] and cp_logits [V_cp] float32 device: the last logits of
  *            each decoder.
@@ -276,10 +323,12 @@ int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* t
  * tk_slot has room for n_frames - 1 more rows (no bucket growth inside).
  * Afterwards tk_slot has advanced n_frames - 1 rows and cp_slot is at 16.
  * Each of the two decoders' scratch is used, so neither may run other work
- * concurrently.  Errors: INVALID_ARG, SHAPE, CAPACITY, KV_FULL, DEVICE. */
+ * concurrently.  Errors: INVALID_ARG, SHAPE, CAPACITY, KV_FULL, UNSUPPORTED,
+ * DEVICE. */
 int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_decoder* cp, int32_t cp_slot,
                            int32_t n_frames, int32_t* codes_io, float* y_io, const float* text,
-                           uint32_t* seen, float penalty, int32_t* codes_out, float* tk_logits,
+                           uint32_t* seen, float penalty, const atd_sampling* tk_sampling,
+                           const atd_sampling* cp_sampling, int32_t* codes_out, float* tk_logits,
                            float* cp_logits, void* stream);
 
 /* Stages of a decode step, for decoder_time_stage. */

@@ -336,6 +336,7 @@ def penalized_argmax(z: np.ndarray, seen: Optional[np.ndarray], rho: float):
 class SampleDraw(NamedTuple):
     """One sampled token and how far the draw sat from a different outcome.
 
+    pos:     the token's place in the kept candidates (0 = largest logit);
     gap:     distance of u from the nearest interior boundary of the
              cumulative distribution (inf with one candidate);
     cut_gap: distance of top_p from the nearest cumulative probability of the
@@ -343,9 +344,19 @@ class SampleDraw(NamedTuple):
     kmargin: k-th largest penalized logit minus the (k+1)-th (inf when k = V).
     """
     tok: int
+    pos: int
     gap: float
     cut_gap: float
     kmargin: float
+
+    def robustness(self, k: int) -> float:
+        """Smallest change (of a probability, or of a logit at the top-k cut)
+        that could alter the token: the gap and the top-p cut always; the
+        k-th / (k+1)-th margin only when the token is the k-th candidate (a
+        swap at the cut elsewhere moves the other boundaries by a fraction of
+        that candidate's small probability)."""
+        r = min(self.gap, self.cut_gap)
+        return min(r, self.kmargin) if self.pos == k - 1 else r
 
 
 def topk_candidates(zp: np.ndarray, k: int) -> np.ndarray:
@@ -403,7 +414,7 @@ def sample_topk(z: np.ndarray, seen: Optional[np.ndarray], rho: float, k: int,
         kmargin = math.inf
     if seen is not None:
         seen[tok] = True
-    return SampleDraw(tok, gap, cut_gap, kmargin)
+    return SampleDraw(tok, i, gap, cut_gap, kmargin)
 
 
 # --------------------------------------------------------------------------
@@ -454,14 +465,14 @@ def choose(z: np.ndarray, seen: Optional[np.ndarray], rho: float, sampling=None,
            i: int = 0) -> Tuple[int, float]:
     """Greedy (sampling None) or sampled choice of one token.  ``sampling`` =
     (k, temperature, top_p, uniforms) and the draw uses uniforms[i].  Returns
-    (token, robustness): the greedy top-2 margin, or for a draw the smallest
-    of its gap, cut_gap and kmargin (a decision that a small change of the
-    logits cannot flip has all three well above zero)."""
+    (token, robustness): the greedy top-2 margin, or SampleDraw.robustness
+    of the draw (a decision that a small change of the logits cannot flip has
+    it well above zero)."""
     if sampling is None:
         return penalized_argmax(z, seen, rho)
     k, t, top_p, u = sampling
     d = sample_topk(z, seen, rho, k, t, top_p, float(u[i]))
-    return d.tok, min(d.gap, d.cut_gap, d.kmargin)
+    return d.tok, d.robustness(k)
 
 
 def code_predictor_frame(cp: Model, y_talker: np.ndarray, c0: int,

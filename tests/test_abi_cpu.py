@@ -227,8 +227,8 @@ def test_dry_run_talker_frames():
         kv = lambda base: ([base + 0x1000 * i for i in range(L)], [base + 0x80000 + 0x1000 * i for i in range(L)])  # noqa: E731
         B.kv_bucket_grow(tk, 0, *kv(0x900000), 40, 0)
         B.decoder_prefill(tk, 0, 0x5000, 8, 0, None, 0x6000, 0)
-        args = lambda n, cpd=cp: (tk, 0, cpd, 0, n, 0x7000, 0x8000, 0x9000, 0xA000, 1.05, None,  # noqa: E731
-                                  0xB000, 0xC000, 0)
+        args = lambda n, cpd=cp, ts=None, cs=None: (  # noqa: E731
+            tk, 0, cpd, 0, n, 0x7000, 0x8000, 0x9000, 0xA000, 1.05, ts, cs, None, 0xB000, 0xC000, 0)
         with pytest.raises(B.AtdError) as ei:          # Code Predictor slot not attached
             B.talker_generate_frames(*args(4))
         assert "Code Predictor slot 0" in str(ei.value)
@@ -252,6 +252,72 @@ def test_dry_run_talker_frames():
         assert B.decoder_get_position(tk, 0) == (12, 40)
         with pytest.raises(B.AtdError):
             B.talker_generate_frames(*args(0))
+        ok = B.atd_sampling(50, 0.9, 1.0, 0x10000)
+        B.talker_generate_frames(*args(3, cp, ok, ok))  # sampled: same positions
+        assert B.decoder_get_position(tk, 0) == (14, 40)
+        for bad in (B.atd_sampling(101, 0.9, 1.0, 0x10000),      # top_k > V = 100
+                    B.atd_sampling(50, 0.9, 1.0, None)):         # no uniforms
+            with pytest.raises(B.AtdError) as ei:
+                B.talker_generate_frames(*args(2, cp, None, bad))
+            assert ei.value.code == B.ATD_ERR_INVALID_ARG
+        assert B.decoder_get_position(tk, 0) == (14, 40)
     finally:
         for h in (tk, cp, small):
             B.decoder_destroy(h)
+
+
+def test_sample_topk_argument_checks():
+    """sample_topk and the sampling settings: every refusal happens in host
+    code before any device call."""
+    ok = dict(top_k=50, temperature=0.9, top_p=1.0, uniforms=0x300)
+    cases = [
+        (dict(ok, top_k=0), "top_k", B.ATD_ERR_INVALID_ARG),
+        (dict(ok, top_k=257), "top_k", B.ATD_ERR_INVALID_ARG),
+        (dict(ok, top_k=1001), "top_k", B.ATD_ERR_INVALID_ARG),      # > V
+        (dict(ok, temperature=0.0), "temperature", B.ATD_ERR_INVALID_ARG),
+        (dict(ok, temperature=float("inf")), "temperature", B.ATD_ERR_INVALID_ARG),
+        (dict(ok, temperature=float("nan")), "temperature", B.ATD_ERR_INVALID_ARG),
+        (dict(ok, top_p=0.0), "top_p", B.ATD_ERR_INVALID_ARG),
+        (dict(ok, top_p=1.5), "top_p", B.ATD_ERR_INVALID_ARG),
+        (dict(ok, top_p=float("nan")), "top_p", B.ATD_ERR_INVALID_ARG),
+        (dict(ok, uniforms=None), "uniforms", B.ATD_ERR_INVALID_ARG),
+    ]
+    for kw, needle, code in cases:
+        with pytest.raises(B.AtdError) as ei:
+            B.sample_topk(0x100, 2, 1000, None, 1.0, B.atd_sampling(**kw), 0x200, 0)
+        assert ei.value.code == code and needle in str(ei.value), (kw, str(ei.value))
+    # 300000 logits in 37 chunks keep 37 * 256 candidates: more than one
+    # workgroup selects from
+    with pytest.raises(B.AtdError) as ei:
+        B.sample_topk(0x100, 1, 300000, None, 1.0, B.atd_sampling(**dict(ok, top_k=256)),
+                      0x200, 0)
+    assert ei.value.code == B.ATD_ERR_UNSUPPORTED
+    with pytest.raises(B.AtdError) as ei:
+        B.sample_topk(0x100, 1, 1000, None, 0.0, B.atd_sampling(**ok), 0x200, 0)
+    assert "penalty" in str(ei.value)
+    with pytest.raises(B.AtdError):
+        B.sample_topk(None, 1, 1000, None, 1.0, B.atd_sampling(**ok), 0x200, 0)
+
+
+def test_dry_run_generate_sampling():
+    """decoder_generate takes sampling settings (checked against the vocab)
+    and advances the position like the greedy form."""
+    h, fw = _create(_cfg())
+    try:
+        L = 2
+        B.kv_bucket_grow(h, 0, [0x1000 * (i + 1) for i in range(L)],
+                         [0x80000 + 0x1000 * i for i in range(L)], 32, 0)
+        B.decoder_prefill(h, 0, 0x5000, 4, 0, None, 0x6000, 0)
+        sp = B.atd_sampling(50, 0.9, 1.0, 0x7000)
+        B.decoder_generate(h, 0, 5, 0x8000, 1, [0], None, 0, None, 1.0, sp, None, None,
+                           0x6000, 0)
+        assert B.decoder_get_position(h, 0) == (9, 32)
+        with pytest.raises(B.AtdError) as ei:
+            B.decoder_generate(h, 0, 5, 0x8000, 1, [0], None, 0, None, 1.0,
+                               B.atd_sampling(101, 0.9, 1.0, 0x7000), None, None, 0x6000, 0)
+        assert ei.value.code == B.ATD_ERR_INVALID_ARG and "top_k" in str(ei.value)
+        B.decoder_generate(h, 0, 5, 0x8000, 1, [0], None, 0, None, 1.0, None, None, None,
+                           0x6000, 0)
+        assert B.decoder_get_position(h, 0) == (14, 32)
+    finally:
+        B.decoder_destroy(h)

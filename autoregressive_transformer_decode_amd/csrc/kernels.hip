@@ -53,6 +53,25 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Inclusive prefix sum over the wave by DPP: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then the last lane of rows 0 / 2 added into rows 1 / 3
+// (row_bcast:15) and lane 31 into rows 2 and 3 (row_bcast:31).  Lanes
+// without a source (or masked off) add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  v += dpp_rows<0x111, 0xF>(v);
+  v += dpp_rows<0x112, 0xF>(v);
+  v += dpp_rows<0x114, 0xF>(v);
+  v += dpp_rows<0x118, 0xF>(v);
+  v += dpp_rows<0x142, 0xA>(v);
+  v += dpp_rows<0x143, 0xC>(v);
+  return v;
+}
+
 // Wave-wide sum, identical in every lane: rows of 16 by DPP, then the four
 // row sums read out and added in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
@@ -1070,21 +1089,32 @@ __device__ TopkSel block_select(const uint32_t (&key)[kSamplePerThread], int kk,
   return TopkSel{P, r, true};
 }
 
-// Exclusive prefix sum of v over the block in thread order (sbuf: one word
-// per wave).
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sbuf) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t incl = v;
+// Exclusive prefix sum over the block in thread order of small values whose
+// set bits all lie in MASK, and the block's total: one ballot per bit gives
+// the wave's prefix (mbcnt) and total; sbuf holds one word per wave.
+template <uint32_t MASK>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sbuf,
+                                                    uint32_t* total = nullptr) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t pre = 0, wtot = 0;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
+  for (int bit = 0; bit < 32; ++bit) {
+    if (!((MASK >> bit) & 1u)) continue;
+    const uint64_t m = __ballot((v >> bit) & 1u);
+    pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))
+           << bit;
+    wtot += (uint32_t)__popcll(m) << bit;
   }
-  if (lane == 63) sbuf[w] = incl;
+  if (lane == 0) sbuf[w] = wtot;
   __syncthreads();
-  uint32_t base = 0;
-  for (int v2 = 0; v2 < w; ++v2) base += sbuf[v2];
-  return base + incl - v;
+  uint32_t base = 0, tot = 0;
+  for (int v2 = 0; v2 < nw; ++v2) {
+    const uint32_t x = sbuf[v2];
+    base += v2 < w ? x : 0u;
+    tot += x;
+  }
+  if (total) *total = tot;
+  return base + pre;
 }
 
 // Writes the selected (key, index) pairs to dst[0..kk) in index order
@@ -1099,7 +1129,7 @@ __device__ void compact_selected(const uint32_t (&key)[kSamplePerThread],
     if (sel.tie ? key[j] > sel.t : key[j] >= sel.t) ++gt;
     else if (sel.tie && key[j] == sel.t) ++eq;
   }
-  const uint32_t base = block_excl_scan(gt | (eq << 16), sbuf);
+  const uint32_t base = block_excl_scan<0x000F000Fu>(gt | (eq << 16), sbuf);
   uint32_t gb = base & 0xffffu, eb = base >> 16;
   const uint32_t r = (uint32_t)sel.r;
 #pragma unroll
@@ -1157,17 +1187,62 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample_part(SampleArgs a) {
   if (t >= kk && t < a.k) dst[t] = make_uint2(0u, 0u);
 }
 
+// Rank of (value `mine`, position p) in list[0..n): the number of entries
+// with a larger value, or an equal value at an earlier position -- one
+// unsigned compare of (value << 32 | ~position) pairs.  Called by whole waves
+// (lanes past the list pass anything); each wave walks the list 64 values at
+// a time, broadcasting one value per step from a register (an immediate lane
+// index).  Entries past the list read as value 0 at positions after p, which
+// never count.
+template <typename Get>
+__device__ __forceinline__ int list_rank(Get get, int n, uint32_t mine, int p) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t me = ((uint64_t)mine << 32) | (uint32_t)~p;
+  int rank = 0;
+  for (int base = 0; base < n; base += 64) {
+    const uint32_t kl = base + lane < n ? get(base + lane) : 0u;
+#pragma unroll
+    for (int jj = 0; jj < 64; ++jj) {
+      const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)kl, jj) << 32) |
+                          (uint32_t)~(base + jj);
+      rank += kj > me ? 1 : 0;
+    }
+  }
+  return rank;
+}
+
+// Candidates cand[0..n) (index order) -> sorted[rank] for the ranks below kk.
+__device__ __forceinline__ void rank_candidates(const uint2* cand, int n, int kk, uint2* sorted) {
+  const int t = threadIdx.x, lane = t & 63;
+  if (t - lane >= n) return;   // the whole wave is past the list
+  const uint2 me = t < n ? cand[t] : make_uint2(0u, 0u);
+  const int rank = list_rank([&](int j) { return cand[j].x; }, n, me.x, t);
+  if (t < n && rank < kk) sorted[rank] = me;
+}
+
+// Prefiltered candidates ranked directly (above this the radix select runs)
+constexpr int kSampleCandMax = 512;
+
 // Row b: the top-k set (from the logits, or from the chunks' candidates),
 // sorted by key descending and index ascending, then the draw: weights
 // exp((v - v_max) / temperature) summed in that order, the shortest prefix
 // whose weight reaches top_p of the total, and the first candidate whose
 // running sum exceeds u times the prefix's weight.
+//
+// The set: groups of g consecutive threads (g the largest power of two <= 64
+// leaving at least 2k groups) each hold a maximum; the k-th largest of these
+// maxima (k distinct keys) is at most the k-th largest key, so the keys at
+// or above it contain the set.  When they are few they are ranked directly;
+// otherwise (ties, or k close to the number of groups) the radix select
+// finds the set.
 __global__ __launch_bounds__(kSampleThreads) void k_sample_final(SampleArgs a) {
   __shared__ uint32_t hist[512];
   __shared__ uint32_t sbuf[kSampleThreads / 64];
-  __shared__ uint2 cand[kTopKMax];
+  __shared__ uint32_t gmax[kSampleThreads / 2];
+  __shared__ uint32_t bound;
+  __shared__ uint2 cand[kSampleCandMax];
   __shared__ uint2 sorted[kTopKMax];
-  const int b = blockIdx.x, t = threadIdx.x;
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63;
   uint32_t key[kSamplePerThread], idx[kSamplePerThread];
   if (a.nblk == 1) {
     load_logit_keys(a, b, 0, a.V, key, idx);
@@ -1185,22 +1260,45 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample_final(SampleArgs a) {
     }
   }
   const int kk = a.k;
-  if (t < kTopKMax) cand[t] = make_uint2(0u, 0u);
-  const TopkSel sel = block_select(key, kk, hist);   // its barriers order the clear above
-  compact_selected(key, idx, sel, kk, cand, sbuf);
+
+  // lower bound of the k-th largest key: the k-th largest group maximum
+  int g = 64;
+  while (g > 2 && (int)blockDim.x / g < 2 * kk) g >>= 1;
+  const int G = blockDim.x / g;
+  uint32_t m = 0u;
+#pragma unroll
+  for (int j = 0; j < kSamplePerThread; ++j) m = max(m, key[j]);
+  for (int off = 1; off < g; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((lane & (g - 1)) == 0) gmax[t / g] = m;
   __syncthreads();
-  if (t < kk) {
-    const uint2 c = cand[t];
-    int rank = 0;
-    for (int j = 0; j < kk; ++j) {
-      const uint32_t kj = cand[j].x;
-      rank += (kj > c.x || (kj == c.x && j < t)) ? 1 : 0;
-    }
-    sorted[rank] = c;
+  if (t - lane < G) {
+    const uint32_t v = t < G ? gmax[t] : 0u;
+    const int r = list_rank([&](int j) { return gmax[j]; }, G, v, t);
+    if (t < G && r == kk - 1) bound = v;
+  }
+  __syncthreads();
+  const uint32_t L = bound;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kSamplePerThread; ++j) mine += (key[j] != 0u && key[j] >= L) ? 1u : 0u;
+  uint32_t nc = 0;
+  const uint32_t base = block_excl_scan<0xFu>(mine, sbuf, &nc);
+  if (nc <= (uint32_t)kSampleCandMax) {
+    uint32_t slot = base;
+#pragma unroll
+    for (int j = 0; j < kSamplePerThread; ++j)
+      if (key[j] != 0u && key[j] >= L) cand[slot++] = make_uint2(key[j], idx[j]);
+    __syncthreads();
+    rank_candidates(cand, (int)nc, kk, sorted);
+  } else {
+    if (t < kTopKMax) cand[t] = make_uint2(0u, 0u);
+    const TopkSel sel = block_select(key, kk, hist);   // its barriers order the clear above
+    compact_selected(key, idx, sel, kk, cand, sbuf);
+    __syncthreads();
+    rank_candidates(cand, kk, kk, sorted);
   }
   __syncthreads();
   if (t >= 64) return;
-  const int lane = t;
   const float vmax = key_value(sorted[0].x);
   float c[4];
   float run = 0.f;
@@ -1212,17 +1310,12 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample_final(SampleArgs a) {
     run += p;
     c[q] = run;
   }
-  float incl = run;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
+  const float incl = wave_incl_scan(run);
   const float excl = incl - run;
 #pragma unroll
   for (int q = 0; q < 4; ++q) c[q] += excl;
-  const float total = __shfl(incl, 63, 64);
-  int m = kk;
+  const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+  int mcut = kk;
   float mass = total;
   if (a.top_p < 1.f) {
     const float thr = a.top_p * total;
@@ -1236,9 +1329,9 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample_final(SampleArgs a) {
       }
     const uint64_t hb = __ballot(qf < 4);
     if (hb) {
-      const int L = __builtin_ctzll(hb);
-      m = L * 4 + __shfl(qf, L, 64) + 1;
-      mass = __shfl(cf, L, 64);
+      const int Lq = __builtin_ctzll(hb);
+      mcut = Lq * 4 + __builtin_amdgcn_readlane(qf, Lq) + 1;
+      mass = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cf), Lq));
     }
   }
   const float u = a.u[(size_t)(a.u_row ? *a.u_row : 0) * a.u_stride + b];
@@ -1246,12 +1339,12 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample_final(SampleArgs a) {
   int qd = 4;
 #pragma unroll
   for (int q = 3; q >= 0; --q)
-    if (lane * 4 + q < m && c[q] > target) qd = q;
+    if (lane * 4 + q < mcut && c[q] > target) qd = q;
   const uint64_t hd = __ballot(qd < 4);
-  int pos = m - 1;
+  int pos = mcut - 1;
   if (hd) {
-    const int L = __builtin_ctzll(hd);
-    pos = L * 4 + __shfl(qd, L, 64);
+    const int Lq = __builtin_ctzll(hd);
+    pos = Lq * 4 + __builtin_amdgcn_readlane(qd, Lq);
   }
   if (lane == 0) {
     const int tok = (int)sorted[pos].y;

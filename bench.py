@@ -21,6 +21,11 @@ Also measured in the same run:
                 rocprofv3 counter summary when it matches the kernel source.
   cpu_baseline  the CPU oracle on this host's cores, on a bounded sample of
                 the same workload (decode steps after the same prefill).
+  sampled       the same K steps with the Qwen TTS sampling defaults (top-k
+                50, temperature 0.9, top-p 1, repetition penalty 1.05) drawn
+                on the device by sample_topk inside the step graph.
+  token_choice_us  microseconds per call of greedy_argmax and sample_topk on
+                one row of the vocabulary.
 """
 
 from __future__ import annotations
@@ -174,15 +179,23 @@ def bench_lm(args, wl):
     y = torch.empty(s.hidden, device="cuda")
     tok = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-    def schedule(n):
-        """Rewind to the first bucket, prefill (untimed), then n greedy steps
-        from the step graph, growing the bucket where the context reaches it;
-        returns the seconds of the decode loop."""
+    seen = torch.zeros(dv.seen_words(s.vocab), dtype=torch.int32, device="cuda")
+    uni = torch.from_numpy(inputs.uniforms(0, 0, P0 + max(K, W) + 1)).cuda()
+
+    def schedule(n, sampled=False):
+        """Rewind to the first bucket, prefill (untimed), then n steps from the
+        step graph (greedy, or the sampling defaults with the penalty),
+        growing the bucket where the context reaches it; returns the seconds
+        of the decode loop."""
         dec.set_position(0, 0)
         if dec.position(0)[1] != caps[0]:
             dec.grow(0, caps[0], kv=buckets[0])
         dec.prefill(X0_d, logits_out=z)
-        dv.greedy_argmax(z, None, 1.0, tok)
+        seen.zero_()
+        if sampled:
+            dv.sample_topk(z, seen, SAMPLING_PENALTY, dv.Sampling(*SAMPLING, uni[0:1]), tok)
+        else:
+            dv.greedy_argmax(z, None, 1.0, tok)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         done, b = 0, 0
@@ -193,7 +206,11 @@ def bench_lm(args, wl):
                 dec.grow(0, caps[b], kv=buckets[b])
                 continue
             k = min(n - done, cap - pos)
-            dec.generate(k, tok, y_out=y, logits_out=z)
+            if sampled:
+                dec.generate(k, tok, y_out=y, logits_out=z, seen=seen, penalty=SAMPLING_PENALTY,
+                             sampling=dv.Sampling(*SAMPLING, uni[1 + done:1 + done + k]))
+            else:
+                dec.generate(k, tok, y_out=y, logits_out=z)
             done += k
         torch.cuda.synchronize()
         return time.perf_counter() - t0
@@ -204,6 +221,10 @@ def bench_lm(args, wl):
         schedule(W)
     dt = schedule(K)
     log(f"timed {K} steps: {dt * 1e3:.1f} ms (buckets {caps})")
+    # the same run with the sampling defaults (graphs captured by a warmup)
+    schedule(K if len(caps) > 1 else min(W, K), sampled=True)
+    dt_s = schedule(K, sampled=True)
+    log(f"timed {K} sampled steps: {dt_s * 1e3:.1f} ms")
 
     # roofline: the dominant kernel's launches, every layer's weights in turn
     # as in a step, timed with HIP events on this stream
@@ -233,6 +254,10 @@ def bench_lm(args, wl):
                       launches_timed=launches),
         step_hbm=dict(algorithmic_bytes=step_bytes, achieved_gbs=step_bytes / (ms_step / 1e3) / 1e9,
                       frac=step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS),
+        sampled=dict(value=K / dt_s, unit="tokens/s", ms_per_step=dt_s * 1e3 / K,
+                     settings=dict(zip(("top_k", "temperature", "top_p"), SAMPLING),
+                                   penalty=SAMPLING_PENALTY)),
+        token_choice_us=time_choice(s.vocab),
     )
     dec.close()
     # the batched workload is the same stack (same weights) with a bf16 cache
@@ -350,6 +375,49 @@ def bench_batched(args, wl, dm=None, steps=None, warmup=None):
     )
 
 
+# the Qwen TTS generation defaults: top-k 50, temperature 0.9, top-p 1.0,
+# repetition penalty 1.05
+SAMPLING = (50, 0.9, 1.0)
+SAMPLING_PENALTY = 1.05
+
+
+def time_choice(V, reps=100):
+    """Microseconds per call of the token-choice kernels on one row of V
+    logits: `reps` calls captured in one graph, replayed between two events
+    (the launch cost inside a replayed step, not the host's): greedy_argmax,
+    and sample_topk with the sampling defaults."""
+    import torch
+    from autoregressive_transformer_decode_amd import device as dv
+    from autoregressive_transformer_decode_amd import inputs
+    z = torch.from_numpy(inputs.normal(0, 9, 0, (V,), scale=3.0)).cuda()
+    seen = torch.zeros(dv.seen_words(V), dtype=torch.int32, device="cuda")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    uni = torch.from_numpy(inputs.uniforms(0, 9, reps)).cuda()
+    out = {}
+    for name in ("greedy_argmax", "sample_topk"):
+        def call(i):
+            if name == "greedy_argmax":
+                dv.greedy_argmax(z, seen, SAMPLING_PENALTY, tok)
+            else:
+                dv.sample_topk(z, seen, SAMPLING_PENALTY, dv.Sampling(*SAMPLING, uni[i:i + 1]), tok)
+        call(0)   # first call sets up the library's scratch outside the capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(reps):
+                call(i)
+        graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e3 / reps
+        del graph
+    out["vocab"] = V
+    return out
+
+
 def bench_frames(args, wl):
     """The Talker frame loop (0.6B shape): 64-row prefill, then frames of one
     Talker step and one Code Predictor pass (2-row prefill + 14 steps),
@@ -381,19 +449,34 @@ def bench_frames(args, wl):
     seen = torch.zeros(dv.seen_words(s.vocab), dtype=torch.int32, device="cuda")
     out = torch.zeros(n, 16, dtype=torch.int32, device="cuda")
 
-    def start():
+    ut = torch.from_numpy(inputs.uniforms(0, 1, n)).cuda()
+    uc = torch.from_numpy(inputs.uniforms(0, 2, (n, 15))).cuda()
+
+    def run(frames, sampled):
+        """Prefill and the first code (untimed), then `frames` frames; returns
+        the seconds of the frame loop."""
         seen.zero_()
         tdec.prefill(X0, y_out=y, logits_out=zt)
-        dv.greedy_argmax(zt, seen, wl.penalty, codes[0:1])
+        ts = cs = None
+        if sampled:
+            ts, cs = dv.Sampling(*SAMPLING, ut), dv.Sampling(*SAMPLING, uc)
+            dv.sample_topk(zt, seen, wl.penalty, dv.Sampling(*SAMPLING, ut[0:1]), codes[0:1])
+        else:
+            dv.greedy_argmax(zt, seen, wl.penalty, codes[0:1])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dv.talker_frames(tdec, cdec, frames, codes, y, text, seen, wl.penalty, codes_out=out,
+                         tk_sampling=ts, cp_sampling=cs)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
 
-    start()   # warm-up run of the loop (captures the frame graphs)
-    dv.talker_frames(tdec, cdec, min(n, 4), codes, y, text, seen, wl.penalty, codes_out=out)
-    start()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    dv.talker_frames(tdec, cdec, n, codes, y, text, seen, wl.penalty, codes_out=out)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    run(min(n, 4), False)   # warm-up runs of the loop (capture the frame graphs)
+    run(min(n, 4), True)
+    # the two legs alternate, twice; each reports its faster run
+    dt, dt_s = float("inf"), float("inf")
+    for _ in range(2):
+        dt = min(dt, run(n, False))
+        dt_s = min(dt_s, run(n, True))
     tdec.close()
     cdec.close()
     fps = n / dt
@@ -411,10 +494,17 @@ def bench_frames(args, wl):
         higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload=wl.name, frames=n, prefill=wl.prefill, penalty=wl.penalty,
                     talker_layers=s.n_layers, cp_layers=c.n_layers, hidden=s.hidden,
-                    step="graph-replayed frames (talker_generate_frames)"),
+                    step="graph-replayed frames (talker_generate_frames)",
+                    timing="greedy and sampled runs of all frames alternate twice; each "
+                           "leg reports its faster run"),
         codes_per_s=16 * fps, rtf_equivalent=(1.0 / fps) / 0.08,
         frame_hbm=dict(algorithmic_bytes=frame_b, achieved_gbs=frame_b * fps / 1e9,
                        frac=frame_b * fps / 1e9 / HBM_PEAK_GBS),
+        sampled=dict(value=n / dt_s, unit="frames/s", ms_per_frame=dt_s * 1e3 / n,
+                     rtf_equivalent=(dt_s / n) / 0.08,
+                     settings=dict(zip(("top_k", "temperature", "top_p"), SAMPLING),
+                                   penalty=wl.penalty, code_predictor="same, no penalty")),
+        token_choice_us=dict(talker=time_choice(s.vocab), code_predictor=time_choice(c.vocab)),
         roofline=None, cpu_baseline=None)
 
 

@@ -14,6 +14,7 @@ import numpy as np
 from autoregressive_transformer_decode_amd import inputs
 from oracle import brute
 from oracle import decoder as od
+from oracle import quant as oq
 from tests._models import tiny_model
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -460,6 +461,77 @@ def check_sampling_frequencies():
         assert set(hits) <= set(exp), (k, set(hits) - set(exp))
         for tok, p in exp.items():
             assert abs(hits.get(tok, 0) / n - p) <= 1.0 / n + 1e-6, (k, tok, hits.get(tok, 0) / n, p)
+
+
+# ---------------------------------------------------------------- block quantization
+
+def check_quant_closed_form():
+    """d = 2^-7 makes every value exact: amax 127 d gives codes 127; 2.5 d
+    rounds away from zero to 3 (and -2.5 d to -3); a zero block has scale 0
+    and codes 0; the 4-bit form packs weight 2i low and 2i+1 high."""
+    d = 2.0 ** -7
+    w = np.zeros((2, 32), np.float32)
+    w[0, 0] = 127 * d
+    w[0, 1] = 2.5 * d
+    w[0, 2] = -2.5 * d
+    w[0, 3] = -1.49 * d
+    codes, scales = oq.quantize(w, oq.Q8)
+    assert list(codes[0, :4]) == [127, 3, -3, -1]
+    assert scales[0, 0] == np.float16(d).view(np.uint16) and scales[1, 0] == 0
+    assert not codes[1].any()
+    # a scale that fp16 cannot hold: 0.1 / 127 is stored rounded, and the
+    # block's largest weight reads back as that rounded scale times 127
+    w2 = np.zeros((1, 32), np.float32)
+    w2[0, 5] = 0.1
+    c2, s2 = oq.quantize(w2, oq.Q8)
+    d16 = float(np.float16(np.float32(0.1) / np.float32(127)))
+    assert c2[0, 5] == 127 and d16 != float(np.float32(0.1) / np.float32(127))
+    assert oq.dequantize(c2, s2, oq.Q8, 32)[0, 5] == d16 * 127
+    # 4-bit: amax 7 d -> d; 2.5 d -> 3 -> nibble 11; -2.5 d -> -3 -> nibble 5
+    w4 = np.zeros((1, 32), np.float32)
+    w4[0, 0], w4[0, 1], w4[0, 2], w4[0, 3] = 7 * d, 2.5 * d, -2.5 * d, -7 * d
+    c4, s4 = oq.quantize(w4, oq.Q4)
+    assert c4.shape == (1, 16)
+    assert c4[0, 0] == (15 | (11 << 4)) and c4[0, 1] == (5 | (1 << 4)), (c4[0, 0], c4[0, 1])
+    assert (c4[0, 2:] == (8 | (8 << 4))).all()
+    assert s4[0, 0] == np.float16(d).view(np.uint16)
+    _close(oq.dequantize(c4, s4, oq.Q4, 32)[0, :4], [7 * d, 3 * d, -3 * d, -7 * d], 0)
+
+
+def check_quant_error_bound():
+    """Every read-back weight lies within half a step of the input, plus the
+    fp16 rounding of the scale over the largest code; the largest |w| of a
+    block reads back as +-QMAX steps; read-back is idempotent."""
+    w = inputs.normal(8, 9, 3, (16, 256), scale=0.02)
+    w[3, :32] *= 1e-3           # a block with a small (fp16-subnormal-free) scale
+    for fmt in (oq.Q8, oq.Q4):
+        codes, scales = oq.quantize(w, fmt)
+        back = oq.dequantize(codes, scales, fmt, 256)
+        d = np.repeat(oq.block_scales(w, fmt).astype(np.float64), 32, axis=1)
+        d16 = np.repeat(scales.view(np.float16).astype(np.float64), 32, axis=1)
+        bound = d / 2 * (1 + 1e-6) + np.abs(d16 - d) * oq.QMAX[fmt]
+        assert (np.abs(back - w) <= bound + 1e-12).all(), fmt
+        q = oq.codes_of(codes, fmt, 256).reshape(16, 8, 32)
+        assert (np.abs(q).max(axis=2) == oq.QMAX[fmt]).all(), fmt
+        c2, s2 = oq.quantize(back.astype(np.float32), fmt)
+        assert np.array_equal(oq.dequantize(c2, s2, fmt, 256), back), fmt
+
+
+def check_quant_bytes_golden():
+    """Byte accounting of the formats against the RKNN page's table: the
+    0.6B Talker matmuls in the 4-bit form (18 bytes per 32, Q4_K's rate) with
+    the head at Q8_0 move 251.0 MB per token.  This count gives 251.07: the
+    page's figure is taken to within 0.1 MB (its Q8_0 row, 471.3, matches
+    this count to the printed digit)."""
+    from autoregressive_transformer_decode_amd import inputs as inp
+    g = {k: float(v) for k, v in read_golden("talker_q8_bytes.txt")}
+    s = inp.TALKER06
+    assert oq.bytes_per_weight(oq.Q8) == g["q8_0_bytes_per_block"] / g["q8_0_weights_per_block"]
+    assert oq.bytes_per_weight(oq.Q4) == g["q4_k_bytes_per_superblock"] / g["q4_k_weights_per_superblock"]
+    head = s.vocab * s.hidden
+    body = s.weight_elems(with_head=True) - head
+    mb = (body * oq.bytes_per_weight(oq.Q4) + head * oq.bytes_per_weight(oq.Q8)) / 1e6
+    assert abs(mb - g["q4_k_mb_per_token"]) <= 0.1, mb
 
 
 # ---------------------------------------------------------------- golden

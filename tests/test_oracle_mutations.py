@@ -6,10 +6,12 @@ import numpy as np
 import pytest
 
 from oracle import decoder as od
+from oracle import quant as oq
 from tests import pins
 from tests.test_oracle_pins import PINS
 
 _orig = {k: getattr(od, k) for k in dir(od) if not k.startswith("__")}
+_orig_q = {k: getattr(oq, k) for k in dir(oq) if not k.startswith("__")}
 
 
 def _all_pins():
@@ -166,6 +168,59 @@ def _topk_high_index_ties(zp, k):
 
 def _topk_one_more(zp, k):
     return _orig["topk_candidates"](zp, k + 1)
+
+
+def _quant_half_even(w, fmt):
+    real = oq._round_half_away
+    oq._round_half_away = np.round
+    try:
+        return _orig_q["quantize"](w, fmt)
+    finally:
+        oq._round_half_away = real
+
+
+def _quant_scale_128(w, fmt):
+    real = dict(oq.QMAX)
+    oq.QMAX[fmt] = real[fmt] + 1
+    try:
+        c, s = _orig_q["quantize"](w, fmt)
+    finally:
+        oq.QMAX.update(real)
+    return np.clip(c, -real[fmt], real[fmt]) if fmt == oq.Q8 else c, s
+
+
+def _dequant_scale_misread(codes, scales, fmt, k):
+    d = scales.view(np.float16).astype(np.float64)
+    return oq.codes_of(codes, fmt, k) * np.repeat(d, 32, axis=1) * (1 + 2.0 ** -12)
+
+
+def _quant_nibbles_swapped(w, fmt):
+    c, s = _orig_q["quantize"](w, fmt)
+    if fmt == oq.Q4:
+        c = ((c >> 4) | (c << 4)).astype(np.uint8)
+    return c, s
+
+
+MUTATIONS_Q = {
+    "quant_rounds_half_even": ("quantize", _quant_half_even),
+    "quant_scale_amax_over_qmax_plus_1": ("quantize", _quant_scale_128),
+    "dequant_scale_misread": ("dequantize", _dequant_scale_misread),
+    "quant_nibbles_swapped": ("quantize", _quant_nibbles_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_Q))
+def test_planted_quant_mistake_is_caught(name, monkeypatch):
+    attr, repl = MUTATIONS_Q[name]
+    monkeypatch.setattr(oq, attr, repl)
+    caught = []
+    for pin in _all_pins():
+        try:
+            pin()
+        except Exception as e:  # noqa: BLE001 -- an error also flags the slip
+            caught.append(type(e).__name__)
+            break
+    assert caught, f"no pin catches the planted mistake {name}"
 
 
 MUTATIONS = {

@@ -30,6 +30,8 @@ ATD_F32 = 0
 ATD_BF16 = 1
 ATD_FLAG_DRY_RUN = 1
 ATD_FLAG_NO_MFMA = 2
+ATD_WFMT_DENSE, ATD_WFMT_Q8, ATD_WFMT_Q4 = 0, 1, 2
+ATD_QBLOCK = 32
 
 STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FULL",
                 -5: "CAPACITY", -6: "DEVICE", -7: "UNSUPPORTED"}
@@ -37,7 +39,7 @@ STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FU
 EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
            "decoder_step", "decoder_embed", "greedy_argmax", "sample_topk", "decoder_generate",
-           "talker_generate_frames", "decoder_time_stage")
+           "talker_generate_frames", "quantize_blocks", "decoder_time_stage")
 
 ATD_STAGE_QKV, ATD_STAGE_ROPE, ATD_STAGE_ATTN, ATD_STAGE_OPROJ, ATD_STAGE_GATEUP, \
     ATD_STAGE_DOWN, ATD_STAGE_HEAD = range(7)
@@ -57,7 +59,7 @@ class atd_config(C.Structure):
                 ("kv_dtype", C.c_int32),
                 ("rope_theta", C.c_double), ("rms_eps", C.c_float),
                 ("max_slots", C.c_int32), ("max_rows", C.c_int32), ("max_ctx", C.c_int32),
-                ("flags", C.c_int32)]
+                ("flags", C.c_int32), ("weight_format", C.c_int32)]
 
 
 ATD_TOPK_MAX = 256
@@ -71,7 +73,8 @@ class atd_sampling(C.Structure):
 class atd_layer_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "attn_norm", "wq", "wk", "wv", "bq", "bk", "bv", "q_norm", "k_norm", "wo",
-        "mlp_norm", "w_gate", "w_up", "w_down")]
+        "mlp_norm", "w_gate", "w_up", "w_down", "wq_scale", "wk_scale", "wv_scale", "wo_scale",
+        "w_gate_scale", "w_up_scale", "w_down_scale")]
 
 
 class atd_weights(C.Structure):
@@ -104,6 +107,7 @@ def _load():
         "talker_generate_frames": ([vp, i32, vp, i32, i32, vp, vp, vp, vp, f32,
                                     C.POINTER(atd_sampling), C.POINTER(atd_sampling), vp, vp, vp,
                                     vp], C.c_int),
+        "quantize_blocks": ([vp, i32, C.c_int64, i32, i32, vp, vp, vp], C.c_int),
         "decoder_time_stage": ([vp, i32, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
     }
     for name, (args, res) in sig.items():
@@ -211,6 +215,11 @@ def talker_generate_frames(tk: int, tk_slot: int, cp: int, cp_slot: int, n_frame
                                       seen, penalty, _sampling(tk_sampling),
                                       _sampling(cp_sampling), codes_out, tk_logits, cp_logits,
                                       stream), tk)
+
+
+def quantize_blocks(w: int, dtype: int, rows: int, cols: int, fmt: int, codes: int, scales: int,
+                    stream: int) -> None:
+    _check(lib.quantize_blocks(w, dtype, rows, cols, fmt, codes, scales, stream))
 
 
 def decoder_time_stage(handle: int, stage: int, slot0: int, B: int, reps: int,

@@ -143,7 +143,24 @@ int check_config(const atd_config* c) {
     return fail(nullptr, ATD_ERR_CAPACITY, "max_ctx %d outside [1, 2^20]", c->max_ctx);
   if (c->flags & ~(ATD_FLAG_DRY_RUN | ATD_FLAG_NO_MFMA))
     return fail(nullptr, ATD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)c->flags);
+  if (c->weight_format != ATD_WFMT_DENSE && c->weight_format != ATD_WFMT_Q8 &&
+      c->weight_format != ATD_WFMT_Q4)
+    return fail(nullptr, ATD_ERR_DTYPE, "weight_format %d is not ATD_WFMT_DENSE/Q8/Q4",
+                c->weight_format);
+  if (c->weight_format != ATD_WFMT_DENSE &&
+      (c->hidden % kQBlock || c->ffn % kQBlock || (c->n_q_heads * c->head_dim) % kQBlock))
+    return fail(nullptr, ATD_ERR_SHAPE,
+                "quantized weights need hidden %d, ffn %d and n_q_heads*head_dim %d to be "
+                "multiples of %d",
+                c->hidden, c->ffn, c->n_q_heads * c->head_dim, kQBlock);
   return ATD_OK;
+}
+
+// Weight type of the seven per-layer matrices.
+int layer_wtype(const atd_config& c) {
+  if (c.weight_format == ATD_WFMT_Q8) return kWQ8;
+  if (c.weight_format == ATD_WFMT_Q4) return kWQ4;
+  return c.dtype == ATD_BF16 ? kWBF16 : kWF32;
 }
 
 #define NEED(ptr, name)                                                                    \
@@ -164,6 +181,22 @@ int check_weights(const atd_config* c, const atd_weights* w) {
   snprintf(name, sizeof name, "layers[%d]." #field, l);           \
   NEED(L.field, name);
     LW(attn_norm) LW(wq) LW(wk) LW(wv) LW(wo) LW(mlp_norm) LW(w_gate) LW(w_up) LW(w_down)
+    {
+      const void* sc[7] = {L.wq_scale, L.wk_scale, L.wv_scale, L.wo_scale,
+                           L.w_gate_scale, L.w_up_scale, L.w_down_scale};
+      static const char* const sn[7] = {"wq_scale", "wk_scale", "wv_scale", "wo_scale",
+                                        "w_gate_scale", "w_up_scale", "w_down_scale"};
+      for (int j = 0; j < 7; ++j) {
+        if (c->weight_format == ATD_WFMT_DENSE) {
+          if (sc[j])
+            return fail(nullptr, ATD_ERR_INVALID_ARG,
+                        "layers[%d].%s is set but weight_format is dense", l, sn[j]);
+        } else if (!sc[j] || ((uintptr_t)sc[j] & 1)) {
+          return fail(nullptr, ATD_ERR_INVALID_ARG, "layers[%d].%s %p is NULL or odd", l, sn[j],
+                      sc[j]);
+        }
+      }
+    }
     if (c->qkv_bias) {
       LW(bq) LW(bk) LW(bv)
     } else if (L.bq || L.bk || L.bv) {
@@ -285,7 +318,7 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
   const atd_config& c = d->cfg;
   const int h = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv;
-  const int bf16 = c.dtype == ATD_BF16;
+  const int wt = layer_wtype(c);
   const int kv_bf16 = c.kv_dtype == ATD_BF16;
   const bool fused = rows.mode == kRowsStep;
   hipError_t e = hipSuccess;
@@ -295,6 +328,9 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
     g.W[0] = W.wq;
     g.W[1] = W.wk;
     g.W[2] = W.wv;
+    g.S[0] = (const uint16_t*)W.wq_scale;
+    g.S[1] = (const uint16_t*)W.wk_scale;
+    g.S[2] = (const uint16_t*)W.wv_scale;
     g.bias[0] = (const float*)W.bq;
     g.bias[1] = (const float*)W.bk;
     g.bias[2] = (const float*)W.bv;
@@ -310,13 +346,14 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
     g.K = h;
     g.N = nqkv;
     g.M = M;
-    STAGE(ATD_STAGE_QKV, launch_gemv(g, kEpiStore, true, bf16, s));
+    STAGE(ATD_STAGE_QKV, launch_gemv(g, kEpiStore, true, wt, s));
     // prefill rows of one slot read each other's keys: append them all first
     if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
     STAGE(ATD_STAGE_ATTN, attention(d, attn_args(d, rows, l, M, max_len_bound, fused), s));
 
     GemvArgs op{};
     op.W[0] = W.wo;
+    op.S[0] = (const uint16_t*)W.wo_scale;
     op.seg_end[0] = op.seg_end[1] = op.seg_end[2] = h;
     op.x = d->o;
     op.ldx = nq;
@@ -325,11 +362,13 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
     op.K = nq;
     op.N = h;
     op.M = M;
-    STAGE(ATD_STAGE_OPROJ, launch_gemv(op, kEpiResidual, false, bf16, s));
+    STAGE(ATD_STAGE_OPROJ, launch_gemv(op, kEpiResidual, false, wt, s));
 
     GemvArgs gu{};
     gu.W[0] = W.w_gate;
     gu.W2 = W.w_up;
+    gu.S[0] = (const uint16_t*)W.w_gate_scale;
+    gu.S2 = (const uint16_t*)W.w_up_scale;
     gu.seg_end[0] = gu.seg_end[1] = gu.seg_end[2] = c.ffn;
     gu.x = x;
     gu.ldx = h;
@@ -340,10 +379,11 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
     gu.K = h;
     gu.N = c.ffn;
     gu.M = M;
-    STAGE(ATD_STAGE_GATEUP, launch_gemv(gu, kEpiSwiglu, true, bf16, s));
+    STAGE(ATD_STAGE_GATEUP, launch_gemv(gu, kEpiSwiglu, true, wt, s));
 
     GemvArgs dn{};
     dn.W[0] = W.w_down;
+    dn.S[0] = (const uint16_t*)W.w_down_scale;
     dn.seg_end[0] = dn.seg_end[1] = dn.seg_end[2] = h;
     dn.x = d->act;
     dn.ldx = c.ffn;
@@ -352,7 +392,7 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
     dn.K = c.ffn;
     dn.N = h;
     dn.M = M;
-    STAGE(ATD_STAGE_DOWN, launch_gemv(dn, kEpiResidual, false, bf16, s));
+    STAGE(ATD_STAGE_DOWN, launch_gemv(dn, kEpiResidual, false, wt, s));
   }
   return e;
 }
@@ -375,7 +415,7 @@ hipError_t run_head_gemv(atd_decoder* d, const float* xrows, int M, int head, fl
   g.K = c.hidden;
   g.N = c.vocab;
   g.M = M;
-  STAGE(ATD_STAGE_HEAD, launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16, s));
+  STAGE(ATD_STAGE_HEAD, launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16 ? kWBF16 : kWF32, s));
   return e;
 }
 
@@ -630,7 +670,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   const size_t o_samp = carve(nblk_s > 1 ? (size_t)nblk_s * kTopKMax * sizeof(uint2) : 0);
   // MFMA path: hi/lo activations of one 64-row chunk and split-K partials of
   // the largest GEMM (q/k/v, o, gate/up, down, LM head)
-  d->mma = cfg->dtype == ATD_BF16 && !(cfg->flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 &&
+  d->mma = cfg->dtype == ATD_BF16 && cfg->weight_format == ATD_WFMT_DENSE &&
+           !(cfg->flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 &&
            nq % 32 == 0 && cfg->ffn % 32 == 0 && std::max(R, S) >= 3;
   size_t o_mss = 0, o_mhi = 0, o_mlo = 0, o_mpart = 0;
   if (d->mma) {
@@ -1010,6 +1051,38 @@ extern "C" int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* 
   }
   hipError_t e = launch_sample(a, (hipStream_t)stream);
   return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "sample_topk");
+}
+
+// ---------------------------------------------------------------- quantization
+
+extern "C" int quantize_blocks(const void* w, int32_t dtype, int64_t rows, int32_t cols,
+                               int32_t format, void* codes, uint16_t* scales, void* stream) {
+  if (!w || !codes || !scales)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "w, codes or scales is NULL");
+  if (!aligned16(w) || !aligned16(codes) || ((uintptr_t)scales & 1))
+    return fail(nullptr, ATD_ERR_INVALID_ARG,
+                "w %p and codes %p must be 16-byte aligned, scales %p 2-byte aligned", w, codes,
+                (void*)scales);
+  if (dtype != ATD_F32 && dtype != ATD_BF16)
+    return fail(nullptr, ATD_ERR_DTYPE, "dtype %d is not ATD_F32 (0) or ATD_BF16 (1)", dtype);
+  if (format != ATD_WFMT_Q8 && format != ATD_WFMT_Q4)
+    return fail(nullptr, ATD_ERR_DTYPE, "format %d is not ATD_WFMT_Q8 or ATD_WFMT_Q4", format);
+  if (rows < 1 || cols < kQBlock || cols % kQBlock)
+    return fail(nullptr, ATD_ERR_SHAPE, "rows %lld, cols %d: cols must be a positive multiple of %d",
+                (long long)rows, cols, kQBlock);
+  if (rows * (int64_t)(cols / kQBlock) > ((int64_t)1 << 40))
+    return fail(nullptr, ATD_ERR_SHAPE, "rows %lld x cols %d is too large", (long long)rows,
+                cols);
+  QuantArgs a{};
+  a.w = w;
+  a.bf16 = dtype == ATD_BF16;
+  a.rows = rows;
+  a.cols = cols;
+  a.q4 = format == ATD_WFMT_Q4;
+  a.codes = codes;
+  a.scales = scales;
+  const hipError_t e = launch_quantize(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "quantize_blocks");
 }
 
 // ---------------------------------------------------------------- generation

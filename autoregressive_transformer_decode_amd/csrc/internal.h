@@ -82,8 +82,15 @@ struct RopeArgs {
 // ---------------------------------------------------------------- GEMV
 enum GemvEpilogue { kEpiStore = 0, kEpiResidual = 1, kEpiSwiglu = 2 };
 
+// Weight storage of a GEMV: dense float32 / bf16, or block-quantized codes
+// (int8, or 4-bit pairs) with one fp16 scale per kQBlock weights of a row.
+enum WeightType { kWF32 = 0, kWBF16 = 1, kWQ8 = 2, kWQ4 = 3 };
+constexpr int kQBlock = 32;
+
 struct GemvArgs {
   const void* W[3];       // row segments [rows_s, K]; segment s ends at seg_end[s]
+  const uint16_t* S[3];   // fp16 block scales [rows_s, K / kQBlock] (quantized types)
+  const uint16_t* S2;     // scales of W2
   const float* bias[3];   // per-segment bias or null (kEpiStore only)
   int seg_end[3];
   const void* W2;         // up-projection [N, K] (kEpiSwiglu)
@@ -260,7 +267,18 @@ struct ReduceArgs {
 // ---------------------------------------------------------------- launchers
 // Each returns the first HIP error of its launches (hipSuccess otherwise).
 hipError_t launch_embed(const EmbedArgs& a, int bf16, hipStream_t s);
-hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int bf16, hipStream_t s);
+hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int wtype, hipStream_t s);
+
+struct QuantArgs {
+  const void* w;         // [rows, cols] float32 or bf16
+  int bf16;
+  int64_t rows;
+  int cols;
+  int q4;                // 0: int8 codes, 1: 4-bit pairs
+  void* codes;
+  uint16_t* scales;      // [rows, cols / kQBlock]
+};
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_rope_append(const RopeArgs& a, int bf16, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream_t s);
 hipError_t launch_advance(const SlotTables& st, RowMap rows, int M, hipStream_t s);

@@ -135,6 +135,86 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
 #endif
 }
 
+// 8- and 2-byte loads through the global address space.
+typedef unsigned int V2U32 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ldg8(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(1))) const V2U32 GV2U32;
+  const V2U32 v = *(GV2U32*)(p);
+  return make_uint2(v.x, v.y);
+#else
+  return *reinterpret_cast<const uint2*>(p);
+#endif
+}
+__device__ __forceinline__ uint16_t ldg2(const uint16_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *(__attribute__((address_space(1))) const uint16_t*)(p);
+#else
+  return *p;
+#endif
+}
+
+// IEEE fp16 bit patterns <-> float (conversion rounds to nearest even).
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Weight chunks of the GEMV: one load per lane per row and chunk, unpacked to
+// N floats.  Quantized formats unpack to code + OFF (unsigned, so each byte
+// converts in one instruction) and carry one fp16 scale per kQBlock weights;
+// the offset leaves once per chunk through the chunk's input sum.
+struct WQ8 {};   // int8 codes
+struct WQ4 {};   // 4-bit codes + 8: weight 2i in the low nibble of byte i, 2i+1 high
+
+template <typename WT>
+struct WFmt {    // dense float32 / bf16
+  static constexpr int N = Vec16<WT>::N, BYTES = 16;
+  static constexpr bool Q = false;
+  static constexpr float OFF = 0.f;
+  __device__ static __forceinline__ uint4 load(const char* p) { return ldg16(p); }
+  __device__ static __forceinline__ void unpack(const uint4& r, float* f) { Vec16<WT>::unpack(r, f); }
+};
+template <>
+struct WFmt<WQ8> {
+  static constexpr int N = 16, BYTES = 16;
+  static constexpr bool Q = true;
+  static constexpr float OFF = 128.f;
+  __device__ static __forceinline__ uint4 load(const char* p) { return ldg16(p); }
+  __device__ static __forceinline__ void unpack(const uint4& r, float* f) {
+    const uint32_t w[4] = {r.x ^ 0x80808080u, r.y ^ 0x80808080u, r.z ^ 0x80808080u,
+                           r.w ^ 0x80808080u};   // code + 128 in every byte
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * j + b] = (float)((w[j] >> (8 * b)) & 0xffu);
+  }
+};
+template <>
+struct WFmt<WQ4> {
+  static constexpr int N = 16, BYTES = 8;
+  static constexpr bool Q = true;
+  static constexpr float OFF = 8.f;
+  __device__ static __forceinline__ uint4 load(const char* p) {
+    const uint2 v = ldg8(p);
+    return make_uint4(v.x, v.y, 0u, 0u);
+  }
+  __device__ static __forceinline__ void unpack(const uint4& r, float* f) {
+    const uint32_t w[2] = {r.x, r.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t lo = w[j] & 0x0f0f0f0fu, hi = (w[j] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f[8 * j + 2 * b] = (float)((lo >> (8 * b)) & 0xffu);
+        f[8 * j + 2 * b + 1] = (float)((hi >> (8 * b)) & 0xffu);
+      }
+    }
+  }
+};
+
 __device__ __forceinline__ void row_of(const RowMap& r, const SlotTables& st, int m,
                                        int& slot, int& pos) {
   if (r.mode == kRowsPrefill) {
@@ -258,7 +338,8 @@ __device__ __forceinline__ T pick3(const T (&v)[3], int i) {
 
 template <typename WT, int MR, int KS, int KI, int EPI, bool NORM, int RW>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
-  constexpr int VEC = Vec16<WT>::N;
+  using F = WFmt<WT>;
+  constexpr int VEC = F::N;
   constexpr int NW = EPI == kEpiSwiglu ? 2 : 1;
   constexpr int BR = (4 / KS) * RW;   // rows per block
   __shared__ float red_ss[4][MR];
@@ -327,18 +408,30 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int sg = rowc < a.seg_end[0] ? 0 : (rowc < a.seg_end[1] ? 1 : 2);
   const int sbeg = sg == 0 ? 0 : (sg == 1 ? a.seg_end[0] : a.seg_end[1]);
   const int nr = min(RW, pick3(a.seg_end, sg) - rowc);   // >= 1
-  const WT* Wp = reinterpret_cast<const WT*>(pick3(a.W, sg)) + (size_t)(rowc - sbeg) * K;
-  const WT* W2p = EPI == kEpiSwiglu ? reinterpret_cast<const WT*>(a.W2) + (size_t)rowc * K : nullptr;
+  const size_t rowb = (size_t)nk * F::BYTES;   // bytes of a weight row
+  const char* Wp = reinterpret_cast<const char*>(pick3(a.W, sg)) + (size_t)(rowc - sbeg) * rowb;
+  const char* W2p =
+      EPI == kEpiSwiglu ? reinterpret_cast<const char*>(a.W2) + (size_t)rowc * rowb : nullptr;
+  const int nb = K / kQBlock;   // scale blocks per row (quantized types)
+  const uint16_t* Sp = F::Q ? pick3(a.S, sg) + (size_t)(rowc - sbeg) * nb : nullptr;
+  const uint16_t* S2p = F::Q && EPI == kEpiSwiglu ? a.S2 + (size_t)rowc * nb : nullptr;
   uint4 w[KI][RW][NW];
+  uint16_t sc[KI][RW][NW];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
     const int cq = lane + 64 * i;
     const int c = min(ks * ql + cq, nk - 1);
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
-      const size_t off = (size_t)min(r, nr - 1) * K + (size_t)c * VEC;
-      w[i][r][0] = ldg16(Wp + off);
-      if constexpr (NW == 2) w[i][r][1] = ldg16(W2p + off);
+      const size_t rr = (size_t)min(r, nr - 1);
+      const size_t off = rr * rowb + (size_t)c * F::BYTES;
+      w[i][r][0] = F::load(Wp + off);
+      if constexpr (NW == 2) w[i][r][1] = F::load(W2p + off);
+      if constexpr (F::Q) {
+        const size_t so = rr * nb + (size_t)c * VEC / kQBlock;
+        sc[i][r][0] = ldg2(Sp + so);
+        if constexpr (NW == 2) sc[i][r][1] = ldg2(S2p + so);
+      }
     }
   }
   // keep the scheduler from hoisting the norm (which waits for the small
@@ -384,7 +477,19 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
   }
 
-  // 4) dot products
+  // 4) dot products (quantized: per chunk, scale * (sum (code + OFF) x - OFF sum x))
+  float xs[MR][KI];
+  if constexpr (F::Q) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        float t = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) t += xv[m][i][e];
+        xs[m][i] = t;
+      }
+  }
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -395,9 +500,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
           float wf[VEC];
-          Vec16<WT>::unpack(w[i][r][t], wf);
+          F::unpack(w[i][r][t], wf);
+          if constexpr (F::Q) {
+            float dq = 0.f;
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) acc = fmaf(wf[e], xv[m][i][e], acc);
+            for (int e = 0; e < VEC; ++e) dq = fmaf(wf[e], xv[m][i][e], dq);
+            acc = fmaf(f16_bits_to_f32(sc[i][r][t]), fmaf(-F::OFF, xs[m][i], dq), acc);
+          } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc = fmaf(wf[e], xv[m][i][e], acc);
+          }
         }
         acc = wave_sum(acc);
         if (lane == 0) red_acc[q][r][m][t] = acc;
@@ -418,6 +530,66 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       *o = v[0] / (1.0f + expf(-v[0])) * v[NW - 1];
     else
       *o = eo + v[0];
+  }
+}
+
+// ------------------------------------------------------------------ block quantization
+// One thread per block of kQBlock weights of a row: d = max|w| / QMAX,
+// code = w / d rounded half away from zero (float32), scale = fp16(d).
+template <typename WT, bool Q4>
+__global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
+  const int nb = a.cols / kQBlock;
+  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= a.rows * nb) return;
+  const int64_t row = blk / nb;
+  const int b = (int)(blk - row * nb);
+  constexpr int VN = Vec16<WT>::N;
+  const char* src = reinterpret_cast<const char*>(a.w) +
+                    ((size_t)row * a.cols + (size_t)b * kQBlock) * sizeof(WT);
+  float v[kQBlock];
+#pragma unroll
+  for (int c = 0; c < kQBlock / VN; ++c) Vec16<WT>::unpack(ldg16(src + 16 * c), v + c * VN);
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < kQBlock; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  const float qmax = Q4 ? 7.f : 127.f;
+  const float d = amax / qmax;
+  int q[kQBlock];
+#pragma unroll
+  for (int e = 0; e < kQBlock; ++e) {
+    float t = d > 0.f ? roundf(v[e] / d) : 0.f;
+    t = fminf(fmaxf(t, -qmax), qmax);
+    q[e] = (int)t;
+  }
+  a.scales[(size_t)row * nb + b] = f32_to_f16_bits(d);
+  if constexpr (Q4) {
+    uint32_t wds[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t wd = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int e = 8 * j + 2 * t;
+        wd |= ((uint32_t)(q[e] + 8) | ((uint32_t)(q[e + 1] + 8) << 4)) << (8 * t);
+      }
+      wds[j] = wd;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.codes) +
+                                          (size_t)row * (a.cols / 2) + (size_t)b * (kQBlock / 2));
+    *dst = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+  } else {
+    uint32_t wds[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t wd = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) wd |= ((uint32_t)q[4 * j + t] & 0xffu) << (8 * t);
+      wds[j] = wd;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.codes) +
+                                          (size_t)row * a.cols + (size_t)b * kQBlock);
+    dst[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+    dst[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
   }
 }
 
@@ -1566,7 +1738,7 @@ static void gemv_shape(int K, int vec, int& ks, int& ki) {
 template <typename WT, int MR, int EPI, bool NORM>
 static void gemv_dispatch_shape(const GemvArgs& a, hipStream_t s) {
   int ks, ki;
-  gemv_shape(a.K, Vec16<WT>::N, ks, ki);
+  gemv_shape(a.K, WFmt<WT>::N, ks, ki);
   // 4 rows per wave group when that still leaves >= 512 blocks
   const int rw = ks == 4 || a.N >= 512 * (4 / ks) * 4 ? 4 : ks;
   const int br = (4 / ks) * rw;   // rows per block
@@ -1623,11 +1795,26 @@ static void gemv_dispatch(const GemvArgs& a, int epi, bool norm, hipStream_t s) 
     gemv_dispatch_mr<WT, kEpiSwiglu, true>(a, s);
 }
 
-hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int bf16, hipStream_t s) {
-  if (bf16)
-    gemv_dispatch<uint16_t>(a, epi, norm, s);
-  else
-    gemv_dispatch<float>(a, epi, norm, s);
+hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int wtype, hipStream_t s) {
+  switch (wtype) {
+    case kWBF16: gemv_dispatch<uint16_t>(a, epi, norm, s); break;
+    case kWQ8: gemv_dispatch<WQ8>(a, epi, norm, s); break;
+    case kWQ4: gemv_dispatch<WQ4>(a, epi, norm, s); break;
+    default: gemv_dispatch<float>(a, epi, norm, s); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+  const int64_t blocks = a.rows * (a.cols / kQBlock);
+  const dim3 grid((unsigned)((blocks + 255) / 256)), block(256);
+  if (a.bf16) {
+    if (a.q4) hipLaunchKernelGGL((k_quantize<uint16_t, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_quantize<uint16_t, false>), grid, block, 0, s, a);
+  } else {
+    if (a.q4) hipLaunchKernelGGL((k_quantize<float, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_quantize<float, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

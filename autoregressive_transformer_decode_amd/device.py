@@ -32,14 +32,34 @@ def _to_dev(arr: np.ndarray, device) -> torch.Tensor:
     return t.to(device, non_blocking=False).contiguous()
 
 
+QUANT_FORMATS = {None: B.ATD_WFMT_DENSE, "q8": B.ATD_WFMT_Q8, "q4": B.ATD_WFMT_Q4}
+_LINEARS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def quantize_blocks(w: torch.Tensor, fmt: str):
+    """(codes, scales) of a dense [N, K] device matrix in the block format
+    ``fmt`` ("q8" or "q4"), from the library's quantizer."""
+    n, k = w.shape
+    code_bytes = n * k if fmt == "q8" else n * k // 2
+    codes = torch.empty(code_bytes, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(n, k // B.ATD_QBLOCK, dtype=torch.int16, device=w.device)
+    B.quantize_blocks(w.data_ptr(), B.ATD_BF16 if w.dtype == torch.bfloat16 else B.ATD_F32, n, k,
+                      QUANT_FORMATS[fmt], codes.data_ptr(), scales.data_ptr(), _stream())
+    return codes, scales
+
+
 class DeviceModel:
     """Weights of one stack in HBM.  ``tables`` may be shared with another
-    stack (the Talker and the Code Predictor use the same code embeddings)."""
+    stack (the Talker and the Code Predictor use the same code embeddings).
+    ``quant`` ("q8" / "q4") stores the seven per-layer matrices block-quantized
+    by the library's quantizer (the dense copies are released)."""
 
     def __init__(self, mw: ModelWeights, device="cuda",
-                 tables: Optional[List[torch.Tensor]] = None):
+                 tables: Optional[List[torch.Tensor]] = None, quant: Optional[str] = None):
         s = mw.shape
         self.shape = s
+        self.quant = quant
+        self.weight_format = QUANT_FORMATS[quant]
         self.keep: List[torch.Tensor] = []
 
         def up(a):
@@ -57,6 +77,15 @@ class DeviceModel:
                 q_norm=up(Lw.q_norm), k_norm=up(Lw.k_norm), wo=up(Lw.wo.storage),
                 mlp_norm=up(Lw.mlp_norm), w_gate=up(Lw.w_gate.storage),
                 w_up=up(Lw.w_up.storage), w_down=up(Lw.w_down.storage)))
+            if quant is not None:
+                L = self.layers[-1]
+                for name in _LINEARS:
+                    codes, scales = quantize_blocks(L[name], quant)
+                    L[name + "_scale"] = scales
+                    self.keep.extend([codes, scales])
+                    dense, L[name] = L[name], codes
+                    self.keep = [t for t in self.keep if t is not dense]
+                torch.cuda.current_stream().synchronize()
         self.final_norm = up(mw.final_norm)
         self.heads = [up(h.storage) for h in mw.heads]
         if tables is None:
@@ -85,7 +114,8 @@ class DeviceModel:
 
 
 def make_config(s: ModelShape, max_slots: int, max_rows: int, max_ctx: int,
-                n_tables: Optional[int] = None, flags: int = 0) -> B.atd_config:
+                n_tables: Optional[int] = None, flags: int = 0,
+                weight_format: int = B.ATD_WFMT_DENSE) -> B.atd_config:
     return B.atd_config(
         n_layers=s.n_layers, hidden=s.hidden, n_q_heads=s.n_q_heads, n_kv_heads=s.n_kv_heads,
         head_dim=s.head_dim, ffn=s.ffn, vocab=s.vocab, n_lm_heads=s.n_lm_heads,
@@ -94,7 +124,8 @@ def make_config(s: ModelShape, max_slots: int, max_rows: int, max_ctx: int,
         dtype=B.ATD_BF16 if s.dtype == BF16 else B.ATD_F32,
         kv_dtype=B.ATD_BF16 if s.kv_dtype == BF16 else B.ATD_F32,
         rope_theta=s.rope_theta, rms_eps=s.rms_eps,
-        max_slots=max_slots, max_rows=max_rows, max_ctx=max_ctx, flags=flags)
+        max_slots=max_slots, max_rows=max_rows, max_ctx=max_ctx, flags=flags,
+        weight_format=weight_format)
 
 
 class Decoder:
@@ -108,7 +139,8 @@ class Decoder:
             s = dataclasses.replace(s, kv_dtype=kv_dtype)
         self.shape = s
         self.cfg = make_config(s, max_slots, max_rows, max_ctx,
-                               flags=0 if mfma else B.ATD_FLAG_NO_MFMA)
+                               flags=0 if mfma else B.ATD_FLAG_NO_MFMA,
+                               weight_format=model.weight_format)
         self.handle = B.decoder_create(self.cfg, model.weights)
         self.kv = {}   # slot -> (list of K tensors, list of V tensors)
         self.kv_dtype = torch.bfloat16 if s.kv_dtype == BF16 else torch.float32

@@ -93,7 +93,29 @@ typedef struct atd_config {
   int32_t max_rows;    /* largest B of a step / T of a prefill               */
   int32_t max_ctx;     /* largest number of cached rows any slot reaches     */
   int32_t flags;       /* ATD_FLAG_* bits                                    */
+  int32_t weight_format; /* ATD_WFMT_*: storage of the seven per-layer
+                            matrices (LM heads and tables stay in dtype)     */
 } atd_config;
+
+/* atd_config.weight_format ("Rockchip NPU sidecars" page, section "The talker
+ * is the only DRAM-bound candidate": the Talker's matmuls as Q8_0, 32 int8
+ * weights and one fp16 scale per block, and re-quantized to Q4_K at 47%
+ * fewer bytes).  Quantized matrices keep their [out, in] shape, cut into
+ * blocks of ATD_QBLOCK consecutive weights of a row; weight = fp16 scale of
+ * its block * its signed code.
+ *   ATD_WFMT_DENSE  the matrices in dtype.
+ *   ATD_WFMT_Q8     codes int8 [out, in]; scales fp16 [out, in / 32].
+ *   ATD_WFMT_Q4     codes 4-bit [out, in / 2] bytes, the code of weight 2i in
+ *                   the low nibble of byte i and of weight 2i+1 in the high
+ *                   nibble, each stored as code + 8 (codes in [-7, 7]);
+ *                   scales fp16 [out, in / 32].
+ * Quantized formats need h, Hq*D and F to be multiples of 32 and run every
+ * call on the matrix-vector kernels (the dequantization is fused there).
+ * quantize_blocks writes both forms from dense weights. */
+#define ATD_WFMT_DENSE 0
+#define ATD_WFMT_Q8 1
+#define ATD_WFMT_Q4 2
+#define ATD_QBLOCK 32
 
 /* atd_config.flags: ATD_FLAG_DRY_RUN makes a host-only decoder: every
  * argument check runs and the host state (slot positions, capacities,
@@ -109,7 +131,8 @@ typedef struct atd_config {
 #define ATD_FLAG_NO_MFMA 2
 
 /* Device pointers of one layer.  Matrices are row-major [out, in] in the
- * config dtype; gains and biases are float32. */
+ * config dtype, or their codes in a quantized weight_format (16-byte
+ * aligned); gains and biases are float32. */
 typedef struct atd_layer_weights {
   const void* attn_norm; /* [h]            input RMSNorm gain               */
   const void* wq;        /* [Hq*D, h]                                       */
@@ -125,6 +148,15 @@ typedef struct atd_layer_weights {
   const void* w_gate;    /* [F, h]                                          */
   const void* w_up;      /* [F, h]                                          */
   const void* w_down;    /* [h, F]                                          */
+  /* fp16 block scales [out, in / 32] of the seven matrices when
+   * weight_format is quantized (NULL otherwise; 2-byte aligned) */
+  const void* wq_scale;
+  const void* wk_scale;
+  const void* wv_scale;
+  const void* wo_scale;
+  const void* w_gate_scale;
+  const void* w_up_scale;
+  const void* w_down_scale;
 } atd_layer_weights;
 
 /* All weights of a stack.  The arrays are host arrays of device pointers;
@@ -330,6 +362,19 @@ int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_decoder* cp, in
                            uint32_t* seen, float penalty, const atd_sampling* tk_sampling,
                            const atd_sampling* cp_sampling, int32_t* codes_out, float* tk_logits,
                            float* cp_logits, void* stream);
+
+/* Block quantization of dense weights into a quantized weight_format
+ * (ATD_WFMT_Q8 or ATD_WFMT_Q4; the formats are described with
+ * atd_config.weight_format).  w: device [rows, cols] in dtype (ATD_F32 or
+ * ATD_BF16), 16-byte aligned, cols a multiple of 32.  For each block of 32
+ * weights of a row: d = max|w| / 127 (Q8) or / 7 (Q4) in float32; code =
+ * w / d (float32 division) rounded to the nearest integer, halves away from
+ * zero, clamped to +-127 (+-7), 0 when d = 0; the scale stored is d rounded
+ * to fp16 (nearest even).  Writes codes (device, 16-byte aligned: rows * cols
+ * bytes for Q8, rows * cols / 2 for Q4) and scales (device uint16 [rows,
+ * cols / 32]) on `stream`.  Errors: INVALID_ARG, DTYPE, SHAPE, DEVICE. */
+int quantize_blocks(const void* w, int32_t dtype, int64_t rows, int32_t cols, int32_t format,
+                    void* codes, uint16_t* scales, void* stream);
 
 /* Stages of a decode step, for decoder_time_stage. */
 enum {

@@ -9,6 +9,7 @@ from __future__ import annotations
 import numpy as np
 
 from oracle import decoder as od
+from oracle import quant as oq
 
 
 def tiny_model(L=2, h=16, hq=4, hkv=2, D=4, F=24, V=40, qk_norm=True,
@@ -39,8 +40,13 @@ def tiny_model(L=2, h=16, hq=4, hkv=2, D=4, F=24, V=40, qk_norm=True,
     return od.make_model(hp, layers, g(h), heads, tabs, dtype=dtype)
 
 
-def oracle_from_weights(mw, dtype=np.float64):
-    """inputs.ModelWeights -> oracle Model (float values of the stored data)."""
+_LINEARS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
+def oracle_from_weights(mw, dtype=np.float64, quant=None):
+    """inputs.ModelWeights -> oracle Model (float values of the stored data).
+    With ``quant`` ("q8" / "q4") the seven per-layer matrices are replaced by
+    the oracle quantizer's read-back of them."""
     s = mw.shape
     hp = dict(n_layers=s.n_layers, hidden=s.hidden, n_q_heads=s.n_q_heads,
               n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, ffn=s.ffn,
@@ -54,6 +60,12 @@ def oracle_from_weights(mw, dtype=np.float64):
             k_norm=Lw.k_norm, wo=Lw.wo.values, mlp_norm=Lw.mlp_norm,
             w_gate=Lw.w_gate.values, w_up=Lw.w_up.values,
             w_down=Lw.w_down.values))
+        if quant is not None:
+            L = layers[-1]
+            for name in _LINEARS:
+                v = np.asarray(L[name], np.float32)
+                codes, scales = oq.quantize(v, quant)
+                L[name] = oq.dequantize(codes, scales, quant, v.shape[1])
     return od.make_model(hp, layers, mw.final_norm,
                          [t.values for t in mw.heads],
                          [t.values for t in mw.tables], dtype=dtype)

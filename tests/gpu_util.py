@@ -40,14 +40,16 @@ class StepCheck:
 
 
 def lm_parity(mw, X0, n_steps, s_init, grow_to=None, seed_check=True, oracle_dtype=np.float64,
-              rho=1.0):
+              rho=1.0, quant=None):
     """Prefill X0, then n_steps teacher-forced steps with the oracle's tokens
-    (bucket growth as the oracle does it).  Returns (StepCheck, oracle trace,
-    GPU logits of every step as numpy)."""
-    om = oracle_from_weights(mw, dtype=oracle_dtype)
+    (bucket growth as the oracle does it).  With ``quant`` the GPU holds the
+    seven per-layer matrices block-quantized and the oracle runs on its own
+    quantizer's read-back of them.  Returns (StepCheck, oracle trace, GPU
+    logits of every step as numpy)."""
+    om = oracle_from_weights(mw, dtype=oracle_dtype, quant=quant)
     ref, _ = od.run_lm(om, X0, n_steps, s_init, rho=rho)
     s = mw.shape
-    dm = dv.DeviceModel(mw)
+    dm = dv.DeviceModel(mw, quant=quant)
     max_ctx = X0.shape[0] + n_steps
     cap_final = od.bucket_for(max_ctx - 1, s_init)
     dec = dv.Decoder(dm, max_slots=1, max_rows=X0.shape[0], max_ctx=max(cap_final, max_ctx))

@@ -40,13 +40,16 @@ def _cfg(**kw):
 class FakeWeights:
     """Aligned, never-dereferenced pointer values for dry-run decoders."""
 
-    def __init__(self, cfg, bias=False, qk=True, misalign=None):
+    def __init__(self, cfg, bias=False, qk=True, misalign=None, scales=False):
         self.next = 0x10000
         self.layers = (B.atd_layer_weights * cfg.n_layers)()
         for l in range(cfg.n_layers):
             for f in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up",
                       "w_down"):
                 setattr(self.layers[l], f, self._p())
+            if scales:
+                for f in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+                    setattr(self.layers[l], f + "_scale", self._p())
             if bias:
                 for f in ("bq", "bk", "bv"):
                     setattr(self.layers[l], f, self._p())
@@ -321,3 +324,48 @@ def test_dry_run_generate_sampling():
         assert B.decoder_get_position(h, 0) == (14, 32)
     finally:
         B.decoder_destroy(h)
+
+
+def test_quantized_config_checks():
+    """weight_format: unknown value, shapes that are not whole blocks, and
+    scale pointers missing (quantized) or present (dense) are refused; a
+    quantized dry-run decoder steps like a dense one."""
+    with pytest.raises(B.AtdError) as ei:
+        B.decoder_create(_cfg(weight_format=7), FakeWeights(_cfg(), scales=True).w)
+    assert ei.value.code == B.ATD_ERR_DTYPE
+    with pytest.raises(B.AtdError) as ei:
+        B.decoder_create(_cfg(weight_format=B.ATD_WFMT_Q8, ffn=136),
+                         FakeWeights(_cfg(), scales=True).w)
+    assert ei.value.code == B.ATD_ERR_SHAPE and "ffn 136" in str(ei.value)
+    with pytest.raises(B.AtdError) as ei:
+        B.decoder_create(_cfg(weight_format=B.ATD_WFMT_Q4), FakeWeights(_cfg()).w)
+    assert ei.value.code == B.ATD_ERR_INVALID_ARG and "wq_scale" in str(ei.value)
+    with pytest.raises(B.AtdError) as ei:
+        B.decoder_create(_cfg(), FakeWeights(_cfg(), scales=True).w)
+    assert ei.value.code == B.ATD_ERR_INVALID_ARG and "dense" in str(ei.value)
+    cfg = _cfg(weight_format=B.ATD_WFMT_Q4)
+    fw = FakeWeights(cfg, scales=True)
+    h = B.decoder_create(cfg, fw.w)
+    try:
+        B.kv_bucket_grow(h, 0, [0x1000, 0x2000], [0x3000, 0x4000], 16, 0)
+        B.decoder_prefill(h, 0, 0x5000, 4, 0, None, 0x6000, 0)
+        assert B.decoder_get_position(h, 0) == (4, 16)
+    finally:
+        B.decoder_destroy(h)
+
+
+def test_quantize_blocks_argument_checks():
+    ok = (0x1000, B.ATD_BF16, 4, 64, B.ATD_WFMT_Q8, 0x2000, 0x3000, 0)
+    cases = [
+        ((None,) + ok[1:], B.ATD_ERR_INVALID_ARG, "NULL"),
+        (ok[:5] + (0x2008,) + ok[6:], B.ATD_ERR_INVALID_ARG, "aligned"),
+        (ok[:6] + (0x3001,) + ok[7:], B.ATD_ERR_INVALID_ARG, "aligned"),
+        ((0x1000, 5) + ok[2:], B.ATD_ERR_DTYPE, "dtype 5"),
+        (ok[:4] + (B.ATD_WFMT_DENSE,) + ok[5:], B.ATD_ERR_DTYPE, "format 0"),
+        (ok[:3] + (48,) + ok[4:], B.ATD_ERR_SHAPE, "cols 48"),
+        (ok[:2] + (0,) + ok[3:], B.ATD_ERR_SHAPE, "rows 0"),
+    ]
+    for args, code, needle in cases:
+        with pytest.raises(B.AtdError) as ei:
+            B.quantize_blocks(*args)
+        assert ei.value.code == code and needle in str(ei.value), (args, str(ei.value))

@@ -1,0 +1,96 @@
+"""Block-quantized weights on the GPU against the oracle.
+
+The library's quantizer writes the same codes and fp16 scales as the
+oracle's (bit for bit: both take the decisions in float32), and decoding with
+quantized matrices -- dequantized inside the matrix-vector kernels -- matches
+the oracle run on the oracle quantizer's read-back of the same weights, to
+the bar of dense weights (normwise 2e-3 on y and logits, tokens where the
+top-2 margin exceeds 1e-2)."""
+
+import numpy as np
+import pytest
+import torch
+
+from autoregressive_transformer_decode_amd import device as dv
+from autoregressive_transformer_decode_amd import inputs
+from oracle import quant as oq
+from tests.gpu_util import lm_parity, small_shape
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _special_rows(k, fmt):
+    """Rows that exercise the rounding: a zero block, exact half steps (away
+    from zero), a scale below fp16's normal range, large values."""
+    qmax = oq.QMAX[fmt]
+    d = 2.0 ** -7 if fmt == "q8" else 2.0 ** -3
+    rows = np.zeros((4, k), np.float32)
+    rows[1, :4] = [qmax * d, 2.5 * d, -2.5 * d, 0.5 * d]
+    rows[1, 4:8] = [1.5 * d, -0.5 * d, -qmax * d, 3.5 * d]
+    rows[2, :32] = np.linspace(-1, 1, 32, dtype=np.float32) * 1e-6
+    rows[3, :] = np.linspace(-900, 700, k, dtype=np.float32)
+    return rows
+
+
+@pytest.mark.parametrize("fmt", ["q8", "q4"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantizer_bitexact(fmt, dtype):
+    for n, k in [(7, 96), (300, 1024), (1000, 2048)]:
+        _log(f"quantize_blocks {fmt} {dtype} [{n}, {k}]")
+        w = inputs.normal(11, 9, n + k, (n, k), scale=0.02)
+        w[:4] = _special_rows(k, fmt)
+        if dtype == "bf16":
+            bits = inputs.to_bf16_bits(w)
+            w = inputs.bf16_bits_to_f32(bits)
+            wd = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            wd = torch.from_numpy(w).cuda()
+        codes, scales = dv.quantize_blocks(wd, fmt)
+        torch.cuda.synchronize()
+        rc, rs = oq.quantize(w, fmt)
+        assert np.array_equal(scales.cpu().numpy().view(np.uint16), rs)
+        got = codes.cpu().numpy().reshape(rc.shape)
+        assert np.array_equal(got.view(rc.dtype), rc)
+
+
+SMALL = {
+    "bf16": ("qb", 2, 256, 8, 2, 64, 512, 700, "bf16", True, False),
+    "f32": ("qf", 2, 128, 4, 2, 64, 384, 500, "f32", True, True),
+}
+
+
+@pytest.mark.parametrize("fmt", ["q8", "q4"])
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+def test_quantized_decode_small(fmt, kind):
+    """Prefill of 9 rows and 24 teacher-forced steps (penalty on), the cache
+    growing 16 -> 32 inside."""
+    shape = small_shape(*SMALL[kind])
+    mw = inputs.make_weights(shape, seed=5)
+    X0 = inputs.normal(5, 2, 3, (9, shape.hidden), scale=1.0)
+    chk, ref, _ = lm_parity(mw, X0, 24, 16, rho=1.1, quant=fmt)
+    _log(f"{fmt} {kind}: {chk.n} checks, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
+    assert chk.tokens_checked >= 10
+
+
+@pytest.mark.parametrize("fmt", ["q8", "q4"])
+def test_quantized_talker17(fmt):
+    """The 1.7B Talker shape with quantized matrices: a 32-row prefill and 6
+    teacher-forced steps against the float32 oracle on the read-back weights;
+    layer 0's matrices are quantized identically on both sides."""
+    wl = inputs.WORKLOADS["talker1.7b"]
+    mw = inputs.make_weights(wl.model, seed=0)
+    X0 = inputs.prefill_embeddings(wl, seed=0)[:32]
+    Lw = mw.layers[0]
+    for name in ("wq", "w_down"):
+        v = getattr(Lw, name)
+        wd = torch.from_numpy(v.storage.view(np.int16)).cuda().view(torch.bfloat16)
+        codes, scales = dv.quantize_blocks(wd, fmt)
+        rc, rs = oq.quantize(np.asarray(v.values, np.float32), fmt)
+        assert np.array_equal(scales.cpu().numpy().view(np.uint16), rs), name
+        assert np.array_equal(codes.cpu().numpy().reshape(rc.shape).view(rc.dtype), rc), name
+    chk, ref, _ = lm_parity(mw, X0, 6, 64, oracle_dtype=np.float32, quant=fmt)
+    _log(f"1.7B {fmt}: {chk.n} checks, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")

@@ -146,6 +146,13 @@ __device__ __forceinline__ uint2 ldg8(const void* p) {
   return *reinterpret_cast<const uint2*>(p);
 #endif
 }
+__device__ __forceinline__ uint32_t ldg4(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *(__attribute__((address_space(1))) const uint32_t*)(p);
+#else
+  return *reinterpret_cast<const uint32_t*>(p);
+#endif
+}
 __device__ __forceinline__ uint16_t ldg2(const uint16_t* p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   return *(__attribute__((address_space(1))) const uint16_t*)(p);
@@ -165,9 +172,31 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
 // Weight chunks of the GEMV: one load per lane per row and chunk, unpacked to
 // N floats.  Quantized formats unpack to code + OFF (unsigned, so each byte
 // converts in one instruction) and carry one fp16 scale per kQBlock weights;
-// the offset leaves once per chunk through the chunk's input sum.
+// the offset leaves once per chunk through the chunk's input sum.  Their
+// chunks are smaller than 16 bytes so that a matrix spreads over as many
+// waves as a bf16 one of the same shape.
 struct WQ8 {};   // int8 codes
 struct WQ4 {};   // 4-bit codes + 8: weight 2i in the low nibble of byte i, 2i+1 high
+
+// bytes of a quantized chunk (one load per lane per row): 16 weights either
+// way, so K / N <= 512 chunks and at most 4 per lane (measured: 8-byte int8
+// or 4-byte 4-bit chunks run no faster; 16-byte 4-bit chunks halve the lanes
+// a row spreads over and run 2x slower)
+constexpr int kQ8ChunkBytes = 16;
+constexpr int kQ4ChunkBytes = 8;
+
+template <int BYTES>
+__device__ __forceinline__ uint4 ldg_chunk(const char* p) {
+  if constexpr (BYTES == 16) {
+    return ldg16(p);
+  } else if constexpr (BYTES == 8) {
+    const uint2 v = ldg8(p);
+    return make_uint4(v.x, v.y, 0u, 0u);
+  } else {
+    static_assert(BYTES == 4, "4, 8 or 16-byte chunks");
+    return make_uint4(ldg4(p), 0u, 0u, 0u);
+  }
+}
 
 template <typename WT>
 struct WFmt {    // dense float32 / bf16
@@ -179,32 +208,30 @@ struct WFmt {    // dense float32 / bf16
 };
 template <>
 struct WFmt<WQ8> {
-  static constexpr int N = 16, BYTES = 16;
+  static constexpr int BYTES = kQ8ChunkBytes, N = BYTES;
   static constexpr bool Q = true;
   static constexpr float OFF = 128.f;
-  __device__ static __forceinline__ uint4 load(const char* p) { return ldg16(p); }
+  __device__ static __forceinline__ uint4 load(const char* p) { return ldg_chunk<BYTES>(p); }
   __device__ static __forceinline__ void unpack(const uint4& r, float* f) {
-    const uint32_t w[4] = {r.x ^ 0x80808080u, r.y ^ 0x80808080u, r.z ^ 0x80808080u,
-                           r.w ^ 0x80808080u};   // code + 128 in every byte
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < BYTES / 4; ++j) {
+      const uint32_t u = w[j] ^ 0x80808080u;   // code + 128 in every byte
 #pragma unroll
-      for (int b = 0; b < 4; ++b) f[4 * j + b] = (float)((w[j] >> (8 * b)) & 0xffu);
+      for (int b = 0; b < 4; ++b) f[4 * j + b] = (float)((u >> (8 * b)) & 0xffu);
+    }
   }
 };
 template <>
 struct WFmt<WQ4> {
-  static constexpr int N = 16, BYTES = 8;
+  static constexpr int BYTES = kQ4ChunkBytes, N = 2 * BYTES;
   static constexpr bool Q = true;
   static constexpr float OFF = 8.f;
-  __device__ static __forceinline__ uint4 load(const char* p) {
-    const uint2 v = ldg8(p);
-    return make_uint4(v.x, v.y, 0u, 0u);
-  }
+  __device__ static __forceinline__ uint4 load(const char* p) { return ldg_chunk<BYTES>(p); }
   __device__ static __forceinline__ void unpack(const uint4& r, float* f) {
-    const uint32_t w[2] = {r.x, r.y};
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < BYTES / 4; ++j) {
       const uint32_t lo = w[j] & 0x0f0f0f0fu, hi = (w[j] >> 4) & 0x0f0f0f0fu;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {

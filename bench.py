@@ -59,19 +59,32 @@ def kernel_hash() -> str:
                          "static void gemv_shape(", "static void gemv_dispatch_shape(", "hipError_t launch_gemv("))
 
 
-def weight_bytes(shape) -> int:
-    return shape.weight_elems(with_head=True) * (2 if shape.dtype == "bf16" else 4)
+# bytes per weight of the block-quantized formats: the code and 2 bytes of
+# fp16 scale per 32 weights
+QUANT_BPW = {"q8": 1.0 + 2.0 / 32, "q4": 0.5 + 2.0 / 32}
+
+
+def weight_bytes(shape, quant=None) -> int:
+    """Bytes of every matrix a step reads once: the layers' seven matrices
+    (block-quantized with ``quant``) and one LM head (in the stack dtype)."""
+    wb = 2 if shape.dtype == "bf16" else 4
+    if quant is None:
+        return shape.weight_elems(with_head=True) * wb
+    head = shape.vocab * shape.hidden
+    body = shape.weight_elems(with_head=True) - head
+    return int(body * QUANT_BPW[quant] + head * wb)
 
 
 def kv_row_bytes(shape) -> int:
     return 2 * shape.n_layers * shape.kv_dim * (2 if shape.kv_dtype == "bf16" else 4)
 
 
-def gateup_bytes(shape) -> int:
-    """Algorithmic bytes of one gate/up launch: both [F, h] matrices once,
-    the input row in and the [F] activation out (float32)."""
-    wb = 2 if shape.dtype == "bf16" else 4
-    return 2 * shape.ffn * shape.hidden * wb + 4 * shape.hidden + 4 * shape.ffn
+def gateup_bytes(shape, quant=None) -> int:
+    """Algorithmic bytes of one gate/up launch: both [F, h] matrices once
+    (codes and scales when quantized), the input row in and the [F]
+    activation out (float32)."""
+    wb = (2 if shape.dtype == "bf16" else 4) if quant is None else QUANT_BPW[quant]
+    return int(2 * shape.ffn * shape.hidden * wb) + 4 * shape.hidden + 4 * shape.ffn
 
 
 def oracle_model(mw, dtype):
@@ -174,6 +187,7 @@ def bench_lm(args, wl):
         caps.append(min(2 * caps[-1], wl.s_max))
     buckets = [dec.alloc_kv(c) for c in caps]
     dec.grow(0, caps[0], kv=buckets[0])
+    cur = dict(dec=dec, buckets=buckets)
     X0_d = torch.from_numpy(X0).cuda()
     z = torch.empty(s.vocab, device="cuda")
     y = torch.empty(s.hidden, device="cuda")
@@ -187,6 +201,7 @@ def bench_lm(args, wl):
         step graph (greedy, or the sampling defaults with the penalty),
         growing the bucket where the context reaches it; returns the seconds
         of the decode loop."""
+        dec, buckets = cur["dec"], cur["buckets"]
         dec.set_position(0, 0)
         if dec.position(0)[1] != caps[0]:
             dec.grow(0, caps[0], kv=buckets[0])
@@ -260,6 +275,31 @@ def bench_lm(args, wl):
         token_choice_us=time_choice(s.vocab),
     )
     dec.close()
+    # the same greedy run with the seven per-layer matrices block-quantized
+    # (int8 / 4-bit codes, fp16 scale per 32 weights, dequantized in the GEMV)
+    if s.dtype == "bf16":
+        out["quantized"] = {}
+        for fmt in ("q8", "q4"):
+            qdm = dv.DeviceModel(mw, quant=fmt)
+            qdec = dv.Decoder(qdm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max)
+            qbuckets = [qdec.alloc_kv(c) for c in caps]
+            qdec.grow(0, caps[0], kv=qbuckets[0])
+            cur.update(dec=qdec, buckets=qbuckets)
+            schedule(W)
+            dt_q = schedule(K)
+            qg = qdec.time_stage(B.ATD_STAGE_GATEUP, 0, 1, reps) / 1e6
+            qb = weight_bytes(s, fmt) + kv_row_bytes(s) * mean_ctx
+            log(f"timed {K} steps, {fmt} weights: {dt_q * 1e3:.1f} ms")
+            out["quantized"][fmt] = dict(
+                value=K / dt_q, unit="tokens/s", ms_per_step=dt_q * 1e3 / K,
+                weight_bytes_per_step=weight_bytes(s, fmt),
+                step_hbm=dict(algorithmic_bytes=qb, achieved_gbs=qb / (dt_q / K) / 1e9,
+                              frac=qb / (dt_q / K) / 1e9 / HBM_PEAK_GBS),
+                gate_up=dict(avg_launch_us=qg * 1e6, bytes_per_launch=gateup_bytes(s, fmt),
+                             achieved_gbs=gateup_bytes(s, fmt) / qg / 1e9))
+            qdec.close()
+            del qdec, qbuckets, qdm
+            torch.cuda.empty_cache()
     # the batched workload is the same stack (same weights) with a bf16 cache
     bwl = inputs.WORKLOADS["batched64"]
     import dataclasses

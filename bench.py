@@ -26,6 +26,10 @@ Also measured in the same run:
                 on the device by sample_topk inside the step graph.
   token_choice_us  microseconds per call of greedy_argmax and sample_topk on
                 one row of the vocabulary.
+  quantized     the same K greedy steps with the seven per-layer matrices
+                block-quantized by the library (int8 and 4-bit codes with one
+                fp16 scale per 32 weights): tokens/s, step bytes and the gate/up
+                kernel's GB/s.
 """
 
 from __future__ import annotations
@@ -45,6 +49,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "autoregressive_transformer_decode_amd", "csrc", "kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemv_talker1.7b_traffic.json")
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_split_batched64_traffic.json")
+QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemv_{}_talker1.7b_traffic.json")
 
 
 def log(msg):
@@ -237,9 +242,11 @@ def bench_lm(args, wl):
     dt = schedule(K)
     log(f"timed {K} steps: {dt * 1e3:.1f} ms (buckets {caps})")
     # the same run with the sampling defaults (graphs captured by a warmup)
-    schedule(K if len(caps) > 1 else min(W, K), sampled=True)
-    dt_s = schedule(K, sampled=True)
-    log(f"timed {K} sampled steps: {dt_s * 1e3:.1f} ms")
+    dt_s = None
+    if not args.no_sampled:
+        schedule(K if len(caps) > 1 else min(W, K), sampled=True)
+        dt_s = schedule(K, sampled=True)
+        log(f"timed {K} sampled steps: {dt_s * 1e3:.1f} ms")
 
     # roofline: the dominant kernel's launches, every layer's weights in turn
     # as in a step, timed with HIP events on this stream
@@ -269,10 +276,11 @@ def bench_lm(args, wl):
                       launches_timed=launches),
         step_hbm=dict(algorithmic_bytes=step_bytes, achieved_gbs=step_bytes / (ms_step / 1e3) / 1e9,
                       frac=step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS),
-        sampled=dict(value=K / dt_s, unit="tokens/s", ms_per_step=dt_s * 1e3 / K,
-                     settings=dict(zip(("top_k", "temperature", "top_p"), SAMPLING),
-                                   penalty=SAMPLING_PENALTY)),
-        token_choice_us=time_choice(s.vocab),
+        sampled=None if dt_s is None else dict(
+            value=K / dt_s, unit="tokens/s", ms_per_step=dt_s * 1e3 / K,
+            settings=dict(zip(("top_k", "temperature", "top_p"), SAMPLING),
+                          penalty=SAMPLING_PENALTY)),
+        token_choice_us=None if args.no_sampled else time_choice(s.vocab),
     )
     dec.close()
     # the same greedy run with the seven per-layer matrices block-quantized
@@ -296,7 +304,8 @@ def bench_lm(args, wl):
                 step_hbm=dict(algorithmic_bytes=qb, achieved_gbs=qb / (dt_q / K) / 1e9,
                               frac=qb / (dt_q / K) / 1e9 / HBM_PEAK_GBS),
                 gate_up=dict(avg_launch_us=qg * 1e6, bytes_per_launch=gateup_bytes(s, fmt),
-                             achieved_gbs=gateup_bytes(s, fmt) / qg / 1e9))
+                             achieved_gbs=gateup_bytes(s, fmt) / qg / 1e9,
+                             traffic=traffic_per_launch(QUANT_TRAFFIC_FILE.format(fmt))))
             qdec.close()
             del qdec, qbuckets, qdm
             torch.cuda.empty_cache()
@@ -559,6 +568,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the 64-stream leg of the default (1.7B) run")
+    ap.add_argument("--no-sampled", action="store_true",
+                    help="skip the sampled leg and the token-choice timing (counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 plain device copies of 256 MiB (counter calibration)")
     args = ap.parse_args()

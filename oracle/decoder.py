@@ -29,7 +29,9 @@ is unique under (value descending, index ascending); the temperature divides
 the logits inside the softmax; top-p keeps the shortest descending prefix
 whose probability reaches top_p; the draw inverts the cumulative distribution
 over the candidates in descending order with a uniform that the caller passes
-in.
+in.  Controls: suppressed tokens (and eos before min_new_tokens) are masked to
+-inf before the penalty; choosing eos stops the sequence, every later choice
+being eos.
 """
 
 from __future__ import annotations
@@ -432,18 +434,26 @@ def bucket_for(pos: int, capacity: int) -> int:
 
 def run_lm(model: Model, X0: np.ndarray, n_steps: int, s_init: int,
            forced: Optional[Sequence[int]] = None, head: int = 0,
-           rho: float = 1.0, on_step=None, sampling=None):
+           rho: float = 1.0, on_step=None, sampling=None, controls: Optional[Controls] = None):
     """Plain LM loop: prefill X0 (token 1 comes from its last row), then
     n_steps steps, step k consuming token k.  Buckets grow before a write at
     position == capacity.  With ``forced`` the fed tokens are taken from it
     (teacher forcing) instead of the chosen ones.  Choices are greedy, or
     with ``sampling`` = (k, temperature, top_p, u[n_steps + 1]) the choice
     after the prefill (index 0) and after step k draws with u[k].  Returns
-    per-step lists of (y, z, tok, margin), index 0 being the prefill."""
+    per-step lists of (y, z, tok, margin), index 0 being the prefill.  With
+    ``controls`` every choice goes through choose_controlled (the steps after
+    a stop still run, fed eos)."""
     cache = Cache(model, s_init)
     seen = np.zeros(model.heads[head].shape[0], bool) if rho != 1.0 else None
+
+    def pick(z, k):
+        if controls is None:
+            return choose(z, seen, rho, sampling, k)
+        return choose_controlled(z, seen, rho, controls, sampling, k)
+
     y, z = prefill(model, cache, X0, head)
-    tok, margin = choose(z, seen, rho, sampling, 0)
+    tok, margin = pick(z, 0)
     out = [(y, z, tok, margin)]
     if on_step:
         on_step(0, cache)
@@ -454,11 +464,53 @@ def run_lm(model: Model, X0: np.ndarray, n_steps: int, s_init: int,
             cache.grow(cap)
         x = embed(model, [fed], [0])
         y, z = step(model, cache, x, head)
-        tok, margin = choose(z, seen, rho, sampling, k)
+        tok, margin = pick(z, k)
         out.append((y, z, tok, margin))
         if on_step:
             on_step(k, cache)
     return out, cache
+
+
+class Controls:
+    """Generation controls of one sequence (ncnn port, Talker section: the
+    codes only matched once suppress and min_new_tokens were applied; ASR
+    report: decoding runs to EOS).  suppress: bool [V] of tokens never chosen
+    (or None); eos: end token or -1; min_new: choices with index below it
+    cannot be eos.  State: ``count`` choices made so far (the index of the
+    next one) and ``eos_step``, the index of the choice that gave eos (-1
+    before); after it every choice returns eos without touching ``seen``."""
+
+    def __init__(self, suppress=None, eos: int = -1, min_new: int = 0, first_index: int = 0):
+        self.suppress = suppress
+        self.eos = eos
+        self.min_new = min_new
+        self.count = first_index
+        self.eos_step = -1
+
+    def mask(self, z: np.ndarray) -> np.ndarray:
+        """Logits with the suppressed tokens (and eos before min_new) at -inf;
+        the penalty leaves -inf in place, so masking before it is the same."""
+        z = np.array(z, dtype=np.float32, copy=True)
+        if self.suppress is not None:
+            z[np.asarray(self.suppress, bool)] = -np.inf
+        if self.eos >= 0 and self.count < self.min_new:
+            z[self.eos] = -np.inf
+        return z
+
+
+def choose_controlled(z: np.ndarray, seen: Optional[np.ndarray], rho: float, ctl: Controls,
+                      sampling=None, i: int = 0) -> Tuple[int, float]:
+    """One choice under the controls: after a stop, eos; otherwise the greedy
+    or sampled choice (``choose``) on the masked logits, and a stop when it
+    is eos.  Returns (token, robustness)."""
+    if ctl.eos_step >= 0:
+        ctl.count += 1
+        return ctl.eos, math.inf
+    tok, r = choose(ctl.mask(z), seen, rho, sampling, i)
+    if ctl.eos >= 0 and tok == ctl.eos:
+        ctl.eos_step = ctl.count
+    ctl.count += 1
+    return tok, r
 
 
 def choose(z: np.ndarray, seen: Optional[np.ndarray], rho: float, sampling=None,

@@ -463,6 +463,42 @@ def check_sampling_frequencies():
             assert abs(hits.get(tok, 0) / n - p) <= 1.0 / n + 1e-6, (k, tok, hits.get(tok, 0) / n, p)
 
 
+# ---------------------------------------------------------------- generation controls
+
+def check_controls():
+    """A suppressed token is never chosen, even as the largest logit; eos is
+    masked until min_new choices were made; choosing eos stops the sequence:
+    later choices are eos and leave the seen set alone; without controls the
+    choice is the plain one."""
+    z = np.array([0.1, 3.0, 2.0, 2.5, -1.0], np.float32)
+    sup = np.array([False, True, False, False, False])
+    ctl = od.Controls(suppress=sup, eos=3, min_new=2)
+    seen = np.zeros(5, bool)
+    t0, _ = od.choose_controlled(z, seen, 1.0, ctl)      # 1 suppressed, eos masked -> 2
+    t1, _ = od.choose_controlled(z, seen, 1.0, ctl)      # still below min_new -> 2
+    t2, _ = od.choose_controlled(z, seen, 1.0, ctl)      # eos allowed: 2.5 > 2.0 -> 3, stop
+    assert (t0, t1, t2) == (2, 2, 3) and ctl.eos_step == 2
+    seen_before = seen.copy()
+    t3, _ = od.choose_controlled(np.array([9, 0, 0, 0, 0], np.float32), seen, 1.0, ctl)
+    assert t3 == 3 and np.array_equal(seen, seen_before) and ctl.count == 4
+    # the penalty still acts on the unmasked logits: 2.5 / 1.5 < 2.0 once 3 is seen
+    ctl2 = od.Controls(eos=-1)
+    seen2 = np.array([False, False, False, True, False])
+    t, _ = od.choose_controlled(np.array([0, 1.0, 2.0, 2.5, 0], np.float32), seen2, 1.5, ctl2)
+    assert t == 2
+    # sampled: the suppressed token has no mass
+    zs = np.log(np.array([1, 2, 3, 4], np.float32))
+    ctl3 = od.Controls(suppress=np.array([False, False, False, True]))
+    hits = {od.choose_controlled(zs, None, 1.0, od.Controls(suppress=ctl3.suppress),
+                                 (4, 1.0, 1.0, np.array([u])))[0]
+            for u in np.linspace(0.01, 0.99, 40)}
+    assert hits == {0, 1, 2}
+    # no controls: the plain choice
+    g, _ = od.penalized_argmax(z, None, 1.0)
+    t, _ = od.choose_controlled(z, None, 1.0, od.Controls())
+    assert t == g == 1
+
+
 # ---------------------------------------------------------------- block quantization
 
 def check_quant_closed_form():

@@ -223,7 +223,27 @@ def test_planted_quant_mistake_is_caught(name, monkeypatch):
     assert caught, f"no pin catches the planted mistake {name}"
 
 
+class _CtlEosAtMin(od.Controls):
+    def mask(self, z):
+        z = np.array(z, dtype=np.float32, copy=True)
+        if self.suppress is not None:
+            z[np.asarray(self.suppress, bool)] = -np.inf
+        if self.eos >= 0 and self.count < self.min_new - 1:
+            z[self.eos] = -np.inf
+        return z
+
+
+def _choose_no_stop(z, seen, rho, ctl, sampling=None, i=0):
+    tok, r = od.choose(ctl.mask(z), seen, rho, sampling, i)
+    if ctl.eos >= 0 and tok == ctl.eos and ctl.eos_step < 0:
+        ctl.eos_step = ctl.count
+    ctl.count += 1
+    return tok, r
+
+
 MUTATIONS = {
+    "controls_eos_one_early": ("Controls", _CtlEosAtMin),
+    "controls_no_stop": ("choose_controlled", _choose_no_stop),
     "sample_walks_ascending": ("sampling_distribution", _dist_ascending),
     "sample_temperature_multiplies": ("sampling_distribution", _dist_temp_multiplies),
     "sample_top_p_ignored": ("sampling_distribution", _dist_top_p_ignored),

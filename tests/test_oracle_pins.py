@@ -30,6 +30,7 @@ PINS = [
     pins.check_sampling_ties_and_penalty,
     pins.check_sampling_greedy_limit,
     pins.check_sampling_frequencies,
+    pins.check_controls,
     pins.check_quant_closed_form,
     pins.check_quant_error_bound,
     pins.check_quant_bytes_golden,

@@ -70,6 +70,11 @@ class atd_sampling(C.Structure):
                 ("uniforms", C.c_void_p)]
 
 
+class atd_controls(C.Structure):
+    _fields_ = [("suppress", C.c_void_p), ("eos", C.c_int32), ("min_new_tokens", C.c_int32),
+                ("first_index", C.c_int32), ("eos_step", C.c_void_p)]
+
+
 class atd_layer_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "attn_norm", "wq", "wk", "wv", "bq", "bk", "bv", "q_norm", "k_norm", "wo",
@@ -100,13 +105,15 @@ def _load():
         "decoder_prefill": ([vp, i32, vp, i32, i32, vp, vp, vp], C.c_int),
         "decoder_step": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, vp, vp], C.c_int),
         "decoder_embed": ([vp, i32, vp, i32, C.POINTER(i32), vp, vp, vp], C.c_int),
-        "greedy_argmax": ([vp, i32, i32, vp, f32, vp, vp, vp], C.c_int),
-        "sample_topk": ([vp, i32, i32, vp, f32, C.POINTER(atd_sampling), vp, vp], C.c_int),
+        "greedy_argmax": ([vp, i32, i32, vp, f32, C.POINTER(atd_controls), vp, vp, vp], C.c_int),
+        "sample_topk": ([vp, i32, i32, vp, f32, C.POINTER(atd_sampling), C.POINTER(atd_controls),
+                         vp, vp], C.c_int),
         "decoder_generate": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, f32,
-                              C.POINTER(atd_sampling), vp, vp, vp, vp], C.c_int),
+                              C.POINTER(atd_sampling), C.POINTER(atd_controls), vp, vp, vp, vp],
+                             C.c_int),
         "talker_generate_frames": ([vp, i32, vp, i32, i32, vp, vp, vp, vp, f32,
-                                    C.POINTER(atd_sampling), C.POINTER(atd_sampling), vp, vp, vp,
-                                    vp], C.c_int),
+                                    C.POINTER(atd_sampling), C.POINTER(atd_sampling),
+                                    C.POINTER(atd_controls), vp, vp, vp, vp], C.c_int),
         "quantize_blocks": ([vp, i32, C.c_int64, i32, i32, vp, vp, vp], C.c_int),
         "decoder_time_stage": ([vp, i32, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
     }
@@ -185,35 +192,37 @@ def decoder_embed(handle: int, B: int, tok, G: int, table_ids, extra, x_out: int
 
 
 def greedy_argmax(logits: int, B: int, V: int, seen, penalty: float, tok_out: int, margin_out,
-                  stream: int) -> None:
-    _check(lib.greedy_argmax(logits, B, V, seen, penalty, tok_out, margin_out, stream))
+                  stream: int, controls=None) -> None:
+    _check(lib.greedy_argmax(logits, B, V, seen, penalty, _byref(controls), tok_out, margin_out,
+                             stream))
 
 
-def _sampling(sp):
-    """None, or an atd_sampling passed by reference."""
-    return None if sp is None else C.byref(sp)
+def _byref(st):
+    """None, or a ctypes struct passed by reference."""
+    return None if st is None else C.byref(st)
 
 
 def sample_topk(logits: int, B: int, V: int, seen, penalty: float, sampling: atd_sampling,
-                tok_out: int, stream: int) -> None:
-    _check(lib.sample_topk(logits, B, V, seen, penalty, C.byref(sampling), tok_out, stream))
+                tok_out: int, stream: int, controls=None) -> None:
+    _check(lib.sample_topk(logits, B, V, seen, penalty, C.byref(sampling), _byref(controls),
+                           tok_out, stream))
 
 
 def decoder_generate(handle: int, slot: int, n_steps: int, tok_io: int, G: int, table_ids,
                      extra, head: int, seen, penalty: float, sampling, tokens_out, y_out,
-                     logits_out: int, stream: int) -> None:
+                     logits_out: int, stream: int, controls=None) -> None:
     _check(lib.decoder_generate(handle, slot, n_steps, tok_io, G, _i32_array(list(table_ids)),
-                                extra, head, seen, penalty, _sampling(sampling), tokens_out,
-                                y_out, logits_out, stream), handle)
+                                extra, head, seen, penalty, _byref(sampling), _byref(controls),
+                                tokens_out, y_out, logits_out, stream), handle)
 
 
 def talker_generate_frames(tk: int, tk_slot: int, cp: int, cp_slot: int, n_frames: int,
                            codes_io: int, y_io: int, text, seen: int, penalty: float,
                            tk_sampling, cp_sampling, codes_out, tk_logits: int, cp_logits: int,
-                           stream: int) -> None:
+                           stream: int, tk_controls=None) -> None:
     _check(lib.talker_generate_frames(tk, tk_slot, cp, cp_slot, n_frames, codes_io, y_io, text,
-                                      seen, penalty, _sampling(tk_sampling),
-                                      _sampling(cp_sampling), codes_out, tk_logits, cp_logits,
+                                      seen, penalty, _byref(tk_sampling), _byref(cp_sampling),
+                                      _byref(tk_controls), codes_out, tk_logits, cp_logits,
                                       stream), tk)
 
 

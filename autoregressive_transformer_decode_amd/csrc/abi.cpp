@@ -43,6 +43,7 @@ struct atd_decoder {
   float* mss = nullptr;        // row sums of squares [kMmaRows, ceil(h / kSsCols)]
   uint16_t *mhi = nullptr, *mlo = nullptr;  // GEMM input as bf16 hi/lo [kMmaRows, Kmax]
   int32_t* counter = nullptr;  // token counter of decoder_generate
+  int32_t* ctl_base = nullptr; // first choice index of a controlled generate call
   size_t part_floats = 0;      // capacity of pacc in floats / D
   bool dry = false;  // ATD_FLAG_DRY_RUN: host state only, no HIP calls
   // stage timing (decoder_time_stage): layers to enqueue, -1 = all
@@ -665,7 +666,7 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   const size_t o_cap = carve((size_t)S * 4);
   const int nblk_v = (cfg->vocab + kArgmaxChunk - 1) / kArgmaxChunk;
   const size_t o_part = carve((size_t)R * nblk_v * 3 * 4);
-  const size_t o_cnt = carve(4);
+  const size_t o_cnt = carve(8);
   const int nblk_s = sample_blocks(cfg->vocab);
   const size_t o_samp = carve(nblk_s > 1 ? (size_t)nblk_s * kTopKMax * sizeof(uint2) : 0);
   // MFMA path: hi/lo activations of one 64-row chunk and split-K partials of
@@ -707,6 +708,7 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->slot_cap = (int*)(base + o_cap);
   d->part = (float*)(base + o_part);
   d->counter = (int32_t*)(base + o_cnt);
+  d->ctl_base = d->counter + 1;
   d->samp = (uint2*)(base + o_samp);
   if (d->mma) {
     d->mss = (float*)(base + o_mss);
@@ -1004,15 +1006,59 @@ SampleArgs sample_args(const float* z, int B, int V, uint32_t* seen, float penal
 }
 }  // namespace
 
+namespace {
+// Validates generation controls for rows of V tokens (d may be NULL).
+int check_controls(atd_decoder* d, const atd_controls* c, int V) {
+  if (c->eos < -1 || c->eos >= V)
+    return fail(d, ATD_ERR_INVALID_ARG, "eos %d outside [-1, %d)", c->eos, V);
+  if (c->min_new_tokens < 0 || c->first_index < 0)
+    return fail(d, ATD_ERR_INVALID_ARG, "min_new_tokens %d or first_index %d is negative",
+                c->min_new_tokens, c->first_index);
+  if (((uintptr_t)c->suppress & 3) || ((uintptr_t)c->eos_step & 3))
+    return fail(d, ATD_ERR_INVALID_ARG, "suppress %p or eos_step %p not 4-byte aligned",
+                (const void*)c->suppress, (void*)c->eos_step);
+  return ATD_OK;
+}
+
+ChoiceCtl choice_ctl(const atd_controls* c, const int32_t* base, const int32_t* ctr) {
+  ChoiceCtl k{};
+  if (!c) return k;
+  k.suppress = c->suppress;
+  k.eos = c->eos;
+  k.min_new = c->min_new_tokens;
+  k.step0 = base ? 0 : c->first_index;
+  k.step_base = base;
+  k.step_ctr = ctr;
+  k.eos_step = c->eos >= 0 ? c->eos_step : nullptr;
+  return k;
+}
+
+// Controls as graph-key entries (first_index is read from the device).
+void key_controls(std::vector<int64_t>& key, const atd_controls* c) {
+  if (!c) {
+    key.push_back(0);
+    return;
+  }
+  key.insert(key.end(), {1, (int64_t)(uintptr_t)c->suppress, c->eos, c->min_new_tokens,
+                         (int64_t)(uintptr_t)c->eos_step});
+}
+}  // namespace
+
 extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
-                             float penalty, int32_t* tok_out, float* margin_out, void* stream) {
+                             float penalty, const atd_controls* controls, int32_t* tok_out,
+                             float* margin_out, void* stream) {
   if (!logits || !tok_out) return fail(nullptr, ATD_ERR_INVALID_ARG, "logits or tok_out is NULL");
   if (B < 1) return fail(nullptr, ATD_ERR_INVALID_ARG, "B = %d < 1", B);
   if (V < 2) return fail(nullptr, ATD_ERR_INVALID_ARG, "V = %d < 2", V);
   if (!(penalty > 0.0f) || !std::isfinite(penalty))
     return fail(nullptr, ATD_ERR_INVALID_ARG, "penalty %g is not a positive number",
                 (double)penalty);
+  if (controls) {
+    const int rc = check_controls(nullptr, controls, V);
+    if (rc) return rc;
+  }
   ArgmaxArgs a{};
+  a.ctl = choice_ctl(controls, nullptr, nullptr);
   a.z = logits;
   a.B = B;
   a.V = V;
@@ -1031,8 +1077,8 @@ extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t
 }
 
 extern "C" int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* seen,
-                           float penalty, const atd_sampling* sampling, int32_t* tok_out,
-                           void* stream) {
+                           float penalty, const atd_sampling* sampling,
+                           const atd_controls* controls, int32_t* tok_out, void* stream) {
   if (!logits || !tok_out || !sampling)
     return fail(nullptr, ATD_ERR_INVALID_ARG, "logits, sampling or tok_out is NULL");
   if (B < 1) return fail(nullptr, ATD_ERR_INVALID_ARG, "B = %d < 1", B);
@@ -1042,7 +1088,9 @@ extern "C" int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* 
                 (double)penalty);
   int rc = check_sampling(nullptr, sampling, V);
   if (rc) return rc;
+  if (controls && (rc = check_controls(nullptr, controls, V)) != ATD_OK) return rc;
   SampleArgs a = sample_args(logits, B, V, seen, penalty, *sampling, tok_out, nullptr);
+  a.ctl = choice_ctl(controls, nullptr, nullptr);
   if (a.nblk > 1) {
     void* p = nullptr;
     rc = choice_scratch((size_t)B * a.nblk * a.k * sizeof(uint2), &p);
@@ -1133,10 +1181,11 @@ void key_sampling(std::vector<int64_t>& key, const atd_sampling* sp) {
 // u = sp->uniforms[u_off + (*u_row) * u_stride].
 hipError_t enqueue_choice(atd_decoder* d, const float* z, uint32_t* seen, float penalty,
                           const atd_sampling* sp, const int32_t* u_row, int u_stride, int u_off,
-                          int32_t* tok, hipStream_t s) {
+                          int32_t* tok, hipStream_t s, const ChoiceCtl& ctl = ChoiceCtl{}) {
   const int V = d->cfg.vocab;
   if (!sp) {
     ArgmaxArgs a{};
+    a.ctl = ctl;
     a.z = z;
     a.B = 1;
     a.V = V;
@@ -1150,6 +1199,7 @@ hipError_t enqueue_choice(atd_decoder* d, const float* z, uint32_t* seen, float 
     return launch_argmax(a, s);
   }
   SampleArgs a = sample_args(z, 1, V, seen, penalty, *sp, tok, d->samp);
+  a.ctl = ctl;
   a.u = sp->uniforms + u_off;
   a.u_row = u_row;
   a.u_stride = u_stride;
@@ -1161,8 +1211,9 @@ hipError_t enqueue_choice(atd_decoder* d, const float* z, uint32_t* seen, float 
 extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, int32_t* tok_io,
                                 int32_t G, const int32_t* table_ids, const float* extra,
                                 int32_t head, uint32_t* seen, float penalty,
-                                const atd_sampling* sampling, int32_t* tokens_out, float* y_out,
-                                float* logits_out, void* stream) {
+                                const atd_sampling* sampling, const atd_controls* controls,
+                                int32_t* tokens_out, float* y_out, float* logits_out,
+                                void* stream) {
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
   const atd_config& c = d->cfg;
   if (slot < 0 || slot >= c.max_slots)
@@ -1181,6 +1232,7 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
   if (!(penalty > 0.0f) || !std::isfinite(penalty))
     return fail(d, ATD_ERR_INVALID_ARG, "penalty %g is not a positive number", (double)penalty);
   if (sampling && (rc = check_sampling(d, sampling, c.vocab)) != ATD_OK) return rc;
+  if (controls && (rc = check_controls(d, controls, c.vocab)) != ATD_OK) return rc;
   if ((int64_t)d->pos[slot] + n_steps > d->cap[slot])
     return fail(d, ATD_ERR_KV_FULL, "slot %d: %d steps from position %d exceed capacity %d",
                 slot, n_steps, d->pos[slot], d->cap[slot]);
@@ -1202,7 +1254,9 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
   key.push_back(float_bits(penalty));
   for (int g = 0; g < G; ++g) key.push_back(table_ids[g]);
   key_sampling(key, sampling);
-  const bool count = tokens_out || sampling;   // the step index lives in d->counter
+  key_controls(key, controls);
+  // the step index lives in d->counter
+  const bool count = tokens_out || sampling || controls;
   hipGraphExec_t exec = nullptr;
   for (auto& ge : d->graphs)
     if (ge.key == key) exec = ge.exec;
@@ -1218,7 +1272,8 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
     hipError_t le = enqueue_step(d, slot, 1, tok_io, G, table_ids, extra, head, y_out, logits_out,
                                  max_cap, cs);
     if (le == hipSuccess)
-      le = enqueue_choice(d, logits_out, seen, penalty, sampling, d->counter, 1, 0, tok_io, cs);
+      le = enqueue_choice(d, logits_out, seen, penalty, sampling, d->counter, 1, 0, tok_io, cs,
+                          choice_ctl(controls, d->ctl_base, d->counter));
     if (le == hipSuccess && count) le = launch_record_token(tok_io, tokens_out, d->counter, cs);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
@@ -1233,6 +1288,7 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
     if (e != hipSuccess) return hip_fail(d, e, "graph cache");
   }
   if (count) e = launch_fill_i32(d->counter, 1, 0, s);
+  if (controls && e == hipSuccess) e = launch_fill_i32(d->ctl_base, 1, controls->first_index, s);
   for (int k = 0; k < n_steps && e == hipSuccess; ++k) e = hipGraphLaunch(exec, s);
   if (e != hipSuccess) return hip_fail(d, e, "decoder_generate replay");
   d->pos[slot] += n_steps;
@@ -1282,7 +1338,8 @@ hipError_t enqueue_cp_pass(atd_decoder* cp, int cp_slot, int32_t* codes, const f
 // u = sp->uniforms[*counter]).
 hipError_t enqueue_talker_step(atd_decoder* tk, int tk_slot, int32_t* codes, const float* text,
                                int32_t* counter, uint32_t* seen, float penalty,
-                               const atd_sampling* sp, float* y, float* tk_logits, hipStream_t s) {
+                               const atd_sampling* sp, const atd_controls* ctl, float* y,
+                               float* tk_logits, hipStream_t s) {
   const atd_config& c = tk->cfg;
   int32_t tabs[kCodeGroups];
   for (int g = 0; g < kCodeGroups; ++g) tabs[g] = g;
@@ -1294,7 +1351,9 @@ hipError_t enqueue_talker_step(atd_decoder* tk, int tk_slot, int32_t* codes, con
   const int max_cap = std::min(tk->cap[tk_slot], c.max_ctx);
   if (e == hipSuccess) e = run_layers(tk, rows, 1, max_cap, tk->x, &ho, s);
   if (e == hipSuccess) e = launch_advance(slots_of(tk), rows, 1, s);
-  if (e == hipSuccess) e = enqueue_choice(tk, tk_logits, seen, penalty, sp, counter, 1, 0, codes, s);
+  if (e == hipSuccess)
+    e = enqueue_choice(tk, tk_logits, seen, penalty, sp, counter, 1, 0, codes, s,
+                       choice_ctl(ctl, tk->ctl_base, counter));
   return e;
 }
 
@@ -1304,7 +1363,8 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
                                       int32_t cp_slot, int32_t n_frames, int32_t* codes_io,
                                       float* y_io, const float* text, uint32_t* seen,
                                       float penalty, const atd_sampling* tk_sampling,
-                                      const atd_sampling* cp_sampling, int32_t* codes_out,
+                                      const atd_sampling* cp_sampling,
+                                      const atd_controls* tk_controls, int32_t* codes_out,
                                       float* tk_logits, float* cp_logits, void* stream) {
   if (!tk) return fail(nullptr, ATD_ERR_INVALID_ARG, "Talker decoder is NULL");
   if (!cp || cp == tk) return fail(tk, ATD_ERR_INVALID_ARG, "Code Predictor decoder is NULL or the Talker's");
@@ -1342,6 +1402,7 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
   int rc = ATD_OK;
   if (tk_sampling && (rc = check_sampling(tk, tk_sampling, tc.vocab)) != ATD_OK) return rc;
   if (cp_sampling && (rc = check_sampling(tk, cp_sampling, cc.vocab)) != ATD_OK) return rc;
+  if (tk_controls && (rc = check_controls(tk, tk_controls, tc.vocab)) != ATD_OK) return rc;
   if (tk->dry) {
     tk->pos[tk_slot] += steps;
     cp->pos[cp_slot] = kCodeGroups;
@@ -1361,6 +1422,7 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
                                 bucket_key(cp, cp_slot)};
     key_sampling(key, tk_sampling);
     key_sampling(key, cp_sampling);
+    key_controls(key, tk_controls);
     for (auto& ge : tk->graphs)
       if (ge.key == key) {
         *out = ge.exec;
@@ -1377,7 +1439,7 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
     hipError_t le = hipSuccess;
     if (full)
       le = enqueue_talker_step(tk, tk_slot, codes_io, text, tk->counter, seen, penalty,
-                               tk_sampling, y_io, tk_logits, cs);
+                               tk_sampling, tk_controls, y_io, tk_logits, cs);
     if (le == hipSuccess)
       le = enqueue_cp_pass(cp, cp_slot, codes_io, y_io, cp_logits, codes_out, tk->counter,
                            cp_sampling, cs);
@@ -1401,6 +1463,8 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
   if (e == hipSuccess && steps > 0) e = graph_for(1, &rest);
   if (e != hipSuccess) return hip_fail(tk, e, "capture of the frame loop");
   e = launch_fill_i32(tk->counter, 1, 0, s);
+  if (tk_controls && e == hipSuccess)
+    e = launch_fill_i32(tk->ctl_base, 1, tk_controls->first_index, s);
   if (e == hipSuccess) e = hipGraphLaunch(first, s);
   for (int f = 1; f < n_frames && e == hipSuccess; ++f) e = hipGraphLaunch(rest, s);
   if (e != hipSuccess) return hip_fail(tk, e, "talker_generate_frames replay");

@@ -150,6 +150,20 @@ struct EmbedArgs {
   int h, M;
 };
 
+// Generation controls of a token choice: suppressed tokens, and eos while the
+// choice index is below min_new, read as -inf; a stopped row (eos_step >= 0)
+// returns eos.  The choice index is step0 + *step_base + *step_ctr (either
+// pointer may be null).
+struct ChoiceCtl {
+  const uint32_t* suppress = nullptr;   // [B, nwords] or null
+  int eos = -1;
+  int min_new = 0;
+  int step0 = 0;
+  const int32_t* step_base = nullptr;   // device value added to step0, or null
+  const int32_t* step_ctr = nullptr;    // device counter added too, or null
+  int32_t* eos_step = nullptr;          // [B] or null (no stop)
+};
+
 struct ArgmaxArgs {
   const float* z;      // [B, V]
   int B, V;
@@ -160,6 +174,7 @@ struct ArgmaxArgs {
   float* margin;
   float* part;         // [B, nblk, 3]
   int nblk;
+  ChoiceCtl ctl;
 };
 
 // top-k sampling: one 1024-thread workgroup selects from up to kSampleChunk
@@ -187,6 +202,7 @@ struct SampleArgs {
   int32_t* tok;          // [B]
   uint2* part;           // [B, nblk, k] candidates (order key, index) when nblk > 1
   int nblk;              // sample_blocks(V)
+  ChoiceCtl ctl;
 };
 
 struct KvCopyArgs {

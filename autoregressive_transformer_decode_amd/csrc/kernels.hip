@@ -1134,6 +1134,30 @@ __global__ __launch_bounds__(256) void k_kv_copy(KvCopyArgs a) {
     dst[i] = src[i];
 }
 
+// ------------------------------------------------------------------ token choice controls
+__device__ __forceinline__ int ctl_step(const ChoiceCtl& c) {
+  return c.step0 + (c.step_base ? *c.step_base : 0) + (c.step_ctr ? *c.step_ctr : 0);
+}
+// true when token i of the row may not be chosen
+__device__ __forceinline__ bool ctl_masked(const ChoiceCtl& c, const uint32_t* sup_row, int i,
+                                           bool eos_blocked) {
+  return (sup_row && ((sup_row[i >> 5] >> (i & 31)) & 1u)) || (eos_blocked && i == c.eos);
+}
+// The row's final token: eos once stopped (stopped = true: the seen set is
+// left alone), and the stop recorded when the choice is eos.
+__device__ __forceinline__ int ctl_finish(const ChoiceCtl& c, int b, int tok, int step,
+                                          bool& stopped) {
+  stopped = false;
+  if (c.eos_step) {
+    if (c.eos_step[b] >= 0) {
+      stopped = true;
+      return c.eos;
+    }
+    if (tok == c.eos) c.eos_step[b] = step;
+  }
+  return tok;
+}
+
 // ------------------------------------------------------------------ argmax
 struct Top2 {
   float v1, v2;
@@ -1172,9 +1196,13 @@ __global__ __launch_bounds__(256) void k_argmax_part(ArgmaxArgs a) {
   const int lo = blk * kArgmaxChunk, hi = min(a.V, lo + kArgmaxChunk);
   const float* z = a.z + (size_t)b * a.V;
   const uint32_t* seen = a.seen ? a.seen + (size_t)b * a.nwords : nullptr;
+  const uint32_t* sup = a.ctl.suppress ? a.ctl.suppress + (size_t)b * a.nwords : nullptr;
+  const int step = ctl_step(a.ctl);
+  const bool eos_blocked = a.ctl.eos >= 0 && step < a.ctl.min_new;
   Top2 t{-INFINITY, -INFINITY, 0x7fffffff};
   for (int i = lo + tid; i < hi; i += 256) {
     float v = z[i];
+    if (ctl_masked(a.ctl, sup, i, eos_blocked)) v = -INFINITY;
     if (seen && ((seen[i >> 5] >> (i & 31)) & 1u)) v = v > 0.f ? v / a.penalty : v * a.penalty;
     if (v > t.v1) {
       t.v2 = t.v1;
@@ -1191,9 +1219,11 @@ __global__ __launch_bounds__(256) void k_argmax_part(ArgmaxArgs a) {
     Top2 r = st[0];
     for (int w = 1; w < 4; ++w) r = top2_merge(r, st[w]);
     if (a.nblk == 1) {   // one block: this is the final result (k_argmax_final is skipped)
-      a.tok[b] = r.i1;
+      bool stopped;
+      const int tok = ctl_finish(a.ctl, b, min(r.i1, a.V - 1), step, stopped);
+      a.tok[b] = tok;
       if (a.margin) a.margin[b] = r.v1 - r.v2;
-      if (a.seen) a.seen[(size_t)b * a.nwords + (r.i1 >> 5)] |= 1u << (r.i1 & 31);
+      if (a.seen && !stopped) a.seen[(size_t)b * a.nwords + (tok >> 5)] |= 1u << (tok & 31);
       return;
     }
     float* p = a.part + ((size_t)b * a.nblk + blk) * 3;
@@ -1212,9 +1242,11 @@ __global__ __launch_bounds__(64) void k_argmax_final(ArgmaxArgs a) {
   }
   t = wave_top2(t);
   if (lane == 0) {
-    a.tok[b] = t.i1;
+    bool stopped;
+    const int tok = ctl_finish(a.ctl, b, min(t.i1, a.V - 1), ctl_step(a.ctl), stopped);
+    a.tok[b] = tok;
     if (a.margin) a.margin[b] = t.v1 - t.v2;
-    if (a.seen) a.seen[(size_t)b * a.nwords + (t.i1 >> 5)] |= 1u << (t.i1 & 31);
+    if (a.seen && !stopped) a.seen[(size_t)b * a.nwords + (tok >> 5)] |= 1u << (tok & 31);
   }
 }
 
@@ -1354,6 +1386,8 @@ __device__ __forceinline__ void load_logit_keys(const SampleArgs& a, int b, int 
   const int i0 = threadIdx.x * e;
   const float* z = a.z + (size_t)b * a.V + lo;
   const uint32_t* seen = a.seen ? a.seen + (size_t)b * a.nwords : nullptr;
+  const uint32_t* sup = a.ctl.suppress ? a.ctl.suppress + (size_t)b * a.nwords : nullptr;
+  const bool eos_blocked = a.ctl.eos >= 0 && ctl_step(a.ctl) < a.ctl.min_new;
 #pragma unroll
   for (int j = 0; j < kSamplePerThread; ++j) {
     key[j] = 0u;
@@ -1362,6 +1396,7 @@ __device__ __forceinline__ void load_logit_keys(const SampleArgs& a, int b, int 
     if (j < e && i < n) {
       float v = z[i];
       const int g = lo + i;
+      if (ctl_masked(a.ctl, sup, g, eos_blocked)) v = -INFINITY;
       if (seen && ((seen[g >> 5] >> (g & 31)) & 1u)) v = v > 0.f ? v / a.penalty : v * a.penalty;
       key[j] = order_key(v);
       idx[j] = (uint32_t)g;
@@ -1546,9 +1581,10 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample_final(SampleArgs a) {
     pos = Lq * 4 + __builtin_amdgcn_readlane(qd, Lq);
   }
   if (lane == 0) {
-    const int tok = (int)sorted[pos].y;
+    bool stopped;
+    const int tok = ctl_finish(a.ctl, b, min((int)sorted[pos].y, a.V - 1), ctl_step(a.ctl), stopped);
     a.tok[b] = tok;
-    if (a.seen) a.seen[(size_t)b * a.nwords + (tok >> 5)] |= 1u << (tok & 31);
+    if (a.seen && !stopped) a.seen[(size_t)b * a.nwords + (tok >> 5)] |= 1u << (tok & 31);
   }
 }
 

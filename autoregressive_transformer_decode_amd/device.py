@@ -210,16 +210,17 @@ class Decoder:
                  seen: Optional[torch.Tensor] = None, penalty: float = 1.0,
                  tokens_out: Optional[torch.Tensor] = None, y_out: Optional[torch.Tensor] = None,
                  logits_out: Optional[torch.Tensor] = None,
-                 sampling: Optional["Sampling"] = None):
+                 sampling: Optional["Sampling"] = None, controls: Optional["Controls"] = None):
         """n_steps steps on the device (graph-replayed step + token choice):
-        greedy, or sampled with ``sampling`` (its uniforms: one per step)."""
+        greedy, or sampled with ``sampling`` (its uniforms: one per step);
+        ``controls``: suppress / eos / min_new_tokens / stop."""
         if logits_out is None:
             logits_out = torch.empty(self.shape.vocab, device="cuda", dtype=torch.float32)
         ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         B.decoder_generate(self.handle, slot, n_steps, tok_io.data_ptr(), len(table_ids),
                            table_ids, ptr(extra), head, ptr(seen), float(penalty),
                            _c_sampling(sampling), ptr(tokens_out), ptr(y_out),
-                           logits_out.data_ptr(), _stream())
+                           logits_out.data_ptr(), _stream(), controls=_c_controls(controls))
         return logits_out
 
     def time_stage(self, stage: int, slot0: int = 0, nrows: int = 1, reps: int = 8) -> float:
@@ -240,7 +241,8 @@ def talker_frames(tk: "Decoder", cp: "Decoder", n_frames: int, codes_io: torch.T
                   penalty: float, codes_out: Optional[torch.Tensor] = None,
                   tk_logits: Optional[torch.Tensor] = None, cp_logits: Optional[torch.Tensor] = None,
                   tk_slot: int = 0, cp_slot: int = 0, tk_sampling: Optional["Sampling"] = None,
-                  cp_sampling: Optional["Sampling"] = None):
+                  cp_sampling: Optional["Sampling"] = None,
+                  tk_controls: Optional["Controls"] = None):
     """n_frames frames of the Talker / Code Predictor loop on the device
     (talker_generate_frames); greedy, or sampled with tk_sampling (uniforms
     [n_frames]) / cp_sampling (uniforms [n_frames, 15]); returns (tk_logits,
@@ -253,7 +255,8 @@ def talker_frames(tk: "Decoder", cp: "Decoder", n_frames: int, codes_io: torch.T
     B.talker_generate_frames(tk.handle, tk_slot, cp.handle, cp_slot, n_frames, codes_io.data_ptr(),
                              y_io.data_ptr(), ptr(text), seen.data_ptr(), float(penalty),
                              _c_sampling(tk_sampling), _c_sampling(cp_sampling), ptr(codes_out),
-                             tk_logits.data_ptr(), cp_logits.data_ptr(), _stream())
+                             tk_logits.data_ptr(), cp_logits.data_ptr(), _stream(),
+                             tk_controls=_c_controls(tk_controls))
     return tk_logits, cp_logits
 
 
@@ -275,21 +278,44 @@ def _c_sampling(sp: Optional[Sampling]):
 
 
 def sample_topk(logits: torch.Tensor, seen: Optional[torch.Tensor], penalty: float,
-                sampling: Sampling, tok_out: torch.Tensor):
+                sampling: Sampling, tok_out: torch.Tensor, controls: Optional["Controls"] = None):
     """Sampled token per row of logits ([V] or [B, V]); row b draws
     sampling.uniforms[b]."""
     Bn, V = (1, logits.shape[0]) if logits.dim() == 1 else logits.shape
     B.sample_topk(logits.data_ptr(), Bn, V, seen.data_ptr() if seen is not None else None,
-                  float(penalty), _c_sampling(sampling), tok_out.data_ptr(), _stream())
+                  float(penalty), _c_sampling(sampling), tok_out.data_ptr(), _stream(),
+                  controls=_c_controls(controls))
     return tok_out
 
 
+@dataclasses.dataclass
+class Controls:
+    """Generation controls (atd_controls): suppress bits (device int32
+    [B, ceil(V/32)] or None), eos (-1: none), min_new_tokens, first_index,
+    eos_step (device int32 [B], -1 while running, or None)."""
+    suppress: Optional[torch.Tensor] = None
+    eos: int = -1
+    min_new_tokens: int = 0
+    first_index: int = 0
+    eos_step: Optional[torch.Tensor] = None
+
+
+def _c_controls(c: Optional[Controls]):
+    if c is None:
+        return None
+    return B.atd_controls(c.suppress.data_ptr() if c.suppress is not None else None, int(c.eos),
+                          int(c.min_new_tokens), int(c.first_index),
+                          c.eos_step.data_ptr() if c.eos_step is not None else None)
+
+
 def greedy_argmax(logits: torch.Tensor, seen: Optional[torch.Tensor], penalty: float,
-                  tok_out: torch.Tensor, margin_out: Optional[torch.Tensor] = None):
+                  tok_out: torch.Tensor, margin_out: Optional[torch.Tensor] = None,
+                  controls: Optional[Controls] = None):
     Bn, V = (1, logits.shape[0]) if logits.dim() == 1 else logits.shape
     B.greedy_argmax(logits.data_ptr(), Bn, V, seen.data_ptr() if seen is not None else None,
                     float(penalty), tok_out.data_ptr(),
-                    margin_out.data_ptr() if margin_out is not None else None, _stream())
+                    margin_out.data_ptr() if margin_out is not None else None, _stream(),
+                    controls=_c_controls(controls))
     return tok_out
 
 

@@ -193,6 +193,30 @@ typedef struct atd_sampling {
 
 #define ATD_TOPK_MAX 256
 
+/* Generation controls of the token choices of a sequence ("Qwen3-TTS ncnn
+ * port", Talker section: the codes only matched the reference once suppress
+ * and min_new_tokens were applied; Audio8-ASR report: decoding runs to EOS).
+ * Each choice has an index in its sequence (stated by the call).
+ *   suppress        device uint32 bits [B, ceil(V/32)] (bit t of row b = word
+ *                   t/32, bit t%32): tokens that are never chosen; or NULL.
+ *   eos             the end token, or -1 (then nothing below applies).
+ *   min_new_tokens  choices with index < min_new_tokens cannot return eos.
+ *   first_index     index of the call's first choice.
+ *   eos_step        device int32 [B] or NULL.  -1 while the row runs; the
+ *                   choice that returns eos writes its index there, and every
+ *                   later choice of the row returns eos without marking the
+ *                   seen set.  NULL: eos is chosen like any token, no stop.
+ * Suppressed tokens (and a blocked eos) count as logit -inf before the
+ * penalty; at least one token of a row must stay choosable.  Decode steps
+ * after a stop still run (fed eos): the caller trims at eos_step. */
+typedef struct atd_controls {
+  const uint32_t* suppress;
+  int32_t eos;
+  int32_t min_new_tokens;
+  int32_t first_index;
+  int32_t* eos_step;
+} atd_controls;
+
 typedef struct atd_decoder atd_decoder;
 
 /* Create a decoder.  Validates cfg and w (all device pointers non-NULL where
@@ -276,10 +300,13 @@ int decoder_embed(atd_decoder* dec, int32_t B, const int32_t* tok, int32_t G,
  * token is the lowest index of the maximum; margin = best - second best
  * (0 on a tie).  Writes tok_out (device int32 [B]) and margin_out (device
  * float32 [B] or NULL) and sets the chosen token's bit in seen.  The logits
- * are not modified.  Uses a device scratch buffer that the library keeps
- * per device (allocated on first use).  Errors: INVALID_ARG, DEVICE. */
+ * are not modified.  controls (or NULL): atd_controls, the choice of every
+ * row having index controls->first_index.  Uses a device scratch buffer
+ * that the library keeps per device (allocated on first use).  Errors:
+ * INVALID_ARG, DEVICE. */
 int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
-                  float penalty, int32_t* tok_out, float* margin_out, void* stream);
+                  float penalty, const atd_controls* controls, int32_t* tok_out,
+                  float* margin_out, void* stream);
 
 /* Sampled token per row (the draw of atd_sampling; qwen3-tts-hip log,
  * device-sampler entry).  logits device [B, V] float32; seen and penalty as
@@ -287,11 +314,12 @@ int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
  * sampling->uniforms[b] (device [B]).  Writes tok_out (device int32 [B]).
  * Rows of up to 8192 logits run in one workgroup each; longer rows first
  * reduce each 8192-logit chunk to its top_k candidates, which needs
- * ceil(V / 8192) * top_k <= 8192.  Uses the per-device scratch buffer of
- * greedy_argmax.  Errors: INVALID_ARG, UNSUPPORTED (V too long for top_k),
+ * ceil(V / 8192) * top_k <= 8192.  controls as in greedy_argmax.  Uses the
+ * per-device scratch buffer of greedy_argmax.  Errors: INVALID_ARG, UNSUPPORTED (V too long for top_k),
  * DEVICE. */
 int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* seen, float penalty,
-                const atd_sampling* sampling, int32_t* tok_out, void* stream);
+                const atd_sampling* sampling, const atd_controls* controls,
+                int32_t* tok_out, void* stream);
 
 
 /* Generation on the device: n_steps decode steps of `slot` with the token
@@ -302,9 +330,10 @@ int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* seen, float
  * `head`, then chooses the token over `seen` (device [ceil(V/32)] or NULL)
  * and `penalty`: the penalized argmax of greedy_argmax when sampling is
  * NULL, else the draw of atd_sampling with u = sampling->uniforms[k]
- * (device [n_steps]).  The token goes to tok_io[0] (the other G-1 ids are
- * held) and, when tokens_out is not NULL, to tokens_out[k] (device int32
- * [n_steps]).  y_out (device [h] or NULL) and logits_out
+ * (device [n_steps]); controls (or NULL) as in atd_controls, step k being
+ * choice controls->first_index + k.  The token goes to tok_io[0] (the other
+ * G-1 ids are held) and, when tokens_out is not NULL, to tokens_out[k]
+ * (device int32 [n_steps]).  y_out (device [h] or NULL) and logits_out
  * (device [V]) hold the last step's outputs.  The launches of one step are
  * captured once into a HIP graph and replayed; the graph is cached for this
  * argument set (sampling settings and uniforms pointer included) and
@@ -315,7 +344,8 @@ int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* seen, float
 int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* tok_io,
                      int32_t G, const int32_t* table_ids, const float* extra, int32_t head,
                      uint32_t* seen, float penalty, const atd_sampling* sampling,
-                     int32_t* tokens_out, float* y_out, float* logits_out, void* stream);
+                     const atd_controls* controls, int32_t* tokens_out, float* y_out,
+                     float* logits_out, void* stream);
 
 /* The Talker's two-level frame loop on the device ("Qwen3-TTS ncnn port",
  * section "Talker: non-standard structure and two-level generation"; the
@@ -346,6 +376,9 @@ int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* t
  * tk_sampling uniforms: device [n_frames] (entry 0 unused); cp_sampling
  *            uniforms: device [n_frames, 15].  Both settings belong to the
  *            captured graphs' key.
+ * tk_controls the Talker's atd_controls (or NULL): frame f's c0 (f >= 1) is
+ *            choice first_index + f; after a stop c0 stays eos (the frames
+ *            still run: trim at eos_step).
  * codes_out  [n_frames, 16] int32 device, or NULL.
  * tk_logits  [V_tk] and cp_logits [V_cp] float32 device: the last logits of
  *            each decoder.
@@ -360,8 +393,8 @@ int decoder_generate(atd_decoder* dec, int32_t slot, int32_t n_steps, int32_t* t
 int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_decoder* cp, int32_t cp_slot,
                            int32_t n_frames, int32_t* codes_io, float* y_io, const float* text,
                            uint32_t* seen, float penalty, const atd_sampling* tk_sampling,
-                           const atd_sampling* cp_sampling, int32_t* codes_out, float* tk_logits,
-                           float* cp_logits, void* stream);
+                           const atd_sampling* cp_sampling, const atd_controls* tk_controls,
+                           int32_t* codes_out, float* tk_logits, float* cp_logits, void* stream);
 
 /* Block quantization of dense weights into a quantized weight_format
  * (ATD_WFMT_Q8 or ATD_WFMT_Q4; the formats are described with

@@ -558,7 +558,7 @@ def code_predictor_frame(cp: Model, y_talker: np.ndarray, c0: int,
 def run_talker(talker: Model, cp: Model, X0: np.ndarray, text: np.ndarray,
                n_frames: int, s_init: int, rho: float = 1.05,
                cp_capacity: int = 16, forced: Optional[Sequence[Sequence[int]]] = None,
-               tk_sampling=None, cp_sampling=None):
+               tk_sampling=None, cp_sampling=None, tk_controls: Optional[Controls] = None):
     """Two-level Talker frame loop (ncnn port, Talker section).
 
     Prefill X0 gives (y_0, z_0) and the main code c0_0 (penalty rho over the
@@ -568,12 +568,19 @@ def run_talker(talker: Model, cp: Model, X0: np.ndarray, text: np.ndarray,
     c0_{f+1}.  ``forced[f]`` (16 codes) replaces frame f's generated codes
     when teacher forcing.  Sampled choices: tk_sampling = (k, temperature,
     top_p, u[n_frames]) draws c0_f with u[f]; cp_sampling = (k, temperature,
-    top_p, u[n_frames, 15]) draws frame f's c_{j+1} with u[f, j].  Returns
-    per-frame dicts."""
+    top_p, u[n_frames, 15]) draws frame f's c_{j+1} with u[f, j].  With
+    ``tk_controls`` every c0 goes through choose_controlled (the prefill's
+    choice first).  Returns per-frame dicts."""
     cache = Cache(talker, s_init)
     seen = np.zeros(talker.heads[0].shape[0], bool)
+
+    def pick(z, f):
+        if tk_controls is None:
+            return choose(z, seen, rho, tk_sampling, f)
+        return choose_controlled(z, seen, rho, tk_controls, tk_sampling, f)
+
     y, z = prefill(talker, cache, X0, 0)
-    c0, m0 = choose(z, seen, rho, tk_sampling, 0)
+    c0, m0 = pick(z, 0)
     frames = []
     for f in range(n_frames):
         if forced is not None:
@@ -595,5 +602,5 @@ def run_talker(talker: Model, cp: Model, X0: np.ndarray, text: np.ndarray,
             for g in range(f + 1):
                 seen[forced[g][0]] = True
         y, z = step(talker, cache, x, 0)
-        c0, m0 = choose(z, seen, rho, tk_sampling, f + 1)
+        c0, m0 = pick(z, f + 1)
     return frames, cache

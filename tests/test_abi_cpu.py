@@ -369,3 +369,33 @@ def test_quantize_blocks_argument_checks():
         with pytest.raises(B.AtdError) as ei:
             B.quantize_blocks(*args)
         assert ei.value.code == code and needle in str(ei.value), (args, str(ei.value))
+
+
+def test_controls_argument_checks():
+    """atd_controls: eos outside [-1, V), negative counts and misaligned
+    pointers are refused before any device call."""
+    for ctl, needle in [(B.atd_controls(None, 10, 0, 0, None), "eos 10"),
+                        (B.atd_controls(None, -2, 0, 0, None), "eos -2"),
+                        (B.atd_controls(None, 3, -1, 0, None), "min_new_tokens"),
+                        (B.atd_controls(None, 3, 0, -4, None), "first_index"),
+                        (B.atd_controls(0x102, 3, 0, 0, None), "aligned"),
+                        (B.atd_controls(None, 3, 0, 0, 0x203), "aligned")]:
+        with pytest.raises(B.AtdError) as ei:
+            B.greedy_argmax(0x100, 1, 10, None, 1.0, 0x200, None, 0, controls=ctl)
+        assert ei.value.code == B.ATD_ERR_INVALID_ARG and needle in str(ei.value), str(ei.value)
+        with pytest.raises(B.AtdError):
+            B.sample_topk(0x100, 1, 10, None, 1.0, B.atd_sampling(5, 1.0, 1.0, 0x300), 0x200, 0,
+                          controls=ctl)
+    h, fw = _create(_cfg())
+    try:
+        B.kv_bucket_grow(h, 0, [0x1000, 0x2000], [0x3000, 0x4000], 32, 0)
+        B.decoder_prefill(h, 0, 0x5000, 4, 0, None, 0x6000, 0)
+        good = B.atd_controls(0x7000, 5, 3, 1, 0x8000)
+        B.decoder_generate(h, 0, 6, 0x9000, 1, [0], None, 0, None, 1.0, None, None, None, 0x6000,
+                           0, controls=good)
+        assert B.decoder_get_position(h, 0) == (10, 32)
+        with pytest.raises(B.AtdError):
+            B.decoder_generate(h, 0, 6, 0x9000, 1, [0], None, 0, None, 1.0, None, None, None,
+                               0x6000, 0, controls=B.atd_controls(None, 100, 0, 0, None))
+    finally:
+        B.decoder_destroy(h)

@@ -72,6 +72,10 @@ def forward_rows(model, rows: Sequence[Sequence[float]]) -> List[List[float]]:
     grp = hq // hkv
     eps = model.rms_eps
     xs = [[float(v) for v in r] for r in rows]
+    if getattr(model, "in_proj", None) is not None:     # input projection
+        b = model.in_proj_bias
+        xs = [[_dot(model.in_proj[i], x) + (float(b[i]) if b is not None else 0.0)
+               for i in range(len(model.in_proj))] for x in xs]
     T = len(xs)
     for L in model.layers:
         Q, K, Vv = [], [], []

@@ -62,8 +62,15 @@ class Model:
     layers: List[dict]                # per layer: see LAYER_KEYS
     final_norm: np.ndarray
     heads: List[np.ndarray]           # [V, h]
-    tables: List[np.ndarray]          # [V_g, h]
+    tables: List[np.ndarray]          # [V_g, h_in]
     dtype: type = np.float64
+    in_proj: Optional[np.ndarray] = None       # [h, h_in] input projection, or None
+    in_proj_bias: Optional[np.ndarray] = None  # [h] or None
+
+    @property
+    def input_dim(self) -> int:
+        """Width of the input rows (tables, extra, prefill rows)."""
+        return self.hidden if self.in_proj is None else self.in_proj.shape[1]
 
 
 LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "bq", "bk", "bv", "q_norm",
@@ -71,13 +78,14 @@ LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "bq", "bk", "bv", "q_norm",
 
 
 def make_model(hp: dict, layers: Sequence[dict], final_norm, heads, tables,
-               dtype=np.float64) -> Model:
+               dtype=np.float64, in_proj=None, in_proj_bias=None) -> Model:
     """Copy the given arrays into the compute dtype (None stays None)."""
     def cv(a):
         return None if a is None else np.asarray(a, dtype=dtype)
     return Model(layers=[{k: cv(L.get(k)) for k in LAYER_KEYS} for L in layers],
                  final_norm=cv(final_norm), heads=[cv(h) for h in heads],
-                 tables=[cv(t) for t in tables], dtype=dtype, **hp)
+                 tables=[cv(t) for t in tables], dtype=dtype, in_proj=cv(in_proj),
+                 in_proj_bias=cv(in_proj_bias), **hp)
 
 
 # --------------------------------------------------------------------------
@@ -220,13 +228,25 @@ def embed(model: Model, toks: Sequence[int], table_ids: Sequence[int],
           extra: Optional[np.ndarray] = None) -> np.ndarray:
     """Step input: sum over g of tables[table_ids[g]][toks[g]], plus extra.
     For the Talker frame this is the 16 code embeddings plus the text
-    embedding (ncnn port, two-level generation)."""
-    x = np.zeros(model.hidden, model.dtype)
+    embedding (ncnn port, two-level generation).  Rows are input_dim wide."""
+    x = np.zeros(model.input_dim, model.dtype)
     for t, g in zip(toks, table_ids):
         x = x + model.tables[g][t]
     if extra is not None:
         x = x + np.asarray(extra, model.dtype)
     return x
+
+
+def project_input(model: Model, x: np.ndarray) -> np.ndarray:
+    """Input rows into the stack's width: x W_in^T + b_in when the stack has
+    an input projection (the qwen3-tts-hip log's Code Predictor stages
+    "prefix projection" and "remaining projection": the Code Predictor's
+    inputs come in the Talker's width), else x."""
+    x = np.asarray(x, model.dtype)
+    if model.in_proj is None:
+        return x
+    y = x @ model.in_proj.T
+    return y + model.in_proj_bias if model.in_proj_bias is not None else y
 
 
 def head_out(model: Model, x: np.ndarray, head: int):
@@ -243,7 +263,7 @@ def step(model: Model, cache: Cache, x: np.ndarray, head: int = 0):
     p = cache.pos
     if p >= cache.capacity:
         raise ValueError("KV cache full")
-    x = np.asarray(x, model.dtype)
+    x = project_input(model, x)
     cos, sin = rope_cos_sin(p, model.head_dim, model.rope_theta)
     for l, L in enumerate(model.layers):
         u = rms_norm(x, L["attn_norm"], model.rms_eps)
@@ -263,7 +283,7 @@ def prefill(model: Model, cache: Cache, X: np.ndarray, head: int = 0):
     """T rows at positions 0..T-1 (the cache is reset first), written as
     whole-block matrix products with a causal mask: row t attends to rows
     0..t.  Returns (y, z) of the last row."""
-    X = np.asarray(X, model.dtype)
+    X = project_input(model, X)
     T = X.shape[0]
     if T == 0 or T > cache.capacity:
         raise ValueError("prefill length out of range")

@@ -241,8 +241,14 @@ def _choose_no_stop(z, seen, rho, ctl, sampling=None, i=0):
     return tok, r
 
 
+def _project_no_bias(model, x):
+    x = np.asarray(x, model.dtype)
+    return x if model.in_proj is None else x @ model.in_proj.T
+
+
 MUTATIONS = {
     "controls_eos_one_early": ("Controls", _CtlEosAtMin),
+    "input_projection_drops_bias": ("project_input", _project_no_bias),
     "controls_no_stop": ("choose_controlled", _choose_no_stop),
     "sample_walks_ascending": ("sampling_distribution", _dist_ascending),
     "sample_temperature_multiplies": ("sampling_distribution", _dist_temp_multiplies),

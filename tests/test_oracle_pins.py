@@ -19,6 +19,7 @@ PINS = [
     pins.check_mlp_closed_form,
     pins.check_projection_orientation,
     pins.check_prefill_equals_steps,
+    pins.check_input_projection,
     pins.check_bucket_copy_invariance,
     pins.check_code_predictor_recompute,
     pins.check_frame_input,

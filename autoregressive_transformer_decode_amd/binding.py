@@ -59,7 +59,7 @@ class atd_config(C.Structure):
                 ("kv_dtype", C.c_int32),
                 ("rope_theta", C.c_double), ("rms_eps", C.c_float),
                 ("max_slots", C.c_int32), ("max_rows", C.c_int32), ("max_ctx", C.c_int32),
-                ("flags", C.c_int32), ("weight_format", C.c_int32)]
+                ("flags", C.c_int32), ("weight_format", C.c_int32), ("input_dim", C.c_int32)]
 
 
 ATD_TOPK_MAX = 256
@@ -85,7 +85,8 @@ class atd_layer_weights(C.Structure):
 class atd_weights(C.Structure):
     _fields_ = [("layers", C.POINTER(atd_layer_weights)), ("final_norm", C.c_void_p),
                 ("lm_heads", C.POINTER(C.c_void_p)), ("tables", C.POINTER(C.c_void_p)),
-                ("table_vocab", C.POINTER(C.c_int32))]
+                ("table_vocab", C.POINTER(C.c_int32)), ("in_proj", C.c_void_p),
+                ("in_proj_bias", C.c_void_p)]
 
 
 def _load():

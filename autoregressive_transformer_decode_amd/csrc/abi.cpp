@@ -22,6 +22,10 @@ struct atd_decoder {
   atd_config cfg{};
   std::vector<atd_layer_weights> layers;
   const float* final_norm = nullptr;
+  const void* in_proj = nullptr;       // [hidden, in_dim] or null
+  const float* in_proj_bias = nullptr;
+  int in_dim = 0;                      // width of the input rows
+  float* xin = nullptr;                // input rows before the projection [max_rows, in_dim]
   std::vector<const void*> heads, tables;
   std::vector<int32_t> table_vocab;
   // host mirror of every slot
@@ -148,6 +152,11 @@ int check_config(const atd_config* c) {
       c->weight_format != ATD_WFMT_Q4)
     return fail(nullptr, ATD_ERR_DTYPE, "weight_format %d is not ATD_WFMT_DENSE/Q8/Q4",
                 c->weight_format);
+  if (c->input_dim != 0 &&
+      (c->input_dim < 8 || c->input_dim % 8 || c->input_dim > (c->dtype == ATD_F32 ? 4096 : 8192)))
+    return fail(nullptr, ATD_ERR_UNSUPPORTED,
+                "input_dim %d: must be 0 or a multiple of 8 in [8, %d]", c->input_dim,
+                c->dtype == ATD_F32 ? 4096 : 8192);
   if (c->weight_format != ATD_WFMT_DENSE &&
       (c->hidden % kQBlock || c->ffn % kQBlock || (c->n_q_heads * c->head_dim) % kQBlock))
     return fail(nullptr, ATD_ERR_SHAPE,
@@ -213,6 +222,16 @@ int check_weights(const atd_config* c, const atd_weights* w) {
 #undef LW
   }
   NEED(w->final_norm, "final_norm");
+  if (w->in_proj) {
+    NEED(w->in_proj, "in_proj");
+    if (w->in_proj_bias) NEED(w->in_proj_bias, "in_proj_bias");
+  } else if (c->input_dim != 0 && c->input_dim != c->hidden) {
+    return fail(nullptr, ATD_ERR_INVALID_ARG,
+                "input_dim %d differs from hidden %d but in_proj is NULL", c->input_dim,
+                c->hidden);
+  } else if (w->in_proj_bias) {
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "in_proj_bias is set but in_proj is NULL");
+  }
   for (int j = 0; j < c->n_lm_heads; ++j) {
     snprintf(name, sizeof name, "lm_heads[%d]", j);
     NEED(w->lm_heads[j], name);
@@ -592,8 +611,37 @@ EmbedArgs embed_args(atd_decoder* d, int B, const int32_t* tok, int G,
   e.tok = tok;
   e.extra = extra;
   e.out = out;
-  e.h = d->cfg.hidden;
+  e.h = d->in_dim;
   e.M = B;
+  return e;
+}
+
+// Where input rows are built: the projection's input, or the residual stream.
+float* in_rows(const atd_decoder* d) { return d->in_proj ? d->xin : d->x; }
+
+// With an input projection: the M rows in d->xin into d->x (in_proj r + bias).
+hipError_t project_rows(atd_decoder* d, int M, hipStream_t s) {
+  if (!d->in_proj) return hipSuccess;
+  const atd_config& c = d->cfg;
+  GemvArgs g{};
+  g.W[0] = d->in_proj;
+  g.bias[0] = d->in_proj_bias;
+  g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = c.hidden;
+  g.x = d->xin;
+  g.ldx = d->in_dim;
+  g.out = d->x;
+  g.ldo = c.hidden;
+  g.K = d->in_dim;
+  g.N = c.hidden;
+  g.M = M;
+  return launch_gemv(g, kEpiStore, false, c.dtype == ATD_BF16 ? kWBF16 : kWF32, s);
+}
+
+// Input rows of M tokens / extra rows built and projected into d->x.
+hipError_t build_inputs(atd_decoder* d, EmbedArgs ea, hipStream_t s) {
+  ea.out = in_rows(d);
+  hipError_t e = launch_embed(ea, d->cfg.dtype == ATD_BF16, s);
+  if (e == hipSuccess) e = project_rows(d, ea.M, s);
   return e;
 }
 
@@ -602,8 +650,7 @@ hipError_t enqueue_step(atd_decoder* d, int slot0, int B, const int32_t* tok, in
                         const int32_t* table_ids, const float* extra, int head, float* y_out,
                         float* logits_out, int max_cap, hipStream_t s) {
   RowMap rows{kRowsStep, slot0, 0};
-  EmbedArgs ea = embed_args(d, B, tok, G, table_ids, extra, d->x);
-  hipError_t e = launch_embed(ea, d->cfg.dtype == ATD_BF16, s);
+  hipError_t e = build_inputs(d, embed_args(d, B, tok, G, table_ids, extra, d->x), s);
   const HeadOut ho{head, y_out, logits_out};
   if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, d->x, &ho, s);
   if (e == hipSuccess) e = launch_advance(slots_of(d), rows, B, s);
@@ -624,6 +671,9 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->cfg = *cfg;
   d->layers.assign(w->layers, w->layers + cfg->n_layers);
   d->final_norm = (const float*)w->final_norm;
+  d->in_proj = w->in_proj;
+  d->in_proj_bias = (const float*)w->in_proj_bias;
+  d->in_dim = cfg->input_dim ? cfg->input_dim : cfg->hidden;
   d->heads.assign(w->lm_heads, w->lm_heads + cfg->n_lm_heads);
   d->tables.assign(w->tables, w->tables + cfg->n_tables);
   d->table_vocab.assign(w->table_vocab, w->table_vocab + cfg->n_tables);
@@ -651,6 +701,7 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   const size_t o_cos = carve((size_t)cfg->max_ctx * half * 4);
   const size_t o_sin = carve((size_t)cfg->max_ctx * half * 4);
   const size_t o_x = carve((size_t)R * h * 4);
+  const size_t o_xin = carve(w->in_proj ? (size_t)R * d->in_dim * 4 : 0);
   const size_t o_qkv = carve((size_t)R * nqkv * 4);
   const size_t o_q = carve((size_t)R * nq * 4);
   const size_t o_o = carve((size_t)R * nq * 4);
@@ -697,6 +748,7 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->cos_t = (float*)(base + o_cos);
   d->sin_t = (float*)(base + o_sin);
   d->x = (float*)(base + o_x);
+  d->xin = w->in_proj ? (float*)(base + o_xin) : nullptr;
   d->qkv = (float*)(base + o_qkv);
   d->q = (float*)(base + o_q);
   d->o = (float*)(base + o_o);
@@ -881,8 +933,7 @@ extern "C" int decoder_prefill(atd_decoder* d, int32_t slot, const float* x, int
   }
   hipStream_t s = (hipStream_t)stream;
   RowMap rows{kRowsPrefill, slot, 0};
-  EmbedArgs ea = embed_args(d, T, nullptr, 0, nullptr, x, d->x);
-  hipError_t e = launch_embed(ea, c.dtype == ATD_BF16, s);
+  hipError_t e = build_inputs(d, embed_args(d, T, nullptr, 0, nullptr, x, d->x), s);
   if (e == hipSuccess) e = run_layers(d, rows, T, T, d->x, nullptr, s);
   if (e == hipSuccess)
     e = run_head_gemv(d, d->x + (size_t)(T - 1) * c.hidden, 1, head, y_out, logits_out, s);
@@ -1313,10 +1364,11 @@ hipError_t enqueue_cp_pass(atd_decoder* cp, int cp_slot, int32_t* codes, const f
   const int G = kCodeGroups - 1;
   // prefill rows: the Talker's output and the embedding of c0 (table 0)
   const int32_t t0 = 0;
-  EmbedArgs r0 = embed_args(cp, 1, nullptr, 0, nullptr, y, cp->x);
-  EmbedArgs r1 = embed_args(cp, 1, codes, 1, &t0, nullptr, cp->x + c.hidden);
+  EmbedArgs r0 = embed_args(cp, 1, nullptr, 0, nullptr, y, in_rows(cp));
+  EmbedArgs r1 = embed_args(cp, 1, codes, 1, &t0, nullptr, in_rows(cp) + cp->in_dim);
   hipError_t e = launch_embed(r0, c.dtype == ATD_BF16, s);
   if (e == hipSuccess) e = launch_embed(r1, c.dtype == ATD_BF16, s);
+  if (e == hipSuccess) e = project_rows(cp, 2, s);
   const RowMap pre{kRowsPrefill, cp_slot, 0};
   if (e == hipSuccess) e = run_layers(cp, pre, 2, 2, cp->x, nullptr, s);
   if (e == hipSuccess) e = run_head_gemv(cp, cp->x + c.hidden, 1, 0, nullptr, cp_logits, s);
@@ -1346,7 +1398,7 @@ hipError_t enqueue_talker_step(atd_decoder* tk, int tk_slot, int32_t* codes, con
   RowMap rows{kRowsStep, tk_slot, 0};
   EmbedArgs ea = embed_args(tk, 1, codes, kCodeGroups, tabs, text, tk->x);
   ea.extra_row = counter;
-  hipError_t e = launch_embed(ea, c.dtype == ATD_BF16, s);
+  hipError_t e = build_inputs(tk, ea, s);
   const HeadOut ho{0, y, tk_logits};
   const int max_cap = std::min(tk->cap[tk_slot], c.max_ctx);
   if (e == hipSuccess) e = run_layers(tk, rows, 1, max_cap, tk->x, &ho, s);
@@ -1371,9 +1423,12 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
   const atd_config &tc = tk->cfg, &cc = cp->cfg;
   if (tk->dry != cp->dry) return fail(tk, ATD_ERR_INVALID_ARG, "one decoder is a dry run, the other not");
   if (n_frames < 1) return fail(tk, ATD_ERR_INVALID_ARG, "n_frames %d < 1", n_frames);
-  if (tc.hidden != cc.hidden)
-    return fail(tk, ATD_ERR_SHAPE, "hidden sizes differ: Talker %d, Code Predictor %d", tc.hidden,
-                cc.hidden);
+  if (tc.hidden != cp->in_dim)
+    return fail(tk, ATD_ERR_SHAPE,
+                "the Code Predictor's input width %d is not the Talker's hidden size %d",
+                cp->in_dim, tc.hidden);
+  if (tk->in_dim != tc.hidden)
+    return fail(tk, ATD_ERR_SHAPE, "the Talker of a frame loop takes no input projection");
   if (tc.n_tables < kCodeGroups)
     return fail(tk, ATD_ERR_SHAPE, "the Talker has %d tables, a frame input needs %d", tc.n_tables,
                 kCodeGroups);

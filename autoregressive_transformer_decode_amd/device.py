@@ -87,6 +87,8 @@ class DeviceModel:
                     self.keep = [t for t in self.keep if t is not dense]
                 torch.cuda.current_stream().synchronize()
         self.final_norm = up(mw.final_norm)
+        self.in_proj = up(mw.in_proj.storage) if mw.in_proj is not None else None
+        self.in_proj_bias = up(mw.in_proj_bias) if mw.in_proj_bias is not None else None
         self.heads = [up(h.storage) for h in mw.heads]
         if tables is None:
             tables = [up(t.storage) for t in mw.tables]
@@ -110,7 +112,9 @@ class DeviceModel:
             final_norm=self.final_norm.data_ptr(),
             lm_heads=C.cast(self._heads, C.POINTER(C.c_void_p)),
             tables=C.cast(self._tables, C.POINTER(C.c_void_p)),
-            table_vocab=C.cast(self._vocab, C.POINTER(C.c_int32)))
+            table_vocab=C.cast(self._vocab, C.POINTER(C.c_int32)),
+            in_proj=self.in_proj.data_ptr() if self.in_proj is not None else None,
+            in_proj_bias=self.in_proj_bias.data_ptr() if self.in_proj_bias is not None else None)
 
 
 def make_config(s: ModelShape, max_slots: int, max_rows: int, max_ctx: int,
@@ -125,7 +129,7 @@ def make_config(s: ModelShape, max_slots: int, max_rows: int, max_ctx: int,
         kv_dtype=B.ATD_BF16 if s.kv_dtype == BF16 else B.ATD_F32,
         rope_theta=s.rope_theta, rms_eps=s.rms_eps,
         max_slots=max_slots, max_rows=max_rows, max_ctx=max_ctx, flags=flags,
-        weight_format=weight_format)
+        weight_format=weight_format, input_dim=s.input_dim)
 
 
 class Decoder:

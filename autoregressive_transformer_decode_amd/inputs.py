@@ -38,6 +38,7 @@ _T_PREFILL = 70_000
 _T_TEXT = 70_001
 _T_TOKENS = 70_002
 _T_KV = 60_000
+_T_INPROJ = 91_000
 
 
 @dataclasses.dataclass(frozen=True)
@@ -61,6 +62,12 @@ class ModelShape:
     table_vocabs: Tuple[int, ...]   # vocab of each embedding table
     model_id: int = 0     # separates the random streams of two stacks
     kv_dtype: str = F32   # KV-cache storage: F32 or BF16
+    input_dim: int = 0    # width of the input rows when projected (0: hidden)
+
+    @property
+    def in_width(self) -> int:
+        """Width of the input rows: tables, extra and prefill rows."""
+        return self.input_dim or self.hidden
 
     @property
     def q_dim(self) -> int:
@@ -76,6 +83,8 @@ class ModelShape:
         n = per_layer * self.n_layers
         if with_head:
             n += self.vocab * h
+        if self.input_dim:
+            n += h * self.input_dim    # the input projection
         return n
 
 
@@ -113,6 +122,11 @@ CP06 = _shape("code_predictor", 5, 1024, 16, 8, 128, 3072, 2048, BF16, True,
               False, [3072] + [2048] * 15, n_heads=15, model_id=1)
 TALKER17 = _shape("talker1.7b", 28, 2048, 16, 8, 128, 6144, 3072, BF16, True,
                   False, [3072])
+# the 1.7B Talker in the frame loop (16 code tables) and its Code Predictor,
+# whose inputs come in the Talker's width through an input projection
+TALKER17F = dataclasses.replace(TALKER17, name="talker1.7b-frames",
+                                table_vocabs=tuple([3072] + [2048] * 15))
+CP17 = dataclasses.replace(CP06, name="code_predictor-1.7b", input_dim=2048)
 # the batched workload states bf16 for the KV cache as well as the weights
 TALKER17_KVBF16 = dataclasses.replace(TALKER17, name="talker1.7b-kvbf16", kv_dtype=BF16)
 
@@ -126,6 +140,9 @@ WORKLOADS: Dict[str, Workload] = {
                            frames=75, penalty=1.05),
     "talker1.7b": Workload("talker1.7b", TALKER17, batch=1, prefill=512,
                            steps=1536, s_init=2048, s_max=2048),
+    "talker1.7b-frames": Workload("talker1.7b-frames", TALKER17F, batch=1, prefill=64,
+                                  steps=74, s_init=256, s_max=256, cp=CP17,
+                                  frames=75, penalty=1.05),
     "batched64": Workload("batched64", TALKER17_KVBF16, batch=64, prefill=0,
                           steps=32, s_init=4096 + 64, s_max=4096 + 64,
                           len_range=(256, 4096)),
@@ -226,12 +243,14 @@ class ModelWeights:
     layers: List[LayerWeights]
     final_norm: np.ndarray          # [h]
     heads: List[Tensor]             # n_lm_heads x [V, h]
-    tables: List[Tensor]            # embedding tables [V_g, h]
+    tables: List[Tensor]            # embedding tables [V_g, in_width]
+    in_proj: Optional[Tensor] = None          # [h, input_dim] when projected
+    in_proj_bias: Optional[np.ndarray] = None  # [h]
 
 
 def make_tables(shape: ModelShape, seed: int = 0) -> List[Tensor]:
     """Embedding tables.  Drawn with model_id 0 so stacks can share them."""
-    return [_stored(normal(seed, 0, _T_TABLE + g, (v, shape.hidden)), shape.dtype)
+    return [_stored(normal(seed, 0, _T_TABLE + g, (v, shape.in_width)), shape.dtype)
             for g, v in enumerate(shape.table_vocabs)]
 
 
@@ -263,7 +282,11 @@ def make_weights(shape: ModelShape, seed: int = 0,
              for j in range(shape.n_lm_heads)]
     if tables is None:
         tables = make_tables(shape, seed)
-    return ModelWeights(shape, layers, ones_h.copy(), heads, tables)
+    in_proj = in_bias = None
+    if shape.input_dim:
+        in_proj = _stored(normal(seed, mid, _T_INPROJ, (h, shape.input_dim)), shape.dtype)
+        in_bias = normal(seed, mid, _T_INPROJ + 1, (h,))
+    return ModelWeights(shape, layers, ones_h.copy(), heads, tables, in_proj, in_bias)
 
 
 def prefill_embeddings(wl: Workload, seed: int = 0) -> np.ndarray:

@@ -563,7 +563,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="talker1.7b",
-                    choices=["talker1.7b", "asr", "tiny", "batched64", "talker0.6b"])
+                    choices=["talker1.7b", "asr", "tiny", "batched64", "talker0.6b",
+                             "talker1.7b-frames"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true",

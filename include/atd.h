@@ -95,6 +95,9 @@ typedef struct atd_config {
   int32_t flags;       /* ATD_FLAG_* bits                                    */
   int32_t weight_format; /* ATD_WFMT_*: storage of the seven per-layer
                             matrices (LM heads and tables stay in dtype)     */
+  int32_t input_dim;   /* width of the input rows (tables, extra, prefill
+                          rows): 0 or hidden, or another multiple of 8 <=
+                          8192 (<= 4096 for F32) with an input projection   */
 } atd_config;
 
 /* atd_config.weight_format ("Rockchip NPU sidecars" page, section "The talker
@@ -167,6 +170,15 @@ typedef struct atd_weights {
   const void* const* lm_heads;     /* host [n_lm_heads] -> device [V, h]     */
   const void* const* tables;       /* host [n_tables] -> device [V_g, h]     */
   const int32_t* table_vocab;      /* host [n_tables]: V_g of each table     */
+  /* Input projection (qwen3-tts-hip log, Code Predictor stages "prefix
+   * projection" / "remaining projection": the Code Predictor of a wider
+   * Talker takes its inputs in the Talker's width).  When set, every input
+   * row r (input_dim wide: embeddings, extra rows, prefill rows) enters the
+   * stack as in_proj r + in_proj_bias.  in_proj: device [hidden, input_dim] in
+   * dtype, 16-byte aligned, or NULL (then input_dim must be 0 or hidden);
+   * in_proj_bias: device [hidden] float32 or NULL. */
+  const void* in_proj;
+  const void* in_proj_bias;
 } atd_weights;
 
 /* Settings of a sampled token choice (qwen3-tts-hip OPTIMIZATION_LOG: the
@@ -261,7 +273,8 @@ int decoder_get_position(const atd_decoder* dec, int32_t slot, int32_t* pos,
                          int32_t* capacity);
 
 /* Prefill: reset `slot` to position 0 and run the T rows of x (device
- * [T, h] float32) at positions 0..T-1 through the stack, each row attending
+ * [T, input_dim] float32; input rows, projected first when the stack has an
+ * input projection) at positions 0..T-1 through the stack, each row attending
  * to the rows before it and itself.  Writes KV rows 0..T-1 and leaves the
  * position at T.  Outputs of the last row: y_out (device [h] float32, the
  * final-norm hidden state; may be NULL) and logits_out (device [V]
@@ -272,10 +285,11 @@ int decoder_prefill(atd_decoder* dec, int32_t slot, const float* x, int32_t T,
 
 /* One decode step of B streams, slots slot0 .. slot0+B-1, each at its own
  * position p.  Input row b = sum over g < G of
- * tables[table_ids[g]][tok[b*G + g]] + extra[b] (extra: device [B, h]
+ * tables[table_ids[g]][tok[b*G + g]] + extra[b] (extra: device [B, input_dim]
  * float32 or NULL; G may be 0 when extra is given).  tok: device int32
  * [B, G]; ids outside [0, V_g) are clamped into range.  table_ids: host
- * [G].  Writes each slot's KV row p, advances its position by one, and
+ * [G].  (With an input projection the row is projected first.)  Writes
+ * each slot's KV row p, advances its position by one, and
  * writes y_out (device [B, h] or NULL) and logits_out (device [B, V]) of
  * LM head `head`.  Positions are mirrored on the host, so a full cache is
  * refused before any work: ATD_ERR_KV_FULL, and the caller grows the bucket
@@ -284,7 +298,7 @@ int decoder_step(atd_decoder* dec, int32_t slot0, int32_t B, const int32_t* tok,
                  int32_t G, const int32_t* table_ids, const float* extra,
                  int32_t head, float* y_out, float* logits_out, void* stream);
 
-/* The input-embedding part of decoder_step alone: x_out (device [B, h]
+/* The input-embedding part of decoder_step alone: x_out (device [B, input_dim]
  * float32) = sum_g tables[table_ids[g]][tok[b*G+g]] + extra[b].  Used to
  * build prefill rows from device-resident tokens.  Errors: INVALID_ARG,
  * CAPACITY, DEVICE. */

@@ -68,7 +68,9 @@ def oracle_from_weights(mw, dtype=np.float64, quant=None):
                 L[name] = oq.dequantize(codes, scales, quant, v.shape[1])
     return od.make_model(hp, layers, mw.final_norm,
                          [t.values for t in mw.heads],
-                         [t.values for t in mw.tables], dtype=dtype)
+                         [t.values for t in mw.tables], dtype=dtype,
+                         in_proj=mw.in_proj.values if mw.in_proj is not None else None,
+                         in_proj_bias=mw.in_proj_bias)
 
 
 def normwise_rel(got, ref) -> float:

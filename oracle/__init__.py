@@ -16,6 +16,8 @@ the definition itself, not any of those algorithms:
   Talker / Code Predictor frame loop.
 * ``brute``    -- a second, loop-only float64 form that recomputes the whole
   sequence from scratch at every step (no cache), for tiny shapes.
+* ``codec``    -- the codec decoder's causal dilated and transposed 1-D
+  convolutions.
 * ``quant``    -- the block-quantized weight formats (int8 and 4-bit codes
   with one fp16 scale per 32 weights): quantize and read back.
 
@@ -24,4 +26,4 @@ on random weights has no printed value to compare with: it is pinned by the
 closed forms and invariants in the tests (see tests/test_oracle_*.py).
 """
 
-from . import decoder, brute, quant  # noqa: F401
+from . import decoder, brute, quant, codec  # noqa: F401

@@ -16,6 +16,7 @@ from autoregressive_transformer_decode_amd import inputs
 from oracle import brute
 from oracle import decoder as od
 from oracle import quant as oq
+from oracle import codec as oc
 from tests._models import tiny_model
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -528,6 +529,58 @@ def check_controls():
     g, _ = od.penalized_argmax(z, None, 1.0)
     t, _ = od.choose_controlled(z, None, 1.0, od.Controls())
     assert t == g == 1
+
+
+# ---------------------------------------------------------------- codec convolutions
+
+def check_conv_causal():
+    """Single channel, dilation 1: numpy's full convolution with the reversed
+    kernel, cut to T; an impulse at frame t0 comes out as the taps at
+    t0 + (K-1-j) d; a 1-tap convolution is the channel matrix product."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((1, 20))
+    w = rng.standard_normal((1, 1, 5))
+    y = oc.conv1d_causal(x, w, None, 1)
+    _close(y[0], np.convolve(x[0], w[0, 0, ::-1])[:20], 1e-13)
+    xi = np.zeros((3, 30))
+    xi[1, 4] = 1.0
+    wi = rng.standard_normal((2, 3, 4))
+    bi = np.array([0.5, -0.25])
+    yi = oc.conv1d_causal(xi, wi, bi, 3)
+    exp = np.zeros((2, 30)) + bi[:, None]
+    for j in range(4):
+        exp[:, 4 + (3 - j) * 3] += wi[:, 1, j]
+    _close(yi, exp, 1e-15)
+    x2 = rng.standard_normal((6, 9))
+    w2 = rng.standard_normal((4, 6, 1))
+    _close(oc.conv1d_causal(x2, w2, None, 7), w2[:, :, 0] @ x2, 1e-13)
+
+
+def check_transconv_phases():
+    """The qwen3-tts-hip log's phase form, out[t s + p] = in[t] W[p] +
+    in[t-1] W[p+s] + bias (in[-1] = 0), equals the transposed convolution's
+    scatter definition; one frame in gives the kernel laid out once."""
+    rng = np.random.default_rng(32)
+    for s_, cin, cout, T in [(3, 4, 5, 7), (8, 2, 3, 4), (1, 3, 2, 5)]:
+        x = rng.standard_normal((cin, T))
+        w = rng.standard_normal((cin, cout, 2 * s_))
+        b = rng.standard_normal(cout)
+        y = oc.transconv1d(x, w, b, s_)
+        assert y.shape == (cout, T * s_)
+        ph = np.zeros((cout, T * s_))
+        for t in range(T):
+            for p in range(s_):
+                v = b + w[:, :, p].T @ x[:, t]
+                if t > 0:
+                    v = v + w[:, :, p + s_].T @ x[:, t - 1]
+                ph[:, t * s_ + p] = v
+        _close(y, ph, 1e-13)
+    x1 = np.zeros((2, 3))
+    x1[0, 0] = 1.0
+    w1 = rng.standard_normal((2, 2, 8))
+    y1 = oc.transconv1d(x1, w1, None, 4)
+    _close(y1[:, :8], w1[0], 1e-15)
+    assert not y1[:, 8:].any()
 
 
 # ---------------------------------------------------------------- block quantization

@@ -7,11 +7,13 @@ import pytest
 
 from oracle import decoder as od
 from oracle import quant as oq
+from oracle import codec as oc
 from tests import pins
 from tests.test_oracle_pins import PINS
 
 _orig = {k: getattr(od, k) for k in dir(od) if not k.startswith("__")}
 _orig_q = {k: getattr(oq, k) for k in dir(oq) if not k.startswith("__")}
+_orig_c = {k: getattr(oc, k) for k in dir(oc) if not k.startswith("__")}
 
 
 def _all_pins():
@@ -199,6 +201,41 @@ def _quant_nibbles_swapped(w, fmt):
     if fmt == oq.Q4:
         c = ((c >> 4) | (c << 4)).astype(np.uint8)
     return c, s
+
+
+def _conv_taps_forward(x, w, b, dilation=1):
+    return _orig_c["conv1d_causal"](x, w[:, :, ::-1], b, dilation)
+
+
+def _transconv_keep_last(x, w, b, stride):
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    cin, T = x.shape
+    full = np.zeros((w.shape[1], (T - 1) * stride + w.shape[2]))
+    for t in range(T):
+        full[:, t * stride:t * stride + w.shape[2]] += np.einsum("ick,i->ck", w, x[:, t])
+    y = full[:, full.shape[1] - T * stride:]
+    return y + (np.asarray(b)[:, None] if b is not None else 0)
+
+
+MUTATIONS_C = {
+    "conv_taps_reversed": ("conv1d_causal", _conv_taps_forward),
+    "transconv_keeps_last_window": ("transconv1d", _transconv_keep_last),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS_C))
+def test_planted_codec_mistake_is_caught(name, monkeypatch):
+    attr, repl = MUTATIONS_C[name]
+    monkeypatch.setattr(oc, attr, repl)
+    caught = []
+    for pin in _all_pins():
+        try:
+            pin()
+        except Exception as e:  # noqa: BLE001 -- an error also flags the slip
+            caught.append(type(e).__name__)
+            break
+    assert caught, f"no pin catches the planted mistake {name}"
 
 
 MUTATIONS_Q = {

@@ -32,6 +32,8 @@ PINS = [
     pins.check_sampling_greedy_limit,
     pins.check_sampling_frequencies,
     pins.check_controls,
+    pins.check_conv_causal,
+    pins.check_transconv_phases,
     pins.check_quant_closed_form,
     pins.check_quant_error_bound,
     pins.check_quant_bytes_golden,

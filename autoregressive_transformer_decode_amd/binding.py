@@ -39,7 +39,8 @@ STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FU
 EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
            "decoder_step", "decoder_embed", "greedy_argmax", "sample_topk", "decoder_generate",
-           "talker_generate_frames", "quantize_blocks", "decoder_time_stage")
+           "talker_generate_frames", "quantize_blocks", "codec_conv1d_causal",
+           "codec_transconv1d_pack", "codec_transconv1d", "decoder_time_stage")
 
 ATD_STAGE_QKV, ATD_STAGE_ROPE, ATD_STAGE_ATTN, ATD_STAGE_OPROJ, ATD_STAGE_GATEUP, \
     ATD_STAGE_DOWN, ATD_STAGE_HEAD = range(7)
@@ -116,6 +117,9 @@ def _load():
                                     C.POINTER(atd_sampling), C.POINTER(atd_sampling),
                                     C.POINTER(atd_controls), vp, vp, vp, vp], C.c_int),
         "quantize_blocks": ([vp, i32, C.c_int64, i32, i32, vp, vp, vp], C.c_int),
+        "codec_conv1d_causal": ([vp, vp, vp, i32, i32, i32, i32, i32, vp, vp], C.c_int),
+        "codec_transconv1d_pack": ([vp, i32, i32, i32, vp, vp], C.c_int),
+        "codec_transconv1d": ([vp, vp, vp, i32, i32, i32, i32, vp, vp], C.c_int),
         "decoder_time_stage": ([vp, i32, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
     }
     for name, (args, res) in sig.items():
@@ -230,6 +234,21 @@ def talker_generate_frames(tk: int, tk_slot: int, cp: int, cp_slot: int, n_frame
 def quantize_blocks(w: int, dtype: int, rows: int, cols: int, fmt: int, codes: int, scales: int,
                     stream: int) -> None:
     _check(lib.quantize_blocks(w, dtype, rows, cols, fmt, codes, scales, stream))
+
+
+def codec_conv1d_causal(x: int, w: int, bias, cin: int, cout: int, T: int, K: int,
+                        dilation: int, y: int, stream: int) -> None:
+    _check(lib.codec_conv1d_causal(x, w, bias, cin, cout, T, K, dilation, y, stream))
+
+
+def codec_transconv1d_pack(w: int, cin: int, cout: int, stride: int, packed: int,
+                           stream: int) -> None:
+    _check(lib.codec_transconv1d_pack(w, cin, cout, stride, packed, stream))
+
+
+def codec_transconv1d(x: int, packed: int, bias, cin: int, cout: int, T: int, stride: int,
+                      y: int, stream: int) -> None:
+    _check(lib.codec_transconv1d(x, packed, bias, cin, cout, T, stride, y, stream))
 
 
 def decoder_time_stage(handle: int, stage: int, slot0: int, B: int, reps: int,

@@ -1184,6 +1184,90 @@ extern "C" int quantize_blocks(const void* w, int32_t dtype, int64_t rows, int32
   return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "quantize_blocks");
 }
 
+// ---------------------------------------------------------------- codec convolutions
+
+namespace {
+int check_conv_ptrs(const void* a, const void* b, const void* c) {
+  if (!a || !b || !c) return fail(nullptr, ATD_ERR_INVALID_ARG, "a NULL tensor pointer");
+  if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) & 3)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "tensor pointers must be 4-byte aligned");
+  return ATD_OK;
+}
+bool too_big(int64_t a, int64_t b) { return a * b >= ((int64_t)1 << 31); }
+}  // namespace
+
+extern "C" int codec_conv1d_causal(const float* x, const float* w, const float* bias,
+                                   int32_t cin, int32_t cout, int32_t T, int32_t K,
+                                   int32_t dilation, float* y, void* stream) {
+  int rc = check_conv_ptrs(x, w, y);
+  if (rc) return rc;
+  if (bias && ((uintptr_t)bias & 3))
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "bias %p not 4-byte aligned", (const void*)bias);
+  if (cin < 1 || cout < 1 || T < 1 || K < 1 || dilation < 1)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "cin %d, cout %d, T %d, K %d, dilation %d: all >= 1",
+                cin, cout, T, K, dilation);
+  if (too_big(cin, K) || too_big(cin, T) || too_big(cout, T) || too_big((int64_t)cout * cin, K))
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "tensor beyond 2^31 elements");
+  ConvArgs a{};
+  a.x = x;
+  a.w = w;
+  a.bias = bias;
+  a.y = y;
+  a.cin = cin;
+  a.cout = cout;
+  a.T = T;
+  a.K = K;
+  a.dil = dilation;
+  a.ldy = T;
+  a.ystride = 1;
+  a.P = 1;
+  const hipError_t e = launch_conv(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "codec_conv1d_causal");
+}
+
+extern "C" int codec_transconv1d_pack(const float* w, int32_t cin, int32_t cout, int32_t stride,
+                                      float* packed, void* stream) {
+  int rc = check_conv_ptrs(w, packed, packed);
+  if (rc) return rc;
+  if (cin < 1 || cout < 1 || stride < 1)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "cin %d, cout %d, stride %d: all >= 1", cin, cout,
+                stride);
+  if (too_big((int64_t)cin * cout, 2 * (int64_t)stride))
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "tensor beyond 2^31 elements");
+  const hipError_t e = launch_pack_transconv(w, cin, cout, stride, packed, (hipStream_t)stream);
+  return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "codec_transconv1d_pack");
+}
+
+extern "C" int codec_transconv1d(const float* x, const float* packed, const float* bias,
+                                 int32_t cin, int32_t cout, int32_t T, int32_t stride, float* y,
+                                 void* stream) {
+  int rc = check_conv_ptrs(x, packed, y);
+  if (rc) return rc;
+  if (bias && ((uintptr_t)bias & 3))
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "bias %p not 4-byte aligned", (const void*)bias);
+  if (cin < 1 || cout < 1 || T < 1 || stride < 1)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "cin %d, cout %d, T %d, stride %d: all >= 1", cin,
+                cout, T, stride);
+  if (too_big(cin, T) || too_big((int64_t)cout * T, stride) ||
+      too_big((int64_t)cin * cout, 2 * (int64_t)stride))
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "tensor beyond 2^31 elements");
+  ConvArgs a{};
+  a.x = x;
+  a.w = packed;
+  a.bias = bias;
+  a.y = y;
+  a.cin = cin;
+  a.cout = cout;
+  a.T = T;
+  a.K = 2;
+  a.dil = 1;
+  a.ldy = T * stride;
+  a.ystride = stride;
+  a.P = stride;
+  const hipError_t e = launch_conv(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "codec_transconv1d");
+}
+
 // ---------------------------------------------------------------- generation
 
 namespace {

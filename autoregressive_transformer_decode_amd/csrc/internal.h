@@ -295,6 +295,23 @@ struct QuantArgs {
   uint16_t* scales;      // [rows, cols / kQBlock]
 };
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+
+// Codec convolutions as GEMMs over (input channel, tap): output frame t of
+// phase p is y[co * ldy + t * ystride + p] = bias[co] + sum over r = ci*K + j
+// of w[p][co][r] * x[ci][t - (K-1-j) * dil]  (x = 0 outside [0, T)).
+struct ConvArgs {
+  const float* x;      // [cin, T] channel-major
+  const float* w;      // [P][cout][cin * K]
+  const float* bias;   // [cout] or null
+  float* y;
+  int cin, cout, T, K, dil;
+  int ldy, ystride, P;
+};
+hipError_t launch_conv(const ConvArgs& a, hipStream_t s);
+// [cin][cout][2s] transposed-convolution weights -> [s][cout][cin * 2] phases
+// (tap 0 reads the previous frame with w[..][p + s], tap 1 the frame with w[..][p])
+hipError_t launch_pack_transconv(const float* w, int cin, int cout, int s_, float* packed,
+                                 hipStream_t s);
 hipError_t launch_rope_append(const RopeArgs& a, int bf16, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream_t s);
 hipError_t launch_advance(const SlotTables& st, RowMap rows, int M, hipStream_t s);

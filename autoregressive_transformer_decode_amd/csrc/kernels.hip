@@ -620,6 +620,83 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ codec convolutions
+// 64 output channels x 64 frames per workgroup, 4 x 4 per thread; the
+// reduction over (input channel, tap) runs in chunks of 16: the weight chunk
+// and the 16 shifted input rows are staged in LDS, each thread then reads
+// 4 weights and 4 inputs per reduction index (float4) for 16 FMAs.
+constexpr int kConvTile = 64, kConvR = 16;
+
+__global__ __launch_bounds__(256) void k_conv1d(ConvArgs a) {
+  __shared__ float Ws[kConvR][kConvTile + 4];
+  __shared__ float Xs[kConvR][kConvTile + 4];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kConvTile, c0 = blockIdx.y * kConvTile, p = blockIdx.z;
+  const int ty = tid >> 4, tx = tid & 15;   // channels 4ty.., frames 4tx..
+  const int R = a.cin * a.K;
+  const float* W = a.w + (size_t)p * a.cout * R;
+  float acc[4][4] = {};
+  for (int r0 = 0; r0 < R; r0 += kConvR) {
+    {   // weights: thread -> channel tid / 4, reduction indices 4 * (tid % 4) ..
+      const int cl = tid >> 2, rl = (tid & 3) * 4, co = c0 + cl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + rl + i;
+        Ws[rl + i][cl] = (co < a.cout && r < R) ? W[(size_t)co * R + r] : 0.f;
+      }
+    }
+    {   // inputs: thread -> reduction index tid / 16, frames 4 * (tid % 16) ..
+      const int rl = tid >> 4, tl = (tid & 15) * 4, r = r0 + rl;
+      const int ci = r / a.K, j = r - ci * a.K;
+      const int shift = (a.K - 1 - j) * a.dil;
+      const float* xr = a.x + (size_t)(r < R ? ci : 0) * a.T;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + tl + i - shift;
+        Xs[rl][tl + i] = (r < R && t >= 0 && t < a.T) ? xr[t] : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < kConvR; ++rr) {
+      const float4 wv = *reinterpret_cast<const float4*>(&Ws[rr][4 * ty]);
+      const float4 xv = *reinterpret_cast<const float4*>(&Xs[rr][4 * tx]);
+      const float wa[4] = {wv.x, wv.y, wv.z, wv.w}, xa[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[i][k] = fmaf(wa[i], xa[k], acc[i][k]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int co = c0 + 4 * ty + i;
+    if (co >= a.cout) continue;
+    const float bv = a.bias ? a.bias[co] : 0.f;
+    float* yr = a.y + (size_t)co * a.ldy + p;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = t0 + 4 * tx + k;
+      if (t < a.T) yr[(size_t)t * a.ystride] = acc[i][k] + bv;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pack_transconv(const float* w, int cin, int cout, int s_,
+                                                        float* packed) {
+  const size_t n = (size_t)s_ * cout * cin * 2;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const int j = (int)(i & 1);
+    const size_t q = i >> 1;
+    const int ci = (int)(q % cin);
+    const size_t q2 = q / cin;
+    const int co = (int)(q2 % cout), p = (int)(q2 / cout);
+    const int k = j == 0 ? p + s_ : p;   // tap 0: previous frame, tap 1: this frame
+    packed[i] = w[((size_t)ci * cout + co) * (2 * s_) + k];
+  }
+}
+
 // ------------------------------------------------------------------ attention
 // Split-K decode attention, one split per wave.  Block (split group, kv head
 // g, row m); wave w takes split 4*blockIdx.x + w of the row's key range
@@ -1865,6 +1942,21 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int wtype, hipStre
     case kWQ4: gemv_dispatch<WQ4>(a, epi, norm, s); break;
     default: gemv_dispatch<float>(a, epi, norm, s); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
+  const dim3 grid((a.T + kConvTile - 1) / kConvTile, (a.cout + kConvTile - 1) / kConvTile, a.P);
+  hipLaunchKernelGGL(k_conv1d, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_transconv(const float* w, int cin, int cout, int s_, float* packed,
+                                 hipStream_t s) {
+  const size_t n = (size_t)s_ * cout * cin * 2;
+  const size_t nb = (n + 255) / 256;
+  const unsigned blocks = (unsigned)(nb < 65535 ? nb : 65535);
+  hipLaunchKernelGGL(k_pack_transconv, dim3(blocks), dim3(256), 0, s, w, cin, cout, s_, packed);
   return hipGetLastError();
 }
 

@@ -343,3 +343,38 @@ def fill_batched_caches(dec: "Decoder", lens: Sequence[int], seed: int = 0) -> N
     for b, n in enumerate(lens):
         dec.set_position(b, int(n))
 
+
+
+def conv1d_causal(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor],
+                  dilation: int = 1, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal dilated 1-D convolution (codec_conv1d_causal): x [Cin, T],
+    w [Cout, Cin, K] float32 on the device -> [Cout, T]."""
+    cin, T = x.shape
+    cout, _, K = w.shape
+    if y is None:
+        y = torch.empty(cout, T, device=x.device, dtype=torch.float32)
+    B.codec_conv1d_causal(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                          cin, cout, T, K, dilation, y.data_ptr(), _stream())
+    return y
+
+
+def transconv1d_pack(w: torch.Tensor, stride: int) -> torch.Tensor:
+    """Phase-packed weights of a transposed convolution w [Cin, Cout, 2s]."""
+    cin, cout, K = w.shape
+    assert K == 2 * stride
+    packed = torch.empty(stride, cout, cin * 2, device=w.device, dtype=torch.float32)
+    B.codec_transconv1d_pack(w.data_ptr(), cin, cout, stride, packed.data_ptr(), _stream())
+    return packed
+
+
+def transconv1d(x: torch.Tensor, packed: torch.Tensor, bias: Optional[torch.Tensor], stride: int,
+                y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Transposed 1-D convolution by phases (codec_transconv1d): x [Cin, T]
+    -> [Cout, T * stride]."""
+    cin, T = x.shape
+    cout = packed.shape[1]
+    if y is None:
+        y = torch.empty(cout, T * stride, device=x.device, dtype=torch.float32)
+    B.codec_transconv1d(x.data_ptr(), packed.data_ptr(), bias.data_ptr() if bias is not None else None,
+                        cin, cout, T, stride, y.data_ptr(), _stream())
+    return y

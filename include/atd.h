@@ -423,6 +423,32 @@ int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_decoder* cp, in
 int quantize_blocks(const void* w, int32_t dtype, int64_t rows, int32_t cols, int32_t format,
                     void* codes, uint16_t* scales, void* stream);
 
+/* Codec decoder convolutions (qwen3-tts-hip OPTIMIZATION_LOG, codec entries:
+ * the decoder's time goes to a dilated causal convolution and a transposed
+ * convolution, the latter rewritten by output phase as GEMMs over prepacked
+ * weights).  float32, channel-major [channels, frames], device pointers
+ * 4-byte aligned; the outputs may not overlap the inputs.
+ *
+ * codec_conv1d_causal: y[co, t] = bias[co] + sum over ci < cin, j < K of
+ *   w[co, ci, j] * x[ci, t - (K-1-j) * dilation], x = 0 before frame 0.
+ *   x [cin, T], w [cout, cin, K], bias [cout] or NULL, y [cout, T].
+ * codec_transconv1d_pack: the weights of a transposed convolution with
+ *   kernel 2 * stride, w [cin, cout, 2 * stride], rearranged once (at load
+ *   time) into packed [stride, cout, cin * 2] for codec_transconv1d.
+ * codec_transconv1d: y[co, t * stride + p] = bias[co] + sum over ci of
+ *   w[ci, co, p] x[ci, t] + w[ci, co, p + stride] x[ci, t - 1] (x[., -1] = 0)
+ *   for t < T, p < stride: the transposed convolution's first T * stride
+ *   outputs.  x [cin, T], y [cout, T * stride].
+ * Errors: INVALID_ARG (NULL / misaligned pointer, sizes < 1, cin * K or a
+ * tensor beyond 2^31 elements), DEVICE. */
+int codec_conv1d_causal(const float* x, const float* w, const float* bias, int32_t cin,
+                        int32_t cout, int32_t T, int32_t K, int32_t dilation, float* y,
+                        void* stream);
+int codec_transconv1d_pack(const float* w, int32_t cin, int32_t cout, int32_t stride,
+                           float* packed, void* stream);
+int codec_transconv1d(const float* x, const float* packed, const float* bias, int32_t cin,
+                      int32_t cout, int32_t T, int32_t stride, float* y, void* stream);
+
 /* Stages of a decode step, for decoder_time_stage. */
 enum {
   ATD_STAGE_QKV = 0,     /* RMSNorm + q/k/v projection                       */

@@ -117,7 +117,7 @@ def _load():
                                     C.POINTER(atd_sampling), C.POINTER(atd_sampling),
                                     C.POINTER(atd_controls), vp, vp, vp, vp], C.c_int),
         "quantize_blocks": ([vp, i32, C.c_int64, i32, i32, vp, vp, vp], C.c_int),
-        "codec_conv1d_causal": ([vp, vp, vp, i32, i32, i32, i32, i32, vp, vp], C.c_int),
+        "codec_conv1d_causal": ([vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp], C.c_int),
         "codec_transconv1d_pack": ([vp, i32, i32, i32, vp, vp], C.c_int),
         "codec_transconv1d": ([vp, vp, vp, i32, i32, i32, i32, vp, vp], C.c_int),
         "decoder_time_stage": ([vp, i32, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
@@ -237,8 +237,8 @@ def quantize_blocks(w: int, dtype: int, rows: int, cols: int, fmt: int, codes: i
 
 
 def codec_conv1d_causal(x: int, w: int, bias, cin: int, cout: int, T: int, K: int,
-                        dilation: int, y: int, stream: int) -> None:
-    _check(lib.codec_conv1d_causal(x, w, bias, cin, cout, T, K, dilation, y, stream))
+                        dilation: int, accumulate: int, y: int, stream: int) -> None:
+    _check(lib.codec_conv1d_causal(x, w, bias, cin, cout, T, K, dilation, accumulate, y, stream))
 
 
 def codec_transconv1d_pack(w: int, cin: int, cout: int, stride: int, packed: int,

@@ -1198,7 +1198,7 @@ bool too_big(int64_t a, int64_t b) { return a * b >= ((int64_t)1 << 31); }
 
 extern "C" int codec_conv1d_causal(const float* x, const float* w, const float* bias,
                                    int32_t cin, int32_t cout, int32_t T, int32_t K,
-                                   int32_t dilation, float* y, void* stream) {
+                                   int32_t dilation, int32_t accumulate, float* y, void* stream) {
   int rc = check_conv_ptrs(x, w, y);
   if (rc) return rc;
   if (bias && ((uintptr_t)bias & 3))
@@ -1221,6 +1221,7 @@ extern "C" int codec_conv1d_causal(const float* x, const float* w, const float* 
   a.ldy = T;
   a.ystride = 1;
   a.P = 1;
+  a.accumulate = accumulate != 0;
   const hipError_t e = launch_conv(a, (hipStream_t)stream);
   return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "codec_conv1d_causal");
 }

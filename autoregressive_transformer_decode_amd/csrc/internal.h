@@ -306,6 +306,7 @@ struct ConvArgs {
   float* y;
   int cin, cout, T, K, dil;
   int ldy, ystride, P;
+  int accumulate;      // 1: y += the result (a residual add)
 };
 hipError_t launch_conv(const ConvArgs& a, hipStream_t s);
 // [cin][cout][2s] transposed-convolution weights -> [s][cout][cin * 2] phases

@@ -678,7 +678,10 @@ __global__ __launch_bounds__(256) void k_conv1d(ConvArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int t = t0 + 4 * tx + k;
-      if (t < a.T) yr[(size_t)t * a.ystride] = acc[i][k] + bv;
+      if (t < a.T) {
+        float* o = yr + (size_t)t * a.ystride;
+        *o = (a.accumulate ? *o : 0.f) + (acc[i][k] + bv);
+      }
     }
   }
 }

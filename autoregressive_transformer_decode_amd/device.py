@@ -346,15 +346,17 @@ def fill_batched_caches(dec: "Decoder", lens: Sequence[int], seed: int = 0) -> N
 
 
 def conv1d_causal(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor],
-                  dilation: int = 1, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  dilation: int = 1, y: Optional[torch.Tensor] = None,
+                  accumulate: bool = False) -> torch.Tensor:
     """Causal dilated 1-D convolution (codec_conv1d_causal): x [Cin, T],
-    w [Cout, Cin, K] float32 on the device -> [Cout, T]."""
+    w [Cout, Cin, K] float32 on the device -> [Cout, T] (added to y when
+    accumulate)."""
     cin, T = x.shape
     cout, _, K = w.shape
     if y is None:
         y = torch.empty(cout, T, device=x.device, dtype=torch.float32)
     B.codec_conv1d_causal(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
-                          cin, cout, T, K, dilation, y.data_ptr(), _stream())
+                          cin, cout, T, K, dilation, int(accumulate), y.data_ptr(), _stream())
     return y
 
 

@@ -353,3 +353,76 @@ def uniforms(seed: int, stream: int, n) -> np.ndarray:
     ``n`` may be a shape."""
     rng = np.random.default_rng([seed, 2, _T_UNIFORM, stream])
     return rng.random(n, dtype=np.float32)
+
+
+
+@dataclasses.dataclass(frozen=True)
+class CodecShape:
+    """Convolution stack of a codec decoder: an input convolution, stages of
+    (transposed convolution with kernel 2s, then residual units of a dilated
+    convolution and a 1-tap convolution added back), an output convolution.
+    Channel-major [channels, frames] float32."""
+    name: str
+    frames: int                      # input frames of the stack
+    channels: Tuple[int, ...]        # width before the first stage, after each stage
+    strides: Tuple[int, ...]
+    kernel: int = 7
+    dilations: Tuple[int, ...] = (1, 3, 9)
+    out_channels: int = 1
+
+
+_CODEC_ID = 12   # model id of the codec stack's random streams
+
+# 6 s of audio: 300 frames of the convolution stack's input, x 480 -> 144000 samples
+CODEC = CodecShape("codec", frames=300, channels=(1024, 512, 256, 128, 64), strides=(8, 5, 4, 3))
+
+
+def codec_layers(c: CodecShape):
+    """The stack in order: ("conv", cin, cout, K, dilation, T, residual) and
+    ("trans", cin, cout, stride, T_in) entries."""
+    T, ch = c.frames, c.channels
+    out = [("conv", ch[0], ch[0], c.kernel, 1, T, False)]
+    for i, s_ in enumerate(c.strides):
+        out.append(("trans", ch[i], ch[i + 1], s_, T))
+        T *= s_
+        for d in c.dilations:
+            out.append(("conv", ch[i + 1], ch[i + 1], c.kernel, d, T, False))
+            out.append(("conv", ch[i + 1], ch[i + 1], 1, 1, T, True))
+    out.append(("conv", ch[-1], c.out_channels, c.kernel, 1, T, False))
+    return out
+
+
+def codec_flops(c: CodecShape) -> float:
+    f = 0.0
+    for L in codec_layers(c):
+        if L[0] == "conv":
+            _, cin, cout, K, _, T, _ = L
+            f += 2.0 * cin * cout * K * T
+        else:
+            _, cin, cout, s_, T = L
+            f += 2.0 * cin * cout * 2 * T * s_
+    return f
+
+
+def make_codec_weights(c: CodecShape, seed: int = 0):
+    """Per layer (weights, bias): conv [cout, cin, K], transposed [cin, cout, 2s];
+    N(0, 1/fan_in) weights (0.09/fan_in for a residual branch's 1-tap
+    convolution) and N(0, 0.01) biases."""
+    ws = []
+    for i, L in enumerate(codec_layers(c)):
+        if L[0] == "conv":
+            _, cin, cout, K, _, _, res = L
+            # a residual branch's last convolution is drawn smaller, so that
+            # twelve residual additions keep the activations O(1)
+            sc = (0.3 if res else 1.0) / math.sqrt(cin * K)
+            w = normal(seed, _CODEC_ID, 2 * i, (cout, cin, K), scale=sc)
+        else:
+            _, cin, cout, s_, _ = L
+            w = normal(seed, _CODEC_ID, 2 * i, (cin, cout, 2 * s_), scale=1.0 / math.sqrt(2 * cin))
+        ws.append((w, normal(seed, _CODEC_ID, 2 * i + 1, (L[2],), scale=0.1)))
+    return ws
+
+
+def codec_input(c: CodecShape, seed: int = 0) -> np.ndarray:
+    """[channels[0], frames] N(0, 1) input of the stack."""
+    return normal(seed, _CODEC_ID, 9999, (c.channels[0], c.frames), scale=1.0)

@@ -557,6 +557,169 @@ def bench_frames(args, wl):
         roofline=None, cpu_baseline=None)
 
 
+ALU_PEAK_TFLOPS = 157.3          # fp32 vector, published (packed FP32 counted)
+ALU_UNPACKED_TFLOPS = 78.6       # 256 CUs x 64 FMA lanes x 2 flops x 2.4 GHz
+
+
+def codec_stack(layers, run_conv, run_trans, h):
+    """Enqueue the codec stack on `h`: run_conv(h, layer_index, out, accumulate)
+    and run_trans(h, layer_index) return their outputs; a dilated convolution
+    followed by a residual 1-tap convolution forms a unit whose result is added
+    to the stage tensor."""
+    u = None
+    for i, L in enumerate(layers):
+        if L[0] == "trans":
+            h = run_trans(h, i)
+        elif L[6]:
+            h = run_conv(u, i, h, True)
+        elif i + 1 < len(layers) and layers[i + 1][0] == "conv" and layers[i + 1][6]:
+            u = run_conv(h, i, None, False)
+        else:
+            h = run_conv(h, i, None, False)
+    return h
+
+
+def bench_codec(args, wl):
+    """The codec decoder's convolution stack (26 causal convolutions, 4
+    transposed) on float32 [channels, frames] tensors: each rep runs the whole
+    stack; per-layer HIP events on the stream give each kernel's time."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from autoregressive_transformer_decode_amd import device as dv
+    from autoregressive_transformer_decode_amd import inputs
+
+    c = wl
+    layers = inputs.codec_layers(c)
+    ws = inputs.make_codec_weights(c, seed=0)
+    dw = []
+    for L, (w, b) in zip(layers, ws):
+        wd, bd = torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
+        dw.append((dv.transconv1d_pack(wd, L[3]) if L[0] == "trans" else wd, bd))
+    x = torch.from_numpy(inputs.codec_input(c, seed=0)).cuda()
+    # one output buffer per layer, allocated before the timed region
+    bufs = []
+    for L in layers:
+        if L[0] == "trans":
+            bufs.append(torch.empty(L[2], L[4] * L[3], device="cuda"))
+        else:
+            bufs.append(None if L[6] else torch.empty(L[2], L[5], device="cuda"))
+    events = None
+
+    def mark(i):
+        if events is not None:
+            events[i].record()
+
+    def run_conv(h, i, out, acc):
+        mark(2 * i)
+        w, b = dw[i]
+        y = dv.conv1d_causal(h, w, b, layers[i][4], y=out if acc else bufs[i], accumulate=acc)
+        mark(2 * i + 1)
+        return y
+
+    def run_trans(h, i):
+        mark(2 * i)
+        y = dv.transconv1d(h, dw[i][0], dw[i][1], layers[i][3], y=bufs[i])
+        mark(2 * i + 1)
+        return y
+
+    reps = args.steps if args.steps is not None else 10
+    warm = max(1, min(args.warmup, 3))
+    for _ in range(warm):
+        out = codec_stack(layers, run_conv, run_trans, x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        out = codec_stack(layers, run_conv, run_trans, x)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    # per-layer times from events around each launch (separate reps)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(layers))]
+    per = np.zeros(len(layers))
+    for _ in range(reps):
+        codec_stack(layers, run_conv, run_trans, x)
+        torch.cuda.synchronize()
+        per += [events[2 * i].elapsed_time(events[2 * i + 1]) for i in range(len(layers))]
+    per = per / reps * 1e-3
+    events = None
+    flops = []
+    for L in layers:
+        if L[0] == "conv":
+            flops.append(2.0 * L[1] * L[2] * L[3] * L[5])
+        else:
+            flops.append(2.0 * L[1] * L[2] * 2 * L[4] * L[3])
+    flops = np.array(flops)
+    conv = np.array([L[0] == "conv" for L in layers])
+    total = float(flops.sum())
+    samples = out.shape[1]
+    conv_t, conv_f = float(per[conv].sum()), float(flops[conv].sum())
+    tr_t, tr_f = float(per[~conv].sum()), float(flops[~conv].sum())
+    # the roofline kernel is k_conv1d, which runs both kinds of layer
+    achieved = total / float(per.sum()) / 1e12
+    log(f"codec stack: {dt * 1e3:.2f} ms ({total / dt / 1e12:.1f} TFLOP/s); causal conv "
+        f"{conv_t * 1e3:.2f} ms at {conv_f / conv_t / 1e12:.1f} TFLOP/s, transposed {tr_t * 1e3:.2f} ms at "
+        f"{tr_f / tr_t / 1e12:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = codec_cpu_baseline(c, args.cpu_seconds)
+    return dict(
+        metric="codec decoder convolution stack: output samples/s", value=samples / dt,
+        unit="samples/s", n_gpus=1, steps=reps, warmup=warm, ms_per_step=dt * 1e3,
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32", data="synthetic",
+        config=dict(workload="codec", frames=c.frames, channels=list(c.channels),
+                    strides=list(c.strides), kernel=c.kernel, dilations=list(c.dilations),
+                    causal_convs=int(conv.sum()), transposed_convs=int((~conv).sum()),
+                    output_samples=int(samples),
+                    step="the whole stack, one launch per layer (codec_conv1d_causal, "
+                         "codec_transconv1d), weights prepacked before timing"),
+        tflops=total / dt / 1e12, gflop_per_step=total / 1e9,
+        audio_s_per_s=samples / 24000.0 / dt,
+        per_layer_ms=[round(t * 1e3, 4) for t in per],
+        transconv=dict(ms=tr_t * 1e3, tflops=tr_f / tr_t / 1e12),
+        causal_conv=dict(ms=conv_t * 1e3, tflops=conv_f / conv_t / 1e12),
+        roofline=dict(bound="alu", achieved=achieved, peak=ALU_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=achieved / ALU_PEAK_TFLOPS, traffic=None,
+                      kernel="k_conv1d (causal and phase-split transposed convolutions), "
+                             "all 30 launches of a stack",
+                      flops_per_launch=total / len(layers),
+                      avg_launch_us=float(per.sum()) / len(layers) * 1e6,
+                      unpacked_fp32_peak=ALU_UNPACKED_TFLOPS),
+        cpu_baseline=cpu)
+
+
+def codec_cpu_baseline(c, budget_s):
+    """The oracle's stack (float64 numpy) on the first input frames of the same
+    workload: every layer, at reduced length (the cost per output sample of a
+    convolution stack does not depend on the length)."""
+    import dataclasses
+    import numpy as np
+    from autoregressive_transformer_decode_amd import inputs
+    from oracle import codec as oc
+
+    frames = max(1, min(c.frames, int(round(c.frames * budget_s / 75.0))))
+    cs = dataclasses.replace(c, frames=frames)
+    layers = inputs.codec_layers(cs)
+    ws = inputs.make_codec_weights(cs, seed=0)
+    h = inputs.codec_input(c, seed=0)[:, :frames].astype(np.float64)
+
+    def run_conv(h, i, out, acc):
+        w, b = ws[i]
+        y = oc.conv1d_causal(h, w, b, layers[i][4])
+        return out + y if acc else y
+
+    def run_trans(h, i):
+        return oc.transconv1d(h, ws[i][0], ws[i][1], layers[i][3])
+
+    t0, c0 = time.perf_counter(), time.process_time()
+    out = codec_stack(layers, run_conv, run_trans, h)
+    dt, cpu_s = time.perf_counter() - t0, time.process_time() - c0
+    # threads actually used: process CPU time over wall time
+    return dict(value=out.shape[1] / dt, unit="samples/s", cores=max(1, round(cpu_s / dt)),
+                kind="oracle",
+                sample=f"the whole stack on the first {frames} of {c.frames} input frames "
+                       f"({out.shape[1]} output samples) in {dt:.1f} s, float64 numpy")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -564,7 +727,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--workload", default="talker1.7b",
                     choices=["talker1.7b", "asr", "tiny", "batched64", "talker0.6b",
-                             "talker1.7b-frames"])
+                             "talker1.7b-frames", "codec"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true",
@@ -592,6 +755,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4, "launches": 8}))
         return
     from autoregressive_transformer_decode_amd import inputs
+    if args.workload == "codec":
+        print(json.dumps(bench_codec(args, inputs.CODEC)), flush=True)
+        return
     wl = inputs.WORKLOADS[args.workload]
     if wl.cp is not None:
         out = bench_frames(args, wl)

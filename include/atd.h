@@ -431,7 +431,8 @@ int quantize_blocks(const void* w, int32_t dtype, int64_t rows, int32_t cols, in
  *
  * codec_conv1d_causal: y[co, t] = bias[co] + sum over ci < cin, j < K of
  *   w[co, ci, j] * x[ci, t - (K-1-j) * dilation], x = 0 before frame 0.
- *   x [cin, T], w [cout, cin, K], bias [cout] or NULL, y [cout, T].
+ *   x [cin, T], w [cout, cin, K], bias [cout] or NULL, y [cout, T]; with
+ *   accumulate = 1 the result is added to y (a residual connection).
  * codec_transconv1d_pack: the weights of a transposed convolution with
  *   kernel 2 * stride, w [cin, cout, 2 * stride], rearranged once (at load
  *   time) into packed [stride, cout, cin * 2] for codec_transconv1d.
@@ -442,8 +443,8 @@ int quantize_blocks(const void* w, int32_t dtype, int64_t rows, int32_t cols, in
  * Errors: INVALID_ARG (NULL / misaligned pointer, sizes < 1, cin * K or a
  * tensor beyond 2^31 elements), DEVICE. */
 int codec_conv1d_causal(const float* x, const float* w, const float* bias, int32_t cin,
-                        int32_t cout, int32_t T, int32_t K, int32_t dilation, float* y,
-                        void* stream);
+                        int32_t cout, int32_t T, int32_t K, int32_t dilation, int32_t accumulate,
+                        float* y, void* stream);
 int codec_transconv1d_pack(const float* w, int32_t cin, int32_t cout, int32_t stride,
                            float* packed, void* stream);
 int codec_transconv1d(const float* x, const float* packed, const float* bias, int32_t cin,

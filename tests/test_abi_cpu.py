@@ -405,21 +405,21 @@ def test_codec_argument_checks():
     """The codec convolutions refuse NULL / misaligned pointers and sizes
     below 1 before any device call."""
     with pytest.raises(B.AtdError) as ei:
-        B.codec_conv1d_causal(None, 0x100, None, 4, 4, 8, 3, 1, 0x200, 0)
+        B.codec_conv1d_causal(None, 0x100, None, 4, 4, 8, 3, 1, 0, 0x200, 0)
     assert ei.value.code == B.ATD_ERR_INVALID_ARG
     with pytest.raises(B.AtdError) as ei:
-        B.codec_conv1d_causal(0x102, 0x100, None, 4, 4, 8, 3, 1, 0x200, 0)
+        B.codec_conv1d_causal(0x102, 0x100, None, 4, 4, 8, 3, 1, 0, 0x200, 0)
     assert "aligned" in str(ei.value)
     for args in [(0, 4, 8, 3, 1), (4, 4, 8, 0, 1), (4, 4, 8, 3, 0), (4, 4, 0, 3, 1)]:
         with pytest.raises(B.AtdError) as ei:
-            B.codec_conv1d_causal(0x100, 0x200, None, *args, 0x300, 0)
+            B.codec_conv1d_causal(0x100, 0x200, None, *args, 0, 0x300, 0)
         assert ei.value.code == B.ATD_ERR_INVALID_ARG
     with pytest.raises(B.AtdError):
-        B.codec_conv1d_causal(0x100, 0x200, 0x301, 4, 4, 8, 3, 1, 0x300, 0)
+        B.codec_conv1d_causal(0x100, 0x200, 0x301, 4, 4, 8, 3, 1, 0, 0x300, 0)
     with pytest.raises(B.AtdError):
         B.codec_transconv1d(0x100, 0x200, None, 4, 4, 8, 0, 0x300, 0)
     with pytest.raises(B.AtdError):
         B.codec_transconv1d_pack(0x100, 4, 0, 2, 0x200, 0)
     with pytest.raises(B.AtdError) as ei:
-        B.codec_conv1d_causal(0x100, 0x200, None, 1 << 16, 4, 1 << 16, 3, 1, 0x300, 0)
+        B.codec_conv1d_causal(0x100, 0x200, None, 1 << 16, 4, 1 << 16, 3, 1, 0, 0x300, 0)
     assert "2^31" in str(ei.value)

@@ -88,3 +88,42 @@ def test_transconv1d(case):
             e = max(e, normwise_rel(got[:, t * s:(t + 1) * s], seg))
     _log(f"  normwise {e:.2e}")
     assert e <= TOL
+
+
+def test_conv1d_accumulate_and_stack():
+    """accumulate adds the result to y (a residual connection); a reduced
+    copy of the decoder stack (16 input frames, narrower channels) run layer by layer equals the
+    oracle's."""
+    x = _rand(7, 0, (48, 100), 1.0)
+    w = _rand(8, 0, (40, 48, 3), 0.1)
+    y0 = _rand(9, 0, (40, 100), 1.0)
+    y = torch.from_numpy(y0.copy()).cuda()
+    dv.conv1d_causal(torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda(), None, 2, y=y,
+                     accumulate=True)
+    torch.cuda.synchronize()
+    assert normwise_rel(y.cpu().numpy(), y0 + oc.conv1d_causal(x, w, None, 2)) <= TOL
+    import dataclasses
+    c = dataclasses.replace(inputs.CODEC, frames=16, channels=(128, 96, 64, 48, 32))
+    layers = inputs.codec_layers(c)
+    ws = inputs.make_codec_weights(c, seed=1)
+    h = inputs.codec_input(c, seed=1).astype(np.float32)
+    hd = torch.from_numpy(h).cuda()
+    h = h.astype(np.float64)
+    for i, (L, (w, b)) in enumerate(zip(layers, ws)):
+        wd, bd = torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
+        if L[0] == "trans":
+            hd = dv.transconv1d(hd, dv.transconv1d_pack(wd, L[3]), bd, L[3])
+            h = oc.transconv1d(h, w, b, L[3])
+        elif L[6]:   # 1-tap convolution of the unit's dilated output, added back
+            dv.conv1d_causal(ud, wd, bd, 1, y=hd, accumulate=True)
+            h = h + oc.conv1d_causal(u, w, b, 1)
+        elif i + 1 < len(layers) and layers[i + 1][0] == "conv" and layers[i + 1][6]:
+            ud = dv.conv1d_causal(hd, wd, bd, L[4])
+            u = oc.conv1d_causal(h, w, b, L[4])
+        else:
+            hd = dv.conv1d_causal(hd, wd, bd, L[4])
+            h = oc.conv1d_causal(h, w, b, L[4])
+    torch.cuda.synchronize()
+    e = normwise_rel(hd.cpu().numpy(), h)
+    _log(f"reduced decoder stack: output {tuple(hd.shape)}, normwise {e:.2e}")
+    assert hd.shape == (1, 16 * 480) and e <= 1e-4

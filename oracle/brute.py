@@ -50,14 +50,37 @@ def _f32(x: float) -> float:
     return struct.unpack("f", struct.pack("f", x))[0]
 
 
-def _rotate(v: List[float], pos: int, theta: float) -> List[float]:
-    """Rotate channel pairs (i, i + D/2) by pos * theta^(-2i/D); the cosine
-    and sine are taken at float32 precision, as the definition fixes."""
+def _freq_positions(pos, half: int, sections) -> List[int]:
+    """Position of each rotary frequency: pos itself (an int), or for
+    (t, h, w) positions under interleaved sections, frequency i in group
+    i // 3 takes h at offset 1 while that group is below s_h, w at offset 2
+    while below s_w, and t otherwise."""
+    if isinstance(pos, int):
+        return [pos] * half
+    t, h, w = pos
+    s_h, s_w = (0, 0) if sections is None else (sections[1], sections[2])
+    out = []
+    for i in range(half):
+        grp, off = divmod(i, 3)
+        if off == 1 and grp < s_h:
+            out.append(h)
+        elif off == 2 and grp < s_w:
+            out.append(w)
+        else:
+            out.append(t)
+    return out
+
+
+def _rotate(v: List[float], pos, theta: float, sections=None) -> List[float]:
+    """Rotate channel pairs (i, i + D/2) by p_i * theta^(-2i/D) with p_i the
+    frequency's position (_freq_positions); the cosine and sine are taken at
+    float32 precision, as the definition fixes."""
     D = len(v)
     half = D // 2
+    ps = _freq_positions(pos, half, sections)
     out = list(v)
     for i in range(half):
-        ang = pos * theta ** (-2.0 * i / D)
+        ang = ps[i] * theta ** (-2.0 * i / D)
         c, s = _f32(math.cos(ang)), _f32(math.sin(ang))
         a, b = v[i], v[i + half]
         out[i] = a * c - b * s
@@ -65,9 +88,10 @@ def _rotate(v: List[float], pos: int, theta: float) -> List[float]:
     return out
 
 
-def forward_rows(model, rows: Sequence[Sequence[float]]) -> List[List[float]]:
+def forward_rows(model, rows: Sequence[Sequence[float]], rope_pos=None) -> List[List[float]]:
     """Residual stream after the last layer for every row, rows at positions
-    0..T-1, row t attending to rows 0..t (recomputed, no cache)."""
+    0..T-1, row t attending to rows 0..t (recomputed, no cache).  rope_pos:
+    per row (t, h, w) rotary positions in place of the row index."""
     hq, hkv, D = model.n_q_heads, model.n_kv_heads, model.head_dim
     grp = hq // hkv
     eps = model.rms_eps
@@ -94,8 +118,10 @@ def forward_rows(model, rows: Sequence[Sequence[float]]) -> List[List[float]]:
             if model.qk_norm:
                 qh = [_rms(a, L["q_norm"], eps) for a in qh]
                 kh = [_rms(a, L["k_norm"], eps) for a in kh]
-            qh = [_rotate(a, t, model.rope_theta) for a in qh]
-            kh = [_rotate(a, t, model.rope_theta) for a in kh]
+            rp = t if rope_pos is None else tuple(int(c) for c in rope_pos[t])
+            sec = getattr(model, "mrope_sections", None)
+            qh = [_rotate(a, rp, model.rope_theta, sec) for a in qh]
+            kh = [_rotate(a, rp, model.rope_theta, sec) for a in kh]
             if model.kv_bf16:
                 kh = [[_bf16(c) for c in a] for a in kh]
                 vh = [[_bf16(c) for c in a] for a in vh]
@@ -127,8 +153,8 @@ def forward_rows(model, rows: Sequence[Sequence[float]]) -> List[List[float]]:
     return xs
 
 
-def last_outputs(model, rows, head: int = 0):
+def last_outputs(model, rows, head: int = 0, rope_pos=None):
     """(y, z) of the last row: final RMSNorm and LM head."""
-    x = forward_rows(model, rows)[-1]
+    x = forward_rows(model, rows, rope_pos)[-1]
     y = _rms(x, model.final_norm, model.rms_eps)
     return y, _matvec(model.heads[head], y)

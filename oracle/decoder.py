@@ -5,7 +5,8 @@ Sources, by page title and section:
 * "Qwen3-TTS ncnn port" (ncnn discussion 6799), section "Talker: non-standard
   structure and two-level generation": 28-layer Qwen3-style Talker, QK RMSNorm
   over head_dim after the q/k projections, 8 KV heads broadcast to 16 query
-  heads, interleaved mRoPE that reduces to plain RoPE for TTS, and the
+  heads, interleaved mRoPE ([24, 20, 20] sections over the frequencies; it
+  reduces to plain RoPE for TTS, where the t/h/w positions agree), and the
   two-level frame loop (one Talker token, then 15 Code Predictor codes; the
   sum of the 16 code embeddings plus the text embedding is the next Talker
   input), repetition penalty 1.05 on the main token.
@@ -66,6 +67,7 @@ class Model:
     dtype: type = np.float64
     in_proj: Optional[np.ndarray] = None       # [h, h_in] input projection, or None
     in_proj_bias: Optional[np.ndarray] = None  # [h] or None
+    mrope_sections: Optional[Tuple[int, int, int]] = None  # (s_t, s_h, s_w), or plain RoPE
 
     @property
     def input_dim(self) -> int:
@@ -119,6 +121,40 @@ def rope_cos_sin(pos: int, head_dim: int, theta: float) -> Tuple[np.ndarray, np.
     i = np.arange(head_dim // 2, dtype=np.float64)
     omega = theta ** (-2.0 * i / head_dim)
     phi = float(pos) * omega
+    return np.cos(phi).astype(np.float32), np.sin(phi).astype(np.float32)
+
+
+def mrope_modality(half: int, sections: Optional[Tuple[int, int, int]]) -> np.ndarray:
+    """Which position (0 = t, 1 = h, 2 = w) drives each rotary frequency
+    i < D/2 under interleaved sections (s_t, s_h, s_w).  The ncnn port's
+    Talker section gives the map for [24, 20, 20] at D = 128: frequency i
+    takes i mod 3 while i < 60 and t from there on.  For other sections the
+    reading is the same interleave: i takes h when i mod 3 = 1 and i < 3 s_h,
+    w when i mod 3 = 2 and i < 3 s_w, and t otherwise (so s_t + s_h + s_w =
+    D/2 with 3 max(s_h, s_w) <= D/2).  None: every frequency takes t."""
+    m = np.zeros(half, np.int64)
+    if sections is None:
+        return m
+    s_t, s_h, s_w = sections
+    if s_t + s_h + s_w != half or 3 * max(s_h, s_w) > half or min(sections) < 0:
+        raise ValueError(f"mRoPE sections {sections} do not fit D/2 = {half}")
+    i = np.arange(half)
+    m[(i % 3 == 1) & (i < 3 * s_h)] = 1
+    m[(i % 3 == 2) & (i < 3 * s_w)] = 2
+    return m
+
+
+def mrope_cos_sin(pos3: Sequence[int], head_dim: int, theta: float,
+                  sections: Optional[Tuple[int, int, int]]) -> Tuple[np.ndarray, np.ndarray]:
+    """Angles of a row with rotary positions (t, h, w): frequency i turns by
+    pos3[modality(i)] * omega_i, evaluated and rounded as in rope_cos_sin.
+    With t = h = w this is rope_cos_sin(t) (the ncnn port's observation that
+    the interleave reduces to plain RoPE for TTS)."""
+    half = head_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    omega = theta ** (-2.0 * i / head_dim)
+    p = np.asarray(pos3, np.float64)[mrope_modality(half, sections)]
+    phi = p * omega
     return np.cos(phi).astype(np.float32), np.sin(phi).astype(np.float32)
 
 
@@ -255,16 +291,23 @@ def head_out(model: Model, x: np.ndarray, head: int):
     return y, y @ model.heads[head].T
 
 
-def step(model: Model, cache: Cache, x: np.ndarray, head: int = 0):
+def step(model: Model, cache: Cache, x: np.ndarray, head: int = 0,
+         rope_pos: Optional[Sequence[int]] = None):
     """One decode step of one stream at position cache.pos; returns (y, z)
     and advances the position by one.  Per layer: input RMSNorm, q/k/v
     projections (+bias), QK norm, RoPE at p, cache append, attention over rows
-    0..p, output projection + residual, post norm, SwiGLU MLP + residual."""
+    0..p, output projection + residual, post norm, SwiGLU MLP + residual.
+    rope_pos = (t, h, w) rotates by those positions (mrope_cos_sin) instead of
+    p; the row is still cached at p."""
     p = cache.pos
     if p >= cache.capacity:
         raise ValueError("KV cache full")
     x = project_input(model, x)
-    cos, sin = rope_cos_sin(p, model.head_dim, model.rope_theta)
+    if rope_pos is None:
+        cos, sin = rope_cos_sin(p, model.head_dim, model.rope_theta)
+    else:
+        cos, sin = mrope_cos_sin(rope_pos, model.head_dim, model.rope_theta,
+                                 model.mrope_sections)
     for l, L in enumerate(model.layers):
         u = rms_norm(x, L["attn_norm"], model.rms_eps)
         q, k, v = _qkv(model, L, u)
@@ -279,16 +322,22 @@ def step(model: Model, cache: Cache, x: np.ndarray, head: int = 0):
     return head_out(model, x, head)
 
 
-def prefill(model: Model, cache: Cache, X: np.ndarray, head: int = 0):
+def prefill(model: Model, cache: Cache, X: np.ndarray, head: int = 0,
+            rope_pos: Optional[np.ndarray] = None):
     """T rows at positions 0..T-1 (the cache is reset first), written as
     whole-block matrix products with a causal mask: row t attends to rows
-    0..t.  Returns (y, z) of the last row."""
+    0..t.  Returns (y, z) of the last row.  rope_pos [T, 3]: the rotary
+    positions (t, h, w) of each row in place of its index."""
     X = project_input(model, X)
     T = X.shape[0]
     if T == 0 or T > cache.capacity:
         raise ValueError("prefill length out of range")
     cache.pos = 0
-    cs = [rope_cos_sin(t, model.head_dim, model.rope_theta) for t in range(T)]
+    if rope_pos is None:
+        cs = [rope_cos_sin(t, model.head_dim, model.rope_theta) for t in range(T)]
+    else:
+        cs = [mrope_cos_sin(rope_pos[t], model.head_dim, model.rope_theta, model.mrope_sections)
+              for t in range(T)]
     cos = np.stack([c for c, _ in cs])[:, None, :]
     sin = np.stack([s for _, s in cs])[:, None, :]
     hq, hkv = model.n_q_heads, model.n_kv_heads

@@ -120,22 +120,104 @@ def check_rope_relative():
 
 
 def check_mrope_degenerates():
-    """Interleaved mRoPE sections [24, 20, 20] (ncnn port: base = c % (D/2),
-    modality = base % 3 when base < 60, else 0) with equal t/h/w positions is
-    plain RoPE."""
+    """Interleaved mRoPE with equal t/h/w positions is plain RoPE (ncnn port,
+    Talker section: for TTS the three positions agree and the interleave
+    reduces to ordinary RoPE), bit for bit, for [24, 20, 20] at D = 128."""
     D = 128
-    rng = np.random.default_rng(9)
+    for p in (0, 1, 37, 4095):
+        c, s = od.mrope_cos_sin((p, p, p), D, 1.0e6, (24, 20, 20))
+        c0, s0 = od.rope_cos_sin(p, D, 1.0e6)
+        assert np.array_equal(c, c0) and np.array_equal(s, s0)
+
+
+def check_mrope_sections():
+    """The frequency map of [24, 20, 20] at D = 128 is the one the ncnn port
+    derives per channel: base = c mod (D/2), modality base mod 3 when
+    base < 60, else 0 (t); it gives 24 / 20 / 20 frequencies to t / h / w."""
+    D = 128
+    m = od.mrope_modality(D // 2, (24, 20, 20))
+    for c in range(D):
+        base = c % (D // 2)
+        assert m[base] == (base % 3 if base < 60 else 0)
+    assert [int(np.sum(m == k)) for k in range(3)] == [24, 20, 20]
+
+
+def check_mrope_single_component():
+    """Positions (0, p, 0): the channel pairs of the h frequencies turn by
+    p omega_i, the rest are left as they are (a turn by angle 0); likewise
+    for w, and for t with (p, 0, 0)."""
+    D = 128
+    rng = np.random.default_rng(10)
     v = rng.standard_normal(D)
-    p = 37
-    pos3 = (p, p, p)
     half = D // 2
     i = np.arange(half)
-    modality = np.where(i < 60, i % 3, 0)
-    ang = np.array([pos3[m] for m in modality], np.float64) * 1.0e6 ** (-2.0 * i / D)
-    c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
-    mr = np.concatenate([v[:half] * c - v[half:] * s, v[half:] * c + v[:half] * s])
-    cos, sin = od.rope_cos_sin(p, D, 1.0e6)
-    _close(od.rope(v, cos, sin), mr, 1e-12)
+    for comp in range(3):
+        p = 29
+        pos3 = [0, 0, 0]
+        pos3[comp] = p
+        got = od.rope(v, *od.mrope_cos_sin(pos3, D, 1.0e6, (24, 20, 20)))
+        if comp == 0:
+            moving = (i % 3 == 0) | (i >= 60)
+        else:
+            moving = (i % 3 == comp) & (i < 60)
+        turned = od.rope(v, *od.rope_cos_sin(p, D, 1.0e6))
+        keep = np.concatenate([~moving, ~moving])
+        assert np.array_equal(got[keep], v[keep])
+        _close(got[~keep], turned[~keep], 1e-15)
+
+
+def check_mrope_relative():
+    """q turned at (t1, h1, w1) against k at (t2, h2, w2): the dot product
+    depends only on the three differences (up to the float32 rounding of
+    cos and sin); a change of one difference alone changes it."""
+    D = 64
+    rng = np.random.default_rng(11)
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    sec = (12, 10, 10)
+
+    def dot(a, b):
+        return (od.rope(q, *od.mrope_cos_sin(a, D, 1.0e4, sec)) @
+                od.rope(k, *od.mrope_cos_sin(b, D, 1.0e4, sec)))
+
+    a, b = (9, 3, 5), (4, 1, 7)
+    base = dot(a, b)
+    for sh in ((10, 0, 0), (0, 6, 0), (0, 0, 13), (2, 40, 7)):
+        a2 = tuple(x + y for x, y in zip(a, sh))
+        b2 = tuple(x + y for x, y in zip(b, sh))
+        assert abs(dot(a2, b2) - base) < 1e-5      # cos / sin are float32
+    for comp in range(3):
+        a3 = list(a)
+        a3[comp] += 3
+        assert abs(dot(tuple(a3), b) - base) > 1e-3
+
+
+def check_mrope_model_brute():
+    """A stack with interleaved sections (4, 2, 2) at D = 16 and distinct
+    t/h/w positions: the cached prefill and the following steps equal the
+    brute-force recompute, which turns every frequency by its own position
+    in scalar loops; the cache rows still go to positions 0, 1, 2, ..."""
+    m = dataclasses.replace(tiny_model(L=2, h=16, hq=2, hkv=1, D=16, F=16, V=24, qk_norm=True,
+                                       bias=True, seed=24, scale=0.5),
+                            mrope_sections=(4, 2, 2))
+    rng = np.random.default_rng(25)
+    rows = [rng.standard_normal(16) for _ in range(7)]
+    # vision-like rows share t and walk a 2 x 2 grid; text rows continue at t = h = w
+    rpos = np.array([[0, 0, 0], [1, 1, 1], [2, 2, 2], [2, 2, 3], [2, 3, 2], [2, 3, 3],
+                     [4, 4, 4]])
+    cache = od.Cache(m, 8)
+    y, z = od.prefill(m, cache, np.stack(rows[:4]), 0, rope_pos=rpos[:4])
+    yb, zb = brute.last_outputs(m, rows[:4], rope_pos=rpos[:4])
+    _close(y, yb, 1e-9)
+    _close(z, zb, 1e-9)
+    for t in range(4, 7):
+        y, z = od.step(m, cache, rows[t], 0, rope_pos=rpos[t])
+        yb, zb = brute.last_outputs(m, rows[:t + 1], rope_pos=rpos[:t + 1])
+        _close(y, yb, 1e-9)
+        _close(z, zb, 1e-9)
+    assert cache.pos == 7
+    # rotary positions that differ from the row index change the outcome
+    _, z_plain = od.prefill(m, od.Cache(m, 8), np.stack(rows), 0)
+    assert np.max(np.abs(z_plain - z)) > 1e-6
 
 
 # ---------------------------------------------------------------- attention

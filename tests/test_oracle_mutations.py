@@ -283,7 +283,33 @@ def _project_no_bias(model, x):
     return x if model.in_proj is None else x @ model.in_proj.T
 
 
+def _mrope_hw_swapped(half, sections):
+    m = _orig["mrope_modality"](half, sections)
+    return np.where(m == 1, 2, np.where(m == 2, 1, m))
+
+
+def _mrope_no_cutoff(half, sections):
+    return np.arange(half) % 3 if sections is not None else np.zeros(half, np.int64)
+
+
+def _mrope_t_only(pos3, head_dim, theta, sections):
+    return od.rope_cos_sin(pos3[0], head_dim, theta)
+
+
+def _step_cache_position(model, cache, x, head=0, rope_pos=None):
+    return _orig["step"](model, cache, x, head)
+
+
+def _prefill_row_index(model, cache, X, head=0, rope_pos=None):
+    return _orig["prefill"](model, cache, X, head)
+
+
 MUTATIONS = {
+    "mrope_h_w_swapped": ("mrope_modality", _mrope_hw_swapped),
+    "mrope_interleave_to_the_end": ("mrope_modality", _mrope_no_cutoff),
+    "mrope_t_position_only": ("mrope_cos_sin", _mrope_t_only),
+    "step_rotates_at_cache_position": ("step", _step_cache_position),
+    "prefill_rotates_at_row_index": ("prefill", _prefill_row_index),
     "controls_eos_one_early": ("Controls", _CtlEosAtMin),
     "input_projection_drops_bias": ("project_input", _project_no_bias),
     "controls_no_stop": ("choose_controlled", _choose_no_stop),

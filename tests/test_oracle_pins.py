@@ -13,6 +13,10 @@ PINS = [
     pins.check_rope_complex_form,
     pins.check_rope_relative,
     pins.check_mrope_degenerates,
+    pins.check_mrope_sections,
+    pins.check_mrope_single_component,
+    pins.check_mrope_relative,
+    pins.check_mrope_model_brute,
     pins.check_attention_closed_form,
     pins.check_attention_invariants,
     pins.check_gqa_equals_mha,

@@ -38,7 +38,7 @@ STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FU
 
 EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
-           "decoder_step", "decoder_embed", "greedy_argmax", "sample_topk", "decoder_generate",
+           "decoder_step", "decoder_prefill_mrope", "decoder_step_mrope", "decoder_embed", "greedy_argmax", "sample_topk", "decoder_generate",
            "talker_generate_frames", "quantize_blocks", "codec_conv1d_causal",
            "codec_transconv1d_pack", "codec_transconv1d", "decoder_time_stage")
 
@@ -60,7 +60,8 @@ class atd_config(C.Structure):
                 ("kv_dtype", C.c_int32),
                 ("rope_theta", C.c_double), ("rms_eps", C.c_float),
                 ("max_slots", C.c_int32), ("max_rows", C.c_int32), ("max_ctx", C.c_int32),
-                ("flags", C.c_int32), ("weight_format", C.c_int32), ("input_dim", C.c_int32)]
+                ("flags", C.c_int32), ("weight_format", C.c_int32), ("input_dim", C.c_int32),
+                ("mrope_sections", C.c_int32 * 3)]
 
 
 ATD_TOPK_MAX = 256
@@ -106,6 +107,9 @@ def _load():
         "decoder_get_position": ([vp, i32, C.POINTER(i32), C.POINTER(i32)], C.c_int),
         "decoder_prefill": ([vp, i32, vp, i32, i32, vp, vp, vp], C.c_int),
         "decoder_step": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, vp, vp], C.c_int),
+        "decoder_prefill_mrope": ([vp, i32, vp, i32, vp, i32, vp, vp, vp], C.c_int),
+        "decoder_step_mrope": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, vp, i32, vp, vp, vp],
+                               C.c_int),
         "decoder_embed": ([vp, i32, vp, i32, C.POINTER(i32), vp, vp, vp], C.c_int),
         "greedy_argmax": ([vp, i32, i32, vp, f32, C.POINTER(atd_controls), vp, vp, vp], C.c_int),
         "sample_topk": ([vp, i32, i32, vp, f32, C.POINTER(atd_sampling), C.POINTER(atd_controls),
@@ -188,6 +192,18 @@ def decoder_step(handle: int, slot0: int, B: int, tok, G: int, table_ids, extra,
                  y_out, logits_out: int, stream: int) -> None:
     _check(lib.decoder_step(handle, slot0, B, tok, G, _i32_array(list(table_ids)), extra, head,
                             y_out, logits_out, stream), handle)
+
+
+def decoder_prefill_mrope(handle: int, slot: int, x: int, T: int, rope_pos, head: int, y_out,
+                          logits_out: int, stream: int) -> None:
+    _check(lib.decoder_prefill_mrope(handle, slot, x, T, rope_pos, head, y_out, logits_out,
+                                     stream), handle)
+
+
+def decoder_step_mrope(handle: int, slot0: int, B: int, tok, G: int, table_ids, extra,
+                       rope_pos, head: int, y_out, logits_out: int, stream: int) -> None:
+    _check(lib.decoder_step_mrope(handle, slot0, B, tok, G, _i32_array(list(table_ids)), extra,
+                                  rope_pos, head, y_out, logits_out, stream), handle)
 
 
 def decoder_embed(handle: int, B: int, tok, G: int, table_ids, extra, x_out: int,

@@ -36,6 +36,7 @@ struct atd_decoder {
   // device scratch, one allocation
   void* mem = nullptr;
   float *cos_t = nullptr, *sin_t = nullptr;
+  float *rcos = nullptr, *rsin = nullptr;  // RoPE rows of an *_mrope call [max_rows, D/2]
   float *x = nullptr, *qkv = nullptr, *q = nullptr, *o = nullptr, *act = nullptr;
   float *pml = nullptr, *pacc = nullptr;
   void** kv_tab = nullptr;
@@ -148,6 +149,17 @@ int check_config(const atd_config* c) {
     return fail(nullptr, ATD_ERR_CAPACITY, "max_ctx %d outside [1, 2^20]", c->max_ctx);
   if (c->flags & ~(ATD_FLAG_DRY_RUN | ATD_FLAG_NO_MFMA))
     return fail(nullptr, ATD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)c->flags);
+  {
+    const int* ms = c->mrope_sections;
+    const int half = c->head_dim / 2;
+    const bool none = ms[0] == 0 && ms[1] == 0 && ms[2] == 0;
+    if (!none && (ms[0] < 0 || ms[1] < 0 || ms[2] < 0 || ms[0] + ms[1] + ms[2] != half ||
+                  3 * std::max(ms[1], ms[2]) > half))
+      return fail(nullptr, ATD_ERR_INVALID_ARG,
+                  "mrope_sections {%d, %d, %d}: need s_t + s_h + s_w = D/2 = %d and "
+                  "3 max(s_h, s_w) <= D/2",
+                  ms[0], ms[1], ms[2], half);
+  }
   if (c->weight_format != ATD_WFMT_DENSE && c->weight_format != ATD_WFMT_Q8 &&
       c->weight_format != ATD_WFMT_Q4)
     return fail(nullptr, ATD_ERR_DTYPE, "weight_format %d is not ATD_WFMT_DENSE/Q8/Q4",
@@ -279,8 +291,8 @@ AttnArgs attn_args(const atd_decoder* d, RowMap rows, int l, int M, int max_len_
   a.k_norm = (const float*)W.k_norm;
   a.qk_norm = c.qk_norm;
   a.eps = c.rms_eps;
-  a.cos_t = d->cos_t;
-  a.sin_t = d->sin_t;
+  a.cos_t = rows.rope_rows ? d->rcos : d->cos_t;
+  a.sin_t = rows.rope_rows ? d->rsin : d->sin_t;
   a.q = d->q;
   a.st = slots_of(d);
   a.rows = rows;
@@ -319,8 +331,8 @@ RopeArgs rope_args(const atd_decoder* d, RowMap rows, int l, int M) {
   r.q_norm = (const float*)W.q_norm;
   r.k_norm = (const float*)W.k_norm;
   r.eps = c.rms_eps;
-  r.cos_t = d->cos_t;
-  r.sin_t = d->sin_t;
+  r.cos_t = rows.rope_rows ? d->rcos : d->cos_t;
+  r.sin_t = rows.rope_rows ? d->rsin : d->sin_t;
   r.st = slots_of(d);
   r.rows = rows;
   r.layer = l;
@@ -645,12 +657,23 @@ hipError_t build_inputs(atd_decoder* d, EmbedArgs ea, hipStream_t s) {
   return e;
 }
 
-// Launch sequence of one decode step of B rows (slots slot0..slot0+B-1).
+// RoPE rows of an *_mrope call from its rotary positions (device [M, 3]).
+hipError_t mrope_rows(atd_decoder* d, const int32_t* rope_pos, int M, hipStream_t s) {
+  const atd_config& c = d->cfg;
+  return launch_mrope_rows(rope_pos, M, c.head_dim / 2, c.mrope_sections[1],
+                           c.mrope_sections[2], c.max_ctx, d->cos_t, d->sin_t, d->rcos,
+                           d->rsin, s);
+}
+
+// Launch sequence of one decode step of B rows (slots slot0..slot0+B-1);
+// rope_pos: rotary positions [B, 3] of the rows, or null (cache positions).
 hipError_t enqueue_step(atd_decoder* d, int slot0, int B, const int32_t* tok, int G,
                         const int32_t* table_ids, const float* extra, int head, float* y_out,
-                        float* logits_out, int max_cap, hipStream_t s) {
-  RowMap rows{kRowsStep, slot0, 0};
-  hipError_t e = build_inputs(d, embed_args(d, B, tok, G, table_ids, extra, d->x), s);
+                        float* logits_out, int max_cap, hipStream_t s,
+                        const int32_t* rope_pos = nullptr) {
+  RowMap rows{kRowsStep, slot0, 0, rope_pos ? 1 : 0};
+  hipError_t e = rope_pos ? mrope_rows(d, rope_pos, B, s) : hipSuccess;
+  if (e == hipSuccess) e = build_inputs(d, embed_args(d, B, tok, G, table_ids, extra, d->x), s);
   const HeadOut ho{head, y_out, logits_out};
   if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, d->x, &ho, s);
   if (e == hipSuccess) e = launch_advance(slots_of(d), rows, B, s);
@@ -700,6 +723,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   };
   const size_t o_cos = carve((size_t)cfg->max_ctx * half * 4);
   const size_t o_sin = carve((size_t)cfg->max_ctx * half * 4);
+  const size_t o_rcos = carve((size_t)R * half * 4);
+  const size_t o_rsin = carve((size_t)R * half * 4);
   const size_t o_x = carve((size_t)R * h * 4);
   const size_t o_xin = carve(w->in_proj ? (size_t)R * d->in_dim * 4 : 0);
   const size_t o_qkv = carve((size_t)R * nqkv * 4);
@@ -747,6 +772,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   char* base = static_cast<char*>(d->mem);
   d->cos_t = (float*)(base + o_cos);
   d->sin_t = (float*)(base + o_sin);
+  d->rcos = (float*)(base + o_rcos);
+  d->rsin = (float*)(base + o_rsin);
   d->x = (float*)(base + o_x);
   d->xin = w->in_proj ? (float*)(base + o_xin) : nullptr;
   d->qkv = (float*)(base + o_qkv);
@@ -907,8 +934,11 @@ extern "C" int decoder_embed(atd_decoder* d, int32_t B, const int32_t* tok, int3
   return e == hipSuccess ? ATD_OK : hip_fail(d, e, "decoder_embed");
 }
 
-extern "C" int decoder_prefill(atd_decoder* d, int32_t slot, const float* x, int32_t T,
-                               int32_t head, float* y_out, float* logits_out, void* stream) {
+namespace {
+
+int prefill_impl(atd_decoder* d, int32_t slot, const float* x, int32_t T,
+                 const int32_t* rope_pos, int32_t head, float* y_out, float* logits_out,
+                 void* stream, const char* name) {
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
   const atd_config& c = d->cfg;
   if (slot < 0 || slot >= c.max_slots)
@@ -932,20 +962,21 @@ extern "C" int decoder_prefill(atd_decoder* d, int32_t slot, const float* x, int
     return ATD_OK;
   }
   hipStream_t s = (hipStream_t)stream;
-  RowMap rows{kRowsPrefill, slot, 0};
-  hipError_t e = build_inputs(d, embed_args(d, T, nullptr, 0, nullptr, x, d->x), s);
+  RowMap rows{kRowsPrefill, slot, 0, rope_pos ? 1 : 0};
+  hipError_t e = rope_pos ? mrope_rows(d, rope_pos, T, s) : hipSuccess;
+  if (e == hipSuccess) e = build_inputs(d, embed_args(d, T, nullptr, 0, nullptr, x, d->x), s);
   if (e == hipSuccess) e = run_layers(d, rows, T, T, d->x, nullptr, s);
   if (e == hipSuccess)
     e = run_head_gemv(d, d->x + (size_t)(T - 1) * c.hidden, 1, head, y_out, logits_out, s);
   if (e == hipSuccess) e = launch_advance(slots_of(d), rows, T, s);
-  if (e != hipSuccess) return hip_fail(d, e, "decoder_prefill");
+  if (e != hipSuccess) return hip_fail(d, e, name);
   d->pos[slot] = T;
   return ATD_OK;
 }
 
-extern "C" int decoder_step(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok,
-                            int32_t G, const int32_t* table_ids, const float* extra,
-                            int32_t head, float* y_out, float* logits_out, void* stream) {
+int step_impl(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok, int32_t G,
+              const int32_t* table_ids, const float* extra, const int32_t* rope_pos,
+              int32_t head, float* y_out, float* logits_out, void* stream, const char* name) {
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
   const atd_config& c = d->cfg;
   if (B < 1 || B > c.max_rows)
@@ -978,10 +1009,42 @@ extern "C" int decoder_step(atd_decoder* d, int32_t slot0, int32_t B, const int3
     return ATD_OK;
   }
   hipError_t e = enqueue_step(d, slot0, B, tok, G, table_ids, extra, head, y_out, logits_out,
-                              max_cap, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(d, e, "decoder_step");
+                              max_cap, (hipStream_t)stream, rope_pos);
+  if (e != hipSuccess) return hip_fail(d, e, name);
   for (int b = 0; b < B; ++b) d->pos[slot0 + b] += 1;
   return ATD_OK;
+}
+
+}  // namespace
+
+extern "C" int decoder_prefill(atd_decoder* d, int32_t slot, const float* x, int32_t T,
+                               int32_t head, float* y_out, float* logits_out, void* stream) {
+  return prefill_impl(d, slot, x, T, nullptr, head, y_out, logits_out, stream,
+                      "decoder_prefill");
+}
+
+extern "C" int decoder_prefill_mrope(atd_decoder* d, int32_t slot, const float* x, int32_t T,
+                                     const int32_t* rope_pos, int32_t head, float* y_out,
+                                     float* logits_out, void* stream) {
+  if (!rope_pos) return fail(d, ATD_ERR_INVALID_ARG, "rope_pos is NULL");
+  return prefill_impl(d, slot, x, T, rope_pos, head, y_out, logits_out, stream,
+                      "decoder_prefill_mrope");
+}
+
+extern "C" int decoder_step(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok,
+                            int32_t G, const int32_t* table_ids, const float* extra,
+                            int32_t head, float* y_out, float* logits_out, void* stream) {
+  return step_impl(d, slot0, B, tok, G, table_ids, extra, nullptr, head, y_out, logits_out,
+                   stream, "decoder_step");
+}
+
+extern "C" int decoder_step_mrope(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok,
+                                  int32_t G, const int32_t* table_ids, const float* extra,
+                                  const int32_t* rope_pos, int32_t head, float* y_out,
+                                  float* logits_out, void* stream) {
+  if (!rope_pos) return fail(d, ATD_ERR_INVALID_ARG, "rope_pos is NULL");
+  return step_impl(d, slot0, B, tok, G, table_ids, extra, rope_pos, head, y_out, logits_out,
+                   stream, "decoder_step_mrope");
 }
 
 // ---------------------------------------------------------------- argmax

@@ -55,7 +55,9 @@ enum RowMode { kRowsStep = 0, kRowsPrefill = 1 };
 struct RowMap {
   int mode;
   int slot0;
-  int row0;   // rows of this launch are rows row0 .. of the call
+  int row0;       // rows of this launch are rows row0 .. of the call
+  int rope_rows;  // 1: the RoPE tables hold one row per call row (row0 + m),
+                  // built from rotary positions; 0: indexed by position
 };
 
 // ---------------------------------------------------------------- rows/KV
@@ -316,6 +318,13 @@ hipError_t launch_pack_transconv(const float* w, int cin, int cout, int s_, floa
 hipError_t launch_rope_append(const RopeArgs& a, int bf16, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream_t s);
 hipError_t launch_advance(const SlotTables& st, RowMap rows, int M, hipStream_t s);
+// RoPE rows of a call with rotary positions pos3 [M][3] (t, h, w): row m,
+// frequency i takes cos/sin of the position table at pos3[m][c(i)], c(i) = 1
+// when i % 3 == 1 and i < 3 sec_h, 2 when i % 3 == 2 and i < 3 sec_w, else 0;
+// positions clamped into [0, max_ctx).
+hipError_t launch_mrope_rows(const int32_t* pos3, int M, int half, int sec_h, int sec_w,
+                             int max_ctx, const float* cos_t, const float* sin_t, float* rcos,
+                             float* rsin, hipStream_t s);
 hipError_t launch_set_slot(const SlotTables& st, int slot, void* const* k, void* const* v,
                            int cap, int pos, int set_ptrs, hipStream_t s);
 hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s);

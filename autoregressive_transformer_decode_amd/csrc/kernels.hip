@@ -311,8 +311,9 @@ __device__ __forceinline__ void rope_head(const RopeArgs& a, int m, int hh, floa
     __syncthreads();
     if (own) {
       const int i = t < half ? t : t - half;
-      const float c = a.cos_t[(size_t)pos * half + i];
-      const float sn = a.sin_t[(size_t)pos * half + i];
+      const size_t rr = (size_t)(a.rows.rope_rows ? a.rows.row0 + m : pos) * half;
+      const float c = a.cos_t[rr + i];
+      const float sn = a.sin_t[rr + i];
       const float x0 = buf[i], x1 = buf[i + half];
       v = t < half ? x0 * c - x1 * sn : x1 * c + x0 * sn;
     }
@@ -701,6 +702,13 @@ __global__ __launch_bounds__(256) void k_pack_transconv(const float* w, int cin,
 }
 
 // ------------------------------------------------------------------ attention
+// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi): ~16 significant bits
+// in two bf16 matrix-core operands
+__device__ __forceinline__ void split_hi_lo(float v, uint16_t& h, uint16_t& l) {
+  h = f32_to_bf16(v);
+  l = f32_to_bf16(v - __uint_as_float((uint32_t)h << 16));
+}
+
 // Split-K decode attention, one split per wave.  Block (split group, kv head
 // g, row m); wave w takes split 4*blockIdx.x + w of the row's key range
 // (attn_chunk keys each, from its valid length) for the R query heads that
@@ -715,51 +723,6 @@ __global__ __launch_bounds__(256) void k_pack_transconv(const float* w, int cin,
 // row (norm, RoPE, rounding to the cache dtype), stores it at the row's
 // position and uses those register values for that key.  Only that wave
 // touches the new row, so no other synchronisation is needed.
-// Per-head RMSNorm (optional) + rotate-half RoPE of a head vector spread over
-// the LPK lanes of a group, VEC channels [dl, dl+VEC) per lane.
-template <int D, int VEC, int LPK>
-__device__ __forceinline__ void norm_rope_lanes(float (&v)[VEC], int dl, bool do_norm,
-                                                const float* gain, float eps, int pos,
-                                                const float* cos_t, const float* sin_t) {
-  constexpr int half = D / 2;
-  static_assert(VEC % 4 == 0, "channels per lane come in float4 groups");
-  if (do_norm) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) ss += v[e] * v[e];
-    ss = group_sum<LPK>(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
-#pragma unroll
-    for (int e = 0; e < VEC; e += 4) {
-      const float4 g = *reinterpret_cast<const float4*>(gain + dl + e);
-      v[e] = v[e] * inv * g.x;
-      v[e + 1] = v[e + 1] * inv * g.y;
-      v[e + 2] = v[e + 2] * inv * g.z;
-      v[e + 3] = v[e + 3] * inv * g.w;
-    }
-  }
-  const bool lo = dl < half;
-  const float* cp = cos_t + (size_t)pos * half + (dl % half);   // channels dl.. pair with dl%half..
-  const float* sp = sin_t + (size_t)pos * half + (dl % half);
-#pragma unroll
-  for (int e = 0; e < VEC; e += 4) {
-    const float4 c4 = *reinterpret_cast<const float4*>(cp + e);
-    const float4 s4 = *reinterpret_cast<const float4*>(sp + e);
-    const float c[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float other = __shfl_xor(v[e + t], LPK / 2, 64);  // channel dl+e+t -/+ D/2
-      v[e + t] = lo ? v[e + t] * c[t] - other * sn[t] : v[e + t] * c[t] + other * sn[t];
-    }
-  }
-}
-
-// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi): ~16 significant bits
-// in two bf16 matrix-core operands
-__device__ __forceinline__ void split_hi_lo(float v, uint16_t& h, uint16_t& l) {
-  h = f32_to_bf16(v);
-  l = f32_to_bf16(v - __uint_as_float((uint32_t)h << 16));
-}
 
 template <typename KT, int VEC>
 __device__ __forceinline__ uint4 pack_kv(const float (&v)[VEC]) {
@@ -819,8 +782,9 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   // then the cache rows: the in-order memory counter lets the query math
   // start before the rows arrive
   const int half = D / 2;
-  const float* cp = a.cos_t + (size_t)pos * half + (dl % half);
-  const float* sp = a.sin_t + (size_t)pos * half + (dl % half);
+  const size_t rr = (size_t)(a.rows.rope_rows ? a.rows.row0 + m : pos) * half;
+  const float* cp = a.cos_t + rr + (dl % half);
+  const float* sp = a.sin_t + rr + (dl % half);
   float4 cs[DPL / 4], sn[DPL / 4];
   if (a.fused) {
 #pragma unroll
@@ -2020,6 +1984,28 @@ hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream
     hipLaunchKernelGGL(k_attn_combine<64>, cgrid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(64) void k_mrope_rows(const int32_t* pos3, int half, int sec_h,
+                                                   int sec_w, int max_ctx, const float* cos_t,
+                                                   const float* sin_t, float* rcos, float* rsin) {
+  const int m = blockIdx.x, i = threadIdx.x;
+  if (i >= half) return;
+  const int r = i % 3;
+  const int c = (r == 1 && i < 3 * sec_h) ? 1 : ((r == 2 && i < 3 * sec_w) ? 2 : 0);
+  int p = pos3[m * 3 + c];
+  p = p < 0 ? 0 : (p >= max_ctx ? max_ctx - 1 : p);
+  rcos[(size_t)m * half + i] = cos_t[(size_t)p * half + i];
+  rsin[(size_t)m * half + i] = sin_t[(size_t)p * half + i];
+}
+
+hipError_t launch_mrope_rows(const int32_t* pos3, int M, int half, int sec_h, int sec_w,
+                             int max_ctx, const float* cos_t, const float* sin_t, float* rcos,
+                             float* rsin, hipStream_t s) {
+  if (M < 1 || half > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mrope_rows, dim3(M), dim3(64), 0, s, pos3, half, sec_h, sec_w, max_ctx,
+                     cos_t, sin_t, rcos, rsin);
   return hipGetLastError();
 }
 

@@ -129,7 +129,8 @@ def make_config(s: ModelShape, max_slots: int, max_rows: int, max_ctx: int,
         kv_dtype=B.ATD_BF16 if s.kv_dtype == BF16 else B.ATD_F32,
         rope_theta=s.rope_theta, rms_eps=s.rms_eps,
         max_slots=max_slots, max_rows=max_rows, max_ctx=max_ctx, flags=flags,
-        weight_format=weight_format, input_dim=s.input_dim)
+        weight_format=weight_format, input_dim=s.input_dim,
+        mrope_sections=(C.c_int32 * 3)(*(s.mrope_sections or (0, 0, 0))))
 
 
 class Decoder:
@@ -188,25 +189,44 @@ class Decoder:
 
     # -- compute
     def prefill(self, x: torch.Tensor, slot: int = 0, head: int = 0,
-                y_out: Optional[torch.Tensor] = None, logits_out: Optional[torch.Tensor] = None):
+                y_out: Optional[torch.Tensor] = None, logits_out: Optional[torch.Tensor] = None,
+                rope_pos: Optional[torch.Tensor] = None):
+        """rope_pos: device int32 [T, 3] rotary (t, h, w) positions of the rows
+        (decoder_prefill_mrope), or None (positions 0..T-1)."""
         T = int(x.shape[0])
         if logits_out is None:
             logits_out = torch.empty(self.shape.vocab, device=x.device, dtype=torch.float32)
-        B.decoder_prefill(self.handle, slot, x.data_ptr(), T, head,
-                          y_out.data_ptr() if y_out is not None else None,
-                          logits_out.data_ptr(), _stream())
+        y = y_out.data_ptr() if y_out is not None else None
+        if rope_pos is None:
+            B.decoder_prefill(self.handle, slot, x.data_ptr(), T, head, y, logits_out.data_ptr(),
+                              _stream())
+        else:
+            assert rope_pos.dtype == torch.int32 and tuple(rope_pos.shape) == (T, 3)
+            B.decoder_prefill_mrope(self.handle, slot, x.data_ptr(), T,
+                                    rope_pos.contiguous().data_ptr(), head, y,
+                                    logits_out.data_ptr(), _stream())
         return y_out, logits_out
 
     def step(self, tok: Optional[torch.Tensor], table_ids: Sequence[int], slot0: int = 0,
              nrows: int = 1, extra: Optional[torch.Tensor] = None, head: int = 0,
-             y_out: Optional[torch.Tensor] = None, logits_out: Optional[torch.Tensor] = None):
+             y_out: Optional[torch.Tensor] = None, logits_out: Optional[torch.Tensor] = None,
+             rope_pos: Optional[torch.Tensor] = None):
+        """rope_pos: device int32 [nrows, 3] rotary (t, h, w) positions
+        (decoder_step_mrope), or None (each slot's cache position)."""
         G = len(table_ids)
         if logits_out is None:
             logits_out = torch.empty(nrows, self.shape.vocab, device="cuda", dtype=torch.float32)
-        B.decoder_step(self.handle, slot0, nrows, tok.data_ptr() if tok is not None else None, G,
-                       table_ids, extra.data_ptr() if extra is not None else None, head,
-                       y_out.data_ptr() if y_out is not None else None, logits_out.data_ptr(),
-                       _stream())
+        tp = tok.data_ptr() if tok is not None else None
+        ex = extra.data_ptr() if extra is not None else None
+        y = y_out.data_ptr() if y_out is not None else None
+        if rope_pos is None:
+            B.decoder_step(self.handle, slot0, nrows, tp, G, table_ids, ex, head, y,
+                           logits_out.data_ptr(), _stream())
+        else:
+            assert rope_pos.dtype == torch.int32 and tuple(rope_pos.shape) == (nrows, 3)
+            B.decoder_step_mrope(self.handle, slot0, nrows, tp, G, table_ids, ex,
+                                 rope_pos.contiguous().data_ptr(), head, y,
+                                 logits_out.data_ptr(), _stream())
         return y_out, logits_out
 
     def generate(self, n_steps: int, tok_io: torch.Tensor, table_ids: Sequence[int] = (0,),

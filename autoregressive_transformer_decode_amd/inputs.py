@@ -63,6 +63,7 @@ class ModelShape:
     model_id: int = 0     # separates the random streams of two stacks
     kv_dtype: str = F32   # KV-cache storage: F32 or BF16
     input_dim: int = 0    # width of the input rows when projected (0: hidden)
+    mrope_sections: Optional[Tuple[int, int, int]] = None   # interleaved t/h/w sections
 
     @property
     def in_width(self) -> int:
@@ -122,6 +123,9 @@ CP06 = _shape("code_predictor", 5, 1024, 16, 8, 128, 3072, 2048, BF16, True,
               False, [3072] + [2048] * 15, n_heads=15, model_id=1)
 TALKER17 = _shape("talker1.7b", 28, 2048, 16, 8, 128, 6144, 3072, BF16, True,
                   False, [3072])
+# the Talkers rotate with interleaved mRoPE, t/h/w sections [24, 20, 20]
+TALKER06 = dataclasses.replace(TALKER06, mrope_sections=(24, 20, 20))
+TALKER17 = dataclasses.replace(TALKER17, mrope_sections=(24, 20, 20))
 # the 1.7B Talker in the frame loop (16 code tables) and its Code Predictor,
 # whose inputs come in the Talker's width through an input projection
 TALKER17F = dataclasses.replace(TALKER17, name="talker1.7b-frames",

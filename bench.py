@@ -26,6 +26,8 @@ Also measured in the same run:
                 on the device by sample_topk inside the step graph.
   token_choice_us  microseconds per call of greedy_argmax and sample_topk on
                 one row of the vocabulary.
+  mrope         eager steps through decoder_step_mrope (distinct t/h/w rotary
+                positions) against eager decoder_step on the same schedule.
   quantized     the same K greedy steps with the seven per-layer matrices
                 block-quantized by the library (int8 and 4-bit codes with one
                 fp16 scale per 32 weights): tokens/s, step bytes and the gate/up
@@ -248,6 +250,44 @@ def bench_lm(args, wl):
         dt_s = schedule(K, sampled=True)
         log(f"timed {K} sampled steps: {dt_s * 1e3:.1f} ms")
 
+    # interleaved mRoPE: eager steps through decoder_step_mrope with distinct
+    # rotary positions against eager decoder_step, same schedule, alternating
+    mrope = None
+    if s.mrope_sections is not None and not args.no_sampled:
+        n_m = min(256, K)
+        rp = torch.tensor([[P0 + k, 7 + k % 5, 11 + k % 3] for k in range(n_m)],
+                          dtype=torch.int32, device="cuda")
+        tk2 = tok.view(1, 1)
+        z2, y2 = z.view(1, -1), y.view(1, -1)
+
+        def eager(use):
+            dec.set_position(0, 0)
+            if dec.position(0)[1] != caps[0]:
+                dec.grow(0, caps[0], kv=buckets[0])
+            dec.prefill(X0_d, logits_out=z)
+            dv.greedy_argmax(z, None, 1.0, tok)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(n_m):
+                dec.step(tk2, [0], y_out=y2, logits_out=z2, rope_pos=rp[k:k + 1] if use else None)
+                dv.greedy_argmax(z, None, 1.0, tok)
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
+
+        eager(True)
+        tm = dict(plain=float("inf"), mrope=float("inf"))
+        for _ in range(2):
+            tm["plain"] = min(tm["plain"], eager(False))
+            tm["mrope"] = min(tm["mrope"], eager(True))
+        mrope = dict(sections=list(s.mrope_sections), steps=n_m,
+                     value=n_m / tm["mrope"], unit="tokens/s",
+                     plain_eager_tokens_per_s=n_m / tm["plain"],
+                     overhead=tm["mrope"] / tm["plain"] - 1.0,
+                     step="eager decoder_step_mrope + greedy_argmax per token, rotary positions "
+                          "(t, h, w) distinct; against eager decoder_step on the same schedule "
+                          "(each leg the faster of two alternating runs)")
+        log(f"mrope eager: {mrope['value']:.1f} tokens/s vs plain {mrope['plain_eager_tokens_per_s']:.1f}")
+
     # roofline: the dominant kernel's launches, every layer's weights in turn
     # as in a step, timed with HIP events on this stream
     reps = 16
@@ -281,6 +321,7 @@ def bench_lm(args, wl):
             settings=dict(zip(("top_k", "temperature", "top_p"), SAMPLING),
                           penalty=SAMPLING_PENALTY)),
         token_choice_us=None if args.no_sampled else time_choice(s.vocab),
+        mrope=mrope,
     )
     dec.close()
     # the same greedy run with the seven per-layer matrices block-quantized

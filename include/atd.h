@@ -98,6 +98,10 @@ typedef struct atd_config {
   int32_t input_dim;   /* width of the input rows (tables, extra, prefill
                           rows): 0 or hidden, or another multiple of 8 <=
                           8192 (<= 4096 for F32) with an input projection   */
+  int32_t mrope_sections[3]; /* (s_t, s_h, s_w) frequency counts of the
+                          interleaved multimodal RoPE used by the *_mrope
+                          entry points; {0, 0, 0}: every frequency follows
+                          the t position.  See decoder_prefill_mrope.      */
 } atd_config;
 
 /* atd_config.weight_format ("Rockchip NPU sidecars" page, section "The talker
@@ -297,6 +301,30 @@ int decoder_prefill(atd_decoder* dec, int32_t slot, const float* x, int32_t T,
 int decoder_step(atd_decoder* dec, int32_t slot0, int32_t B, const int32_t* tok,
                  int32_t G, const int32_t* table_ids, const float* extra,
                  int32_t head, float* y_out, float* logits_out, void* stream);
+
+/* Rotary positions apart from the cache position (interleaved multimodal
+ * RoPE; "Qwen3-TTS ncnn port", Talker section: the Talker's mRoPE cuts the
+ * D/2 rotary frequencies into t / h / w sections [24, 20, 20], interleaved:
+ * frequency i follows position i mod 3 while i < 60 and t above).
+ * decoder_prefill_mrope is decoder_prefill and decoder_step_mrope is
+ * decoder_step, except that row r (a prefill row, or the row of slot
+ * slot0 + r) turns its q and k by the positions rope_pos[r] = (t, h, w)
+ * (device int32 [T or B, 3]) instead of its cache position: frequency i
+ * takes h when i % 3 == 1 and i < 3 s_h, w when i % 3 == 2 and i < 3 s_w,
+ * t otherwise, with (s_t, s_h, s_w) = atd_config.mrope_sections
+ * (s_t + s_h + s_w = D/2, 3 max(s_h, s_w) <= D/2; {0, 0, 0}: all t).
+ * Cache rows, their positions and the attended length are unchanged.  With
+ * t = h = w = the cache position the result equals the plain entry point's
+ * bit for bit.  Rotary positions are read on the device and clamped into
+ * [0, max_ctx) (the angle table's rows).  Errors: as the plain entry
+ * points, and INVALID_ARG when rope_pos is NULL. */
+int decoder_prefill_mrope(atd_decoder* dec, int32_t slot, const float* x, int32_t T,
+                          const int32_t* rope_pos, int32_t head, float* y_out,
+                          float* logits_out, void* stream);
+int decoder_step_mrope(atd_decoder* dec, int32_t slot0, int32_t B, const int32_t* tok,
+                       int32_t G, const int32_t* table_ids, const float* extra,
+                       const int32_t* rope_pos, int32_t head, float* y_out,
+                       float* logits_out, void* stream);
 
 /* The input-embedding part of decoder_step alone: x_out (device [B, input_dim]
  * float32) = sum_g tables[table_ids[g]][tok[b*G+g]] + extra[b].  Used to

@@ -51,7 +51,7 @@ def oracle_from_weights(mw, dtype=np.float64, quant=None):
     hp = dict(n_layers=s.n_layers, hidden=s.hidden, n_q_heads=s.n_q_heads,
               n_kv_heads=s.n_kv_heads, head_dim=s.head_dim, ffn=s.ffn,
               rope_theta=s.rope_theta, rms_eps=s.rms_eps, qk_norm=s.qk_norm,
-              kv_bf16=(s.kv_dtype == "bf16"))
+              kv_bf16=(s.kv_dtype == "bf16"), mrope_sections=s.mrope_sections)
     layers = []
     for Lw in mw.layers:
         layers.append(dict(

@@ -423,3 +423,38 @@ def test_codec_argument_checks():
     with pytest.raises(B.AtdError) as ei:
         B.codec_conv1d_causal(0x100, 0x200, None, 1 << 16, 4, 1 << 16, 3, 1, 0, 0x300, 0)
     assert "2^31" in str(ei.value)
+
+
+@pytest.mark.parametrize("sec,ok", [((0, 0, 0), True), ((24, 20, 20), True), ((64, 0, 0), True),
+                                    ((22, 21, 21), True), ((24, 20, 21), False),
+                                    ((-4, 34, 34), False), ((4, 30, 30), False)])
+def test_mrope_sections_and_entry_checks(sec, ok):
+    """mrope_sections must cover D/2 = 64 frequencies with 3 max(s_h, s_w) <=
+    64; the *_mrope entry points refuse a NULL rope_pos and otherwise follow
+    the plain entry points' schedule."""
+    cfg = _cfg(head_dim=128, n_q_heads=4, n_kv_heads=2)
+    cfg.mrope_sections = (C.c_int32 * 3)(*sec)
+    if not ok:
+        with pytest.raises(B.AtdError) as ei:
+            B.decoder_create(cfg, FakeWeights(cfg).w)
+        assert ei.value.code == B.ATD_ERR_INVALID_ARG and "mrope_sections" in str(ei.value)
+        return
+    h, fw = _create(cfg)
+    try:
+        B.kv_bucket_grow(h, 0, [0x900000 + 0x1000 * i for i in range(cfg.n_layers)],
+                         [0xA00000 + 0x1000 * i for i in range(cfg.n_layers)], 16, 0)
+        with pytest.raises(B.AtdError) as ei:
+            B.decoder_prefill_mrope(h, 0, 0x5000, 3, None, 0, None, 0x6000, 0)
+        assert "rope_pos is NULL" in str(ei.value)
+        with pytest.raises(B.AtdError) as ei:
+            B.decoder_prefill_mrope(h, 0, 0x5000, 17, 0x7100, 0, None, 0x6000, 0)
+        assert ei.value.code == B.ATD_ERR_CAPACITY
+        B.decoder_prefill_mrope(h, 0, 0x5000, 3, 0x7100, 0, None, 0x6000, 0)
+        assert B.decoder_get_position(h, 0) == (3, 16)
+        with pytest.raises(B.AtdError) as ei:
+            B.decoder_step_mrope(h, 0, 1, 0x7000, 1, [0], None, None, 0, None, 0x6000, 0)
+        assert "rope_pos is NULL" in str(ei.value)
+        B.decoder_step_mrope(h, 0, 1, 0x7000, 1, [0], None, 0x7100, 0, None, 0x6000, 0)
+        assert B.decoder_get_position(h, 0) == (4, 16)
+    finally:
+        B.decoder_destroy(h)

@@ -622,70 +622,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
 }
 
 // ------------------------------------------------------------------ codec convolutions
-// 64 output channels x 64 frames per workgroup, 4 x 4 per thread; the
-// reduction over (input channel, tap) runs in chunks of 16: the weight chunk
-// and the 16 shifted input rows are staged in LDS, each thread then reads
-// 4 weights and 4 inputs per reduction index (float4) for 16 FMAs.
-constexpr int kConvTile = 64, kConvR = 16;
-
-__global__ __launch_bounds__(256) void k_conv1d(ConvArgs a) {
-  __shared__ float Ws[kConvR][kConvTile + 4];
-  __shared__ float Xs[kConvR][kConvTile + 4];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kConvTile, c0 = blockIdx.y * kConvTile, p = blockIdx.z;
-  const int ty = tid >> 4, tx = tid & 15;   // channels 4ty.., frames 4tx..
-  const int R = a.cin * a.K;
-  const float* W = a.w + (size_t)p * a.cout * R;
-  float acc[4][4] = {};
-  for (int r0 = 0; r0 < R; r0 += kConvR) {
-    {   // weights: thread -> channel tid / 4, reduction indices 4 * (tid % 4) ..
-      const int cl = tid >> 2, rl = (tid & 3) * 4, co = c0 + cl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + rl + i;
-        Ws[rl + i][cl] = (co < a.cout && r < R) ? W[(size_t)co * R + r] : 0.f;
-      }
-    }
-    {   // inputs: thread -> reduction index tid / 16, frames 4 * (tid % 16) ..
-      const int rl = tid >> 4, tl = (tid & 15) * 4, r = r0 + rl;
-      const int ci = r / a.K, j = r - ci * a.K;
-      const int shift = (a.K - 1 - j) * a.dil;
-      const float* xr = a.x + (size_t)(r < R ? ci : 0) * a.T;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + tl + i - shift;
-        Xs[rl][tl + i] = (r < R && t >= 0 && t < a.T) ? xr[t] : 0.f;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rr = 0; rr < kConvR; ++rr) {
-      const float4 wv = *reinterpret_cast<const float4*>(&Ws[rr][4 * ty]);
-      const float4 xv = *reinterpret_cast<const float4*>(&Xs[rr][4 * tx]);
-      const float wa[4] = {wv.x, wv.y, wv.z, wv.w}, xa[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[i][k] = fmaf(wa[i], xa[k], acc[i][k]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int co = c0 + 4 * ty + i;
-    if (co >= a.cout) continue;
-    const float bv = a.bias ? a.bias[co] : 0.f;
-    float* yr = a.y + (size_t)co * a.ldy + p;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = t0 + 4 * tx + k;
-      if (t < a.T) {
-        float* o = yr + (size_t)t * a.ystride;
-        *o = (a.accumulate ? *o : 0.f) + (acc[i][k] + bv);
-      }
-    }
-  }
-}
+// (k_conv1d follows the matrix-core GEMM section below: it shares its types)
 
 __global__ __launch_bounds__(256) void k_pack_transconv(const float* w, int cin, int cout, int s_,
                                                         float* packed) {
@@ -1902,6 +1839,177 @@ static void gemv_dispatch(const GemvArgs& a, int epi, bool norm, hipStream_t s) 
     gemv_dispatch_mr<WT, kEpiSwiglu, true>(a, s);
 }
 
+// ------------------------------------------------------------------ codec convolution GEMM
+// One launch is a GEMM y[co][t] = sum_r W[co][r] X[r][t] over r = (input channel
+// ci, tap j), X[r][t] = x[ci][t - (K-1-j) dil] (zero before frame 0), on the
+// float32 matrix cores (v_mfma_f32_16x16x4f32: products and sums in float32).
+// Phases (blockIdx.z = p < P) take their own weights [P][cout][R] and write
+// y[co][t * ystride + p] (a transposed convolution by phase: K = 2 taps, the
+// previous frame and this one).  Workgroup: 4 waves in 2 x 2, each wave
+// (16 WM) channels x (16 WN) frames; the reduction runs in chunks of BK,
+// staged in LDS, the next chunk's global loads held in registers while the
+// MFMAs run on this one.  Within each 16 reduction indices an LDS row holds
+// index k at (k % 4) * 4 + k / 4, so that a lane reads its four MFMA k-steps
+// (k = 4s + lane / 16) as one float4.
+template <int WM, int WN, int BK>
+__global__ __launch_bounds__(256) void k_conv1d(ConvArgs a) {
+  constexpr int BM = 32 * WM, BN = 32 * WN, LD = BK + 4;
+  constexpr int AE = BM * BK / 256, BE = BN * BK / 256;   // elements per thread
+  constexpr int AT = BK / AE;                               // threads per A row
+  constexpr int BT = 256 / BK;                              // threads per B row
+  static_assert(AE >= 1 && BE >= 1 && BK % 16 == 0, "tile shape");
+  __shared__ __align__(16) float As[2][BM][LD];
+  __shared__ __align__(16) float Bs[2][BN][LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.y * BM, t0 = blockIdx.x * BN, p = blockIdx.z;
+  const int R = a.cin * a.K;
+  const float* W = a.w + (size_t)p * a.cout * R;
+  // A: thread -> channel row am, reduction indices ak .. ak + AE - 1 (contiguous in W)
+  const int am = tid / AT, ak = (tid % AT) * AE;
+  const bool arow = c0 + am < a.cout;
+  const float* wr = W + (size_t)(arow ? c0 + am : 0) * R;
+  // B: thread -> reduction index bk, frames bn .. bn + BE - 1 (contiguous in x)
+  const int bk = tid / BT, bn = (tid % BT) * BE;
+  const int bkp = (bk & ~15) | ((bk & 3) * 4 + ((bk & 15) >> 2));
+  float ra[AE], rb[BE];
+  // weight rows in 16-byte pieces when every row start is 16-byte aligned
+  const bool avec = (AE % 4 == 0) && (R % 4 == 0) && (((uintptr_t)W & 15) == 0);
+  // input rows likewise when T % 4 == 0 (frame groups of 4 never straddle 0 or T)
+  const bool bvec = (BE % 4 == 0) && (a.T % 4 == 0) && (((uintptr_t)a.x & 15) == 0);
+  auto load = [&](int r0) {
+    if (avec) {
+#pragma unroll
+      for (int e = 0; e < AE; e += 4) {
+        const int r = r0 + ak + e;
+        const float4 v = (arow && r < R) ? *reinterpret_cast<const float4*>(wr + r)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        ra[e] = v.x;
+        ra[e + 1] = v.y;
+        ra[e + 2] = v.z;
+        ra[e + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < AE; ++e) {
+        const int r = r0 + ak + e;
+        ra[e] = (arow && r < R) ? wr[r] : 0.f;
+      }
+    }
+    const int r = r0 + bk;
+    const int ci = r / a.K, j = r - ci * a.K;
+    const int t = t0 + bn - (a.K - 1 - j) * a.dil;
+    const float* xr = a.x + (size_t)(r < R ? ci : 0) * a.T;
+    if (bvec) {
+      // the BE frames from BE / 4 + 1 aligned 16-byte pieces (each wholly
+      // inside or outside [0, T), as T % 4 == 0), then shifted by t % 4
+      const int tb = t & ~3, m = t & 3;
+      float v[BE + 4];
+#pragma unroll
+      for (int q = 0; q < BE / 4 + 1; ++q) {
+        const int tq = tb + 4 * q;
+        const float4 f = (r < R && tq >= 0 && tq < a.T)
+                             ? *reinterpret_cast<const float4*>(xr + tq)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+      switch (m) {   // constant register indices in every branch
+        case 0:
+#pragma unroll
+          for (int e = 0; e < BE; ++e) rb[e] = v[e];
+          break;
+        case 1:
+#pragma unroll
+          for (int e = 0; e < BE; ++e) rb[e] = v[e + 1];
+          break;
+        case 2:
+#pragma unroll
+          for (int e = 0; e < BE; ++e) rb[e] = v[e + 2];
+          break;
+        default:
+#pragma unroll
+          for (int e = 0; e < BE; ++e) rb[e] = v[e + 3];
+          break;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < BE; ++e)
+        rb[e] = (r < R && t + e >= 0 && t + e < a.T) ? xr[t + e] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < AE; ++e) {
+      const int k = ak + e;
+      As[buf][am][(k & ~15) | ((k & 3) * 4 + ((k & 15) >> 2))] = ra[e];
+    }
+#pragma unroll
+    for (int e = 0; e < BE; ++e) Bs[buf][bn + e][bkp] = rb[e];
+  };
+  Floatx4 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int k = 0; k < WN; ++k) acc[i][k] = Floatx4{0.f, 0.f, 0.f, 0.f};
+  const int wm0 = (wave >> 1) * 16 * WM, wn0 = (wave & 1) * 16 * WN;
+  const int lr = lane & 15, lq = (lane >> 4) * 4;
+  const int nchunk = (R + BK - 1) / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunk) load((c + 1) * BK);
+#pragma unroll
+    for (int g = 0; g < BK; g += 16) {
+      float4 fa[WM], fb[WN];
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+        fa[i] = *reinterpret_cast<const float4*>(&As[buf][wm0 + 16 * i + lr][g + lq]);
+#pragma unroll
+      for (int k = 0; k < WN; ++k)
+        fb[k] = *reinterpret_cast<const float4*>(&Bs[buf][wn0 + 16 * k + lr][g + lq]);
+#pragma unroll
+      for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int k = 0; k < WN; ++k) {
+          acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i].x, fb[k].x, acc[i][k], 0, 0, 0);
+          acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i].y, fb[k].y, acc[i][k], 0, 0, 0);
+          acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i].z, fb[k].z, acc[i][k], 0, 0, 0);
+          acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i].w, fb[k].w, acc[i][k], 0, 0, 0);
+        }
+    }
+    if (c + 1 < nchunk) store(buf ^ 1);
+    __syncthreads();
+  }
+  // lane holds rows 4 (lane / 16) + e, column lane % 16 of each 16 x 16 block
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int co = c0 + wm0 + 16 * i + lq + e;
+      if (co >= a.cout) continue;
+      const float bv = a.bias ? a.bias[co] : 0.f;
+      float* yr = a.y + (size_t)co * a.ldy + p;
+#pragma unroll
+      for (int k = 0; k < WN; ++k) {
+        const int t = t0 + wn0 + 16 * k + lr;
+        if (t < a.T) {
+          float* o = yr + (size_t)t * a.ystride;
+          *o = (a.accumulate ? *o : 0.f) + (acc[i][k][e] + bv);
+        }
+      }
+    }
+}
+
+template <int WM, int WN, int BK>
+void conv_launch(const ConvArgs& a, hipStream_t s) {
+  const dim3 g((a.T + 32 * WN - 1) / (32 * WN), (a.cout + 32 * WM - 1) / (32 * WM), a.P);
+  hipLaunchKernelGGL((k_conv1d<WM, WN, BK>), g, dim3(256), 0, s, a);
+}
+
 hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int wtype, hipStream_t s) {
   switch (wtype) {
     case kWBF16: gemv_dispatch<uint16_t>(a, epi, norm, s); break;
@@ -1912,9 +2020,18 @@ hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int wtype, hipStre
   return hipGetLastError();
 }
 
+// Tile of a convolution GEMM (measured over the codec decoder's layer shapes):
+// 64 x 64 while that grid gives ~3 workgroups per compute unit, then 64 x 32
+// with a deeper reduction chunk, then 32 x 32; 32 x 64 for <= 32 output
+// channels, where a 64-channel tile would be mostly idle.
 hipError_t launch_conv(const ConvArgs& a, hipStream_t s) {
-  const dim3 grid((a.T + kConvTile - 1) / kConvTile, (a.cout + kConvTile - 1) / kConvTile, a.P);
-  hipLaunchKernelGGL(k_conv1d, grid, dim3(256), 0, s, a);
+  auto blocks = [&](int bm, int bn) {
+    return (long)((a.T + bn - 1) / bn) * ((a.cout + bm - 1) / bm) * a.P;
+  };
+  if (a.cout <= 32) conv_launch<1, 2, 64>(a, s);
+  else if (blocks(64, 64) >= 700) conv_launch<2, 2, 32>(a, s);
+  else if (blocks(64, 32) >= 400) conv_launch<2, 1, 64>(a, s);
+  else conv_launch<1, 1, 64>(a, s);
   return hipGetLastError();
 }
 

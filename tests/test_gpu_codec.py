@@ -34,6 +34,9 @@ CONV_CASES = [   # cin, cout, T, K, dilation
     (128, 128, 257, 1, 1),
     (7, 1, 300, 7, 1),        # output convolution to one channel
     (512, 512, 2400, 7, 3),   # a first-stage residual convolution at full length
+    (8, 8, 1, 7, 1),          # one frame: only the last tap sees data
+    (16, 8, 20, 7, 9),        # taps reaching before frame 0 for every t (shifts up to 54)
+    (1024, 1024, 300, 7, 1),  # the input convolution (the smallest grid)
 ]
 
 
@@ -60,6 +63,8 @@ TRANS_CASES = [   # cin, cout, T, stride
     (512, 256, 2400, 5),
     (256, 128, 12000, 4),
     (128, 64, 48000, 3),
+    (9, 4, 1, 2),             # one input frame: only the first tap of each phase
+    (5, 3, 11, 1),            # stride 1 (kernel 2)
 ]
 
 

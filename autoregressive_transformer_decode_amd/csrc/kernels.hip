@@ -1591,7 +1591,13 @@ __device__ __forceinline__ Bf16x8 as_bf16x8(uint4 v) {
 // fragments go straight to registers.  Both come through a P-deep register
 // ring, so the loads of P stages are in flight while a stage is multiplied,
 // and the in-order memory counter only ever waits for the oldest stage.
-template <int P>
+// NCH > 0: every workgroup walks exactly NCH stages, fully unrolled, with
+// every load issued unconditionally (clamped addresses; groups past the split
+// end are zeroed when written to LDS), so the compiler's counter waits are
+// exact (with the stage loop it waited for every outstanding load at the
+// loop head: measured 12-32% slower on the 64-row shapes).  NCH = 0: the
+// stage loop, for other stage counts.
+template <int P, int NCH>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   // LDS tile [buf][hi/lo][row][8 x 16 bytes]; the 16-byte chunk c of row r
   // sits at c ^ (r & 7) so that a fragment read spreads over the banks
@@ -1630,14 +1636,60 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) wr[p][s] = ldg16(wp + min(kb + c * kMmaCh + s * 32, K - 32));
   };
+  Floatx4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = Floatx4{0.f, 0.f, 0.f, 0.f};
+  // one stage's MFMAs on LDS buffer buf with the weights of ring slot p
+  auto mma_stage = [&](int p, int buf) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int pos = (s * 4 + lg) ^ (li & 7);
+      const Bf16x8 b = as_bf16x8(wr[p][s]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sa[buf][0][i * 16 + li][pos]), b,
+                                                         acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sa[buf][1][i * 16 + li][pos]), b,
+                                                         acc[i], 0, 0, 0);
+      }
+    }
+  };
+  if constexpr (NCH > 0) {
+    auto issue_a_all = [&](int p, int c) {
+      const int kk = min(kb + c * kMmaCh + sc * 8, K - 8) - sc * 8;
+      ar[p][0] = ldg16(sh + kk);
+      ar[p][1] = ldg16(sh + (size_t)32 * K + kk);
+      ar[p][2] = ldg16(sl + kk);
+      ar[p][3] = ldg16(sl + (size_t)32 * K + kk);
+    };
+#pragma unroll
+    for (int p = 0; p < P && p < NCH; ++p) {
+      issue_a_all(p, p);
+      issue_w(p, p);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int p = c % P, buf = c & 1;
+      const int sw = sc ^ (srow & 7);
+      // whole groups: K and the split ends are multiples of 32 (a mask, not a
+      // select: a select of the register ring became a scratch access)
+      const uint32_t mk = 0u - (uint32_t)(kb + c * kMmaCh + sc * 8 < ke);
+      auto keep = [mk](uint4 v) { return make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk); };
+      sa[buf][0][srow][sw] = keep(ar[p][0]);
+      sa[buf][0][srow + 32][sw] = keep(ar[p][1]);
+      sa[buf][1][srow][sw] = keep(ar[p][2]);
+      sa[buf][1][srow + 32][sw] = keep(ar[p][3]);
+      __syncthreads();
+      if (c + P < NCH) issue_a_all(p, c + P);
+      mma_stage(p, buf);
+      if (c + P < NCH) issue_w(p, c + P);
+    }
+  } else {
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     issue_a(p, p);
     issue_w(p, p);
   }
-  Floatx4 acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = Floatx4{0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < nch; c0 += P) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -1651,21 +1703,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         sa[buf][1][srow + 32][sw] = ar[p][3];
         __syncthreads();
         issue_a(p, c + P);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int pos = (s * 4 + lg) ^ (li & 7);
-          const Bf16x8 b = as_bf16x8(wr[p][s]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sa[buf][0][i * 16 + li][pos]), b,
-                                                             acc[i], 0, 0, 0);
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sa[buf][1][i * 16 + li][pos]), b,
-                                                             acc[i], 0, 0, 0);
-          }
-        }
+        mma_stage(p, buf);
         issue_w(p, c + P);
       }
     }
+  }
   }
   // C layout: column li, rows 4 * lg + r of each 16x16 tile
   if (row < a.N) {
@@ -2193,7 +2235,19 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   const dim3 grid((a.N + kMmaBlockN - 1) / kMmaBlockN, a.ks);
-  hipLaunchKernelGGL(k_gemm<2>, grid, dim3(256), 0, s, a);
+  // stages of a split (the last split may hold fewer real ones: the rest
+  // read zero activations)
+  switch ((a.kc + kMmaCh - 1) / kMmaCh) {
+    case 1: hipLaunchKernelGGL((k_gemm<2, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm<2, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm<2, 3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_gemm<2, 4>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((k_gemm<2, 6>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_gemm<2, 8>), grid, dim3(256), 0, s, a); break;
+    case 12: hipLaunchKernelGGL((k_gemm<2, 12>), grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_gemm<2, 16>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm<2, 0>), grid, dim3(256), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -45,8 +45,9 @@ struct atd_decoder {
   uint2* samp = nullptr;       // sampler chunk candidates [sample_blocks(V), kTopKMax]
   bool mma = false;            // MFMA path for chunks of >= 3 rows
   float* mpart = nullptr;      // split-K partials of the MFMA GEMMs
-  float* mss = nullptr;        // row sums of squares [kMmaRows, ceil(h / kSsCols)]
-  uint16_t *mhi = nullptr, *mlo = nullptr;  // GEMM input as bf16 hi/lo [kMmaRows, Kmax]
+  int mma_rows = 0;            // rows of one MFMA prefill chunk (multiple of kMmaRows)
+  float* mss = nullptr;        // row sums of squares [mma_rows, ceil(h / kSsCols)]
+  uint16_t *mhi = nullptr, *mlo = nullptr;  // GEMM input as bf16 hi/lo [mma_rows, Kmax]
   int32_t* counter = nullptr;  // token counter of decoder_generate
   int32_t* ctl_base = nullptr; // first choice index of a controlled generate call
   size_t part_floats = 0;      // capacity of pacc in floats / D
@@ -455,7 +456,8 @@ hipError_t run_head_gemv(atd_decoder* d, const float* xrows, int M, int head, fl
 // GEMM of the chunk's activations (d->mhi / d->mlo, [kMmaRows, K]) with an
 // [N, K] weight given as up to three row segments; split partials into d->mpart.
 hipError_t mma_gemm(atd_decoder* d, const void* w0, const void* w1, const void* w2, int e0,
-                    int e1, int N, int K, hipStream_t s) {
+                    int e1, int N, int K, int M, hipStream_t s) {
+  const int tiles = (M + kMmaRows - 1) / kMmaRows;
   GemmArgs g{};
   g.hi = d->mhi;
   g.lo = d->mlo;
@@ -467,11 +469,15 @@ hipError_t mma_gemm(atd_decoder* d, const void* w0, const void* w1, const void* 
   g.seg_end[2] = N;
   g.K = K;
   g.N = N;
-  g.kc = mma_kc(N, K);
-  g.ks = mma_ks(N, K);
+  g.kc = mma_kc(N, K, tiles);
+  g.ks = mma_ks(N, K, tiles);
+  g.mrows = tiles * kMmaRows;
   g.part = d->mpart;
   return launch_gemm(g, s);
 }
+
+// Splits of the GEMM of an [N, K] weight over M rows (as mma_gemm takes them).
+int mma_splits(int N, int K, int M) { return mma_ks(N, K, (M + kMmaRows - 1) / kMmaRows); }
 
 // Reductions of the splits of the last GEMM (N columns, ks splits) over M rows.
 ReduceArgs mma_red(atd_decoder* d, int N, int ks, int M, float* out, int ldo) {
@@ -480,6 +486,7 @@ ReduceArgs mma_red(atd_decoder* d, int N, int ks, int M, float* out, int ldo) {
   r.ks = ks;
   r.N = N;
   r.M = M;
+  r.mrows = (M + kMmaRows - 1) / kMmaRows * kMmaRows;
   r.seg_end[0] = r.seg_end[1] = r.seg_end[2] = N;
   r.out = out;
   r.ldo = ldo;
@@ -527,8 +534,8 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
     const atd_layer_weights& W = d->layers[l];
     const float* next_gain =
         l + 1 < c.n_layers ? (const float*)d->layers[l + 1].attn_norm : d->final_norm;
-    STAGE(ATD_STAGE_QKV, mma_gemm(d, W.wq, W.wk, W.wv, nq, nq + nkv, nqkv, h, s));
-    ReduceArgs rq = mma_red(d, nqkv, mma_ks(nqkv, h), M, d->qkv, nqkv);
+    STAGE(ATD_STAGE_QKV, mma_gemm(d, W.wq, W.wk, W.wv, nq, nq + nkv, nqkv, h, M, s));
+    ReduceArgs rq = mma_red(d, nqkv, mma_splits(nqkv, h, M), M, d->qkv, nqkv);
     rq.bias[0] = (const float*)W.bq;
     rq.bias[1] = (const float*)W.bk;
     rq.bias[2] = (const float*)W.bv;
@@ -541,21 +548,21 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
     aa.o_hi = d->mhi;
     aa.o_lo = d->mlo;
     STAGE(ATD_STAGE_ATTN, attention(d, aa, s));
-    STAGE(ATD_STAGE_OPROJ, mma_gemm(d, W.wo, W.wo, W.wo, h, h, h, nq, s));
-    STAGE(ATD_STAGE_OPROJ, mma_residual(d, mma_ks(h, nq), M, x, (const float*)W.mlp_norm, s));
-    STAGE(ATD_STAGE_GATEUP, mma_gemm(d, W.w_gate, W.w_up, W.w_up, F, 2 * F, 2 * F, h, s));
-    ReduceArgs rg = mma_red(d, 2 * F, mma_ks(2 * F, h), M, nullptr, 0);
+    STAGE(ATD_STAGE_OPROJ, mma_gemm(d, W.wo, W.wo, W.wo, h, h, h, nq, M, s));
+    STAGE(ATD_STAGE_OPROJ, mma_residual(d, mma_splits(h, nq, M), M, x, (const float*)W.mlp_norm, s));
+    STAGE(ATD_STAGE_GATEUP, mma_gemm(d, W.w_gate, W.w_up, W.w_up, F, 2 * F, 2 * F, h, M, s));
+    ReduceArgs rg = mma_red(d, 2 * F, mma_splits(2 * F, h, M), M, nullptr, 0);
     rg.ss = d->mss;
     rg.hi = d->mhi;
     rg.lo = d->mlo;
     STAGE(ATD_STAGE_GATEUP, launch_reduce(rg, kRedSwiglu, s));
-    STAGE(ATD_STAGE_DOWN, mma_gemm(d, W.w_down, W.w_down, W.w_down, h, h, h, F, s));
-    STAGE(ATD_STAGE_DOWN, mma_residual(d, mma_ks(h, F), M, x, next_gain, s));
+    STAGE(ATD_STAGE_DOWN, mma_gemm(d, W.w_down, W.w_down, W.w_down, h, h, h, F, M, s));
+    STAGE(ATD_STAGE_DOWN, mma_residual(d, mma_splits(h, F, M), M, x, next_gain, s));
   }
   if (ho) {
     const void* Wh = d->heads[ho->head];
-    STAGE(ATD_STAGE_HEAD, mma_gemm(d, Wh, Wh, Wh, c.vocab, c.vocab, c.vocab, h, s));
-    ReduceArgs rh = mma_red(d, c.vocab, mma_ks(c.vocab, h), M, ho->logits, c.vocab);
+    STAGE(ATD_STAGE_HEAD, mma_gemm(d, Wh, Wh, Wh, c.vocab, c.vocab, c.vocab, h, M, s));
+    ReduceArgs rh = mma_red(d, c.vocab, mma_splits(c.vocab, h, M), M, ho->logits, c.vocab);
     rh.ss = d->mss;
     rh.x = x;
     rh.gain = d->final_norm;
@@ -566,14 +573,17 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
 }
 
 // Rows of a call run through the stack (and the LM head when `ho` is set):
-// chunks of kMmaRows on the MFMA path, one after the other (which keeps a
-// prefill causal: a chunk's rows only read keys of earlier rows, already
-// appended), otherwise the GEMV path.
+// chunks on the MFMA path, one after the other (which keeps a prefill causal:
+// a chunk's rows only read keys of earlier rows, already appended), otherwise
+// the GEMV path.
 hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
                       const HeadOut* ho, hipStream_t s) {
   const int h = d->cfg.hidden, V = d->cfg.vocab;
   hipError_t e = hipSuccess;
-  const int step = d->mma && M >= 3 ? kMmaRows : M;
+  // decode steps in chunks of kMmaRows streams; a prefill in chunks of up to
+  // d->mma_rows rows, each taken layer by layer (a chunk's rows read the keys
+  // of earlier chunks and their own, appended first)
+  const int step = d->mma && M >= 3 ? (rows.mode == kRowsPrefill ? d->mma_rows : kMmaRows) : M;
   for (int c0 = 0; c0 < M && e == hipSuccess; c0 += step) {
     RowMap r = rows;
     r.row0 = rows.row0 + c0;
@@ -752,13 +762,20 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
            nq % 32 == 0 && cfg->ffn % 32 == 0 && std::max(R, S) >= 3;
   size_t o_mss = 0, o_mhi = 0, o_mlo = 0, o_mpart = 0;
   if (d->mma) {
-    auto parts = [](int n, int k) { return (size_t)mma_ks(n, k) * kMmaRows * n; };
-    const size_t pmax = std::max({parts(nqkv, h), parts(h, nq), parts(2 * cfg->ffn, h),
-                                  parts(h, cfg->ffn), parts(cfg->vocab, h)});
-    o_mss = carve((size_t)kMmaRows * ((h + kSsCols - 1) / kSsCols) * 4);
+    // prefill chunks of up to kMmaPrefillRows rows (row tiles of kMmaRows)
+    d->mma_rows = std::max(kMmaRows, (std::min(R, kMmaPrefillRows) + kMmaRows - 1) / kMmaRows *
+                                         kMmaRows);
+    // partials of the largest GEMM at every row-tile count a chunk can have
+    size_t pmax = 0;
+    for (int t = 1; t <= d->mma_rows / kMmaRows; ++t) {
+      auto parts = [t](int n, int k) { return (size_t)mma_ks(n, k, t) * t * kMmaRows * n; };
+      pmax = std::max({pmax, parts(nqkv, h), parts(h, nq), parts(2 * cfg->ffn, h),
+                       parts(h, cfg->ffn), parts(cfg->vocab, h)});
+    }
+    o_mss = carve((size_t)d->mma_rows * ((h + kSsCols - 1) / kSsCols) * 4);
     const size_t kmax = std::max({(size_t)h, (size_t)nq, (size_t)cfg->ffn});
-    o_mhi = carve((size_t)kMmaRows * kmax * 2);
-    o_mlo = carve((size_t)kMmaRows * kmax * 2);
+    o_mhi = carve((size_t)d->mma_rows * kmax * 2);
+    o_mlo = carve((size_t)d->mma_rows * kmax * 2);
     o_mpart = carve(pmax * 4);
   }
 

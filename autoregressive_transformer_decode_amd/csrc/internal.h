@@ -137,7 +137,7 @@ struct AttnArgs {
   float* pml;         // [M, Hq, nsplit_max, 2] running max and sum
   float* pacc;        // [M, Hq, nsplit_max, D]
   float* o;           // [M, Hq * D] (combine output)
-  uint16_t* o_hi;     // or, when set, bf16 hi/lo parts of o: [kMmaRows, Hq * D]
+  uint16_t* o_hi;     // or, when set, bf16 hi/lo parts of o: [M, Hq * D]
   uint16_t* o_lo;
 };
 
@@ -219,19 +219,25 @@ struct KvCopyArgs {
 // bf16(v - hi)), so the products keep ~16 bits of the float32 input while the
 // bf16 weights are used exactly; each float32 activation is split into bf16
 // hi + lo parts as it is staged, so the products carry ~16 mantissa bits.
-constexpr int kMmaRows = 64;     // rows per GEMM chunk
+constexpr int kMmaRows = 64;     // rows per GEMM row tile (and per decode-step chunk)
+constexpr int kMmaPrefillRows = 512;   // most rows of one layer-major prefill chunk
 constexpr int kMmaBlockN = 64;   // weight rows per workgroup (16 per wave)
 constexpr int kMmaCh = 64;       // K per pipeline stage
 constexpr int kMmaCUs = 256;     // compute units of the part
 constexpr int kSsCols = 256;     // columns per partial sum of squares
 
-// K per split of the GEMM of an [N, K] weight (a multiple of kMmaCh): the
-// fewest splits that give every compute unit a workgroup, raised (up to 4x)
-// to a whole number of workgroups per unit when one exists, so that no
-// partial round of workgroups trails the rest (measured on the 1.7B shapes)
-inline int mma_kc(int N, int K) {
-  const int nb = (N + kMmaBlockN - 1) / kMmaBlockN;
-  const int k0 = (kMmaCUs + nb - 1) / nb;
+// K per split of the GEMM of an [N, K] weight over `tiles` row tiles (a
+// multiple of kMmaCh): the fewest splits that give every compute unit a
+// workgroup and keep a split within 16 stages, raised (up to 4x) to a whole
+// number of workgroups per unit when one exists, so that no partial round of
+// workgroups trails the rest (measured on the 1.7B shapes)
+inline int mma_kc(int N, int K, int tiles = 1) {
+  const int nb = (N + kMmaBlockN - 1) / kMmaBlockN * tiles;
+  // at most 16 stages per split: the stage counts the GEMM kernel has fully
+  // unrolled forms for
+  const int kmin = (K + 16 * kMmaCh - 1) / (16 * kMmaCh);
+  const int kfill = (kMmaCUs + nb - 1) / nb;
+  const int k0 = kfill > kmin ? kfill : kmin;
   int ks = k0;
   for (int k = k0; k <= 4 * k0; ++k)
     if ((nb * k) % kMmaCUs == 0) {
@@ -242,19 +248,20 @@ inline int mma_kc(int N, int K) {
   kc = (kc + kMmaCh - 1) / kMmaCh * kMmaCh;
   return (int)(kc < K ? kc : (K + kMmaCh - 1) / kMmaCh * kMmaCh);
 }
-inline int mma_ks(int N, int K) {
-  const int kc = mma_kc(N, K);
+inline int mma_ks(int N, int K, int tiles = 1) {
+  const int kc = mma_kc(N, K, tiles);
   return (K + kc - 1) / kc;
 }
 
 struct GemmArgs {
-  const uint16_t* hi;  // activations as bf16 hi + lo parts [kMmaRows, K]; rows >= M may
+  const uint16_t* hi;  // activations as bf16 hi + lo parts [mrows, K]; rows >= M may
   const uint16_t* lo;  // hold anything (each output row depends on its own row only)
   const void* W[3];    // bf16 row segments [rows_s, K]
   int seg_end[3];
   int K, N;            // K multiple of 32
   int kc, ks;          // K per split (multiple of kMmaCh) and number of splits
-  float* part;         // [ks, kMmaRows, N]
+  int mrows;           // rows of the call, rounded up to row tiles of kMmaRows
+  float* part;         // [ks, mrows, N]
 };
 
 enum ReduceEpilogue { kRedStore = 0, kRedResidual = 1, kRedSwiglu = 2 };
@@ -263,13 +270,14 @@ enum ReduceEpilogue { kRedStore = 0, kRedResidual = 1, kRedSwiglu = 2 };
 // the residual reduction leaves x * g (the next GEMM's input, as hi/lo) and
 // partial sums of squares of x; the reduction after that GEMM applies inv_m.
 struct ReduceArgs {
-  const float* part;   // [ks, kMmaRows, N]
+  const float* part;   // [ks, mrows, N]
   int ks, N, M;        // ks = 0: no partials (kRedResidual then only refreshes hi/lo, ss)
+  int mrows;           // row stride of a split's partials
   const float* bias[3];  // kRedStore: per-segment bias or null
   int seg_end[3];
   float* out;          // kRedStore: [M, ldo] written; kRedResidual: [M, ldo] updated
   int ldo;
-  uint16_t* hi;        // kRedResidual: x * gain; kRedSwiglu: the activation ([kMmaRows, N or N/2])
+  uint16_t* hi;        // kRedResidual: x * gain; kRedSwiglu: the activation ([M, N or N/2])
   uint16_t* lo;
   const float* gain;   // kRedResidual: gain of the next norm; kRedStore: gain for y_out
   // kRedResidual writes ss [M, gridDim.x] (kSsCols-column partial sums of squares

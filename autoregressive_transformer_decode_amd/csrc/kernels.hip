@@ -1582,9 +1582,10 @@ __device__ __forceinline__ Bf16x8 as_bf16x8(uint4 v) {
   return c.b;
 }
 
-// Split-K GEMM of a chunk of up to 64 rows: part[split, m, n] = sum over the
-// split's K range of (hi + lo)[m, k] * W[n, k]: bf16 MFMA 16x16x32, float32
-// accumulation.  Workgroup (64 weight rows, split): wave w owns 16 rows.  The
+// Split-K GEMM of the rows of a call, in row tiles of 64: part[split, m, n] =
+// sum over the split's K range of (hi + lo)[m, k] * W[n, k]: bf16 MFMA
+// 16x16x32, float32 accumulation.  Workgroup (64 weight rows, split, row
+// tile): wave w owns 16 weight rows.  The
 // split is walked in 64-wide stages; each stage's activation tile (64 rows,
 // hi and lo) is read with row-contiguous loads into a double-buffered LDS
 // tile, from which every wave reads its MFMA fragments, while the weight
@@ -1605,6 +1606,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * kMmaBlockN + wave * 16, split = blockIdx.y;
+  const int r0 = blockIdx.z * kMmaRows;   // the workgroup's row tile
   const int K = a.K;
   const int kb = split * a.kc, ke = min(K, kb + a.kc);
   const int nch = (ke - kb + kMmaCh - 1) / kMmaCh;
@@ -1617,8 +1619,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
                        (size_t)(row < a.N ? row - sb : 0) * K + lg * 8;
   // staging: thread -> rows srow and srow + 32, 16-byte group sc
   const int srow = tid >> 3, sc = tid & 7;
-  const uint16_t* sh = a.hi + (size_t)srow * K + sc * 8;
-  const uint16_t* sl = a.lo + (size_t)srow * K + sc * 8;
+  const uint16_t* sh = a.hi + (size_t)(r0 + srow) * K + sc * 8;
+  const uint16_t* sl = a.lo + (size_t)(r0 + srow) * K + sc * 8;
 
   uint4 ar[P][4], wr[P][2];
   auto issue_a = [&](int p, int c) {
@@ -1711,7 +1713,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   }
   // C layout: column li, rows 4 * lg + r of each 16x16 tile
   if (row < a.N) {
-    float* Pp = a.part + (size_t)split * kMmaRows * a.N + row;
+    float* Pp = a.part + ((size_t)split * a.mrows + r0) * a.N + row;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1730,7 +1732,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     float t = 0.f;
     if (n < NO) {
       float v = 0.f;
-      for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * kMmaRows + m) * a.N + n];
+      for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * a.mrows + m) * a.N + n];
       float* o = a.out + (size_t)m * a.ldo + n;
       t = *o + v;
       *o = t;
@@ -1757,7 +1759,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
   if constexpr (EPI == kRedSwiglu) {
     float g = 0.f, u = 0.f;
     for (int s = 0; s < a.ks; ++s) {
-      const float* P = a.part + ((size_t)s * kMmaRows + m) * a.N;
+      const float* P = a.part + ((size_t)s * a.mrows + m) * a.N;
       g += P[n];
       u += P[NO + n];
     }
@@ -1766,7 +1768,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     split_hi_lo(g / (1.0f + expf(-g)) * u, a.hi[(size_t)m * NO + n], a.lo[(size_t)m * NO + n]);
   } else {
     float v = 0.f;
-    for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * kMmaRows + m) * a.N + n];
+    for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * a.mrows + m) * a.N + n];
     v *= inv;
     const int sg = n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
     const int sb = sg == 0 ? 0 : (sg == 1 ? a.seg_end[0] : a.seg_end[1]);
@@ -2234,7 +2236,8 @@ hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-  const dim3 grid((a.N + kMmaBlockN - 1) / kMmaBlockN, a.ks);
+  if (a.mrows < kMmaRows || a.mrows % kMmaRows) return hipErrorInvalidValue;
+  const dim3 grid((a.N + kMmaBlockN - 1) / kMmaBlockN, a.ks, a.mrows / kMmaRows);
   // stages of a split (the last split may hold fewer real ones: the rest
   // read zero activations)
   switch ((a.kc + kMmaCh - 1) / kMmaCh) {

@@ -26,6 +26,7 @@ Also measured in the same run:
                 on the device by sample_topk inside the step graph.
   token_choice_us  microseconds per call of greedy_argmax and sample_topk on
                 one row of the vocabulary.
+  prefill       the 512-row prefill alone (MFMA, layer by layer), best of three.
   mrope         eager steps through decoder_step_mrope (distinct t/h/w rotary
                 positions) against eager decoder_step on the same schedule.
   quantized     the same K greedy steps with the seven per-layer matrices
@@ -69,6 +70,12 @@ def kernel_hash() -> str:
 # bytes per weight of the block-quantized formats: the code and 2 bytes of
 # fp16 scale per 32 weights
 QUANT_BPW = {"q8": 1.0 + 2.0 / 32, "q4": 0.5 + 2.0 / 32}
+
+
+def weight_elems_layers(shape) -> int:
+    """Weights of the per-layer matrices (no LM head, no input projection)."""
+    h, q, kv, f = shape.hidden, shape.q_dim, shape.kv_dim, shape.ffn
+    return (h * q + 2 * h * kv + q * h + 3 * h * f) * shape.n_layers
 
 
 def weight_bytes(shape, quant=None) -> int:
@@ -241,6 +248,20 @@ def bench_lm(args, wl):
     W = K if len(caps) > 1 else W
     if W:
         schedule(W)
+    # the prefill alone (MFMA GEMMs over all its rows, layer by layer): the
+    # faster of three runs
+    pf = float("inf")
+    for _ in range(3):
+        dec.set_position(0, 0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dec.prefill(X0_d, logits_out=z)
+        torch.cuda.synchronize()
+        pf = min(pf, time.perf_counter() - t0)
+    # 2 flops per weight and row for the layers (the LM head runs on the last row),
+    # plus the causal attention products (q.k and p.v over the rows before each row)
+    pf_flops = 2.0 * P0 * weight_elems_layers(s) + 2.0 * s.hidden * s.vocab + \
+        2.0 * 2 * s.n_layers * s.n_q_heads * s.head_dim * (P0 * (P0 + 1) / 2)
     dt = schedule(K)
     log(f"timed {K} steps: {dt * 1e3:.1f} ms (buckets {caps})")
     # the same run with the sampling defaults (graphs captured by a warmup)
@@ -322,6 +343,11 @@ def bench_lm(args, wl):
                           penalty=SAMPLING_PENALTY)),
         token_choice_us=None if args.no_sampled else time_choice(s.vocab),
         mrope=mrope,
+        prefill=dict(rows=P0, ms=pf * 1e3, tokens_per_s=P0 / pf, tflops=pf_flops / pf / 1e12,
+                     mfma_peak_tflops=2500.0,
+                     note="bf16 MFMA with float32 activations as bf16 hi + lo operands (two "
+                          "products per weight); rows layer by layer in chunks of up to 512, "
+                          "GEMMs over 64-row tiles"),
     )
     dec.close()
     # the same greedy run with the seven per-layer matrices block-quantized

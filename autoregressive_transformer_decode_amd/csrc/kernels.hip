@@ -714,6 +714,9 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   if (k0 >= len) return;
   const int k1 = min(len, k0 + chunk);
   const bool owns_new = a.fused && k1 == len;
+  // the cached keys this wave reads: the owner of the new row takes that row
+  // from its registers, first, and reads the cache only below it
+  const int kend = owns_new ? k1 - 1 : k1;
 
   // position-dependent small loads first (RoPE table, gains, the new row),
   // then the cache rows: the in-order memory counter lets the query math
@@ -769,13 +772,15 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
     }
   }
 
-  // keys past the split end are clamped to its last key (always in bounds)
-  // and masked out in the softmax
+  // keys past the range end are clamped to its last key (always in bounds;
+  // row 0 when the range is empty, then never used) and masked out in the
+  // softmax
   uint4 kr[U][NV], vr[U][NV];
+  const int klast = kend > 0 ? kend - 1 : 0;
   auto load = [&](int kb) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = min(kb + u * KPW + sub, k1 - 1);
+      const int key = min(kb + u * KPW + sub, klast);
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         kr[u][v] = ldg16(Kh + (size_t)key * D + v * VEC);
@@ -855,23 +860,48 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[j][e] = 0.f;
   }
+  // the new row (as stored, rounded to the cache dtype) opens the state of
+  // the owner's first lane group: score s, weight 1, value v
+  if (owns_new) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      float d = 0.f;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float kv[VEC];
+        Vec16<KT>::unpack(knew[v], kv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d = fmaf(qv[j][v * VEC + e], kv[e], d);
+      }
+      d = group_sum<LPK>(d);
+      if (sub == 0) {
+        mx[j] = d;
+        ls[j] = 1.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          float vv[VEC];
+          Vec16<KT>::unpack(vnew[v], vv);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[j][v * VEC + e] = vv[e];
+        }
+      }
+    }
+  }
 
-  for (int kb = k0; kb < k1; kb += TILE) {
+  for (int kb = k0; kb < kend; kb += TILE) {
     // the tile's raw rows (unpacked to float where used, to keep registers low)
     uint4 kc[U][NV], vc[U][NV];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int key = kb + u * KPW + sub;
-      ok[u] = key < k1;
-      const bool fresh = owns_new && key == pos;   // the cache row may not be written yet
+      ok[u] = kb + u * KPW + sub < kend;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        kc[u][v] = fresh ? knew[v] : kr[u][v];
-        vc[u][v] = fresh ? vnew[v] : vr[u][v];
+        kc[u][v] = kr[u][v];
+        vc[u][v] = vr[u][v];
       }
     }
-    if (kb + TILE < k1) load(kb + TILE);
+    if (kb + TILE < kend) load(kb + TILE);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       float sc[U];

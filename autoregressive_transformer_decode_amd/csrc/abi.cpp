@@ -45,7 +45,7 @@ struct atd_decoder {
   uint2* samp = nullptr;       // sampler chunk candidates [sample_blocks(V), kTopKMax]
   bool mma = false;            // MFMA path for chunks of >= 3 rows
   float* mpart = nullptr;      // split-K partials of the MFMA GEMMs
-  int mma_rows = 0;            // rows of one MFMA prefill chunk (multiple of kMmaRows)
+  int mma_rows = 0;            // most rows of one MFMA chunk (multiple of kMmaRows)
   float* mss = nullptr;        // row sums of squares [mma_rows, ceil(h / kSsCols)]
   uint16_t *mhi = nullptr, *mlo = nullptr;  // GEMM input as bf16 hi/lo [mma_rows, Kmax]
   int32_t* counter = nullptr;  // token counter of decoder_generate
@@ -580,10 +580,11 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, flo
                       const HeadOut* ho, hipStream_t s) {
   const int h = d->cfg.hidden, V = d->cfg.vocab;
   hipError_t e = hipSuccess;
-  // decode steps in chunks of kMmaRows streams; a prefill in chunks of up to
-  // d->mma_rows rows, each taken layer by layer (a chunk's rows read the keys
-  // of earlier chunks and their own, appended first)
-  const int step = d->mma && M >= 3 ? (rows.mode == kRowsPrefill ? d->mma_rows : kMmaRows) : M;
+  // chunks of up to d->mma_rows rows (decode streams, or prefill rows), each
+  // taken layer by layer: the GEMMs stream the weights once per chunk over its
+  // 64-row tiles (a prefill chunk's rows read the keys of earlier chunks and
+  // their own, appended first)
+  const int step = d->mma && M >= 3 ? d->mma_rows : M;
   for (int c0 = 0; c0 < M && e == hipSuccess; c0 += step) {
     RowMap r = rows;
     r.row0 = rows.row0 + c0;
@@ -762,7 +763,7 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
            nq % 32 == 0 && cfg->ffn % 32 == 0 && std::max(R, S) >= 3;
   size_t o_mss = 0, o_mhi = 0, o_mlo = 0, o_mpart = 0;
   if (d->mma) {
-    // prefill chunks of up to kMmaPrefillRows rows (row tiles of kMmaRows)
+    // chunks of up to kMmaPrefillRows rows (row tiles of kMmaRows)
     d->mma_rows = std::max(kMmaRows, (std::min(R, kMmaPrefillRows) + kMmaRows - 1) / kMmaRows *
                                          kMmaRows);
     // partials of the largest GEMM at every row-tile count a chunk can have

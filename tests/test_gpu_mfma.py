@@ -27,15 +27,16 @@ def _log(msg):
 MFMA_SHAPE = ("mfma", 2, 288, 8, 2, 128, 672, 1000, "bf16", True, True)
 
 
-@pytest.mark.parametrize("T", [3, 64, 66, 133])
+@pytest.mark.parametrize("T", [3, 64, 66, 133, 514, 600])
 def test_prefill_chunks(T):
-    """Prefill of T rows: full 64-row chunks, a ragged MFMA chunk, and a
-    1-2 row tail on the vector path; then teacher-forced steps read the KV
-    rows every chunk appended."""
+    """Prefill of T rows: one chunk of ragged 64-row tiles (3, 64, 66, 133), a
+    full 512-row chunk then a 2-row tail on the vector path (514) or a second
+    MFMA chunk (600); then teacher-forced steps read the KV rows every chunk
+    appended."""
     shape = small_shape(*MFMA_SHAPE)
     mw = inputs.make_weights(shape, seed=7)
     X0 = inputs.normal(7, 2, 11, (T, shape.hidden), scale=1.0)
-    chk, ref, _ = lm_parity(mw, X0, 6, 256)
+    chk, ref, _ = lm_parity(mw, X0, 6, 256 if T < 256 else 1024)
     _log(f"prefill T={T}: {chk.n} checks, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
 
 

@@ -547,7 +547,12 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
     AttnArgs aa = attn_args(d, rows, l, M, max_len_bound, fused);
     aa.o_hi = d->mhi;
     aa.o_lo = d->mlo;
-    STAGE(ATD_STAGE_ATTN, attention(d, aa, s));
+    // a prefill chunk's rows share one slot: one pass over key tiles per
+    // query tile; decode streams each read their own cache (split kernel)
+    if (fused)
+      STAGE(ATD_STAGE_ATTN, attention(d, aa, s));
+    else
+      STAGE(ATD_STAGE_ATTN, launch_attn_prefill(aa, kv_bf16, D, Hq / Hkv, s));
     STAGE(ATD_STAGE_OPROJ, mma_gemm(d, W.wo, W.wo, W.wo, h, h, h, nq, M, s));
     STAGE(ATD_STAGE_OPROJ, mma_residual(d, mma_splits(h, nq, M), M, x, (const float*)W.mlp_norm, s));
     STAGE(ATD_STAGE_GATEUP, mma_gemm(d, W.w_gate, W.w_up, W.w_up, F, 2 * F, 2 * F, h, M, s));

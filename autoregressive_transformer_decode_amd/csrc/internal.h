@@ -325,6 +325,9 @@ hipError_t launch_pack_transconv(const float* w, int cin, int cout, int s_, floa
                                  hipStream_t s);
 hipError_t launch_rope_append(const RopeArgs& a, int bf16, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream_t s);
+// Causal attention of a prefill chunk (rows in kRowsPrefill mode, non-fused,
+// k_direct set) in one pass over key tiles: writes o (or o_hi / o_lo).
+hipError_t launch_attn_prefill(const AttnArgs& a, int bf16, int D, int r, hipStream_t s);
 hipError_t launch_advance(const SlotTables& st, RowMap rows, int M, hipStream_t s);
 // RoPE rows of a call with rotary positions pos3 [M][3] (t, h, w): row m,
 // frequency i takes cos/sin of the position table at pos3[m][c(i)], c(i) = 1

@@ -2084,6 +2084,247 @@ void conv_launch(const ConvArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_conv1d<WM, WN, BK>), g, dim3(256), 0, s, a);
 }
 
+// ------------------------------------------------------------------ prefill attention
+// Causal attention of a prefill chunk's rows on the float32 matrix cores
+// (v_mfma_f32_16x16x4f32), flash style.  Workgroup = 16 query rows x HP query
+// heads of one KV head x KS key lanes: wave (head j, key lane kp) takes keys
+// kp*32 .. kp*32+31 of every staged tile of KS*32 keys, with its own running
+// max / sum / output; the KS partial states of a head are merged at the end.
+// Tiles are staged once in LDS (float32) for all waves, the next tile's loads
+// in flight while the current one is computed.  Per 32 keys a wave forms
+// S = Q K^T (16 x 32), masks keys past each row's position, updates the
+// running max / sum, writes P through LDS to reach the A layout and
+// accumulates O += P V.  The contraction order over channels (and over keys
+// in P V) is permuted so that a lane's operands of four successive MFMA
+// k-steps are four adjacent floats, read with one 16-byte LDS load: k-step
+// 4j + t of lane group lg takes index 16j + 4lg + t.
+template <typename KT, int D, int HP, int KS>
+__global__ __launch_bounds__(64 * HP * KS) void k_attn_prefill(AttnArgs a) {
+  constexpr int NW = HP * KS;          // waves
+  constexpr int NT = 64 * NW;          // threads
+  constexpr int KI = 32 * KS;          // keys staged per iteration
+  constexpr int DS = D + 4;            // LDS row stride (16-byte aligned)
+  constexpr int NB = D / 16;           // 16-column blocks of O
+  constexpr int VEC = Vec16<KT>::N;
+  constexpr int PER = KI * D / VEC / NT;   // 16-byte loads per thread per matrix
+  static_assert(PER * VEC * NT == KI * D, "tile does not divide over the threads");
+  __shared__ __align__(16) float Ks[KI * DS];
+  __shared__ __align__(16) float Vs[KI * DS];
+  __shared__ __align__(16) float Ps[NW][16 * 36];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int jh = wave % HP, kp = wave / HP;
+  const int R = a.Hq / a.Hkv, groups = R / HP;
+  const int g = blockIdx.y / groups;
+  const int h = g * R + (blockIdx.y % groups) * HP + jh;
+  const int m0 = (gridDim.x - 1 - blockIdx.x) * 16;   // longest key ranges first
+  const int p0 = a.rows.row0;                          // position of the launch's row 0
+  const int kmax = p0 + min(m0 + 16, a.M);             // keys the rows read
+  const KT* Kh = reinterpret_cast<const KT*>(a.k_direct) + (size_t)g * a.cap_direct * D;
+  const KT* Vh = reinterpret_cast<const KT*>(a.v_direct) + (size_t)g * a.cap_direct * D;
+
+  // queries as A operands (row m0 + li), pre-scaled by 1/sqrt(D)
+  float qf[D / 4];
+  {
+    const float* qp = a.q + ((size_t)min(m0 + li, a.M - 1) * a.Hq + h) * D;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(qp + 16 * j + 4 * lg);
+      qf[4 * j] = v.x * a.scale;
+      qf[4 * j + 1] = v.y * a.scale;
+      qf[4 * j + 2] = v.z * a.scale;
+      qf[4 * j + 3] = v.w * a.scale;
+    }
+  }
+  Floatx4 o[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) o[b] = Floatx4{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mrow[i] = -1e30f;
+    lrow[i] = 0.f;
+  }
+
+  // tile loads (key rows clamped into the valid range; the rows past kmax
+  // are masked below)
+  uint4 kr[PER], vr[PER];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = tid + e * NT;
+      const int r = idx / (D / VEC), c = (idx % (D / VEC)) * VEC;
+      const int key = min(k0 + r, kmax - 1);
+      kr[e] = ldg16(Kh + (size_t)key * D + c);
+      vr[e] = ldg16(Vh + (size_t)key * D + c);
+    }
+  };
+  const int nit = (kmax + KI - 1) / KI;
+  load_tile(0);
+  for (int it = 0; it < nit; ++it) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = tid + e * NT;
+      const int r = idx / (D / VEC), c = (idx % (D / VEC)) * VEC;
+      float kv[VEC], vv[VEC];
+      Vec16<KT>::unpack(kr[e], kv);
+      Vec16<KT>::unpack(vr[e], vv);
+#pragma unroll
+      for (int t = 0; t < VEC; t += 4) {
+        *reinterpret_cast<float4*>(&Ks[r * DS + c + t]) =
+            make_float4(kv[t], kv[t + 1], kv[t + 2], kv[t + 3]);
+        *reinterpret_cast<float4*>(&Vs[r * DS + c + t]) =
+            make_float4(vv[t], vv[t + 1], vv[t + 2], vv[t + 3]);
+      }
+    }
+    __syncthreads();
+    load_tile((it + 1) * KI);   // next tile in flight during the math
+    const int kb0 = it * KI + kp * 32;   // first key of this wave's 32
+    const float* Kw = Ks + kp * 32 * DS;
+    const float* Vw = Vs + kp * 32 * DS;
+    // S = Q K^T for two 16-key blocks
+    Floatx4 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sc[kb] = Floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float4 kf = *reinterpret_cast<const float4*>(Kw + (kb * 16 + li) * DS + 16 * j + 4 * lg);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * j], kf.x, sc[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * j + 1], kf.y, sc[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * j + 2], kf.z, sc[kb], 0, 0, 0);
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * j + 3], kf.w, sc[kb], 0, 0, 0);
+      }
+    }
+    // lane holds rows m0 + 4 lg + i, keys kb0 + 16 kb + li
+    float* Pw = Ps[wave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pos = p0 + m0 + 4 * lg + i;
+      float s0 = sc[0][i], s1 = sc[1][i];
+      if (kb0 + li > pos) s0 = -1e30f;
+      if (kb0 + 16 + li > pos) s1 = -1e30f;
+      float tm = fmaxf(s0, s1);
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) tm = fmaxf(tm, __shfl_xor(tm, off, 64));
+      const float mn = fmaxf(mrow[i], tm);
+      const float c = expf(mrow[i] - mn);
+      const float e0 = expf(s0 - mn), e1 = expf(s1 - mn);
+      float ts = e0 + e1;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) ts += __shfl_xor(ts, off, 64);
+      lrow[i] = lrow[i] * c + ts;
+      mrow[i] = mn;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b][i] *= c;
+      Pw[(4 * lg + i) * 36 + li] = e0;
+      Pw[(4 * lg + i) * 36 + 16 + li] = e1;
+    }
+    // P is read back by other lanes of the same wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O += P V
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float4 pa = *reinterpret_cast<const float4*>(Pw + li * 36 + 16 * j + 4 * lg);
+      const float* vrow = Vw + (16 * j + 4 * lg) * DS + li;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa.x, vrow[16 * b], o[b], 0, 0, 0);
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa.y, vrow[DS + 16 * b], o[b], 0, 0, 0);
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa.z, vrow[2 * DS + 16 * b], o[b], 0, 0, 0);
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa.w, vrow[3 * DS + 16 * b], o[b], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // the tile buffers are refilled next
+  }
+  // merge the key lanes of a head: lanes kp > 0 leave (max, sum, O) in LDS
+  // (the K buffer, free after the last barrier), key lane 0 combines
+  if (KS > 1) {
+    static_assert(KS == 1 || (KS - 1) * HP * 16 * (D + 2) <= KI * DS, "merge area");
+    if (kp > 0) {
+      float* mg = Ks + ((kp - 1) * HP + jh) * 16 * (D + 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lg + i;
+        if (li == 0) {
+          mg[r * (D + 2) + D] = mrow[i];
+          mg[r * (D + 2) + D + 1] = lrow[i];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) mg[r * (D + 2) + 16 * b + li] = o[b][i];
+      }
+    }
+    __syncthreads();
+    if (kp > 0) return;
+#pragma unroll
+    for (int q = 1; q < KS; ++q) {
+      const float* mg = Ks + ((q - 1) * HP + jh) * 16 * (D + 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lg + i;
+        const float m2 = mg[r * (D + 2) + D], l2 = mg[r * (D + 2) + D + 1];
+        const float mn = fmaxf(mrow[i], m2);
+        const float c1 = expf(mrow[i] - mn), c2 = expf(m2 - mn);
+        lrow[i] = lrow[i] * c1 + l2 * c2;
+        mrow[i] = mn;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) o[b][i] = o[b][i] * c1 + mg[r * (D + 2) + 16 * b + li] * c2;
+      }
+    }
+  }
+  // rows m0 + 4 lg + i, channels 16 b + li
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 4 * lg + i;
+    if (m >= a.M) continue;
+    const float inv = 1.0f / lrow[i];
+    const size_t off = ((size_t)m * a.Hq + h) * D;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float v = o[b][i] * inv;
+      if (a.o_hi) {
+        uint16_t hv, lv;
+        split_hi_lo(v, hv, lv);
+        a.o_hi[off + 16 * b + li] = hv;
+        a.o_lo[off + 16 * b + li] = lv;
+      } else {
+        a.o[off + 16 * b + li] = v;
+      }
+    }
+  }
+}
+
+// heads per workgroup and key lanes by group size: 1 -> 1 x 2 (two waves),
+// 2 -> 2 x 2, 4 and 8 -> 4 x 1 (8: two workgroups per KV head)
+template <typename KT, int D>
+static void attn_prefill_r(const AttnArgs& a, int r, hipStream_t s) {
+  const int hp = r < 4 ? r : 4;
+  const dim3 grid((a.M + 15) / 16, a.Hkv * (r / hp));
+  if (r == 1)
+    hipLaunchKernelGGL((k_attn_prefill<KT, D, 1, 2>), grid, dim3(128), 0, s, a);
+  else if (r == 2)
+    hipLaunchKernelGGL((k_attn_prefill<KT, D, 2, 2>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_prefill<KT, D, 4, 1>), grid, dim3(256), 0, s, a);
+}
+
+hipError_t launch_attn_prefill(const AttnArgs& a, int bf16, int D, int r, hipStream_t s) {
+  if (a.fused || a.rows.mode != kRowsPrefill || !a.k_direct || a.M < 1 ||
+      (r != 1 && r != 2 && r != 4 && r != 8) || a.Hq != a.Hkv * r)
+    return hipErrorInvalidValue;
+  if (bf16) {
+    if (D == 64) attn_prefill_r<uint16_t, 64>(a, r, s);
+    else attn_prefill_r<uint16_t, 128>(a, r, s);
+  } else {
+    if (D == 64) attn_prefill_r<float, 64>(a, r, s);
+    else attn_prefill_r<float, 128>(a, r, s);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int wtype, hipStream_t s) {
   switch (wtype) {
     case kWBF16: gemv_dispatch<uint16_t>(a, epi, norm, s); break;

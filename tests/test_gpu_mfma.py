@@ -40,6 +40,32 @@ def test_prefill_chunks(T):
     _log(f"prefill T={T}: {chk.n} checks, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
 
 
+PREFILL_ATTN = [
+    # name, L, h, Hq, Hkv, D, F, V, dtype, qk_norm, bias, kv dtype, T
+    ("r1_d64_kvf32", 2, 256, 4, 4, 64, 512, 600, "bf16", False, True, "f32", 97),
+    ("r2_d64_kvbf16", 2, 256, 4, 2, 64, 512, 600, "bf16", True, False, "bf16", 130),
+    ("r2_d128_kvf32", 2, 256, 4, 2, 128, 512, 600, "bf16", True, False, "f32", 300),
+    ("r4_d64_kvf32", 2, 256, 8, 2, 64, 512, 600, "bf16", True, True, "f32", 45),
+    ("r8_d128_kvf32", 2, 256, 8, 1, 128, 512, 600, "bf16", True, True, "f32", 70),
+    ("r8_d128_kvbf16", 2, 256, 8, 1, 128, 512, 600, "bf16", False, False, "bf16", 17),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_ATTN, ids=[c[0] for c in PREFILL_ATTN])
+def test_prefill_attention_group_sizes(case):
+    """Prefill chunks' causal attention (16 query rows x a KV head's query
+    heads per workgroup, key tiles split over waves and merged) for every
+    GQA group size, both head dims and both cache dtypes, T ragged against
+    the 16-row and 64-key tiles; later layers and the teacher-forced steps
+    read every prefill row's keys."""
+    name, L, h, hq, hkv, D, F, V, dt, qk, bias, kvdt, T = case
+    shape = small_shape(name, L, h, hq, hkv, D, F, V, dt, qk, bias, kv_dtype=kvdt)
+    mw = inputs.make_weights(shape, seed=17)
+    X0 = inputs.normal(17, 2, 13, (T, h), scale=1.0)
+    chk, ref, _ = lm_parity(mw, X0, 4, 512)
+    _log(f"prefill attention {name} T={T}: {chk.n} checks, worst {chk.worst:.2e}")
+
+
 def test_prefill_mfma_equals_vector_path():
     """The same prefill through both paths agrees to the tolerance (and
     both agree with the oracle)."""

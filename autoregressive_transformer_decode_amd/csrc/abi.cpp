@@ -473,7 +473,13 @@ hipError_t mma_gemm(atd_decoder* d, const void* w0, const void* w1, const void* 
   g.ks = mma_ks(N, K, tiles);
   g.mrows = tiles * kMmaRows;
   g.part = d->mpart;
-  return launch_gemm(g, s);
+  // several row tiles (prefill chunks): 128 x 128 output tiles share each
+  // operand tile over more MFMAs, when they still give every compute unit a
+  // workgroup (measured at 512 rows of the 1.7B shape: gate/up 92 -> 65 us,
+  // QKV 33 -> 26, down 49 -> 46; the O projection's 128 workgroups: 18 -> 24,
+  // so it stays on 64 x 64 tiles); one tile (decode streams) streams weights
+  const long big = (long)((N + 127) / 128) * g.ks * ((g.mrows + 127) / 128);
+  return tiles > 1 && big >= kMmaCUs ? launch_gemm_tile(g, s) : launch_gemm(g, s);
 }
 
 // Splits of the GEMM of an [N, K] weight over M rows (as mma_gemm takes them).

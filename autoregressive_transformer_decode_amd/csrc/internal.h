@@ -349,6 +349,9 @@ hipError_t launch_record_tokens(const int32_t* src, int n, int32_t* out, int32_t
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// The same product over 128 x 128 output tiles (calls of more than one row
+// tile: prefill chunks); same arguments and partials layout.
+hipError_t launch_gemm_tile(const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, int epi, hipStream_t s);
 
 }  // namespace atd

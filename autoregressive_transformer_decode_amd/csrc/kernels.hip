@@ -1751,6 +1751,146 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   }
 }
 
+// Split-K GEMM of a prefill chunk over 128 x 128 output tiles: part[split,
+// m, n] = sum over the split's K range of (hi + lo)[m, k] * W[n, k] (bf16 MFMA
+// 16x16x32, float32 accumulation), as k_gemm, for calls of more than one
+// 64-row tile.  Workgroup (128 rows x 128 weight rows, split): wave (wm, wn)
+// owns rows wm*64.. and weight rows wn*64.. (4 x 4 MFMA tiles).  Both operand
+// tiles (activation hi and lo, weights) pass through a double-buffered LDS
+// tile in 32-wide stages, the next stage's loads in registers during the
+// math; a stage costs a wave 12 fragment reads for 32 MFMAs, where the
+// 64 x 64 tile of k_gemm pays one per MFMA and re-reads each activation tile
+// for every 64 weight rows.  The linear workgroup id is remapped so that each
+// XCD (workgroups go round-robin over the 8, each with its own L2) walks one
+// contiguous range of (row tile fastest, then split, then weight tile).
+template <int NST>
+__global__ __launch_bounds__(256) void k_gemm_tile(GemmArgs a) {
+  constexpr int BM = 128, BN = 128, BK = 32;
+  // NST > 0: every workgroup walks NST stages, fully unrolled, through a
+  // P-deep register ring (loads of P stages in flight; stages past the split
+  // end read in-bounds data and are zeroed at the LDS write); NST = 0: a
+  // stage loop with one stage in flight
+  constexpr int P = NST == 0 ? 1 : (NST < 4 ? NST : 4);
+  // [buf][act hi, act lo, weights][row][4 chunks of 16 bytes]; chunk c of row
+  // r sits at c ^ ((r >> 1) & 3), so a fragment read (16 rows, 4 chunks)
+  // spreads over the banks
+  __shared__ uint4 sm[2][3][BM][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nrt = (a.mrows + BM - 1) / BM;
+  int rt, split, wt;
+  {
+    int b = blockIdx.x;
+    const int t8 = gridDim.x & ~7;
+    if (b < t8) b = (b & 7) * (t8 >> 3) + (b >> 3);
+    rt = b % nrt;
+    b /= nrt;
+    split = b % a.ks;
+    wt = b / a.ks;
+  }
+  const int K = a.K;
+  const int kb = split * a.kc, ke = min(K, kb + a.kc);
+  const int nst = NST > 0 ? NST : (ke - kb) / BK;   // K and split ends: multiples of 32
+
+  // staging: thread -> rows sr and sr + 64 of each operand tile, chunk sc;
+  // rows past the call's rows (or past N) read an in-bounds row whose
+  // results are not stored
+  const int sr = tid >> 2, sc = tid & 3;
+  const int sw = sc ^ ((sr >> 1) & 3);
+  const int m0 = min(rt * BM + sr, a.mrows - 1), m1 = min(rt * BM + sr + 64, a.mrows - 1);
+  const uint16_t* h0 = a.hi + (size_t)m0 * K + sc * 8;
+  const uint16_t* h1 = a.hi + (size_t)m1 * K + sc * 8;
+  const uint16_t* l0 = a.lo + (size_t)m0 * K + sc * 8;
+  const uint16_t* l1 = a.lo + (size_t)m1 * K + sc * 8;
+  auto wrow = [&](int n) {
+    const int sg = n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
+    const int sb = sg == 0 ? 0 : (sg == 1 ? a.seg_end[0] : a.seg_end[1]);
+    return reinterpret_cast<const uint16_t*>(pick3(a.W, sg)) + (size_t)(n < a.N ? n - sb : 0) * K +
+           sc * 8;
+  };
+  const uint16_t* w0 = wrow(wt * BN + sr);
+  const uint16_t* w1 = wrow(wt * BN + sr + 64);
+
+  uint4 ra[P][4], rb[P][2];
+  auto issue = [&](int p, int c) {
+    const int k = min(kb + c * BK, K - BK);
+    ra[p][0] = ldg16(h0 + k);
+    ra[p][1] = ldg16(h1 + k);
+    ra[p][2] = ldg16(l0 + k);
+    ra[p][3] = ldg16(l1 + k);
+    rb[p][0] = ldg16(w0 + k);
+    rb[p][1] = ldg16(w1 + k);
+  };
+  Floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = Floatx4{0.f, 0.f, 0.f, 0.f};
+  const int pos = lg ^ ((li >> 1) & 3);
+  // ring slot p to LDS buffer buf; activations of stages past the split end
+  // are zeroed (a mask, not a select of the ring)
+  auto put = [&](int p, int buf, int c) {
+    const uint32_t mk = 0u - (uint32_t)(kb + c * BK < ke);
+    auto keep = [mk](uint4 v) { return make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk); };
+    sm[buf][0][sr][sw] = keep(ra[p][0]);
+    sm[buf][0][sr + 64][sw] = keep(ra[p][1]);
+    sm[buf][1][sr][sw] = keep(ra[p][2]);
+    sm[buf][1][sr + 64][sw] = keep(ra[p][3]);
+    sm[buf][2][sr][sw] = rb[p][0];
+    sm[buf][2][sr + 64][sw] = rb[p][1];
+  };
+  auto mma = [&](int buf) {
+    Bf16x8 bw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bw[j] = as_bf16x8(sm[buf][2][wn * 64 + j * 16 + li][pos]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Bf16x8 ah = as_bf16x8(sm[buf][0][wm * 64 + i * 16 + li][pos]);
+      const Bf16x8 al = as_bf16x8(sm[buf][1][wm * 64 + i * 16 + li][pos]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  if constexpr (NST > 0) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue(p, p);
+#pragma unroll
+    for (int c = 0; c < NST; ++c) {
+      const int p = c % P, buf = c & 1;
+      put(p, buf, c);
+      __syncthreads();
+      if (c + P < NST) issue(p, c + P);
+      mma(buf);
+    }
+  } else {
+    issue(0, 0);
+    for (int c = 0; c < nst; ++c) {
+      const int buf = c & 1;
+      put(0, buf, c);
+      __syncthreads();
+      issue(0, min(c + 1, nst - 1));   // the last stage re-reads itself (unused)
+      mma(buf);
+    }
+  }
+  // C layout: column li (weight row), rows 4 lg + r (activation rows)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = wt * BN + wn * 64 + j * 16 + li;
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = rt * BM + wm * 64 + i * 16 + 4 * lg + r;
+        if (m < a.mrows) a.part[((size_t)split * a.mrows + m) * a.N + n] = acc[i][j][r];
+      }
+  }
+}
+
 // out = epi(sum over splits, in order); one thread per (row, column).
 template <int EPI>
 __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
@@ -2521,6 +2661,26 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     case 12: hipLaunchKernelGGL((k_gemm<2, 12>), grid, dim3(256), 0, s, a); break;
     case 16: hipLaunchKernelGGL((k_gemm<2, 16>), grid, dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL((k_gemm<2, 0>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
+  if (a.mrows < kMmaRows || a.mrows % kMmaRows || a.K % 32 || a.kc % 32 || a.ks < 1 ||
+      (long)a.kc * (a.ks - 1) >= a.K)
+    return hipErrorInvalidValue;
+  const dim3 grid((a.N + 127) / 128 * a.ks * ((a.mrows + 127) / 128));
+  // 32-wide stages of a split (the last split may hold fewer real ones)
+  switch (a.kc / 32) {
+    case 2: hipLaunchKernelGGL(k_gemm_tile<2>, grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(k_gemm_tile<4>, grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL(k_gemm_tile<6>, grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(k_gemm_tile<8>, grid, dim3(256), 0, s, a); break;
+    case 12: hipLaunchKernelGGL(k_gemm_tile<12>, grid, dim3(256), 0, s, a); break;
+    case 16: hipLaunchKernelGGL(k_gemm_tile<16>, grid, dim3(256), 0, s, a); break;
+    case 24: hipLaunchKernelGGL(k_gemm_tile<24>, grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL(k_gemm_tile<32>, grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(k_gemm_tile<0>, grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }

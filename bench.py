@@ -347,7 +347,8 @@ def bench_lm(args, wl):
                      mfma_peak_tflops=2500.0,
                      note="bf16 MFMA with float32 activations as bf16 hi + lo operands (two "
                           "products per weight); rows layer by layer in chunks of up to 512, "
-                          "GEMMs over 64-row tiles, causal flash attention on the float32 "
+                          "GEMMs over 128 x 128 output tiles (64-row tiles where those leave "
+                          "compute units idle), causal flash attention on the float32 "
                           "matrix cores"),
     )
     dec.close()

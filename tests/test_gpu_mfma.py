@@ -66,6 +66,33 @@ def test_prefill_attention_group_sizes(case):
     _log(f"prefill attention {name} T={T}: {chk.n} checks, worst {chk.worst:.2e}")
 
 
+TILE_GEMM = [
+    # name, L, h, Hq, Hkv, D, F, V, dtype, qk_norm, bias, T
+    # 450 rows (4 row tiles of 128, the last one ragged): QKV, O, gate/up and
+    # down take the 128 x 128 tiles; N = 1248 ragged against them; QKV and
+    # down end in a short split; 20 / 10-stage splits take the stage loop,
+    # O's 8-stage splits the unrolled ring
+    ("tiles_ragged", 2, 1248, 16, 8, 128, 2496, 3001, "bf16", True, True, 450),
+    # 200 rows: gate/up on the 128 x 128 tiles in 5 splits of 4 unrolled
+    # stages, the last split holding one real stage (three zeroed)
+    ("tiles_short_split", 2, 544, 8, 2, 128, 1792, 1000, "bf16", True, False, 200),
+]
+
+
+@pytest.mark.parametrize("case", TILE_GEMM, ids=[c[0] for c in TILE_GEMM])
+def test_prefill_tile_gemm(case):
+    """Prefill chunks whose GEMMs give every compute unit a 128 x 128-tile
+    workgroup run on those tiles (the host's split rule decides per GEMM);
+    shapes chosen so the tiles meet ragged N, rows past the call, short
+    final splits and both the unrolled and the looped stage walk."""
+    name, L, h, hq, hkv, D, F, V, dt, qk, bias, T = case
+    shape = small_shape(name, L, h, hq, hkv, D, F, V, dt, qk, bias)
+    mw = inputs.make_weights(shape, seed=19)
+    X0 = inputs.normal(19, 2, 17, (T, h), scale=1.0)
+    chk, ref, _ = lm_parity(mw, X0, 3, 512)
+    _log(f"tile GEMM {name} T={T}: {chk.n} checks, worst {chk.worst:.2e}")
+
+
 def test_prefill_mfma_equals_vector_path():
     """The same prefill through both paths agrees to the tolerance (and
     both agree with the oracle)."""

@@ -1007,12 +1007,13 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
 // One block per (head, row).  The split weights are formed once in LDS;
 // thread t accumulates the float4 channel group t % (D/4) over splits
 // t / (D/4), t / (D/4) + NSP, ... (independent loads), and the NSP partial
-// sums are added in a fixed order.
-template <int D>
+// sums are added in a fixed order.  PRE partials per thread are loaded
+// together with the position and statistics (all of a row's partials when
+// PRE * NSP covers its splits: one memory round trip instead of several).
+template <int D, int PRE>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   constexpr int NC = D / 4;        // float4 channel groups
   constexpr int NSP = 256 / NC;    // split phases
-  constexpr int PRE = 4;           // partials per thread loaded ahead of the position
   __shared__ float wgt[kAttnSplitsMax + 1];
   __shared__ float red[2][4];
   __shared__ float4 part[NSP][NC];
@@ -1021,14 +1022,14 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   const int c = tid % NC, sp = tid / NC;
   const float4* pa = reinterpret_cast<const float4*>(a.pacc) + base * NC + c;
   // the first partials and statistics are read together with the position
+  // (branch-free: indexes past the split stride re-read its last slot; only
+  // splits below the row's count are used)
   float4 pre[PRE];
+  const int slast = a.nsplit_max - 1;
 #pragma unroll
-  for (int i = 0; i < PRE; ++i) {
-    const int s = sp + i * NSP;
-    pre[i] = s < a.nsplit_max ? pa[(size_t)s * NC] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float m0 = tid < a.nsplit_max ? a.pml[(base + tid) * 2] : -1e30f;
-  const float l0 = tid < a.nsplit_max ? a.pml[(base + tid) * 2 + 1] : 0.f;
+  for (int i = 0; i < PRE; ++i) pre[i] = pa[(size_t)min(sp + i * NSP, slast) * NC];
+  const float m0 = a.pml[(base + min(tid, slast)) * 2];
+  const float l0 = a.pml[(base + min(tid, slast)) * 2 + 1];
   int slot, pos;
   row_of(a.rows, a.st, m, slot, pos);
   const int len = pos + 1;
@@ -2552,10 +2553,15 @@ hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream
   }
   if (a.nsplit_max == 1) return hipGetLastError();   // the split kernel wrote o
   dim3 cgrid(a.Hq, a.M);
-  if (D == 64)
-    hipLaunchKernelGGL(k_attn_combine<64>, cgrid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, s, a);
+  // all partials up front when 4 per thread do not cover the split stride
+  const bool deep = a.nsplit_max > 4 * (256 / (D / 4));
+  if (D == 64) {
+    if (deep) hipLaunchKernelGGL((k_attn_combine<64, 16>), cgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_combine<64, 4>), cgrid, dim3(256), 0, s, a);
+  } else {
+    if (deep) hipLaunchKernelGGL((k_attn_combine<128, 16>), cgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_combine<128, 4>), cgrid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

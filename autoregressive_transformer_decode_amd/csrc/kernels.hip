@@ -1758,8 +1758,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 // 64-row tile.  Workgroup (128 rows x 128 weight rows, split): wave (wm, wn)
 // owns rows wm*64.. and weight rows wn*64.. (4 x 4 MFMA tiles).  Both operand
 // tiles (activation hi and lo, weights) pass through a double-buffered LDS
-// tile in 32-wide stages, the next stage's loads in registers during the
-// math; a stage costs a wave 12 fragment reads for 32 MFMAs, where the
+// tile in 32-wide stages, the loads of the next stages (up to four) in a
+// register ring during the math; a stage costs a wave 12 fragment reads for
+// 32 MFMAs, where the
 // 64 x 64 tile of k_gemm pays one per MFMA and re-reads each activation tile
 // for every 64 weight rows.  The linear workgroup id is remapped so that each
 // XCD (workgroups go round-robin over the 8, each with its own L2) walks one
@@ -2236,9 +2237,10 @@ void conv_launch(const ConvArgs& a, hipStream_t s) {
 // S = Q K^T (16 x 32), masks keys past each row's position, updates the
 // running max / sum, writes P through LDS to reach the A layout and
 // accumulates O += P V.  The contraction order over channels (and over keys
-// in P V) is permuted so that a lane's operands of four successive MFMA
-// k-steps are four adjacent floats, read with one 16-byte LDS load: k-step
-// 4j + t of lane group lg takes index 16j + 4lg + t.
+// in P V) is permuted so that a lane's Q, K and P operands of four
+// successive MFMA k-steps are four adjacent floats, read with one 16-byte LDS
+// load (V, the B operand of P V, is read per k-step): k-step 4j + t of lane
+// group lg takes index 16j + 4lg + t.
 template <typename KT, int D, int HP, int KS>
 __global__ __launch_bounds__(64 * HP * KS) void k_attn_prefill(AttnArgs a) {
   constexpr int NW = HP * KS;          // waves

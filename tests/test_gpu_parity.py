@@ -57,6 +57,19 @@ def test_ragged_shapes_buckets_and_splits(case):
     _log(f"{name}: {chk.n} steps, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
 
 
+def test_long_context_many_splits():
+    """One KV head (D = 128) at batch 1 after a 3000-row prefill: a step
+    splits the row into up to 188 pieces per head, so the attention combine
+    takes its 16 up-front partials per thread and walks the rest; the
+    prefill runs in 512-row chunks whose attention reads keys up to 3000
+    rows back."""
+    shape = small_shape("long", 2, 256, 8, 1, 128, 512, 700, "bf16", True, False)
+    mw = inputs.make_weights(shape, seed=23)
+    X0 = inputs.normal(23, 2, 19, (3000, shape.hidden), scale=1.0)
+    chk, ref, _ = lm_parity(mw, X0, 4, 4096)
+    _log(f"long context: {chk.n} checks, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
+
+
 def test_multi_stream_steps():
     """B = 5 streams with different prefill lengths stepped together (rows
     map to slots 0..4, each at its own position); every stream equals its

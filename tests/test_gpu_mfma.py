@@ -93,6 +93,40 @@ def test_prefill_tile_gemm(case):
     _log(f"tile GEMM {name} T={T}: {chk.n} checks, worst {chk.worst:.2e}")
 
 
+@pytest.mark.parametrize("T", [200, 700])
+def test_prefill_every_row_keys(T):
+    """Every prefill row, not only the last: the last layer's K and V rows at
+    all T positions (each one depends on the earlier layers' attention
+    output of its own row, so on the causal attention over the rows before
+    it) match the oracle's cache, row by row, to the bar; T = 700 spans a
+    512-row chunk and a second one that reads its keys."""
+    shape = small_shape("rows", 3, 256, 8, 2, 128, 512, 600, "bf16", True, False, kv_dtype="f32")
+    mw = inputs.make_weights(shape, seed=29)
+    X0 = inputs.normal(29, 2, 23, (T, shape.hidden), scale=1.0)
+    om = oracle_from_weights(mw)
+    cache = od.Cache(om, 1024)
+    od.prefill(om, cache, X0, 0)
+    dm = dv.DeviceModel(mw)
+    dec = dv.Decoder(dm, max_slots=1, max_rows=T, max_ctx=1024)
+    dec.grow(0, 1024)
+    y = torch.empty(shape.hidden, device="cuda")
+    z = torch.empty(shape.vocab, device="cuda")
+    dec.prefill(torch.from_numpy(np.asarray(X0, np.float32)).cuda(), y_out=y, logits_out=z)
+    torch.cuda.synchronize()
+    ks, vs = dec.kv[0]
+    last = shape.n_layers - 1
+    Kg = ks[last].float().cpu().numpy()[:, :T]
+    Vg = vs[last].float().cpu().numpy()[:, :T]
+    dec.close()
+    worst = 0.0
+    for t in range(T):
+        e = max(normwise_rel(Kg[:, t], cache.K[last][:, t]),
+                normwise_rel(Vg[:, t], cache.V[last][:, t]))
+        worst = max(worst, e)
+        assert e <= TOL, f"row {t}: normwise error {e:.3e} > {TOL}"
+    _log(f"prefill T={T}: every row's last-layer K/V, worst {worst:.2e}")
+
+
 def test_prefill_mfma_equals_vector_path():
     """The same prefill through both paths agrees to the tolerance (and
     both agree with the oracle)."""

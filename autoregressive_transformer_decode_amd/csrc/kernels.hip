@@ -282,63 +282,61 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
 // then Hkv key heads, then Hkv value heads.  q and k heads get the optional
 // per-head RMSNorm over D and rotate-half RoPE at the row's position; q goes
 // to q_out, k and v are stored (rounded for a bf16 cache) into the cache row.
-// Called by every thread of a block of >= D threads (uniform barriers);
-// threads t < D own one channel each.
-template <typename KT>
-__device__ __forceinline__ void rope_head(const RopeArgs& a, int m, int hh, float* buf,
-                                          float* red) {
-  const int t = threadIdx.x, D = a.D, half = D >> 1;
+// All (row, head slot) items of a call: G = 64 / (D/2)
+// items per wave, lane l of an item holding channels l and l + D/2 (the
+// rotate-half pair, so the rotation needs no exchange); the QK-norm's sum of
+// squares is a shuffle reduction over the item's lanes.  One wave per item
+// (two at D = 64), no LDS or barriers (a prefill chunk has M x (Hq + 2 Hkv)
+// items; at 512 rows of the 1.7B shape this form takes 6-7 us per layer,
+// one 128-thread block per item with LDS reductions took 11 us).
+template <typename KT, int D>
+__global__ __launch_bounds__(256) void k_rope_append(RopeArgs a) {
+  constexpr int half = D / 2, G = 64 / half;
+  const int lane = threadIdx.x & 63, sub = lane / half, l = lane % half;
+  const int nh = a.Hq + 2 * a.Hkv;
+  const int item = (blockIdx.x * 4 + (threadIdx.x >> 6)) * G + sub;
+  if (item >= a.M * nh) return;   // whole items only: the reduction stays within one
+  const int m = item / nh, hh = item % nh;
   int slot, pos;
   row_of(a.rows, a.st, m, slot, pos);
-  const int ld = (a.Hq + 2 * a.Hkv) * D;
+  const int ld = nh * D;
   const int kind = hh < a.Hq ? 0 : (hh < a.Hq + a.Hkv ? 1 : 2);
   const int hd = kind == 0 ? hh : (kind == 1 ? hh - a.Hq : hh - a.Hq - a.Hkv);
   const int col = (kind == 0 ? 0 : (kind == 1 ? a.Hq * D : (a.Hq + a.Hkv) * D)) + hd * D;
-  const bool own = t < D;
-  float v = own ? a.qkv[(size_t)m * ld + col + t] : 0.f;
-  if (kind < 2 && a.qk_norm) {
-    const float s2 = wave_sum(v * v);
-    if ((t & 63) == 0) red[t >> 6] = s2;
-    __syncthreads();
-    float tot = 0.f;
-    for (int w = 0; w < D / 64; ++w) tot += red[w];
-    const float inv = 1.0f / sqrtf(tot / (float)D + a.eps);
-    if (own) v = v * inv * (kind == 0 ? a.q_norm[t] : a.k_norm[t]);
-    __syncthreads();
-  }
+  const float* src = a.qkv + (size_t)m * ld + col;
+  float v0 = src[l], v1 = src[l + half];
   if (kind < 2) {
-    if (own) buf[t] = v;
-    __syncthreads();
-    if (own) {
-      const int i = t < half ? t : t - half;
-      const size_t rr = (size_t)(a.rows.rope_rows ? a.rows.row0 + m : pos) * half;
-      const float c = a.cos_t[rr + i];
-      const float sn = a.sin_t[rr + i];
-      const float x0 = buf[i], x1 = buf[i + half];
-      v = t < half ? x0 * c - x1 * sn : x1 * c + x0 * sn;
+    if (a.qk_norm) {
+      float s2 = v0 * v0 + v1 * v1;
+#pragma unroll
+      for (int off = 1; off < half; off <<= 1) s2 += __shfl_xor(s2, off, 64);
+      const float inv = 1.0f / sqrtf(s2 / (float)D + a.eps);
+      const float* g = kind == 0 ? a.q_norm : a.k_norm;
+      v0 = v0 * inv * g[l];
+      v1 = v1 * inv * g[l + half];
     }
-    __syncthreads();
+    const size_t rr = (size_t)(a.rows.rope_rows ? a.rows.row0 + m : pos) * half;
+    const float c = a.cos_t[rr + l], sn = a.sin_t[rr + l];
+    const float x0 = v0, x1 = v1;
+    v0 = x0 * c - x1 * sn;
+    v1 = x1 * c + x0 * sn;
   }
-  if (!own) return;
   if (kind == 0) {
-    a.q_out[((size_t)m * a.Hq + hd) * D + t] = v;
+    float* q = a.q_out + ((size_t)m * a.Hq + hd) * D;
+    q[l] = v0;
+    q[l + half] = v1;
   } else {
     void* const* kv = a.st.kv + ((size_t)slot * a.st.L + a.layer) * 2;
     const int cap = a.st.cap[slot];
-    KT* dst = reinterpret_cast<KT*>(kv[kind - 1]) + ((size_t)hd * cap + pos) * D + t;
-    if constexpr (sizeof(KT) == 2)
-      *dst = f32_to_bf16(v);
-    else
-      *dst = v;
+    KT* dst = reinterpret_cast<KT*>(kv[kind - 1]) + ((size_t)hd * cap + pos) * D;
+    if constexpr (sizeof(KT) == 2) {
+      dst[l] = f32_to_bf16(v0);
+      dst[l + half] = f32_to_bf16(v1);
+    } else {
+      dst[l] = v0;
+      dst[l + half] = v1;
+    }
   }
-}
-
-// Standalone form: one block of D threads per (row, head slot).
-template <typename KT>
-__global__ __launch_bounds__(128) void k_rope_append(RopeArgs a) {
-  __shared__ float buf[128];
-  __shared__ float red[2];
-  rope_head<KT>(a, blockIdx.y, blockIdx.x, buf, red);
 }
 
 // ------------------------------------------------------------------ GEMV
@@ -2519,11 +2517,17 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_rope_append(const RopeArgs& a, int bf16, hipStream_t s) {
-  dim3 grid(a.Hq + 2 * a.Hkv, a.M);
-  if (bf16)
-    hipLaunchKernelGGL(k_rope_append<uint16_t>, grid, dim3(a.D), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_rope_append<float>, grid, dim3(a.D), 0, s, a);
+  if ((a.D != 64 && a.D != 128) || a.M < 1) return hipErrorInvalidValue;
+  const long items = (long)a.M * (a.Hq + 2 * a.Hkv);
+  const int per_block = 4 * (128 / a.D);   // waves x items per wave
+  const dim3 grid((unsigned)((items + per_block - 1) / per_block));
+  if (a.D == 64) {
+    if (bf16) hipLaunchKernelGGL((k_rope_append<uint16_t, 64>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_rope_append<float, 64>), grid, dim3(256), 0, s, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL((k_rope_append<uint16_t, 128>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_rope_append<float, 128>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

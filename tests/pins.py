@@ -416,6 +416,141 @@ def check_frame_input():
     _close(x, exp, 0)
 
 
+# ---------------------------------------------------------------- loops
+
+def _greedy_f32(z, seen, rho):
+    """Penalised greedy choice written as a scalar float32 loop (independent of
+    penalized_argmax): a seen token's logit is divided by rho when positive and
+    multiplied by it otherwise; the lowest index of the maximum wins.  Returns
+    (token, margin to the runner-up)."""
+    r = np.float32(rho)
+    vals = []
+    for i, v in enumerate(np.asarray(z, np.float64)):
+        v = np.float32(v)
+        if seen is not None and i in seen:
+            v = np.float32(v / r) if v > 0 else np.float32(v * r)
+        vals.append(v)
+    tok = 0
+    for i in range(1, len(vals)):
+        if vals[i] > vals[tok]:
+            tok = i
+    second = max(v for i, v in enumerate(vals) if i != tok)
+    return tok, float(vals[tok] - second)
+
+
+def check_run_lm_brute():
+    """The plain LM loop against a from-scratch recompute (RKNN page:
+    stepwise decode equals full recompute; Audio8-ASR report: growth when the
+    write position reaches the bucket).  The prefill's last row gives token 1,
+    step k feeds the embedding of token k (the previous choice), and every
+    step's (y, z) equals the float64 brute force over all rows fed so far.
+    The bucket starts at 4 and doubles right before a row lands on the
+    capacity: 4 -> 8 before writing row 4, 8 -> 16 before row 8."""
+    m = _brute_model(False)
+    rng = np.random.default_rng(24)
+    X0 = rng.standard_normal((3, 12))
+    caps = []
+    out, cache = od.run_lm(m, X0, 7, 4,
+                           on_step=lambda k, c: caps.append((k, c.pos, c.capacity)))
+    assert len(out) == 8, len(out)
+    rows = list(X0)
+    for k in range(8):
+        yb, zb = brute.last_outputs(m, rows)
+        _close(out[k][0], yb, 1e-9)
+        _close(out[k][1], zb, 1e-9)
+        tok, margin = _greedy_f32(zb, None, 1.0)
+        assert margin > 1e-4, "fixture has a near tie"
+        assert out[k][2] == tok, (k, out[k][2], tok)
+        rows.append(m.tables[0][tok])
+    assert caps == [(0, 3, 4), (1, 4, 4), (2, 5, 8), (3, 6, 8), (4, 7, 8), (5, 8, 8),
+                    (6, 9, 16), (7, 10, 16)], caps
+
+
+def check_run_lm_asr_stress_golden():
+    """The Audio8-ASR report's 256->512 migration stress run through run_lm: an
+    85-row prefill and 180 decoder steps give 181 tokens (the prefill's
+    included); the bucket starts at 128 and migrates twice, to 256 in the step
+    that writes row 128 (step 44) and to 512 in the step that writes row 256
+    (step 172), ending at 512."""
+    rows = {r[0]: r[1:] for r in read_golden("asr_bucket_runs.txt")}
+    pre, toks, final, migr = (int(v) for v in rows["stress"])
+    m = tiny_model(L=1, h=8, hq=2, hkv=1, D=4, F=8, V=16, tables=(16,), bias=True,
+                   qk_norm=False, seed=71)
+    X0 = np.random.default_rng(72).standard_normal((pre, 8))
+    caps = []
+    out, cache = od.run_lm(m, X0, toks - 1, 128,
+                           on_step=lambda k, c: caps.append(c.capacity))
+    assert len(out) == toks, len(out)
+    moves = [k for k in range(1, len(caps)) if caps[k] != caps[k - 1]]
+    assert (cache.capacity, len(moves)) == (final, migr), (cache.capacity, moves)
+    assert moves == [128 - pre + 1, 256 - pre + 1], moves
+    assert cache.pos == pre + toks - 1
+
+
+def _talker_pair(seed):
+    """A 1-layer Talker (6 main codes, 16 code tables) and a 1-layer Code
+    Predictor (15 heads of 5 codes) sharing the code tables, as the 0.6B
+    Talker and its Code Predictor do."""
+    tk = tiny_model(L=1, h=16, hq=2, hkv=1, D=4, F=8, V=6, n_heads=1,
+                    tables=(6,) + (5,) * 15, bias=False, seed=seed, scale=0.6)
+    cp = tiny_model(L=1, h=16, hq=2, hkv=1, D=4, F=8, V=5, n_heads=15,
+                    tables=(6,) + (5,) * 14, bias=False, seed=seed + 1, scale=0.6)
+    cp.tables = tk.tables[:15]
+    return tk, cp
+
+
+def check_run_talker_brute(rho=4.0):
+    """The two-level frame loop against a from-scratch recompute ("Qwen3-TTS
+    ncnn port", Talker section).  The Talker's prefill gives frame 0's main
+    code c0 (penalty over an empty seen set).  Frame f: the Code Predictor
+    recomputes from rows [y_f, E_tk[c0_f]]; head j's greedy code is c_{j+1}
+    and its table-j embedding is the next row.  The next Talker row is the sum
+    of the frame's 16 code embeddings (table g holds group g) plus text row
+    f + 1, and the next c0 is the penalised greedy choice over the c0 codes
+    chosen so far.  rho = 4 makes the seen set decide choices: the same run
+    with rho = 1 picks different main codes."""
+    tk, cp = _talker_pair(81)
+    rng = np.random.default_rng(82)
+    X0 = rng.standard_normal((3, 16))
+    n_frames = 4
+    text = rng.standard_normal((n_frames, 16))
+    frames, _ = od.run_talker(tk, cp, X0, text, n_frames, 8, rho=rho, cp_capacity=16)
+    assert len(frames) == n_frames
+    rows = list(X0)
+    seen = set()
+    y, z = brute.last_outputs(tk, rows)
+    c0, margin = _greedy_f32(z, seen, rho)
+    assert margin > 1e-4, "fixture has a near tie"
+    main = []
+    for f in range(n_frames):
+        _close(frames[f]["y"], y, 1e-9)
+        _close(frames[f]["z"], z, 1e-9)
+        assert frames[f]["c0"] == c0, (f, frames[f]["c0"], c0)
+        seen.add(c0)
+        main.append(c0)
+        cp_rows = [np.asarray(y), tk.tables[0][c0]]
+        codes = []
+        for j in range(15):
+            yy, zz = brute.last_outputs(cp, cp_rows, head=j)
+            _close(frames[f]["cp"][j][1], zz, 1e-9)
+            c, mg = _greedy_f32(zz, None, 1.0)
+            assert mg > 1e-4, "fixture has a near tie"
+            codes.append(c)
+            if j < 14:
+                cp_rows.append(cp.tables[j + 1][c])
+        assert frames[f]["codes"] == codes, (f, frames[f]["codes"], codes)
+        if f + 1 == n_frames:
+            break
+        x = tk.tables[0][c0] + sum(tk.tables[g][codes[g - 1]] for g in range(1, 16)) + text[f + 1]
+        rows.append(x)
+        y, z = brute.last_outputs(tk, rows)
+        c0, margin = _greedy_f32(z, seen, rho)
+        assert margin > 1e-4, "fixture has a near tie"
+    if rho != 1.0:
+        plain, _ = od.run_talker(tk, cp, X0, text, n_frames, 8, rho=1.0, cp_capacity=16)
+        assert [fr["c0"] for fr in plain] != main, "the penalty decides no choice here"
+
+
 # ---------------------------------------------------------------- penalty / argmax
 
 def check_penalty_and_argmax():

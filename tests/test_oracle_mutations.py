@@ -304,6 +304,79 @@ def _prefill_row_index(model, cache, X, head=0, rope_pos=None):
     return _orig["prefill"](model, cache, X, head)
 
 
+def _run_lm_slip(slip):
+    """run_lm with one slip: 'feed_prev' feeds token k-1 to step k, 'grow_early'
+    grows one row before the write position reaches the capacity, 'short'
+    runs one step fewer."""
+    def run(model, X0, n_steps, s_init, forced=None, head=0, rho=1.0, on_step=None,
+            sampling=None, controls=None):
+        cache = od.Cache(model, s_init)
+        y, z = od.prefill(model, cache, X0, head)
+        tok, margin = od.penalized_argmax(z, None, 1.0)
+        out = [(y, z, tok, margin)]
+        if on_step:
+            on_step(0, cache)
+        last = n_steps if slip != "short" else n_steps - 1
+        for k in range(1, last + 1):
+            fed = out[-1][2] if slip != "feed_prev" or len(out) < 2 else out[-2][2]
+            pos = cache.pos + (1 if slip == "grow_early" else 0)
+            cap = od.bucket_for(pos, cache.capacity)
+            if cap != cache.capacity:
+                cache.grow(cap)
+            y, z = od.step(model, cache, od.embed(model, [fed], [0]), head)
+            tok, margin = od.penalized_argmax(z, None, 1.0)
+            out.append((y, z, tok, margin))
+            if on_step:
+                on_step(k, cache)
+        return out, cache
+    return run
+
+
+def _run_talker_slip(slip):
+    """run_talker (greedy, no forcing) with one slip: 'text_f' adds text row f
+    instead of f + 1, 'seen_early' marks the unpenalised best token seen before
+    the penalised choice, 'no_c0' leaves c0's embedding out of the next input,
+    'cp_penalty' applies the penalty to the Code Predictor's codes too."""
+    def run(talker, cp, X0, text, n_frames, s_init, rho=1.05, cp_capacity=16, forced=None,
+            tk_sampling=None, cp_sampling=None, tk_controls=None):
+        cache = od.Cache(talker, s_init)
+        seen = np.zeros(talker.heads[0].shape[0], bool)
+
+        def pick(z):
+            if slip == "seen_early":
+                seen[int(np.argmax(z))] = True
+            return od.penalized_argmax(z, seen, rho)
+
+        y, z = od.prefill(talker, cache, X0, 0)
+        c0, m0 = pick(z)
+        frames = []
+        for f in range(n_frames):
+            cc = od.Cache(cp, cp_capacity)
+            cseen = np.zeros(cp.heads[0].shape[0], bool)
+            yy, zz = od.prefill(cp, cc, np.stack([y, cp.tables[0][c0]]), 0)
+            choice = (lambda v: od.penalized_argmax(v, cseen, rho)) if slip == "cp_penalty" \
+                else (lambda v: od.penalized_argmax(v, None, 1.0))
+            c, m = choice(zz)
+            codes, trace = [c], [(yy, zz, m)]
+            for j in range(1, len(cp.heads)):
+                yy, zz = od.step(cp, cc, od.embed(cp, [codes[-1]], [j]), j)
+                c, m = choice(zz)
+                codes.append(c)
+                trace.append((yy, zz, m))
+            frames.append(dict(y=y, z=z, c0=c0, margin=m0, codes=codes, cp=trace))
+            if f == n_frames - 1:
+                break
+            used = [c0] + codes
+            ids = list(range(16))
+            if slip == "no_c0":
+                used, ids = used[1:], ids[1:]
+            x = od.embed(talker, used, ids, text[f] if slip == "text_f" else text[f + 1])
+            y, z = od.step(talker, cache, x, 0)
+            c0, m0 = pick(z)
+        return frames, cache
+    return run
+
+
 MUTATIONS = {
     "mrope_h_w_swapped": ("mrope_modality", _mrope_hw_swapped),
     "mrope_interleave_to_the_end": ("mrope_modality", _mrope_no_cutoff),
@@ -337,6 +410,13 @@ MUTATIONS = {
     "grow_copies_short": ("Cache", _ShortGrowCache),
     "prefill_no_causal_mask": ("prefill", _prefill_no_mask),
     "code_predictor_one_head": ("code_predictor_frame", _cp_head0),
+    "lm_feeds_previous_token": ("run_lm", _run_lm_slip("feed_prev")),
+    "lm_grows_one_row_early": ("run_lm", _run_lm_slip("grow_early")),
+    "lm_one_step_short": ("run_lm", _run_lm_slip("short")),
+    "talker_text_row_f": ("run_talker", _run_talker_slip("text_f")),
+    "talker_seen_before_choice": ("run_talker", _run_talker_slip("seen_early")),
+    "talker_input_drops_c0": ("run_talker", _run_talker_slip("no_c0")),
+    "talker_penalty_on_code_predictor": ("run_talker", _run_talker_slip("cp_penalty")),
 }
 
 

@@ -43,6 +43,9 @@ PINS = [
     pins.check_quant_bytes_golden,
     pins.check_bucket_schedule_golden,
     pins.check_talker_bytes_golden,
+    pins.check_run_lm_brute,
+    pins.check_run_lm_asr_stress_golden,
+    pins.check_run_talker_brute,
 ]
 
 

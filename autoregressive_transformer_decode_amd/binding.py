@@ -38,7 +38,7 @@ STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FU
 
 EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
-           "decoder_step", "decoder_prefill_mrope", "decoder_step_mrope", "decoder_embed", "greedy_argmax", "sample_topk", "decoder_generate",
+           "decoder_step", "decoder_step_slots", "atd_workspace_bytes", "decoder_prefill_mrope", "decoder_step_mrope", "decoder_embed", "greedy_argmax", "sample_topk", "decoder_generate",
            "talker_generate_frames", "quantize_blocks", "codec_conv1d_causal",
            "codec_transconv1d_pack", "codec_transconv1d", "decoder_time_stage")
 
@@ -107,6 +107,9 @@ def _load():
         "decoder_get_position": ([vp, i32, C.POINTER(i32), C.POINTER(i32)], C.c_int),
         "decoder_prefill": ([vp, i32, vp, i32, i32, vp, vp, vp], C.c_int),
         "decoder_step": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, vp, vp], C.c_int),
+        "decoder_step_slots": ([vp, i32, C.POINTER(i32), vp, i32, C.POINTER(i32), vp, i32, vp,
+                                vp, vp], C.c_int),
+        "atd_workspace_bytes": ([C.POINTER(atd_config), i32, C.POINTER(C.c_size_t)], C.c_int),
         "decoder_prefill_mrope": ([vp, i32, vp, i32, vp, i32, vp, vp, vp], C.c_int),
         "decoder_step_mrope": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, vp, i32, vp, vp, vp],
                                C.c_int),
@@ -192,6 +195,19 @@ def decoder_step(handle: int, slot0: int, B: int, tok, G: int, table_ids, extra,
                  y_out, logits_out: int, stream: int) -> None:
     _check(lib.decoder_step(handle, slot0, B, tok, G, _i32_array(list(table_ids)), extra, head,
                             y_out, logits_out, stream), handle)
+
+
+def decoder_step_slots(handle: int, B: int, slots, tok, G: int, table_ids, extra, head: int,
+                       y_out, logits_out: int, stream: int) -> None:
+    _check(lib.decoder_step_slots(handle, B, _i32_array(list(slots)), tok, G,
+                                  _i32_array(list(table_ids)), extra, head, y_out, logits_out,
+                                  stream), handle)
+
+
+def atd_workspace_bytes(cfg: atd_config, input_projection: int) -> int:
+    out = C.c_size_t(0)
+    _check(lib.atd_workspace_bytes(C.byref(cfg), input_projection, C.byref(out)))
+    return out.value
 
 
 def decoder_prefill_mrope(handle: int, slot: int, x: int, T: int, rope_pos, head: int, y_out,

@@ -48,6 +48,8 @@ struct atd_decoder {
   int mma_rows = 0;            // most rows of one MFMA chunk (multiple of kMmaRows)
   float* mss = nullptr;        // row sums of squares [mma_rows, ceil(h / kSsCols)]
   uint16_t *mhi = nullptr, *mlo = nullptr;  // GEMM input as bf16 hi/lo [mma_rows, Kmax]
+  int32_t* slot_list = nullptr;  // device [max_rows]: slots of a decoder_step_slots call
+  std::vector<int32_t> step_slots;  // host copy of that list while its call enqueues
   int32_t* counter = nullptr;  // token counter of decoder_generate
   int32_t* ctl_base = nullptr; // first choice index of a controlled generate call
   size_t part_floats = 0;      // capacity of pacc in floats / D
@@ -304,7 +306,9 @@ AttnArgs attn_args(const atd_decoder* d, RowMap rows, int l, int M, int max_len_
   a.nsplit_max = attn_max_splits(max_len_bound, M, c.n_kv_heads, waves);
   a.waves = waves;
   if (rows.mode == kRowsPrefill || M == 1) {  // one slot: pass its rows directly
-    const int slot = rows.mode == kRowsPrefill ? rows.slot0 : rows.slot0 + rows.row0;
+    const int slot = rows.mode == kRowsPrefill ? rows.slot0
+                     : rows.slot_list               ? d->step_slots[rows.row0]
+                                                    : rows.slot0 + rows.row0;
     a.k_direct = d->kp[slot][l];
     a.v_direct = d->vp[slot][l];
     a.cap_direct = d->cap[slot];
@@ -687,19 +691,96 @@ hipError_t mrope_rows(atd_decoder* d, const int32_t* rope_pos, int M, hipStream_
                            d->rsin, s);
 }
 
-// Launch sequence of one decode step of B rows (slots slot0..slot0+B-1);
-// rope_pos: rotary positions [B, 3] of the rows, or null (cache positions).
+// Launch sequence of one decode step of B rows (slots slot0..slot0+B-1, or
+// the slots of d->step_slots when `listed`); rope_pos: rotary positions
+// [B, 3] of the rows, or null (cache positions).
 hipError_t enqueue_step(atd_decoder* d, int slot0, int B, const int32_t* tok, int G,
                         const int32_t* table_ids, const float* extra, int head, float* y_out,
                         float* logits_out, int max_cap, hipStream_t s,
-                        const int32_t* rope_pos = nullptr) {
+                        const int32_t* rope_pos = nullptr, bool listed = false) {
   RowMap rows{kRowsStep, slot0, 0, rope_pos ? 1 : 0};
-  hipError_t e = rope_pos ? mrope_rows(d, rope_pos, B, s) : hipSuccess;
+  hipError_t e = hipSuccess;
+  if (listed) {
+    rows.slot_list = d->slot_list;
+    e = launch_slot_list(d->slot_list, d->step_slots.data(), B, s);
+  }
+  if (e == hipSuccess && rope_pos) e = mrope_rows(d, rope_pos, B, s);
   if (e == hipSuccess) e = build_inputs(d, embed_args(d, B, tok, G, table_ids, extra, d->x), s);
   const HeadOut ho{head, y_out, logits_out};
   if (e == hipSuccess) e = run_layers(d, rows, B, max_cap, d->x, &ho, s);
   if (e == hipSuccess) e = launch_advance(slots_of(d), rows, B, s);
   return e;
+}
+
+// Byte offsets of the decoder's device scratch (one allocation) for a config.
+struct ScratchPlan {
+  size_t o_cos, o_sin, o_rcos, o_rsin, o_x, o_xin, o_qkv, o_q, o_o, o_act, o_pml, o_pacc, o_kv,
+      o_pos, o_cap, o_part, o_cnt, o_list, o_samp, o_mss = 0, o_mhi = 0, o_mlo = 0, o_mpart = 0;
+  size_t total = 0;
+  size_t part_floats = 0;  // attention partials capacity, in floats per head dim
+  bool mma = false;
+  int mma_rows = 0;
+};
+
+void plan_scratch(const atd_config& c, bool in_proj, ScratchPlan& p) {
+  const int R = c.max_rows, S = c.max_slots, h = c.hidden, D = c.head_dim;
+  const int nq = c.n_q_heads * D, nqkv = nq + 2 * c.n_kv_heads * D;
+  const int in_dim = c.input_dim ? c.input_dim : h;
+  const size_t half = D / 2;
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  p.o_cos = carve((size_t)c.max_ctx * half * 4);
+  p.o_sin = carve((size_t)c.max_ctx * half * 4);
+  p.o_rcos = carve((size_t)R * half * 4);
+  p.o_rsin = carve((size_t)R * half * 4);
+  p.o_x = carve((size_t)R * h * 4);
+  p.o_xin = carve(in_proj ? (size_t)R * in_dim * 4 : 0);
+  p.o_qkv = carve((size_t)R * nqkv * 4);
+  p.o_q = carve((size_t)R * nq * 4);
+  p.o_o = carve((size_t)R * nq * 4);
+  p.o_act = carve((size_t)R * c.ffn * 4);
+  // attention partials: M * Hq * attn_max_splits(L, M, Hkv) <= this many per head dim
+  p.part_floats = (size_t)c.n_q_heads *
+                  std::min((size_t)R * ((c.max_ctx + kAttnMinChunk - 1) / kAttnMinChunk),
+                           (size_t)(kAttnWavesMax / c.n_kv_heads + R));
+  p.o_pml = carve(p.part_floats * 2 * 4);
+  p.o_pacc = carve(p.part_floats * D * 4);
+  p.o_kv = carve((size_t)S * c.n_layers * 2 * sizeof(void*));
+  p.o_pos = carve((size_t)S * 4);
+  p.o_cap = carve((size_t)S * 4);
+  const int nblk_v = (c.vocab + kArgmaxChunk - 1) / kArgmaxChunk;
+  p.o_part = carve((size_t)R * nblk_v * 3 * 4);
+  p.o_cnt = carve(8);
+  p.o_list = carve((size_t)R * 4);
+  const int nblk_s = sample_blocks(c.vocab);
+  p.o_samp = carve(nblk_s > 1 ? (size_t)nblk_s * kTopKMax * sizeof(uint2) : 0);
+  // MFMA path: hi/lo activations of one 64-row chunk and split-K partials of
+  // the largest GEMM (q/k/v, o, gate/up, down, LM head)
+  p.mma = c.dtype == ATD_BF16 && c.weight_format == ATD_WFMT_DENSE &&
+          !(c.flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 && nq % 32 == 0 && c.ffn % 32 == 0 &&
+          std::max(R, S) >= 3;
+  if (p.mma) {
+    // chunks of up to kMmaPrefillRows rows (row tiles of kMmaRows)
+    p.mma_rows = std::max(kMmaRows, (std::min(R, kMmaPrefillRows) + kMmaRows - 1) / kMmaRows *
+                                        kMmaRows);
+    // partials of the largest GEMM at every row-tile count a chunk can have
+    size_t pmax = 0;
+    for (int t = 1; t <= p.mma_rows / kMmaRows; ++t) {
+      auto parts = [t](int n, int k) { return (size_t)mma_ks(n, k, t) * t * kMmaRows * n; };
+      pmax = std::max({pmax, parts(nqkv, h), parts(h, nq), parts(2 * c.ffn, h),
+                       parts(h, c.ffn), parts(c.vocab, h)});
+    }
+    p.o_mss = carve((size_t)p.mma_rows * ((h + kSsCols - 1) / kSsCols) * 4);
+    const size_t kmax = std::max({(size_t)h, (size_t)nq, (size_t)c.ffn});
+    p.o_mhi = carve((size_t)p.mma_rows * kmax * 2);
+    p.o_mlo = carve((size_t)p.mma_rows * kmax * 2);
+    p.o_mpart = carve(pmax * 4);
+  }
+  p.total = off;
 }
 
 }  // namespace
@@ -734,62 +815,20 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
     *out = d;
     return ATD_OK;
   }
-  const int R = cfg->max_rows, h = cfg->hidden, D = cfg->head_dim;
-  const int nq = cfg->n_q_heads * D, nqkv = nq + 2 * cfg->n_kv_heads * D;
+  ScratchPlan sp;
+  plan_scratch(*cfg, w->in_proj != nullptr, sp);
+  d->part_floats = sp.part_floats;
+  d->mma = sp.mma;
+  d->mma_rows = sp.mma_rows;
+  const size_t off = sp.total;
+  const size_t o_cos = sp.o_cos, o_sin = sp.o_sin, o_rcos = sp.o_rcos, o_rsin = sp.o_rsin,
+               o_x = sp.o_x, o_xin = sp.o_xin, o_qkv = sp.o_qkv, o_q = sp.o_q, o_o = sp.o_o,
+               o_act = sp.o_act, o_pml = sp.o_pml, o_pacc = sp.o_pacc, o_kv = sp.o_kv,
+               o_pos = sp.o_pos, o_cap = sp.o_cap, o_part = sp.o_part, o_cnt = sp.o_cnt,
+               o_list = sp.o_list, o_samp = sp.o_samp, o_mss = sp.o_mss, o_mhi = sp.o_mhi,
+               o_mlo = sp.o_mlo, o_mpart = sp.o_mpart;
+  const int D = cfg->head_dim;
   const size_t half = D / 2;
-  size_t off = 0;
-  auto carve = [&](size_t bytes) {
-    size_t o = off;
-    off += align256(bytes);
-    return o;
-  };
-  const size_t o_cos = carve((size_t)cfg->max_ctx * half * 4);
-  const size_t o_sin = carve((size_t)cfg->max_ctx * half * 4);
-  const size_t o_rcos = carve((size_t)R * half * 4);
-  const size_t o_rsin = carve((size_t)R * half * 4);
-  const size_t o_x = carve((size_t)R * h * 4);
-  const size_t o_xin = carve(w->in_proj ? (size_t)R * d->in_dim * 4 : 0);
-  const size_t o_qkv = carve((size_t)R * nqkv * 4);
-  const size_t o_q = carve((size_t)R * nq * 4);
-  const size_t o_o = carve((size_t)R * nq * 4);
-  const size_t o_act = carve((size_t)R * cfg->ffn * 4);
-  // attention partials: M * Hq * attn_max_splits(L, M, Hkv) <= this many per head dim
-  d->part_floats = (size_t)cfg->n_q_heads *
-                   std::min((size_t)R * ((cfg->max_ctx + kAttnMinChunk - 1) / kAttnMinChunk),
-                            (size_t)(kAttnWavesMax / cfg->n_kv_heads + R));
-  const size_t o_pml = carve(d->part_floats * 2 * 4);
-  const size_t o_pacc = carve(d->part_floats * D * 4);
-  const size_t o_kv = carve((size_t)S * cfg->n_layers * 2 * sizeof(void*));
-  const size_t o_pos = carve((size_t)S * 4);
-  const size_t o_cap = carve((size_t)S * 4);
-  const int nblk_v = (cfg->vocab + kArgmaxChunk - 1) / kArgmaxChunk;
-  const size_t o_part = carve((size_t)R * nblk_v * 3 * 4);
-  const size_t o_cnt = carve(8);
-  const int nblk_s = sample_blocks(cfg->vocab);
-  const size_t o_samp = carve(nblk_s > 1 ? (size_t)nblk_s * kTopKMax * sizeof(uint2) : 0);
-  // MFMA path: hi/lo activations of one 64-row chunk and split-K partials of
-  // the largest GEMM (q/k/v, o, gate/up, down, LM head)
-  d->mma = cfg->dtype == ATD_BF16 && cfg->weight_format == ATD_WFMT_DENSE &&
-           !(cfg->flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 &&
-           nq % 32 == 0 && cfg->ffn % 32 == 0 && std::max(R, S) >= 3;
-  size_t o_mss = 0, o_mhi = 0, o_mlo = 0, o_mpart = 0;
-  if (d->mma) {
-    // chunks of up to kMmaPrefillRows rows (row tiles of kMmaRows)
-    d->mma_rows = std::max(kMmaRows, (std::min(R, kMmaPrefillRows) + kMmaRows - 1) / kMmaRows *
-                                         kMmaRows);
-    // partials of the largest GEMM at every row-tile count a chunk can have
-    size_t pmax = 0;
-    for (int t = 1; t <= d->mma_rows / kMmaRows; ++t) {
-      auto parts = [t](int n, int k) { return (size_t)mma_ks(n, k, t) * t * kMmaRows * n; };
-      pmax = std::max({pmax, parts(nqkv, h), parts(h, nq), parts(2 * cfg->ffn, h),
-                       parts(h, cfg->ffn), parts(cfg->vocab, h)});
-    }
-    o_mss = carve((size_t)d->mma_rows * ((h + kSsCols - 1) / kSsCols) * 4);
-    const size_t kmax = std::max({(size_t)h, (size_t)nq, (size_t)cfg->ffn});
-    o_mhi = carve((size_t)d->mma_rows * kmax * 2);
-    o_mlo = carve((size_t)d->mma_rows * kmax * 2);
-    o_mpart = carve(pmax * 4);
-  }
 
   hipError_t e = hipGetDevice(&d->device);
   if (e == hipSuccess) e = hipMalloc(&d->mem, off);
@@ -816,6 +855,7 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->slot_cap = (int*)(base + o_cap);
   d->part = (float*)(base + o_part);
   d->counter = (int32_t*)(base + o_cnt);
+  d->slot_list = (int32_t*)(base + o_list);
   d->ctl_base = d->counter + 1;
   d->samp = (uint2*)(base + o_samp);
   if (d->mma) {
@@ -845,6 +885,21 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
     return rc;
   }
   *out = d;
+  return ATD_OK;
+}
+
+extern "C" int atd_workspace_bytes(const atd_config* cfg, int32_t input_projection,
+                                   size_t* out) {
+  if (!out) return fail(nullptr, ATD_ERR_INVALID_ARG, "out is NULL");
+  const int rc = check_config(cfg);
+  if (rc) return rc;
+  if (cfg->flags & ATD_FLAG_DRY_RUN) {
+    *out = 0;
+    return ATD_OK;
+  }
+  ScratchPlan sp;
+  plan_scratch(*cfg, input_projection != 0, sp);
+  *out = sp.total;
   return ATD_OK;
 }
 
@@ -1003,16 +1058,34 @@ int prefill_impl(atd_decoder* d, int32_t slot, const float* x, int32_t T,
   return ATD_OK;
 }
 
-int step_impl(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok, int32_t G,
-              const int32_t* table_ids, const float* extra, const int32_t* rope_pos,
-              int32_t head, float* y_out, float* logits_out, void* stream, const char* name) {
+// slots: host list of the B rows' slots, or null for slot0 .. slot0 + B - 1.
+int step_impl(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* slots,
+              const int32_t* tok, int32_t G, const int32_t* table_ids, const float* extra,
+              const int32_t* rope_pos, int32_t head, float* y_out, float* logits_out,
+              void* stream, const char* name) {
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
   const atd_config& c = d->cfg;
   if (B < 1 || B > c.max_rows)
     return fail(d, ATD_ERR_CAPACITY, "B = %d outside [1, max_rows %d]", B, c.max_rows);
-  if (slot0 < 0 || slot0 + B > c.max_slots)
-    return fail(d, ATD_ERR_INVALID_ARG, "slots [%d, %d) outside [0, %d)", slot0, slot0 + B,
-                c.max_slots);
+  std::vector<int32_t> list(B);
+  if (slots) {
+    std::vector<char> used(c.max_slots, 0);
+    for (int b = 0; b < B; ++b) {
+      if (slots[b] < 0 || slots[b] >= c.max_slots)
+        return fail(d, ATD_ERR_INVALID_ARG, "slots[%d] = %d outside [0, %d)", b, slots[b],
+                    c.max_slots);
+      if (used[slots[b]])
+        return fail(d, ATD_ERR_INVALID_ARG, "slots[%d] = %d appears twice in one step", b,
+                    slots[b]);
+      used[slots[b]] = 1;
+      list[b] = slots[b];
+    }
+  } else {
+    if (slot0 < 0 || slot0 + B > c.max_slots)
+      return fail(d, ATD_ERR_INVALID_ARG, "slots [%d, %d) outside [0, %d)", slot0, slot0 + B,
+                  c.max_slots);
+    for (int b = 0; b < B; ++b) list[b] = slot0 + b;
+  }
   if (!logits_out) return fail(d, ATD_ERR_INVALID_ARG, "logits_out is NULL");
   if (y_out && !aligned16(y_out))
     return fail(d, ATD_ERR_INVALID_ARG, "y_out %p not 16-byte aligned", (void*)y_out);
@@ -1022,7 +1095,7 @@ int step_impl(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok, int3
   if (rc) return rc;
   int max_cap = 0;
   for (int b = 0; b < B; ++b) {
-    const int sl = slot0 + b;
+    const int sl = list[b];
     if (!d->attached[sl])
       return fail(d, ATD_ERR_INVALID_ARG, "slot %d has no KV buffers attached", sl);
     if (d->pos[sl] >= d->cap[sl])
@@ -1034,13 +1107,15 @@ int step_impl(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok, int3
     max_cap = std::max(max_cap, std::min(d->cap[sl], c.max_ctx));
   }
   if (d->dry) {
-    for (int b = 0; b < B; ++b) d->pos[slot0 + b] += 1;
+    for (int b = 0; b < B; ++b) d->pos[list[b]] += 1;
     return ATD_OK;
   }
+  if (slots) d->step_slots = list;
   hipError_t e = enqueue_step(d, slot0, B, tok, G, table_ids, extra, head, y_out, logits_out,
-                              max_cap, (hipStream_t)stream, rope_pos);
+                              max_cap, (hipStream_t)stream, rope_pos, slots != nullptr);
+  d->step_slots.clear();
   if (e != hipSuccess) return hip_fail(d, e, name);
-  for (int b = 0; b < B; ++b) d->pos[slot0 + b] += 1;
+  for (int b = 0; b < B; ++b) d->pos[list[b]] += 1;
   return ATD_OK;
 }
 
@@ -1063,8 +1138,17 @@ extern "C" int decoder_prefill_mrope(atd_decoder* d, int32_t slot, const float* 
 extern "C" int decoder_step(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok,
                             int32_t G, const int32_t* table_ids, const float* extra,
                             int32_t head, float* y_out, float* logits_out, void* stream) {
-  return step_impl(d, slot0, B, tok, G, table_ids, extra, nullptr, head, y_out, logits_out,
-                   stream, "decoder_step");
+  return step_impl(d, slot0, B, nullptr, tok, G, table_ids, extra, nullptr, head, y_out,
+                   logits_out, stream, "decoder_step");
+}
+
+extern "C" int decoder_step_slots(atd_decoder* d, int32_t B, const int32_t* slots,
+                                  const int32_t* tok, int32_t G, const int32_t* table_ids,
+                                  const float* extra, int32_t head, float* y_out,
+                                  float* logits_out, void* stream) {
+  if (!slots) return fail(d, ATD_ERR_INVALID_ARG, "slots is NULL");
+  return step_impl(d, 0, B, slots, tok, G, table_ids, extra, nullptr, head, y_out, logits_out,
+                   stream, "decoder_step_slots");
 }
 
 extern "C" int decoder_step_mrope(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok,
@@ -1072,8 +1156,8 @@ extern "C" int decoder_step_mrope(atd_decoder* d, int32_t slot0, int32_t B, cons
                                   const int32_t* rope_pos, int32_t head, float* y_out,
                                   float* logits_out, void* stream) {
   if (!rope_pos) return fail(d, ATD_ERR_INVALID_ARG, "rope_pos is NULL");
-  return step_impl(d, slot0, B, tok, G, table_ids, extra, rope_pos, head, y_out, logits_out,
-                   stream, "decoder_step_mrope");
+  return step_impl(d, slot0, B, nullptr, tok, G, table_ids, extra, rope_pos, head, y_out,
+                   logits_out, stream, "decoder_step_mrope");
 }
 
 // ---------------------------------------------------------------- argmax
@@ -1082,12 +1166,16 @@ namespace {
 struct ChoiceScratch {
   void* p = nullptr;
   size_t bytes = 0;
+  std::vector<void*> retired;   // smaller buffers, never freed
 };
 std::mutex g_choice_mu;
 std::map<int, ChoiceScratch> g_choice_scratch;
 
-// Device scratch of greedy_argmax / sample_topk, one per device, grown on
-// demand (calls that overlap on one device share it).
+// Device scratch of greedy_argmax / sample_topk, one per device (calls that
+// overlap on one device share it).  A call that needs more space gets a new,
+// larger buffer; the old one is kept allocated until the process ends, since
+// work already queued, or a graph a caller captured around an earlier call,
+// may still use its address.
 int choice_scratch(size_t need, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1095,12 +1183,12 @@ int choice_scratch(size_t need, void** out) {
   std::lock_guard<std::mutex> lk(g_choice_mu);
   ChoiceScratch& sc = g_choice_scratch[dev];
   if (sc.bytes < need) {
-    if (sc.p) (void)hipFree(sc.p);
-    sc.p = nullptr;
-    sc.bytes = 0;
-    const size_t bytes = std::max(need, size_t(1) << 16);
-    e = hipMalloc(&sc.p, bytes);
+    const size_t bytes = std::max(need, std::max(2 * sc.bytes, size_t(1) << 16));
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
     if (e != hipSuccess) return hip_fail(nullptr, e, "hipMalloc of token-choice scratch");
+    if (sc.p) sc.retired.push_back(sc.p);
+    sc.p = p;
     sc.bytes = bytes;
   }
   *out = sc.p;

@@ -48,8 +48,9 @@ inline int attn_max_splits(int max_len, int M, int Hkv, int waves) {
 }
 
 // How the rows of a launch map to (slot, position):
-//  kRowsStep:    row m -> slot slot0 + m at that slot's current position
-//  kRowsPrefill: row m -> slot slot0 at position m
+//  kRowsStep:    row m -> slot slot_list[row0 + m] (or slot0 + row0 + m when
+//                there is no list) at that slot's current position
+//  kRowsPrefill: row m -> slot slot0 at position row0 + m
 enum RowMode { kRowsStep = 0, kRowsPrefill = 1 };
 
 struct RowMap {
@@ -58,6 +59,21 @@ struct RowMap {
   int row0;       // rows of this launch are rows row0 .. of the call
   int rope_rows;  // 1: the RoPE tables hold one row per call row (row0 + m),
                   // built from rotary positions; 0: indexed by position
+  const int32_t* slot_list = nullptr;  // device [rows of the call]: slot of each
+                                       // step row, or null (contiguous slots)
+};
+
+// Slot of step row r (a row of the whole call).
+inline ATD_HD int step_slot(const RowMap& rm, int r) {
+  return rm.slot_list ? rm.slot_list[r] : rm.slot0 + r;
+}
+
+// Host slot list -> device (up to kSlotListChunk entries per launch, passed by
+// value, so the copy needs no staging buffer and can be captured in a graph).
+constexpr int kSlotListChunk = 256;
+struct SlotListArgs {
+  int32_t v[kSlotListChunk];
+  int n, off;
 };
 
 // ---------------------------------------------------------------- rows/KV
@@ -329,6 +345,8 @@ hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream
 // k_direct set) in one pass over key tiles: writes o (or o_hi / o_lo).
 hipError_t launch_attn_prefill(const AttnArgs& a, int bf16, int D, int r, hipStream_t s);
 hipError_t launch_advance(const SlotTables& st, RowMap rows, int M, hipStream_t s);
+// dst[i] = slots[i], i < n (host values, written on the stream)
+hipError_t launch_slot_list(int32_t* dst, const int32_t* slots, int n, hipStream_t s);
 // RoPE rows of a call with rotary positions pos3 [M][3] (t, h, w): row m,
 // frequency i takes cos/sin of the position table at pos3[m][c(i)], c(i) = 1
 // when i % 3 == 1 and i < 3 sec_h, 2 when i % 3 == 2 and i < 3 sec_w, else 0;

@@ -248,7 +248,7 @@ __device__ __forceinline__ void row_of(const RowMap& r, const SlotTables& st, in
     slot = r.slot0;
     pos = r.row0 + m;
   } else {
-    slot = r.slot0 + r.row0 + m;
+    slot = step_slot(r, r.row0 + m);
     pos = st.pos[slot];
   }
 }
@@ -1109,8 +1109,13 @@ __global__ void k_advance(SlotTables st, RowMap rows, int M) {
   if (rows.mode == kRowsPrefill) {
     if (m == 0) st.pos[rows.slot0] = M;
   } else if (m < M) {
-    st.pos[rows.slot0 + m] += 1;
+    st.pos[step_slot(rows, rows.row0 + m)] += 1;
   }
+}
+
+__global__ void k_slot_list(int32_t* dst, SlotListArgs a) {
+  const int i = threadIdx.x;
+  if (i < a.n) dst[a.off + i] = a.v[i];
 }
 
 struct SlotSetArgs {
@@ -2691,6 +2696,19 @@ hipError_t launch_mrope_rows(const int32_t* pos3, int M, int half, int sec_h, in
 hipError_t launch_advance(const SlotTables& st, RowMap rows, int M, hipStream_t s) {
   hipLaunchKernelGGL(k_advance, dim3((M + 255) / 256), dim3(256), 0, s, st, rows, M);
   return hipGetLastError();
+}
+
+hipError_t launch_slot_list(int32_t* dst, const int32_t* slots, int n, hipStream_t s) {
+  for (int off = 0; off < n; off += kSlotListChunk) {
+    SlotListArgs a{};
+    a.n = n - off < kSlotListChunk ? n - off : kSlotListChunk;
+    a.off = off;
+    for (int i = 0; i < a.n; ++i) a.v[i] = slots[off + i];
+    hipLaunchKernelGGL(k_slot_list, dim3(1), dim3(kSlotListChunk), 0, s, dst, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_set_slot(const SlotTables& st, int slot, void* const* k, void* const* v,

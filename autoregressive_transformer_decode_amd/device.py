@@ -210,16 +210,24 @@ class Decoder:
     def step(self, tok: Optional[torch.Tensor], table_ids: Sequence[int], slot0: int = 0,
              nrows: int = 1, extra: Optional[torch.Tensor] = None, head: int = 0,
              y_out: Optional[torch.Tensor] = None, logits_out: Optional[torch.Tensor] = None,
-             rope_pos: Optional[torch.Tensor] = None):
+             rope_pos: Optional[torch.Tensor] = None, slots: Optional[Sequence[int]] = None):
         """rope_pos: device int32 [nrows, 3] rotary (t, h, w) positions
-        (decoder_step_mrope), or None (each slot's cache position)."""
+        (decoder_step_mrope), or None (each slot's cache position).  slots: the
+        slot of each row (decoder_step_slots), or None for slot0 .. slot0 +
+        nrows - 1."""
         G = len(table_ids)
+        if slots is not None:
+            nrows = len(slots)
         if logits_out is None:
             logits_out = torch.empty(nrows, self.shape.vocab, device="cuda", dtype=torch.float32)
         tp = tok.data_ptr() if tok is not None else None
         ex = extra.data_ptr() if extra is not None else None
         y = y_out.data_ptr() if y_out is not None else None
-        if rope_pos is None:
+        if slots is not None:
+            assert rope_pos is None, "decoder_step_slots takes cache positions"
+            B.decoder_step_slots(self.handle, nrows, list(slots), tp, G, table_ids, ex, head, y,
+                                 logits_out.data_ptr(), _stream())
+        elif rope_pos is None:
             B.decoder_step(self.handle, slot0, nrows, tp, G, table_ids, ex, head, y,
                            logits_out.data_ptr(), _stream())
         else:

@@ -10,8 +10,10 @@ same values: every tensor has an integer id; its elements are drawn in blocks
 of ``BLOCK`` values, block ``b`` from ``numpy.random.default_rng([seed,
 model_id, tensor_id, b])`` as float32 standard normals times the scale.  For
 bf16 models the float32 draw is rounded to bf16 (round to nearest even).
-Norm gains are 1.  Block seeding makes the values independent of how many
-threads draw them.
+Norm gains are 1 (the workloads' configuration); with ``gain_sd`` > 0 every
+gain vector is 1 + gain_sd * N(0, 1) instead, each drawn under its own tensor
+id (so a kernel that reads the wrong gain vector shows).  Block seeding makes
+the values independent of how many threads draw them.
 """
 
 from __future__ import annotations
@@ -39,6 +41,9 @@ _T_TEXT = 70_001
 _T_TOKENS = 70_002
 _T_KV = 60_000
 _T_INPROJ = 91_000
+# gains: per layer base + 11..14 (input, q, k, post-attention); final 92_000
+_T_G_ATTN, _T_G_Q, _T_G_K, _T_G_MLP = range(11, 15)
+_T_G_FINAL = 92_000
 
 
 @dataclasses.dataclass(frozen=True)
@@ -259,10 +264,17 @@ def make_tables(shape: ModelShape, seed: int = 0) -> List[Tensor]:
 
 
 def make_weights(shape: ModelShape, seed: int = 0,
-                 tables: Optional[List[Tensor]] = None) -> ModelWeights:
+                 tables: Optional[List[Tensor]] = None, gain_sd: float = 0.0) -> ModelWeights:
+    """All weights of a stack.  Gains are 1, or with gain_sd > 0 drawn as
+    1 + gain_sd * N(0, 1) (float32), a separate draw per gain vector."""
     h, q, kv, f, d = shape.hidden, shape.q_dim, shape.kv_dim, shape.ffn, shape.head_dim
     mid = shape.model_id
-    ones_h = np.ones(h, np.float32)
+
+    def gain(tid, n):
+        if gain_sd <= 0.0:
+            return np.ones(n, np.float32)
+        return (np.float32(1.0) + normal(seed, mid, tid, (n,), scale=gain_sd)).astype(np.float32)
+
     layers = []
     for l in range(shape.n_layers):
         base = 1000 * (l + 1)
@@ -274,12 +286,12 @@ def make_weights(shape: ModelShape, seed: int = 0,
             return normal(seed, mid, base + k, (n,)) if shape.qkv_bias else None
 
         layers.append(LayerWeights(
-            attn_norm=ones_h.copy(),
+            attn_norm=gain(base + _T_G_ATTN, h),
             wq=w(_T_WQ, (q, h)), wk=w(_T_WK, (kv, h)), wv=w(_T_WV, (kv, h)),
             bq=b(_T_BQ, q), bk=b(_T_BK, kv), bv=b(_T_BV, kv),
-            q_norm=np.ones(d, np.float32) if shape.qk_norm else None,
-            k_norm=np.ones(d, np.float32) if shape.qk_norm else None,
-            wo=w(_T_WO, (h, q)), mlp_norm=ones_h.copy(),
+            q_norm=gain(base + _T_G_Q, d) if shape.qk_norm else None,
+            k_norm=gain(base + _T_G_K, d) if shape.qk_norm else None,
+            wo=w(_T_WO, (h, q)), mlp_norm=gain(base + _T_G_MLP, h),
             w_gate=w(_T_WG, (f, h)), w_up=w(_T_WU, (f, h)), w_down=w(_T_WD, (h, f)),
         ))
     heads = [_stored(normal(seed, mid, _T_HEAD + j, (shape.vocab, h)), shape.dtype)
@@ -290,7 +302,7 @@ def make_weights(shape: ModelShape, seed: int = 0,
     if shape.input_dim:
         in_proj = _stored(normal(seed, mid, _T_INPROJ, (h, shape.input_dim)), shape.dtype)
         in_bias = normal(seed, mid, _T_INPROJ + 1, (h,))
-    return ModelWeights(shape, layers, ones_h.copy(), heads, tables, in_proj, in_bias)
+    return ModelWeights(shape, layers, gain(_T_G_FINAL, h), heads, tables, in_proj, in_bias)
 
 
 def prefill_embeddings(wl: Workload, seed: int = 0) -> np.ndarray:

@@ -235,17 +235,30 @@ typedef struct atd_controls {
 
 typedef struct atd_decoder atd_decoder;
 
-/* Create a decoder.  Validates cfg and w (all device pointers non-NULL where
+/* Create a decoder ("NEON library" page, "Contracts": every argument is
+ * validated before any work and a refused call leaves nothing behind;
+ * "Rockchip NPU sidecars" page: an unsupported setting is an error, never a
+ * silent fallback).  Validates cfg and w (all device pointers non-NULL where
  * required, 16-byte aligned), then allocates its device scratch (residual
  * stream, projections, attention partials, RoPE table, slot tables) sized by
- * max_rows, max_slots and max_ctx.  Slots start with no KV buffers attached
- * (attach them with kv_bucket_grow).  *out is set only on ATD_OK.
- * Errors: INVALID_ARG, SHAPE, DTYPE, UNSUPPORTED, DEVICE. */
+ * max_rows, max_slots and max_ctx: atd_workspace_bytes bytes.  Slots start
+ * with no KV buffers attached (attach them with kv_bucket_grow).  *out is set
+ * only on ATD_OK.  Errors: INVALID_ARG, SHAPE, DTYPE, UNSUPPORTED, DEVICE. */
 int decoder_create(const atd_config* cfg, const atd_weights* w, atd_decoder** out);
 
-/* Release the decoder and its scratch (the caller's weights and KV buffers
- * are untouched).  Waits for work still queued that uses the scratch.
- * NULL is accepted. */
+/* Device bytes decoder_create allocates for cfg (input_projection: 1 when the
+ * weights will carry an input projection).  The decoder owns this scratch
+ * rather than taking a caller workspace per call: the graphs that
+ * decoder_generate and talker_generate_frames capture hold its addresses, so
+ * it has to live exactly as long as the handle.  The query lets a caller
+ * budget device memory before creating.  0 for a dry-run config.  Errors:
+ * INVALID_ARG and the config errors of decoder_create. */
+int atd_workspace_bytes(const atd_config* cfg, int32_t input_projection, size_t* out);
+
+/* Release the decoder and its scratch ("NEON library" page, "Contracts": the
+ * caller's storage is never the library's; the weights and KV buffers are
+ * untouched).  Waits for work still queued that uses the scratch.  NULL is
+ * accepted. */
 int decoder_destroy(atd_decoder* dec);
 
 /* Message of the last error on this decoder, or of the last failed
@@ -276,7 +289,10 @@ int decoder_set_position(atd_decoder* dec, int32_t slot, int32_t pos, void* stre
 int decoder_get_position(const atd_decoder* dec, int32_t slot, int32_t* pos,
                          int32_t* capacity);
 
-/* Prefill: reset `slot` to position 0 and run the T rows of x (device
+/* Prefill ("qwen3-tts-hip OPTIMIZATION_LOG", Talker and Code Predictor
+ * prefill stages; "Audio8-ASR dynamic KV-cache bucket", dynamic window
+ * mechanism: the prompt fills cache rows 0..T-1 of the slot's bucket): reset
+ * `slot` to position 0 and run the T rows of x (device
  * [T, input_dim] float32; input rows, projected first when the stack has an
  * input projection) at positions 0..T-1 through the stack, each row attending
  * to the rows before it and itself.  Writes KV rows 0..T-1 and leaves the
@@ -287,8 +303,13 @@ int decoder_get_position(const atd_decoder* dec, int32_t slot, int32_t* pos,
 int decoder_prefill(atd_decoder* dec, int32_t slot, const float* x, int32_t T,
                     int32_t head, float* y_out, float* logits_out, void* stream);
 
-/* One decode step of B streams, slots slot0 .. slot0+B-1, each at its own
- * position p.  Input row b = sum over g < G of
+/* One decode step ("qwen3-tts-hip OPTIMIZATION_LOG", DecodeStepStack entry:
+ * per layer the input norm, q/k/v projection, q/k layout and cache write,
+ * attention, output projection + residual, post norm, gate/up, SwiGLU, down
+ * + residual; "Audio8-ASR dynamic KV-cache bucket", dynamic window mechanism:
+ * the step writes row p of the slot's bucket and attends to rows 0..p) of B
+ * streams, slots slot0 .. slot0+B-1, each at its own position p.  Input row
+ * b = sum over g < G of
  * tables[table_ids[g]][tok[b*G + g]] + extra[b] (extra: device [B, input_dim]
  * float32 or NULL; G may be 0 when extra is given).  tok: device int32
  * [B, G]; ids outside [0, V_g) are clamped into range.  table_ids: host
@@ -301,6 +322,21 @@ int decoder_prefill(atd_decoder* dec, int32_t slot, const float* x, int32_t T,
 int decoder_step(atd_decoder* dec, int32_t slot0, int32_t B, const int32_t* tok,
                  int32_t G, const int32_t* table_ids, const float* extra,
                  int32_t head, float* y_out, float* logits_out, void* stream);
+
+/* decoder_step over any set of slots: row b of tok / extra / y_out /
+ * logits_out belongs to slot slots[b] (host int32 [B], distinct, any order),
+ * so a batch can step whichever streams are ready ("Audio8-ASR dynamic
+ * KV-cache bucket", dynamic window mechanism: the host owns each stream's
+ * cache and schedules its steps).  The list is host memory because every slot
+ * is validated and its position mirrored on the host before anything is
+ * enqueued ("NEON library" page, "Contracts"); the library writes it into its
+ * own device scratch on `stream` (kernel arguments, no staging buffer), so the
+ * array may be reused once the call returns.  Results equal decoder_step on
+ * the same rows.  Errors: as decoder_step, and INVALID_ARG for a NULL list, a
+ * slot outside [0, max_slots) or a slot listed twice. */
+int decoder_step_slots(atd_decoder* dec, int32_t B, const int32_t* slots, const int32_t* tok,
+                       int32_t G, const int32_t* table_ids, const float* extra, int32_t head,
+                       float* y_out, float* logits_out, void* stream);
 
 /* Rotary positions apart from the cache position (interleaved multimodal
  * RoPE; "Qwen3-TTS ncnn port", Talker section: the Talker's mRoPE cuts the
@@ -344,8 +380,11 @@ int decoder_embed(atd_decoder* dec, int32_t B, const int32_t* tok, int32_t G,
  * float32 [B] or NULL) and sets the chosen token's bit in seen.  The logits
  * are not modified.  controls (or NULL): atd_controls, the choice of every
  * row having index controls->first_index.  Uses a device scratch buffer
- * that the library keeps per device (allocated on first use).  Errors:
- * INVALID_ARG, DEVICE. */
+ * that the library keeps per device (allocated on first use; a call that
+ * needs more space gets a larger one, and earlier ones stay allocated until
+ * the process ends, so a graph captured around an earlier call stays valid).
+ * Two calls that overlap on different streams of one device share it and
+ * race.  Errors: INVALID_ARG, DEVICE. */
 int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
                   float penalty, const atd_controls* controls, int32_t* tok_out,
                   float* margin_out, void* stream);

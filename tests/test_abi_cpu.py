@@ -197,6 +197,61 @@ def test_dry_run_step_argument_checks():
         B.decoder_destroy(h)
 
 
+def test_dry_run_step_slots():
+    """decoder_step_slots: the listed slots (any subset, any order) advance and
+    no other; a bad list is refused before anything changes."""
+    cfg = _cfg()
+    h, fw = _create(cfg)
+    try:
+        for s in range(4):
+            B.kv_bucket_grow(h, s, [0x900000 + 0x1000 * (i + 8 * s) for i in range(2)],
+                             [0xA00000 + 0x1000 * (i + 8 * s) for i in range(2)], 4, 0)
+        B.decoder_step_slots(h, 2, [3, 1], 0x7000, 1, [0], None, 0, None, 0x6000, 0)
+        assert [B.decoder_get_position(h, s)[0] for s in range(4)] == [0, 1, 0, 1]
+        B.decoder_step_slots(h, 3, [1, 0, 3], 0x7000, 1, [0], None, 0, None, 0x6000, 0)
+        assert [B.decoder_get_position(h, s)[0] for s in range(4)] == [1, 2, 0, 2]
+        cases = [
+            ([2, 2], B.ATD_ERR_INVALID_ARG, "appears twice"),
+            ([0, 4], B.ATD_ERR_INVALID_ARG, "slots[1] = 4 outside [0, 4)"),
+            ([-1], B.ATD_ERR_INVALID_ARG, "slots[0] = -1"),
+        ]
+        for slots, code, needle in cases:
+            with pytest.raises(B.AtdError) as ei:
+                B.decoder_step_slots(h, len(slots), slots, 0x7000, 1, [0], None, 0, None,
+                                     0x6000, 0)
+            assert ei.value.code == code and needle in str(ei.value), (slots, ei.value)
+        with pytest.raises(B.AtdError) as ei:
+            B.decoder_step_slots(h, 9, list(range(9)), 0x7000, 1, [0], None, 0, None, 0x6000, 0)
+        assert ei.value.code == B.ATD_ERR_CAPACITY
+        B.decoder_set_position(h, 3, 4, 0)
+        with pytest.raises(B.AtdError) as ei:      # slot 3 full: nothing advances
+            B.decoder_step_slots(h, 2, [2, 3], 0x7000, 1, [0], None, 0, None, 0x6000, 0)
+        assert ei.value.code == B.ATD_ERR_KV_FULL and "slot 3" in str(ei.value)
+        assert [B.decoder_get_position(h, s)[0] for s in range(4)] == [1, 2, 0, 4]
+        rc = B.lib.decoder_step_slots(h, 1, None, 0x7000, 1, B._i32_array([0]), None, 0, None,
+                                      0x6000, 0)
+        assert rc == B.ATD_ERR_INVALID_ARG and "slots is NULL" in B.decoder_last_error(h)
+    finally:
+        B.decoder_destroy(h)
+
+
+def test_workspace_bytes():
+    """atd_workspace_bytes: what decoder_create allocates; grows with the
+    rows, slots and context the decoder is sized for; 0 for a dry run; config
+    errors as decoder_create."""
+    base = dict(flags=0)
+    small = B.atd_workspace_bytes(_cfg(**base), 0)
+    assert small > 0 and small % 256 == 0
+    assert B.atd_workspace_bytes(_cfg(max_rows=64, **base), 0) > small
+    assert B.atd_workspace_bytes(_cfg(max_ctx=4096, **base), 0) > small
+    assert B.atd_workspace_bytes(_cfg(max_slots=64, **base), 0) > small
+    assert B.atd_workspace_bytes(_cfg(input_dim=128, **base), 1) > small
+    assert B.atd_workspace_bytes(_cfg(), 0) == 0
+    with pytest.raises(B.AtdError) as ei:
+        B.atd_workspace_bytes(_cfg(head_dim=96, **base), 0)
+    assert ei.value.code == B.ATD_ERR_UNSUPPORTED
+
+
 def test_greedy_argmax_argument_checks():
     for args, needle in [((0, 1, 10, None, 1.0, 0x100, None, 0), "NULL"),
                          ((0x100, 0, 10, None, 1.0, 0x100, None, 0), "B = 0"),

@@ -11,7 +11,7 @@ from autoregressive_transformer_decode_amd import device as dv
 from autoregressive_transformer_decode_amd import inputs
 from oracle import decoder as od
 from tests._models import oracle_from_weights
-from tests.gpu_util import MARGIN, small_shape
+from tests.gpu_util import GAIN_SD, MARGIN, small_shape
 from tests.test_gpu_sampling import EPS, _seen_mask, _seen_words
 
 pytestmark = pytest.mark.gpu
@@ -81,7 +81,7 @@ def test_generate_controls():
     graph = eager choices bit for bit, and equal to the oracle's controlled
     run up to its first close decision; the stop makes the rest eos."""
     shape = small_shape("gen", 2, 256, 8, 2, 128, 512, 700, "bf16", True, False)
-    mw = inputs.make_weights(shape, seed=7)
+    mw = inputs.make_weights(shape, seed=7, gain_sd=GAIN_SD)
     X0 = inputs.normal(7, 2, 1, (9, 256), scale=1.0)
     om = oracle_from_weights(mw)
     n = 40
@@ -153,8 +153,8 @@ def test_talker_frames_controls():
     c0 stays eos."""
     wl = inputs.WORKLOADS["talker0.6b"]
     n_frames = 8
-    tmw = inputs.make_weights(wl.model, seed=0)
-    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables)
+    tmw = inputs.make_weights(wl.model, seed=0, gain_sd=GAIN_SD)
+    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables, gain_sd=GAIN_SD)
     X0 = inputs.prefill_embeddings(wl, seed=0)
     text = inputs.text_embeddings(wl, seed=0)
     ot = oracle_from_weights(tmw, np.float32)

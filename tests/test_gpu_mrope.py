@@ -15,7 +15,7 @@ from autoregressive_transformer_decode_amd import device as dv
 from autoregressive_transformer_decode_amd import inputs
 from oracle import decoder as od
 from tests._models import oracle_from_weights
-from tests.gpu_util import MARGIN, StepCheck, small_shape
+from tests.gpu_util import GAIN_SD, MARGIN, StepCheck, small_shape
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def test_mrope_prefill_and_steps(kind):
     of 64 + 6 for bf16), then 8 teacher-forced steps at the following text
     positions, against the oracle."""
     shape = _shape(kind)
-    mw = inputs.make_weights(shape, seed=31)
+    mw = inputs.make_weights(shape, seed=31, gain_sd=GAIN_SD)
     X0 = inputs.normal(31, 2, 5, (70, shape.hidden), scale=1.0)
     rp, nxt = grid_positions(10, 6, 8, 12)
     assert rp.shape == (70, 3)
@@ -91,7 +91,7 @@ def test_mrope_batched_step(kind):
     """Three streams with different histories step together, each row with
     its own distinct (t, h, w) (bf16: the MFMA path at B = 3)."""
     shape = _shape(kind)
-    mw = inputs.make_weights(shape, seed=32)
+    mw = inputs.make_weights(shape, seed=32, gain_sd=GAIN_SD)
     om = oracle_from_weights(mw, np.float64)
     dm = dv.DeviceModel(mw)
     dec = dv.Decoder(dm, max_slots=3, max_rows=16, max_ctx=64)
@@ -129,7 +129,7 @@ def test_mrope_equal_positions_bitwise():
     ones' logits bit for bit (prefill of 70 rows, steps of one and of three
     streams); a rotary position beyond max_ctx reads as max_ctx - 1."""
     shape = _shape("bf16")
-    mw = inputs.make_weights(shape, seed=33)
+    mw = inputs.make_weights(shape, seed=33, gain_sd=GAIN_SD)
     dm = dv.DeviceModel(mw)
     X0 = torch.from_numpy(inputs.normal(33, 2, 6, (70, shape.hidden), scale=1.0)).cuda()
     rp = torch.arange(70, dtype=torch.int32, device="cuda").view(70, 1).repeat(1, 3).contiguous()

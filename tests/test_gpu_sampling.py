@@ -21,7 +21,7 @@ from autoregressive_transformer_decode_amd import device as dv
 from autoregressive_transformer_decode_amd import inputs
 from oracle import decoder as od
 from tests._models import oracle_from_weights
-from tests.gpu_util import MARGIN, small_shape
+from tests.gpu_util import GAIN_SD, MARGIN, small_shape
 
 pytestmark = pytest.mark.gpu
 
@@ -146,7 +146,7 @@ def test_generate_sampled():
     sampling settings in a row, so the graph key must hold the settings), and
     follow the oracle's sampled run up to its first close decision."""
     shape = small_shape("gen", 2, 256, 8, 2, 128, 512, 700, "bf16", True, False)
-    mw = inputs.make_weights(shape, seed=7)
+    mw = inputs.make_weights(shape, seed=7, gain_sd=GAIN_SD)
     X0 = inputs.normal(7, 2, 1, (9, 256), scale=1.0)
     n1, n2 = 25, 15
     u = inputs.uniforms(7, 0, n1 + n2 + 1)
@@ -206,8 +206,8 @@ def test_talker06_sampled_frames():
     to its first close decision."""
     wl = inputs.WORKLOADS["talker0.6b"]
     n_frames = 6
-    tmw = inputs.make_weights(wl.model, seed=0)
-    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables)
+    tmw = inputs.make_weights(wl.model, seed=0, gain_sd=GAIN_SD)
+    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables, gain_sd=GAIN_SD)
     X0 = inputs.prefill_embeddings(wl, seed=0)
     text = inputs.text_embeddings(wl, seed=0)
     ut = inputs.uniforms(0, 1, n_frames)

@@ -9,7 +9,7 @@ from autoregressive_transformer_decode_amd import device as dv
 from autoregressive_transformer_decode_amd import inputs
 from oracle import decoder as od
 from tests._models import normwise_rel, oracle_from_weights
-from tests.gpu_util import MARGIN, TOL
+from tests.gpu_util import GAIN_SD, MARGIN, TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -24,11 +24,12 @@ def test_talker06_frames_teacher_forced():
     """0.6B Talker + 5-layer Code Predictor: 64-row prefill, then frames of
     one Code Predictor pass (2-row prefill + 14 steps, head j for group j)
     and one Talker step (16 code embeddings + text embedding, penalty 1.05).
-    Every pass is fed the oracle's codes and compared."""
+    Every pass is fed the oracle's codes and compared, over 20 frames
+    (20 Talker outputs and 300 Code Predictor passes)."""
     wl = inputs.WORKLOADS["talker0.6b"]
-    n_frames = 6
-    tmw = inputs.make_weights(wl.model, seed=0)
-    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables)
+    n_frames = 20
+    tmw = inputs.make_weights(wl.model, seed=0, gain_sd=GAIN_SD)
+    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables, gain_sd=GAIN_SD)
     X0 = inputs.prefill_embeddings(wl, seed=0)
     text = inputs.text_embeddings(wl, seed=0)
     ot = oracle_from_weights(tmw, np.float32)
@@ -91,11 +92,15 @@ def test_talker06_frames_teacher_forced():
 
 
 def test_talker17_prefill_and_steps():
-    """1.7B Talker shape: 512-row prefill then teacher-forced steps; at the
-    end the context is pushed to 2048 rows (the full workload length) and the
-    last step is checked for determinism and normalisation."""
+    """1.7B Talker shape: 512-row prefill, then teacher-forced steps to context
+    2048, the full workload length.  The first four steps (fed the oracle's
+    greedy tokens) are compared, then steps fed a seeded token sequence, and the
+    steps at context 1280 (the workload's mean) and 2048 (its last) are
+    compared with the oracle.  The oracle gets the cache state of those steps
+    from one prefill over all earlier rows (a row's keys and values depend only
+    on the rows before it), then runs the step itself at that position."""
     wl = inputs.WORKLOADS["talker1.7b"]
-    mw = inputs.make_weights(wl.model, seed=0)
+    mw = inputs.make_weights(wl.model, seed=0, gain_sd=GAIN_SD)
     X0 = inputs.prefill_embeddings(wl, seed=0)
     om = oracle_from_weights(mw, np.float32)
     n_check = 4
@@ -103,8 +108,9 @@ def test_talker17_prefill_and_steps():
     dm = dv.DeviceModel(mw)
     dec = dv.Decoder(dm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max)
     dec.grow(0, wl.s_init)
-    y = torch.empty(1, wl.model.hidden, device="cuda")
-    z = torch.empty(1, wl.model.vocab, device="cuda")
+    h, V = wl.model.hidden, wl.model.vocab
+    y = torch.empty(1, h, device="cuda")
+    z = torch.empty(1, V, device="cuda")
     dec.prefill(torch.from_numpy(X0).cuda(), y_out=y[0], logits_out=z[0])
     tok = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
     worst = 0.0
@@ -117,16 +123,32 @@ def test_talker17_prefill_and_steps():
         worst = max(worst, e)
         assert e <= TOL, (k, e)
     print(f"talker1.7b: {n_check} steps after prefill 512, worst {worst:.2e}", flush=True)
-    # run on to context 2048 feeding the GPU's own argmax
-    gt = torch.zeros(1, dtype=torch.int32, device="cuda")
-    while dec.position(0)[0] < wl.s_max - 1:
-        dv.greedy_argmax(z[0], None, 1.0, gt)
-        dec.step(gt.view(1, 1), [0], y_out=y, logits_out=z)
+    # rows 512..515 took the oracle's tokens; rows 516..2047 a seeded sequence
+    p0 = wl.prefill + n_check
+    seq = np.random.default_rng([0, 2, 70_010]).integers(0, V, wl.s_max - p0)
+    fed = [int(ref[k][2]) for k in range(n_check)] + [int(t) for t in seq]
+    checks = (1279, wl.s_max - 1)          # write positions: contexts 1280 and 2048
+    toks_d = torch.tensor(seq, dtype=torch.int32, device="cuda").view(-1, 1)
+    got = {}
+    for i in range(len(seq)):
+        p = p0 + i
+        dec.step(toks_d[i:i + 1], [0], y_out=y, logits_out=z)
+        if p in checks:
+            torch.cuda.synchronize()
+            got[p] = (y[0].cpu().numpy().copy(), z[0].cpu().numpy().copy())
     torch.cuda.synchronize()
-    assert dec.position(0) == (wl.s_max - 1, wl.s_max)
-    yv = y[0].cpu().numpy()
-    assert np.isfinite(z.cpu().numpy()).all()
-    assert abs(np.sqrt(np.mean(yv.astype(np.float64) ** 2)) - 1.0) < 1e-3   # unit gains
+    assert dec.position(0) == (wl.s_max, wl.s_max)
+    E = om.tables[0]
+    rows = np.concatenate([X0, np.stack([E[t] for t in fed])]).astype(np.float32)
+    assert rows.shape[0] == wl.s_max
+    cache = od.Cache(om, wl.s_max)
+    od.prefill(om, cache, rows[:wl.s_max - 1], 0)
+    for p in checks:
+        cache.pos = p
+        yr, zr = od.step(om, cache, rows[p], 0)
+        e = max(normwise_rel(got[p][0], yr), normwise_rel(got[p][1], zr))
+        print(f"talker1.7b: context {p + 1}: normwise error {e:.2e}", flush=True)
+        assert e <= TOL, (p, e)
     dec.close()
 
 
@@ -138,8 +160,10 @@ def test_talker06_native_frame_loop():
     continuation)."""
     wl = inputs.WORKLOADS["talker0.6b"]
     n_frames = 8
-    tmw = inputs.make_weights(wl.model, seed=0)
-    cmw = inputs.make_weights(wl.cp, seed=0, tables=tmw.tables)
+    # weights seed 4: the oracle's free-running loop makes 39 choices before its
+    # first top-2 margin <= 1e-2 (seed 0 only 11), so the comparison spans frames
+    tmw = inputs.make_weights(wl.model, seed=4, gain_sd=GAIN_SD)
+    cmw = inputs.make_weights(wl.cp, seed=4, tables=tmw.tables, gain_sd=GAIN_SD)
     X0 = inputs.prefill_embeddings(wl, seed=0)
     text = inputs.text_embeddings(wl, seed=0)
     ot = oracle_from_weights(tmw, np.float32)
@@ -221,6 +245,6 @@ def test_talker06_native_frame_loop():
         break
     print(f"native frames: {n_frames} frames equal to eager calls; {checked} codes equal to the "
           f"oracle before its first margin <= {MARGIN}", flush=True)
-    assert checked >= 16
+    assert checked >= 32
     tdec.close()
     cdec.close()

@@ -39,6 +39,7 @@ struct atd_decoder {
   float *rcos = nullptr, *rsin = nullptr;  // RoPE rows of an *_mrope call [max_rows, D/2]
   float *x = nullptr, *qkv = nullptr, *q = nullptr, *o = nullptr, *act = nullptr;
   float *pml = nullptr, *pacc = nullptr;
+  int* attn_ticket = nullptr;  // [max_rows, Hkv] ticket counters of the attention
   void** kv_tab = nullptr;
   int *slot_pos = nullptr, *slot_cap = nullptr;
   float* part = nullptr;       // argmax partials [max_rows, nblk, 3]
@@ -316,6 +317,7 @@ AttnArgs attn_args(const atd_decoder* d, RowMap rows, int l, int M, int max_len_
   a.scale = 1.0f / std::sqrt((float)c.head_dim);
   a.pml = d->pml;
   a.pacc = d->pacc;
+  a.ticket = d->attn_ticket;
   a.o = d->o;
   return a;
 }
@@ -715,7 +717,8 @@ hipError_t enqueue_step(atd_decoder* d, int slot0, int B, const int32_t* tok, in
 // Byte offsets of the decoder's device scratch (one allocation) for a config.
 struct ScratchPlan {
   size_t o_cos, o_sin, o_rcos, o_rsin, o_x, o_xin, o_qkv, o_q, o_o, o_act, o_pml, o_pacc, o_kv,
-      o_pos, o_cap, o_part, o_cnt, o_list, o_samp, o_mss = 0, o_mhi = 0, o_mlo = 0, o_mpart = 0;
+      o_pos, o_cap, o_part, o_cnt, o_list, o_ticket, o_samp, o_mss = 0, o_mhi = 0, o_mlo = 0,
+      o_mpart = 0;
   size_t total = 0;
   size_t part_floats = 0;  // attention partials capacity, in floats per head dim
   bool mma = false;
@@ -756,6 +759,7 @@ void plan_scratch(const atd_config& c, bool in_proj, ScratchPlan& p) {
   p.o_part = carve((size_t)R * nblk_v * 3 * 4);
   p.o_cnt = carve(8);
   p.o_list = carve((size_t)R * 4);
+  p.o_ticket = carve((size_t)R * c.n_kv_heads * 4);   // zeroed with the tables above
   const int nblk_s = sample_blocks(c.vocab);
   p.o_samp = carve(nblk_s > 1 ? (size_t)nblk_s * kTopKMax * sizeof(uint2) : 0);
   // MFMA path: hi/lo activations of one 64-row chunk and split-K partials of
@@ -825,7 +829,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
                o_x = sp.o_x, o_xin = sp.o_xin, o_qkv = sp.o_qkv, o_q = sp.o_q, o_o = sp.o_o,
                o_act = sp.o_act, o_pml = sp.o_pml, o_pacc = sp.o_pacc, o_kv = sp.o_kv,
                o_pos = sp.o_pos, o_cap = sp.o_cap, o_part = sp.o_part, o_cnt = sp.o_cnt,
-               o_list = sp.o_list, o_samp = sp.o_samp, o_mss = sp.o_mss, o_mhi = sp.o_mhi,
+               o_list = sp.o_list, o_ticket = sp.o_ticket, o_samp = sp.o_samp,
+               o_mss = sp.o_mss, o_mhi = sp.o_mhi,
                o_mlo = sp.o_mlo, o_mpart = sp.o_mpart;
   const int D = cfg->head_dim;
   const size_t half = D / 2;
@@ -856,6 +861,7 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->part = (float*)(base + o_part);
   d->counter = (int32_t*)(base + o_cnt);
   d->slot_list = (int32_t*)(base + o_list);
+  d->attn_ticket = (int*)(base + o_ticket);
   d->ctl_base = d->counter + 1;
   d->samp = (uint2*)(base + o_samp);
   if (d->mma) {

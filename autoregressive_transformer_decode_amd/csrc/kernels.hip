@@ -650,8 +650,12 @@ __device__ __forceinline__ void split_hi_lo(float v, uint16_t& h, uint16_t& l) {
 // share KV head g.  A key row of D elements is read by LPK lanes with
 // 16-byte loads, so a wave covers KPW keys per load; U key groups are in
 // flight per iteration.  Each lane group keeps an online softmax state
-// (max, sum, weighted V); groups are merged with shuffles in a fixed order and
-// the split's state is written for k_attn_combine.
+// (max, sum, weighted V); groups are merged with shuffles in a fixed order,
+// then the block's four waves through LDS in wave order.  A (row, KV head)
+// with one block writes o there; with several, each block writes its state
+// at the device-coherent level and takes a ticket, and the last block to
+// arrive merges all of them in block order, so the result never depends on
+// the order of arrival (and the combine needs no launch of its own).
 //
 // Fused mode (decode steps): the wave applies the QK norm and RoPE to its raw
 // queries itself, and the wave of the row's last split builds the new k/v
@@ -673,6 +677,49 @@ __device__ __forceinline__ uint4 pack_kv(const float (&v)[VEC]) {
                    __float_as_uint(v[3]));
   }
   return r;
+}
+
+// Attention output of 4 channels at o[off] (or their bf16 hi / lo parts).
+__device__ __forceinline__ void store_o4(const AttnArgs& a, size_t off, float4 v) {
+  if (a.o_hi) {
+    const float f[4] = {v.x, v.y, v.z, v.w};
+    uint16_t hv[4], lv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_hi_lo(f[i], hv[i], lv[i]);
+    *reinterpret_cast<uint2*>(a.o_hi + off) =
+        make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+    *reinterpret_cast<uint2*>(a.o_lo + off) =
+        make_uint2(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
+  } else {
+    *reinterpret_cast<float4*>(a.o + off) = v;
+  }
+}
+
+// Stores and loads at the device-coherent level (relaxed atomics of device
+// scope: they bypass the per-XCD caches), for values one workgroup writes
+// and another, possibly on another XCD, reads within the same kernel.
+__device__ __forceinline__ uint64_t pack2(float x, float y) {
+  return (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+}
+__device__ __forceinline__ void store_coherent2(float* p, float x, float y) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), pack2(x, y), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent4(float* p, float4 v) {
+  store_coherent2(p, v.x, v.y);
+  store_coherent2(p + 2, v.z, v.w);
+}
+__device__ __forceinline__ void load_coherent2(const float* p, float& x, float& y) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  x = __uint_as_float((uint32_t)u);
+  y = __uint_as_float((uint32_t)(u >> 32));
+}
+__device__ __forceinline__ float4 load_coherent4(const float* p) {
+  float4 v;
+  load_coherent2(p, v.x, v.y);
+  load_coherent2(p + 2, v.z, v.w);
+  return v;
 }
 
 template <typename KT, int D, int R, int LPK, int U>
@@ -709,9 +756,14 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   const int len = pos + 1;
   const int chunk = attn_chunk(len, a.M, a.Hkv, a.waves);
   const int k0 = split * chunk;
-  if (k0 >= len) return;
+  // a block whose four splits all start past the row's length has nothing to
+  // do (uniform over the block); a wave of a live block whose split does
+  // still takes part in the block's merge, with an empty state
+  if (blockIdx.x * 4 * chunk >= len) return;
+  if (a.nsplit_max == 1 && k0 >= len) return;   // single split: no merge below
+  const bool has_keys = k0 < len;
   const int k1 = min(len, k0 + chunk);
-  const bool owns_new = a.fused && k1 == len;
+  const bool owns_new = a.fused && has_keys && k1 == len;
   // the cached keys this wave reads: the owner of the new row takes that row
   // from its registers, first, and reads the cache only below it
   const int kend = owns_new ? k1 - 1 : k1;
@@ -786,7 +838,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       }
     }
   };
-  load(k0);
+  if (has_keys) load(k0);
   // the norm and RoPE below wait only for the small loads above
   __builtin_amdgcn_sched_barrier(0);
 
@@ -959,147 +1011,135 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
     }
   }
   if (a.nsplit_max == 1) {
-    // a single split per row and head: its state is the result (the combine
-    // kernel is skipped; acc / l is what it would compute for one split)
+    // a single split per row and head: its state is the result (acc / l)
     if (lane < LPK) {
 #pragma unroll
       for (int j = 0; j < R; ++j) {
         const size_t off = ((size_t)m * a.Hq + g * R + j) * D + dl;
 #pragma unroll
-        for (int e = 0; e < DPL; e += 4) {
-          const float v[4] = {acc[j][e] / ls[j], acc[j][e + 1] / ls[j], acc[j][e + 2] / ls[j],
-                              acc[j][e + 3] / ls[j]};
-          if (a.o_hi) {
-            uint16_t hv[4], lv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) split_hi_lo(v[i], hv[i], lv[i]);
-            *reinterpret_cast<uint2*>(a.o_hi + off + e) =
-                make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
-            *reinterpret_cast<uint2*>(a.o_lo + off + e) =
-                make_uint2(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
-          } else {
-            *reinterpret_cast<float4*>(a.o + off + e) = make_float4(v[0], v[1], v[2], v[3]);
-          }
-        }
+        for (int e = 0; e < DPL; e += 4)
+          store_o4(a, off + e, make_float4(acc[j][e] / ls[j], acc[j][e + 1] / ls[j],
+                                            acc[j][e + 2] / ls[j], acc[j][e + 3] / ls[j]));
       }
     }
     return;
   }
+
+  // the block's four waves merged in LDS, in wave order
+  constexpr int NC = D / 4;           // float4 channel groups of a head
+  constexpr int ITEMS = R * NC;       // (head, channel group) items of the block
+  static_assert(ITEMS <= 256, "one item per thread at most");
+  __shared__ float s_m[4][R], s_l[4][R];
+  __shared__ float4 s_a[4][R][NC];
   if (lane < LPK) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      const size_t base = ((size_t)m * a.Hq + g * R + j) * a.nsplit_max + split;
 #pragma unroll
       for (int e = 0; e < DPL; e += 4)
-        *reinterpret_cast<float4*>(a.pacc + base * D + dl + e) =
-            make_float4(acc[j][e], acc[j][e + 1], acc[j][e + 2], acc[j][e + 3]);
+        s_a[wave][j][(dl + e) / 4] = make_float4(acc[j][e], acc[j][e + 1], acc[j][e + 2], acc[j][e + 3]);
       if (lane == 0) {
-        a.pml[base * 2] = mx[j];
-        a.pml[base * 2 + 1] = ls[j];
+        s_m[wave][j] = mx[j];
+        s_l[wave][j] = ls[j];
       }
     }
   }
-}
-
-// o[m, h*D + d] = sum_s acc_s[d] e^(m_s - M) / sum_s l_s e^(m_s - M).
-// One block per (head, row).  The split weights are formed once in LDS;
-// thread t accumulates the float4 channel group t % (D/4) over splits
-// t / (D/4), t / (D/4) + NSP, ... (independent loads), and the NSP partial
-// sums are added in a fixed order.  PRE partials per thread are loaded
-// together with the position and statistics (all of a row's partials when
-// PRE * NSP covers its splits: one memory round trip instead of several).
-template <int D, int PRE>
-__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  constexpr int NC = D / 4;        // float4 channel groups
-  constexpr int NSP = 256 / NC;    // split phases
-  __shared__ float wgt[kAttnSplitsMax + 1];
-  __shared__ float red[2][4];
-  __shared__ float4 part[NSP][NC];
-  const int h = blockIdx.x, m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t base = ((size_t)m * a.Hq + h) * a.nsplit_max;
-  const int c = tid % NC, sp = tid / NC;
-  const float4* pa = reinterpret_cast<const float4*>(a.pacc) + base * NC + c;
-  // the first partials and statistics are read together with the position
-  // (branch-free: indexes past the split stride re-read its last slot; only
-  // splits below the row's count are used)
-  float4 pre[PRE];
-  const int slast = a.nsplit_max - 1;
-#pragma unroll
-  for (int i = 0; i < PRE; ++i) pre[i] = pa[(size_t)min(sp + i * NSP, slast) * NC];
-  const float m0 = a.pml[(base + min(tid, slast)) * 2];
-  const float l0 = a.pml[(base + min(tid, slast)) * 2 + 1];
-  int slot, pos;
-  row_of(a.rows, a.st, m, slot, pos);
-  const int len = pos + 1;
-  const int chunk = attn_chunk(len, a.M, a.Hkv, a.waves);
-  const int ns = (len + chunk - 1) / chunk;
-  float mloc = tid < ns ? m0 : -1e30f;
-  for (int s = tid + 256; s < ns; s += 256) mloc = fmaxf(mloc, a.pml[(base + s) * 2]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
-  if (lane == 0) red[0][wave] = mloc;
   __syncthreads();
-  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  float lloc = 0.f;
-  if (tid < ns) {
-    const float w = expf(m0 - M);
-    wgt[tid] = w;
-    lloc = l0 * w;
-  }
-  for (int s = tid + 256; s < ns; s += 256) {
-    const float w = expf(a.pml[(base + s) * 2] - M);
-    wgt[s] = w;
-    lloc += a.pml[(base + s) * 2 + 1] * w;
-  }
-  lloc = wave_sum(lloc);
-  if (lane == 0) red[1][wave] = lloc;
-  __syncthreads();
-  const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int ns = (len + chunk - 1) / chunk;   // splits of this row
+  const int nblk = (ns + 3) / 4;              // blocks of this (row, KV head)
+  const int blk = blockIdx.x;
+  const int item = tid % ITEMS, j = item / NC, c = item % NC;
+  const size_t head = (size_t)m * a.Hq + g * R + j;
+  if (tid < ITEMS) {
+    float M = s_m[0][j];
 #pragma unroll
-  for (int i = 0; i < PRE; ++i) {
-    const int s = sp + i * NSP;
-    if (s < ns) {
-      const float w = wgt[s];
-      o.x = fmaf(pre[i].x, w, o.x);
-      o.y = fmaf(pre[i].y, w, o.y);
-      o.z = fmaf(pre[i].z, w, o.z);
-      o.w = fmaf(pre[i].w, w, o.w);
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][j]);
+    float L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float cw = expf(s_m[w][j] - M);
+      L = fmaf(s_l[w][j], cw, L);
+      const float4 v = s_a[w][j][c];
+      A = make_float4(fmaf(v.x, cw, A.x), fmaf(v.y, cw, A.y), fmaf(v.z, cw, A.z), fmaf(v.w, cw, A.w));
     }
-  }
-#pragma unroll 4
-  for (int s = sp + PRE * NSP; s < ns; s += NSP) {
-    const float4 v = pa[(size_t)s * NC];
-    const float w = wgt[s];
-    o.x = fmaf(v.x, w, o.x);
-    o.y = fmaf(v.y, w, o.y);
-    o.z = fmaf(v.z, w, o.z);
-    o.w = fmaf(v.w, w, o.w);
-  }
-  part[sp][c] = o;
-  __syncthreads();
-  if (tid < NC) {
-    float4 r = part[0][c];
-    for (int p = 1; p < NSP; ++p) {
-      r.x += part[p][c].x;
-      r.y += part[p][c].y;
-      r.z += part[p][c].z;
-      r.w += part[p][c].w;
-    }
-    const float v[4] = {r.x / L, r.y / L, r.z / L, r.w / L};
-    if (a.o_hi) {
-      const size_t off = ((size_t)m * a.Hq + h) * D + 4 * c;
-      uint16_t hv[4], lv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) split_hi_lo(v[i], hv[i], lv[i]);
-      *reinterpret_cast<uint2*>(a.o_hi + off) =
-          make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
-      *reinterpret_cast<uint2*>(a.o_lo + off) =
-          make_uint2(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
+    if (nblk == 1) {
+      store_o4(a, head * D + 4 * c, make_float4(A.x / L, A.y / L, A.z / L, A.w / L));
     } else {
-      float4* out = reinterpret_cast<float4*>(a.o + ((size_t)m * a.Hq + h) * D) + c;
-      *out = make_float4(v[0], v[1], v[2], v[3]);
+      // the block's partial, written through to the device-coherent level so
+      // that the block that merges them (on any XCD) reads the values stored
+      const size_t pb = head * a.nsplit_max + blk;
+      store_coherent4(a.pacc + pb * D + 4 * c, A);
+      if (c == 0) store_coherent2(a.pml + pb * 2, M, L);
     }
+  }
+  if (nblk == 1) return;
+  // ticket of this (row, KV head): the block that arrives last merges every
+  // block's partial, in block order (the result does not depend on which
+  // block arrives last)
+  __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores are complete
+  __shared__ int s_last;
+  __syncthreads();
+  if (tid == 0) {
+    int* t = a.ticket + (size_t)m * a.Hkv + g;
+    const int old = __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == nblk - 1;
+    if (last) __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // P phases per item: phase p merges blocks p, p + P, ... (online, in order),
+  // then the phases are merged in order
+  constexpr int P = 256 / ITEMS;
+  __shared__ float s_pm[P][ITEMS], s_pl[P][ITEMS];
+  __shared__ float4 s_pa[P][ITEMS];
+  const int ph = tid / ITEMS;
+  if (ph < P) {
+    float M = -1e30f, L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    // a batch of partials is loaded together (one memory round trip), then
+    // merged in order; indexes past the last block re-read it and are skipped
+    constexpr int NB = 8;
+    for (int b0 = ph; b0 < nblk; b0 += NB * P) {
+      float bm[NB], bl[NB];
+      float4 v[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const size_t pb = head * a.nsplit_max + min(b0 + i * P, nblk - 1);
+        load_coherent2(a.pml + pb * 2, bm[i], bl[i]);
+        v[i] = load_coherent4(a.pacc + pb * D + 4 * c);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (b0 + i * P < nblk) {
+          const float nm = fmaxf(M, bm[i]);
+          const float ca = expf(M - nm), cb = expf(bm[i] - nm);
+          L = L * ca + bl[i] * cb;
+          A = make_float4(A.x * ca + v[i].x * cb, A.y * ca + v[i].y * cb,
+                          A.z * ca + v[i].z * cb, A.w * ca + v[i].w * cb);
+          M = nm;
+        }
+      }
+    }
+    s_pm[ph][item] = M;
+    s_pl[ph][item] = L;
+    s_pa[ph][item] = A;
+  }
+  __syncthreads();
+  if (tid < ITEMS) {
+    float M = s_pm[0][item];
+#pragma unroll
+    for (int q = 1; q < P; ++q) M = fmaxf(M, s_pm[q][item]);
+    float L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      const float cq = expf(s_pm[q][item] - M);
+      L = fmaf(s_pl[q][item], cq, L);
+      const float4 v = s_pa[q][item];
+      A = make_float4(fmaf(v.x, cq, A.x), fmaf(v.y, cq, A.y), fmaf(v.z, cq, A.z), fmaf(v.w, cq, A.w));
+    }
+    store_o4(a, head * D + 4 * c, make_float4(A.x / L, A.y / L, A.z / L, A.w / L));
   }
 }
 
@@ -2656,17 +2696,6 @@ hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream
       attn_dispatch_r<float, 64>(a, r, grid, s);
     else
       attn_dispatch_r<float, 128>(a, r, grid, s);
-  }
-  if (a.nsplit_max == 1) return hipGetLastError();   // the split kernel wrote o
-  dim3 cgrid(a.Hq, a.M);
-  // all partials up front when 4 per thread do not cover the split stride
-  const bool deep = a.nsplit_max > 4 * (256 / (D / 4));
-  if (D == 64) {
-    if (deep) hipLaunchKernelGGL((k_attn_combine<64, 16>), cgrid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_combine<64, 4>), cgrid, dim3(256), 0, s, a);
-  } else {
-    if (deep) hipLaunchKernelGGL((k_attn_combine<128, 16>), cgrid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_combine<128, 4>), cgrid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -40,7 +40,7 @@ EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
            "decoder_step", "decoder_step_slots", "atd_workspace_bytes", "decoder_prefill_mrope", "decoder_step_mrope", "decoder_embed", "greedy_argmax", "sample_topk", "decoder_generate",
            "talker_generate_frames", "quantize_blocks", "codec_conv1d_causal",
-           "codec_transconv1d_pack", "codec_transconv1d", "decoder_time_stage")
+           "codec_transconv1d_pack", "codec_transconv1d", "decoder_time_stage", "atd_read_stream")
 
 ATD_STAGE_QKV, ATD_STAGE_ROPE, ATD_STAGE_ATTN, ATD_STAGE_OPROJ, ATD_STAGE_GATEUP, \
     ATD_STAGE_DOWN, ATD_STAGE_HEAD = range(7)
@@ -128,6 +128,7 @@ def _load():
         "codec_transconv1d_pack": ([vp, i32, i32, i32, vp, vp], C.c_int),
         "codec_transconv1d": ([vp, vp, vp, i32, i32, i32, i32, vp, vp], C.c_int),
         "decoder_time_stage": ([vp, i32, i32, i32, i32, vp, C.POINTER(C.c_double)], C.c_int),
+        "atd_read_stream": ([vp, C.c_size_t, i32, vp, vp, C.POINTER(C.c_double)], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -287,4 +288,10 @@ def decoder_time_stage(handle: int, stage: int, slot0: int, B: int, reps: int,
                        stream: int) -> float:
     us = C.c_double(0.0)
     _check(lib.decoder_time_stage(handle, stage, slot0, B, reps, stream, C.byref(us)), handle)
+    return us.value
+
+
+def atd_read_stream(buf: int, nbytes: int, reps: int, sink: int, stream: int) -> float:
+    us = C.c_double(0.0)
+    _check(lib.atd_read_stream(buf, nbytes, reps, sink, stream, C.byref(us)))
     return us.value

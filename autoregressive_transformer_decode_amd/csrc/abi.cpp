@@ -1799,6 +1799,34 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
   return ATD_OK;
 }
 
+// ---------------------------------------------------------------- read-stream bandwidth
+
+extern "C" int atd_read_stream(const void* buf, size_t bytes, int32_t reps, uint32_t* sink,
+                               void* stream, double* us_per_read) {
+  if (!buf || !sink || !us_per_read)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "buf, sink or us_per_read is NULL");
+  if (!aligned16(buf)) return fail(nullptr, ATD_ERR_INVALID_ARG, "buf %p not 16-byte aligned", buf);
+  if (bytes < 16 || bytes % 16)
+    return fail(nullptr, ATD_ERR_INVALID_ARG, "bytes %zu not a positive multiple of 16", bytes);
+  if (reps < 1) return fail(nullptr, ATD_ERR_INVALID_ARG, "reps %d < 1", reps);
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = launch_read_stream(buf, bytes, sink, s);   // warm-up pass
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch_read_stream(buf, bytes, sink, s);
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "atd_read_stream");
+  *us_per_read = (double)ms * 1e3 / reps;
+  return ATD_OK;
+}
+
 // ---------------------------------------------------------------- stage timing
 
 extern "C" int decoder_time_stage(atd_decoder* d, int32_t stage, int32_t slot0, int32_t B,

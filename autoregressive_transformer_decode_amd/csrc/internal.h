@@ -367,6 +367,8 @@ hipError_t launch_record_tokens(const int32_t* src, int n, int32_t* out, int32_t
 // dst[i] = src[i], i < n
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+// one full read of `bytes` (a multiple of 16) at buf, 16-byte loads
+hipError_t launch_read_stream(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // The same product over 128 x 128 output tiles (calls of more than one row
 // tile: prefill chunks); same arguments and partials layout.

@@ -8,9 +8,12 @@ norm, LM head, penalized greedy argmax feeding the next step) on synthetic
 seeded weights and inputs already resident in HBM.  The default workload is
 the 1.7B Talker shape at batch 1: a 512-row prefill (untimed), then K greedy
 steps replayed from a HIP graph on the device (K = 1536 runs the context to
-2048).  The same run then times the batched workload on the same weights (64
-streams, seeded cache lengths in [256, 4096], bf16 cache, 32 iterations of
-one step per stream) and reports it under "batch64".  Prints one JSON line.
+2048; with fewer steps, untimed steps first move the context so that the
+timed ones sit around the workload's mean context, 1280, and config.context
+names the timed range).  The same run then times the batched workload on the
+same weights (64 streams, seeded cache lengths in [256, 4096], bf16 cache, 32
+iterations of one step per stream) and reports it under "batch64", with its
+own CPU oracle baseline.  Prints one JSON line.
 
 Also measured in the same run:
   roofline      the dominant kernel (RMSNorm + gate/up + SwiGLU GEMV): its
@@ -21,6 +24,9 @@ Also measured in the same run:
                 rocprofv3 counter summary when it matches the kernel source.
   cpu_baseline  the CPU oracle on this host's cores, on a bounded sample of
                 the same workload (decode steps after the same prefill).
+  hbm_attainable  the device's attainable read bandwidth: the library's
+                streaming read kernel over 4 GiB (past the 256 MB memory-side
+                cache); step_hbm.frac_of_attainable is the step against it.
   sampled       the same K steps with the Qwen TTS sampling defaults (top-k
                 50, temperature 0.9, top-p 1, repetition penalty 1.05) drawn
                 on the device by sample_topk inside the step graph.
@@ -144,6 +150,52 @@ def cpu_baseline(mw, X0, s_init, budget_s, max_steps):
                        f"prefill untimed")
 
 
+def cpu_baseline_batched(mw, wl, budget_s):
+    """The oracle (float32, as it stands) on the batched workload: streams in a
+    seeded order, each with its synthetic cache (the seeded bf16 window of
+    every layer, upcast to float32 outside the timing) stepped twice, as two
+    iterations (the first from its input row, the second from its greedy
+    token), until the time budget is spent.  Streams are independent, so
+    tokens/s over the sampled stream-steps is the rate of whole iterations."""
+    import numpy as np
+    from autoregressive_transformer_decode_amd import inputs
+    from oracle import decoder as od
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    s = wl.model
+    om = oracle_model(mw, np.float32)
+    lens = inputs.batched_lengths(wl, seed=0)
+    X1 = inputs.batched_first_inputs(wl, seed=0)
+    pools = [inputs.batched_kv_pool(s, l, seed=0) for l in range(s.n_layers)]
+    order = np.random.default_rng(1).permutation(wl.batch)
+    spent, n_tok, used = 0.0, 0, []
+    for b in order:
+        b, n = int(b), int(lens[b])
+        cache = od.Cache(om, n + 2)
+        for l in range(s.n_layers):
+            k, v = inputs.batched_kv(s, b, n, l, pool=pools[l])
+            cache.K[l][:, :n] = inputs.bf16_bits_to_f32(k)
+            cache.V[l][:, :n] = inputs.bf16_bits_to_f32(v)
+        cache.pos = n
+        t0 = time.perf_counter()
+        _, z = od.step(om, cache, X1[b].astype(np.float32), 0)
+        _, z = od.step(om, cache, om.tables[0][int(np.argmax(z))], 0)
+        spent += time.perf_counter() - t0
+        n_tok += 2
+        used.append(b)
+        del cache
+        if spent > budget_s and len(used) >= 2:
+            break
+    return dict(value=n_tok / spent, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{len(used)} of {wl.batch} streams (cache lengths "
+                       f"{int(lens[used].min())}..{int(lens[used].max())}), two steps each as "
+                       f"two iterations, float32 numpy; caches upcast from the seeded bf16 "
+                       f"pool outside the timing; {spent:.1f} s timed")
+
+
 def _source_hash(starts) -> str:
     with open(KERNEL_SRC) as f:
         src = f.read()
@@ -175,6 +227,22 @@ def traffic_per_launch(path=None, hashfn=None):
     return t.get("bytes_per_launch")
 
 
+def read_stream_gbs(nbytes=4 << 30, reps=5):
+    """Attainable read bandwidth: the library's streaming read kernel over a
+    4 GiB buffer (well past the 256 MB memory-side cache), mean of `reps`
+    full reads after a warm-up read."""
+    import torch
+    from autoregressive_transformer_decode_amd import binding as B
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    us = B.atd_read_stream(buf.data_ptr(), nbytes, reps, sink.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    del buf
+    torch.cuda.empty_cache()
+    return dict(gbs=nbytes / (us / 1e6) / 1e9, bytes=nbytes, us_per_read=us, reads=reps,
+                kernel="k_read_stream (grid-stride 16-byte loads, 4096 workgroups)")
+
+
 def bench_lm(args, wl):
     import numpy as np
     import torch
@@ -194,10 +262,14 @@ def bench_lm(args, wl):
     W = args.warmup
     if P0 + max(K, W) > wl.s_max:
         raise SystemExit(f"--steps/--warmup beyond the {wl.s_max}-row context of {wl.name}")
+    # fewer timed steps than the workload's: fast-forward (untimed) so that the
+    # timed steps sit around the workload's mean context ((P0 + 1 + s_max) / 2)
+    skip = max(0, int(round((P0 + 1 + wl.s_max) / 2.0 - P0 - (K + 1) / 2.0)))
+    skip = min(skip, wl.s_max - P0 - max(K, W))
     # bucket ladder: the cache doubles before a write at its capacity (ASR report's
     # dynamic window); the buckets are allocated up front, outside the timing
     caps = [wl.s_init]
-    while caps[-1] < P0 + max(K, W):
+    while caps[-1] < P0 + skip + max(K, W):
         caps.append(min(2 * caps[-1], wl.s_max))
     buckets = [dec.alloc_kv(c) for c in caps]
     dec.grow(0, caps[0], kv=buckets[0])
@@ -208,13 +280,13 @@ def bench_lm(args, wl):
     tok = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     seen = torch.zeros(dv.seen_words(s.vocab), dtype=torch.int32, device="cuda")
-    uni = torch.from_numpy(inputs.uniforms(0, 0, P0 + max(K, W) + 1)).cuda()
+    uni = torch.from_numpy(inputs.uniforms(0, 0, skip + max(K, W) + 1)).cuda()
 
     def schedule(n, sampled=False):
-        """Rewind to the first bucket, prefill (untimed), then n steps from the
-        step graph (greedy, or the sampling defaults with the penalty),
-        growing the bucket where the context reaches it; returns the seconds
-        of the decode loop."""
+        """Rewind to the first bucket, prefill (untimed), `skip` untimed steps,
+        then n timed steps from the step graph (greedy, or the sampling
+        defaults with the penalty), growing the bucket where the context
+        reaches it; returns the seconds of the timed steps."""
         dec, buckets = cur["dec"], cur["buckets"]
         dec.set_position(0, 0)
         if dec.position(0)[1] != caps[0]:
@@ -225,22 +297,30 @@ def bench_lm(args, wl):
             dv.sample_topk(z, seen, SAMPLING_PENALTY, dv.Sampling(*SAMPLING, uni[0:1]), tok)
         else:
             dv.greedy_argmax(z, None, 1.0, tok)
+        state = dict(done=0, b=0)
+
+        def run(n_steps):
+            end = state["done"] + n_steps
+            while state["done"] < end:
+                done = state["done"]
+                pos, cap = dec.position(0)
+                if pos >= cap:
+                    state["b"] += 1
+                    dec.grow(0, caps[state["b"]], kv=buckets[state["b"]])
+                    continue
+                k = min(end - done, cap - pos)
+                if sampled:
+                    dec.generate(k, tok, y_out=y, logits_out=z, seen=seen,
+                                 penalty=SAMPLING_PENALTY,
+                                 sampling=dv.Sampling(*SAMPLING, uni[1 + done:1 + done + k]))
+                else:
+                    dec.generate(k, tok, y_out=y, logits_out=z)
+                state["done"] = done + k
+
+        run(skip)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        done, b = 0, 0
-        while done < n:
-            pos, cap = dec.position(0)
-            if pos >= cap:
-                b += 1
-                dec.grow(0, caps[b], kv=buckets[b])
-                continue
-            k = min(n - done, cap - pos)
-            if sampled:
-                dec.generate(k, tok, y_out=y, logits_out=z, seen=seen, penalty=SAMPLING_PENALTY,
-                             sampling=dv.Sampling(*SAMPLING, uni[1 + done:1 + done + k]))
-            else:
-                dec.generate(k, tok, y_out=y, logits_out=z)
-            done += k
+        run(n)
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
@@ -263,7 +343,8 @@ def bench_lm(args, wl):
     pf_flops = 2.0 * P0 * weight_elems_layers(s) + 2.0 * s.hidden * s.vocab + \
         2.0 * 2 * s.n_layers * s.n_q_heads * s.head_dim * (P0 * (P0 + 1) / 2)
     dt = schedule(K)
-    log(f"timed {K} steps: {dt * 1e3:.1f} ms (buckets {caps})")
+    log(f"timed {K} steps (context {P0 + skip + 1}..{P0 + skip + K}): {dt * 1e3:.1f} ms "
+        f"(buckets {caps})")
     # the same run with the sampling defaults (graphs captured by a warmup)
     dt_s = None
     if not args.no_sampled:
@@ -318,14 +399,16 @@ def bench_lm(args, wl):
     achieved = per_launch / avg_s / 1e9
     traffic = traffic_per_launch()
 
-    mean_ctx = P0 + (K + 1) / 2.0
+    attainable = read_stream_gbs()
+    mean_ctx = P0 + skip + (K + 1) / 2.0
     step_bytes = weight_bytes(s) + kv_row_bytes(s) * mean_ctx
     ms_step = dt * 1e3 / K
     out = dict(
         metric=METRIC, value=K / dt, unit="tokens/s", n_gpus=1, steps=K, warmup=W,
         ms_per_step=ms_step, higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="bf16" if s.dtype == "bf16" else "f32", data="synthetic",
-        config=dict(workload=wl.name, batch=1, prefill=P0, context=[P0 + 1, P0 + K],
+        config=dict(workload=wl.name, batch=1, prefill=P0,
+                    context=[P0 + skip + 1, P0 + skip + K],
                     layers=s.n_layers, hidden=s.hidden, heads=[s.n_q_heads, s.n_kv_heads],
                     head_dim=s.head_dim, ffn=s.ffn, vocab=s.vocab,
                     step="graph-replayed decode step + greedy argmax on device",
@@ -336,7 +419,9 @@ def bench_lm(args, wl):
                       bytes_per_launch=per_launch, avg_launch_us=avg_s * 1e6,
                       launches_timed=launches),
         step_hbm=dict(algorithmic_bytes=step_bytes, achieved_gbs=step_bytes / (ms_step / 1e3) / 1e9,
-                      frac=step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS),
+                      frac=step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+                      frac_of_attainable=step_bytes / (ms_step / 1e3) / 1e9 / attainable["gbs"]),
+        hbm_attainable=attainable,
         sampled=None if dt_s is None else dict(
             value=K / dt_s, unit="tokens/s", ms_per_step=dt_s * 1e3 / K,
             settings=dict(zip(("top_k", "temperature", "top_p"), SAMPLING),
@@ -384,7 +469,7 @@ def bench_lm(args, wl):
     same_stack = dataclasses.replace(bwl.model, name=s.name, kv_dtype=s.kv_dtype) == s
     if not args.no_batched and same_stack:
         log("batched64 ...")
-        out["batch64"] = bench_batched(args, bwl, dm=dm, steps=bwl.steps, warmup=4)
+        out["batch64"] = bench_batched(args, bwl, dm=dm, mw=mw, steps=bwl.steps, warmup=4)
     del dm
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
@@ -406,7 +491,7 @@ def attn_stage_bytes(shape, lens) -> int:
     return int(sum(int(l) for l in lens)) * per_row + B * per_row + B * (qkv + shape.q_dim) * 4
 
 
-def bench_batched(args, wl, dm=None, steps=None, warmup=None):
+def bench_batched(args, wl, dm=None, mw=None, steps=None, warmup=None):
     """The batched workload: 64 streams, one decode step each per iteration,
     seeded cache lengths, tokens fed back by the on-device greedy argmax."""
     import numpy as np
@@ -419,8 +504,10 @@ def bench_batched(args, wl, dm=None, steps=None, warmup=None):
     Bn = wl.batch
     K = steps if steps is not None else wl.steps
     W = warmup if warmup is not None else 4
+    if mw is None:
+        mw = inputs.make_weights(s, seed=0)
     if dm is None:
-        dm = dv.DeviceModel(inputs.make_weights(s, seed=0))
+        dm = dv.DeviceModel(mw)
     lens = inputs.batched_lengths(wl, seed=0)
     X1 = torch.from_numpy(inputs.batched_first_inputs(wl, seed=0)).cuda()
     dec = dv.Decoder(dm, max_slots=Bn, max_rows=Bn, max_ctx=wl.s_max, kv_dtype=s.kv_dtype)
@@ -470,7 +557,12 @@ def bench_batched(args, wl, dm=None, steps=None, warmup=None):
     mean_ctx = float(lens.mean()) + (K + 1) / 2.0
     step_bytes = weight_bytes(s) + kv_row_bytes(s) * mean_ctx * Bn
     ms_it = dt * 1e3 / K
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("batched cpu baseline (oracle) ...")
+        cpu = cpu_baseline_batched(mw, wl, args.cpu_seconds)
     return dict(
+        cpu_baseline=cpu,
         value=Bn * K / dt, unit="tokens/s", streams=Bn, iterations=K, warmup=W,
         ms_per_iteration=ms_it,
         config=dict(workload=wl.name, batch=Bn, kv_lengths=[int(lens.min()), int(lens.max())],
@@ -480,7 +572,7 @@ def bench_batched(args, wl, dm=None, steps=None, warmup=None):
                       frac=a_gbs / HBM_PEAK_GBS,
                       traffic=traffic_per_launch(ATTN_TRAFFIC_FILE, attn_kernel_hash),
                       traffic_kernel="k_attn_split (counters of the split kernel alone)",
-                      kernel="attention stage (k_attn_split + k_attn_combine), 64 rows",
+                      kernel="attention stage (k_attn_split, combine inside), 64 rows",
                       bytes_per_launch=a_bytes, avg_launch_us=st["attention"],
                       launches_timed=reps * s.n_layers),
         gemm_gate_up=dict(us=st["gate_up"], tflops=gu_flops / (st["gate_up"] / 1e6) / 1e12,
@@ -837,7 +929,7 @@ def main():
                    scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
                    config=r["config"], roofline=r["roofline"], gemm_gate_up=r["gemm_gate_up"],
                    stage_us_per_layer=r["stage_us_per_layer"], step_hbm=r["step_hbm"],
-                   cpu_baseline=None)
+                   cpu_baseline=r["cpu_baseline"])
     else:
         out = bench_lm(args, wl)
     print(json.dumps(out), flush=True)

@@ -547,6 +547,19 @@ enum {
 int decoder_time_stage(atd_decoder* dec, int32_t stage, int32_t slot0, int32_t B,
                        int32_t reps, void* stream, double* us_per_layer);
 
+/* Measurement: the attainable read bandwidth of this device ("Rockchip NPU
+ * sidecars" page: a DRAM-bound decode is judged against a measured read
+ * ceiling, taken over a working set larger than the caches).  Reads the
+ * `bytes` at buf (device, 16-byte aligned, a multiple of 16; pass more than
+ * the 256 MB memory-side cache) once as a warm-up and then `reps` times with
+ * a grid-stride streaming kernel of 16-byte loads, between two HIP events on
+ * `stream`, and returns the mean microseconds of one read (bytes / that time
+ * is the attainable bandwidth).  sink: device uint32 scratch the kernel may
+ * write (its value means nothing).  Waits for the stream.  Errors:
+ * INVALID_ARG, DEVICE. */
+int atd_read_stream(const void* buf, size_t bytes, int32_t reps, uint32_t* sink, void* stream,
+                    double* us_per_read);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,7 +38,7 @@ STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "SHAPE", -3: "DTYPE", -4: "KV_FU
 
 EXPORTS = ("decoder_create", "decoder_destroy", "decoder_last_error", "kv_bucket_grow",
            "decoder_set_position", "decoder_get_position", "decoder_prefill",
-           "decoder_step", "decoder_step_slots", "atd_workspace_bytes", "decoder_prefill_mrope", "decoder_step_mrope", "decoder_embed", "greedy_argmax", "sample_topk", "decoder_generate",
+           "decoder_step", "decoder_step_slots", "atd_workspace_bytes", "decoder_prefill_mrope", "decoder_step_mrope", "decoder_embed", "greedy_argmax", "greedy_argmax_noalloc", "sample_topk", "decoder_generate",
            "talker_generate_frames", "quantize_blocks", "codec_conv1d_causal",
            "codec_transconv1d_pack", "codec_transconv1d", "decoder_time_stage", "atd_read_stream")
 
@@ -115,6 +115,8 @@ def _load():
                                C.c_int),
         "decoder_embed": ([vp, i32, vp, i32, C.POINTER(i32), vp, vp, vp], C.c_int),
         "greedy_argmax": ([vp, i32, i32, vp, f32, C.POINTER(atd_controls), vp, vp, vp], C.c_int),
+        "greedy_argmax_noalloc": ([vp, i32, i32, vp, f32, C.POINTER(atd_controls), vp, vp, vp],
+                                  C.c_int),
         "sample_topk": ([vp, i32, i32, vp, f32, C.POINTER(atd_sampling), C.POINTER(atd_controls),
                          vp, vp], C.c_int),
         "decoder_generate": ([vp, i32, i32, vp, i32, C.POINTER(i32), vp, i32, vp, f32,
@@ -233,6 +235,12 @@ def greedy_argmax(logits: int, B: int, V: int, seen, penalty: float, tok_out: in
                   stream: int, controls=None) -> None:
     _check(lib.greedy_argmax(logits, B, V, seen, penalty, _byref(controls), tok_out, margin_out,
                              stream))
+
+
+def greedy_argmax_noalloc(logits: int, B: int, V: int, seen, penalty: float, tok_out: int,
+                          margin_out, stream: int, controls=None) -> None:
+    _check(lib.greedy_argmax_noalloc(logits, B, V, seen, penalty, _byref(controls), tok_out,
+                                     margin_out, stream))
 
 
 def _byref(st):

@@ -1281,9 +1281,11 @@ void key_controls(std::vector<int64_t>& key, const atd_controls* c) {
 }
 }  // namespace
 
-extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
-                             float penalty, const atd_controls* controls, int32_t* tok_out,
-                             float* margin_out, void* stream) {
+namespace {
+// Checks and arguments of a greedy_argmax call (partials not yet assigned).
+int argmax_args(const float* logits, int32_t B, int32_t V, uint32_t* seen, float penalty,
+                const atd_controls* controls, int32_t* tok_out, float* margin_out,
+                ArgmaxArgs& a) {
   if (!logits || !tok_out) return fail(nullptr, ATD_ERR_INVALID_ARG, "logits or tok_out is NULL");
   if (B < 1) return fail(nullptr, ATD_ERR_INVALID_ARG, "B = %d < 1", B);
   if (V < 2) return fail(nullptr, ATD_ERR_INVALID_ARG, "V = %d < 2", V);
@@ -1294,7 +1296,7 @@ extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t
     const int rc = check_controls(nullptr, controls, V);
     if (rc) return rc;
   }
-  ArgmaxArgs a{};
+  a = ArgmaxArgs{};
   a.ctl = choice_ctl(controls, nullptr, nullptr);
   a.z = logits;
   a.B = B;
@@ -1305,12 +1307,41 @@ extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t
   a.tok = tok_out;
   a.margin = margin_out;
   a.nblk = (V + kArgmaxChunk - 1) / kArgmaxChunk;
+  return ATD_OK;
+}
+}  // namespace
+
+extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
+                             float penalty, const atd_controls* controls, int32_t* tok_out,
+                             float* margin_out, void* stream) {
+  ArgmaxArgs a;
+  int rc = argmax_args(logits, B, V, seen, penalty, controls, tok_out, margin_out, a);
+  if (rc) return rc;
   void* p = nullptr;
-  const int rc = choice_scratch((size_t)B * a.nblk * 3 * sizeof(float), &p);
+  rc = choice_scratch((size_t)B * a.nblk * 3 * sizeof(float), &p);
   if (rc) return rc;
   a.part = (float*)p;
   hipError_t e = launch_argmax(a, (hipStream_t)stream);
   return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "greedy_argmax");
+}
+
+extern "C" int greedy_argmax_noalloc(const float* logits, int32_t B, int32_t V, uint32_t* seen,
+                                     float penalty, const atd_controls* controls,
+                                     int32_t* tok_out, float* margin_out, void* stream) {
+  ArgmaxArgs a;
+  const int rc = argmax_args(logits, B, V, seen, penalty, controls, tok_out, margin_out, a);
+  if (rc) return rc;
+  const size_t need = (size_t)B * a.nblk * 3;
+  if (need > kNoAllocScratchFloats)
+    return fail(nullptr, ATD_ERR_CAPACITY,
+                "B = %d rows of V = %d need %zu floats of partials, beyond the fixed %zu", B, V,
+                need, kNoAllocScratchFloats);
+  float* p = nullptr;
+  hipError_t e = noalloc_scratch(&p);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "greedy_argmax_noalloc scratch address");
+  a.part = p;
+  e = launch_argmax(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATD_OK : hip_fail(nullptr, e, "greedy_argmax_noalloc");
 }
 
 extern "C" int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* seen,

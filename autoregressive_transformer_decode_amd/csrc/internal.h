@@ -359,6 +359,12 @@ hipError_t launch_set_slot(const SlotTables& st, int slot, void* const* k, void*
                            int cap, int pos, int set_ptrs, hipStream_t s);
 hipError_t launch_kv_copy(const KvCopyArgs& a, hipStream_t s);
 hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s);
+// Allocation-free token choice: the argmax partials of greedy_argmax_noalloc
+// live in a fixed device array of kNoAllocScratchFloats floats (one per GPU);
+// its address on the current device (taken once per device) goes to *out.
+constexpr size_t kNoAllocScratchFloats = size_t(1) << 16;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(float** out);
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
 hipError_t launch_record_token(const int32_t* tok, int32_t* out, int32_t* counter, hipStream_t s);
 // out[*counter * n + i] = src[i] for i < n (out may be null), then ++*counter; n <= 64

@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace atd {
@@ -2801,6 +2803,31 @@ hipError_t launch_argmax(const ArgmaxArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_argmax_part, dim3(a.nblk, a.B), dim3(256), 0, s, a);
   if (a.nblk > 1) hipLaunchKernelGGL(k_argmax_final, dim3(a.B), dim3(64), 0, s, a);
   return hipGetLastError();
+}
+
+// Partials of greedy_argmax_noalloc: a file-scope device array, so the call
+// needs no allocation (each GPU the library runs on holds its own copy until
+// the process ends).  In host code `scratch` only stands for the symbol; the
+// array's address on a device is taken once with hipGetSymbolAddress while
+// that device is current, and only that address is handed to kernels.
+static __device__ __align__(256) float scratch[kNoAllocScratchFloats];
+
+hipError_t noalloc_scratch(float** out) {
+  static std::mutex mu;
+  static float* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<float*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s) {

@@ -389,6 +389,20 @@ int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
                   float penalty, const atd_controls* controls, int32_t* tok_out,
                   float* margin_out, void* stream);
 
+/* greedy_argmax for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as greedy_argmax (bit for bit), but its per-row
+ * partials live in a fixed device array of the library (256 KB on each GPU
+ * it runs on, held until the process ends) instead of a buffer allocated on
+ * first use: the call allocates nothing.  B * ceil(V / 4096) * 3 may not
+ * exceed 65536 (e.g. 574 rows of a 151936-token vocabulary), else
+ * ATD_ERR_CAPACITY.  Every call on one GPU shares that array and it keeps
+ * the last call's partials: calls that overlap on one GPU (on different
+ * streams) race.  Errors: as greedy_argmax, and CAPACITY. */
+int greedy_argmax_noalloc(const float* logits, int32_t B, int32_t V, uint32_t* seen,
+                          float penalty, const atd_controls* controls, int32_t* tok_out,
+                          float* margin_out, void* stream);
+
 /* Sampled token per row (the draw of atd_sampling; qwen3-tts-hip log,
  * device-sampler entry).  logits device [B, V] float32; seen and penalty as
  * in greedy_argmax (the chosen token's bit is set); row b draws

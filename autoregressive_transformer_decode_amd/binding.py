@@ -16,7 +16,9 @@ import os
 import torch  # noqa: F401  (imported for its HIP runtime)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libatd.so")
+# ATD_LIBRARY names another build of the same library (e.g. the host-sanitized
+# one that build.py makes with --sanitize); the default is the in-tree build.
+LIB_PATH = os.environ.get("ATD_LIBRARY") or os.path.join(HERE, "libatd.so")
 
 ATD_OK = 0
 ATD_ERR_INVALID_ARG = -1

@@ -65,7 +65,8 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
     lib = ASAN_LIB if sanitize else LIB
     out_tmp = lib + ".tmp"
     link = ["-shared-libsan", *SANITIZE_FLAGS] if sanitize else []
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link, "-o", out_tmp, *objs]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *link, "-o", out_tmp, *objs,
+           "-ldl"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

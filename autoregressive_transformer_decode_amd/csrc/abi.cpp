@@ -1,12 +1,14 @@
 // C-ABI entry points: host-side validation, decoder state and the launch
 // sequence of a step.  Every check runs before any HIP call, so a refused
 // call leaves the decoder unchanged and touches no device.
+#include <dlfcn.h>
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -70,6 +72,40 @@ struct atd_decoder {
 namespace {
 
 thread_local std::string g_err;
+
+// ROCTx ranges around the enqueue of each entry point (and each layer of a
+// step), for timelines: on only when ATD_ROCTX=1.  The ROCTx library is
+// opened on first use, so a default build depends on nothing beyond HIP.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+const Roctx& roctx() {
+  static Roctx r;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const char* on = getenv("ATD_ROCTX");
+    if (!on || strcmp(on, "1") != 0) return;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_GLOBAL);
+    if (!h) h = dlopen("libroctx64.so", RTLD_NOW | RTLD_GLOBAL);
+    if (!h) return;
+    r.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    r.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (!r.push || !r.pop) r = Roctx{};
+  });
+  return r;
+}
+struct Range {
+  bool on;
+  explicit Range(const char* name) : on(roctx().push != nullptr) {
+    if (on) roctx().push(name);
+  }
+  ~Range() {
+    if (on) roctx().pop();
+  }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
 
 int fail(atd_decoder* d, int code, const char* fmt, ...) {
   char buf[512];
@@ -362,6 +398,7 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
   const bool fused = rows.mode == kRowsStep;
   hipError_t e = hipSuccess;
   for (int l = 0; l < c.n_layers; ++l) {
+    const Range range("layer");
     const atd_layer_weights& W = d->layers[l];
     GemvArgs g{};
     g.W[0] = W.wq;
@@ -543,6 +580,7 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
   hipError_t e = hipSuccess;
   STAGE(ATD_STAGE_QKV, mma_residual(d, 0, M, x, (const float*)d->layers[0].attn_norm, s));
   for (int l = 0; l < c.n_layers; ++l) {
+    const Range range("layer");
     const atd_layer_weights& W = d->layers[l];
     const float* next_gain =
         l + 1 < c.n_layers ? (const float*)d->layers[l + 1].attn_norm : d->final_norm;
@@ -929,6 +967,7 @@ extern "C" const char* decoder_last_error(const atd_decoder* d) {
 
 extern "C" int kv_bucket_grow(atd_decoder* d, int32_t slot, void* const* k_new,
                               void* const* v_new, int32_t s_new, void* stream) {
+  const Range range("kv_bucket_grow");
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
   const atd_config& c = d->cfg;
   if (slot < 0 || slot >= c.max_slots)
@@ -1012,6 +1051,7 @@ extern "C" int decoder_get_position(const atd_decoder* d, int32_t slot, int32_t*
 extern "C" int decoder_embed(atd_decoder* d, int32_t B, const int32_t* tok, int32_t G,
                              const int32_t* table_ids, const float* extra, float* x_out,
                              void* stream) {
+  const Range range("decoder_embed");
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
   if (B < 1 || B > d->cfg.max_rows)
     return fail(d, ATD_ERR_CAPACITY, "B = %d outside [1, max_rows %d]", B, d->cfg.max_rows);
@@ -1129,6 +1169,7 @@ int step_impl(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* slots,
 
 extern "C" int decoder_prefill(atd_decoder* d, int32_t slot, const float* x, int32_t T,
                                int32_t head, float* y_out, float* logits_out, void* stream) {
+  const Range range("decoder_prefill");
   return prefill_impl(d, slot, x, T, nullptr, head, y_out, logits_out, stream,
                       "decoder_prefill");
 }
@@ -1136,6 +1177,7 @@ extern "C" int decoder_prefill(atd_decoder* d, int32_t slot, const float* x, int
 extern "C" int decoder_prefill_mrope(atd_decoder* d, int32_t slot, const float* x, int32_t T,
                                      const int32_t* rope_pos, int32_t head, float* y_out,
                                      float* logits_out, void* stream) {
+  const Range range("decoder_prefill_mrope");
   if (!rope_pos) return fail(d, ATD_ERR_INVALID_ARG, "rope_pos is NULL");
   return prefill_impl(d, slot, x, T, rope_pos, head, y_out, logits_out, stream,
                       "decoder_prefill_mrope");
@@ -1144,6 +1186,7 @@ extern "C" int decoder_prefill_mrope(atd_decoder* d, int32_t slot, const float* 
 extern "C" int decoder_step(atd_decoder* d, int32_t slot0, int32_t B, const int32_t* tok,
                             int32_t G, const int32_t* table_ids, const float* extra,
                             int32_t head, float* y_out, float* logits_out, void* stream) {
+  const Range range("decoder_step");
   return step_impl(d, slot0, B, nullptr, tok, G, table_ids, extra, nullptr, head, y_out,
                    logits_out, stream, "decoder_step");
 }
@@ -1152,6 +1195,7 @@ extern "C" int decoder_step_slots(atd_decoder* d, int32_t B, const int32_t* slot
                                   const int32_t* tok, int32_t G, const int32_t* table_ids,
                                   const float* extra, int32_t head, float* y_out,
                                   float* logits_out, void* stream) {
+  const Range range("decoder_step_slots");
   if (!slots) return fail(d, ATD_ERR_INVALID_ARG, "slots is NULL");
   return step_impl(d, 0, B, slots, tok, G, table_ids, extra, nullptr, head, y_out, logits_out,
                    stream, "decoder_step_slots");
@@ -1161,6 +1205,7 @@ extern "C" int decoder_step_mrope(atd_decoder* d, int32_t slot0, int32_t B, cons
                                   int32_t G, const int32_t* table_ids, const float* extra,
                                   const int32_t* rope_pos, int32_t head, float* y_out,
                                   float* logits_out, void* stream) {
+  const Range range("decoder_step_mrope");
   if (!rope_pos) return fail(d, ATD_ERR_INVALID_ARG, "rope_pos is NULL");
   return step_impl(d, slot0, B, nullptr, tok, G, table_ids, extra, rope_pos, head, y_out,
                    logits_out, stream, "decoder_step_mrope");
@@ -1314,6 +1359,7 @@ int argmax_args(const float* logits, int32_t B, int32_t V, uint32_t* seen, float
 extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t* seen,
                              float penalty, const atd_controls* controls, int32_t* tok_out,
                              float* margin_out, void* stream) {
+  const Range range("greedy_argmax");
   ArgmaxArgs a;
   int rc = argmax_args(logits, B, V, seen, penalty, controls, tok_out, margin_out, a);
   if (rc) return rc;
@@ -1328,6 +1374,7 @@ extern "C" int greedy_argmax(const float* logits, int32_t B, int32_t V, uint32_t
 extern "C" int greedy_argmax_noalloc(const float* logits, int32_t B, int32_t V, uint32_t* seen,
                                      float penalty, const atd_controls* controls,
                                      int32_t* tok_out, float* margin_out, void* stream) {
+  const Range range("greedy_argmax_noalloc");
   ArgmaxArgs a;
   const int rc = argmax_args(logits, B, V, seen, penalty, controls, tok_out, margin_out, a);
   if (rc) return rc;
@@ -1347,6 +1394,7 @@ extern "C" int greedy_argmax_noalloc(const float* logits, int32_t B, int32_t V, 
 extern "C" int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* seen,
                            float penalty, const atd_sampling* sampling,
                            const atd_controls* controls, int32_t* tok_out, void* stream) {
+  const Range range("sample_topk");
   if (!logits || !tok_out || !sampling)
     return fail(nullptr, ATD_ERR_INVALID_ARG, "logits, sampling or tok_out is NULL");
   if (B < 1) return fail(nullptr, ATD_ERR_INVALID_ARG, "B = %d < 1", B);
@@ -1373,6 +1421,7 @@ extern "C" int sample_topk(const float* logits, int32_t B, int32_t V, uint32_t* 
 
 extern "C" int quantize_blocks(const void* w, int32_t dtype, int64_t rows, int32_t cols,
                                int32_t format, void* codes, uint16_t* scales, void* stream) {
+  const Range range("quantize_blocks");
   if (!w || !codes || !scales)
     return fail(nullptr, ATD_ERR_INVALID_ARG, "w, codes or scales is NULL");
   if (!aligned16(w) || !aligned16(codes) || ((uintptr_t)scales & 1))
@@ -1416,6 +1465,7 @@ bool too_big(int64_t a, int64_t b) { return a * b >= ((int64_t)1 << 31); }
 extern "C" int codec_conv1d_causal(const float* x, const float* w, const float* bias,
                                    int32_t cin, int32_t cout, int32_t T, int32_t K,
                                    int32_t dilation, int32_t accumulate, float* y, void* stream) {
+  const Range range("codec_conv1d_causal");
   int rc = check_conv_ptrs(x, w, y);
   if (rc) return rc;
   if (bias && ((uintptr_t)bias & 3))
@@ -1445,6 +1495,7 @@ extern "C" int codec_conv1d_causal(const float* x, const float* w, const float* 
 
 extern "C" int codec_transconv1d_pack(const float* w, int32_t cin, int32_t cout, int32_t stride,
                                       float* packed, void* stream) {
+  const Range range("codec_transconv1d_pack");
   int rc = check_conv_ptrs(w, packed, packed);
   if (rc) return rc;
   if (cin < 1 || cout < 1 || stride < 1)
@@ -1459,6 +1510,7 @@ extern "C" int codec_transconv1d_pack(const float* w, int32_t cin, int32_t cout,
 extern "C" int codec_transconv1d(const float* x, const float* packed, const float* bias,
                                  int32_t cin, int32_t cout, int32_t T, int32_t stride, float* y,
                                  void* stream) {
+  const Range range("codec_transconv1d");
   int rc = check_conv_ptrs(x, packed, y);
   if (rc) return rc;
   if (bias && ((uintptr_t)bias & 3))
@@ -1567,6 +1619,7 @@ extern "C" int decoder_generate(atd_decoder* d, int32_t slot, int32_t n_steps, i
                                 const atd_sampling* sampling, const atd_controls* controls,
                                 int32_t* tokens_out, float* y_out, float* logits_out,
                                 void* stream) {
+  const Range range("decoder_generate");
   if (!d) return fail(nullptr, ATD_ERR_INVALID_ARG, "decoder is NULL");
   const atd_config& c = d->cfg;
   if (slot < 0 || slot >= c.max_slots)
@@ -1720,6 +1773,7 @@ extern "C" int talker_generate_frames(atd_decoder* tk, int32_t tk_slot, atd_deco
                                       const atd_sampling* cp_sampling,
                                       const atd_controls* tk_controls, int32_t* codes_out,
                                       float* tk_logits, float* cp_logits, void* stream) {
+  const Range range("talker_generate_frames");
   if (!tk) return fail(nullptr, ATD_ERR_INVALID_ARG, "Talker decoder is NULL");
   if (!cp || cp == tk) return fail(tk, ATD_ERR_INVALID_ARG, "Code Predictor decoder is NULL or the Talker's");
   const atd_config &tc = tk->cfg, &cc = cp->cfg;

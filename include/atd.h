@@ -43,6 +43,9 @@
  *    the KV cache in atd_config.kv_dtype (float32 or bf16 each); arithmetic
  *    accumulates in float32.
  *  - A decoder is used from one host thread at a time.
+ *  - With the environment variable ATD_ROCTX=1, each entry point's enqueue
+ *    (and each layer of a step) is wrapped in a ROCTx range named after it,
+ *    for timelines (rocprofv3 --marker-trace); off otherwise.
  */
 #ifndef ATD_H
 #define ATD_H

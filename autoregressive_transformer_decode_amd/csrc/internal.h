@@ -153,7 +153,7 @@ struct AttnArgs {
   float* pml;         // [M, Hq, nsplit_max, 2] running max and sum of each block
   float* pacc;        // [M, Hq, nsplit_max, D] (block b of a row at index b)
   int* ticket;        // [M, Hkv] arrivals of a row's blocks (zero between launches)
-  float* o;           // [M, Hq * D] (combine output)
+  float* o;           // [M, Hq * D] attention output
   uint16_t* o_hi;     // or, when set, bf16 hi/lo parts of o: [M, Hq * D]
   uint16_t* o_lo;
 };

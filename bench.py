@@ -58,6 +58,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "autoregressive_transformer_decode_amd", "csrc", "kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemv_talker1.7b_traffic.json")
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_split_batched64_traffic.json")
+GEMM_COUNTER_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_counters.json")
 QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemv_{}_talker1.7b_traffic.json")
 
 
@@ -212,6 +213,31 @@ def attn_kernel_hash() -> str:
     """Hash of the split-K attention kernel's source and its launch shape."""
     return _source_hash(("template <typename KT, int D, int R, int LPK, int U>",
                          "static void attn_dispatch_r(", "hipError_t launch_attention("))
+
+
+def gemm_kernel_hash() -> str:
+    """Hash of the two matrix-core GEMM kernels' sources."""
+    return _source_hash(("template <int P, int NCH>\n__global__ __launch_bounds__(256) void k_gemm(",
+                         "template <int NST>\n__global__ __launch_bounds__(256) void k_gemm_tile("))
+
+
+def gemm_counters(role, rows):
+    """Matrix-core counters of one GEMM from the committed summary (busy share
+    of the launch, fetched bytes over weight bytes), or None when the GEMM
+    kernels changed since the counters were taken."""
+    try:
+        with open(GEMM_COUNTER_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != gemm_kernel_hash():
+        return None
+    for r in t.get("kernels", []):
+        if r["role"] == role and r["rows"] == rows:
+            return dict(kernel=r["kernel"], mfma_busy_frac=r["mfma_busy_over_duration"],
+                        fetch_over_weights=r["fetch_mib"] / r["weight_mib"],
+                        lds_bank_conflicts=r["lds_bank_conflicts"])
+    return None
 
 
 def traffic_per_launch(path=None, hashfn=None):
@@ -429,7 +455,7 @@ def bench_lm(args, wl):
         token_choice_us=None if args.no_sampled else time_choice(s.vocab),
         mrope=mrope,
         prefill=dict(rows=P0, ms=pf * 1e3, tokens_per_s=P0 / pf, tflops=pf_flops / pf / 1e12,
-                     mfma_peak_tflops=2500.0,
+                     mfma_peak_tflops=2500.0, gate_up_counters=gemm_counters("gate/up", P0),
                      note="bf16 MFMA with float32 activations as bf16 hi + lo operands (two "
                           "products per weight); rows layer by layer in chunks of up to 512, "
                           "GEMMs over 128 x 128 output tiles (64-row tiles where those leave "
@@ -577,7 +603,8 @@ def bench_batched(args, wl, dm=None, mw=None, steps=None, warmup=None):
                       launches_timed=reps * s.n_layers),
         gemm_gate_up=dict(us=st["gate_up"], tflops=gu_flops / (st["gate_up"] / 1e6) / 1e12,
                           mfma_peak_tflops=2500.0,
-                          weight_gbs=gu_w / (st["gate_up"] / 1e6) / 1e9),
+                          weight_gbs=gu_w / (st["gate_up"] / 1e6) / 1e9,
+                          counters=gemm_counters("gate/up", Bn)),
         stage_us_per_layer=st,
         step_hbm=dict(algorithmic_bytes=step_bytes,
                       achieved_gbs=step_bytes / (ms_it / 1e3) / 1e9,

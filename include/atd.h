@@ -538,9 +538,9 @@ int codec_transconv1d(const float* x, const float* packed, const float* bias, in
 enum {
   ATD_STAGE_QKV = 0,     /* RMSNorm + q/k/v projection                       */
   ATD_STAGE_ROPE = 1,    /* QK norm + RoPE + cache append of a prefill block  */
-  ATD_STAGE_ATTN = 2,    /* split-K attention + combine (for decode steps it
-                            also applies the QK norm + RoPE and appends the
-                            new cache row)                                   */
+  ATD_STAGE_ATTN = 2,    /* split-K attention, its splits merged in the same
+                            launch (for decode steps it also applies the QK
+                            norm + RoPE and appends the new cache row)       */
   ATD_STAGE_OPROJ = 3,   /* output projection + residual                      */
   ATD_STAGE_GATEUP = 4,  /* RMSNorm + gate/up projection + SwiGLU             */
   ATD_STAGE_DOWN = 5,    /* down projection + residual                        */

@@ -51,6 +51,15 @@ struct atd_decoder {
   int mma_rows = 0;            // most rows of one MFMA chunk (multiple of kMmaRows)
   float* mss = nullptr;        // row sums of squares [mma_rows, ceil(h / kSsCols)]
   uint16_t *mhi = nullptr, *mlo = nullptr;  // GEMM input as bf16 hi/lo [mma_rows, Kmax]
+  // second hi/lo pair of a <= 64-row chunk [kMmaRows, Kmax]: a GEMM whose
+  // epilogue writes the next input reads the other pair
+  uint16_t *mhi2 = nullptr, *mlo2 = nullptr;
+  int* mticket = nullptr;      // [max column tiles] tickets of the decode GEMMs
+  // the MFMA decode path's copy of the weights in B-operand order (one
+  // allocation, made at decoder_create): per layer q/k/v, o, gate/up
+  // interleaved, down; per head
+  void* bmem = nullptr;
+  std::vector<const uint16_t*> bq_sw, bo_sw, bgu_sw, bdown_sw, bhead_sw;
   int32_t* slot_list = nullptr;  // device [max_rows]: slots of a decoder_step_slots call
   std::vector<int32_t> step_slots;  // host copy of that list while its call enqueues
   int32_t* counter = nullptr;  // token counter of decoder_generate
@@ -548,14 +557,44 @@ ReduceArgs mma_red(atd_decoder* d, int N, int ks, int M, float* out, int ldo) {
 // x += splits (ks = 0: none), then x * gain as the next GEMM's hi/lo input
 // and the row sums of squares for its norm factor
 hipError_t mma_residual(atd_decoder* d, int ks, int M, float* x, const float* gain,
-                        hipStream_t s) {
+                        hipStream_t s, int frag = 0) {
   const int h = d->cfg.hidden;
   ReduceArgs r = mma_red(d, h, ks, M, x, h);
+  r.frag = frag;
   r.ss = d->mss;
   r.gain = gain;
   r.hi = d->mhi;
   r.lo = d->mlo;
   return launch_reduce(r, kRedResidual, s);
+}
+
+// GEMM of a chunk of <= kMmaRows rows with its reduction and epilogue in
+// one launch (k_gemm_dec): input hi / lo (64 x K, fragment order), an
+// [N, K] weight in B-operand order (wb, made at decoder_create; kDecSwiglu:
+// gate and up interleaved), bias segments ending at e0, e1, N; the
+// epilogue's own fields of `g` are set by the caller.
+hipError_t dec_gemm(atd_decoder* d, DecGemmArgs g, const uint16_t* hi, const uint16_t* lo,
+                    const uint16_t* wb, int e0, int e1, int N, int K, int M, int epi,
+                    hipStream_t s) {
+  g.hi = hi;
+  g.lo = lo;
+  g.Wb = wb;
+  g.nblk = (int)bfrag_blocks(N, epi == kDecSwiglu);
+  g.seg_end[0] = e0;
+  g.seg_end[1] = e1;
+  g.seg_end[2] = N;
+  g.K = K;
+  g.N = N;
+  g.M = M;
+  g.cb = dec_cb(epi, K);
+  g.kc = dec_kc(dec_tiles(N, epi, K), K);
+  g.ks = (K + g.kc - 1) / g.kc;
+  g.part = d->mpart;
+  g.ticket = d->mticket;
+  g.hn = d->cfg.hidden;
+  g.eps = d->cfg.rms_eps;
+  g.nss_in = (d->cfg.hidden + kSsCols - 1) / kSsCols;
+  return launch_gemm_dec(g, epi, s);
 }
 
 // LM-head outputs of a call's rows (row 0 of the span the pointers address).
@@ -566,10 +605,12 @@ struct HeadOut {
 };
 
 // MFMA path for one chunk of 3..kMmaRows rows: every layer, then (if asked)
-// the final norm and LM head.  Kernel chain per layer: GEMM q/k/v of x*g ->
-// norm factor + bias -> attention (split + combine, o as hi/lo) -> GEMM o ->
-// residual (+ x*g as hi/lo, sums of squares) -> GEMM gate/up -> norm factor
-// + SwiGLU (as hi/lo) -> GEMM down -> residual (+ x*g for the next norm).
+// the final norm and LM head.  Steps per layer: GEMM q/k/v of x*g, norm
+// factor + bias -> attention (o as hi/lo) -> GEMM o, residual (+ x*g as
+// hi/lo, sums of squares) -> GEMM gate/up, norm factor + SwiGLU (as hi/lo) ->
+// GEMM down, residual (+ x*g for the next norm).  A chunk of one row tile
+// (decode streams, short prefills) takes each step in one launch (k_gemm_dec);
+// larger chunks run each GEMM's reduction as a launch of its own.
 hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
                          const HeadOut* ho, hipStream_t s) {
   const atd_config& c = d->cfg;
@@ -578,8 +619,62 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
   const int kv_bf16 = c.kv_dtype == ATD_BF16;
   const bool fused = rows.mode == kRowsStep;
   hipError_t e = hipSuccess;
-  STAGE(ATD_STAGE_QKV, mma_residual(d, 0, M, x, (const float*)d->layers[0].attn_norm, s));
-  for (int l = 0; l < c.n_layers; ++l) {
+  // one row tile: GEMMs with the reduction and epilogue in the same launch,
+  // the hi / lo input (in MFMA-fragment order) alternating between two
+  // buffers (a GEMM's epilogue writes the next GEMM's input while its other
+  // workgroups still read)
+  const bool one_tile = M <= kMmaRows;
+  STAGE(ATD_STAGE_QKV,
+        mma_residual(d, 0, M, x, (const float*)d->layers[0].attn_norm, s, one_tile ? 1 : 0));
+  for (int l = 0; l < c.n_layers && one_tile; ++l) {
+    const Range range("layer");
+    const atd_layer_weights& W = d->layers[l];
+    const float* next_gain =
+        l + 1 < c.n_layers ? (const float*)d->layers[l + 1].attn_norm : d->final_norm;
+    DecGemmArgs gq{};
+    gq.out = d->qkv;
+    gq.ldo = nqkv;
+    gq.bias[0] = (const float*)W.bq;
+    gq.bias[1] = (const float*)W.bk;
+    gq.bias[2] = (const float*)W.bv;
+    gq.ss_in = d->mss;
+    STAGE(ATD_STAGE_QKV, dec_gemm(d, gq, d->mhi, d->mlo, d->bq_sw[l], nq, nq + nkv, nqkv, h,
+                                  M, kDecStore, s));
+    if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
+    AttnArgs aa = attn_args(d, rows, l, M, max_len_bound, fused);
+    aa.o_hi = d->mhi2;
+    aa.o_lo = d->mlo2;
+    aa.o_frag = 1;
+    if (fused)
+      STAGE(ATD_STAGE_ATTN, attention(d, aa, s));
+    else
+      STAGE(ATD_STAGE_ATTN, launch_attn_prefill(aa, kv_bf16, D, Hq / Hkv, s));
+    DecGemmArgs go{};
+    go.out = x;
+    go.ldo = h;
+    go.ohi = d->mhi;
+    go.olo = d->mlo;
+    go.gain = (const float*)W.mlp_norm;
+    go.ss_out = d->mss;
+    STAGE(ATD_STAGE_OPROJ, dec_gemm(d, go, d->mhi2, d->mlo2, d->bo_sw[l], h, h, h, nq, M,
+                                    kDecResidual, s));
+    DecGemmArgs gg{};
+    gg.ohi = d->mhi2;
+    gg.olo = d->mlo2;
+    gg.ss_in = d->mss;
+    STAGE(ATD_STAGE_GATEUP, dec_gemm(d, gg, d->mhi, d->mlo, d->bgu_sw[l], 2 * F, 2 * F, 2 * F,
+                                     h, M, kDecSwiglu, s));
+    DecGemmArgs gd{};
+    gd.out = x;
+    gd.ldo = h;
+    gd.ohi = d->mhi;
+    gd.olo = d->mlo;
+    gd.gain = next_gain;
+    gd.ss_out = d->mss;
+    STAGE(ATD_STAGE_DOWN, dec_gemm(d, gd, d->mhi2, d->mlo2, d->bdown_sw[l], h, h, h,
+                                   F, M, kDecResidual, s));
+  }
+  for (int l = 0; l < c.n_layers && !one_tile; ++l) {
     const Range range("layer");
     const atd_layer_weights& W = d->layers[l];
     const float* next_gain =
@@ -614,7 +709,20 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
     STAGE(ATD_STAGE_DOWN, mma_gemm(d, W.w_down, W.w_down, W.w_down, h, h, h, F, M, s));
     STAGE(ATD_STAGE_DOWN, mma_residual(d, mma_splits(h, F, M), M, x, next_gain, s));
   }
-  if (ho) {
+  if (ho && one_tile) {
+    // split partials of the head from the fragment-order input, then the
+    // norm factor (and y_out) in the reduction
+    DecGemmArgs gh{};
+    STAGE(ATD_STAGE_HEAD, dec_gemm(d, gh, d->mhi, d->mlo, d->bhead_sw[ho->head], c.vocab,
+                                   c.vocab, c.vocab, h, M, kDecParts, s));
+    const int kch = dec_kc(dec_tiles(c.vocab, kDecParts, h), h);
+    ReduceArgs rh = mma_red(d, c.vocab, (h + kch - 1) / kch, M, ho->logits, c.vocab);
+    rh.ss = d->mss;
+    rh.x = x;
+    rh.gain = d->final_norm;
+    rh.y_out = ho->y_out;
+    STAGE(ATD_STAGE_HEAD, launch_reduce(rh, kRedStore, s));
+  } else if (ho) {
     const void* Wh = d->heads[ho->head];
     STAGE(ATD_STAGE_HEAD, mma_gemm(d, Wh, Wh, Wh, c.vocab, c.vocab, c.vocab, h, M, s));
     ReduceArgs rh = mma_red(d, c.vocab, mma_splits(c.vocab, h, M), M, ho->logits, c.vocab);
@@ -756,7 +864,8 @@ hipError_t enqueue_step(atd_decoder* d, int slot0, int B, const int32_t* tok, in
 struct ScratchPlan {
   size_t o_cos, o_sin, o_rcos, o_rsin, o_x, o_xin, o_qkv, o_q, o_o, o_act, o_pml, o_pacc, o_kv,
       o_pos, o_cap, o_part, o_cnt, o_list, o_ticket, o_samp, o_mss = 0, o_mhi = 0, o_mlo = 0,
-      o_mpart = 0;
+      o_mpart = 0, o_mhi2 = 0, o_mlo2 = 0, o_mticket = 0, o_bw = 0;
+  size_t bw_layer = 0, bw_head = 0;   // elements of one layer's / head's B-order copy
   size_t total = 0;
   size_t part_floats = 0;  // attention partials capacity, in floats per head dim
   bool mma = false;
@@ -786,10 +895,23 @@ void plan_scratch(const atd_config& c, bool in_proj, ScratchPlan& p) {
   p.o_act = carve((size_t)R * c.ffn * 4);
   // attention partials: M * Hq * attn_max_splits(L, M, Hkv) <= this many per head dim
   p.part_floats = (size_t)c.n_q_heads *
-                  std::min((size_t)R * ((c.max_ctx + kAttnMinChunk - 1) / kAttnMinChunk),
-                           (size_t)(kAttnWavesMax / c.n_kv_heads + R));
+                  std::max(std::min((size_t)R * ((c.max_ctx + kAttnMinChunk - 1) / kAttnMinChunk),
+                                    (size_t)(kAttnWavesMax / c.n_kv_heads + R)),
+                           (size_t)R * attn_max_splits(c.max_ctx, R, c.n_kv_heads, 0));
   p.o_pml = carve(p.part_floats * 2 * 4);
   p.o_pacc = carve(p.part_floats * D * 4);
+  // MFMA path (bf16 dense weights, chunks of >= 3 rows possible)
+  p.mma = c.dtype == ATD_BF16 && c.weight_format == ATD_WFMT_DENSE &&
+          !(c.flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 && nq % 32 == 0 && c.ffn % 32 == 0 &&
+          std::max(R, S) >= 3;
+  if (p.mma) {
+    // the decode GEMMs' weights in B-operand order: q/k/v, o, gate/up, down
+    // per layer, then the heads (filled at creation, outside the zeroed part)
+    p.bw_layer = (bfrag_blocks(nqkv, false) * h + bfrag_blocks(h, false) * nq +
+                  bfrag_blocks(2 * c.ffn, true) * h + bfrag_blocks(h, false) * c.ffn) * 16;
+    p.bw_head = bfrag_blocks(c.vocab, false) * h * 16;
+    p.o_bw = carve((p.bw_layer * c.n_layers + p.bw_head * c.n_lm_heads) * 2);
+  }
   p.o_kv = carve((size_t)S * c.n_layers * 2 * sizeof(void*));
   p.o_pos = carve((size_t)S * 4);
   p.o_cap = carve((size_t)S * 4);
@@ -802,9 +924,6 @@ void plan_scratch(const atd_config& c, bool in_proj, ScratchPlan& p) {
   p.o_samp = carve(nblk_s > 1 ? (size_t)nblk_s * kTopKMax * sizeof(uint2) : 0);
   // MFMA path: hi/lo activations of one 64-row chunk and split-K partials of
   // the largest GEMM (q/k/v, o, gate/up, down, LM head)
-  p.mma = c.dtype == ATD_BF16 && c.weight_format == ATD_WFMT_DENSE &&
-          !(c.flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 && nq % 32 == 0 && c.ffn % 32 == 0 &&
-          std::max(R, S) >= 3;
   if (p.mma) {
     // chunks of up to kMmaPrefillRows rows (row tiles of kMmaRows)
     p.mma_rows = std::max(kMmaRows, (std::min(R, kMmaPrefillRows) + kMmaRows - 1) / kMmaRows *
@@ -816,11 +935,25 @@ void plan_scratch(const atd_config& c, bool in_proj, ScratchPlan& p) {
       pmax = std::max({pmax, parts(nqkv, h), parts(h, nq), parts(2 * c.ffn, h),
                        parts(h, c.ffn), parts(c.vocab, h)});
     }
+    // the decode GEMMs (one row tile): per-split 64 x 64 tiles of each GEMM
+    auto dparts = [](int n, int k, int epi) {
+      const int t = dec_tiles(n, epi, k), kc = dec_kc(t, k);
+      return (size_t)t * ((k + kc - 1) / kc) * kMmaRows * 16 * dec_cb(epi, k);
+    };
+    pmax = std::max({pmax, dparts(nqkv, h, kDecStore), dparts(h, nq, kDecResidual),
+                     dparts(2 * c.ffn, h, kDecSwiglu), dparts(h, c.ffn, kDecResidual),
+                     dparts(c.vocab, h, kDecParts)});
     p.o_mss = carve((size_t)p.mma_rows * ((h + kSsCols - 1) / kSsCols) * 4);
     const size_t kmax = std::max({(size_t)h, (size_t)nq, (size_t)c.ffn});
     p.o_mhi = carve((size_t)p.mma_rows * kmax * 2);
     p.o_mlo = carve((size_t)p.mma_rows * kmax * 2);
     p.o_mpart = carve(pmax * 4);
+    p.o_mhi2 = carve((size_t)kMmaRows * kmax * 2);
+    p.o_mlo2 = carve((size_t)kMmaRows * kmax * 2);
+    const int tmax = std::max({dec_tiles(nqkv, kDecStore, h), dec_tiles(h, kDecResidual, nq),
+                               dec_tiles(h, kDecResidual, c.ffn),
+                               dec_tiles(2 * c.ffn, kDecSwiglu, h)});
+    p.o_mticket = carve((size_t)tmax * 4);   // zeroed with the rest
   }
   p.total = off;
 }
@@ -869,7 +1002,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
                o_pos = sp.o_pos, o_cap = sp.o_cap, o_part = sp.o_part, o_cnt = sp.o_cnt,
                o_list = sp.o_list, o_ticket = sp.o_ticket, o_samp = sp.o_samp,
                o_mss = sp.o_mss, o_mhi = sp.o_mhi,
-               o_mlo = sp.o_mlo, o_mpart = sp.o_mpart;
+               o_mlo = sp.o_mlo, o_mpart = sp.o_mpart, o_mhi2 = sp.o_mhi2,
+               o_mlo2 = sp.o_mlo2, o_mticket = sp.o_mticket;
   const int D = cfg->head_dim;
   const size_t half = D / 2;
 
@@ -907,6 +1041,9 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
     d->mhi = (uint16_t*)(base + o_mhi);
     d->mlo = (uint16_t*)(base + o_mlo);
     d->mpart = (float*)(base + o_mpart);
+    d->mhi2 = (uint16_t*)(base + o_mhi2);
+    d->mlo2 = (uint16_t*)(base + o_mlo2);
+    d->mticket = (int*)(base + o_mticket);
   }
 
   // RoPE table: phi = p * theta^(-2i/D) in double, cos/sin rounded to float.
@@ -921,6 +1058,39 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   e = hipMemcpy(d->cos_t, ct.data(), ct.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(d->sin_t, sn.data(), sn.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemset(base + o_kv, 0, off - o_kv);
+  if (e == hipSuccess && d->mma) {
+    // the decode GEMMs' weights in B-operand order
+    const int h = cfg->hidden, nq = cfg->n_q_heads * D, nkv = cfg->n_kv_heads * D;
+    const int nqkv = nq + 2 * nkv, F = cfg->ffn;
+    uint16_t* bw = (uint16_t*)(base + sp.o_bw);
+    auto swz = [&](const void* a0, const void* a1, const void* a2, int e0, int e1, int N, int K,
+                   bool sw) {
+      SwizzleArgs z{};
+      z.src[0] = (const uint16_t*)a0;
+      z.src[1] = (const uint16_t*)a1;
+      z.src[2] = (const uint16_t*)a2;
+      z.seg_end[0] = e0;
+      z.seg_end[1] = e1;
+      z.seg_end[2] = N;
+      z.N = N;
+      z.K = K;
+      z.swiglu = sw;
+      z.dst = bw;
+      bw += bfrag_blocks(N, sw) * (size_t)K * 16;
+      if (e == hipSuccess) e = launch_swizzle_b(z, nullptr);
+      return (const uint16_t*)z.dst;
+    };
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      const atd_layer_weights& W = d->layers[l];
+      d->bq_sw.push_back(swz(W.wq, W.wk, W.wv, nq, nq + nkv, nqkv, h, false));
+      d->bo_sw.push_back(swz(W.wo, W.wo, W.wo, h, h, h, nq, false));
+      d->bgu_sw.push_back(swz(W.w_gate, W.w_up, W.w_up, 2 * F, 2 * F, 2 * F, h, true));
+      d->bdown_sw.push_back(swz(W.w_down, W.w_down, W.w_down, h, h, h, F, false));
+    }
+    for (int j = 0; j < cfg->n_lm_heads; ++j)
+      d->bhead_sw.push_back(swz(d->heads[j], d->heads[j], d->heads[j], cfg->vocab, cfg->vocab,
+                                cfg->vocab, h, false));
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     rc = hip_fail(nullptr, e, "decoder scratch initialisation");

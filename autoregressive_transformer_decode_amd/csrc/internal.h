@@ -24,16 +24,25 @@ constexpr int kAttnMinChunk = 16;     // fewest keys per split
 #endif
 
 // Keys per attention split for a row whose valid length is len, in a launch
-// of M rows over Hkv KV heads aiming at `waves` splits in total: every row
-// gets the same number of splits (all waves busy), each at least
-// kAttnMinChunk keys, a multiple of 16.  Depends on (len, M, Hkv, waves)
-// only, never on the cache capacity (results do not change when a bucket
-// grows).
+// of M rows over Hkv KV heads.  With a split-count target (waves > 0: few
+// rows) every row gets the same number of splits (all waves busy), each at
+// least kAttnMinChunk keys, a multiple of 16.  Without one (waves = 0: many
+// rows of mixed lengths) every split takes kAttnRowChunk keys (more only past
+// kAttnSplitsMax splits), so that the splits of long and short rows take
+// about equally long and the launch does not end on a few long rows.  Either
+// way the chunk depends on (len, M, Hkv, waves) only, never on the cache
+// capacity (results do not change when a bucket grows).
+constexpr int kAttnRowChunk = 128;
 inline ATD_HD int attn_splits_per_head(int M, int Hkv, int waves) {
   const int per = waves / (M * Hkv);
   return per < 1 ? 1 : (per > kAttnSplitsMax ? kAttnSplitsMax : per);
 }
 inline ATD_HD int attn_chunk(int len, int M, int Hkv, int waves) {
+  if (waves == 0) {
+    int c = (len + kAttnSplitsMax - 1) / kAttnSplitsMax;
+    c = (c + 15) & ~15;
+    return c < kAttnRowChunk ? kAttnRowChunk : c;
+  }
   const int per = attn_splits_per_head(M, Hkv, waves);
   int c = (len + per - 1) / per;
   c = (c + 15) & ~15;
@@ -42,6 +51,10 @@ inline ATD_HD int attn_chunk(int len, int M, int Hkv, int waves) {
 
 // Upper bound of the split count of any row of length <= max_len.
 inline int attn_max_splits(int max_len, int M, int Hkv, int waves) {
+  if (waves == 0) {
+    const int a = (max_len + kAttnRowChunk - 1) / kAttnRowChunk;
+    return a < kAttnSplitsMax ? a : kAttnSplitsMax;
+  }
   const int a = (max_len + kAttnMinChunk - 1) / kAttnMinChunk;
   const int b = attn_splits_per_head(M, Hkv, waves);
   return a < b ? a : b;
@@ -143,7 +156,7 @@ struct AttnArgs {
   SlotTables st;
   RowMap rows;
   int layer, M, Hq, Hkv, nsplit_max;   // nsplit_max: split stride of the partials
-  int waves;                           // split-count target (attn_chunk)
+  int waves;                           // split-count target, 0: fixed chunks (attn_chunk)
   // single-slot launches: the slot's cache rows of this layer and capacity,
   // passed directly so no pointer table is read (null: use st)
   void* k_direct;
@@ -156,6 +169,7 @@ struct AttnArgs {
   float* o;           // [M, Hq * D] attention output
   uint16_t* o_hi;     // or, when set, bf16 hi/lo parts of o: [M, Hq * D]
   uint16_t* o_lo;
+  int o_frag;         // o_hi / o_lo in MFMA-fragment order (frag_off; M <= 64)
 };
 
 struct EmbedArgs {
@@ -241,7 +255,7 @@ constexpr int kMmaPrefillRows = 512;   // most rows of one layer-major prefill c
 constexpr int kMmaBlockN = 64;   // weight rows per workgroup (16 per wave)
 constexpr int kMmaCh = 64;       // K per pipeline stage
 constexpr int kMmaCUs = 256;     // compute units of the part
-constexpr int kSsCols = 256;     // columns per partial sum of squares
+constexpr int kSsCols = 16;      // columns per partial sum of squares (one MFMA column block)
 
 // K per split of the GEMM of an [N, K] weight over `tiles` row tiles (a
 // multiple of kMmaCh): the fewest splits that give every compute unit a
@@ -283,6 +297,102 @@ struct GemmArgs {
 
 enum ReduceEpilogue { kRedStore = 0, kRedResidual = 1, kRedSwiglu = 2 };
 
+// GEMM of one 64-row tile of decode rows with the split-K reduction and the
+// epilogue in the same launch (k_gemm_dec).  Epilogues: kDecParts leaves the
+// split sums in part [ks, kMmaRows, N] for a later reduction; kDecStore writes
+// out = inv_m * sum + bias; kDecResidual adds the sum into x (out) and leaves
+// x * gain as the next GEMM's hi / lo input and kSsCols-column sums of squares
+// of x; kDecSwiglu (N = 2 F: W[0] gate rows, W[1] up rows) leaves
+// silu(inv_m g) * inv_m u as hi / lo.
+enum DecEpilogue { kDecParts = 0, kDecStore = 1, kDecResidual = 2, kDecSwiglu = 3 };
+
+// Offset of element (row r, column k) of a 64-row activation tile held in
+// MFMA-fragment order: [k / 32][r / 16][(k % 32) / 8][r % 16][k % 8], so that
+// the A-operand fragment of a 16x16x32 MFMA (lane 16 g + i: row i, columns
+// 8 g .. 8 g + 7 of a 32-wide step) is one contiguous 1 KB run.  A wave reads
+// such runs from L2 at about three times the rate of the same fragments out
+// of row-major rows (16 rows x 64 bytes per load).
+inline ATD_HD size_t frag_off(int r, int k) {
+  return ((size_t)((k >> 5) * 4 + (r >> 4)) * 64 + ((k >> 3) & 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
+constexpr int kDecKStep = 32;         // K per MFMA step
+constexpr int kDecWaves = 8;          // waves per workgroup
+constexpr int kDecMaxSteps = 16;      // most K steps per wave (kc <= 16 * 8 * 32)
+
+// Weights of the decode GEMMs in MFMA B-operand order: 16-row blocks, each
+// [K / 32][512] bf16 with the fragment of K step s at s * 512 (lane 16 g + i:
+// row i, columns 32 s + 8 g .. + 7), so that a wave reads a fragment as one
+// contiguous 1 KB run (the same fragment out of row-major rows is 16 runs of
+// 64 bytes, 4 KB apart at K = 2048, measured at ~3.3 against ~4.3 TB/s).
+// Block b holds rows 16 b .. 16 b + 15 of the matrix (rows past N zero); in
+// SwiGLU order block 4 t + j holds gate rows 32 t + 16 j .. (j < 2) or up
+// rows 32 t + 16 (j - 2) .. (j >= 2).
+inline ATD_HD size_t bfrag_blocks(int N, bool swiglu) {
+  return swiglu ? (size_t)(N / 2 + 31) / 32 * 4 : (size_t)(N + 15) / 16;
+}
+struct SwizzleArgs {
+  const uint16_t* src[3];   // row segments (SwiGLU: gate [F, K], up [F, K])
+  int seg_end[3];
+  int N, K;                 // N rows (SwiGLU: 2 F); K a multiple of 32
+  int swiglu;
+  uint16_t* dst;            // bfrag_blocks(N, swiglu) * K * 16 elements
+};
+
+struct DecGemmArgs {
+  const uint16_t* hi;   // activations as bf16 hi + lo parts, 64 x K in fragment order
+  const uint16_t* lo;
+  const uint16_t* Wb;   // the weights in B-operand order (bfrag_blocks of them)
+  int nblk;             // 16-row blocks of Wb
+  int seg_end[3];       // kDecStore: the bias segments' ends
+  int K, N;             // K a multiple of 32; N output columns (kDecSwiglu: 2 F)
+  int kc, ks;           // K per split (256 times 1-4, 6, 8, 12 or 16) and splits
+  int cb;               // 16-column blocks per tile (dec_cb)
+  int M;                // rows the epilogue writes (rows >= M are never stored)
+  float* part;          // kDecParts: [ks, kMmaRows, N]; else [tiles, ks, 64 x 16 cb]
+  int* ticket;          // [tiles] counters, zero between launches
+  float* out;           // kDecStore: [M, ldo] written; kDecResidual: x [M, ldo] updated
+  int ldo;
+  const float* bias[3]; // kDecStore: per-segment bias or null
+  uint16_t* ohi;        // kDecResidual: x * gain (64 x N); kDecSwiglu: 64 x F; fragment order
+  uint16_t* olo;
+  const float* gain;    // kDecResidual
+  const float* ss_in;   // kDecStore / kDecSwiglu: [M, nss_in] sums of squares, or null
+  int nss_in, hn;
+  float eps;
+  float* ss_out;        // kDecResidual: [M, N / kSsCols]
+};
+
+// 16-column blocks per tile: one for q/k/v and for residual GEMMs with K <=
+// 2048 (more workgroups for the same split count, so fewer and smaller split
+// tiles to merge, for activation rows short enough to read once per 16
+// columns), four otherwise (SwiGLU: 32 gate + 32 up rows).  Measured on the
+// 1.7B shape at 64 rows.
+inline ATD_HD int dec_cb(int epi, int K) {
+  return epi == kDecStore || (epi == kDecResidual && K <= 2048) ? 1 : 4;
+}
+inline ATD_HD int dec_tiles(int N, int epi, int K) {
+  const int tc = 16 * dec_cb(epi, K);
+  return epi == kDecSwiglu ? (N / 2 + tc / 2 - 1) / (tc / 2) : (N + tc - 1) / tc;
+}
+
+// K per split (kc) of a k_gemm_dec launch over `tiles` column tiles: as
+// many splits as keep the launch within one workgroup per compute unit (all
+// workgroups resident at once, so the last one of a tile never waits for a
+// second round), at least one K step per wave and at most kDecMaxSteps; the
+// steps per wave are rounded up to a count the kernel is built for.
+inline int dec_kc(int tiles, int K) {
+  const int span = kDecWaves * kDecKStep;   // K of one step of every wave
+  const int nall = (K + span - 1) / span;   // steps of the whole K range
+  int ks = kMmaCUs / tiles;
+  if (ks < 1) ks = 1;
+  if (ks > nall) ks = nall;
+  int nks = (nall + ks - 1) / ks;
+  if (nks < (nall + kDecMaxSteps - 1) / kDecMaxSteps) nks = (nall + kDecMaxSteps - 1) / kDecMaxSteps;
+  nks = nks <= 4 ? nks : (nks <= 8 ? (nks + 1) / 2 * 2 : (nks + 3) / 4 * 4);
+  if (nks > kDecMaxSteps) nks = kDecMaxSteps;
+  return nks * span;
+}
+
 // RMSNorm(x) W^T = inv_m * ((x * g) W^T) with inv_m = 1 / sqrt(mean(x_m^2) + eps):
 // the residual reduction leaves x * g (the next GEMM's input, as hi/lo) and
 // partial sums of squares of x; the reduction after that GEMM applies inv_m.
@@ -297,7 +407,7 @@ struct ReduceArgs {
   uint16_t* hi;        // kRedResidual: x * gain; kRedSwiglu: the activation ([M, N or N/2])
   uint16_t* lo;
   const float* gain;   // kRedResidual: gain of the next norm; kRedStore: gain for y_out
-  // kRedResidual writes ss [M, gridDim.x] (kSsCols-column partial sums of squares
+  // kRedResidual writes ss [M, nss] (kSsCols-column partial sums of squares
   // of the updated rows); kRedStore / kRedSwiglu with ss set scale the sums by
   // inv_m from ss [M, nss] over hn columns.
   float* ss;
@@ -305,6 +415,7 @@ struct ReduceArgs {
   float eps;
   const float* x;      // kRedStore: rows whose norm goes to y_out ([M, hn])
   float* y_out;        // kRedStore: x * inv_m * gain [M, hn] or null
+  int frag;            // hi / lo written in MFMA-fragment order (frag_off; M <= 64)
 };
 
 // ---------------------------------------------------------------- launchers
@@ -380,5 +491,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // tile: prefill chunks); same arguments and partials layout.
 hipError_t launch_gemm_tile(const GemmArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, int epi, hipStream_t s);
+hipError_t launch_gemm_dec(const DecGemmArgs& a, int epi, hipStream_t s);
+hipError_t launch_swizzle_b(const SwizzleArgs& a, hipStream_t s);
 
 }  // namespace atd

@@ -682,12 +682,17 @@ __device__ __forceinline__ uint4 pack_kv(const float (&v)[VEC]) {
 }
 
 // Attention output of 4 channels at o[off] (or their bf16 hi / lo parts).
+template <int D>
 __device__ __forceinline__ void store_o4(const AttnArgs& a, size_t off, float4 v) {
   if (a.o_hi) {
     const float f[4] = {v.x, v.y, v.z, v.w};
     uint16_t hv[4], lv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) split_hi_lo(f[i], hv[i], lv[i]);
+    if (a.o_frag) {   // off = m * Hq * D + column, the column a multiple of 4
+      const int HD = a.Hq * D;
+      off = frag_off((int)(off / HD), (int)(off % HD));
+    }
     *reinterpret_cast<uint2*>(a.o_hi + off) =
         make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
     *reinterpret_cast<uint2*>(a.o_lo + off) =
@@ -1020,7 +1025,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
         const size_t off = ((size_t)m * a.Hq + g * R + j) * D + dl;
 #pragma unroll
         for (int e = 0; e < DPL; e += 4)
-          store_o4(a, off + e, make_float4(acc[j][e] / ls[j], acc[j][e + 1] / ls[j],
+          store_o4<D>(a, off + e, make_float4(acc[j][e] / ls[j], acc[j][e + 1] / ls[j],
                                             acc[j][e + 2] / ls[j], acc[j][e + 3] / ls[j]));
       }
     }
@@ -1065,7 +1070,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       A = make_float4(fmaf(v.x, cw, A.x), fmaf(v.y, cw, A.y), fmaf(v.z, cw, A.z), fmaf(v.w, cw, A.w));
     }
     if (nblk == 1) {
-      store_o4(a, head * D + 4 * c, make_float4(A.x / L, A.y / L, A.z / L, A.w / L));
+      store_o4<D>(a, head * D + 4 * c, make_float4(A.x / L, A.y / L, A.z / L, A.w / L));
     } else {
       // the block's partial, written through to the device-coherent level so
       // that the block that merges them (on any XCD) reads the values stored
@@ -1141,7 +1146,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
       const float4 v = s_pa[q][item];
       A = make_float4(fmaf(v.x, cq, A.x), fmaf(v.y, cq, A.y), fmaf(v.z, cq, A.z), fmaf(v.w, cq, A.w));
     }
-    store_o4(a, head * D + 4 * c, make_float4(A.x / L, A.y / L, A.z / L, A.w / L));
+    store_o4<D>(a, head * D + 4 * c, make_float4(A.x / L, A.y / L, A.z / L, A.w / L));
   }
 }
 
@@ -1945,7 +1950,6 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
   const int n = blockIdx.x * 256 + tid;
   const int NO = EPI == kRedSwiglu ? a.N / 2 : a.N;
   if constexpr (EPI == kRedResidual) {
-    __shared__ float red[4];
     float t = 0.f;
     if (n < NO) {
       float v = 0.f;
@@ -1953,18 +1957,22 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
       float* o = a.out + (size_t)m * a.ldo + n;
       t = *o + v;
       *o = t;
-      split_hi_lo(t * a.gain[n], a.hi[(size_t)m * a.N + n], a.lo[(size_t)m * a.N + n]);
+      const size_t ho = a.frag ? frag_off(m, n) : (size_t)m * a.N + n;
+      split_hi_lo(t * a.gain[n], a.hi[ho], a.lo[ho]);
     }
-    const float sq = wave_sum(t * t);
-    if ((tid & 63) == 0) red[tid >> 6] = sq;
-    __syncthreads();
-    if (tid == 0) a.ss[(size_t)m * gridDim.x + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+    // one sum of squares per kSsCols = 16 columns (16 lanes)
+    const float sq = group_sum<16>(t * t);
+    const int b = (blockIdx.x * 256 + tid) / kSsCols;
+    if ((tid & 15) == 0 && b < a.nss) a.ss[(size_t)m * a.nss + b] = sq;
     return;
   }
+  // the row's norm factor: the wave's lanes add strided parts of its sums
+  // of squares, then the wave's sum (the same in every lane)
   float inv = 1.f;
   if (a.ss) {
     float ss = 0.f;
-    for (int b = 0; b < a.nss; ++b) ss += a.ss[(size_t)m * a.nss + b];
+    for (int b = tid & 63; b < a.nss; b += 64) ss += a.ss[(size_t)m * a.nss + b];
+    ss = wave_sum(ss);
     inv = 1.0f / sqrtf(ss / (float)a.hn + a.eps);
   }
   if constexpr (EPI == kRedStore) {
@@ -1982,7 +1990,8 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
     }
     g *= inv;
     u *= inv;
-    split_hi_lo(g / (1.0f + expf(-g)) * u, a.hi[(size_t)m * NO + n], a.lo[(size_t)m * NO + n]);
+    const size_t ho = a.frag ? frag_off(m, n) : (size_t)m * NO + n;
+    split_hi_lo(g / (1.0f + expf(-g)) * u, a.hi[ho], a.lo[ho]);
   } else {
     float v = 0.f;
     for (int s = 0; s < a.ks; ++s) v += a.part[((size_t)s * a.mrows + m) * a.N + n];
@@ -1997,10 +2006,11 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs a) {
 // The same epilogues with 4 consecutive columns per thread (16-byte partial
 // and residual accesses, 8-byte hi / lo stores), for N (N / 2 for SwiGLU) a
 // multiple of 4.  Each column's splits are still added in order; a wave
-// covers one 256-column block, whose sum of squares it writes (residual).
+// covers one 256-column block and writes the sums of squares of its
+// 16-column groups (residual).
 template <int EPI>
 __global__ __launch_bounds__(256) void k_reduce4(ReduceArgs a) {
-  const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int n = (blockIdx.x * 256 + tid) * 4;
   const int NO = EPI == kRedSwiglu ? a.N / 2 : a.N;
   auto sum_parts = [&](int col) {
@@ -2014,7 +2024,13 @@ __global__ __launch_bounds__(256) void k_reduce4(ReduceArgs a) {
     }
     return v;
   };
+  // off = m * width + column, the column a multiple of 4 (fragment order:
+  // the four values stay contiguous)
   auto store_hi_lo = [&](const float (&v)[4], size_t off) {
+    if (a.frag) {
+      const int width = EPI == kRedSwiglu ? a.N / 2 : a.N;
+      off = frag_off(m, (int)(off - (size_t)m * width));
+    }
     uint16_t hv[4], lv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) split_hi_lo(v[i], hv[i], lv[i]);
@@ -2039,16 +2055,19 @@ __global__ __launch_bounds__(256) void k_reduce4(ReduceArgs a) {
       store_hi_lo(xg, (size_t)m * a.N + n);
       sq = (t.x * t.x + t.y * t.y) + (t.z * t.z + t.w * t.w);
     }
-    sq = wave_sum(sq);
-    const int b = blockIdx.x * 4 + wave;   // the wave's 256-column block
-    const int nss = (NO + 255) / 256;
-    if (lane == 0 && b < nss) a.ss[(size_t)m * nss + b] = sq;
+    // one sum of squares per kSsCols = 16 columns (4 lanes)
+    sq = group_sum<4>(sq);
+    const int b = (blockIdx.x * 256 + tid) * 4 / kSsCols;
+    if ((lane & 3) == 0 && b < a.nss) a.ss[(size_t)m * a.nss + b] = sq;
     return;
   }
+  // the row's norm factor: the wave's lanes add strided parts of its sums
+  // of squares, then the wave's sum (the same in every lane)
   float inv = 1.f;
   if (a.ss) {
     float ss = 0.f;
-    for (int b = 0; b < a.nss; ++b) ss += a.ss[(size_t)m * a.nss + b];
+    for (int b = tid & 63; b < a.nss; b += 64) ss += a.ss[(size_t)m * a.nss + b];
+    ss = wave_sum(ss);
     inv = 1.0f / sqrtf(ss / (float)a.hn + a.eps);
   }
   if constexpr (EPI == kRedStore) {
@@ -2083,6 +2102,354 @@ __global__ __launch_bounds__(256) void k_reduce4(ReduceArgs a) {
       v.w += bb.w;
     }
     *reinterpret_cast<float4*>(a.out + (size_t)m * a.ldo + n) = v;
+  }
+}
+
+// ------------------------------------------------------------------ weights in B-operand order
+// One thread per 16-byte chunk of the destination: chunk c is lane c % 64 of
+// K step (c / 64) % (K / 32) of block c / (64 K / 32).
+__global__ __launch_bounds__(256) void k_swizzle_b(SwizzleArgs a) {
+  const int nks = a.K / 32;
+  const size_t nblk = bfrag_blocks(a.N, a.swiglu != 0);
+  const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= nblk * nks * 64) return;
+  const int lane = (int)(c % 64), li = lane & 15, lg = lane >> 4;
+  const int ks = (int)((c / 64) % nks);
+  const int blk = (int)(c / 64 / nks);
+  const uint16_t* base;
+  int row;
+  bool valid;
+  if (a.swiglu) {
+    const int F = a.N / 2, t = blk / 4, j = blk % 4;
+    row = t * 32 + (j & 1) * 16 + li;
+    valid = row < F;
+    base = j < 2 ? a.src[0] : a.src[1];
+  } else {
+    const int n = blk * 16 + li;
+    valid = n < a.N;
+    const int sg = n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
+    const int sb = sg == 0 ? 0 : (sg == 1 ? a.seg_end[0] : a.seg_end[1]);
+    base = pick3(a.src, sg);
+    row = n - sb;
+  }
+  const uint4 v = valid ? ldg16(base + (size_t)row * a.K + ks * 32 + lg * 8) : make_uint4(0, 0, 0, 0);
+  *reinterpret_cast<uint4*>(a.dst + c * 8) = v;
+}
+
+// ------------------------------------------------------------------ decode GEMM, reduction inside
+// GEMM of one 64-row tile (the rows of up to 64 decode streams, or a short
+// prefill chunk) with its split-K reduction and epilogue in the same launch:
+// C[m, n] = sum_k (hi + lo)[m, k] W[n, k], bf16 MFMA 16x16x32 with float32
+// accumulation.  Workgroup (column tile of CB 16-column blocks, split) of
+// eight waves: they take the split's 32-wide K steps in turn (wave w steps
+// w, w + 8, ...) and each computes the whole tile over its steps.  A wave
+// loads its fragments straight into registers, each a contiguous 1 KB run:
+// the weights (held in B-operand order) from memory, the activations (held
+// in MFMA-fragment order) mostly from L2.  Eight waves with few steps each keep every wave's chain of memory
+// round trips short; there is no LDS staging and no barrier in the loop.
+// The waves' tiles are added in LDS in a fixed order (w + (w + 4), then
+// 0..3).  Narrow tiles give a matrix more workgroups for the same split
+// count (fewer, smaller split tiles to merge) at the price of reading the
+// activations once per tile.  With several splits each workgroup writes its
+// tile at the device-coherent level and takes the tile's ticket; the last to
+// arrive adds the ks tiles in split order (so the sum never depends on the
+// arrival order) and applies the epilogue.  kDecSwiglu tiles hold CB / 2
+// blocks of gate rows, then the matching up rows.
+template <int NKS, int EPI, int CB>
+__global__ __launch_bounds__(512) void k_gemm_dec(DecGemmArgs a) {
+  constexpr int NWV = kDecWaves, NT = 64 * NWV;
+  constexpr int DMAX = CB == 4 ? 3 : 4;
+  constexpr int DEPTH = NKS < DMAX ? NKS : DMAX;   // K steps of loads in flight per wave
+  constexpr int TC = 16 * CB;                      // tile columns
+  constexpr bool SW = EPI == kDecSwiglu;
+  // epilogue items: a float4 column group of a row (SwiGLU: a gate group and
+  // the matching up group); TPR items a row, IT items a tile, NH per thread
+  constexpr int TPR = SW ? TC / 8 : TC / 4;
+  constexpr int IT = kMmaRows * TPR;
+  constexpr int NH = (IT + NT - 1) / NT;
+  constexpr int AT = IT < NT ? IT : NT;             // threads with items
+  constexpr int NV = SW ? 2 : 1;                    // float4 values an item
+  static_assert(!SW || CB % 2 == 0, "SwiGLU tiles pair gate and up blocks");
+  static_assert(EPI == kDecParts || EPI == kDecResidual || NH == 1, "one item per thread");
+  __shared__ float4 s_t[4][kMmaRows][TC / 4];   // four partial tiles
+  __shared__ float s_inv[kMmaRows];              // the rows' norm factors
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int K = a.K;
+  const int kb = split * a.kc, ke = min(K, kb + a.kc);
+
+  // the lane's weight fragments: block tile * CB + j (blocks past the matrix
+  // read its last block; their sums are never stored), K step s at s * 512
+  const int nks_all = K / kDecKStep;
+  const uint16_t* wblk[CB];
+#pragma unroll
+  for (int j = 0; j < CB; ++j)
+    wblk[j] = a.Wb + (size_t)min(tile * CB + j, a.nblk - 1) * nks_all * 512 + lane * 8;
+
+  uint4 wv[DEPTH][CB], av[DEPTH][4][2];
+  // K step t of this wave: weights first, then the activations (a 1 KB run
+  // per fragment; addresses clamped into the matrix)
+  auto issue = [&](int d, int t) {
+    const int k = min(kb + (t * NWV + wave) * kDecKStep, K - kDecKStep);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) wv[d][j] = ldg16(wblk[j] + (size_t)(k >> 5) * 512);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t f = ((size_t)((k >> 5) * 4 + i) * 64 + lane) * 8;
+      av[d][i][0] = ldg16(a.hi + f);
+      av[d][i][1] = ldg16(a.lo + f);
+    }
+  };
+  Floatx4 acc[4][CB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) acc[i][j] = Floatx4{0.f, 0.f, 0.f, 0.f};
+  // the norm factor inv_m of every row (store and SwiGLU epilogues): wave w
+  // takes rows 8 w .. 8 w + 7, eight lanes a row, each adding every eighth
+  // of the row's sums of squares; their loads go out ahead of the operands
+  constexpr bool NORMED = EPI == kDecStore || EPI == kDecSwiglu;
+  constexpr int SSL = 16;   // sums a lane loads in the first pass
+  const int rr = wave * 8 + (lane >> 3), rq = lane & 7;
+  float ssv[SSL];
+  const float* sp = NORMED && a.ss_in ? a.ss_in + (size_t)min(rr, a.M - 1) * a.nss_in : nullptr;
+  if constexpr (NORMED) {
+#pragma unroll
+    for (int i = 0; i < SSL; ++i) {
+      const int b = rq + 8 * i;
+      ssv[i] = sp && b < a.nss_in ? sp[b] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(d, d);
+  // the loads stay where they are written (the scheduler would otherwise
+  // sink them next to their use and serialise the memory round trips)
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NORMED) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < SSL; ++i) ss += ssv[i];
+    if (sp)
+      for (int b = rq + 8 * SSL; b < a.nss_in; b += 8) ss += sp[b];
+    ss = group_sum<8>(ss);
+    if (rq == 0) s_inv[rr] = a.ss_in ? 1.0f / sqrtf(ss / (float)a.hn + a.eps) : 1.f;
+  }
+#pragma unroll
+  for (int t = 0; t < NKS; ++t) {
+    const int d = t % DEPTH;
+    // steps past the split end meet zero activations (a mask, so that the
+    // step's MFMAs and the counter waits stay unconditional)
+    const uint32_t mk = 0u - (uint32_t)(kb + (t * NWV + wave) * kDecKStep < ke);
+    auto keep = [mk](uint4 v) { return make_uint4(v.x & mk, v.y & mk, v.z & mk, v.w & mk); };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const Bf16x8 ah = as_bf16x8(keep(av[d][i][0])), al = as_bf16x8(keep(av[d][i][1]));
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        const Bf16x8 b = as_bf16x8(wv[d][j]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[i][j], 0, 0, 0);
+      }
+    }
+    if (t + DEPTH < NKS) issue(d, t + DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // the waves' tiles added in LDS (C layout: column 16 j + li, rows 16 i +
+  // 4 lg + r): waves 4..7 store, waves 0..3 add theirs (tile w + tile w + 4)
+  float* st = reinterpret_cast<float*>(&s_t[wave & 3][0][0]);
+  if (wave >= 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[(i * 16 + lg * 4 + r) * TC + j * 16 + li] = acc[i][j][r];
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* p = st + (i * 16 + lg * 4 + r) * TC + j * 16 + li;
+          *p = acc[i][j][r] + *p;
+        }
+  }
+  __syncthreads();
+  // item h of this thread: row er[h], column group c[h] (its columns 4 c ..
+  // 4 c + 3; SwiGLU: gate columns 4 c .., up columns TC / 2 + 4 c ..)
+  const bool act = tid < AT;
+  int er[NH], cg[NH];
+  float4 v[NH][NV];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int ii = min(h * NT + tid, IT - 1);
+    er[h] = ii / TPR;
+    cg[h] = ii % TPR;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int c4 = (u ? TC / 8 : 0) + cg[h];
+      float4 x = s_t[0][er[h]][c4];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const float4 y = s_t[w][er[h]][c4];
+        x = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+      }
+      v[h][u] = x;
+    }
+  }
+
+  if constexpr (EPI == kDecParts) {
+    if (!act) return;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      float* pp = a.part + ((size_t)split * kMmaRows + er[h]) * a.N;
+      const int n = tile * TC + 4 * cg[h];
+      if (n + 4 <= a.N) {
+        *reinterpret_cast<float4*>(pp + n) = v[h][0];
+      } else {
+        const float f[4] = {v[h][0].x, v[h][0].y, v[h][0].z, v[h][0].w};
+        for (int e = 0; e < 4 && n + e < a.N; ++e) pp[n + e] = f[e];
+      }
+    }
+    return;
+  } else {
+    constexpr int TSZ = kMmaRows * TC;   // floats of one split's tile
+    if (a.ks > 1) {
+      // piece p (two floats) of thread tid at [tile, split, p, tid]: every
+      // store (and load below) of a wave covers 512 contiguous bytes
+      float* tp = a.part + ((size_t)tile * a.ks + split) * TSZ + tid * 2;
+      if (act) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int u = 0; u < NV; ++u) {
+            const int p = (h * NV + u) * 2;
+            store_coherent2(tp + p * (2 * AT), v[h][u].x, v[h][u].y);
+            store_coherent2(tp + (p + 1) * (2 * AT), v[h][u].z, v[h][u].w);
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0);   // this thread's tile stores are complete
+      __syncthreads();
+      if (tid == 0) {
+        int* t = a.ticket + tile;
+        const int old = __hip_atomic_fetch_add(t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == a.ks - 1;
+        if (last) __hip_atomic_store(t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+      }
+      __syncthreads();
+      if (!s_last) return;
+    }
+    if (!act) return;   // whole waves (AT is a multiple of 64)
+    // the epilogue's operands (rows clamped below M: rows >= M are never
+    // stored) are loaded ahead of the split tiles, in the same round trip
+    float4 bb[NH], xo[NH], g[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int erc = min(er[h], a.M - 1);
+      const int n = min(tile * TC + 4 * cg[h], a.N - 4);   // N is a multiple of 4
+      if constexpr (EPI == kDecStore) {
+        // segment ends are multiples of 4: a column group lies in one segment
+        const int sg = n < a.seg_end[0] ? 0 : (n < a.seg_end[1] ? 1 : 2);
+        const int sb = sg == 0 ? 0 : (sg == 1 ? a.seg_end[0] : a.seg_end[1]);
+        const float* bp = pick3(a.bias, sg);
+        bb[h] = bp ? *reinterpret_cast<const float4*>(bp + (n - sb)) : make_float4(0.f, 0.f, 0.f, 0.f);
+      } else if constexpr (EPI == kDecResidual) {
+        xo[h] = *reinterpret_cast<const float4*>(a.out + (size_t)erc * a.ldo + n);
+        g[h] = *reinterpret_cast<const float4*>(a.gain + n);
+      }
+    }
+    if (a.ks > 1) {
+      // every split's tile, added in split order; up to NB splits' loads in
+      // flight at once (indexes past the last split re-read it and are skipped)
+      constexpr int NB = 8;
+      const float* tb = a.part + (size_t)tile * a.ks * TSZ + tid * 2;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int u = 0; u < NV; ++u) v[h][u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s0 = 0; s0 < a.ks; s0 += NB) {
+        float4 w4[NB][NH][NV];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float* sp = tb + (size_t)min(s0 + b, a.ks - 1) * TSZ;
+#pragma unroll
+          for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int u = 0; u < NV; ++u) {
+              const int p = (h * NV + u) * 2;
+              load_coherent2(sp + p * (2 * AT), w4[b][h][u].x, w4[b][h][u].y);
+              load_coherent2(sp + (p + 1) * (2 * AT), w4[b][h][u].z, w4[b][h][u].w);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (s0 + b < a.ks) {
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+              for (int u = 0; u < NV; ++u)
+                v[h][u] = make_float4(v[h][u].x + w4[b][h][u].x, v[h][u].y + w4[b][h][u].y,
+                                      v[h][u].z + w4[b][h][u].z, v[h][u].w + w4[b][h][u].w);
+          }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int row = er[h];
+      const float inv = NORMED ? s_inv[row] : 1.f;
+      if constexpr (EPI == kDecStore) {
+        const int n = tile * TC + 4 * cg[h];
+        if (row < a.M && n < a.N)
+          *reinterpret_cast<float4*>(a.out + (size_t)row * a.ldo + n) =
+              make_float4(v[h][0].x * inv + bb[h].x, v[h][0].y * inv + bb[h].y,
+                          v[h][0].z * inv + bb[h].z, v[h][0].w * inv + bb[h].w);
+      } else if constexpr (EPI == kDecResidual) {
+        const int n = tile * TC + 4 * cg[h];
+        float sq = 0.f;
+        if (row < a.M && n < a.N) {
+          const float4 t = make_float4(xo[h].x + v[h][0].x, xo[h].y + v[h][0].y,
+                                       xo[h].z + v[h][0].z, xo[h].w + v[h][0].w);
+          *reinterpret_cast<float4*>(a.out + (size_t)row * a.ldo + n) = t;
+          const float xg[4] = {t.x * g[h].x, t.y * g[h].y, t.z * g[h].z, t.w * g[h].w};
+          uint16_t hv[4], lv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) split_hi_lo(xg[e], hv[e], lv[e]);
+          const size_t off = frag_off(row, n);
+          *reinterpret_cast<uint2*>(a.ohi + off) =
+              make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+          *reinterpret_cast<uint2*>(a.olo + off) =
+              make_uint2(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
+          sq = (t.x * t.x + t.y * t.y) + (t.z * t.z + t.w * t.w);
+        }
+        // kSsCols = 16 columns: four adjacent lanes (all active here)
+        sq = group_sum<4>(sq);
+        if ((cg[h] & 3) == 0 && row < a.M && n < a.N)
+          a.ss_out[(size_t)row * ((a.N + kSsCols - 1) / kSsCols) + n / kSsCols] = sq;
+      } else {   // kDecSwiglu
+        const int F = a.N / 2;
+        const int n = tile * (TC / 2) + 4 * cg[h];
+        if (row < a.M && n < F) {   // F is a multiple of 4 (checked at launch)
+          const float4 gv = v[h][0], uv = v[h][1];
+          const float gg[4] = {gv.x * inv, gv.y * inv, gv.z * inv, gv.w * inv};
+          const float uu[4] = {uv.x * inv, uv.y * inv, uv.z * inv, uv.w * inv};
+          uint16_t hv[4], lv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) split_hi_lo(gg[e] / (1.0f + expf(-gg[e])) * uu[e], hv[e], lv[e]);
+          const size_t off = frag_off(row, n);
+          *reinterpret_cast<uint2*>(a.ohi + off) =
+              make_uint2(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16));
+          *reinterpret_cast<uint2*>(a.olo + off) =
+              make_uint2(lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
+        }
+      }
+    }
   }
 }
 
@@ -2568,8 +2935,9 @@ __global__ __launch_bounds__(64 * HP * KS) void k_attn_prefill(AttnArgs a) {
       if (a.o_hi) {
         uint16_t hv, lv;
         split_hi_lo(v, hv, lv);
-        a.o_hi[off + 16 * b + li] = hv;
-        a.o_lo[off + 16 * b + li] = lv;
+        const size_t oo = a.o_frag ? frag_off(m, h * D + 16 * b + li) : off + 16 * b + li;
+        a.o_hi[oo] = hv;
+        a.o_lo[oo] = lv;
       } else {
         a.o[off + 16 * b + li] = v;
       }
@@ -2925,6 +3293,53 @@ hipError_t launch_reduce(const ReduceArgs& a, int epi, hipStream_t s) {
     hipLaunchKernelGGL(k_reduce<kRedResidual>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_reduce<kRedSwiglu>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int EPI, int CB>
+static void gemm_dec_dispatch(const DecGemmArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 block(64 * kDecWaves);
+  switch (a.kc / (kDecWaves * kDecKStep)) {
+    case 1: hipLaunchKernelGGL((k_gemm_dec<1, EPI, CB>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_dec<2, EPI, CB>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm_dec<3, EPI, CB>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_gemm_dec<4, EPI, CB>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((k_gemm_dec<6, EPI, CB>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_gemm_dec<8, EPI, CB>), grid, block, 0, s, a); break;
+    case 12: hipLaunchKernelGGL((k_gemm_dec<12, EPI, CB>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_dec<16, EPI, CB>), grid, block, 0, s, a); break;
+  }
+}
+
+hipError_t launch_swizzle_b(const SwizzleArgs& a, hipStream_t s) {
+  if (a.K < 32 || a.K % 32 || a.N < 1 || (a.swiglu && a.N % 2) || !a.dst) return hipErrorInvalidValue;
+  const size_t chunks = bfrag_blocks(a.N, a.swiglu != 0) * (a.K / 32) * 64;
+  hipLaunchKernelGGL(k_swizzle_b, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_dec(const DecGemmArgs& a, int epi, hipStream_t s) {
+  const int span = kDecWaves * kDecKStep;
+  const int nks = a.kc / span;
+  const bool nks_ok = nks >= 1 && nks <= kDecMaxSteps && (nks <= 4 || nks % 2 == 0) &&
+                      (nks <= 8 || nks % 4 == 0);
+  if (a.K < kDecKStep || a.K % kDecKStep || a.kc % span || !nks_ok || a.ks < 1 ||
+      (long)a.kc * (a.ks - 1) >= a.K || (long)a.kc * a.ks < a.K || a.N < 4 || a.M < 1 ||
+      a.M > kMmaRows || a.cb != dec_cb(epi, a.K) || !a.Wb ||
+      (size_t)a.nblk != bfrag_blocks(a.N, epi == kDecSwiglu))
+    return hipErrorInvalidValue;
+  if (epi != kDecParts && (a.N % 4 || a.seg_end[0] % 4 || a.seg_end[1] % 4 || !a.ticket))
+    return hipErrorInvalidValue;
+  if (epi == kDecSwiglu && (a.N / 2) % 4) return hipErrorInvalidValue;
+  const dim3 grid(dec_tiles(a.N, epi, a.K), a.ks);
+  switch (epi * 8 + a.cb) {
+    case kDecParts * 8 + 4: gemm_dec_dispatch<kDecParts, 4>(a, grid, s); break;
+    case kDecStore * 8 + 1: gemm_dec_dispatch<kDecStore, 1>(a, grid, s); break;
+    case kDecResidual * 8 + 1: gemm_dec_dispatch<kDecResidual, 1>(a, grid, s); break;
+    case kDecResidual * 8 + 4: gemm_dec_dispatch<kDecResidual, 4>(a, grid, s); break;
+    case kDecSwiglu * 8 + 4: gemm_dec_dispatch<kDecSwiglu, 4>(a, grid, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

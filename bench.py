@@ -216,8 +216,9 @@ def attn_kernel_hash() -> str:
 
 
 def gemm_kernel_hash() -> str:
-    """Hash of the two matrix-core GEMM kernels' sources."""
-    return _source_hash(("template <int P, int NCH>\n__global__ __launch_bounds__(256) void k_gemm(",
+    """Hash of the matrix-core GEMM kernels' sources (64-row decode GEMM,
+    128 x 128 prefill tiles)."""
+    return _source_hash(("template <int NKS, int EPI, int CB>\n__global__ __launch_bounds__(512) void k_gemm_dec(",
                          "template <int NST>\n__global__ __launch_bounds__(256) void k_gemm_tile("))
 
 

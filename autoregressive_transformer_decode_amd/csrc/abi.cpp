@@ -46,7 +46,7 @@ struct atd_decoder {
   int *slot_pos = nullptr, *slot_cap = nullptr;
   float* part = nullptr;       // argmax partials [max_rows, nblk, 3]
   uint2* samp = nullptr;       // sampler chunk candidates [sample_blocks(V), kTopKMax]
-  bool mma = false;            // MFMA path for chunks of >= 3 rows
+  bool mma = false;            // MFMA path for chunks of >= kMmaMinRows rows
   float* mpart = nullptr;      // split-K partials of the MFMA GEMMs
   int mma_rows = 0;            // most rows of one MFMA chunk (multiple of kMmaRows)
   float* mss = nullptr;        // row sums of squares [mma_rows, ceil(h / kSsCols)]
@@ -747,7 +747,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, flo
   // taken layer by layer: the GEMMs stream the weights once per chunk over its
   // 64-row tiles (a prefill chunk's rows read the keys of earlier chunks and
   // their own, appended first)
-  const int step = d->mma && M >= 3 ? d->mma_rows : M;
+  const int step = d->mma && M >= kMmaMinRows ? d->mma_rows : M;
   for (int c0 = 0; c0 < M && e == hipSuccess; c0 += step) {
     RowMap r = rows;
     r.row0 = rows.row0 + c0;
@@ -761,7 +761,7 @@ hipError_t run_layers(atd_decoder* d, RowMap rows, int M, int max_len_bound, flo
       hc.y_out = ho->y_out ? ho->y_out + (size_t)c0 * h : nullptr;
       hc.logits = ho->logits + (size_t)c0 * V;
     }
-    if (d->mma && cm >= 3) {
+    if (d->mma && cm >= kMmaMinRows) {
       e = run_chunk_mma(d, r, cm, bound, xc, ho ? &hc : nullptr, s);
     } else {
       e = run_layers_gemv(d, r, cm, bound, xc, s);
@@ -900,10 +900,10 @@ void plan_scratch(const atd_config& c, bool in_proj, ScratchPlan& p) {
                            (size_t)R * attn_max_splits(c.max_ctx, R, c.n_kv_heads, 0));
   p.o_pml = carve(p.part_floats * 2 * 4);
   p.o_pacc = carve(p.part_floats * D * 4);
-  // MFMA path (bf16 dense weights, chunks of >= 3 rows possible)
+  // MFMA path (bf16 dense weights, chunks of >= kMmaMinRows rows possible)
   p.mma = c.dtype == ATD_BF16 && c.weight_format == ATD_WFMT_DENSE &&
           !(c.flags & ATD_FLAG_NO_MFMA) && h % 32 == 0 && nq % 32 == 0 && c.ffn % 32 == 0 &&
-          std::max(R, S) >= 3;
+          std::max(R, S) >= kMmaMinRows;
   if (p.mma) {
     // the decode GEMMs' weights in B-operand order: q/k/v, o, gate/up, down
     // per layer, then the heads (filled at creation, outside the zeroed part)

@@ -245,7 +245,12 @@ struct KvCopyArgs {
   int Hkv, D, rows, s_old, s_new, elem_bytes;
 };
 
-// ---------------------------------------------------------------- MFMA path (M >= 3 rows)
+// ---------------------------------------------------------------- MFMA path (M >= kMmaMinRows)
+// Fewest rows a call takes the matrix-core path with.  Measured on the 1.7B
+// shape (bf16 cache, context 1000), ms per step of M streams, matrix-core /
+// vector path: 3 rows 1.98 / 1.89, 4 rows 1.95 / 1.93, 6 rows 2.30 / 2.94,
+// 8 rows 2.37 / 3.71 (the vector path streams the weights once per 2 rows).
+constexpr int kMmaMinRows = 5;
 // Activations enter a GEMM as a bf16 pair hi + lo (hi = bf16(v), lo =
 // bf16(v - hi)), so the products keep ~16 bits of the float32 input while the
 // bf16 weights are used exactly; each float32 activation is split into bf16

@@ -135,7 +135,7 @@ typedef struct atd_config {
 #define ATD_FLAG_DRY_RUN 1
 /* ATD_FLAG_NO_MFMA keeps every call on the matrix-vector kernels.  Without it,
  * a decoder with bf16 weights whose h, Hq*D and F are multiples of 32 runs
- * calls of 3 or more rows (batched steps, prefill) in chunks of up to 64 rows
+ * calls of 5 or more rows (batched steps, prefill) in chunks of up to 64 rows
  * through matrix-core GEMMs: activations split into bf16 hi + lo parts, float32
  * accumulation, results within the same tolerance as the vector path. */
 #define ATD_FLAG_NO_MFMA 2

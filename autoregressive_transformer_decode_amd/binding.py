@@ -32,6 +32,7 @@ ATD_F32 = 0
 ATD_BF16 = 1
 ATD_FLAG_DRY_RUN = 1
 ATD_FLAG_NO_MFMA = 2
+ATD_FLAG_NO_L2_PREFETCH = 4
 ATD_WFMT_DENSE, ATD_WFMT_Q8, ATD_WFMT_Q4 = 0, 1, 2
 ATD_QBLOCK = 32
 

@@ -68,6 +68,9 @@ struct atd_decoder {
   bool dry = false;  // ATD_FLAG_DRY_RUN: host state only, no HIP calls
   // stage timing (decoder_time_stage): layers to enqueue, -1 = all
   int only_stage = -1;
+  // L2 prefetch from the step attention launch: bytes of the O projection
+  // and gate/up weights to pull ahead (0 = none)
+  size_t pf_budget = 0;
   // graph cache of decoder_generate
   hipStream_t cap_stream = nullptr;
   struct GraphEntry {
@@ -196,7 +199,7 @@ int check_config(const atd_config* c) {
     return fail(nullptr, ATD_ERR_CAPACITY, "max_rows %d outside [1, 65536]", c->max_rows);
   if (c->max_ctx < 1 || c->max_ctx > (1 << 20))
     return fail(nullptr, ATD_ERR_CAPACITY, "max_ctx %d outside [1, 2^20]", c->max_ctx);
-  if (c->flags & ~(ATD_FLAG_DRY_RUN | ATD_FLAG_NO_MFMA))
+  if (c->flags & ~(ATD_FLAG_DRY_RUN | ATD_FLAG_NO_MFMA | ATD_FLAG_NO_L2_PREFETCH))
     return fail(nullptr, ATD_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)c->flags);
   {
     const int* ms = c->mrope_sections;
@@ -396,6 +399,35 @@ RopeArgs rope_args(const atd_decoder* d, RowMap rows, int l, int M) {
   return r;
 }
 
+// The prefetch plan of layer l's step attention: the O projection's weights,
+// then as many gate/up blocks as the budget leaves (whole blocks only, so no
+// load passes the end of a matrix).
+L2Prefetch prefetch_plan(const atd_decoder* d, const atd_layer_weights& W, int wt) {
+  L2Prefetch p{};
+  if (d->pf_budget == 0) return p;
+  const atd_config& c = d->cfg;
+  const int h = c.hidden, nq = c.n_q_heads * c.head_dim;
+  int br;
+  size_t rb;
+  gemv_block_rows(h, nq, wt, br, rb);
+  p.base[0] = (const char*)W.wo;
+  p.bb[0] = (size_t)br * rb;
+  p.nblk[0] = (int)std::min<size_t>(h / br, d->pf_budget / p.bb[0]);
+  size_t left = d->pf_budget - (size_t)p.nblk[0] * p.bb[0];
+  gemv_block_rows(c.ffn, h, wt, br, rb);
+  const size_t bb = (size_t)br * rb;
+  const int ng = (int)std::min<size_t>(c.ffn / br, left / (2 * bb));
+  p.nreg = 1;
+  if (ng > 0) {
+    p.base[1] = (const char*)W.w_gate;
+    p.base[2] = (const char*)W.w_up;
+    p.bb[1] = p.bb[2] = bb;
+    p.nblk[1] = p.nblk[2] = ng;
+    p.nreg = 3;
+  }
+  return p;
+}
+
 // GEMV path: the per-layer launch sequence for M <= 2 rows (or float32 weights).
 hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
                            hipStream_t s) {
@@ -434,7 +466,11 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
     STAGE(ATD_STAGE_QKV, launch_gemv(g, kEpiStore, true, wt, s));
     // prefill rows of one slot read each other's keys: append them all first
     if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
-    STAGE(ATD_STAGE_ATTN, attention(d, attn_args(d, rows, l, M, max_len_bound, fused), s));
+    {
+      AttnArgs aa = attn_args(d, rows, l, M, max_len_bound, fused);
+      if (fused) aa.pf = prefetch_plan(d, W, wt);
+      STAGE(ATD_STAGE_ATTN, attention(d, aa, s));
+    }
 
     GemvArgs op{};
     op.W[0] = W.wo;
@@ -895,9 +931,8 @@ void plan_scratch(const atd_config& c, bool in_proj, ScratchPlan& p) {
   p.o_act = carve((size_t)R * c.ffn * 4);
   // attention partials: M * Hq * attn_max_splits(L, M, Hkv) <= this many per head dim
   p.part_floats = (size_t)c.n_q_heads *
-                  std::max(std::min((size_t)R * ((c.max_ctx + kAttnMinChunk - 1) / kAttnMinChunk),
-                                    (size_t)(kAttnWavesMax / c.n_kv_heads + R)),
-                           (size_t)R * attn_max_splits(c.max_ctx, R, c.n_kv_heads, 0));
+                  std::min((size_t)R * ((c.max_ctx + kAttnMinChunk - 1) / kAttnMinChunk),
+                           (size_t)(kAttnWavesMax / c.n_kv_heads + R));
   p.o_pml = carve(p.part_floats * 2 * 4);
   p.o_pacc = carve(p.part_floats * D * 4);
   // MFMA path (bf16 dense weights, chunks of >= kMmaMinRows rows possible)
@@ -995,6 +1030,7 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->part_floats = sp.part_floats;
   d->mma = sp.mma;
   d->mma_rows = sp.mma_rows;
+  d->pf_budget = cfg->flags & ATD_FLAG_NO_L2_PREFETCH ? 0 : kL2PrefetchBytes;
   const size_t off = sp.total;
   const size_t o_cos = sp.o_cos, o_sin = sp.o_sin, o_rcos = sp.o_rcos, o_rsin = sp.o_rsin,
                o_x = sp.o_x, o_xin = sp.o_xin, o_qkv = sp.o_qkv, o_q = sp.o_q, o_o = sp.o_o,

@@ -24,25 +24,16 @@ constexpr int kAttnMinChunk = 16;     // fewest keys per split
 #endif
 
 // Keys per attention split for a row whose valid length is len, in a launch
-// of M rows over Hkv KV heads.  With a split-count target (waves > 0: few
-// rows) every row gets the same number of splits (all waves busy), each at
-// least kAttnMinChunk keys, a multiple of 16.  Without one (waves = 0: many
-// rows of mixed lengths) every split takes kAttnRowChunk keys (more only past
-// kAttnSplitsMax splits), so that the splits of long and short rows take
-// about equally long and the launch does not end on a few long rows.  Either
-// way the chunk depends on (len, M, Hkv, waves) only, never on the cache
-// capacity (results do not change when a bucket grows).
-constexpr int kAttnRowChunk = 128;
+// of M rows over Hkv KV heads aiming at `waves` splits in total: every row
+// gets the same number of splits (all waves busy), each at least
+// kAttnMinChunk keys, a multiple of 16.  Depends on (len, M, Hkv, waves)
+// only, never on the cache capacity (results do not change when a bucket
+// grows).
 inline ATD_HD int attn_splits_per_head(int M, int Hkv, int waves) {
   const int per = waves / (M * Hkv);
   return per < 1 ? 1 : (per > kAttnSplitsMax ? kAttnSplitsMax : per);
 }
 inline ATD_HD int attn_chunk(int len, int M, int Hkv, int waves) {
-  if (waves == 0) {
-    int c = (len + kAttnSplitsMax - 1) / kAttnSplitsMax;
-    c = (c + 15) & ~15;
-    return c < kAttnRowChunk ? kAttnRowChunk : c;
-  }
   const int per = attn_splits_per_head(M, Hkv, waves);
   int c = (len + per - 1) / per;
   c = (c + 15) & ~15;
@@ -51,10 +42,6 @@ inline ATD_HD int attn_chunk(int len, int M, int Hkv, int waves) {
 
 // Upper bound of the split count of any row of length <= max_len.
 inline int attn_max_splits(int max_len, int M, int Hkv, int waves) {
-  if (waves == 0) {
-    const int a = (max_len + kAttnRowChunk - 1) / kAttnRowChunk;
-    return a < kAttnSplitsMax ? a : kAttnSplitsMax;
-  }
   const int a = (max_len + kAttnMinChunk - 1) / kAttnMinChunk;
   const int b = attn_splits_per_head(M, Hkv, waves);
   return a < b ? a : b;
@@ -139,6 +126,26 @@ struct GemvArgs {
 
 
 
+// Weights that later launches read, pulled into the L2 of the XCD whose
+// compute units will read them.  The L2 of each XCD keeps its lines across
+// kernel boundaries, and workgroup w of every launch runs on XCD w % 8
+// (measured), so block b of a later 1-D launch finds on its own XCD whatever
+// a workgroup on XCD b % 8 loaded.  Region r describes such a launch: its
+// block b reads bytes [b * bb, (b + 1) * bb) of base[r] (bb a multiple of
+// 16), and the first nblk[r] blocks are covered.  The loads only warm the
+// cache: nothing is computed from them.
+constexpr int kPfRegions = 3;
+struct L2Prefetch {
+  const char* base[kPfRegions];
+  size_t bb[kPfRegions];
+  int nblk[kPfRegions];
+  int nreg;     // regions in use, 0 = no prefetch
+};
+// Bytes a step attention launch prefetches: 3 of the 4 MiB of each XCD's L2
+// (measured on the 1.7B step, O projection + gate/up prefix: 16 MiB 952,
+// 24 MiB 959, 28 MiB 939, 32 MiB 940 tokens/s against 926 without).
+constexpr size_t kL2PrefetchBytes = (size_t)24 << 20;
+
 struct AttnArgs {
   // fused (decode steps): q and the new k/v row come raw from qkv and get the
   // QK norm + RoPE here; the last split's wave appends the new row to the
@@ -170,6 +177,9 @@ struct AttnArgs {
   uint16_t* o_hi;     // or, when set, bf16 hi/lo parts of o: [M, Hq * D]
   uint16_t* o_lo;
   int o_frag;         // o_hi / o_lo in MFMA-fragment order (frag_off; M <= 64)
+  // with pf.nreg > 0 the launch has one more z slice (z = M) whose
+  // workgroups only run the prefetch
+  L2Prefetch pf;
 };
 
 struct EmbedArgs {
@@ -427,6 +437,9 @@ struct ReduceArgs {
 // Each returns the first HIP error of its launches (hipSuccess otherwise).
 hipError_t launch_embed(const EmbedArgs& a, int bf16, hipStream_t s);
 hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int wtype, hipStream_t s);
+// Rows of every weight matrix that block b of a launch_gemv of this shape
+// reads (rows b * br .. b * br + br - 1), and the bytes of a dense weight row.
+void gemv_block_rows(int N, int K, int wtype, int& br, size_t& row_bytes);
 
 struct QuantArgs {
   const void* w;         // [rows, cols] float32 or bf16

@@ -729,6 +729,39 @@ __device__ __forceinline__ float4 load_coherent4(const float* p) {
   return v;
 }
 
+// Prefetch workgroup j of P in a launch whose workgroup `lin` it is (on XCD
+// lin % 8): with the other prefetch workgroups of its XCD it loads every
+// 16-byte chunk that the covered blocks b = x, x + 8, ... of each region
+// read.  256 threads, eight loads in flight per thread: a share arrives over
+// a few round trips, which keeps the prefetch from crowding out the loads of
+// the launch's own workgroups (a whole share in one round trip was slower).
+__device__ __forceinline__ void l2_prefetch(const L2Prefetch& p, int j, int P, int lin) {
+  constexpr int NT = 256, U = 8;
+  const int x = lin & 7;
+  const int j0 = (x - (lin - j)) & 7;               // first prefetch workgroup on XCD x
+  const int per = (P - j0 + 7) >> 3, idx = j >> 3;  // workgroups on XCD x, this one's index
+  uint32_t acc = 0;
+  for (int r = 0; r < p.nreg; ++r) {
+    const uint32_t c16 = (uint32_t)(p.bb[r] >> 4);
+    const int nb = (p.nblk[r] - x + 7) >> 3;   // covered blocks on XCD x
+    if (nb <= 0) continue;
+    const uint32_t total = (uint32_t)nb * c16;
+    for (uint32_t t0 = (uint32_t)idx * NT * U + threadIdx.x; t0 < total; t0 += (uint32_t)per * NT * U) {
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t t = t0 + u * NT;
+        const uint32_t b = (uint32_t)x + 8u * (t / c16), c = t % c16;
+        v[u] = t < total ? ldg16(p.base[r] + (size_t)b * p.bb[r] + (size_t)c * 16)
+                         : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc |= v[u].x | v[u].y | v[u].z | v[u].w;
+    }
+  }
+  asm volatile("" ::"v"(acc));   // the loads count as used
+}
+
 template <typename KT, int D, int R, int LPK, int U>
 __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   constexpr int VEC = Vec16<KT>::N;   // channels per 16-byte load
@@ -738,6 +771,11 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   constexpr int TILE = KPW * U;       // keys per wave per tile (U rows per lane group)
   static_assert(NV >= 1 && DPL % 4 == 0, "a lane holds whole 16-byte groups");
 
+  if ((int)blockIdx.z == a.M) {   // the prefetch slice
+    const int j = blockIdx.x + gridDim.x * blockIdx.y, P = gridDim.x * gridDim.y;
+    l2_prefetch(a.pf, j, P, j + P * a.M);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x * 4 + wave, g = blockIdx.y, m = blockIdx.z;
   const int sub = lane / LPK, dl = (lane % LPK) * DPL;
@@ -2499,12 +2537,28 @@ static void gemv_shape(int K, int vec, int& ks, int& ki) {
   ki = ((nk + ks - 1) / ks + 63) / 64;
 }
 
+// rows per wave group: 4 when that still leaves >= 512 blocks
+static int gemv_rw(int N, int ks) { return ks == 4 || N >= 512 * (4 / ks) * 4 ? 4 : ks; }
+
+void gemv_block_rows(int N, int K, int wtype, int& br, size_t& row_bytes) {
+  int vec, bytes;
+  switch (wtype) {
+    case kWBF16: vec = WFmt<uint16_t>::N; bytes = WFmt<uint16_t>::BYTES; break;
+    case kWQ8: vec = WFmt<WQ8>::N; bytes = WFmt<WQ8>::BYTES; break;
+    case kWQ4: vec = WFmt<WQ4>::N; bytes = WFmt<WQ4>::BYTES; break;
+    default: vec = WFmt<float>::N; bytes = WFmt<float>::BYTES; break;
+  }
+  int ks, ki;
+  gemv_shape(K, vec, ks, ki);
+  br = (4 / ks) * gemv_rw(N, ks);
+  row_bytes = (size_t)(K / vec) * bytes;
+}
+
 template <typename WT, int MR, int EPI, bool NORM>
 static void gemv_dispatch_shape(const GemvArgs& a, hipStream_t s) {
   int ks, ki;
   gemv_shape(a.K, WFmt<WT>::N, ks, ki);
-  // 4 rows per wave group when that still leaves >= 512 blocks
-  const int rw = ks == 4 || a.N >= 512 * (4 / ks) * 4 ? 4 : ks;
+  const int rw = gemv_rw(a.N, ks);
   const int br = (4 / ks) * rw;   // rows per block
   const dim3 grid((a.N + br - 1) / br), block(256);
 #define ATD_GEMV(KS_, KI_, RW_) \
@@ -3055,7 +3109,10 @@ static void attn_dispatch_r(const AttnArgs& a, int r, dim3 grid, hipStream_t s) 
 }
 
 hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream_t s) {
-  dim3 grid((a.nsplit_max + 3) / 4, a.Hkv, a.M);
+  if (a.pf.nreg < 0 || a.pf.nreg > kPfRegions) return hipErrorInvalidValue;
+  for (int i = 0; i < a.pf.nreg; ++i)
+    if (!a.pf.base[i] || a.pf.bb[i] % 16 || a.pf.nblk[i] < 0) return hipErrorInvalidValue;
+  dim3 grid((a.nsplit_max + 3) / 4, a.Hkv, a.M + (a.pf.nreg > 0 ? 1 : 0));
   if (bf16) {
     if (D == 64)
       attn_dispatch_r<uint16_t, 64>(a, r, grid, s);

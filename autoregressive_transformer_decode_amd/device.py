@@ -137,14 +137,16 @@ class Decoder:
     """A decoder handle plus the KV buckets it holds for each slot."""
 
     def __init__(self, model: DeviceModel, max_slots: int = 1, max_rows: int = 1,
-                 max_ctx: int = 4096, mfma: bool = True, kv_dtype: Optional[str] = None):
+                 max_ctx: int = 4096, mfma: bool = True, kv_dtype: Optional[str] = None,
+                 l2_prefetch: bool = True):
         self.model = model
         s = model.shape
         if kv_dtype is not None and kv_dtype != s.kv_dtype:
             s = dataclasses.replace(s, kv_dtype=kv_dtype)
         self.shape = s
         self.cfg = make_config(s, max_slots, max_rows, max_ctx,
-                               flags=0 if mfma else B.ATD_FLAG_NO_MFMA,
+                               flags=(0 if mfma else B.ATD_FLAG_NO_MFMA) |
+                               (0 if l2_prefetch else B.ATD_FLAG_NO_L2_PREFETCH),
                                weight_format=model.weight_format)
         self.handle = B.decoder_create(self.cfg, model.weights)
         self.kv = {}   # slot -> (list of K tensors, list of V tensors)

@@ -283,7 +283,8 @@ def bench_lm(args, wl):
     X0 = inputs.prefill_embeddings(wl, seed=0)
     log(f"weights generated in {time.perf_counter() - t:.1f}s")
     dm = dv.DeviceModel(mw)
-    dec = dv.Decoder(dm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max)
+    dec = dv.Decoder(dm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max,
+                     l2_prefetch=not args.no_l2_prefetch)
     P0 = wl.prefill
     K = args.steps if args.steps is not None else wl.steps
     W = args.warmup
@@ -439,7 +440,7 @@ def bench_lm(args, wl):
                     layers=s.n_layers, hidden=s.hidden, heads=[s.n_q_heads, s.n_kv_heads],
                     head_dim=s.head_dim, ffn=s.ffn, vocab=s.vocab,
                     step="graph-replayed decode step + greedy argmax on device",
-                    kv_buckets=caps),
+                    kv_buckets=caps, l2_prefetch=not args.no_l2_prefetch),
         roofline=dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=traffic,
                       kernel="k_gemv (RMSNorm + gate/up + SwiGLU), bf16 weights",
@@ -470,7 +471,8 @@ def bench_lm(args, wl):
         out["quantized"] = {}
         for fmt in ("q8", "q4"):
             qdm = dv.DeviceModel(mw, quant=fmt)
-            qdec = dv.Decoder(qdm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max)
+            qdec = dv.Decoder(qdm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max,
+                              l2_prefetch=not args.no_l2_prefetch)
             qbuckets = [qdec.alloc_kv(c) for c in caps]
             qdec.grow(0, caps[0], kv=qbuckets[0])
             cur.update(dec=qdec, buckets=qbuckets)
@@ -671,8 +673,10 @@ def bench_frames(args, wl):
     cmw = inputs.make_weights(c, seed=0, tables=tmw.tables)
     tdm = dv.DeviceModel(tmw)
     cdm = dv.DeviceModel(cmw, tables=tdm.tables)
-    tdec = dv.Decoder(tdm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_init)
-    cdec = dv.Decoder(cdm, max_slots=1, max_rows=2, max_ctx=inputs.CP_CAPACITY)
+    tdec = dv.Decoder(tdm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_init,
+                      l2_prefetch=not args.no_l2_prefetch)
+    cdec = dv.Decoder(cdm, max_slots=1, max_rows=2, max_ctx=inputs.CP_CAPACITY,
+                      l2_prefetch=not args.no_l2_prefetch)
     tdec.grow(0, wl.s_init)
     cdec.grow(0, inputs.CP_CAPACITY)
     if wl.prefill + n - 1 > wl.s_init:
@@ -733,6 +737,7 @@ def bench_frames(args, wl):
         config=dict(workload=wl.name, frames=n, prefill=wl.prefill, penalty=wl.penalty,
                     talker_layers=s.n_layers, cp_layers=c.n_layers, hidden=s.hidden,
                     step="graph-replayed frames (talker_generate_frames)",
+                    l2_prefetch=not args.no_l2_prefetch,
                     timing="greedy and sampled runs of all frames alternate twice; each "
                            "leg reports its faster run"),
         codes_per_s=16 * fps, rtf_equivalent=(1.0 / fps) / 0.08,
@@ -923,6 +928,9 @@ def main():
                     help="skip the 64-stream leg of the default (1.7B) run")
     ap.add_argument("--no-sampled", action="store_true",
                     help="skip the sampled leg and the token-choice timing (counter runs)")
+    ap.add_argument("--no-l2-prefetch", action="store_true",
+                    help="decoders without the step attention's L2 weight prefetch "
+                         "(ATD_FLAG_NO_L2_PREFETCH; counter runs of the stand-alone gate/up GEMV)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 plain device copies of 256 MiB (counter calibration)")
     args = ap.parse_args()

@@ -139,6 +139,14 @@ typedef struct atd_config {
  * through matrix-core GEMMs: activations split into bf16 hi + lo parts, float32
  * accumulation, results within the same tolerance as the vector path. */
 #define ATD_FLAG_NO_MFMA 2
+/* ATD_FLAG_NO_L2_PREFETCH turns off the weight prefetch of the decode step's
+ * attention launch.  Without it, a step that runs on the matrix-vector
+ * kernels (fewer than 5 rows, or any step of a decoder without the
+ * matrix-core path) appends workgroups to each layer's attention launch that
+ * load the O projection's weights and then gate/up blocks (24 MiB in all)
+ * into the L2 of the XCD whose workgroups will read them next.  Results are
+ * identical either way. */
+#define ATD_FLAG_NO_L2_PREFETCH 4
 
 /* Device pointers of one layer.  Matrices are row-major [out, in] in the
  * config dtype, or their codes in a quantized weight_format (16-byte

@@ -100,6 +100,18 @@ def test_create_rejects_config(kw, code, needle):
     assert needle in str(ei.value)
 
 
+def test_create_accepts_documented_flags():
+    """Every flag atd.h documents is accepted; the next bit is not."""
+    for f in (B.ATD_FLAG_NO_MFMA, B.ATD_FLAG_NO_L2_PREFETCH,
+              B.ATD_FLAG_NO_MFMA | B.ATD_FLAG_NO_L2_PREFETCH):
+        cfg = _cfg(flags=B.ATD_FLAG_DRY_RUN | f)
+        h = B.decoder_create(cfg, FakeWeights(cfg).w)
+        B.decoder_destroy(h)
+    with pytest.raises(B.AtdError):
+        cfg = _cfg(flags=B.ATD_FLAG_DRY_RUN | 8)
+        B.decoder_create(cfg, FakeWeights(cfg).w)
+
+
 def test_create_rejects_weights():
     cfg = _cfg()
     with pytest.raises(B.AtdError) as ei:

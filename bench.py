@@ -71,7 +71,8 @@ def kernel_hash() -> str:
     launch shape), so that stored counters stay valid while other kernels in
     the file change."""
     return _source_hash(("template <typename WT, int MR, int KS, int KI, int EPI, bool NORM, int RW>",
-                         "static void gemv_shape(", "static void gemv_dispatch_shape(", "hipError_t launch_gemv("))
+                         "static void gemv_shape(", "static int gemv_rw(",
+                         "static void gemv_dispatch_shape(", "hipError_t launch_gemv("))
 
 
 # bytes per weight of the block-quantized formats: the code and 2 bytes of
@@ -241,15 +242,18 @@ def gemm_counters(role, rows):
     return None
 
 
-def traffic_per_launch(path=None, hashfn=None):
+def traffic_per_launch(algo, path=None, hashfn=None):
     """HBM bytes per launch from a committed counter summary, or None when the
-    kernel's source changed since the counters were taken."""
+    kernel's source changed since the counters were taken or the summary is of
+    another shape (its algorithmic bytes per launch differ from ``algo``)."""
     try:
         with open(path or TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_hash") != (hashfn or kernel_hash)():
+        return None
+    if t.get("algorithmic_bytes_per_launch") != algo:
         return None
     return t.get("bytes_per_launch")
 
@@ -293,7 +297,7 @@ def bench_lm(args, wl):
     # fewer timed steps than the workload's: fast-forward (untimed) so that the
     # timed steps sit around the workload's mean context ((P0 + 1 + s_max) / 2)
     skip = max(0, int(round((P0 + 1 + wl.s_max) / 2.0 - P0 - (K + 1) / 2.0)))
-    skip = min(skip, wl.s_max - P0 - max(K, W))
+    skip = 0 if args.no_fast_forward else min(skip, wl.s_max - P0 - max(K, W))
     # bucket ladder: the cache doubles before a write at its capacity (ASR report's
     # dynamic window); the buckets are allocated up front, outside the timing
     caps = [wl.s_init]
@@ -425,7 +429,7 @@ def bench_lm(args, wl):
     launches = reps * s.n_layers
     per_launch = gateup_bytes(s)
     achieved = per_launch / avg_s / 1e9
-    traffic = traffic_per_launch()
+    traffic = traffic_per_launch(per_launch)
 
     attainable = read_stream_gbs()
     mean_ctx = P0 + skip + (K + 1) / 2.0
@@ -467,7 +471,7 @@ def bench_lm(args, wl):
     dec.close()
     # the same greedy run with the seven per-layer matrices block-quantized
     # (int8 / 4-bit codes, fp16 scale per 32 weights, dequantized in the GEMV)
-    if s.dtype == "bf16":
+    if s.dtype == "bf16" and not args.no_quantized:
         out["quantized"] = {}
         for fmt in ("q8", "q4"):
             qdm = dv.DeviceModel(mw, quant=fmt)
@@ -488,7 +492,8 @@ def bench_lm(args, wl):
                               frac=qb / (dt_q / K) / 1e9 / HBM_PEAK_GBS),
                 gate_up=dict(avg_launch_us=qg * 1e6, bytes_per_launch=gateup_bytes(s, fmt),
                              achieved_gbs=gateup_bytes(s, fmt) / qg / 1e9,
-                             traffic=traffic_per_launch(QUANT_TRAFFIC_FILE.format(fmt))))
+                             traffic=traffic_per_launch(gateup_bytes(s, fmt),
+                                                        QUANT_TRAFFIC_FILE.format(fmt))))
             qdec.close()
             del qdec, qbuckets, qdm
             torch.cuda.empty_cache()
@@ -599,7 +604,7 @@ def bench_batched(args, wl, dm=None, mw=None, steps=None, warmup=None):
                     layers=s.n_layers, hidden=s.hidden, ffn=s.ffn, vocab=s.vocab),
         roofline=dict(bound="hbm", achieved=a_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=a_gbs / HBM_PEAK_GBS,
-                      traffic=traffic_per_launch(ATTN_TRAFFIC_FILE, attn_kernel_hash),
+                      traffic=traffic_per_launch(a_bytes, ATTN_TRAFFIC_FILE, attn_kernel_hash),
                       traffic_kernel="k_attn_split (counters of the split kernel alone)",
                       kernel="attention stage (k_attn_split, combine inside), 64 rows",
                       bytes_per_launch=a_bytes, avg_launch_us=st["attention"],
@@ -928,6 +933,11 @@ def main():
                     help="skip the 64-stream leg of the default (1.7B) run")
     ap.add_argument("--no-sampled", action="store_true",
                     help="skip the sampled leg and the token-choice timing (counter runs)")
+    ap.add_argument("--no-fast-forward", action="store_true",
+                    help="time the steps right after the prefill instead of centring them on "
+                         "the workload's mean context (short counter runs)")
+    ap.add_argument("--no-quantized", action="store_true",
+                    help="skip the int8 / 4-bit weight legs (short counter runs)")
     ap.add_argument("--no-l2-prefetch", action="store_true",
                     help="decoders without the step attention's L2 weight prefetch "
                          "(ATD_FLAG_NO_L2_PREFETCH; counter runs of the stand-alone gate/up GEMV)")

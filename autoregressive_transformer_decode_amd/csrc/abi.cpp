@@ -400,11 +400,12 @@ RopeArgs rope_args(const atd_decoder* d, RowMap rows, int l, int M) {
 }
 
 // The prefetch plan of layer l's step attention: the O projection's weights,
-// then as many gate/up blocks as the budget leaves (whole blocks only, so no
-// load passes the end of a matrix).
-L2Prefetch prefetch_plan(const atd_decoder* d, const atd_layer_weights& W, int wt) {
+// then as many gate/up blocks as the budget leaves, then down blocks if gate/up
+// fit whole (whole blocks only, so no load passes the end of a matrix).
+L2Prefetch prefetch_plan(const atd_decoder* d, const atd_layer_weights& W, int wt, int wgs) {
   L2Prefetch p{};
-  if (d->pf_budget == 0) return p;
+  const size_t budget = d->pf_budget * std::min(wgs, kPfWorkgroups) / kPfWorkgroups;
+  if (budget == 0) return p;
   const atd_config& c = d->cfg;
   const int h = c.hidden, nq = c.n_q_heads * c.head_dim;
   int br;
@@ -412,8 +413,8 @@ L2Prefetch prefetch_plan(const atd_decoder* d, const atd_layer_weights& W, int w
   gemv_block_rows(h, nq, wt, br, rb);
   p.base[0] = (const char*)W.wo;
   p.bb[0] = (size_t)br * rb;
-  p.nblk[0] = (int)std::min<size_t>(h / br, d->pf_budget / p.bb[0]);
-  size_t left = d->pf_budget - (size_t)p.nblk[0] * p.bb[0];
+  p.nblk[0] = (int)std::min<size_t>(h / br, budget / p.bb[0]);
+  size_t left = budget - (size_t)p.nblk[0] * p.bb[0];
   gemv_block_rows(c.ffn, h, wt, br, rb);
   const size_t bb = (size_t)br * rb;
   const int ng = (int)std::min<size_t>(c.ffn / br, left / (2 * bb));
@@ -424,6 +425,17 @@ L2Prefetch prefetch_plan(const atd_decoder* d, const atd_layer_weights& W, int w
     p.bb[1] = p.bb[2] = bb;
     p.nblk[1] = p.nblk[2] = ng;
     p.nreg = 3;
+    left -= 2 * (size_t)ng * bb;
+  }
+  if (ng == c.ffn / br) {
+    gemv_block_rows(h, c.ffn, wt, br, rb);
+    p.bb[3] = (size_t)br * rb;
+    const int nd = (int)std::min<size_t>(h / br, left / p.bb[3]);
+    if (nd > 0) {
+      p.base[3] = (const char*)W.w_down;
+      p.nblk[3] = nd;
+      p.nreg = 4;
+    }
   }
   return p;
 }
@@ -468,7 +480,12 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
     if (!fused) STAGE(ATD_STAGE_ROPE, launch_rope_append(rope_args(d, rows, l, M), kv_bf16, s));
     {
       AttnArgs aa = attn_args(d, rows, l, M, max_len_bound, fused);
-      if (fused) aa.pf = prefetch_plan(d, W, wt);
+      // only where a row's keys can span several blocks: their ticket merge
+      // makes the launch long enough to hide the loads (a one-block launch,
+      // e.g. over the Code Predictor's 16-row cache, would only be lengthened);
+      // the prefetch slice has one workgroup per (block, KV head)
+      const int gx = (aa.nsplit_max + 3) / 4;
+      if (fused && gx > 1) aa.pf = prefetch_plan(d, W, wt, gx * c.n_kv_heads);
       STAGE(ATD_STAGE_ATTN, attention(d, aa, s));
     }
 

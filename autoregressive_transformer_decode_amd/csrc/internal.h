@@ -134,7 +134,7 @@ struct GemvArgs {
 // block b reads bytes [b * bb, (b + 1) * bb) of base[r] (bb a multiple of
 // 16), and the first nblk[r] blocks are covered.  The loads only warm the
 // cache: nothing is computed from them.
-constexpr int kPfRegions = 3;
+constexpr int kPfRegions = 4;
 struct L2Prefetch {
   const char* base[kPfRegions];
   size_t bb[kPfRegions];
@@ -145,6 +145,10 @@ struct L2Prefetch {
 // (measured on the 1.7B step, O projection + gate/up prefix: 16 MiB 952,
 // 24 MiB 959, 28 MiB 939, 32 MiB 940 tokens/s against 926 without).
 constexpr size_t kL2PrefetchBytes = (size_t)24 << 20;
+// Prefetch workgroups for the whole budget: a launch whose slice has fewer
+// (gx * Hkv of them) prefetches proportionally less, so that each
+// workgroup's share, and the time it takes, stay the same.
+constexpr int kPfWorkgroups = 256;
 
 struct AttnArgs {
   // fused (decode steps): q and the new k/v row come raw from qkv and get the

@@ -142,10 +142,12 @@ typedef struct atd_config {
 /* ATD_FLAG_NO_L2_PREFETCH turns off the weight prefetch of the decode step's
  * attention launch.  Without it, a step that runs on the matrix-vector
  * kernels (fewer than 5 rows, or any step of a decoder without the
- * matrix-core path) appends workgroups to each layer's attention launch that
- * load the O projection's weights and then gate/up blocks (24 MiB in all)
- * into the L2 of the XCD whose workgroups will read them next.  Results are
- * identical either way. */
+ * matrix-core path) and whose attention can span several blocks per row
+ * (contexts above 64) appends workgroups to each layer's attention launch that
+ * load the O projection's weights, then gate/up blocks, then (where gate/up
+ * fit whole) down blocks into the L2 of the XCD whose workgroups will read
+ * them next: 24 MiB, or proportionally less where the launch has fewer than
+ * 256 (block, KV head) pairs.  Results are identical either way. */
 #define ATD_FLAG_NO_L2_PREFETCH 4
 
 /* Device pointers of one layer.  Matrices are row-major [out, in] in the

@@ -167,7 +167,7 @@ struct AttnArgs {
   SlotTables st;
   RowMap rows;
   int layer, M, Hq, Hkv, nsplit_max;   // nsplit_max: split stride of the partials
-  int waves;                           // split-count target, 0: fixed chunks (attn_chunk)
+  int waves;                           // split-count target of the launch (attn_chunk)
   // single-slot launches: the slot's cache rows of this layer and capacity,
   // passed directly so no pointer table is read (null: use st)
   void* k_direct;

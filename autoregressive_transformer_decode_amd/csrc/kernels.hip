@@ -4,22 +4,28 @@
 // qwen3-tts-hip OPTIMIZATION_LOG (DecodeStepStack entry): input norm, q/k/v
 // projection, q/k layout + cache write, attention, output projection +
 // residual, post norm, gate/up projection, SwiGLU, down projection +
-// residual.  Here the norms are fused into the projection that consumes
-// them, SwiGLU into the gate/up projection, the residual adds into the
-// projections that produce them, and no layout permute exists at all (the
+// residual.  Here it is five launches: the norms are fused into the
+// projection that consumes them, SwiGLU into the gate/up projection, the
+// residual adds into the projections that produce them, the QK norm, RoPE
+// and cache append into the attention, and no layout permute exists (the
 // cache row is written in its final [Hkv, S, D] place).
 //
-// Decode at batch 1 is bound by HBM bandwidth: every weight byte is read
-// once per step and used for one multiply-add per row.  The projections are
-// therefore GEMVs that stream 16-byte vectors of weights per lane with all
-// 64 lanes of a wave on consecutive addresses of one row, several rows per
-// wave for bytes in flight, and the normalised input vector staged once per
-// workgroup in LDS.  No matrix-core (MFMA) work is involved at this size.
+// At batch 1 the step is bound by HBM bandwidth and launch latency: every
+// weight byte is read once and used for one multiply-add, so the projections
+// are GEMVs (k_gemv) that stream 16-byte vectors of weights per lane, all 64
+// lanes of a wave on consecutive addresses of a row, with the input row held
+// in registers.  The attention launch also carries workgroups that load the
+// next launches' weights into the L2 of the XCDs that will read them
+// (l2_prefetch).  From 5 rows on, the projections run on the matrix cores:
+// k_gemm_dec for chunks of up to 64 rows (split reduction and epilogue in
+// the same launch), k_gemm_tile / k_gemm for prefill chunks, with the
+// float32 activations as bf16 hi + lo operands.
 //
-// Attention at decode reads the K and V rows once; the key range is split
-// into fixed chunks (split-K over the sequence) whose partial softmax
-// states (running max, sum, weighted V) are merged in a fixed order, so
-// results do not depend on the cache capacity or on launch timing.
+// Attention at decode reads the K and V rows once; each row's key range is
+// split into chunks set by its valid length (split-K over the sequence)
+// whose partial softmax states (running max, sum, weighted V) are merged in a
+// fixed order inside the launch, so results depend neither on the cache
+// capacity nor on launch timing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -289,6 +289,20 @@ def bench_lm(args, wl):
     dm = dv.DeviceModel(mw)
     dec = dv.Decoder(dm, max_slots=1, max_rows=wl.prefill, max_ctx=wl.s_max,
                      l2_prefetch=not args.no_l2_prefetch)
+    if args.roofline_only:
+        # the roofline kernel alone, as measured for the bench line: its
+        # launches for every layer's weights in turn between two HIP events
+        reps = 16
+        dec.grow(0, wl.s_init)   # time_stage steps an attached slot
+        dec.time_stage(B.ATD_STAGE_GATEUP, 0, 1, 4)
+        avg_s = dec.time_stage(B.ATD_STAGE_GATEUP, 0, 1, reps) / 1e6
+        per_launch = gateup_bytes(s)
+        dec.close()
+        return dict(roofline_only=True, workload=wl.name, launches_timed=reps * s.n_layers,
+                    kernel="k_gemv (RMSNorm + gate/up + SwiGLU), bf16 weights",
+                    avg_launch_us=avg_s * 1e6, bytes_per_launch=per_launch,
+                    achieved_gbs=per_launch / avg_s / 1e9,
+                    frac=per_launch / avg_s / 1e9 / HBM_PEAK_GBS)
     P0 = wl.prefill
     K = args.steps if args.steps is not None else wl.steps
     W = args.warmup
@@ -938,6 +952,8 @@ def main():
                          "the workload's mean context (short counter runs)")
     ap.add_argument("--no-quantized", action="store_true",
                     help="skip the int8 / 4-bit weight legs (short counter runs)")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the stand-alone timing of the roofline kernel (for its kernel trace)")
     ap.add_argument("--no-l2-prefetch", action="store_true",
                     help="decoders without the step attention's L2 weight prefetch "
                          "(ATD_FLAG_NO_L2_PREFETCH; counter runs of the stand-alone gate/up GEMV)")

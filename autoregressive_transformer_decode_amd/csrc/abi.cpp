@@ -440,7 +440,8 @@ L2Prefetch prefetch_plan(const atd_decoder* d, const atd_layer_weights& W, int w
   return p;
 }
 
-// GEMV path: the per-layer launch sequence for M <= 2 rows (or float32 weights).
+// GEMV path: the per-layer launch sequence for fewer than kMmaMinRows rows (or any
+// rows without the matrix-core path: float32 or quantized weights, ATD_FLAG_NO_MFMA).
 hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound, float* x,
                            hipStream_t s) {
   const atd_config& c = d->cfg;

@@ -86,17 +86,20 @@ def test_mrope_prefill_and_steps(kind):
     assert chk.tokens_checked >= 5
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f32"])
-def test_mrope_batched_step(kind):
-    """Three streams with different histories step together, each row with
-    its own distinct (t, h, w) (bf16: the MFMA path at B = 3)."""
+@pytest.mark.parametrize("kind,B", [("bf16", 3), ("bf16", 5), ("f32", 3)])
+def test_mrope_batched_step(kind, B):
+    """B streams with different histories step together, each row with its
+    own distinct (t, h, w): bf16 at B = 3 on the vector path (two launches of
+    two rows and one), at B = 5 on the matrix-core path; f32 on the vector
+    path."""
     shape = _shape(kind)
     mw = inputs.make_weights(shape, seed=32, gain_sd=GAIN_SD)
     om = oracle_from_weights(mw, np.float64)
     dm = dv.DeviceModel(mw)
-    dec = dv.Decoder(dm, max_slots=3, max_rows=16, max_ctx=64)
-    lens = (5, 9, 16)
-    step_pos = np.array([[7, 3, 9], [12, 12, 5], [2, 30, 31]], np.int32)
+    dec = dv.Decoder(dm, max_slots=B, max_rows=16, max_ctx=64)
+    lens = (5, 9, 16, 3, 12)[:B]
+    step_pos = np.array([[7, 3, 9], [12, 12, 5], [2, 30, 31], [4, 8, 1], [20, 2, 33]],
+                        np.int32)[:B]
     z_refs, toks = [], []
     for b, T in enumerate(lens):
         dec.grow(b, 64)
@@ -109,19 +112,19 @@ def test_mrope_batched_step(kind):
         t = 17 * b + 3
         toks.append(t)
         z_refs.append(od.step(om, cache, om.tables[0][t], 0, rope_pos=step_pos[b]))
-    z = torch.empty(3, shape.vocab, device="cuda")
-    y = torch.empty(3, shape.hidden, device="cuda")
-    tok = torch.tensor(toks, dtype=torch.int32, device="cuda").view(3, 1)
-    dec.step(tok, [0], slot0=0, nrows=3, y_out=y, logits_out=z,
+    z = torch.empty(B, shape.vocab, device="cuda")
+    y = torch.empty(B, shape.hidden, device="cuda")
+    tok = torch.tensor(toks, dtype=torch.int32, device="cuda").view(B, 1)
+    dec.step(tok, [0], slot0=0, nrows=B, y_out=y, logits_out=z,
              rope_pos=torch.from_numpy(step_pos).cuda())
     torch.cuda.synchronize()
     chk = StepCheck()
-    for b in range(3):
+    for b in range(B):
         chk.add(y[b].cpu().numpy(), z[b].cpu().numpy(), z_refs[b][0], z_refs[b][1],
                 f"{kind} row {b}")
         assert dec.position(b)[0] == lens[b] + 1
     dec.close()
-    _log(f"mrope batched {kind}: worst {chk.worst:.2e}")
+    _log(f"mrope batched {kind} B={B}: worst {chk.worst:.2e}")
 
 
 def test_mrope_equal_positions_bitwise():

@@ -110,10 +110,10 @@ def test_multi_stream_steps():
 
 
 def test_step_slot_list():
-    """decoder_step_slots over non-contiguous slots in scrambled order: three
-    rows (matrix-core chunk), two rows (vector kernels) and one row (the
-    single-slot attention path) stepping subsets of six streams; every row
-    equals its own stream's oracle run, and streams left out do not move."""
+    """decoder_step_slots over non-contiguous slots in scrambled order: two to
+    four rows (vector kernels), one row (the single-slot attention path), five
+    and six rows (a matrix-core chunk) stepping subsets of six streams; every
+    row equals its own stream's oracle run, and streams left out do not move."""
     shape = small_shape("slots", 2, 256, 8, 2, 128, 512, 500, "bf16", True, False)
     mw = inputs.make_weights(shape, seed=41, gain_sd=GAIN_SD)
     om = oracle_from_weights(mw)
@@ -132,7 +132,7 @@ def test_step_slot_list():
         dec.prefill(torch.from_numpy(X).cuda(), slot=b)
     steps = {b: 0 for b in range(n)}
     worst = 0.0
-    for slots in ([5, 1, 3], [4, 0], [2], [3, 0, 5, 2], [1]):
+    for slots in ([5, 1, 3], [4, 0], [2], [3, 0, 5, 2], [1], [0, 2, 4, 1, 5], [5, 4, 3, 2, 1, 0]):
         Bn = len(slots)
         y = torch.empty(Bn, shape.hidden, device="cuda")
         z = torch.empty(Bn, shape.vocab, device="cuda")

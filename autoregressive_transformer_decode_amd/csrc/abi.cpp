@@ -71,6 +71,9 @@ struct atd_decoder {
   // L2 prefetch from the step attention launch: bytes of the O projection
   // and gate/up weights to pull ahead (0 = none)
   size_t pf_budget = 0;
+  // dense bf16 weights streamed with the nontemporal cache policy (weights
+  // larger than the memory-side cache, which they could not stay in anyway)
+  bool stream_nt = false;
   // graph cache of decoder_generate
   hipStream_t cap_stream = nullptr;
   struct GraphEntry {
@@ -230,11 +233,26 @@ int check_config(const atd_config* c) {
   return ATD_OK;
 }
 
-// Weight type of the seven per-layer matrices.
-int layer_wtype(const atd_config& c) {
+// Weight type of the seven per-layer matrices (dense bf16 of a decoder whose
+// weights exceed the memory-side cache: streamed nontemporally).
+int layer_wtype(const atd_decoder* d) {
+  const atd_config& c = d->cfg;
   if (c.weight_format == ATD_WFMT_Q8) return kWQ8;
   if (c.weight_format == ATD_WFMT_Q4) return kWQ4;
-  return c.dtype == ATD_BF16 ? kWBF16 : kWF32;
+  return c.dtype != ATD_BF16 ? kWF32 : d->stream_nt ? kWBF16NT : kWBF16;
+}
+// ... and of the LM heads (always dense)
+int head_wtype(const atd_decoder* d) {
+  return d->cfg.dtype != ATD_BF16 ? kWF32 : d->stream_nt ? kWBF16NT : kWBF16;
+}
+
+// Bytes of a decoder's dense matrices: the seven per layer and the LM heads.
+size_t dense_weight_bytes(const atd_config& c) {
+  const size_t h = c.hidden, nq = (size_t)c.n_q_heads * c.head_dim,
+               nkv = (size_t)c.n_kv_heads * c.head_dim, F = c.ffn;
+  const size_t per_layer = (nq + 2 * nkv) * h + h * nq + 3 * F * h;
+  const size_t el = c.dtype == ATD_BF16 ? 2 : 4;
+  return (per_layer * c.n_layers + (size_t)c.n_lm_heads * c.vocab * h) * el;
 }
 
 #define NEED(ptr, name)                                                                    \
@@ -447,7 +465,7 @@ hipError_t run_layers_gemv(atd_decoder* d, RowMap rows, int M, int max_len_bound
   const atd_config& c = d->cfg;
   const int h = c.hidden, D = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
   const int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv;
-  const int wt = layer_wtype(c);
+  const int wt = layer_wtype(d);
   const int kv_bf16 = c.kv_dtype == ATD_BF16;
   const bool fused = rows.mode == kRowsStep;
   hipError_t e = hipSuccess;
@@ -554,7 +572,7 @@ hipError_t run_head_gemv(atd_decoder* d, const float* xrows, int M, int head, fl
   g.K = c.hidden;
   g.N = c.vocab;
   g.M = M;
-  STAGE(ATD_STAGE_HEAD, launch_gemv(g, kEpiStore, true, c.dtype == ATD_BF16 ? kWBF16 : kWF32, s));
+  STAGE(ATD_STAGE_HEAD, launch_gemv(g, kEpiStore, true, head_wtype(d), s));
   return e;
 }
 
@@ -874,7 +892,7 @@ hipError_t project_rows(atd_decoder* d, int M, hipStream_t s) {
   g.K = d->in_dim;
   g.N = c.hidden;
   g.M = M;
-  return launch_gemv(g, kEpiStore, false, c.dtype == ATD_BF16 ? kWBF16 : kWF32, s);
+  return launch_gemv(g, kEpiStore, false, head_wtype(d), s);
 }
 
 // Input rows of M tokens / extra rows built and projected into d->x.
@@ -1049,6 +1067,8 @@ extern "C" int decoder_create(const atd_config* cfg, const atd_weights* w, atd_d
   d->mma = sp.mma;
   d->mma_rows = sp.mma_rows;
   d->pf_budget = cfg->flags & ATD_FLAG_NO_L2_PREFETCH ? 0 : kL2PrefetchBytes;
+  d->stream_nt = cfg->weight_format == ATD_WFMT_DENSE && cfg->dtype == ATD_BF16 &&
+                 dense_weight_bytes(*cfg) > kMallBytes;
   const size_t off = sp.total;
   const size_t o_cos = sp.o_cos, o_sin = sp.o_sin, o_rcos = sp.o_rcos, o_rsin = sp.o_rsin,
                o_x = sp.o_x, o_xin = sp.o_xin, o_qkv = sp.o_qkv, o_q = sp.o_q, o_o = sp.o_o,

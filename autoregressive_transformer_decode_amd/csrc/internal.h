@@ -102,7 +102,10 @@ enum GemvEpilogue { kEpiStore = 0, kEpiResidual = 1, kEpiSwiglu = 2 };
 
 // Weight storage of a GEMV: dense float32 / bf16, or block-quantized codes
 // (int8, or 4-bit pairs) with one fp16 scale per kQBlock weights of a row.
-enum WeightType { kWF32 = 0, kWBF16 = 1, kWQ8 = 2, kWQ4 = 3 };
+// kWBF16NT: bf16 weights streamed with the nontemporal cache policy (for
+// decoders whose weights exceed the memory-side cache, kMallBytes)
+enum WeightType { kWF32 = 0, kWBF16 = 1, kWQ8 = 2, kWQ4 = 3, kWBF16NT = 4 };
+constexpr size_t kMallBytes = (size_t)256 << 20;
 constexpr int kQBlock = 32;
 
 struct GemvArgs {

@@ -161,6 +161,20 @@ __device__ __forceinline__ uint32_t ldg4(const void* p) {
   return *reinterpret_cast<const uint32_t*>(p);
 #endif
 }
+
+// The 16-byte load with the nontemporal cache policy (bit nt), for weights
+// that a launch streams once: the caches let such lines go first, so the
+// stream does not push out what is read again (activations, weights
+// prefetched into L2 for the next launch).
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(1))) const V4U32 GV4U32;
+  const V4U32 v = __builtin_nontemporal_load((GV4U32*)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
 __device__ __forceinline__ uint16_t ldg2(const uint16_t* p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   return *(__attribute__((address_space(1))) const uint16_t*)(p);
@@ -213,6 +227,18 @@ struct WFmt {    // dense float32 / bf16
   static constexpr float OFF = 0.f;
   __device__ static __forceinline__ uint4 load(const char* p) { return ldg16(p); }
   __device__ static __forceinline__ void unpack(const uint4& r, float* f) { Vec16<WT>::unpack(r, f); }
+};
+// bf16 weights loaded with the nontemporal policy: for decoders whose weights
+// do not fit the memory-side cache (measured: the 1.7B step and the stand-alone
+// gate/up GEMV faster; a decoder that fits, such as the ASR shape, slower)
+struct Bf16Nt {};
+template <>
+struct WFmt<Bf16Nt> {
+  static constexpr int N = 8, BYTES = 16;
+  static constexpr bool Q = false;
+  static constexpr float OFF = 0.f;
+  __device__ static __forceinline__ uint4 load(const char* p) { return ldg16_nt(p); }
+  __device__ static __forceinline__ void unpack(const uint4& r, float* f) { Vec16<uint16_t>::unpack(r, f); }
 };
 template <>
 struct WFmt<WQ8> {
@@ -2238,7 +2264,7 @@ __global__ __launch_bounds__(512) void k_gemm_dec(DecGemmArgs a) {
   auto issue = [&](int d, int t) {
     const int k = min(kb + (t * NWV + wave) * kDecKStep, K - kDecKStep);
 #pragma unroll
-    for (int j = 0; j < CB; ++j) wv[d][j] = ldg16(wblk[j] + (size_t)(k >> 5) * 512);
+    for (int j = 0; j < CB; ++j) wv[d][j] = ldg16_nt(wblk[j] + (size_t)(k >> 5) * 512);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const size_t f = ((size_t)((k >> 5) * 4 + i) * 64 + lane) * 8;
@@ -2549,7 +2575,8 @@ static int gemv_rw(int N, int ks) { return ks == 4 || N >= 512 * (4 / ks) * 4 ? 
 void gemv_block_rows(int N, int K, int wtype, int& br, size_t& row_bytes) {
   int vec, bytes;
   switch (wtype) {
-    case kWBF16: vec = WFmt<uint16_t>::N; bytes = WFmt<uint16_t>::BYTES; break;
+    case kWBF16:
+    case kWBF16NT: vec = WFmt<uint16_t>::N; bytes = WFmt<uint16_t>::BYTES; break;
     case kWQ8: vec = WFmt<WQ8>::N; bytes = WFmt<WQ8>::BYTES; break;
     case kWQ4: vec = WFmt<WQ4>::N; bytes = WFmt<WQ4>::BYTES; break;
     default: vec = WFmt<float>::N; bytes = WFmt<float>::BYTES; break;
@@ -3039,6 +3066,7 @@ hipError_t launch_attn_prefill(const AttnArgs& a, int bf16, int D, int r, hipStr
 hipError_t launch_gemv(const GemvArgs& a, int epi, bool norm, int wtype, hipStream_t s) {
   switch (wtype) {
     case kWBF16: gemv_dispatch<uint16_t>(a, epi, norm, s); break;
+    case kWBF16NT: gemv_dispatch<Bf16Nt>(a, epi, norm, s); break;
     case kWQ8: gemv_dispatch<WQ8>(a, epi, norm, s); break;
     case kWQ4: gemv_dispatch<WQ4>(a, epi, norm, s); break;
     default: gemv_dispatch<float>(a, epi, norm, s); break;

@@ -246,13 +246,15 @@ int head_wtype(const atd_decoder* d) {
   return d->cfg.dtype != ATD_BF16 ? kWF32 : d->stream_nt ? kWBF16NT : kWBF16;
 }
 
-// Bytes of a decoder's dense matrices: the seven per layer and the LM heads.
+// Bytes of a decoder's dense matrices: the seven per layer, the LM heads and
+// the input projection (when the input rows are narrower or wider than h).
 size_t dense_weight_bytes(const atd_config& c) {
   const size_t h = c.hidden, nq = (size_t)c.n_q_heads * c.head_dim,
                nkv = (size_t)c.n_kv_heads * c.head_dim, F = c.ffn;
   const size_t per_layer = (nq + 2 * nkv) * h + h * nq + 3 * F * h;
+  const size_t in_proj = c.input_dim && c.input_dim != c.hidden ? (size_t)c.input_dim * h : 0;
   const size_t el = c.dtype == ATD_BF16 ? 2 : 4;
-  return (per_layer * c.n_layers + (size_t)c.n_lm_heads * c.vocab * h) * el;
+  return (per_layer * c.n_layers + (size_t)c.n_lm_heads * c.vocab * h + in_proj) * el;
 }
 
 #define NEED(ptr, name)                                                                    \

@@ -16,7 +16,8 @@
 // lanes of a wave on consecutive addresses of a row, with the input row held
 // in registers.  The attention launch also carries workgroups that load the
 // next launches' weights into the L2 of the XCDs that will read them
-// (l2_prefetch).  From 5 rows on, the projections run on the matrix cores:
+// (l2_prefetch), and weights read once are streamed with the nontemporal
+// cache policy so that they do not evict those lines.  From 5 rows on, the projections run on the matrix cores:
 // k_gemm_dec for chunks of up to 64 rows (split reduction and epilogue in
 // the same launch), k_gemm_tile / k_gemm for prefill chunks, with the
 // float32 activations as bf16 hi + lo operands.

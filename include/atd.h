@@ -147,7 +147,8 @@ typedef struct atd_config {
  * load the O projection's weights, then gate/up blocks, then (where gate/up
  * fit whole) down blocks into the L2 of the XCD whose workgroups will read
  * them next: 24 MiB, or proportionally less where the launch has fewer than
- * 256 (block, KV head) pairs.  Results are identical either way. */
+ * 256 (block, KV head) pairs, and nothing where that share cannot take the
+ * whole O projection.  Results are identical either way. */
 #define ATD_FLAG_NO_L2_PREFETCH 4
 
 /* Device pointers of one layer.  Matrices are row-major [out, in] in the

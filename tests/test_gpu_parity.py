@@ -216,11 +216,12 @@ def assert_logits_unchanged(zt, z):
     return np.array_equal(zt.cpu().numpy(), z)
 
 
-def _run_ids(mw, X0, steps, s_init, tok_seq, l2_prefetch=True):
+def _run_ids(mw, X0, steps, s_init, tok_seq, l2_prefetch=True, max_ctx=512):
     """GPU run teacher-forced by tok_seq; returns every step's logits."""
     s = mw.shape
     dm = dv.DeviceModel(mw)
-    dec = dv.Decoder(dm, max_slots=1, max_rows=X0.shape[0], max_ctx=512, l2_prefetch=l2_prefetch)
+    dec = dv.Decoder(dm, max_slots=1, max_rows=X0.shape[0], max_ctx=max_ctx,
+                     l2_prefetch=l2_prefetch)
     dec.grow(0, s_init)
     z = torch.empty(1, s.vocab, device="cuda")
     dec.prefill(torch.from_numpy(X0).cuda(), logits_out=z[0])
@@ -254,25 +255,27 @@ def test_bucket_growth_bitwise_and_determinism():
 
 
 @pytest.mark.parametrize("dims", [
-    # small matrices (fewer O-projection blocks than XCDs on some), bf16
-    ("pf_small", 2, 256, 8, 2, 128, 512, 1000, "bf16"),
-    # O + gate/up beyond the 24 MiB budget: the prefetch covers a prefix of
-    # the gate/up blocks (the 1.7B layer widths)
-    ("pf_wide", 2, 2048, 16, 8, 128, 6144, 1000, "bf16"),
-    # float32 weights, head_dim 64
-    ("pf_f32", 1, 512, 8, 4, 64, 1024, 500, "f32"),
+    # small matrices (fewer O-projection blocks than XCDs on some), bf16: at a
+    # 512-row bucket the slice (16 workgroups, 1.5 MiB) takes O, gate/up and down
+    ("pf_small", 2, 256, 8, 2, 128, 512, 1000, "bf16", 512),
+    # the 1.7B layer widths at a 2048-row bucket: O + a prefix of the gate/up
+    # blocks (24 MiB)
+    ("pf_wide", 2, 2048, 16, 8, 128, 6144, 1000, "bf16", 2048),
+    # float32 weights, head_dim 64: O + a gate/up prefix (3 MiB)
+    ("pf_f32", 1, 512, 8, 4, 64, 1024, 500, "f32", 512),
 ])
 def test_l2_prefetch_leaves_results_unchanged(dims):
     """The workgroups that the step attention launch appends only load weights
     into L2: every step's logits equal those of a decoder without them, bit
-    for bit, over 60 steps with bucket growth."""
-    name, L, h, hq, hkv, D, F, V, dt = dims
+    for bit, over 60 steps.  The bucket is sized so that the slice exists (it
+    must be able to take the whole O projection)."""
+    name, L, h, hq, hkv, D, F, V, dt, cap = dims
     shape = small_shape(name, L, h, hq, hkv, D, F, V, dt, True, False)
     mw = inputs.make_weights(shape, seed=8, gain_sd=GAIN_SD)
     X0 = inputs.normal(8, 2, 1, (5, h), scale=1.0)
     toks = np.random.default_rng(8).integers(0, V, 60)
-    a = _run_ids(mw, X0, 60, 16, toks, l2_prefetch=True)
-    b = _run_ids(mw, X0, 60, 16, toks, l2_prefetch=False)
+    a = _run_ids(mw, X0, 60, cap, toks, l2_prefetch=True, max_ctx=cap)
+    b = _run_ids(mw, X0, 60, cap, toks, l2_prefetch=False, max_ctx=cap)
     for k in range(len(a)):
         assert np.all(np.isfinite(a[k]))
         assert np.array_equal(a[k], b[k]), f"step {k}: the prefetch changed the logits"

@@ -724,6 +724,9 @@ hipError_t run_chunk_mma(atd_decoder* d, RowMap rows, int M, int max_len_bound, 
     aa.o_hi = d->mhi2;
     aa.o_lo = d->mlo2;
     aa.o_frag = 1;
+    // many rows: the blocks' states are merged by a second launch, so no
+    // block holds its compute unit through the ticket's round trips
+    aa.defer = 1;
     if (fused)
       STAGE(ATD_STAGE_ATTN, attention(d, aa, s));
     else

@@ -184,6 +184,10 @@ struct AttnArgs {
   uint16_t* o_hi;     // or, when set, bf16 hi/lo parts of o: [M, Hq * D]
   uint16_t* o_lo;
   int o_frag;         // o_hi / o_lo in MFMA-fragment order (frag_off; M <= 64)
+  // deferred merge: the blocks of a (row, KV head) write their partial states
+  // and a second launch (k_attn_merge) merges them, in place of the
+  // last-arriving block (no prefetch slice with it)
+  int defer;
   // with pf.nreg > 0 the launch has one more z slice (z = M) whose
   // workgroups only run the prefetch
   L2Prefetch pf;

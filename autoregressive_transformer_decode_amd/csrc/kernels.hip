@@ -795,7 +795,83 @@ __device__ __forceinline__ void l2_prefetch(const L2Prefetch& p, int j, int P, i
   asm volatile("" ::"v"(acc));   // the loads count as used
 }
 
-template <typename KT, int D, int R, int LPK, int U>
+// Merge of the partial states of the nblk blocks of (row m, KV head g) in
+// block order, by the 256 threads of one workgroup: P phases per (query head,
+// channel group) item, phase p merging blocks p, p + P, ... online, then the
+// phases merged in order; writes the attention output.  COH: read the states
+// at the device-coherent level (written in the same launch), else plainly
+// (written by an earlier launch).
+template <int D, int R, bool COH>
+__device__ __forceinline__ void attn_merge_states(const AttnArgs& a, int m, int g, int nblk) {
+  constexpr int NC = D / 4;
+  constexpr int ITEMS = R * NC;
+  constexpr int P = 256 / ITEMS;
+  __shared__ float s_pm[P][ITEMS], s_pl[P][ITEMS];
+  __shared__ float4 s_pa[P][ITEMS];
+  const int tid = threadIdx.x;
+  const int item = tid % ITEMS, j = item / NC, c = item % NC;
+  const size_t head = (size_t)m * a.Hq + g * R + j;
+  const int ph = tid / ITEMS;
+  if (ph < P) {
+    float M = -1e30f, L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    // a batch of partials is loaded together (one memory round trip), then
+    // merged in order; indexes past the last block re-read it and are skipped
+    constexpr int NB = 8;
+    for (int b0 = ph; b0 < nblk; b0 += NB * P) {
+      float bm[NB], bl[NB];
+      float4 v[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const size_t pb = head * a.nsplit_max + min(b0 + i * P, nblk - 1);
+        if constexpr (COH) {
+          load_coherent2(a.pml + pb * 2, bm[i], bl[i]);
+          v[i] = load_coherent4(a.pacc + pb * D + 4 * c);
+        } else {
+          const float2 t = *reinterpret_cast<const float2*>(a.pml + pb * 2);
+          bm[i] = t.x;
+          bl[i] = t.y;
+          v[i] = *reinterpret_cast<const float4*>(a.pacc + pb * D + 4 * c);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (b0 + i * P < nblk) {
+          const float nm = fmaxf(M, bm[i]);
+          const float ca = expf(M - nm), cb = expf(bm[i] - nm);
+          L = L * ca + bl[i] * cb;
+          A = make_float4(A.x * ca + v[i].x * cb, A.y * ca + v[i].y * cb,
+                          A.z * ca + v[i].z * cb, A.w * ca + v[i].w * cb);
+          M = nm;
+        }
+      }
+    }
+    s_pm[ph][item] = M;
+    s_pl[ph][item] = L;
+    s_pa[ph][item] = A;
+  }
+  __syncthreads();
+  if (tid < ITEMS) {
+    float M = s_pm[0][item];
+#pragma unroll
+    for (int q = 1; q < P; ++q) M = fmaxf(M, s_pm[q][item]);
+    float L = 0.f;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      const float cq = expf(s_pm[q][item] - M);
+      L = fmaf(s_pl[q][item], cq, L);
+      const float4 v = s_pa[q][item];
+      A = make_float4(fmaf(v.x, cq, A.x), fmaf(v.y, cq, A.y), fmaf(v.z, cq, A.z), fmaf(v.w, cq, A.w));
+    }
+    store_o4<D>(a, head * D + 4 * c, make_float4(A.x / L, A.y / L, A.z / L, A.w / L));
+  }
+}
+
+// DEFER: the blocks of a (row, KV head) only write their partial states;
+// k_attn_merge (the next launch) merges them.  Otherwise the last block to
+// arrive merges them in this launch.
+template <typename KT, int D, int R, int LPK, int U, bool DEFER>
 __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   constexpr int VEC = Vec16<KT>::N;   // channels per 16-byte load
   constexpr int DPL = D / LPK;        // channels per lane (LPK lanes per key row)
@@ -1145,12 +1221,19 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
     } else {
       // the block's partial, written through to the device-coherent level so
       // that the block that merges them (on any XCD) reads the values stored
+      // (deferred: plain stores, the launch boundary makes them visible)
       const size_t pb = head * a.nsplit_max + blk;
-      store_coherent4(a.pacc + pb * D + 4 * c, A);
-      if (c == 0) store_coherent2(a.pml + pb * 2, M, L);
+      if constexpr (DEFER) {
+        *reinterpret_cast<float4*>(a.pacc + pb * D + 4 * c) = A;
+        if (c == 0) *reinterpret_cast<float2*>(a.pml + pb * 2) = make_float2(M, L);
+      } else {
+        store_coherent4(a.pacc + pb * D + 4 * c, A);
+        if (c == 0) store_coherent2(a.pml + pb * 2, M, L);
+      }
     }
   }
   if (nblk == 1) return;
+  if constexpr (DEFER) return;
   // ticket of this (row, KV head): the block that arrives last merges every
   // block's partial, in block order (the result does not depend on which
   // block arrives last)
@@ -1166,59 +1249,20 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
-  // P phases per item: phase p merges blocks p, p + P, ... (online, in order),
-  // then the phases are merged in order
-  constexpr int P = 256 / ITEMS;
-  __shared__ float s_pm[P][ITEMS], s_pl[P][ITEMS];
-  __shared__ float4 s_pa[P][ITEMS];
-  const int ph = tid / ITEMS;
-  if (ph < P) {
-    float M = -1e30f, L = 0.f;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    // a batch of partials is loaded together (one memory round trip), then
-    // merged in order; indexes past the last block re-read it and are skipped
-    constexpr int NB = 8;
-    for (int b0 = ph; b0 < nblk; b0 += NB * P) {
-      float bm[NB], bl[NB];
-      float4 v[NB];
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const size_t pb = head * a.nsplit_max + min(b0 + i * P, nblk - 1);
-        load_coherent2(a.pml + pb * 2, bm[i], bl[i]);
-        v[i] = load_coherent4(a.pacc + pb * D + 4 * c);
-      }
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        if (b0 + i * P < nblk) {
-          const float nm = fmaxf(M, bm[i]);
-          const float ca = expf(M - nm), cb = expf(bm[i] - nm);
-          L = L * ca + bl[i] * cb;
-          A = make_float4(A.x * ca + v[i].x * cb, A.y * ca + v[i].y * cb,
-                          A.z * ca + v[i].z * cb, A.w * ca + v[i].w * cb);
-          M = nm;
-        }
-      }
-    }
-    s_pm[ph][item] = M;
-    s_pl[ph][item] = L;
-    s_pa[ph][item] = A;
-  }
-  __syncthreads();
-  if (tid < ITEMS) {
-    float M = s_pm[0][item];
-#pragma unroll
-    for (int q = 1; q < P; ++q) M = fmaxf(M, s_pm[q][item]);
-    float L = 0.f;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-      const float cq = expf(s_pm[q][item] - M);
-      L = fmaf(s_pl[q][item], cq, L);
-      const float4 v = s_pa[q][item];
-      A = make_float4(fmaf(v.x, cq, A.x), fmaf(v.y, cq, A.y), fmaf(v.z, cq, A.z), fmaf(v.w, cq, A.w));
-    }
-    store_o4<D>(a, head * D + 4 * c, make_float4(A.x / L, A.y / L, A.z / L, A.w / L));
-  }
+  attn_merge_states<D, R, true>(a, m, g, nblk);
+}
+
+// The deferred merge: one workgroup per (KV head, row) of a DEFER launch.
+template <int D, int R>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  const int g = blockIdx.x, m = blockIdx.y;
+  int slot, pos;
+  row_of(a.rows, a.st, m, slot, pos);
+  const int len = pos + 1;
+  const int chunk = attn_chunk(len, a.M, a.Hkv, a.waves);
+  const int nblk = ((len + chunk - 1) / chunk + 3) / 4;
+  if (nblk == 1) return;   // that row's block wrote the output itself
+  attn_merge_states<D, R, false>(a, m, g, nblk);
 }
 
 // ------------------------------------------------------------------ slot bookkeeping
@@ -3135,16 +3179,30 @@ static void attn_dispatch_r(const AttnArgs& a, int r, dim3 grid, hipStream_t s) 
   constexpr int LPK0 = sizeof(KT) == 2 ? 8 : 16;
   constexpr int LPK = LPK0 < D / Vec16<KT>::N ? LPK0 : D / Vec16<KT>::N;
   constexpr int U = 2;
+  const dim3 mgrid(a.Hkv, a.M);
+  if (a.defer) {
+    switch (r) {
+      case 1: hipLaunchKernelGGL((k_attn_split<KT, D, 1, LPK, U, true>), grid, dim3(256), 0, s, a);
+              hipLaunchKernelGGL((k_attn_merge<D, 1>), mgrid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((k_attn_split<KT, D, 2, LPK, U, true>), grid, dim3(256), 0, s, a);
+              hipLaunchKernelGGL((k_attn_merge<D, 2>), mgrid, dim3(256), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((k_attn_split<KT, D, 4, LPK, U, true>), grid, dim3(256), 0, s, a);
+              hipLaunchKernelGGL((k_attn_merge<D, 4>), mgrid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((k_attn_split<KT, D, 8, LPK, U, true>), grid, dim3(256), 0, s, a);
+               hipLaunchKernelGGL((k_attn_merge<D, 8>), mgrid, dim3(256), 0, s, a); break;
+    }
+    return;
+  }
   switch (r) {
-    case 1: hipLaunchKernelGGL((k_attn_split<KT, D, 1, LPK, U>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_split<KT, D, 2, LPK, U>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_split<KT, D, 4, LPK, U>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_attn_split<KT, D, 8, LPK, U>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_attn_split<KT, D, 1, LPK, U, false>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_attn_split<KT, D, 2, LPK, U, false>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_attn_split<KT, D, 4, LPK, U, false>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_attn_split<KT, D, 8, LPK, U, false>), grid, dim3(256), 0, s, a); break;
   }
 }
 
 hipError_t launch_attention(const AttnArgs& a, int bf16, int D, int r, hipStream_t s) {
-  if (a.pf.nreg < 0 || a.pf.nreg > kPfRegions) return hipErrorInvalidValue;
+  if (a.pf.nreg < 0 || a.pf.nreg > kPfRegions || (a.defer && a.pf.nreg)) return hipErrorInvalidValue;
   for (int i = 0; i < a.pf.nreg; ++i)
     if (!a.pf.base[i] || a.pf.bb[i] % 16 || a.pf.nblk[i] < 0) return hipErrorInvalidValue;
   dim3 grid((a.nsplit_max + 3) / 4, a.Hkv, a.M + (a.pf.nreg > 0 ? 1 : 0));

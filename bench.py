@@ -211,8 +211,11 @@ def _source_hash(starts) -> str:
 
 
 def attn_kernel_hash() -> str:
-    """Hash of the split-K attention kernel's source and its launch shape."""
-    return _source_hash(("template <typename KT, int D, int R, int LPK, int U>",
+    """Hash of the split-K attention kernels' sources (split, state merge) and
+    their launch shape."""
+    return _source_hash(("template <int D, int R, bool COH>",
+                         "template <typename KT, int D, int R, int LPK, int U, bool DEFER>",
+                         "template <int D, int R>\n__global__ __launch_bounds__(256) void k_attn_merge(",
                          "static void attn_dispatch_r(", "hipError_t launch_attention("))
 
 
@@ -619,8 +622,8 @@ def bench_batched(args, wl, dm=None, mw=None, steps=None, warmup=None):
         roofline=dict(bound="hbm", achieved=a_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=a_gbs / HBM_PEAK_GBS,
                       traffic=traffic_per_launch(a_bytes, ATTN_TRAFFIC_FILE, attn_kernel_hash),
-                      traffic_kernel="k_attn_split (counters of the split kernel alone)",
-                      kernel="attention stage (k_attn_split, combine inside), 64 rows",
+                      traffic_kernel="k_attn_split + k_attn_merge (counters of the stage's two launches)",
+                      kernel="attention stage (k_attn_split, then k_attn_merge for the blocks' states), 64 rows",
                       bytes_per_launch=a_bytes, avg_launch_us=st["attention"],
                       launches_timed=reps * s.n_layers),
         gemm_gate_up=dict(us=st["gate_up"], tflops=gu_flops / (st["gate_up"] / 1e6) / 1e12,

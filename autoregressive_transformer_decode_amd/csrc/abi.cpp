@@ -341,7 +341,7 @@ SlotTables slots_of(const atd_decoder* d) {
 
 // Split-count target of the attention for M rows: enough waves to spread the
 // KV stream over the chip, few enough that each split carries real work.
-int attn_waves(int M) { return M <= 4 ? 1024 : kAttnWavesMax; }
+int attn_waves(int M) { return M <= 4 ? kAttnWavesFew : kAttnWavesMax; }
 
 // Launch a stage unless decoder_time_stage restricts the sequence to another.
 #define STAGE(stage, call)                                              \

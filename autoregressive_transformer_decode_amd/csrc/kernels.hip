@@ -25,8 +25,9 @@
 // Attention at decode reads the K and V rows once; each row's key range is
 // split into chunks set by its valid length (split-K over the sequence)
 // whose partial softmax states (running max, sum, weighted V) are merged in a
-// fixed order inside the launch, so results depend neither on the cache
-// capacity nor on launch timing.
+// fixed order, inside the launch for up to 4 rows and by a second launch
+// (k_attn_merge) for more, so results depend neither on the cache capacity
+// nor on launch timing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
